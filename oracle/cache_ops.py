@@ -1,0 +1,109 @@
+"""Oracle: writing new K/V rows into slots, copying blocks, int8 quantise-on-write.
+
+Test infrastructure only (see the package docstring).
+
+Pool layout used throughout: ``pool[block][head][offset][dim]``; a slot is
+``block * block_size + offset`` (the lookup of "PagedAttention — 把 KV cache
+当虚拟内存页来管理", 实践案例 / 案例 2). New rows are ``new[i][head][dim]``.
+
+* :func:`write_kv` — every row ``i`` with ``slot[i] >= 0`` goes to its slot,
+  rounded to nearest even into the pool dtype. Negative slots are skipped.
+* :func:`copy_blocks` — copy-on-write copies whole blocks: the note's 案例 3
+  says the copy unit is one block, not the whole prompt.
+* :func:`write_kv_int8` — FP16 -> INT8 cache compression is listed by "KV
+  Cache与长上下文管理" (section 二.3 and its summary list) without a scheme. The
+  scheme here is this project's reading: symmetric int8 codes in [-127, 127]
+  with one fp16 scale per (block, head), separately for K and V.
+
+  Within one call the rows that land in one (block, head) form a group:
+    a     = max |x| over the group (fp32)
+    s_new = fp16(a / 127)                (IEEE fp32 divide, then RNE to fp16)
+    s_old = 0 if the group writes offset 0 (a block being opened), else the
+            stored scale
+    s     = max(s_old, s_new)
+  If ``s > s_old > 0`` every row of the block that the call does not write is
+  re-coded: ``q' = clamp(rne(fp32(q) * s_old / s), -127, 127)`` (fp32 product,
+  IEEE fp32 divide). New rows: ``q = clamp(rne(x / s), -127, 127)`` in fp32, or
+  0 when ``s == 0``. The stored scale becomes ``s``.
+  Parity unpinned beyond this definition: the pages fix no int8 scheme.
+"""
+
+from __future__ import annotations
+
+from collections import OrderedDict
+
+import numpy as np
+
+F32 = np.float32
+
+
+def write_kv(k_pool: np.ndarray, v_pool: np.ndarray, k_new: np.ndarray, v_new: np.ndarray,
+             slot_mapping, block_size: int = 16) -> None:
+    """Scatter rows into float pools in place (f32 or f16 pools)."""
+    for i, sl in enumerate(np.asarray(slot_mapping, dtype=np.int64)):
+        if sl < 0:
+            continue
+        b, o = int(sl) // block_size, int(sl) % block_size
+        k_pool[b, :, o, :] = np.asarray(k_new[i]).astype(k_pool.dtype)
+        v_pool[b, :, o, :] = np.asarray(v_new[i]).astype(v_pool.dtype)
+
+
+def copy_blocks(pools, pairs) -> None:
+    """``pool[dst] = pool[src]`` for every (src, dst) pair, in pair order.
+
+    ``pools`` is a list of arrays whose first axis is the block id (K, V and,
+    for int8, the two scale arrays).
+    """
+    for src, dst in np.asarray(pairs, dtype=np.int64).reshape(-1, 2):
+        for p in pools:
+            p[dst] = p[src].copy()
+
+
+def _quantise_group(codes: np.ndarray, scales: np.ndarray, b: int, h: int,
+                    offsets: list, rows: list, block_size: int) -> None:
+    """Apply the int8 group rule to one (block, head) of one tensor."""
+    x = np.stack([np.asarray(r, dtype=F32) for r in rows])          # [G][D] fp32
+    a = np.max(np.abs(x)) if x.size else F32(0)
+    s_new = np.float16(F32(a) / F32(127.0))
+    opened = 0 in offsets
+    s_old = F32(0.0) if opened else F32(scales[b, h])
+    s = max(F32(s_old), F32(s_new))
+    if s_old > 0 and s > s_old:
+        for r in range(block_size):
+            if r in offsets:
+                continue
+            old = codes[b, h, r, :].astype(F32)
+            codes[b, h, r, :] = np.clip(np.rint((old * s_old) / F32(s)), -127, 127).astype(np.int8)
+    for o, row in zip(offsets, x):
+        if s == 0:
+            codes[b, h, o, :] = 0
+        else:
+            codes[b, h, o, :] = np.clip(np.rint(row / F32(s)), -127, 127).astype(np.int8)
+    scales[b, h] = np.float16(s)
+
+
+def write_kv_int8(k_codes: np.ndarray, k_scale: np.ndarray, v_codes: np.ndarray,
+                  v_scale: np.ndarray, k_new: np.ndarray, v_new: np.ndarray,
+                  slot_mapping, block_size: int = 16) -> None:
+    """Quantise-on-write into int8 pools with per-(block, head) fp16 scales."""
+    groups: "OrderedDict[int, list]" = OrderedDict()
+    for i, sl in enumerate(np.asarray(slot_mapping, dtype=np.int64)):
+        if sl < 0:
+            continue
+        groups.setdefault(int(sl) // block_size, []).append((int(sl) % block_size, i))
+    H = k_codes.shape[1]
+    for b, members in groups.items():
+        offsets = [o for o, _ in members]
+        for h in range(H):
+            _quantise_group(k_codes, k_scale, b, h, offsets,
+                            [k_new[i][h] for _, i in members], block_size)
+            _quantise_group(v_codes, v_scale, b, h, offsets,
+                            [v_new[i][h] for _, i in members], block_size)
+
+
+def kv_bytes_per_token(layers: int, hidden: int, bytes_per_value: int) -> int:
+    """KV cache bytes one token keeps: 2 (K and V) x layers x hidden x bytes.
+
+    The note's 实践案例 / 案例 1 uses this to show why the cache is large.
+    """
+    return 2 * layers * hidden * bytes_per_value

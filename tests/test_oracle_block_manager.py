@@ -1,0 +1,219 @@
+"""Pins for the oracle's block-manager model (CPU only)."""
+
+import copy
+
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle.block_manager import BlockManager, InvalidArg, OutOfBlocks, OutOfRange, StateError
+
+
+def test_cow_worked_example(load_golden):
+    g = load_golden("cow_ref4.json")
+    bm = BlockManager(16, 16, free_order=range(16))
+    bm.add_seq(0, 20)                          # block 0 full, block 1 holds 4 tokens
+    for child in (1, 2, 3):
+        bm.fork(0, child)
+    shared = bm.table(0)[0][-1]
+    assert bm.ref_count(shared) == g["initial_ref_count"]
+    slot, src, dst = bm.append(1)
+    assert g["after_first_append"]["copied"] and (src, dst) == (shared, bm.table(1)[0][-1])
+    assert bm.ref_count(shared) == g["after_first_append"]["shared_ref_count"]
+    assert bm.ref_count(dst) == g["after_first_append"]["copy_ref_count"]
+    assert slot == dst * 16 + 4
+    # Extension: the next two sharers copy too, the last one writes in place.
+    assert bm.append(2)[1] == shared and bm.ref_count(shared) == 2
+    assert bm.append(3)[1] == shared and bm.ref_count(shared) == 1
+    s0, src0, _ = bm.append(0)
+    assert src0 == -1 and s0 == shared * 16 + 4
+    # The full first block stays shared by all four: full blocks are never copied.
+    assert bm.ref_count(bm.table(0)[0][0]) == 4
+
+
+def test_slot_follows_the_locate_rule(load_golden):
+    g = load_golden("locate_worked_example.json")
+    # Free list arranged so the sequence receives exactly the example's table.
+    order = g["block_table"] + [b for b in range(8) if b not in g["block_table"]]
+    bm = BlockManager(8, g["block_size"], free_order=order)
+    slots = bm.add_seq(0, 35)
+    assert bm.table(0)[0] == g["block_table"]
+    assert slots[g["token_index"]] == g["physical"] * 16 + g["offset"]
+
+
+def test_blocks_are_allocated_on_demand():
+    bm = BlockManager(64, 16, free_order=W.free_order(3, 64))
+    bm.add_seq(7, 0)
+    for n in range(1, 200):
+        bm.append(7)
+        row, ctx = bm.table(7)
+        assert ctx == n and len(row) == -(-n // 16)
+    assert bm.num_free() == 64 - 13
+
+
+def test_fragmentation_case(load_golden):
+    g = load_golden("fragmentation_2048x2.json")
+    blocks = lambda t: t // 16
+    total = blocks(g["user_a_tokens"]) + 8 + blocks(g["user_b_tokens"]) + 8
+    # Contiguous first-fit model: A | X | B | Y laid out back to back.
+    layout = [("A", blocks(g["user_a_tokens"])), ("X", 8), ("B", blocks(g["user_b_tokens"])), ("Y", 8)]
+    free_runs = [n for name, n in layout if name in ("A", "B")]
+    assert (max(free_runs) >= blocks(g["new_user_tokens"])) == g["contiguous_allocation_succeeds"]
+    # Paged: the same occupancy, then A and B leave; the new user still fits.
+    bm = BlockManager(total, 16, free_order=range(total))
+    bm.add_seq(0, g["user_a_tokens"])
+    bm.add_seq(1, 128)
+    bm.add_seq(2, g["user_b_tokens"])
+    bm.add_seq(3, 128)
+    assert bm.num_free() == 0
+    bm.free_seq(0)
+    bm.free_seq(2)
+    ok = True
+    try:
+        bm.add_seq(4, g["new_user_tokens"])
+    except OutOfBlocks:
+        ok = False
+    assert ok == g["paged_allocation_succeeds"]
+    row, _ = bm.table(4)
+    assert sorted(row) == list(range(128)) + list(range(136, 264))
+
+
+def test_ring_moves_no_data_and_keeps_logical_order(load_golden):
+    g = load_golden("ring_window.json")
+    Wb = 4
+    bm = BlockManager(32, 16, free_order=W.free_order(5, 32), window_blocks=Wb)
+    bm.add_seq(0, 0)
+    for _ in range(Wb * 16):
+        bm.append(0)
+    before, ctx = bm.table(0)
+    free_before = bm.num_free()
+    slot, src, dst = bm.append(0)               # token 64: the window is full
+    after, ctx2 = bm.table(0)
+    assert (src, dst) == (-1, -1)               # nothing copied
+    assert after == before[1:] + [before[0]]    # oldest page reused as the newest
+    assert slot == before[0] * 16               # the new token goes into it
+    assert bm.num_free() == free_before         # no allocation at all
+    assert ctx == 64 and ctx2 == 49
+    assert g["kv_bytes_moved_per_slide"] == 0
+    # Many more slides: the row stays W blocks, the live context stays in range.
+    for _ in range(1000):
+        bm.append(0)
+        row, c = bm.table(0)
+        assert len(row) == Wb and (Wb - 1) * 16 < c <= Wb * 16
+        assert sorted(row) == sorted(before)
+
+
+def test_ring_with_a_shared_oldest_block_takes_a_fresh_one():
+    bm = BlockManager(16, 16, free_order=range(16), window_blocks=2)
+    bm.add_seq(0, 32)
+    bm.fork(0, 1)
+    slot, src, dst = bm.append(1)
+    row1, _ = bm.table(1)
+    assert row1 == [1, 2] and bm.ref_count(0) == 1 and bm.ref_count(2) == 1
+    assert (src, dst) == (-1, -1) and slot == 2 * 16
+
+
+def _invariants(bm: BlockManager):
+    refs = [0] * bm.num_blocks
+    for st in bm.seqs.values():
+        for b in st.table:
+            refs[b] += 1
+    assert refs == bm.ref
+    free = set(bm.free)
+    used = {b for b in range(bm.num_blocks) if bm.ref[b] > 0}
+    assert len(free) == len(bm.free)
+    assert free.isdisjoint(used) and free | used == set(range(bm.num_blocks))
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_operation_sequences_keep_the_invariants(seed):
+    rng = W.rng(seed, 77)
+    window = int(rng.integers(0, 2)) * int(rng.integers(2, 6))
+    bm = BlockManager(48, 16, free_order=W.free_order(seed, 48), window_blocks=window)
+    content = {}          # slot -> token id written there (models the pool)
+    owner_tokens = {}     # seq -> list of token ids in logical order
+    next_id = 0
+    serial = 0            # unique id of every appended token
+    live = []
+    for _ in range(600):
+        op = rng.integers(0, 10)
+        try:
+            if op == 0 or not live:
+                s = next_id
+                n = int(rng.integers(0, 40))
+                if window:
+                    n = min(n, window * 16)
+                slots = bm.add_seq(s, n)
+                ids = list(range(next_id * 1000, next_id * 1000 + n))
+                for sl, tid in zip(slots, ids):
+                    content[int(sl)] = tid
+                owner_tokens[s] = ids
+                live.append(s)
+                next_id += 1
+            elif op == 1:
+                p = live[int(rng.integers(len(live)))]
+                c = next_id
+                bm.fork(p, c)
+                owner_tokens[c] = list(owner_tokens[p])
+                live.append(c)
+                next_id += 1
+            elif op == 2:
+                s = live.pop(int(rng.integers(len(live))))
+                bm.free_seq(s)
+                del owner_tokens[s]
+            else:
+                s = live[int(rng.integers(len(live)))]
+                shared_before = {b: bm.ref[b] for b in range(bm.num_blocks)}
+                slot, src, dst = bm.append(s)
+                if src >= 0:
+                    # Copy-on-write only when the block was shared.
+                    assert shared_before[src] > 1
+                    for o in range(16):
+                        if src * 16 + o in content:
+                            content[dst * 16 + o] = content[src * 16 + o]
+                # The block written into is never shared at write time.
+                assert bm.ref[slot // 16] == 1
+                tid = 10 ** 9 + serial
+                serial += 1
+                content[slot] = tid
+                owner_tokens[s].append(tid)
+        except OutOfBlocks:
+            pass
+        _invariants(bm)
+        # Every live sequence reads back exactly its own tokens through its table.
+        for s in live:
+            row, ctx = bm.table(s)
+            toks = owner_tokens[s][len(owner_tokens[s]) - ctx:]
+            got = [content.get(row[t // 16] * 16 + t % 16) for t in range(ctx)]
+            assert got == toks
+
+
+def test_calls_are_atomic_on_error():
+    bm = BlockManager(4, 16, free_order=range(4))
+    bm.add_seq(0, 48)
+    bm.fork(0, 1)
+    snap = copy.deepcopy(bm.__dict__)
+    with pytest.raises(OutOfBlocks):
+        bm.add_seq(2, 33)
+    assert bm.__dict__ == snap
+    bm.add_seq(2, 16)                 # takes the last block
+    snap = copy.deepcopy(bm.__dict__)
+    with pytest.raises(OutOfBlocks):
+        bm.append(0)                  # offset 0: needs a fresh block
+    assert bm.__dict__ == snap
+    with pytest.raises(StateError):
+        bm.fork(0, 1)
+    with pytest.raises(StateError):
+        bm.free_seq(9)
+    with pytest.raises(StateError):
+        bm.append(9)
+    with pytest.raises(OutOfRange):
+        bm.export([0], 2)
+    with pytest.raises(InvalidArg):
+        BlockManager(4, 16, free_order=[0, 0, 1, 2])
+    assert bm.__dict__ == snap
+    # Freeing the sharers releases the blocks back to the tail of the free list.
+    bm.free_seq(0)
+    assert bm.num_free() == 0
+    bm.free_seq(1)
+    assert list(bm.free) == [0, 1, 2]
