@@ -1,0 +1,278 @@
+"""Benchmark: one paged decode step of an OPT-13B-shaped layer on one MI355X.
+
+A step is the whole hot path for a batch of 64 sequences (contexts drawn
+uniformly from 128..2048 tokens, 40 heads x 128, fp16 KV in 16-token blocks
+scattered over a pool 1.25x the need): host block-manager appends, uploads of
+slots / tables / context lengths, copy-on-write block copies (none arise in
+this workload), the write of the new token's K/V into its slot, and paged
+decode attention.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+Prints one JSON line. ``value`` is KV bytes read per second over the whole
+step (wall clock, inputs resident in HBM); ``roofline`` rates the decode
+kernel alone (algorithmic KV bytes / its average duration from HIP events on
+its stream) against MI355X's 8 TB/s; ``cpu_baseline`` times the fp64 CPU
+oracle on a bounded sample of the same batch. Inputs are synthetic N(0,1).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import subprocess
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, 8 TB/s
+METRIC = "paged decode attention: KV GB/s read (% of HBM peak); decode steps·seqs/s"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--partition-tokens", type=int, default=-1,
+                    help="split-K partition size (0 = single pass, -1 = the tuned default)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="skip contiguous / probe measurements")
+    ap.add_argument("--cpu-baseline-only", action="store_true", help=argparse.SUPPRESS)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help=argparse.SUPPRESS)
+    return ap.parse_args()
+
+
+DEFAULT_PARTITION_TOKENS = 256
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle on a bounded sample (run in a child process so the
+# thread count is fixed before numpy loads).
+def cpu_baseline_child(seconds: float) -> None:
+    import numpy as np
+    import workloads as W
+    from oracle import attention as OA
+    from oracle import cache_ops as OC
+    from oracle import paging as OP
+    from oracle.block_manager import BlockManager
+
+    wl = W.opt13b()
+    H, D = wl.num_heads, wl.head_dim
+    bm = BlockManager(wl.num_blocks, 16, free_order=W.free_order(wl.seed, wl.num_blocks))
+    done_bytes = 0
+    seqs = 0
+    spent = 0.0
+    for s, ctx in enumerate(wl.context_lens):
+        K = W.normal_np((ctx, H, D), wl.seed, W.STREAM_K, s, dtype=np.float16)
+        V = W.normal_np((ctx, H, D), wl.seed, W.STREAM_V, s, dtype=np.float16)
+        q = W.normal_np((1, H, D), wl.seed, W.STREAM_Q, s, dtype=np.float16)
+        nb = -(-ctx // 16)
+        kp = np.zeros((nb, H, 16, D), np.float16)
+        vp = np.zeros((nb, H, 16, D), np.float16)
+        slots = bm.add_seq(s, ctx)
+        table, _ = bm.table(s)
+        local = {b: i for i, b in enumerate(table)}       # compact pool for this sequence
+        OC.write_kv(kp, vp, K, V, [local[int(x) // 16] * 16 + int(x) % 16 for x in slots])
+        t0 = time.perf_counter()
+        OA.paged_decode(q, kp, vp, [list(range(nb))], [ctx])
+        spent += time.perf_counter() - t0
+        done_bytes += ctx * H * D * 2 * 2
+        seqs += 1
+        if spent >= seconds:
+            break
+    print(json.dumps({"seconds": spent, "bytes": done_bytes, "seqs": seqs}))
+
+
+def cpu_baseline(seconds: float) -> dict:
+    env = dict(os.environ, OMP_NUM_THREADS="1", OPENBLAS_NUM_THREADS="1", MKL_NUM_THREADS="1",
+               HIP_VISIBLE_DEVICES="", CUDA_VISIBLE_DEVICES="")
+    r = subprocess.run([sys.executable, os.path.abspath(__file__), "--cpu-baseline-only",
+                        "--cpu-seconds", str(seconds)], capture_output=True, text=True, env=env,
+                       cwd=ROOT, timeout=600)
+    if r.returncode != 0:
+        return {"error": r.stderr[-500:]}
+    d = json.loads(r.stdout.strip().splitlines()[-1])
+    return {"value": round(d["bytes"] / d["seconds"] / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"fp64 numpy oracle (gather through the block table + attention) over the first "
+                      f"{d['seqs']} of the 64 sequences, all 40 heads; {d['bytes'] / 1e6:.1f} MB of KV "
+                      f"in {d['seconds']:.2f} s on one thread",
+            "seqs_per_s": round(d["seqs"] / d["seconds"], 4)}
+
+
+# ---------------------------------------------------------------------------
+def main():
+    args = parse()
+    if args.cpu_baseline_only:
+        cpu_baseline_child(args.cpu_seconds)
+        return 0
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (pass --gpus 1)",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    import workloads as W
+    import paged_kv_cache_249_amd as pk
+    from paged_kv_cache_249_amd.engine import PagedDecodeEngine
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    ptok = DEFAULT_PARTITION_TOKENS if args.partition_tokens < 0 else args.partition_tokens
+    K, Wm = args.steps, args.warmup
+    wl = W.opt13b()
+    S, H, D = wl.num_seqs, wl.num_heads, wl.head_dim
+    # The first timed step attends over exactly the workload's contexts; the
+    # warm-up steps before it and the timed steps after it each add one token.
+    prefill = [c - 1 - Wm for c in wl.context_lens]
+    if min(prefill) < 0:
+        raise SystemExit("warmup longer than the shortest context")
+    final_need = sum(-(-(c + K) // 16) for c in wl.context_lens)
+    num_blocks = max(wl.num_blocks, -(-5 * final_need // 4))
+    cap = -(-(max(wl.context_lens) + K) // 16)
+    eng = PagedDecodeEngine(num_blocks, H, D, pk.PA_F16, S, cap,
+                            free_order=W.free_order(wl.seed, num_blocks), device=dev,
+                            partition_tokens=ptok)
+    for s in range(S):
+        k = W.normal_torch((prefill[s], H, D), wl.seed, W.STREAM_K, s, dtype=torch.float16, device=dev)
+        v = W.normal_torch((prefill[s], H, D), wl.seed, W.STREAM_V, s, dtype=torch.float16, device=dev)
+        eng.add_sequence(s, k, v)
+    ring = 4
+    knew = [W.normal_torch((S, H, D), wl.seed, W.STREAM_KNEW, i, dtype=torch.float16, device=dev) for i in range(ring)]
+    vnew = [W.normal_torch((S, H, D), wl.seed, W.STREAM_VNEW, i, dtype=torch.float16, device=dev) for i in range(ring)]
+    q = W.normal_torch((S, H, D), wl.seed, W.STREAM_Q, dtype=torch.float16, device=dev)
+    out = torch.empty_like(q)
+    seqs = np.arange(S)
+    torch.cuda.synchronize()
+    assert pk.pa_check_errors() == 0
+
+    for i in range(Wm):
+        eng.step(seqs, knew[i % ring], vnew[i % ring], q, out)
+    torch.cuda.synchronize()
+
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    kv_bytes = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        eng.step(seqs, knew[i % ring], vnew[i % ring], q, out, decode_events=events[i])
+        kv_bytes.append(int(eng.last_ctx.astype(np.int64).sum()) * H * D * 2 * 2)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    dev_err = pk.pa_check_errors()
+    wall = t1 - t0
+    dec_ms = [a.elapsed_time(b) for a, b in events]
+    dec_avg_s = sum(dec_ms) / len(dec_ms) / 1e3
+    bytes_avg = sum(kv_bytes) / len(kv_bytes)
+    achieved = bytes_avg / dec_avg_s / 1e9
+    value = sum(kv_bytes) / wall / 1e9
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": Wm,
+        "ms_per_step": round(wall / K * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": "OPT-13B-shaped single-layer paged decode: 64 seqs, ctx ~U[128,2048] "
+                        "(seed 2), 40 heads x 128, fp16 KV, 16-token blocks scattered over a pool "
+                        "1.25x the need; step = block-manager append + uploads + write_kv + decode",
+            "global_batch": S,
+            "seq_len": int(np.mean(wl.context_lens)),
+            "parallelism": "none (1 GPU)",
+            "partition_tokens": ptok,
+            "num_blocks": num_blocks,
+        },
+        "decode_steps_seqs_per_s": round(S * K / wall, 1),
+        "decode_kernel_us": round(dec_avg_s * 1e6, 2),
+        "decode_kernel_us_p10_p90": [round(float(np.percentile(dec_ms, 10)) * 1e3, 2),
+                                     round(float(np.percentile(dec_ms, 90)) * 1e3, 2)],
+        "kv_bytes_per_decode": int(bytes_avg),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+        "device_error_bits": dev_err,
+    }
+
+    if not args.no_extras:
+        result["extras"] = extras(eng, wl, q, ptok, dev)
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def _time_calls(fn, reps=20):
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in ev:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in ev)
+    return ms[len(ms) // 2] / 1e3
+
+
+def extras(eng, wl, q, ptok, dev):
+    """Decode alone at several partition sizes, the contiguous twin and a copy probe."""
+    import numpy as np
+    import torch
+    import workloads as W
+    import paged_kv_cache_249_amd as pk
+
+    S, H, D = wl.num_seqs, wl.num_heads, wl.head_dim
+    seqs = np.arange(S)
+    tables, ctx = eng.bm.export(seqs, eng.cap)
+    nbytes = int(ctx.astype(np.int64).sum()) * H * D * 4
+    out = torch.empty_like(q)
+    tabd = torch.from_numpy(tables).to(dev)
+    ctxd = torch.from_numpy(ctx).to(dev)
+    maxc = int(ctx.max())
+    res = {"ctx_sum": int(ctx.sum())}
+
+    def paged(p):
+        need = pk.pa_decode_workspace_bytes(eng.pool, S, maxc, p)
+        ws = torch.empty(max(need // 4, 1), dtype=torch.float32, device=dev)
+        return lambda: pk.pa_decode(eng.pool, q, out, tabd, ctxd, maxc, partition_tokens=p, workspace=ws)
+
+    for p in (0, 128, 256, 512, 1024):
+        res[f"decode_only_gbs_ptok{p}"] = round(nbytes / _time_calls(paged(p)) / 1e9, 1)
+    # The same contexts in a contiguous [S][H][T][D] cache, no table.
+    T = -(-maxc // 16) * 16
+    kc = torch.randn((S, H, T, D), device=dev, dtype=torch.float16)
+    vc = torch.randn((S, H, T, D), device=dev, dtype=torch.float16)
+    nb = pk.contiguous_workspace_bytes(S, H, D, T, ptok)
+    ws = torch.empty(max(nb // 4, 1), dtype=torch.float32, device=dev)
+    t_contig = _time_calls(lambda: pk.pa_decode_contiguous(kc, vc, q, out, ctxd, partition_tokens=ptok,
+                                                           workspace=ws))
+    t_paged = _time_calls(paged(ptok))
+    res["contiguous_gbs"] = round(nbytes / t_contig / 1e9, 1)
+    res["paged_gbs"] = round(nbytes / t_paged / 1e9, 1)
+    res["paged_vs_contiguous_overhead"] = round(t_paged / t_contig - 1.0, 4)
+    del kc, vc
+    # Streaming copy probe: achievable HBM bandwidth (read + write bytes).
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device=dev)
+    b = torch.empty(n, dtype=torch.uint8, device=dev)
+    t_copy = _time_calls(lambda: pk.pa_stream_copy(b, a))
+    res["stream_copy_gbs"] = round(2 * n / t_copy / 1e9, 1)
+    return res
+
+
+if __name__ == "__main__":
+    sys.exit(main())

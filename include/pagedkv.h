@@ -1,0 +1,295 @@
+/*
+ * pagedkv.h — C ABI of the paged KV cache and paged decode attention library
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The method: each sequence's KV cache is cut into fixed blocks of 16 tokens
+ * that live anywhere in one shared physical pool; a per-sequence block table
+ * maps logical block -> physical block, and the attention of one new query
+ * token per sequence reads its context through that table
+ * ("PagedAttention — 把 KV cache 当虚拟内存页来管理", 是什么 and 实践案例 / 案例 2;
+ * "One Deep Concept #01 — PagedAttention: From Operating System Virtual Memory
+ * to Large Language Model Memory Systems", §4 Core Innovation).
+ *
+ * Conventions for every call
+ * --------------------------
+ * - Return value: PA_OK (0) or a negative pa_status. No call throws or
+ *   aborts. pa_last_error() gives a text for the last failing call of the
+ *   calling thread.
+ * - Ownership: the caller allocates every device buffer (pools, scales, q,
+ *   out, tables, slots, workspace). The library never allocates or frees
+ *   device memory; it only keeps small host descriptors.
+ * - Asynchrony: device calls validate their host-visible arguments, enqueue
+ *   kernels on the caller's stream and return. On a validation error nothing
+ *   is enqueued. A launch failure returns PA_ERR_HIP.
+ * - Device-side indices (table entries, slots, copy pairs) are range-checked
+ *   in the kernels: an out-of-range entry is skipped (a table entry is
+ *   treated as masked, a slot or pair is not written) and a sticky device
+ *   error word is set; pa_check_errors() reads and clears it.
+ * - Layouts (all row-major, element type given by the pool dtype):
+ *     K, V pools    [num_blocks][num_heads][block_size][head_dim]
+ *     int8 scales   [num_blocks][num_heads] fp16 (one per block and head)
+ *     q, out        [num_seqs][num_heads][head_dim]
+ *     new K, V rows [n][num_heads][head_dim]
+ *     block tables  int32 [num_seqs][max_blocks], logical order
+ *     context lens  int32 [num_seqs]
+ *     slot mapping  int64 [n], slot = physical_block * block_size + offset
+ * - Supported geometry: block_size 16, head_dim 64 or 128, num_heads >= 1.
+ *
+ * The block manager (pa_bm_*) is host-only: it touches no device memory and
+ * needs no GPU.
+ */
+#ifndef PAGEDKV_H_
+#define PAGEDKV_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* An opaque stream handle: a hipStream_t (NULL = the default stream). */
+typedef void* pa_stream;
+
+typedef int32_t pa_status;
+enum {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = -1,   /* null pointer, negative size, bad combination   */
+  PA_ERR_UNSUPPORTED = -2,   /* geometry or dtype outside the supported set    */
+  PA_ERR_OUT_OF_BLOCKS = -3, /* block manager: the free list cannot serve it   */
+  PA_ERR_OUT_OF_RANGE = -4,  /* an index or capacity out of range              */
+  PA_ERR_STATE = -5,         /* unknown / duplicate sequence, double free      */
+  PA_ERR_HIP = -6            /* a HIP runtime call failed                      */
+};
+
+typedef enum { PA_F32 = 0, PA_F16 = 1, PA_I8 = 2 } pa_dtype;
+
+/* Device error word bits, reported by pa_check_errors(). */
+enum {
+  PA_DEV_BAD_TABLE_ENTRY = 1,  /* a table entry outside [0, num_blocks)        */
+  PA_DEV_BAD_SLOT = 2,         /* a slot outside the pool                      */
+  PA_DEV_BAD_PAIR = 4,         /* a copy pair outside the pool                 */
+  PA_DEV_BAD_CONTEXT = 8,      /* context_lens[s] < 0 or > the stated maximum  */
+  PA_DEV_BAD_RUN = 16          /* int8 write: one block hit by more than 16 rows
+                                  of one run (duplicate slots)                 */
+};
+
+/* Text of the last failing call on this thread ("" if none). Never NULL. */
+const char* pa_last_error(void);
+
+/* Library version as 10000*major + 100*minor + patch. */
+int32_t pa_version(void);
+
+/* ----------------------------------------------------------------------------
+ * Pool descriptor.
+ *
+ * The pool is the shared physical block store of the method ("One Deep
+ * Concept #01", §4 Core Innovation: logical KV blocks -> block table ->
+ * physical GPU blocks). K and V are separate arrays; int8 pools carry one fp16
+ * scale per (block, head) for K and one for V.
+ * ------------------------------------------------------------------------- */
+typedef struct pa_pool pa_pool;
+
+/* Bytes the caller must allocate for one of K or V (*kv_bytes) and for one of
+ * the int8 scale arrays (*scale_bytes, 0 unless kv_dtype == PA_I8).
+ * Errors: PA_ERR_INVALID_ARG (null outputs, non-positive sizes),
+ * PA_ERR_UNSUPPORTED (block_size != 16, head_dim not 64/128). */
+pa_status pa_pool_bytes(int32_t num_blocks, int32_t block_size, int32_t num_heads,
+                        int32_t head_dim, pa_dtype kv_dtype, int64_t* kv_bytes,
+                        int64_t* scale_bytes);
+
+/* Create a descriptor over caller-owned device buffers. k_cache / v_cache must
+ * each hold pa_pool_bytes(...)->kv_bytes and be 16-byte aligned; k_scale /
+ * v_scale must be given for PA_I8 and NULL otherwise. The buffers stay owned
+ * by the caller and must outlive the descriptor. *out receives the handle.
+ * Errors: as pa_pool_bytes, plus PA_ERR_INVALID_ARG for null or misaligned
+ * buffers and scales given for a float pool. */
+pa_status pa_alloc_pool(int32_t num_blocks, int32_t block_size, int32_t num_heads,
+                        int32_t head_dim, pa_dtype kv_dtype, void* k_cache, void* v_cache,
+                        void* k_scale, void* v_scale, pa_pool** out);
+
+/* Destroy the descriptor (never the buffers). NULL is accepted. */
+pa_status pa_free_pool(pa_pool* pool);
+
+/* ----------------------------------------------------------------------------
+ * Write new K/V rows into their slots (reshape-and-cache).
+ *
+ * Row i of k_new / v_new ([n][num_heads][head_dim], dtype src_dtype, PA_F32
+ * or PA_F16) is stored at slot_mapping[i] (device int64): block
+ * slot / block_size, offset slot % block_size — the lookup of "PagedAttention
+ * — 把 KV cache 当虚拟内存页来管理", 实践案例 / 案例 2. A negative slot skips the
+ * row. Float pools store the row rounded to nearest even.
+ *
+ * int8 pools quantise on write (the FP16 -> INT8 compression listed in "KV
+ * Cache与长上下文管理", section 二.3; the scheme is this library's): rows of one
+ * call that land in one (block, head) form a group with a = max|x|;
+ * s_new = fp16(a / 127); s_old = 0 if the group writes offset 0, else the
+ * stored scale; s = max(s_old, s_new). If s > s_old > 0 the block's rows not
+ * written by the call are re-coded as clamp(rne(q * s_old / s), -127, 127);
+ * new rows are clamp(rne(x / s), -127, 127) (0 if s == 0); the stored scale
+ * becomes s. All arithmetic is IEEE fp32 with correctly rounded division.
+ * Precondition for int8 pools: the entries of slot_mapping that hit one block
+ * are adjacent (true for decode, one row per sequence, and for a sequence's
+ * prefill in token order); otherwise the result for that block is unspecified
+ * (never out of bounds).
+ * Duplicate slots in one call leave one of the rows (which one is unspecified).
+ * n == 0 is a no-op. Errors: PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_HIP.
+ */
+pa_status pa_write_kv(pa_pool* pool, const void* k_new, const void* v_new, pa_dtype src_dtype,
+                      const int64_t* slot_mapping, int32_t n, pa_stream stream);
+
+/* ----------------------------------------------------------------------------
+ * Copy whole blocks (copy-on-write).
+ *
+ * For every pair p < n of pairs ([n][2] device int32, {src, dst}) copies
+ * K[src] -> K[dst] and V[src] -> V[dst] over all heads and offsets, plus the
+ * two scales of an int8 pool. The unit of the copy is one block, as in
+ * "PagedAttention — 把 KV cache 当虚拟内存页来管理", 实践案例 / 案例 3. Pairs are
+ * independent: no dst may appear twice or also be a src in the same call.
+ * n == 0 is a no-op. Errors: PA_ERR_INVALID_ARG, PA_ERR_HIP.
+ */
+pa_status pa_copy_blocks(pa_pool* pool, const int32_t* pairs, int32_t n, pa_stream stream);
+
+/* ----------------------------------------------------------------------------
+ * Paged decode attention.
+ *
+ * For each sequence s and head h, with ctx = context_lens[s] and
+ * k_t = K[table[s][t / 16]][h][t % 16] (int8: code * scale[block][h]):
+ *     out[s][h] = sum_{t < ctx} softmax_t(q[s][h] . k_t * sm_scale) v_t
+ * ("One Deep Concept #01", §2 Background: softmax(Q K^T / sqrt(d)) V; the
+ * table indirection of "PagedAttention — 把 KV cache 当虚拟内存页来管理",
+ * 实践案例 / 案例 2). Accumulation is fp32; out is stored in q_dtype (round to
+ * nearest even for PA_F16). ctx == 0 gives zeros. Only the first
+ * ceil(ctx / 16) table entries of a row are read; tokens at t >= ctx are
+ * never used, whatever the pool holds there.
+ *
+ * q_dtype: PA_F32 or PA_F16 (q and out). sm_scale <= 0 selects 1/sqrt(head_dim).
+ * partition_tokens == 0: one workgroup per (sequence, head) covers the whole
+ * context (single pass; workspace may be NULL).
+ * partition_tokens  > 0 (a multiple of 16): split-K. Every (sequence, head,
+ * partition of partition_tokens tokens) is decoded on its own and writes its
+ * partial (m, l, o) into workspace; a second kernel merges them by
+ * log-sum-exp. Sequences with a single partition are written directly.
+ * max_context_len bounds every context_lens[s] (larger values are clamped and
+ * flagged with PA_DEV_BAD_CONTEXT); max_blocks is the row stride of
+ * block_tables and must be >= ceil(max_context_len / 16).
+ * Errors: PA_ERR_INVALID_ARG (null pointers, bad sizes, workspace too small),
+ * PA_ERR_UNSUPPORTED, PA_ERR_HIP.
+ */
+pa_status pa_decode_workspace_bytes(const pa_pool* pool, int32_t num_seqs,
+                                    int32_t max_context_len, int32_t partition_tokens,
+                                    int64_t* bytes);
+
+pa_status pa_decode(pa_pool* pool, const void* q, pa_dtype q_dtype, void* out,
+                    const int32_t* block_tables, int32_t max_blocks,
+                    const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
+                    float sm_scale, int32_t partition_tokens, void* workspace,
+                    int64_t workspace_bytes, pa_stream stream);
+
+/* Layout of the split-K workspace, for callers that inspect partials: with
+ * P = ceil(max_context_len / partition_tokens), the workspace holds
+ *   m [num_seqs][num_heads][P] fp32   largest logit of the partition (natural units)
+ *   l [num_seqs][num_heads][P] fp32   sum of exp(logit - m)
+ *   o [num_seqs][num_heads][P][head_dim] fp32  attention over the partition alone
+ * back to back, in that order. Entries of partitions past a sequence's context
+ * are not written. */
+
+/* Read and clear the sticky device error word (PA_DEV_* bits). Synchronises
+ * the stream first. *device_error may be NULL to only clear. */
+pa_status pa_check_errors(pa_stream stream, int32_t* device_error);
+
+/* ----------------------------------------------------------------------------
+ * Measurement helpers (not part of the method).
+ *
+ * pa_decode_contiguous runs the same decode arithmetic over a contiguous cache
+ * k[num_seqs][num_heads][max_tokens][head_dim] (same for v), with no block
+ * table, so that the cost of the table indirection can be measured on equal
+ * terms ("PagedAttention — 把 KV cache 当虚拟内存页来管理", 踩过的坑 states an
+ * attention-kernel slowdown from the indirection). Float KV only.
+ * pa_stream_copy copies bytes (a multiple of 16, 16-byte aligned pointers)
+ * with a plain streaming kernel: a bandwidth probe and a counter calibration.
+ * ------------------------------------------------------------------------- */
+pa_status pa_decode_contiguous(const void* k, const void* v, pa_dtype kv_dtype, int32_t num_heads,
+                               int32_t head_dim, int32_t max_tokens, const void* q,
+                               pa_dtype q_dtype, void* out, const int32_t* context_lens,
+                               int32_t num_seqs, float sm_scale, int32_t partition_tokens,
+                               void* workspace, int64_t workspace_bytes, pa_stream stream);
+
+pa_status pa_stream_copy(void* dst, const void* src, int64_t bytes, pa_stream stream);
+
+/* ----------------------------------------------------------------------------
+ * Host block manager.
+ *
+ * Free list, per-block reference counts, copy-on-write on append and a
+ * sliding-window ring:
+ *  - blocks are handed out on demand from the shared free list; any free block
+ *    serves ("KV Cache与长上下文管理", the section on fragmentation);
+ *  - a sequence appending into a block whose count is above one gets a copy:
+ *    the shared count drops by one and the copy starts at one ("PagedAttention
+ *    — 把 KV cache 当虚拟内存页来管理", 实践案例 / 案例 3);
+ *  - with window_blocks > 0 a sequence keeps at most that many live blocks;
+ *    the oldest is invalidated and its physical block reused for new tokens,
+ *    editing only the table ("KV Cache与长上下文管理", the section on the second
+ *    problem paging solves; "PagedAttention的终极用途", part 三).
+ * Policy details: the free list is FIFO, initialised in free_order (NULL =
+ * ascending ids); allocation pops the head; blocks whose count drops to zero
+ * go to the tail in logical order. Copy-on-write is triggered only by an
+ * append at offset > 0 into a shared last block. A ring eviction of a block
+ * still shared by another sequence drops its count and takes a fresh block.
+ * Every call is atomic: on error the state is unchanged. Not thread-safe: the
+ * caller serialises calls on one manager.
+ * ------------------------------------------------------------------------- */
+typedef struct pa_bm pa_bm;
+
+/* free_order: NULL or a permutation of [0, num_blocks) (host int32).
+ * Errors: PA_ERR_INVALID_ARG (sizes, not a permutation), PA_ERR_UNSUPPORTED. */
+pa_status pa_bm_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order,
+                       int32_t window_blocks, pa_bm** out);
+pa_status pa_bm_destroy(pa_bm* bm);
+
+/* Register seq with prefill_tokens tokens; slots_out (host int64
+ * [prefill_tokens], may be NULL when prefill_tokens == 0) receives their
+ * slots. Errors: PA_ERR_STATE (seq exists), PA_ERR_INVALID_ARG (negative, or
+ * more blocks than the window), PA_ERR_OUT_OF_BLOCKS. */
+pa_status pa_bm_add_seq(pa_bm* bm, int64_t seq, int32_t prefill_tokens, int64_t* slots_out);
+
+/* child shares every block of parent; each count rises by one.
+ * Errors: PA_ERR_STATE (unknown parent, existing child). */
+pa_status pa_bm_fork(pa_bm* bm, int64_t parent, int64_t child);
+
+/* Make room for one token of seq. *slot_out receives its slot; *copy_src /
+ * *copy_dst receive the block pair to copy first, or -1 / -1.
+ * Errors: PA_ERR_STATE, PA_ERR_OUT_OF_BLOCKS. */
+pa_status pa_bm_append(pa_bm* bm, int64_t seq, int64_t* slot_out, int32_t* copy_src,
+                       int32_t* copy_dst);
+
+/* pa_bm_append for seqs[0..n) in order, atomically as a whole. slots_out
+ * [n]; pairs_out [n][2] receives the copy pairs compacted in order, and
+ * *n_pairs their number. Errors: as pa_bm_append (state unchanged). */
+pa_status pa_bm_append_batch(pa_bm* bm, const int64_t* seqs, int32_t n, int64_t* slots_out,
+                             int32_t* pairs_out, int32_t* n_pairs);
+
+/* Release seq; blocks whose count reaches zero return to the free list.
+ * Errors: PA_ERR_STATE. */
+pa_status pa_bm_free_seq(pa_bm* bm, int64_t seq);
+
+/* Table row (logical order) and live context length of seq. row may be NULL
+ * to query sizes only. Errors: PA_ERR_STATE, PA_ERR_OUT_OF_RANGE (cap too
+ * small). */
+pa_status pa_bm_table(const pa_bm* bm, int64_t seq, int32_t* row, int32_t cap,
+                      int32_t* n_blocks, int32_t* ctx_len);
+
+/* Rows of seqs[0..n) into tables [n][cap] (unused entries -1) and their live
+ * context lengths into ctx_out [n]. Errors: PA_ERR_STATE, PA_ERR_OUT_OF_RANGE. */
+pa_status pa_bm_export(const pa_bm* bm, const int64_t* seqs, int32_t n, int32_t* tables,
+                       int32_t cap, int32_t* ctx_out);
+
+pa_status pa_bm_ref_count(const pa_bm* bm, int32_t block, int32_t* out);
+pa_status pa_bm_num_free(const pa_bm* bm, int32_t* out);
+/* The free list in order (head first) into out [cap]; *n receives its length. */
+pa_status pa_bm_free_list(const pa_bm* bm, int32_t* out, int32_t cap, int32_t* n);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H_ */

@@ -1,0 +1,92 @@
+"""Build libpagedkv.so for gfx950, in-tree.
+
+    python -m paged_kv_cache_249_amd.build
+
+HIP sources are compiled by hipcc for gfx950 only; the host block manager by
+g++. Objects go to ``paged_kv_cache_249_amd/_build``; the shared library is
+written next to this file. Compiling needs no GPU.
+"""
+
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(PKG, "_build")
+LIB = os.path.join(PKG, "libpagedkv.so")
+
+HIP_SOURCES = ["api.hip", "decode.hip", "cache_ops.hip"]
+CXX_SOURCES = ["block_manager.cpp"]
+
+ARCH = "gfx950"
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+CXX = os.environ.get("CXX", "g++")
+
+HIP_FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fno-gpu-rdc",
+    # Packed fp32 instructions stay off: only scalar / float2 fp32 code is
+    # emitted as single-lane-width VALU ops.
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function", "-Wno-unused-command-line-argument",
+    f"-I{INCLUDE}", f"-I{CSRC}",
+]
+CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", f"-I{INCLUDE}", f"-I{CSRC}"]
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"command failed ({r.returncode}): {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    return r
+
+
+def build(verbose: bool = False, save_temps: str | None = None) -> str:
+    """Compile every source and link libpagedkv.so; returns its path."""
+    if not os.path.exists(HIPCC):
+        raise RuntimeError(f"hipcc not found at {HIPCC}")
+    os.makedirs(BUILD, exist_ok=True)
+    jobs = []
+    for src in HIP_SOURCES:
+        obj = os.path.join(BUILD, src + ".o")
+        cmd = [HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        if save_temps:
+            os.makedirs(save_temps, exist_ok=True)
+            cmd += ["--save-temps"]
+        jobs.append((cmd, obj, save_temps))
+    for src in CXX_SOURCES:
+        obj = os.path.join(BUILD, src + ".o")
+        jobs.append(([CXX, *CXX_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj], obj, None))
+
+    def compile_one(job):
+        cmd, obj, temps = job
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True, cwd=temps or BUILD)
+        if r.returncode != 0:
+            raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+        if verbose and (r.stderr.strip()):
+            print(r.stderr, flush=True)
+        return obj
+
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
+        objs = list(ex.map(compile_one, jobs))
+    tmp = LIB + ".tmp"
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    verbose = "-v" in sys.argv
+    temps = None
+    for a in sys.argv[1:]:
+        if a.startswith("--save-temps="):
+            temps = a.split("=", 1)[1]
+    print(build(verbose=verbose, save_temps=temps))

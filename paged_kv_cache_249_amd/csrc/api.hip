@@ -1,0 +1,292 @@
+// C ABI of libpagedkv: argument validation, the error model, the pool
+// descriptor and the device error word. Kernels live in decode.hip and
+// cache_ops.hip; the host block manager in block_manager.cpp.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <new>
+#include <string>
+
+#include "pa_internal.h"
+
+namespace pa {
+
+namespace {
+thread_local std::string g_last_error;
+
+constexpr int kMaxDevices = 64;
+std::mutex g_err_mutex;
+int32_t* g_err_ptr[kMaxDevices] = {};
+}  // namespace
+
+// The sticky device error word (one per device; each GPU holds its own copy).
+__device__ int32_t g_device_error;
+
+pa_status fail(pa_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+void clear_error() { g_last_error.clear(); }
+
+// Device address of g_device_error on the current device (looked up once per
+// device). Returns nullptr if the lookup fails; kernels then skip flagging.
+int32_t* device_error_ptr() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_err_mutex);
+  if (!g_err_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(g_device_error)) != hipSuccess) return nullptr;
+    g_err_ptr[dev] = static_cast<int32_t*>(ptr);
+  }
+  return g_err_ptr[dev];
+}
+
+int read_and_clear_device_error(void* stream, int32_t* value) {
+  int32_t* ptr = device_error_ptr();
+  if (!ptr) return int(hipErrorInvalidSymbol);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int32_t host = 0;
+  hipError_t e = hipMemcpyAsync(&host, ptr, sizeof(host), hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return int(e);
+  const int32_t zero = 0;
+  e = hipMemcpyAsync(ptr, &zero, sizeof(zero), hipMemcpyHostToDevice, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return int(e);
+  if (value) *value = host;
+  return 0;
+}
+
+}  // namespace pa
+
+using pa::fail;
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+pa_status check_geometry(const char* fn, int32_t num_blocks, int32_t block_size, int32_t num_heads,
+                         int32_t head_dim, pa_dtype kv_dtype) {
+  if (num_blocks <= 0 || num_heads <= 0 || block_size <= 0 || head_dim <= 0)
+    return fail(PA_ERR_INVALID_ARG, "%s: sizes must be positive (blocks=%d bs=%d heads=%d dim=%d)", fn,
+                num_blocks, block_size, num_heads, head_dim);
+  if (!pa::geometry_supported(block_size, head_dim))
+    return fail(PA_ERR_UNSUPPORTED, "%s: block_size=%d head_dim=%d (supported: 16 and 64/128)", fn,
+                block_size, head_dim);
+  if (kv_dtype != PA_F32 && kv_dtype != PA_F16 && kv_dtype != PA_I8)
+    return fail(PA_ERR_UNSUPPORTED, "%s: kv dtype %d", fn, int(kv_dtype));
+  return PA_OK;
+}
+
+pa_status hip_status(const char* fn, int e) {
+  if (e == 0) return PA_OK;
+  return fail(PA_ERR_HIP, "%s: HIP error %d (%s)", fn, e, hipGetErrorString(hipError_t(e)));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_last_error(void) { return pa::g_last_error.c_str(); }
+
+int32_t pa_version(void) { return 100; }
+
+pa_status pa_pool_bytes(int32_t num_blocks, int32_t block_size, int32_t num_heads, int32_t head_dim,
+                        pa_dtype kv_dtype, int64_t* kv_bytes, int64_t* scale_bytes) {
+  if (!kv_bytes || !scale_bytes) return fail(PA_ERR_INVALID_ARG, "pa_pool_bytes: NULL output");
+  pa_status st = check_geometry("pa_pool_bytes", num_blocks, block_size, num_heads, head_dim, kv_dtype);
+  if (st != PA_OK) return st;
+  *kv_bytes = int64_t(num_blocks) * num_heads * block_size * head_dim * pa::elem_bytes(kv_dtype);
+  *scale_bytes = kv_dtype == PA_I8 ? int64_t(num_blocks) * num_heads * 2 : 0;
+  return PA_OK;
+}
+
+pa_status pa_alloc_pool(int32_t num_blocks, int32_t block_size, int32_t num_heads, int32_t head_dim,
+                        pa_dtype kv_dtype, void* k_cache, void* v_cache, void* k_scale, void* v_scale,
+                        pa_pool** out) {
+  if (!out) return fail(PA_ERR_INVALID_ARG, "pa_alloc_pool: out is NULL");
+  *out = nullptr;
+  pa_status st = check_geometry("pa_alloc_pool", num_blocks, block_size, num_heads, head_dim, kv_dtype);
+  if (st != PA_OK) return st;
+  if (!k_cache || !v_cache) return fail(PA_ERR_INVALID_ARG, "pa_alloc_pool: NULL cache buffer");
+  if (!aligned16(k_cache) || !aligned16(v_cache))
+    return fail(PA_ERR_INVALID_ARG, "pa_alloc_pool: cache buffers must be 16-byte aligned");
+  if (kv_dtype == PA_I8) {
+    if (!k_scale || !v_scale) return fail(PA_ERR_INVALID_ARG, "pa_alloc_pool: int8 pool needs scales");
+  } else if (k_scale || v_scale) {
+    return fail(PA_ERR_INVALID_ARG, "pa_alloc_pool: scales given for a float pool");
+  }
+  pa_pool* p = new (std::nothrow) pa_pool();
+  if (!p) return fail(PA_ERR_INVALID_ARG, "pa_alloc_pool: out of host memory");
+  *p = pa_pool{num_blocks, block_size, num_heads, head_dim, kv_dtype, k_cache, v_cache, k_scale, v_scale};
+  *out = p;
+  return PA_OK;
+}
+
+pa_status pa_free_pool(pa_pool* pool) {
+  delete pool;
+  return PA_OK;
+}
+
+pa_status pa_write_kv(pa_pool* pool, const void* k_new, const void* v_new, pa_dtype src_dtype,
+                      const int64_t* slot_mapping, int32_t n, pa_stream stream) {
+  if (!pool) return fail(PA_ERR_INVALID_ARG, "pa_write_kv: pool is NULL");
+  if (n < 0) return fail(PA_ERR_INVALID_ARG, "pa_write_kv: n=%d", n);
+  if (n == 0) return PA_OK;
+  if (!k_new || !v_new || !slot_mapping) return fail(PA_ERR_INVALID_ARG, "pa_write_kv: NULL buffer");
+  if (src_dtype != PA_F32 && src_dtype != PA_F16)
+    return fail(PA_ERR_UNSUPPORTED, "pa_write_kv: source dtype %d (F32 or F16)", int(src_dtype));
+  if (!aligned16(k_new) || !aligned16(v_new))
+    return fail(PA_ERR_INVALID_ARG, "pa_write_kv: new rows must be 16-byte aligned");
+  return hip_status("pa_write_kv", pa::launch_write_kv(pool, k_new, v_new, src_dtype, slot_mapping, n, stream));
+}
+
+pa_status pa_copy_blocks(pa_pool* pool, const int32_t* pairs, int32_t n, pa_stream stream) {
+  if (!pool) return fail(PA_ERR_INVALID_ARG, "pa_copy_blocks: pool is NULL");
+  if (n < 0) return fail(PA_ERR_INVALID_ARG, "pa_copy_blocks: n=%d", n);
+  if (n == 0) return PA_OK;
+  if (!pairs) return fail(PA_ERR_INVALID_ARG, "pa_copy_blocks: pairs is NULL");
+  if (n > 65535) return fail(PA_ERR_INVALID_ARG, "pa_copy_blocks: n=%d > 65535 pairs per call", n);
+  return hip_status("pa_copy_blocks", pa::launch_copy_blocks(pool, pairs, n, stream));
+}
+
+static int64_t num_partitions(int32_t max_ctx, int32_t partition_tokens) {
+  if (partition_tokens <= 0) return 1;
+  const int64_t p = (int64_t(max_ctx) + partition_tokens - 1) / partition_tokens;
+  return p < 1 ? 1 : p;
+}
+
+static int64_t workspace_bytes_for(int64_t S, int64_t H, int64_t D, int64_t P) {
+  if (P <= 1) return 0;
+  return S * H * P * (2 + D) * 4;
+}
+
+pa_status pa_decode_workspace_bytes(const pa_pool* pool, int32_t num_seqs, int32_t max_context_len,
+                                    int32_t partition_tokens, int64_t* bytes) {
+  if (!pool || !bytes) return fail(PA_ERR_INVALID_ARG, "pa_decode_workspace_bytes: NULL argument");
+  if (num_seqs < 0 || max_context_len < 0 || partition_tokens < 0 || partition_tokens % pa::kBlockSize)
+    return fail(PA_ERR_INVALID_ARG, "pa_decode_workspace_bytes: bad sizes");
+  *bytes = workspace_bytes_for(num_seqs, pool->num_heads, pool->head_dim,
+                               num_partitions(max_context_len, partition_tokens));
+  return PA_OK;
+}
+
+static pa_status decode_common(const char* fn, pa::DecodeArgs& a, void* workspace, int64_t ws_bytes,
+                               pa_stream stream) {
+  if (!a.q || !a.out || !a.ctx) return fail(PA_ERR_INVALID_ARG, "%s: NULL buffer", fn);
+  if (a.q_dtype != PA_F32 && a.q_dtype != PA_F16)
+    return fail(PA_ERR_UNSUPPORTED, "%s: q dtype %d (F32 or F16)", fn, int(a.q_dtype));
+  if (a.num_seqs < 0 || a.max_ctx < 0) return fail(PA_ERR_INVALID_ARG, "%s: negative size", fn);
+  if (a.partition_tokens < 0 || a.partition_tokens % pa::kBlockSize)
+    return fail(PA_ERR_INVALID_ARG, "%s: partition_tokens=%d (0 or a multiple of 16)", fn, a.partition_tokens);
+  if (a.q_dtype == PA_F16 && !aligned16(a.q))
+    return fail(PA_ERR_INVALID_ARG, "%s: fp16 q must be 16-byte aligned", fn);
+  if (!(a.sm_scale > 0.f) || std::isinf(a.sm_scale)) a.sm_scale = 1.0f / std::sqrt(float(a.head_dim));
+  const int64_t P = num_partitions(a.max_ctx, a.partition_tokens);
+  const int64_t grid = int64_t(a.num_seqs) * a.num_heads * P;
+  if (grid > int64_t(0x7fffffff)) return fail(PA_ERR_INVALID_ARG, "%s: grid of %lld workgroups too large", fn, (long long)grid);
+  a.num_partitions = int32_t(P);
+  a.ws_m = a.ws_l = a.ws_o = nullptr;
+  const int64_t need = workspace_bytes_for(a.num_seqs, a.num_heads, a.head_dim, P);
+  if (need > 0) {
+    if (!workspace || ws_bytes < need)
+      return fail(PA_ERR_INVALID_ARG, "%s: workspace of %lld bytes needed, %lld given", fn, (long long)need,
+                  (long long)ws_bytes);
+    if (!aligned16(workspace)) return fail(PA_ERR_INVALID_ARG, "%s: workspace must be 16-byte aligned", fn);
+    const int64_t n = int64_t(a.num_seqs) * a.num_heads * P;
+    a.ws_m = static_cast<float*>(workspace);
+    a.ws_l = a.ws_m + n;
+    a.ws_o = a.ws_l + n;
+  }
+  if (a.num_seqs == 0) return PA_OK;
+  return hip_status(fn, pa::launch_decode(a, stream));
+}
+
+pa_status pa_decode(pa_pool* pool, const void* q, pa_dtype q_dtype, void* out, const int32_t* block_tables,
+                    int32_t max_blocks, const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
+                    float sm_scale, int32_t partition_tokens, void* workspace, int64_t workspace_bytes,
+                    pa_stream stream) {
+  if (!pool) return fail(PA_ERR_INVALID_ARG, "pa_decode: pool is NULL");
+  if (!block_tables) return fail(PA_ERR_INVALID_ARG, "pa_decode: block_tables is NULL");
+  if (max_context_len < 0 || max_blocks < 0 ||
+      int64_t(max_blocks) * pa::kBlockSize < int64_t(max_context_len))
+    return fail(PA_ERR_INVALID_ARG, "pa_decode: max_blocks=%d cannot hold max_context_len=%d", max_blocks,
+                max_context_len);
+  pa::DecodeArgs a{};
+  a.q = q;
+  a.q_dtype = q_dtype;
+  a.out = out;
+  a.k = pool->k_cache;
+  a.v = pool->v_cache;
+  a.k_scale = pool->k_scale;
+  a.v_scale = pool->v_scale;
+  a.kv_dtype = pool->kv_dtype;
+  a.tables = block_tables;
+  a.max_blocks = max_blocks;
+  a.max_tokens = 0;
+  a.ctx = context_lens;
+  a.num_seqs = num_seqs;
+  a.num_heads = pool->num_heads;
+  a.head_dim = pool->head_dim;
+  a.num_blocks = pool->num_blocks;
+  a.max_ctx = max_context_len;
+  a.sm_scale = sm_scale;
+  a.partition_tokens = partition_tokens;
+  return decode_common("pa_decode", a, workspace, workspace_bytes, stream);
+}
+
+pa_status pa_decode_contiguous(const void* k, const void* v, pa_dtype kv_dtype, int32_t num_heads,
+                               int32_t head_dim, int32_t max_tokens, const void* q, pa_dtype q_dtype,
+                               void* out, const int32_t* context_lens, int32_t num_seqs, float sm_scale,
+                               int32_t partition_tokens, void* workspace, int64_t workspace_bytes,
+                               pa_stream stream) {
+  if (!k || !v) return fail(PA_ERR_INVALID_ARG, "pa_decode_contiguous: NULL cache");
+  if (kv_dtype != PA_F32 && kv_dtype != PA_F16)
+    return fail(PA_ERR_UNSUPPORTED, "pa_decode_contiguous: float KV only");
+  if (num_heads <= 0 || max_tokens < 0 || max_tokens % pa::kBlockSize)
+    return fail(PA_ERR_INVALID_ARG, "pa_decode_contiguous: heads=%d max_tokens=%d (a multiple of 16)",
+                num_heads, max_tokens);
+  if (head_dim != 64 && head_dim != 128) return fail(PA_ERR_UNSUPPORTED, "pa_decode_contiguous: head_dim %d", head_dim);
+  if (!aligned16(k) || !aligned16(v)) return fail(PA_ERR_INVALID_ARG, "pa_decode_contiguous: unaligned cache");
+  pa::DecodeArgs a{};
+  a.q = q;
+  a.q_dtype = q_dtype;
+  a.out = out;
+  a.k = k;
+  a.v = v;
+  a.kv_dtype = kv_dtype;
+  a.tables = nullptr;
+  a.max_tokens = max_tokens;
+  a.ctx = context_lens;
+  a.num_seqs = num_seqs;
+  a.num_heads = num_heads;
+  a.head_dim = head_dim;
+  a.num_blocks = 0;
+  a.max_ctx = max_tokens;
+  a.sm_scale = sm_scale;
+  a.partition_tokens = partition_tokens;
+  return decode_common("pa_decode_contiguous", a, workspace, workspace_bytes, stream);
+}
+
+pa_status pa_check_errors(pa_stream stream, int32_t* device_error) {
+  return hip_status("pa_check_errors", pa::read_and_clear_device_error(stream, device_error));
+}
+
+pa_status pa_stream_copy(void* dst, const void* src, int64_t bytes, pa_stream stream) {
+  if (!dst || !src || bytes < 0 || bytes % 16 || !aligned16(dst) || !aligned16(src))
+    return fail(PA_ERR_INVALID_ARG, "pa_stream_copy: bad arguments");
+  return hip_status("pa_stream_copy", pa::launch_stream_copy(dst, src, bytes, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,327 @@
+// Host block manager of the paged KV cache (no device memory).
+//
+// Policy (the pages fix the mechanism, this file fixes the details):
+//  * On-demand allocation from one shared free list; any free block serves
+//    ("KV Cache与长上下文管理", the section on fragmentation). The free list is a
+//    FIFO initialised in the caller's order; a block whose count reaches zero
+//    returns to the tail.
+//  * Per-block reference counts and copy-on-write on append ("PagedAttention —
+//    把 KV cache 当虚拟内存页来管理", 核心要点 and 实践案例 / 案例 3): an append at
+//    offset > 0 into a last block shared by others takes a fresh block, drops
+//    the shared count by one and reports the (src, dst) pair to copy first.
+//  * Sliding-window ring ("KV Cache与长上下文管理", the section on the second
+//    problem paging solves; "PagedAttention的终极用途", part 三): with a window of
+//    W blocks, opening block W+1 invalidates the oldest live block and reuses
+//    its physical id for the new one; only the table row changes (front
+//    dropped, id appended). An oldest block still shared by another sequence
+//    cannot be overwritten: its count drops and a fresh block is taken.
+//  * Every call is atomic; batched appends roll back through an undo log.
+#include <algorithm>
+#include <deque>
+#include <new>
+#include <unordered_map>
+#include <vector>
+
+#include "pa_internal.h"
+
+namespace {
+
+struct Seq {
+  std::deque<int32_t> table;  // live physical blocks in logical order
+  int64_t tokens = 0;         // tokens appended in total
+  int64_t evicted = 0;        // blocks dropped by the ring
+};
+
+enum class Kind : int8_t { kInPlace, kFresh, kRingReuse, kRingFresh, kCow };
+
+struct Undo {
+  int64_t seq;
+  Kind kind;
+  int32_t a;  // old / src block
+  int32_t b;  // new / dst block
+};
+
+}  // namespace
+
+struct pa_bm {
+  int32_t num_blocks;
+  int32_t block_size;
+  int32_t window;
+  std::deque<int32_t> free_list;
+  std::vector<int32_t> ref;
+  std::unordered_map<int64_t, Seq> seqs;
+
+  int64_t live_tokens(const Seq& s) const { return s.tokens - int64_t(block_size) * s.evicted; }
+
+  int32_t take_free() {
+    int32_t b = free_list.front();
+    free_list.pop_front();
+    ref[b] = 1;
+    return b;
+  }
+
+  void give_back(int32_t b) {  // exact inverse of take_free
+    ref[b] = 0;
+    free_list.push_front(b);
+  }
+
+  // One append; fills *u with what undoes it.
+  pa_status append(int64_t id, int64_t* slot, int32_t* src, int32_t* dst, Undo* u) {
+    auto it = seqs.find(id);
+    if (it == seqs.end()) return pa::fail(PA_ERR_STATE, "pa_bm_append: unknown sequence %lld", (long long)id);
+    Seq& s = it->second;
+    const int32_t offset = int32_t(s.tokens % block_size);
+    *src = -1;
+    *dst = -1;
+    u->seq = id;
+    if (offset == 0) {
+      if (window > 0 && int32_t(s.table.size()) == window) {
+        const int32_t oldest = s.table.front();
+        if (ref[oldest] == 1) {
+          s.table.pop_front();
+          s.table.push_back(oldest);  // reused in place: no KV data moves
+          *u = Undo{id, Kind::kRingReuse, oldest, -1};
+        } else {
+          if (free_list.empty())
+            return pa::fail(PA_ERR_OUT_OF_BLOCKS, "pa_bm_append: no free block (ring, shared oldest)");
+          s.table.pop_front();
+          ref[oldest] -= 1;
+          const int32_t b = take_free();
+          s.table.push_back(b);
+          *u = Undo{id, Kind::kRingFresh, oldest, b};
+        }
+        s.evicted += 1;
+      } else {
+        if (free_list.empty()) return pa::fail(PA_ERR_OUT_OF_BLOCKS, "pa_bm_append: no free block");
+        const int32_t b = take_free();
+        s.table.push_back(b);
+        *u = Undo{id, Kind::kFresh, -1, b};
+      }
+    } else {
+      const int32_t last = s.table.back();
+      if (ref[last] > 1) {
+        if (free_list.empty())
+          return pa::fail(PA_ERR_OUT_OF_BLOCKS, "pa_bm_append: no free block for copy-on-write");
+        const int32_t b = take_free();
+        ref[last] -= 1;
+        s.table.back() = b;
+        *src = last;
+        *dst = b;
+        *u = Undo{id, Kind::kCow, last, b};
+      } else {
+        *u = Undo{id, Kind::kInPlace, -1, -1};
+      }
+    }
+    s.tokens += 1;
+    *slot = int64_t(s.table.back()) * block_size + offset;
+    return PA_OK;
+  }
+
+  void undo(const Undo& u) {
+    Seq& s = seqs.at(u.seq);
+    s.tokens -= 1;
+    switch (u.kind) {
+      case Kind::kInPlace:
+        break;
+      case Kind::kFresh:
+        s.table.pop_back();
+        give_back(u.b);
+        break;
+      case Kind::kRingReuse:
+        s.table.pop_back();
+        s.table.push_front(u.a);
+        s.evicted -= 1;
+        break;
+      case Kind::kRingFresh:
+        s.table.pop_back();
+        give_back(u.b);
+        ref[u.a] += 1;
+        s.table.push_front(u.a);
+        s.evicted -= 1;
+        break;
+      case Kind::kCow:
+        give_back(u.b);
+        ref[u.a] += 1;
+        s.table.back() = u.a;
+        break;
+    }
+  }
+};
+
+extern "C" {
+
+pa_status pa_bm_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order,
+                       int32_t window_blocks, pa_bm** out) {
+  if (!out) return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_create: out is NULL");
+  *out = nullptr;
+  if (num_blocks <= 0 || block_size <= 0 || window_blocks < 0)
+    return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_create: num_blocks=%d block_size=%d window=%d",
+                    num_blocks, block_size, window_blocks);
+  if (block_size != pa::kBlockSize)
+    return pa::fail(PA_ERR_UNSUPPORTED, "pa_bm_create: block_size %d (only 16)", block_size);
+  pa_bm* bm = new (std::nothrow) pa_bm();
+  if (!bm) return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_create: out of host memory");
+  bm->num_blocks = num_blocks;
+  bm->block_size = block_size;
+  bm->window = window_blocks;
+  bm->ref.assign(num_blocks, 0);
+  if (free_order) {
+    std::vector<char> seen(num_blocks, 0);
+    for (int32_t i = 0; i < num_blocks; ++i) {
+      const int32_t b = free_order[i];
+      if (b < 0 || b >= num_blocks || seen[b]) {
+        delete bm;
+        return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_create: free_order is not a permutation (entry %d)", i);
+      }
+      seen[b] = 1;
+      bm->free_list.push_back(b);
+    }
+  } else {
+    for (int32_t b = 0; b < num_blocks; ++b) bm->free_list.push_back(b);
+  }
+  *out = bm;
+  pa::clear_error();
+  return PA_OK;
+}
+
+pa_status pa_bm_destroy(pa_bm* bm) {
+  delete bm;
+  return PA_OK;
+}
+
+pa_status pa_bm_add_seq(pa_bm* bm, int64_t seq, int32_t prefill_tokens, int64_t* slots_out) {
+  if (!bm) return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_add_seq: bm is NULL");
+  if (bm->seqs.count(seq)) return pa::fail(PA_ERR_STATE, "pa_bm_add_seq: sequence %lld exists", (long long)seq);
+  if (prefill_tokens < 0) return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_add_seq: negative prefill");
+  if (prefill_tokens > 0 && !slots_out) return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_add_seq: slots_out is NULL");
+  const int32_t nb = (prefill_tokens + bm->block_size - 1) / bm->block_size;
+  if (bm->window > 0 && nb > bm->window)
+    return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_add_seq: prefill needs %d blocks, window is %d", nb, bm->window);
+  if (size_t(nb) > bm->free_list.size())
+    return pa::fail(PA_ERR_OUT_OF_BLOCKS, "pa_bm_add_seq: needs %d blocks, %zu free", nb, bm->free_list.size());
+  Seq s;
+  for (int32_t i = 0; i < nb; ++i) s.table.push_back(bm->take_free());
+  s.tokens = prefill_tokens;
+  for (int32_t t = 0; t < prefill_tokens; ++t)
+    slots_out[t] = int64_t(s.table[t / bm->block_size]) * bm->block_size + t % bm->block_size;
+  bm->seqs.emplace(seq, std::move(s));
+  return PA_OK;
+}
+
+pa_status pa_bm_fork(pa_bm* bm, int64_t parent, int64_t child) {
+  if (!bm) return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_fork: bm is NULL");
+  auto it = bm->seqs.find(parent);
+  if (it == bm->seqs.end()) return pa::fail(PA_ERR_STATE, "pa_bm_fork: unknown parent %lld", (long long)parent);
+  if (bm->seqs.count(child)) return pa::fail(PA_ERR_STATE, "pa_bm_fork: child %lld exists", (long long)child);
+  Seq c = it->second;
+  for (int32_t b : c.table) bm->ref[b] += 1;
+  bm->seqs.emplace(child, std::move(c));
+  return PA_OK;
+}
+
+pa_status pa_bm_append(pa_bm* bm, int64_t seq, int64_t* slot_out, int32_t* copy_src, int32_t* copy_dst) {
+  if (!bm || !slot_out || !copy_src || !copy_dst) return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_append: NULL argument");
+  Undo u;
+  return bm->append(seq, slot_out, copy_src, copy_dst, &u);
+}
+
+pa_status pa_bm_append_batch(pa_bm* bm, const int64_t* seqs, int32_t n, int64_t* slots_out,
+                             int32_t* pairs_out, int32_t* n_pairs) {
+  if (!bm || n < 0 || (n > 0 && (!seqs || !slots_out || !pairs_out)) || !n_pairs)
+    return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_append_batch: bad arguments");
+  std::vector<Undo> log;
+  log.reserve(n);
+  int32_t np = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    int32_t src, dst;
+    Undo u;
+    const pa_status st = bm->append(seqs[i], &slots_out[i], &src, &dst, &u);
+    if (st != PA_OK) {
+      for (auto r = log.rbegin(); r != log.rend(); ++r) bm->undo(*r);
+      return st;
+    }
+    log.push_back(u);
+    if (src >= 0) {
+      pairs_out[2 * np] = src;
+      pairs_out[2 * np + 1] = dst;
+      ++np;
+    }
+  }
+  *n_pairs = np;
+  return PA_OK;
+}
+
+pa_status pa_bm_free_seq(pa_bm* bm, int64_t seq) {
+  if (!bm) return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_free_seq: bm is NULL");
+  auto it = bm->seqs.find(seq);
+  if (it == bm->seqs.end()) return pa::fail(PA_ERR_STATE, "pa_bm_free_seq: unknown sequence %lld", (long long)seq);
+  for (int32_t b : it->second.table) {
+    bm->ref[b] -= 1;
+    if (bm->ref[b] == 0) bm->free_list.push_back(b);
+  }
+  bm->seqs.erase(it);
+  return PA_OK;
+}
+
+pa_status pa_bm_table(const pa_bm* bm, int64_t seq, int32_t* row, int32_t cap, int32_t* n_blocks,
+                      int32_t* ctx_len) {
+  if (!bm) return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_table: bm is NULL");
+  auto it = bm->seqs.find(seq);
+  if (it == bm->seqs.end()) return pa::fail(PA_ERR_STATE, "pa_bm_table: unknown sequence %lld", (long long)seq);
+  const Seq& s = it->second;
+  const int32_t nb = int32_t(s.table.size());
+  if (n_blocks) *n_blocks = nb;
+  if (ctx_len) *ctx_len = int32_t(bm->live_tokens(s));
+  if (row) {
+    if (cap < nb) return pa::fail(PA_ERR_OUT_OF_RANGE, "pa_bm_table: cap %d < %d blocks", cap, nb);
+    std::copy(s.table.begin(), s.table.end(), row);
+    std::fill(row + nb, row + cap, -1);
+  }
+  return PA_OK;
+}
+
+pa_status pa_bm_export(const pa_bm* bm, const int64_t* seqs, int32_t n, int32_t* tables, int32_t cap,
+                       int32_t* ctx_out) {
+  if (!bm || n < 0 || cap < 0 || (n > 0 && (!seqs || !tables || !ctx_out)))
+    return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_export: bad arguments");
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = bm->seqs.find(seqs[i]);
+    if (it == bm->seqs.end())
+      return pa::fail(PA_ERR_STATE, "pa_bm_export: unknown sequence %lld", (long long)seqs[i]);
+    if (int32_t(it->second.table.size()) > cap)
+      return pa::fail(PA_ERR_OUT_OF_RANGE, "pa_bm_export: sequence %lld holds %zu blocks > cap %d",
+                      (long long)seqs[i], it->second.table.size(), cap);
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    const Seq& s = bm->seqs.find(seqs[i])->second;
+    int32_t* row = tables + int64_t(i) * cap;
+    std::copy(s.table.begin(), s.table.end(), row);
+    std::fill(row + s.table.size(), row + cap, -1);
+    ctx_out[i] = int32_t(bm->live_tokens(s));
+  }
+  return PA_OK;
+}
+
+pa_status pa_bm_ref_count(const pa_bm* bm, int32_t block, int32_t* out) {
+  if (!bm || !out) return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_ref_count: NULL argument");
+  if (block < 0 || block >= bm->num_blocks)
+    return pa::fail(PA_ERR_OUT_OF_RANGE, "pa_bm_ref_count: block %d outside [0, %d)", block, bm->num_blocks);
+  *out = bm->ref[block];
+  return PA_OK;
+}
+
+pa_status pa_bm_num_free(const pa_bm* bm, int32_t* out) {
+  if (!bm || !out) return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_num_free: NULL argument");
+  *out = int32_t(bm->free_list.size());
+  return PA_OK;
+}
+
+pa_status pa_bm_free_list(const pa_bm* bm, int32_t* out, int32_t cap, int32_t* n) {
+  if (!bm || !n || (cap > 0 && !out)) return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_free_list: NULL argument");
+  *n = int32_t(bm->free_list.size());
+  if (cap < *n) return pa::fail(PA_ERR_OUT_OF_RANGE, "pa_bm_free_list: cap %d < %d", cap, *n);
+  std::copy(bm->free_list.begin(), bm->free_list.end(), out);
+  return PA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,276 @@
+// Cache-side kernels for gfx950: writing new K/V rows into their slots,
+// copy-on-write block copies, and a plain streaming copy.
+//
+// write_kv (reshape-and-cache): row i of the new K/V goes to slot
+// slots[i] = block * 16 + offset, the lookup of "PagedAttention — 把 KV cache
+// 当虚拟内存页来管理", 实践案例 / 案例 2. Writing new tokens into pages is also the
+// only data movement of the sliding window ("KV Cache与长上下文管理", the section
+// on the second problem paging solves: the new token is written into the page
+// the oldest data occupied).
+//
+// int8 pools quantise on write with one fp16 scale per (block, head), for K
+// and V separately (FP16 -> INT8 compression is listed in "KV Cache与长上下文管理",
+// section 二.3, without a scheme; the group rule below is this library's and
+// is stated in pagedkv.h). One wave handles one run of adjacent slot entries
+// that hit the same block (at most 16 rows), for one head and one tensor.
+//
+// copy_blocks: whole-block copies, the copy-on-write unit of the study note's
+// 实践案例 / 案例 3.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <type_traits>
+
+#include "device_common.h"
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+constexpr int kThreads = 256;
+
+template <typename T>
+__device__ __forceinline__ float ld_f(const T* p) {
+  return float(*p);
+}
+
+// ---------------------------------------------------------------------------
+// Float pools: one thread per 16 destination bytes.
+template <typename DST, typename SRC, int D>
+__global__ __launch_bounds__(kThreads) void write_kv_kernel(const SRC* __restrict__ k_new,
+                                                            const SRC* __restrict__ v_new,
+                                                            DST* __restrict__ k_pool,
+                                                            DST* __restrict__ v_pool,
+                                                            const int64_t* __restrict__ slots, int n,
+                                                            int H, int num_blocks, int32_t* err) {
+  constexpr int kEPT = 16 / int(sizeof(DST));   // elements per thread
+  constexpr int kCPR = D / kEPT;                // threads per (row, head)
+  const int64_t idx = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+  const int64_t total = int64_t(n) * H * kCPR;
+  if (idx >= total) return;
+  const int64_t row = idx / kCPR;   // (i, h)
+  const int chunk = int(idx % kCPR);
+  const int64_t i = row / H;
+  const int h = int(row % H);
+  const int64_t slot = slots[i];
+  if (slot < 0) return;
+  const int64_t blk = slot / kBlockSize;
+  const int off = int(slot % kBlockSize);
+  if (blk >= num_blocks) {
+    flag_error(err, PA_DEV_BAD_SLOT);
+    return;
+  }
+  const SRC* src = (blockIdx.y == 0 ? k_new : v_new) + row * D + chunk * kEPT;
+  DST* dst = (blockIdx.y == 0 ? k_pool : v_pool) + ((blk * H + h) * kBlockSize + off) * D + chunk * kEPT;
+  DST vals[kEPT];
+#pragma unroll
+  for (int e = 0; e < kEPT; ++e) vals[e] = DST(ld_f(src + e));
+  *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(vals);
+}
+
+// ---------------------------------------------------------------------------
+// int8 pools: one wave per (run leader i, head h, tensor).
+template <typename SRC, int D>
+__global__ __launch_bounds__(kThreads) void write_kv_i8_kernel(
+    const SRC* __restrict__ k_new, const SRC* __restrict__ v_new, int8_t* __restrict__ k_pool,
+    int8_t* __restrict__ v_pool, _Float16* __restrict__ k_scale, _Float16* __restrict__ v_scale,
+    const int64_t* __restrict__ slots, int n, int H, int num_blocks, int32_t* err) {
+  constexpr int kDPL = D / kWave;   // dims per lane
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t wid = int64_t(blockIdx.x) * (kThreads / kWave) + wave_uniform(threadIdx.x / kWave);
+  if (wid >= int64_t(n) * H) return;
+  const int64_t i = wid / H;
+  const int h = int(wid % H);
+  const int64_t slot = slots[i];
+  if (slot < 0) return;
+  const int64_t blk = slot / kBlockSize;
+  if (blk >= num_blocks) {
+    if (lane == 0) flag_error(err, PA_DEV_BAD_SLOT);
+    return;
+  }
+  if (i > 0) {
+    const int64_t prev = slots[i - 1];
+    if (prev >= 0 && prev / kBlockSize == blk) return;   // not the first row of its run
+  }
+  const bool is_v = blockIdx.y != 0;
+  const SRC* src = is_v ? v_new : k_new;
+  int8_t* pool = is_v ? v_pool : k_pool;
+  _Float16* scale = is_v ? v_scale : k_scale;
+
+  // The run: rows i .. i+R-1 hitting block blk.
+  uint32_t mask = 0;
+  int R = 0;
+  bool dup = false;
+  while (R < kBlockSize && i + R < n) {
+    const int64_t sl = slots[i + R];
+    if (sl < 0 || sl / kBlockSize != blk) break;
+    const uint32_t bit = 1u << int(sl % kBlockSize);
+    dup |= (mask & bit) != 0;
+    mask |= bit;
+    ++R;
+  }
+  if (i + R < n && R == kBlockSize) {
+    const int64_t sl = slots[i + R];
+    dup |= sl >= 0 && sl / kBlockSize == blk;
+  }
+  if (dup && lane == 0) flag_error(err, PA_DEV_BAD_RUN);
+
+  float a = 0.f;
+  for (int r = 0; r < R; ++r) {
+    const SRC* x = src + ((i + r) * H + h) * D + lane * kDPL;
+#pragma unroll
+    for (int e = 0; e < kDPL; ++e) a = fmaxf(a, fabsf(ld_f(x + e)));
+  }
+  a = wave_max(a);
+  const float s_new = float(_Float16(a / 127.0f));
+  const int64_t sidx = blk * H + h;
+  const float s_old = (mask & 1u) ? 0.f : float(scale[sidx]);
+  const float s = fmaxf(s_old, s_new);
+  int8_t* tile = pool + sidx * kBlockSize * D;
+
+  if (s_old > 0.f && s > s_old) {
+    for (int o = 0; o < kBlockSize; ++o) {
+      if (mask & (1u << o)) continue;
+#pragma unroll
+      for (int e = 0; e < kDPL; ++e) {
+        int8_t* c = tile + o * D + lane * kDPL + e;
+        const float qf = __builtin_rintf((float(*c) * s_old) / s);
+        *c = int8_t(fminf(fmaxf(qf, -127.f), 127.f));
+      }
+    }
+  }
+  for (int r = 0; r < R; ++r) {
+    const int o = int(slots[i + r] % kBlockSize);
+    const SRC* x = src + ((i + r) * H + h) * D + lane * kDPL;
+#pragma unroll
+    for (int e = 0; e < kDPL; ++e) {
+      float qf = 0.f;
+      if (s > 0.f) qf = fminf(fmaxf(__builtin_rintf(ld_f(x + e) / s), -127.f), 127.f);
+      tile[o * D + lane * kDPL + e] = int8_t(qf);
+    }
+  }
+  if (lane == 0) scale[sidx] = _Float16(s);
+}
+
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void copy_blocks_kernel(const int32_t* __restrict__ pairs, int n,
+                                                               char* __restrict__ k, char* __restrict__ v,
+                                                               int64_t block_bytes, _Float16* ks,
+                                                               _Float16* vs, int H, int num_blocks,
+                                                               int32_t* err) {
+  const int pair = blockIdx.y;
+  const int src = pairs[2 * pair];
+  const int dst = pairs[2 * pair + 1];
+  if (unsigned(src) >= unsigned(num_blocks) || unsigned(dst) >= unsigned(num_blocks)) {
+    if (blockIdx.x == 0 && blockIdx.z == 0 && threadIdx.x == 0) flag_error(err, PA_DEV_BAD_PAIR);
+    return;
+  }
+  char* base = blockIdx.z == 0 ? k : v;
+  const int64_t off = (int64_t(blockIdx.x) * kThreads + threadIdx.x) * 16;
+  if (off < block_bytes) {
+    const uint4 val = *reinterpret_cast<const uint4*>(base + int64_t(src) * block_bytes + off);
+    *reinterpret_cast<uint4*>(base + int64_t(dst) * block_bytes + off) = val;
+  }
+  if (ks && blockIdx.x == 0) {
+    _Float16* sc = blockIdx.z == 0 ? ks : vs;
+    for (int hh = threadIdx.x; hh < H; hh += kThreads) sc[int64_t(dst) * H + hh] = sc[int64_t(src) * H + hh];
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void stream_copy_kernel(uint4* __restrict__ dst,
+                                                               const uint4* __restrict__ src,
+                                                               int64_t n16) {
+  constexpr int kUnroll = 4;
+  const int64_t stride = int64_t(gridDim.x) * kThreads;
+  int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+  for (; i + (kUnroll - 1) * stride < n16; i += kUnroll * stride) {
+    uint4 r[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) r[u] = src[i + u * stride];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) dst[i + u * stride] = r[u];
+  }
+  for (; i < n16; i += stride) dst[i] = src[i];
+}
+
+template <typename DST, typename SRC>
+int launch_write_float(const pa_pool* p, const void* k_new, const void* v_new, const int64_t* slots,
+                       int32_t n, hipStream_t st) {
+  const int cpr = p->head_dim / (16 / int(sizeof(DST)));
+  const int64_t total = int64_t(n) * p->num_heads * cpr;
+  const dim3 grid(unsigned((total + kThreads - 1) / kThreads), 2);
+  if (p->head_dim == 64)
+    hipLaunchKernelGGL((write_kv_kernel<DST, SRC, 64>), grid, dim3(kThreads), 0, st,
+                       static_cast<const SRC*>(k_new), static_cast<const SRC*>(v_new),
+                       static_cast<DST*>(p->k_cache), static_cast<DST*>(p->v_cache), slots, n,
+                       p->num_heads, p->num_blocks, device_error_ptr());
+  else
+    hipLaunchKernelGGL((write_kv_kernel<DST, SRC, 128>), grid, dim3(kThreads), 0, st,
+                       static_cast<const SRC*>(k_new), static_cast<const SRC*>(v_new),
+                       static_cast<DST*>(p->k_cache), static_cast<DST*>(p->v_cache), slots, n,
+                       p->num_heads, p->num_blocks, device_error_ptr());
+  return int(hipGetLastError());
+}
+
+template <typename SRC>
+int launch_write_i8(const pa_pool* p, const void* k_new, const void* v_new, const int64_t* slots,
+                    int32_t n, hipStream_t st) {
+  const int64_t waves = int64_t(n) * p->num_heads;
+  const dim3 grid(unsigned((waves + (kThreads / kWave) - 1) / (kThreads / kWave)), 2);
+  auto args = [&](auto kern) {
+    hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, st, static_cast<const SRC*>(k_new),
+                       static_cast<const SRC*>(v_new), static_cast<int8_t*>(p->k_cache),
+                       static_cast<int8_t*>(p->v_cache), static_cast<_Float16*>(p->k_scale),
+                       static_cast<_Float16*>(p->v_scale), slots, n, p->num_heads, p->num_blocks,
+                       device_error_ptr());
+  };
+  if (p->head_dim == 64)
+    args(write_kv_i8_kernel<SRC, 64>);
+  else
+    args(write_kv_i8_kernel<SRC, 128>);
+  return int(hipGetLastError());
+}
+
+}  // namespace
+
+int launch_write_kv(const pa_pool* p, const void* k_new, const void* v_new, pa_dtype src,
+                    const int64_t* slots, int32_t n, void* stream) {
+  if (n == 0) return 0;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  switch (p->kv_dtype) {
+    case PA_F32:
+      return src == PA_F32 ? launch_write_float<float, float>(p, k_new, v_new, slots, n, st)
+                           : launch_write_float<float, _Float16>(p, k_new, v_new, slots, n, st);
+    case PA_F16:
+      return src == PA_F32 ? launch_write_float<_Float16, float>(p, k_new, v_new, slots, n, st)
+                           : launch_write_float<_Float16, _Float16>(p, k_new, v_new, slots, n, st);
+    case PA_I8:
+      return src == PA_F32 ? launch_write_i8<float>(p, k_new, v_new, slots, n, st)
+                           : launch_write_i8<_Float16>(p, k_new, v_new, slots, n, st);
+  }
+  return int(hipErrorInvalidValue);
+}
+
+int launch_copy_blocks(const pa_pool* p, const int32_t* pairs, int32_t n, void* stream) {
+  if (n == 0) return 0;
+  const int64_t block_bytes = int64_t(p->num_heads) * kBlockSize * p->head_dim * elem_bytes(p->kv_dtype);
+  const dim3 grid(unsigned((block_bytes / 16 + kThreads - 1) / kThreads), unsigned(n), 2);
+  hipLaunchKernelGGL(copy_blocks_kernel, grid, dim3(kThreads), 0, static_cast<hipStream_t>(stream), pairs,
+                     n, static_cast<char*>(p->k_cache), static_cast<char*>(p->v_cache), block_bytes,
+                     static_cast<_Float16*>(p->k_scale), static_cast<_Float16*>(p->v_scale),
+                     p->num_heads, p->num_blocks, device_error_ptr());
+  return int(hipGetLastError());
+}
+
+int launch_stream_copy(void* dst, const void* src, int64_t bytes, void* stream) {
+  const int64_t n16 = bytes / 16;
+  if (n16 == 0) return 0;
+  int64_t blocks = (n16 + kThreads - 1) / kThreads;
+  if (blocks > 256 * 64) blocks = 256 * 64;
+  hipLaunchKernelGGL(stream_copy_kernel, dim3(unsigned(blocks)), dim3(kThreads), 0,
+                     static_cast<hipStream_t>(stream), static_cast<uint4*>(dst),
+                     static_cast<const uint4*>(src), n16);
+  return int(hipGetLastError());
+}
+
+}  // namespace pa

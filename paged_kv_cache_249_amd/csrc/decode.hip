@@ -1,0 +1,465 @@
+// Paged decode attention for gfx950.
+//
+// Computes, for every sequence s and head h, softmax(q . k_t * scale) v over
+// the sequence's first ctx[s] tokens ("One Deep Concept #01 — PagedAttention:
+// From Operating System Virtual Memory to Large Language Model Memory
+// Systems", §2 Background), where token t lives in physical block
+// table[s][t / 16] at offset t % 16 ("PagedAttention — 把 KV cache 当虚拟内存页来
+// 管理", 实践案例 / 案例 2). Decode reads a lot and computes little (same note,
+// 学到什么), so the kernel is built around HBM streaming, not matrix cores.
+//
+// Work decomposition. One workgroup (4 waves) per (sequence, head, partition).
+// A partition is a run of whole 16-token blocks; in single-pass mode it covers
+// the whole context. Inside the workgroup each wave owns whole blocks (block
+// j of the partition goes to wave j % 4) and keeps its own online-softmax
+// state, so the hot loop has no barriers.
+//
+// Tile mapping. One (block, head) tile is 16 rows of head_dim elements,
+// contiguous in the pool. A wave reads it with NLD 16-byte loads per lane;
+// load i of lane l covers bytes [i*1024 + 16*l, +16) of the tile, so every
+// load instruction moves 1 KiB contiguous. In bytes-per-row terms, the 16
+// rows split into groups of TPI = 64 / CPT rows per load, CPT lanes per row
+// (CPT = row bytes / 16). Lane l therefore always sees the same CPT-th slice
+// of head_dim (its "column", l % CPT) of rows i*TPI + l / CPT.
+//
+// Per block, per lane: the partial dot of its slice with q for each of its NLD
+// rows, summed over the CPT lanes of the row with DPP row operations (no LDS);
+// then an fp32 online-softmax update on the lane's own rows in base 2
+// (logits pre-multiplied by log2 e), and acc[e] += p * v for its slice. Lanes
+// of different row groups are independent softmax streams until the epilogue,
+// which merges all (wave, row-group) streams of the workgroup through LDS with
+// the log-sum-exp identity.
+//
+// Masking: only the last block of a sequence can be partial. Rows at t >= ctx
+// get logit -inf and their raw K/V registers are zeroed before use, so stale
+// or NaN data in unused slots never reaches the result. A table entry outside
+// the pool flags the device error word and its block is treated as empty.
+//
+// Split-K. A partition writes m (largest logit, natural units), l (sum of
+// exp(logit - m)) and o (its normalised output, fp32) into the workspace; the
+// reduce kernel merges partitions as out = sum w_p o_p / sum w_p with
+// w_p = exp(m_p - M) l_p. Sequences with one partition are written directly.
+//
+// XCD-aware order: work item w enumerates (partition, head, sequence) with the
+// sequence fastest. Workgroup ids are dealt to the 8 XCDs round-robin; groups
+// of 4 consecutive work items are steered onto one XCD, so the 4 sequences
+// next to each other in the batch (e.g. samples sharing a prompt's blocks)
+// read those blocks through the same L2 at about the same time, while the
+// deal stays interleaved at that granularity for load balance.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <type_traits>
+
+#include "device_common.h"
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * kWave;
+constexpr int kXcds = 8;
+constexpr int kXcdGroup = 4;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegBig = -1.0e30f;   // finite "no logit yet" so exp2(m - m_new) stays defined
+
+template <typename KV, int D>
+struct Geo {
+  static constexpr int kRowBytes = D * int(sizeof(KV));
+  static constexpr int kCPT = kRowBytes / 16;      // lanes per row
+  static constexpr int kTPI = kWave / kCPT;        // rows per wave-wide load
+  static constexpr int kNLD = kBlockSize / kTPI;   // loads per lane per tile
+  static constexpr int kEPC = 16 / int(sizeof(KV));  // elements per lane per row
+  static constexpr int kTileBytes = kBlockSize * kRowBytes;
+  static_assert(kCPT >= 4 && kCPT <= 32, "unsupported row size");
+};
+
+struct Params {
+  const void* q;
+  void* out;
+  const char* k;
+  const char* v;
+  const _Float16* k_scale;
+  const _Float16* v_scale;
+  const int32_t* tables;
+  int64_t max_tokens;       // contiguous layout row length
+  const int32_t* ctx;
+  int32_t max_blocks;
+  int32_t num_seqs;
+  int32_t num_heads;
+  int32_t num_blocks;
+  int32_t max_ctx;
+  int32_t partition_blocks;
+  int32_t num_partitions;
+  float scale_log2;
+  float* ws_m;
+  float* ws_l;
+  float* ws_o;
+  int32_t* err;
+};
+
+// Bijection from dispatch order g to work item w: inside every chunk of
+// kXcds * kXcdGroup ids, the ids that land on XCD x (g % kXcds == x) take the
+// kXcdGroup consecutive work items x*kXcdGroup ... ; a ragged tail maps to itself.
+__device__ __forceinline__ int xcd_remap(int g, int total) {
+  constexpr int kChunk = kXcds * kXcdGroup;
+  const int full = (total / kChunk) * kChunk;
+  if (g >= full) return g;
+  const int base = g - g % kChunk;
+  const int r = g % kChunk;
+  return base + (r % kXcds) * kXcdGroup + r / kXcds;
+}
+
+// q slice of one lane, in the form its dot product wants.
+template <typename KV, typename QT, int EPC>
+struct QSlice {
+  float f[EPC];
+  __device__ void load(const QT* src) {
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) f[e] = float(src[e]);
+  }
+};
+
+template <>
+struct QSlice<_Float16, _Float16, 8> {
+  uint32_t w[4];
+  __device__ void load(const _Float16* src) {
+    const uint4 r = *reinterpret_cast<const uint4*>(src);
+    w[0] = r.x; w[1] = r.y; w[2] = r.z; w[3] = r.w;
+  }
+};
+
+template <typename KV, typename QT, int EPC>
+__device__ __forceinline__ float dot16(const uint4& r, const QSlice<KV, QT, EPC>& q) {
+  const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+  float s = 0.f;
+  if constexpr (std::is_same<KV, float>::value) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s = fmaf(__builtin_bit_cast(float, w[j]), q.f[j], s);
+  } else if constexpr (std::is_same<KV, _Float16>::value) {
+    if constexpr (std::is_same<QT, _Float16>::value) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) s = __builtin_amdgcn_fdot2(as_h2(w[j]), as_h2(q.w[j]), s, false);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        s = fmaf(lo_f16(w[j]), q.f[2 * j], s);
+        s = fmaf(hi_f16(w[j]), q.f[2 * j + 1], s);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      s = fmaf(i8_at<0>(w[j]), q.f[4 * j + 0], s);
+      s = fmaf(i8_at<1>(w[j]), q.f[4 * j + 1], s);
+      s = fmaf(i8_at<2>(w[j]), q.f[4 * j + 2], s);
+      s = fmaf(i8_at<3>(w[j]), q.f[4 * j + 3], s);
+    }
+  }
+  return s;
+}
+
+template <typename KV, int EPC>
+__device__ __forceinline__ void axpy16(float p, const uint4& r, float (&acc)[EPC]) {
+  const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+  if constexpr (std::is_same<KV, float>::value) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[j] = fmaf(p, __builtin_bit_cast(float, w[j]), acc[j]);
+  } else if constexpr (std::is_same<KV, _Float16>::value) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      acc[2 * j] = fmaf(p, lo_f16(w[j]), acc[2 * j]);
+      acc[2 * j + 1] = fmaf(p, hi_f16(w[j]), acc[2 * j + 1]);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      acc[4 * j + 0] = fmaf(p, i8_at<0>(w[j]), acc[4 * j + 0]);
+      acc[4 * j + 1] = fmaf(p, i8_at<1>(w[j]), acc[4 * j + 1]);
+      acc[4 * j + 2] = fmaf(p, i8_at<2>(w[j]), acc[4 * j + 2]);
+      acc[4 * j + 3] = fmaf(p, i8_at<3>(w[j]), acc[4 * j + 3]);
+    }
+  }
+}
+
+template <typename QT>
+__device__ __forceinline__ QT to_out(float x) {
+  return QT(x);   // fp32 -> fp16 conversion rounds to nearest even
+}
+
+template <typename KV, typename QT, int D, bool kPaged>
+__global__ __launch_bounds__(kThreads) void decode_kernel(Params p) {
+  using G = Geo<KV, D>;
+  constexpr int CPT = G::kCPT, TPI = G::kTPI, NLD = G::kNLD, EPC = G::kEPC;
+  constexpr bool kInt8 = std::is_same<KV, int8_t>::value;
+
+  const int total = p.num_seqs * p.num_heads * p.num_partitions;
+  const int w = xcd_remap(int(blockIdx.x), total);
+  const int s = w % p.num_seqs;
+  const int h = (w / p.num_seqs) % p.num_heads;
+  const int part = w / (p.num_seqs * p.num_heads);
+
+  int ctx = p.ctx[s];
+  const bool bad_ctx = ctx < 0 || ctx > p.max_ctx;
+  if (bad_ctx) ctx = ctx < 0 ? 0 : p.max_ctx;
+  const int nblk = (ctx + kBlockSize - 1) / kBlockSize;
+  const int seq_parts = nblk == 0 ? 1 : (nblk + p.partition_blocks - 1) / p.partition_blocks;
+  if (part >= seq_parts) return;
+  const int blk_begin = part * p.partition_blocks;
+  const int blk_end = min(blk_begin + p.partition_blocks, nblk);
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = wave_uniform(threadIdx.x / kWave);
+  const int grp = lane / CPT;
+  const int col = lane % CPT;
+  const int64_t sh = int64_t(s) * p.num_heads + h;
+
+  QSlice<KV, QT, EPC> qs;
+  qs.load(reinterpret_cast<const QT*>(p.q) + sh * D + col * EPC);
+
+  const int32_t* trow = p.tables + int64_t(s) * p.max_blocks;
+  const int64_t block_stride = int64_t(p.num_heads) * G::kTileBytes;
+
+  // Byte offset of tile (block b of this sequence, head h); *ok is false for a
+  // table entry outside the pool (the tile is then read from block 0 and masked).
+  auto tile_offset = [&](int b, bool* ok) -> int64_t {
+    if constexpr (kPaged) {
+      const int phys = trow[b];
+      *ok = unsigned(phys) < unsigned(p.num_blocks);
+      return (*ok ? int64_t(phys) : 0) * block_stride + int64_t(h) * G::kTileBytes;
+    } else {
+      *ok = true;
+      return (sh * p.max_tokens + int64_t(b) * kBlockSize) * G::kRowBytes;
+    }
+  };
+  auto load_tile = [&](const char* base, int64_t off, uint4 (&r)[NLD]) {
+    const char* src = base + off + lane * 16;
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) r[i] = *reinterpret_cast<const uint4*>(src + i * 1024);
+  };
+  auto block_scales = [&](int b, int64_t off, bool ok, float* ks, float* vs) {
+    if constexpr (kInt8) {
+      const int phys = ok ? trow[b] : 0;
+      *ks = float(p.k_scale[int64_t(phys) * p.num_heads + h]);
+      *vs = float(p.v_scale[int64_t(phys) * p.num_heads + h]);
+    } else {
+      *ks = 1.f;
+      *vs = 1.f;
+    }
+  };
+
+  float m = kNegBig, l = 0.f;
+  float acc[EPC];
+#pragma unroll
+  for (int e = 0; e < EPC; ++e) acc[e] = 0.f;
+
+  // A bad table entry is only recorded here and flagged after the loop: a
+  // store inside the loop would stop the compiler from fetching table entries
+  // through the scalar cache.
+  bool bad_entry = false;
+  int b = blk_begin + wave;
+  uint4 kc[NLD], vc[NLD];
+  bool ok_c = true;
+  int64_t off_c = 0;
+  if (b < blk_end) {
+    off_c = tile_offset(b, &ok_c);
+    load_tile(p.k, off_c, kc);
+    load_tile(p.v, off_c, vc);
+  }
+  for (; b < blk_end; b += kWaves) {
+    // Issue the next tile's loads before working on this one.
+    const int bn = b + kWaves;
+    uint4 kn[NLD], vn[NLD];
+    bool ok_n = true;
+    int64_t off_n = 0;
+    if (bn < blk_end) {
+      off_n = tile_offset(bn, &ok_n);
+      load_tile(p.k, off_n, kn);
+      load_tile(p.v, off_n, vn);
+    }
+    float kscale, vscale;
+    block_scales(b, off_c, ok_c, &kscale, &vscale);
+    bad_entry |= !ok_c;
+
+    const int t0 = b * kBlockSize;
+    float sc[NLD];
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) sc[i] = group_sum<CPT>(dot16(kc[i], qs)) * (kscale * p.scale_log2);
+    if (t0 + kBlockSize > ctx || !ok_c) {
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) {
+        if (!ok_c || t0 + i * TPI + grp >= ctx) {
+          sc[i] = -INFINITY;
+          vc[i] = make_uint4(0u, 0u, 0u, 0u);
+        }
+      }
+    }
+    float bmax = sc[0];
+#pragma unroll
+    for (int i = 1; i < NLD; ++i) bmax = fmaxf(bmax, sc[i]);
+    const float mn = fmaxf(m, bmax);
+    const float alpha = __builtin_amdgcn_exp2f(m - mn);
+    l *= alpha;
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) acc[e] *= alpha;
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const float pi = __builtin_amdgcn_exp2f(sc[i] - mn);
+      l += pi;
+      axpy16<KV, EPC>(pi * vscale, vc[i], acc);
+    }
+    m = mn;
+
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      kc[i] = kn[i];
+      vc[i] = vn[i];
+    }
+    ok_c = ok_n;
+    off_c = off_n;
+  }
+
+  if (bad_entry && lane == 0) flag_error(p.err, PA_DEV_BAD_TABLE_ENTRY);
+  if (bad_ctx && threadIdx.x == 0 && part == 0) flag_error(p.err, PA_DEV_BAD_CONTEXT);
+
+  // Epilogue: merge the kWaves * TPI softmax streams of the workgroup.
+  constexpr int kStreams = kWaves * TPI;
+  __shared__ float s_m[kStreams];
+  __shared__ float s_l[kStreams];
+  __shared__ float s_acc[kStreams][D];
+  const int j = wave * TPI + grp;
+#pragma unroll
+  for (int e = 0; e < EPC; ++e) s_acc[j][col * EPC + e] = acc[e];
+  if (col == 0) {
+    s_m[j] = m;
+    s_l[j] = l;
+  }
+  __syncthreads();
+  if (threadIdx.x < D) {
+    const int d = threadIdx.x;
+    float M = kNegBig;
+#pragma unroll
+    for (int t = 0; t < kStreams; ++t) M = fmaxf(M, s_m[t]);
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int t = 0; t < kStreams; ++t) {
+      const float wgt = __builtin_amdgcn_exp2f(s_m[t] - M);
+      L = fmaf(wgt, s_l[t], L);
+      O = fmaf(wgt, s_acc[t][d], O);
+    }
+    const float res = L > 0.f ? O / L : 0.f;
+    if (seq_parts == 1) {
+      reinterpret_cast<QT*>(p.out)[sh * D + d] = to_out<QT>(res);
+    } else {
+      const int64_t slot = sh * p.num_partitions + part;
+      p.ws_o[slot * D + d] = res;
+      if (d == 0) {
+        p.ws_m[slot] = M * kLn2;
+        p.ws_l[slot] = L;
+      }
+    }
+  }
+}
+
+// Merge the partitions of every (sequence, head) that has more than one.
+template <typename QT, int D>
+__global__ __launch_bounds__(D) void reduce_kernel(Params p) {
+  const int sh = blockIdx.x;
+  const int s = sh / p.num_heads;
+  int ctx = p.ctx[s];
+  ctx = ctx < 0 ? 0 : (ctx > p.max_ctx ? p.max_ctx : ctx);
+  const int nblk = (ctx + kBlockSize - 1) / kBlockSize;
+  const int parts = nblk == 0 ? 1 : (nblk + p.partition_blocks - 1) / p.partition_blocks;
+  if (parts <= 1) return;
+  const float* m = p.ws_m + int64_t(sh) * p.num_partitions;
+  const float* l = p.ws_l + int64_t(sh) * p.num_partitions;
+  const float* o = p.ws_o + int64_t(sh) * p.num_partitions * D;
+
+  float M = kNegBig;
+  for (int i = threadIdx.x; i < parts; i += D) M = fmaxf(M, m[i]);
+  M = wave_max(M);
+  __shared__ float s_max[D / kWave];
+  if ((threadIdx.x & (kWave - 1)) == 0) s_max[threadIdx.x / kWave] = M;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < D / kWave; ++i) M = fmaxf(M, s_max[i]);
+
+  const int d = threadIdx.x;
+  float L = 0.f, O = 0.f;
+  for (int i = 0; i < parts; ++i) {
+    const float wgt = __builtin_amdgcn_exp2f((m[i] - M) * kLog2e) * l[i];
+    L += wgt;
+    O = fmaf(wgt, o[int64_t(i) * D + d], O);
+  }
+  reinterpret_cast<QT*>(p.out)[int64_t(sh) * D + d] = to_out<QT>(O / L);
+}
+
+template <typename KV, typename QT, int D, bool kPaged>
+int launch_typed(const Params& p, int grid, int sh_count, hipStream_t st) {
+  hipLaunchKernelGGL((decode_kernel<KV, QT, D, kPaged>), dim3(grid), dim3(kThreads), 0, st, p);
+  if (p.num_partitions > 1)
+    hipLaunchKernelGGL((reduce_kernel<QT, D>), dim3(sh_count), dim3(D), 0, st, p);
+  return int(hipGetLastError());
+}
+
+template <typename KV, typename QT, bool kPaged>
+int launch_d(const Params& p, int D, int grid, int sh_count, hipStream_t st) {
+  return D == 64 ? launch_typed<KV, QT, 64, kPaged>(p, grid, sh_count, st)
+                 : launch_typed<KV, QT, 128, kPaged>(p, grid, sh_count, st);
+}
+
+template <typename KV, bool kPaged>
+int launch_q(const Params& p, pa_dtype qd, int D, int grid, int sh_count, hipStream_t st) {
+  return qd == PA_F32 ? launch_d<KV, float, kPaged>(p, D, grid, sh_count, st)
+                      : launch_d<KV, _Float16, kPaged>(p, D, grid, sh_count, st);
+}
+
+}  // namespace
+
+int launch_decode(const DecodeArgs& a, void* stream) {
+  Params p;
+  p.q = a.q;
+  p.out = a.out;
+  p.k = static_cast<const char*>(a.k);
+  p.v = static_cast<const char*>(a.v);
+  p.k_scale = static_cast<const _Float16*>(a.k_scale);
+  p.v_scale = static_cast<const _Float16*>(a.v_scale);
+  p.tables = a.tables;
+  p.max_tokens = a.max_tokens;
+  p.ctx = a.ctx;
+  p.max_blocks = a.max_blocks;
+  p.num_seqs = a.num_seqs;
+  p.num_heads = a.num_heads;
+  p.num_blocks = a.num_blocks;
+  p.max_ctx = a.max_ctx;
+  // Single pass: one partition large enough for any context.
+  p.partition_blocks = a.partition_tokens > 0 ? a.partition_tokens / kBlockSize
+                                               : (a.max_ctx + kBlockSize - 1) / kBlockSize + 1;
+  p.num_partitions = a.num_partitions;
+  p.scale_log2 = a.sm_scale * kLog2e;
+  p.ws_m = a.ws_m;
+  p.ws_l = a.ws_l;
+  p.ws_o = a.ws_o;
+  p.err = device_error_ptr();
+  const int sh_count = a.num_seqs * a.num_heads;
+  const int grid = sh_count * a.num_partitions;
+  if (grid == 0) return 0;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool paged = a.tables != nullptr;
+  switch (a.kv_dtype) {
+    case PA_F32:
+      return paged ? launch_q<float, true>(p, a.q_dtype, a.head_dim, grid, sh_count, st)
+                   : launch_q<float, false>(p, a.q_dtype, a.head_dim, grid, sh_count, st);
+    case PA_F16:
+      return paged ? launch_q<_Float16, true>(p, a.q_dtype, a.head_dim, grid, sh_count, st)
+                   : launch_q<_Float16, false>(p, a.q_dtype, a.head_dim, grid, sh_count, st);
+    case PA_I8:
+      return launch_q<int8_t, true>(p, a.q_dtype, a.head_dim, grid, sh_count, st);
+  }
+  return int(hipErrorInvalidValue);
+}
+
+}  // namespace pa

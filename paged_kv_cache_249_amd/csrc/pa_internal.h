@@ -1,0 +1,78 @@
+// Internal declarations shared by the host C++ and HIP sources of libpagedkv.
+#pragma once
+
+#include <cstdint>
+#include <cstdio>
+#include <cstdarg>
+
+#include "pagedkv.h"
+
+struct pa_pool {
+  int32_t num_blocks;
+  int32_t block_size;
+  int32_t num_heads;
+  int32_t head_dim;
+  pa_dtype kv_dtype;
+  void* k_cache;
+  void* v_cache;
+  void* k_scale;   // fp16 [num_blocks][num_heads], int8 pools only
+  void* v_scale;
+};
+
+namespace pa {
+
+constexpr int kBlockSize = 16;
+
+// Records the message of a failing call for pa_last_error() and returns st.
+pa_status fail(pa_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+void clear_error();
+
+inline int64_t elem_bytes(pa_dtype t) {
+  return t == PA_F32 ? 4 : t == PA_F16 ? 2 : 1;
+}
+
+inline bool geometry_supported(int32_t block_size, int32_t head_dim) {
+  return block_size == kBlockSize && (head_dim == 64 || head_dim == 128);
+}
+
+// Kernel launchers (decode.hip, cache_ops.hip). Arguments are validated by the
+// C-ABI layer before these are called. Each returns hipSuccess or the launch
+// error as an int.
+struct DecodeArgs {
+  const void* q;
+  pa_dtype q_dtype;
+  void* out;
+  const void* k;          // pool base, or contiguous [S][H][T][D] base
+  const void* v;
+  const void* k_scale;    // int8 pools only
+  const void* v_scale;
+  pa_dtype kv_dtype;
+  const int32_t* tables;  // nullptr => contiguous layout
+  int32_t max_blocks;     // table row stride
+  int64_t max_tokens;     // contiguous layout: tokens per (seq, head) row
+  const int32_t* ctx;
+  int32_t num_seqs;
+  int32_t num_heads;
+  int32_t head_dim;
+  int32_t num_blocks;     // pool size, for range checks
+  int32_t max_ctx;
+  float sm_scale;
+  int32_t partition_tokens;  // 0 => single pass
+  int32_t num_partitions;    // ceil(max_ctx / partition_tokens), 1 for single pass
+  float* ws_m;
+  float* ws_l;
+  float* ws_o;
+};
+
+int launch_decode(const DecodeArgs& a, void* stream);
+int launch_write_kv(const pa_pool* p, const void* k_new, const void* v_new, pa_dtype src,
+                    const int64_t* slots, int32_t n, void* stream);
+int launch_copy_blocks(const pa_pool* p, const int32_t* pairs, int32_t n, void* stream);
+int launch_stream_copy(void* dst, const void* src, int64_t bytes, void* stream);
+int read_and_clear_device_error(void* stream, int32_t* value);
+
+// Device address of the sticky error word on the current device (nullptr if
+// the lookup fails; kernels then skip flagging).
+int32_t* device_error_ptr();
+
+}  // namespace pa
