@@ -271,6 +271,10 @@ def extras(eng, wl, q, ptok, dev):
     b = torch.empty(n, dtype=torch.uint8, device=dev)
     t_copy = _time_calls(lambda: pk.pa_stream_copy(b, a))
     res["stream_copy_gbs"] = round(2 * n / t_copy / 1e9, 1)
+    big = torch.empty(4 << 30, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1024, dtype=torch.int32, device=dev)
+    t_read = _time_calls(lambda: pk.pa_stream_read(big, sink))
+    res["stream_read_gbs"] = round(big.numel() / t_read / 1e9, 1)
     return res
 
 

@@ -206,7 +206,8 @@ pa_status pa_check_errors(pa_stream stream, int32_t* device_error);
  * terms ("PagedAttention — 把 KV cache 当虚拟内存页来管理", 踩过的坑 states an
  * attention-kernel slowdown from the indirection). Float KV only.
  * pa_stream_copy copies bytes (a multiple of 16, 16-byte aligned pointers)
- * with a plain streaming kernel: a bandwidth probe and a counter calibration.
+ * with a plain streaming kernel: a bandwidth probe and a counter calibration
+ * (a copy of known size for the HBM byte counters).
  * ------------------------------------------------------------------------- */
 pa_status pa_decode_contiguous(const void* k, const void* v, pa_dtype kv_dtype, int32_t num_heads,
                                int32_t head_dim, int32_t max_tokens, const void* q,
@@ -215,6 +216,11 @@ pa_status pa_decode_contiguous(const void* k, const void* v, pa_dtype kv_dtype, 
                                void* workspace, int64_t workspace_bytes, pa_stream stream);
 
 pa_status pa_stream_copy(void* dst, const void* src, int64_t bytes, pa_stream stream);
+
+/* Reads bytes (a multiple of 16, 16-byte aligned) with a plain streaming
+ * kernel and folds them into a checksum: the read-only bandwidth probe. sink
+ * is device memory of at least 4096 bytes that may receive a word. */
+pa_status pa_stream_read(const void* src, int64_t bytes, void* sink, pa_stream stream);
 
 /* ----------------------------------------------------------------------------
  * Host block manager.

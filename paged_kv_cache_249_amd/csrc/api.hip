@@ -289,4 +289,10 @@ pa_status pa_stream_copy(void* dst, const void* src, int64_t bytes, pa_stream st
   return hip_status("pa_stream_copy", pa::launch_stream_copy(dst, src, bytes, stream));
 }
 
+pa_status pa_stream_read(const void* src, int64_t bytes, void* sink, pa_stream stream) {
+  if (!src || !sink || bytes < 0 || bytes % 16 || !aligned16(src))
+    return fail(PA_ERR_INVALID_ARG, "pa_stream_read: bad arguments");
+  return hip_status("pa_stream_read", pa::launch_stream_read(src, bytes, sink, stream));
+}
+
 }  // extern "C"

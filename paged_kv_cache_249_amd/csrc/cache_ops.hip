@@ -193,6 +193,25 @@ __global__ __launch_bounds__(kThreads) void stream_copy_kernel(uint4* __restrict
   for (; i < n16; i += stride) dst[i] = src[i];
 }
 
+// Reads n16 16-byte words and folds them into a checksum; the store that
+// keeps the loads alive fires only for one checksum value in 2^32.
+__global__ __launch_bounds__(kThreads) void stream_read_kernel(const uint4* __restrict__ src, int64_t n16,
+                                                               uint32_t* __restrict__ sink) {
+  constexpr int kUnroll = 4;
+  const int64_t stride = int64_t(gridDim.x) * kThreads;
+  int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+  uint32_t acc = 0;
+  for (; i + (kUnroll - 1) * stride < n16; i += kUnroll * stride) {
+    uint4 r[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) r[u] = src[i + u * stride];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) acc ^= r[u].x ^ r[u].y ^ r[u].z ^ r[u].w;
+  }
+  for (; i < n16; i += stride) acc ^= src[i].x ^ src[i].y ^ src[i].z ^ src[i].w;
+  if (acc == 0x9E3779B9u) sink[blockIdx.x & 1023] = acc;
+}
+
 template <typename DST, typename SRC>
 int launch_write_float(const pa_pool* p, const void* k_new, const void* v_new, const int64_t* slots,
                        int32_t n, hipStream_t st) {
@@ -270,6 +289,17 @@ int launch_stream_copy(void* dst, const void* src, int64_t bytes, void* stream) 
   hipLaunchKernelGGL(stream_copy_kernel, dim3(unsigned(blocks)), dim3(kThreads), 0,
                      static_cast<hipStream_t>(stream), static_cast<uint4*>(dst),
                      static_cast<const uint4*>(src), n16);
+  return int(hipGetLastError());
+}
+
+int launch_stream_read(const void* src, int64_t bytes, void* sink, void* stream) {
+  const int64_t n16 = bytes / 16;
+  if (n16 == 0) return 0;
+  int64_t blocks = (n16 + kThreads - 1) / kThreads;
+  if (blocks > 256 * 8) blocks = 256 * 8;
+  hipLaunchKernelGGL(stream_read_kernel, dim3(unsigned(blocks)), dim3(kThreads), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const uint4*>(src), n16,
+                     static_cast<uint32_t*>(sink));
   return int(hipGetLastError());
 }
 

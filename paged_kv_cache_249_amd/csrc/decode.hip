@@ -65,6 +65,7 @@ constexpr int kXcdGroup = 4;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegBig = -1.0e30f;   // finite "no logit yet" so exp2(m - m_new) stays defined
+constexpr int kRsrcWord3 = 0x00020000;  // buffer resource word 3 for raw dword access on gfx9-family parts
 
 template <typename KV, int D>
 struct Geo {
@@ -220,14 +221,27 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Params p) {
   QSlice<KV, QT, EPC> qs;
   qs.load(reinterpret_cast<const QT*>(p.q) + sh * D + col * EPC);
 
-  const int32_t* trow = p.tables + int64_t(s) * p.max_blocks;
+  const int32_t* trow = kPaged ? p.tables + int64_t(s) * p.max_blocks : nullptr;
   const int64_t block_stride = int64_t(p.num_heads) * G::kTileBytes;
 
-  // Byte offset of tile (block b of this sequence, head h); *ok is false for a
-  // table entry outside the pool (the tile is then read from block 0 and masked).
-  auto tile_offset = [&](int b, bool* ok) -> int64_t {
+  // This wave's blocks are first, first + 4, first + 8, ... (k-th at first + 4k).
+  const int first = blk_begin + wave;
+  const int iters = first < blk_end ? (blk_end - first + kWaves - 1) / kWaves : 0;
+
+  // Table entry of the wave's k-th block. Reads are wave-uniform and the loop
+  // stores nothing, so they go through the scalar cache and are counted apart
+  // from the vector loads: each is issued half an iteration before it is used.
+  auto entry = [&](int k) -> int {
     if constexpr (kPaged) {
-      const int phys = trow[b];
+      return trow[first + kWaves * k];
+    } else {
+      return 0;
+    }
+  };
+  // Byte offset of the tile of (block b, head h); *ok is false for a table
+  // entry outside the pool (the tile is then read from block 0 and masked).
+  auto tile_offset = [&](int b, int phys, bool* ok) -> int64_t {
+    if constexpr (kPaged) {
       *ok = unsigned(phys) < unsigned(p.num_blocks);
       return (*ok ? int64_t(phys) : 0) * block_stride + int64_t(h) * G::kTileBytes;
     } else {
@@ -235,65 +249,61 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Params p) {
       return (sh * p.max_tokens + int64_t(b) * kBlockSize) * G::kRowBytes;
     }
   };
+  // A tile is read through a buffer resource built per tile (uniform base in
+  // SGPRs, loop-invariant lane offset): no 64-bit vector address arithmetic in
+  // the loop, and the hardware clamps any access outside the tile to zero.
   auto load_tile = [&](const char* base, int64_t off, uint4 (&r)[NLD]) {
-    const char* src = base + off + lane * 16;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base + off), 0, G::kTileBytes, kRsrcWord3);
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) r[i] = *reinterpret_cast<const uint4*>(src + i * 1024);
+    for (int i = 0; i < NLD; ++i)
+      r[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, lane * 16 + i * 1024, 0, 0));
   };
-  auto block_scales = [&](int b, int64_t off, bool ok, float* ks, float* vs) {
+  struct TileRef {
+    int b;
+    bool ok;
+    float kscale, vscale;
+  };
+  // Issue the loads of the wave's k-th tile (table entry phys) into (kr, vr).
+  auto fetch = [&](int k, int phys, uint4 (&kr)[NLD], uint4 (&vr)[NLD]) -> TileRef {
+    TileRef t;
+    t.b = first + k * kWaves;
+    const int64_t off = tile_offset(t.b, phys, &t.ok);
+    load_tile(p.k, off, kr);
+    load_tile(p.v, off, vr);
     if constexpr (kInt8) {
-      const int phys = ok ? trow[b] : 0;
-      *ks = float(p.k_scale[int64_t(phys) * p.num_heads + h]);
-      *vs = float(p.v_scale[int64_t(phys) * p.num_heads + h]);
+      const int64_t si = int64_t(t.ok ? phys : 0) * p.num_heads + h;
+      t.kscale = float(p.k_scale[si]);
+      t.vscale = float(p.v_scale[si]);
     } else {
-      *ks = 1.f;
-      *vs = 1.f;
+      t.kscale = 1.f;
+      t.vscale = 1.f;
     }
+    return t;
   };
 
   float m = kNegBig, l = 0.f;
   float acc[EPC];
 #pragma unroll
   for (int e = 0; e < EPC; ++e) acc[e] = 0.f;
-
   // A bad table entry is only recorded here and flagged after the loop: a
   // store inside the loop would stop the compiler from fetching table entries
-  // through the scalar cache.
+  // and scales through the scalar cache.
   bool bad_entry = false;
-  int b = blk_begin + wave;
-  uint4 kc[NLD], vc[NLD];
-  bool ok_c = true;
-  int64_t off_c = 0;
-  if (b < blk_end) {
-    off_c = tile_offset(b, &ok_c);
-    load_tile(p.k, off_c, kc);
-    load_tile(p.v, off_c, vc);
-  }
-  for (; b < blk_end; b += kWaves) {
-    // Issue the next tile's loads before working on this one.
-    const int bn = b + kWaves;
-    uint4 kn[NLD], vn[NLD];
-    bool ok_n = true;
-    int64_t off_n = 0;
-    if (bn < blk_end) {
-      off_n = tile_offset(bn, &ok_n);
-      load_tile(p.k, off_n, kn);
-      load_tile(p.v, off_n, vn);
-    }
-    float kscale, vscale;
-    block_scales(b, off_c, ok_c, &kscale, &vscale);
-    bad_entry |= !ok_c;
 
-    const int t0 = b * kBlockSize;
+  // Online-softmax update with one tile.
+  auto process = [&](const TileRef& t, const uint4 (&kr)[NLD], uint4 (&vr)[NLD]) {
+    bad_entry |= !t.ok;
+    const int t0 = t.b * kBlockSize;
     float sc[NLD];
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) sc[i] = group_sum<CPT>(dot16(kc[i], qs)) * (kscale * p.scale_log2);
-    if (t0 + kBlockSize > ctx || !ok_c) {
+    for (int i = 0; i < NLD; ++i) sc[i] = group_sum<CPT>(dot16(kr[i], qs)) * (t.kscale * p.scale_log2);
+    if (t0 + kBlockSize > ctx || !t.ok) {
 #pragma unroll
       for (int i = 0; i < NLD; ++i) {
-        if (!ok_c || t0 + i * TPI + grp >= ctx) {
+        if (!t.ok || t0 + i * TPI + grp >= ctx) {
           sc[i] = -INFINITY;
-          vc[i] = make_uint4(0u, 0u, 0u, 0u);
+          vr[i] = make_uint4(0u, 0u, 0u, 0u);
         }
       }
     }
@@ -309,17 +319,37 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Params p) {
     for (int i = 0; i < NLD; ++i) {
       const float pi = __builtin_amdgcn_exp2f(sc[i] - mn);
       l += pi;
-      axpy16<KV, EPC>(pi * vscale, vc[i], acc);
+      axpy16<KV, EPC>(pi * t.vscale, vr[i], acc);
     }
     m = mn;
+  };
 
-#pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      kc[i] = kn[i];
-      vc[i] = vn[i];
+  // Two register buffers in turn. Inside the loop the next tile's loads are
+  // always issued before the current tile is used, so every wait leaves one
+  // tile in flight; the last one or two tiles are peeled off so that no load
+  // is issued that nothing consumes.
+  if (iters > 0) {
+    uint4 ka[NLD], va[NLD], kb[NLD], vb[NLD];
+    const int last = iters - 1;
+    int e_next = entry(min(1, last));
+    TileRef ta = fetch(0, entry(0), ka, va);
+    int k = 0;
+    for (; k + 2 < iters; k += 2) {
+      const int e1 = e_next;
+      const int e2 = entry(k + 2);
+      const TileRef tb = fetch(k + 1, e1, kb, vb);
+      process(ta, ka, va);
+      e_next = entry(min(k + 3, last));
+      ta = fetch(k + 2, e2, ka, va);
+      process(tb, kb, vb);
     }
-    ok_c = ok_n;
-    off_c = off_n;
+    if (k + 1 < iters) {
+      const TileRef tb = fetch(k + 1, e_next, kb, vb);
+      process(ta, ka, va);
+      process(tb, kb, vb);
+    } else {
+      process(ta, ka, va);
+    }
   }
 
   if (bad_entry && lane == 0) flag_error(p.err, PA_DEV_BAD_TABLE_ENTRY);

@@ -69,6 +69,7 @@ int launch_write_kv(const pa_pool* p, const void* k_new, const void* v_new, pa_d
                     const int64_t* slots, int32_t n, void* stream);
 int launch_copy_blocks(const pa_pool* p, const int32_t* pairs, int32_t n, void* stream);
 int launch_stream_copy(void* dst, const void* src, int64_t bytes, void* stream);
+int launch_stream_read(const void* src, int64_t bytes, void* sink, void* stream);
 int read_and_clear_device_error(void* stream, int32_t* value);
 
 // Device address of the sticky error word on the current device (nullptr if

@@ -104,6 +104,8 @@ class PagedDecodeEngine:
         max_ctx = int(ctx_np.max()) if n else 0
         self.last_ctx = ctx_np.copy()
         self.last_pairs = npairs
+        self.last_pair_list = pairs.copy()
+        self.last_slots = slots_np[:n].copy()
 
         cur = torch.cuda.current_stream(self.device) if stream is None else stream
         with torch.cuda.stream(cur):

@@ -67,6 +67,7 @@ _SIGS = {
     "pa_decode_contiguous": ([_vp, _vp, _i32, _i32, _i32, _i32, _vp, _i32, _vp, _vp, _i32, _f32, _i32,
                               _vp, _i64, _vp], _i32),
     "pa_stream_copy": ([_vp, _vp, _i64, _vp], _i32),
+    "pa_stream_read": ([_vp, _i64, _vp, _vp], _i32),
     "pa_bm_create": ([_i32, _i32, _vp, _i32, C.POINTER(_vp)], _i32),
     "pa_bm_destroy": ([_vp], _i32),
     "pa_bm_add_seq": ([_vp, _i64, _i32, _vp], _i32),
@@ -288,6 +289,14 @@ def pa_stream_copy(dst, src, stream=None) -> None:
         raise PagedKVError(PA_ERR_INVALID_ARG, "dst too small")
     _check(lib.pa_stream_copy(_ptr(dst, "dst"), _ptr(src, "src"), nbytes, _stream(stream, src)),
            "pa_stream_copy")
+
+
+def pa_stream_read(src, sink, stream=None) -> None:
+    """Read every byte of ``src`` once (bandwidth probe); ``sink`` >= 4096 bytes."""
+    if sink.numel() * sink.element_size() < 4096:
+        raise PagedKVError(PA_ERR_INVALID_ARG, "sink must hold 4096 bytes")
+    _check(lib.pa_stream_read(_ptr(src, "src"), src.numel() * src.element_size(), _ptr(sink, "sink"),
+                              _stream(stream, src)), "pa_stream_read")
 
 
 # ---------------------------------------------------------------------------
