@@ -185,6 +185,19 @@ pa_status pa_decode(pa_pool* pool, const void* q, pa_dtype q_dtype, void* out,
                     float sm_scale, int32_t partition_tokens, void* workspace,
                     int64_t workspace_bytes, pa_stream stream);
 
+/* pa_decode with a schedule: seq_order (device int32 [num_seqs], a
+ * permutation of the batch, or NULL for batch order) is the order in which
+ * sequences are dispatched, all heads of a sequence together. Passing the
+ * batch sorted by decreasing context length (longest first) shortens the
+ * tail of a single-pass launch, whose per-sequence work is proportional to
+ * the context. Results do not depend on the order. An entry outside
+ * [0, num_seqs) flags PA_DEV_BAD_CONTEXT and that work is skipped. */
+pa_status pa_decode_ordered(pa_pool* pool, const void* q, pa_dtype q_dtype, void* out,
+                            const int32_t* block_tables, int32_t max_blocks,
+                            const int32_t* context_lens, const int32_t* seq_order, int32_t num_seqs,
+                            int32_t max_context_len, float sm_scale, int32_t partition_tokens,
+                            void* workspace, int64_t workspace_bytes, pa_stream stream);
+
 /* Layout of the split-K workspace, for callers that inspect partials: with
  * P = ceil(max_context_len / partition_tokens), the workspace holds
  *   m [num_seqs][num_heads][P] fp32   largest logit of the partition (natural units)
@@ -204,7 +217,8 @@ pa_status pa_check_errors(pa_stream stream, int32_t* device_error);
  * k[num_seqs][num_heads][max_tokens][head_dim] (same for v), with no block
  * table, so that the cost of the table indirection can be measured on equal
  * terms ("PagedAttention — 把 KV cache 当虚拟内存页来管理", 踩过的坑 states an
- * attention-kernel slowdown from the indirection). Float KV only.
+ * attention-kernel slowdown from the indirection). Float KV only; seq_order
+ * as in pa_decode_ordered (may be NULL).
  * pa_stream_copy copies bytes (a multiple of 16, 16-byte aligned pointers)
  * with a plain streaming kernel: a bandwidth probe and a counter calibration
  * (a copy of known size for the HBM byte counters).
@@ -212,8 +226,9 @@ pa_status pa_check_errors(pa_stream stream, int32_t* device_error);
 pa_status pa_decode_contiguous(const void* k, const void* v, pa_dtype kv_dtype, int32_t num_heads,
                                int32_t head_dim, int32_t max_tokens, const void* q,
                                pa_dtype q_dtype, void* out, const int32_t* context_lens,
-                               int32_t num_seqs, float sm_scale, int32_t partition_tokens,
-                               void* workspace, int64_t workspace_bytes, pa_stream stream);
+                               const int32_t* seq_order, int32_t num_seqs, float sm_scale,
+                               int32_t partition_tokens, void* workspace, int64_t workspace_bytes,
+                               pa_stream stream);
 
 pa_status pa_stream_copy(void* dst, const void* src, int64_t bytes, pa_stream stream);
 

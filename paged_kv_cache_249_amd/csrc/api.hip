@@ -217,6 +217,15 @@ pa_status pa_decode(pa_pool* pool, const void* q, pa_dtype q_dtype, void* out, c
                     int32_t max_blocks, const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
                     float sm_scale, int32_t partition_tokens, void* workspace, int64_t workspace_bytes,
                     pa_stream stream) {
+  return pa_decode_ordered(pool, q, q_dtype, out, block_tables, max_blocks, context_lens, nullptr, num_seqs,
+                           max_context_len, sm_scale, partition_tokens, workspace, workspace_bytes, stream);
+}
+
+pa_status pa_decode_ordered(pa_pool* pool, const void* q, pa_dtype q_dtype, void* out,
+                            const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens,
+                            const int32_t* seq_order, int32_t num_seqs, int32_t max_context_len, float sm_scale,
+                            int32_t partition_tokens, void* workspace, int64_t workspace_bytes,
+                            pa_stream stream) {
   if (!pool) return fail(PA_ERR_INVALID_ARG, "pa_decode: pool is NULL");
   if (!block_tables) return fail(PA_ERR_INVALID_ARG, "pa_decode: block_tables is NULL");
   if (max_context_len < 0 || max_blocks < 0 ||
@@ -236,6 +245,7 @@ pa_status pa_decode(pa_pool* pool, const void* q, pa_dtype q_dtype, void* out, c
   a.max_blocks = max_blocks;
   a.max_tokens = 0;
   a.ctx = context_lens;
+  a.order = seq_order;
   a.num_seqs = num_seqs;
   a.num_heads = pool->num_heads;
   a.head_dim = pool->head_dim;
@@ -248,9 +258,9 @@ pa_status pa_decode(pa_pool* pool, const void* q, pa_dtype q_dtype, void* out, c
 
 pa_status pa_decode_contiguous(const void* k, const void* v, pa_dtype kv_dtype, int32_t num_heads,
                                int32_t head_dim, int32_t max_tokens, const void* q, pa_dtype q_dtype,
-                               void* out, const int32_t* context_lens, int32_t num_seqs, float sm_scale,
-                               int32_t partition_tokens, void* workspace, int64_t workspace_bytes,
-                               pa_stream stream) {
+                               void* out, const int32_t* context_lens, const int32_t* seq_order,
+                               int32_t num_seqs, float sm_scale, int32_t partition_tokens, void* workspace,
+                               int64_t workspace_bytes, pa_stream stream) {
   if (!k || !v) return fail(PA_ERR_INVALID_ARG, "pa_decode_contiguous: NULL cache");
   if (kv_dtype != PA_F32 && kv_dtype != PA_F16)
     return fail(PA_ERR_UNSUPPORTED, "pa_decode_contiguous: float KV only");
@@ -269,6 +279,7 @@ pa_status pa_decode_contiguous(const void* k, const void* v, pa_dtype kv_dtype, 
   a.tables = nullptr;
   a.max_tokens = max_tokens;
   a.ctx = context_lens;
+  a.order = seq_order;
   a.num_seqs = num_seqs;
   a.num_heads = num_heads;
   a.head_dim = head_dim;

@@ -41,7 +41,8 @@
 // w_p = exp(m_p - M) l_p. Sequences with one partition are written directly.
 //
 // XCD-aware order: work item w enumerates (partition, head, sequence) with the
-// sequence fastest. Workgroup ids are dealt to the 8 XCDs round-robin; groups
+// sequence fastest (or, when the caller passes a schedule, (partition,
+// scheduled sequence, head) with the head fastest, e.g. longest first). Workgroup ids are dealt to the 8 XCDs round-robin; groups
 // of 4 consecutive work items are steered onto one XCD, so the 4 sequences
 // next to each other in the batch (e.g. samples sharing a prompt's blocks)
 // read those blocks through the same L2 at about the same time, while the
@@ -58,7 +59,11 @@
 namespace pa {
 namespace {
 
-constexpr int kWaves = 4;
+// Waves per workgroup: each owns every kWaves-th block of the partition.
+#ifndef PA_DECODE_WAVES
+#define PA_DECODE_WAVES 4
+#endif
+constexpr int kWaves = PA_DECODE_WAVES;
 constexpr int kThreads = kWaves * kWave;
 constexpr int kXcds = 8;
 constexpr int kXcdGroup = 4;
@@ -66,6 +71,22 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegBig = -1.0e30f;   // finite "no logit yet" so exp2(m - m_new) stays defined
 constexpr int kRsrcWord3 = 0x00020000;  // buffer resource word 3 for raw dword access on gfx9-family parts
+
+// Cache policy of the K/V tile loads (buffer instruction aux bits; 2 = nt,
+// non-temporal): KV rows are read once per step, so they are streamed.
+#ifndef PA_DECODE_LOAD_AUX
+#define PA_DECODE_LOAD_AUX 2
+#endif
+// Tiles each wave keeps in flight beyond the one it works on: 1 = register
+// double buffering (~110 VGPRs, 4 waves per SIMD); 0 = one tile per wave and
+// more waves per SIMD (~60 VGPRs).
+#ifndef PA_DECODE_PREFETCH
+#define PA_DECODE_PREFETCH 1
+#endif
+// Minimum waves per SIMD the register allocator must leave room for.
+#ifndef PA_DECODE_MIN_WAVES
+#define PA_DECODE_MIN_WAVES (PA_DECODE_PREFETCH ? 4 : 8)
+#endif
 
 template <typename KV, int D>
 struct Geo {
@@ -88,6 +109,7 @@ struct Params {
   const int32_t* tables;
   int64_t max_tokens;       // contiguous layout row length
   const int32_t* ctx;
+  const int32_t* order;     // optional schedule: the r-th sequence dispatched is order[r]
   int32_t max_blocks;
   int32_t num_seqs;
   int32_t num_heads;
@@ -192,40 +214,64 @@ __device__ __forceinline__ QT to_out(float x) {
 }
 
 template <typename KV, typename QT, int D, bool kPaged>
-__global__ __launch_bounds__(kThreads) void decode_kernel(Params p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PA_DECODE_MIN_WAVES)))
+void decode_kernel(Params p) {
   using G = Geo<KV, D>;
   constexpr int CPT = G::kCPT, TPI = G::kTPI, NLD = G::kNLD, EPC = G::kEPC;
   constexpr bool kInt8 = std::is_same<KV, int8_t>::value;
 
   const int total = p.num_seqs * p.num_heads * p.num_partitions;
   const int w = xcd_remap(int(blockIdx.x), total);
-  const int s = w % p.num_seqs;
-  const int h = (w / p.num_seqs) % p.num_heads;
+  int s, h;
   const int part = w / (p.num_seqs * p.num_heads);
-
-  int ctx = p.ctx[s];
-  const bool bad_ctx = ctx < 0 || ctx > p.max_ctx;
-  if (bad_ctx) ctx = ctx < 0 ? 0 : p.max_ctx;
-  const int nblk = (ctx + kBlockSize - 1) / kBlockSize;
-  const int seq_parts = nblk == 0 ? 1 : (nblk + p.partition_blocks - 1) / p.partition_blocks;
-  if (part >= seq_parts) return;
-  const int blk_begin = part * p.partition_blocks;
-  const int blk_end = min(blk_begin + p.partition_blocks, nblk);
+  if (p.order) {
+    // Scheduled: ranks of the caller's order (e.g. longest first) in groups
+    // of kXcdGroup; a group's items run head by head, so the group's
+    // sequences with one head form kXcdGroup consecutive items (one XCD).
+    const int r = w % (p.num_seqs * p.num_heads);
+    const int g = r / (kXcdGroup * p.num_heads);
+    const int gs = min(kXcdGroup, p.num_seqs - g * kXcdGroup);
+    const int q_in = r - g * kXcdGroup * p.num_heads;
+    h = q_in / gs;
+    s = p.order[g * kXcdGroup + q_in % gs];
+    if (unsigned(s) >= unsigned(p.num_seqs)) {
+      if (threadIdx.x == 0) flag_error(p.err, PA_DEV_BAD_CONTEXT);
+      return;
+    }
+  } else {
+    s = w % p.num_seqs;
+    h = (w / p.num_seqs) % p.num_heads;
+  }
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = wave_uniform(threadIdx.x / kWave);
   const int grp = lane / CPT;
   const int col = lane % CPT;
   const int64_t sh = int64_t(s) * p.num_heads + h;
-
-  QSlice<KV, QT, EPC> qs;
-  qs.load(reinterpret_cast<const QT*>(p.q) + sh * D + col * EPC);
-
+  const int blk_begin = part * p.partition_blocks;
+  // This wave's blocks are first, first + 4, first + 8, ... (k-th at first + 4k).
+  const int first = blk_begin + wave;
   const int32_t* trow = kPaged ? p.tables + int64_t(s) * p.max_blocks : nullptr;
   const int64_t block_stride = int64_t(p.num_heads) * G::kTileBytes;
 
-  // This wave's blocks are first, first + 4, first + 8, ... (k-th at first + 4k).
-  const int first = blk_begin + wave;
+  // Loads that do not depend on the context length go out together with it:
+  // the wave's first two table entries (inside the row; unused if past the
+  // context) and its q slice. The first tile then waits for one round trip.
+  int ctx = p.ctx[s];
+  int e0 = 0, e1 = 0;
+  if constexpr (kPaged) {
+    e0 = first < p.max_blocks ? trow[first] : 0;
+    e1 = first + kWaves < p.max_blocks ? trow[first + kWaves] : 0;
+  }
+  QSlice<KV, QT, EPC> qs;
+  qs.load(reinterpret_cast<const QT*>(p.q) + sh * D + col * EPC);
+
+  const bool bad_ctx = ctx < 0 || ctx > p.max_ctx;
+  if (bad_ctx) ctx = ctx < 0 ? 0 : p.max_ctx;
+  const int nblk = (ctx + kBlockSize - 1) / kBlockSize;
+  const int seq_parts = nblk == 0 ? 1 : (nblk + p.partition_blocks - 1) / p.partition_blocks;
+  if (part >= seq_parts) return;
+  const int blk_end = min(blk_begin + p.partition_blocks, nblk);
   const int iters = first < blk_end ? (blk_end - first + kWaves - 1) / kWaves : 0;
 
   // Table entry of the wave's k-th block. Reads are wave-uniform and the loop
@@ -257,7 +303,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Params p) {
         __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base + off), 0, G::kTileBytes, kRsrcWord3);
 #pragma unroll
     for (int i = 0; i < NLD; ++i)
-      r[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, lane * 16 + i * 1024, 0, 0));
+      r[i] = __builtin_bit_cast(
+          uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, lane * 16 + i * 1024, 0, PA_DECODE_LOAD_AUX));
   };
   struct TileRef {
     int b;
@@ -328,11 +375,20 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Params p) {
   // always issued before the current tile is used, so every wait leaves one
   // tile in flight; the last one or two tiles are peeled off so that no load
   // is issued that nothing consumes.
-  if (iters > 0) {
+  if (PA_DECODE_PREFETCH == 0) {
+    int e = e0;
+    for (int k = 0; k < iters; ++k) {
+      const int e_next = k + 1 < iters ? (k == 0 ? e1 : entry(k + 1)) : 0;   // consumed next iteration
+      uint4 ka[NLD], va[NLD];
+      const TileRef ta = fetch(k, e, ka, va);
+      process(ta, ka, va);
+      e = e_next;
+    }
+  } else if (iters > 0) {
     uint4 ka[NLD], va[NLD], kb[NLD], vb[NLD];
     const int last = iters - 1;
-    int e_next = entry(min(1, last));
-    TileRef ta = fetch(0, entry(0), ka, va);
+    int e_next = last >= 1 ? e1 : e0;
+    TileRef ta = fetch(0, e0, ka, va);
     int k = 0;
     for (; k + 2 < iters; k += 2) {
       const int e1 = e_next;
@@ -460,6 +516,7 @@ int launch_decode(const DecodeArgs& a, void* stream) {
   p.tables = a.tables;
   p.max_tokens = a.max_tokens;
   p.ctx = a.ctx;
+  p.order = a.order;
   p.max_blocks = a.max_blocks;
   p.num_seqs = a.num_seqs;
   p.num_heads = a.num_heads;

@@ -51,6 +51,7 @@ struct DecodeArgs {
   int32_t max_blocks;     // table row stride
   int64_t max_tokens;     // contiguous layout: tokens per (seq, head) row
   const int32_t* ctx;
+  const int32_t* order;   // optional schedule (permutation of the batch), may be null
   int32_t num_seqs;
   int32_t num_heads;
   int32_t head_dim;

@@ -63,8 +63,10 @@ _SIGS = {
     "pa_copy_blocks": ([_vp, _vp, _i32, _vp], _i32),
     "pa_decode_workspace_bytes": ([_vp, _i32, _i32, _i32, _pi64], _i32),
     "pa_decode": ([_vp, _vp, _i32, _vp, _vp, _i32, _vp, _i32, _i32, _f32, _i32, _vp, _i64, _vp], _i32),
+    "pa_decode_ordered": ([_vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _f32, _i32, _vp, _i64, _vp],
+                          _i32),
     "pa_check_errors": ([_vp, _pi32], _i32),
-    "pa_decode_contiguous": ([_vp, _vp, _i32, _i32, _i32, _i32, _vp, _i32, _vp, _vp, _i32, _f32, _i32,
+    "pa_decode_contiguous": ([_vp, _vp, _i32, _i32, _i32, _i32, _vp, _i32, _vp, _vp, _vp, _i32, _f32, _i32,
                               _vp, _i64, _vp], _i32),
     "pa_stream_copy": ([_vp, _vp, _i64, _vp], _i32),
     "pa_stream_read": ([_vp, _i64, _vp, _vp], _i32),
@@ -236,8 +238,12 @@ def pa_decode_workspace_bytes(pool: Pool, num_seqs: int, max_context_len: int,
 
 
 def pa_decode(pool: Pool, q, out, block_tables, context_lens, max_context_len: int,
-              sm_scale: float = 0.0, partition_tokens: int = 0, workspace=None, stream=None) -> None:
-    """Paged decode: ``q``/``out`` ``[S][heads][head_dim]``, tables int32 ``[S][max_blocks]``."""
+              sm_scale: float = 0.0, partition_tokens: int = 0, workspace=None, stream=None,
+              seq_order=None) -> None:
+    """Paged decode: ``q``/``out`` ``[S][heads][head_dim]``, tables int32 ``[S][max_blocks]``.
+
+    ``seq_order`` (int32 ``[S]`` device permutation) selects pa_decode_ordered.
+    """
     torch = _torch()
     S = int(q.shape[0])
     if tuple(q.shape) != (S, pool.num_heads, pool.head_dim) or out.shape != q.shape or out.dtype != q.dtype:
@@ -245,15 +251,25 @@ def pa_decode(pool: Pool, q, out, block_tables, context_lens, max_context_len: i
     if block_tables.dim() != 2 or block_tables.shape[0] < S or context_lens.numel() < S:
         raise PagedKVError(PA_ERR_INVALID_ARG, "block_tables/context_lens do not cover the batch")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib.pa_decode(pool.handle, _ptr(q, "q"), dtype_code(q.dtype), _ptr(out, "out"),
-                         _ptr(block_tables, "block_tables", torch.int32), int(block_tables.shape[1]),
-                         _ptr(context_lens, "context_lens", torch.int32), S, int(max_context_len),
-                         float(sm_scale), int(partition_tokens), _ptr(workspace, "workspace"),
-                         ws_bytes, _stream(stream, q)), "pa_decode")
+    if seq_order is None:
+        _check(lib.pa_decode(pool.handle, _ptr(q, "q"), dtype_code(q.dtype), _ptr(out, "out"),
+                             _ptr(block_tables, "block_tables", torch.int32), int(block_tables.shape[1]),
+                             _ptr(context_lens, "context_lens", torch.int32), S, int(max_context_len),
+                             float(sm_scale), int(partition_tokens), _ptr(workspace, "workspace"),
+                             ws_bytes, _stream(stream, q)), "pa_decode")
+        return
+    if seq_order.numel() < S:
+        raise PagedKVError(PA_ERR_INVALID_ARG, "seq_order does not cover the batch")
+    _check(lib.pa_decode_ordered(pool.handle, _ptr(q, "q"), dtype_code(q.dtype), _ptr(out, "out"),
+                                 _ptr(block_tables, "block_tables", torch.int32), int(block_tables.shape[1]),
+                                 _ptr(context_lens, "context_lens", torch.int32),
+                                 _ptr(seq_order, "seq_order", torch.int32), S, int(max_context_len),
+                                 float(sm_scale), int(partition_tokens), _ptr(workspace, "workspace"),
+                                 ws_bytes, _stream(stream, q)), "pa_decode_ordered")
 
 
 def pa_decode_contiguous(k, v, q, out, context_lens, sm_scale: float = 0.0,
-                         partition_tokens: int = 0, workspace=None, stream=None) -> None:
+                         partition_tokens: int = 0, workspace=None, stream=None, seq_order=None) -> None:
     """Decode over a contiguous cache ``[S][heads][max_tokens][head_dim]`` (measurement twin)."""
     torch = _torch()
     S, H, T, D = (int(x) for x in k.shape)
@@ -262,7 +278,8 @@ def pa_decode_contiguous(k, v, q, out, context_lens, sm_scale: float = 0.0,
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.pa_decode_contiguous(_ptr(k, "k"), _ptr(v, "v"), dtype_code(k.dtype), H, D, T,
                                     _ptr(q, "q"), dtype_code(q.dtype), _ptr(out, "out"),
-                                    _ptr(context_lens, "context_lens", torch.int32), S,
+                                    _ptr(context_lens, "context_lens", torch.int32),
+                                    _ptr(seq_order, "seq_order", torch.int32), S,
                                     float(sm_scale), int(partition_tokens), _ptr(workspace, "workspace"),
                                     ws_bytes, _stream(stream, q)), "pa_decode_contiguous")
 

@@ -119,8 +119,8 @@ def test_device_calls_validate_before_launching():
         assert L.pa_decode(h, q, pk.PA_F16, out, tab, 8, ctx, 0, 100, 0.0, 0, None, 0, None) == 0
         # Single pass needs no workspace.
         assert L.pa_decode_workspace_bytes(h, 4, 100, 0, C.byref(need)) == 0 and need.value == 0
-        assert L.pa_decode_contiguous(p(0x1000), p(0x2000), pk.PA_I8, 2, 64, 32, q, pk.PA_F16, out, ctx, 1,
-                                      0.0, 0, None, 0, None) == pk.PA_ERR_UNSUPPORTED
+        assert L.pa_decode_contiguous(p(0x1000), p(0x2000), pk.PA_I8, 2, 64, 32, q, pk.PA_F16, out, ctx, None,
+                                      1, 0.0, 0, None, 0, None) == pk.PA_ERR_UNSUPPORTED
         assert L.pa_stream_copy(p(0x1000), p(0x2000), 24, None) == pk.PA_ERR_INVALID_ARG
     finally:
         L.pa_free_pool(h)

@@ -228,3 +228,53 @@ def test_contiguous_twin_matches_the_oracle():
         pk.pa_decode_contiguous(kd, vd, qd, out, ctxd, partition_tokens=ptok, workspace=ws)
         torch.cuda.synchronize()
         assert_close(out.cpu().numpy(), ref, F16_ATOL, F16_RTOL, f"contiguous ptok={ptok}")
+
+
+def test_schedule_does_not_change_results():
+    # pa_decode_ordered only changes the dispatch order: every (sequence,
+    # head) reduces in the same order, so outputs are bit-identical.
+    pk = _pk()
+    ctx = [700, 96, 513, 16, 1, 2000, 45, 129, 300]
+    b = Batch(ctx, 5, 128, "f16", "f16", seed=64)
+    maxc = max(ctx)
+    for ptok in (0, 64):
+        base, _ = b.gpu(ptok)
+        for order in (np.argsort(-np.array(ctx), kind="stable"), W.rng(64, ptok).permutation(len(ctx))):
+            out = torch.empty_like(b.qd)
+            ws = None
+            if ptok:
+                nb = pk.pa_decode_workspace_bytes(b.pool, len(ctx), maxc, ptok)
+                ws = torch.empty(nb // 4, dtype=torch.float32, device=DEV)
+            pk.pa_decode(b.pool, b.qd, out, b.tabd, b.ctxd, maxc, partition_tokens=ptok, workspace=ws,
+                         seq_order=torch.from_numpy(order.astype(np.int32)).to(DEV))
+            torch.cuda.synchronize()
+            assert pk.pa_check_errors() == 0
+            assert np.array_equal(out.cpu().numpy().view(np.uint16), base.view(np.uint16))
+
+
+def test_out_of_range_indices_are_flagged_not_followed():
+    # Host-forced bad inputs that the kernels' own range checks turn into the
+    # sticky error word: a table entry past the pool, a context above the
+    # stated maximum, a schedule entry past the batch, a slot past the pool
+    # and a copy pair past the pool. Every kernel exits normally.
+    pk = _pk()
+    b = Batch([40, 20], 2, 64, "f16", "f16", seed=65)
+    tab = b.tab.copy()
+    tab[0, 1] = b.NB + 5
+    out = torch.empty_like(b.qd)
+    pk.pa_decode(b.pool, b.qd, out, torch.from_numpy(tab).to(DEV), b.ctxd, 40)
+    assert pk.pa_check_errors() & pk.PA_DEV_BAD_TABLE_ENTRY
+    assert not np.isnan(out.cpu().numpy()).any()
+    pk.pa_decode(b.pool, b.qd, out, b.tabd, torch.tensor([40, 20], dtype=torch.int32, device=DEV), 32)
+    assert pk.pa_check_errors() & pk.PA_DEV_BAD_CONTEXT
+    pk.pa_decode(b.pool, b.qd, out, b.tabd, b.ctxd, 40,
+                 seq_order=torch.tensor([0, 7], dtype=torch.int32, device=DEV))
+    assert pk.pa_check_errors() & pk.PA_DEV_BAD_CONTEXT
+    rows = torch.zeros((1, 2, 64), dtype=torch.float16, device=DEV)
+    before = b.kd.clone()
+    pk.pa_write_kv(b.pool, rows, rows, torch.tensor([b.NB * 16 + 3], dtype=torch.int64, device=DEV))
+    assert pk.pa_check_errors() & pk.PA_DEV_BAD_SLOT
+    pk.pa_copy_blocks(b.pool, torch.tensor([[0, b.NB]], dtype=torch.int32, device=DEV))
+    assert pk.pa_check_errors() & pk.PA_DEV_BAD_PAIR
+    assert torch.equal(before, b.kd)
+    assert pk.pa_check_errors() == 0

@@ -25,7 +25,7 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 F16_ATOL, F16_RTOL = 5e-3, 1e-2
 INT8_ABS = 2e-2
-BENCH_PTOK = 256
+BENCH_PTOK = 512
 
 
 def _pk():
@@ -79,7 +79,7 @@ def test_opt13b_full_size():
     assert np.array_equal(ot, nt) and np.array_equal(oc, nc)
     assert list(nc) == wl.context_lens
     outs = {BENCH_PTOK: out.cpu().numpy()}
-    for ptok in (0, 512):
+    for ptok in (0, 256, 1024):
         outs[ptok] = _decode_out(eng, pk, np.arange(S), q, ptok)
     qh = q.cpu().numpy()
     sample = sorted({int(np.argmin(wl.context_lens)), int(np.argmax(wl.context_lens)), 0, 31, 63})
