@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--partition-tokens", type=int, default=-1,
                     help="split-K partition size (0 = single pass, -1 = the tuned default)")
+    ap.add_argument("--workload", default="opt13b",
+                    choices=["opt13b", "long_context", "int8_ring", "shared_prefix", "tiny"],
+                    help="opt13b is the headline line; the others measure the remaining workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip contiguous / probe measurements")
     ap.add_argument("--profile-run", action="store_true",
@@ -238,30 +241,13 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    ptok = DEFAULT_PARTITION_TOKENS if args.partition_tokens < 0 else args.partition_tokens
     K, Wm = args.steps, args.warmup
-    wl = W.opt13b()
-    S, H, D = wl.num_seqs, wl.num_heads, wl.head_dim
-    # The first timed step attends over exactly the workload's contexts; the
-    # warm-up steps before it and the timed steps after it each add one token.
-    prefill = [c - 1 - Wm for c in wl.context_lens]
-    if min(prefill) < 0:
-        raise SystemExit("warmup longer than the shortest context")
-    final_need = sum(-(-(c + K) // 16) for c in wl.context_lens)
-    num_blocks = max(wl.num_blocks, -(-5 * final_need // 4))
-    cap = -(-(max(wl.context_lens) + K) // 16)
-    eng = PagedDecodeEngine(num_blocks, H, D, pk.PA_F16, S, cap,
-                            free_order=W.free_order(wl.seed, num_blocks), device=dev,
-                            partition_tokens=ptok)
-    for s in range(S):
-        k = W.normal_torch((prefill[s], H, D), wl.seed, W.STREAM_K, s, dtype=torch.float16, device=dev)
-        v = W.normal_torch((prefill[s], H, D), wl.seed, W.STREAM_V, s, dtype=torch.float16, device=dev)
-        eng.add_sequence(s, k, v)
-    ring = 4
-    knew = [W.normal_torch((S, H, D), wl.seed, W.STREAM_KNEW, i, dtype=torch.float16, device=dev) for i in range(ring)]
-    vnew = [W.normal_torch((S, H, D), wl.seed, W.STREAM_VNEW, i, dtype=torch.float16, device=dev) for i in range(ring)]
-    q = W.normal_torch((S, H, D), wl.seed, W.STREAM_Q, dtype=torch.float16, device=dev)
-    out = torch.empty_like(q)
+    ws = setup_workload(args.workload, args, dev, K, Wm)
+    eng, wl, S, H, D = ws["eng"], ws["wl"], ws["S"], ws["H"], ws["D"]
+    knew, vnew, q, out, ptok = ws["knew"], ws["vnew"], ws["q"], ws["out"], ws["ptok"]
+    ring = len(knew)
+    kv_bytes_of = ws["kv_bytes_of"]
+    num_blocks = eng.pool.num_blocks
     seqs = np.arange(S)
     torch.cuda.synchronize()
     assert pk.pa_check_errors() == 0
@@ -281,7 +267,7 @@ def main():
             eng.step(seqs, knew[i % ring], vnew[i % ring], q, out)
         torch.cuda.synchronize()
         print(json.dumps({"profile_run": True, "steps": K, "calibration_bytes": CALIBRATION_BYTES,
-                          "kv_bytes_per_decode": int(eng.last_ctx.astype(np.int64).sum()) * H * D * 4,
+                          "kv_bytes_per_decode": kv_bytes_of(eng.last_ctx),
                           "decode_source_sha256": _sha256(DECODE_SOURCE)}))
         return 0
 
@@ -291,7 +277,7 @@ def main():
     t0 = time.perf_counter()
     for i in range(K):
         eng.step(seqs, knew[i % ring], vnew[i % ring], q, out, decode_events=events[i])
-        kv_bytes.append(int(eng.last_ctx.astype(np.int64).sum()) * H * D * 2 * 2)
+        kv_bytes.append(kv_bytes_of(eng.last_ctx))
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     dev_err = pk.pa_check_errors()
@@ -313,14 +299,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16",
+        "dtype": ws["dtype"],
         "data": "synthetic",
         "config": {
-            "workload": "OPT-13B-shaped single-layer paged decode: 64 seqs, ctx ~U[128,2048] "
-                        "(seed 2), 40 heads x 128, fp16 KV, 16-token blocks scattered over a pool "
-                        "1.25x the need; step = block-manager append + uploads + write_kv + decode",
+            "workload": ws["desc"],
             "global_batch": S,
-            "seq_len": int(np.mean(wl.context_lens)),
+            "seq_len": int(np.mean(eng.last_ctx)),
             "parallelism": "none (1 GPU)",
             "partition_tokens": ptok,
             "num_blocks": num_blocks,
@@ -336,12 +320,129 @@ def main():
         "device_error_bits": dev_err,
     }
 
-    if not args.no_extras:
-        result["extras"] = extras(eng, wl, q, ptok, dev)
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    if "unique_bytes_of" in ws:
+        ub = ws["unique_bytes_of"](eng.last_ctx)
+        result["unique_kv_bytes_per_decode"] = ub
+        result["unique_gbs"] = round(ub / dec_avg_s / 1e9, 2)
+    if args.workload == "opt13b":
+        if not args.no_extras:
+            result["extras"] = extras(eng, wl, q, ptok, dev)
+        if not args.no_cpu_baseline:
+            result["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(result), flush=True)
     return 0
+
+
+def setup_workload(name, args, dev, K, Wm):
+    """Pool, block manager and inputs of one workload, ready for warm-up steps.
+
+    The state is built so that the first timed step (after Wm warm-up steps)
+    is the workload's stated step.
+    """
+    import numpy as np
+    import torch
+    import workloads as W
+    import paged_kv_cache_249_amd as pk
+    from paged_kv_cache_249_amd.engine import PagedDecodeEngine
+
+    f16 = torch.float16
+    wl = getattr(W, name)()
+    S, H, D = wl.num_seqs, wl.num_heads, wl.head_dim
+    ptok_default = wl.partition_tokens if wl.partition_tokens else DEFAULT_PARTITION_TOKENS
+    ptok = ptok_default if args.partition_tokens < 0 else args.partition_tokens
+    seqs = np.arange(S)
+    ring = 4
+    elem = wl.kv_elem_bytes()
+
+    def kv_bytes_of(ctx):
+        ctx = np.asarray(ctx, dtype=np.int64)
+        b = int(ctx.sum()) * H * D * 2 * elem
+        if wl.kv_dtype == "i8":
+            b += int(((ctx + 15) // 16).sum()) * H * 2 * 2       # one fp16 scale per (block, head), K and V
+        return b
+
+    out = {"wl": wl, "S": S, "H": H, "D": D, "ptok": ptok, "kv_bytes_of": kv_bytes_of}
+    src_dtype = torch.float32 if wl.kv_dtype in ("f32", "i8") else f16
+    q_dtype = torch.float32 if wl.q_dtype == "f32" else f16
+    code = {"f32": pk.PA_F32, "f16": pk.PA_F16, "i8": pk.PA_I8}[wl.kv_dtype]
+    out["dtype"] = wl.kv_dtype
+    out["knew"] = [W.normal_torch((S, H, D), wl.seed, W.STREAM_KNEW, i, dtype=src_dtype, device=dev)
+                   for i in range(ring)]
+    out["vnew"] = [W.normal_torch((S, H, D), wl.seed, W.STREAM_VNEW, i, dtype=src_dtype, device=dev)
+                   for i in range(ring)]
+    out["q"] = W.normal_torch((S, H, D), wl.seed, W.STREAM_Q, dtype=q_dtype, device=dev)
+    out["out"] = torch.empty_like(out["q"])
+
+    if name in ("opt13b", "long_context", "tiny"):
+        # Prefill ctx - 1 - Wm tokens per sequence, then every step adds one.
+        prefill = [c - 1 - Wm for c in wl.context_lens]
+        if min(prefill) < 0:
+            raise SystemExit("warmup longer than the shortest context")
+        final_need = sum(-(-(c + K) // 16) for c in wl.context_lens)
+        nb = max(wl.num_blocks, -(-5 * final_need // 4))
+        cap = -(-(max(wl.context_lens) + K) // 16)
+        eng = PagedDecodeEngine(nb, H, D, code, S, cap, free_order=W.free_order(wl.seed, nb), device=dev,
+                                partition_tokens=ptok)
+        for s in range(S):
+            k = W.normal_torch((prefill[s], H, D), wl.seed, W.STREAM_K, s, dtype=src_dtype, device=dev)
+            v = W.normal_torch((prefill[s], H, D), wl.seed, W.STREAM_V, s, dtype=src_dtype, device=dev)
+            eng.add_sequence(s, k, v)
+            del k, v
+        out["desc"] = {
+            "opt13b": "OPT-13B-shaped single-layer paged decode: 64 seqs, ctx ~U[128,2048] (seed 2), 40 heads "
+                      "x 128, fp16 KV, 16-token blocks scattered over a pool 1.25x the need; step = "
+                      "block-manager append + uploads + write_kv + decode",
+            "long_context": "long-context split-K paged decode: 4 seqs x 131072 tokens, 32 heads x 128, fp16 KV, "
+                            "partitions of 512 tokens + reduce kernel; step = append + uploads + write_kv + "
+                            "decode",
+            "tiny": "tiny paged decode: 4 seqs, ctx {17,33,50,100}, 8 heads x 64, fp32 q/K/V, pool of 64 blocks",
+        }[name]
+    elif name == "int8_ring":
+        # After gen - 1 - Wm appended tokens the warm-up steps begin; tokens
+        # whose blocks the ring evicts before the first timed step are only
+        # appended on the host (no live row depends on them).
+        Wb, gen = wl.window_blocks, wl.generated_tokens
+        eng = PagedDecodeEngine(wl.num_blocks, H, D, code, S, Wb, window_blocks=Wb,
+                                free_order=W.free_order(wl.seed, wl.num_blocks), device=dev,
+                                partition_tokens=ptok, pool_fill=0)
+        for s in range(S):
+            eng.add_sequence(s, prefill_tokens=0)
+        start = gen - 1 - Wm
+        first_kept = max(0, gen - Wb * 16)
+        for t in range(min(first_kept, start)):
+            eng.bm.append_batch(seqs)
+        for t in range(min(first_kept, start), start):
+            eng.step(seqs, out["knew"][t % ring], out["vnew"][t % ring], None, None, decode=False)
+        out["desc"] = ("sliding-window ring with int8 KV: 128 seqs, 256-block (4096-token) ring per seq, step "
+                       "after 8192 generated tokens, 32 heads x 128, int8 codes + one fp16 scale per (block, "
+                       "head) for K and V; step = append (ring eviction every 16 steps) + uploads + int8 "
+                       "write_kv + decode")
+    elif name == "shared_prefix":
+        P, Sm, pt, priv = wl.prompts, wl.samples, wl.prompt_tokens, wl.private_tokens
+        cap = -(-(pt + priv + K) // 16)
+        nb = max(wl.num_blocks, -(-5 * (P * -(-pt // 16) + S * -(-(priv + K) // 16) + S) // 4))
+        eng = PagedDecodeEngine(nb, H, D, code, S, cap, free_order=W.free_order(wl.seed, nb), device=dev,
+                                partition_tokens=ptok)
+        for p in range(P):
+            k = W.normal_torch((pt, H, D), wl.seed, W.STREAM_K, p, dtype=src_dtype, device=dev)
+            v = W.normal_torch((pt, H, D), wl.seed, W.STREAM_V, p, dtype=src_dtype, device=dev)
+            eng.add_sequence(p * Sm, k, v)
+            for j in range(1, Sm):
+                eng.fork(p * Sm, p * Sm + j)
+        for t in range(priv - 1 - Wm):
+            eng.step(seqs, out["knew"][t % ring], out["vnew"][t % ring], None, None, decode=False)
+
+        def unique_bytes_of(ctx):
+            ctx = np.asarray(ctx, dtype=np.int64)
+            return (P * pt + int((ctx - pt).sum())) * H * D * 2 * elem
+
+        out["unique_bytes_of"] = unique_bytes_of
+        out["desc"] = ("shared-prefix parallel sampling: 8 prompts x 4 samples, 1024 prompt tokens shared "
+                       "(ref count 4) + 256 private tokens per sample, 40 heads x 128, fp16 KV; step = append + "
+                       "uploads + write_kv + decode")
+    torch.cuda.synchronize()
+    out["eng"] = eng
+    return out
 
 
 def _time_calls(fn, reps=20):
