@@ -316,7 +316,7 @@ def main():
         "kv_bytes_per_decode": int(bytes_avg),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": recorded_traffic()},
+                     "traffic": recorded_traffic() if args.workload == "opt13b" else None},
         "device_error_bits": dev_err,
     }
 
