@@ -198,6 +198,24 @@ pa_status pa_decode_ordered(pa_pool* pool, const void* q, pa_dtype q_dtype, void
                             int32_t max_context_len, float sm_scale, int32_t partition_tokens,
                             void* workspace, int64_t workspace_bytes, pa_stream stream);
 
+/* pa_write_kv followed by pa_decode_ordered, in one launch, for float pools:
+ * row s of k_new / v_new ([num_seqs][num_heads][head_dim], src_dtype PA_F32
+ * or PA_F16) is sequence s's newest token and slot_mapping[s] (device int64)
+ * its slot, i.e. the slot of token context_lens[s] - 1 (what a decode step's
+ * append returns). The workgroup that reads a sequence's last block stores
+ * the row there and uses it directly, so the step needs no separate write
+ * launch. The pool ends up byte-identical to pa_write_kv's result and out
+ * identical to the two calls. A negative slot writes nothing; a slot that is
+ * not the newest token's flags PA_DEV_BAD_SLOT and is not written.
+ * Errors: PA_ERR_UNSUPPORTED for int8 pools (their quantisation works on
+ * whole blocks: use pa_write_kv), otherwise as pa_decode. */
+pa_status pa_write_decode(pa_pool* pool, const void* k_new, const void* v_new, pa_dtype src_dtype,
+                          const int64_t* slot_mapping, const void* q, pa_dtype q_dtype, void* out,
+                          const int32_t* block_tables, int32_t max_blocks,
+                          const int32_t* context_lens, const int32_t* seq_order, int32_t num_seqs,
+                          int32_t max_context_len, float sm_scale, int32_t partition_tokens,
+                          void* workspace, int64_t workspace_bytes, pa_stream stream);
+
 /* Layout of the split-K workspace, for callers that inspect partials: with
  * P = ceil(max_context_len / partition_tokens), the workspace holds
  *   m [num_seqs][num_heads][P] fp32   largest logit of the partition (natural units)
@@ -205,6 +223,16 @@ pa_status pa_decode_ordered(pa_pool* pool, const void* q, pa_dtype q_dtype, void
  *   o [num_seqs][num_heads][P][head_dim] fp32  attention over the partition alone
  * back to back, in that order. Entries of partitions past a sequence's context
  * are not written. */
+
+/* Upload a step's small host data (slots, table rows, context lengths, ...)
+ * with a compute kernel that reads pinned host memory directly: host_src must
+ * come from hipHostMalloc (or another pinned, device-mapped allocation) and
+ * stay unchanged until the copy has run; dst is device memory. bytes is a
+ * multiple of 16 and both pointers are 16-byte aligned. Unlike a DMA copy it
+ * runs on the caller's compute queue, so the kernels that follow it start
+ * without a cross-engine hand-off. Errors: PA_ERR_INVALID_ARG (including a
+ * source that is not pinned host memory), PA_ERR_HIP. */
+pa_status pa_stage_copy(void* dst, const void* host_src, int64_t bytes, pa_stream stream);
 
 /* Read and clear the sticky device error word (PA_DEV_* bits). Synchronises
  * the stream first. *device_error may be NULL to only clear. */

@@ -256,6 +256,50 @@ pa_status pa_decode_ordered(pa_pool* pool, const void* q, pa_dtype q_dtype, void
   return decode_common("pa_decode", a, workspace, workspace_bytes, stream);
 }
 
+pa_status pa_write_decode(pa_pool* pool, const void* k_new, const void* v_new, pa_dtype src_dtype,
+                          const int64_t* slot_mapping, const void* q, pa_dtype q_dtype, void* out,
+                          const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens,
+                          const int32_t* seq_order, int32_t num_seqs, int32_t max_context_len, float sm_scale,
+                          int32_t partition_tokens, void* workspace, int64_t workspace_bytes,
+                          pa_stream stream) {
+  if (!pool) return fail(PA_ERR_INVALID_ARG, "pa_write_decode: pool is NULL");
+  if (pool->kv_dtype == PA_I8)
+    return fail(PA_ERR_UNSUPPORTED, "pa_write_decode: int8 pools quantise per block; use pa_write_kv");
+  if (src_dtype != PA_F32 && src_dtype != PA_F16)
+    return fail(PA_ERR_UNSUPPORTED, "pa_write_decode: source dtype %d (F32 or F16)", int(src_dtype));
+  if (num_seqs > 0 && (!k_new || !v_new || !slot_mapping))
+    return fail(PA_ERR_INVALID_ARG, "pa_write_decode: NULL new rows or slots");
+  if (!aligned16(k_new) || !aligned16(v_new))
+    return fail(PA_ERR_INVALID_ARG, "pa_write_decode: new rows must be 16-byte aligned");
+  if (!block_tables) return fail(PA_ERR_INVALID_ARG, "pa_write_decode: block_tables is NULL");
+  if (max_context_len < 0 || max_blocks < 0 || int64_t(max_blocks) * pa::kBlockSize < int64_t(max_context_len))
+    return fail(PA_ERR_INVALID_ARG, "pa_write_decode: max_blocks=%d cannot hold max_context_len=%d", max_blocks,
+                max_context_len);
+  pa::DecodeArgs a{};
+  a.q = q;
+  a.q_dtype = q_dtype;
+  a.out = out;
+  a.k = pool->k_cache;
+  a.v = pool->v_cache;
+  a.kv_dtype = pool->kv_dtype;
+  a.tables = block_tables;
+  a.max_blocks = max_blocks;
+  a.ctx = context_lens;
+  a.order = seq_order;
+  a.num_seqs = num_seqs;
+  a.num_heads = pool->num_heads;
+  a.head_dim = pool->head_dim;
+  a.num_blocks = pool->num_blocks;
+  a.max_ctx = max_context_len;
+  a.sm_scale = sm_scale;
+  a.partition_tokens = partition_tokens;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.new_dtype = src_dtype;
+  a.slots = slot_mapping;
+  return decode_common("pa_write_decode", a, workspace, workspace_bytes, stream);
+}
+
 pa_status pa_decode_contiguous(const void* k, const void* v, pa_dtype kv_dtype, int32_t num_heads,
                                int32_t head_dim, int32_t max_tokens, const void* q, pa_dtype q_dtype,
                                void* out, const int32_t* context_lens, const int32_t* seq_order,
@@ -298,6 +342,18 @@ pa_status pa_stream_copy(void* dst, const void* src, int64_t bytes, pa_stream st
   if (!dst || !src || bytes < 0 || bytes % 16 || !aligned16(dst) || !aligned16(src))
     return fail(PA_ERR_INVALID_ARG, "pa_stream_copy: bad arguments");
   return hip_status("pa_stream_copy", pa::launch_stream_copy(dst, src, bytes, stream));
+}
+
+pa_status pa_stage_copy(void* dst, const void* host_src, int64_t bytes, pa_stream stream) {
+  if (!dst || !host_src || bytes < 0 || bytes % 16 || !aligned16(dst) || !aligned16(host_src))
+    return fail(PA_ERR_INVALID_ARG, "pa_stage_copy: bad arguments");
+  if (bytes == 0) return PA_OK;
+  void* view = nullptr;
+  hipError_t e = hipHostGetDevicePointer(&view, const_cast<void*>(host_src), 0);
+  if (e != hipSuccess || !view)
+    return fail(PA_ERR_INVALID_ARG, "pa_stage_copy: source is not pinned host memory (%s)", hipGetErrorString(e));
+  if (!aligned16(view)) return fail(PA_ERR_INVALID_ARG, "pa_stage_copy: device view of the source is unaligned");
+  return hip_status("pa_stage_copy", pa::launch_stage_copy(dst, view, bytes, stream));
 }
 
 pa_status pa_stream_read(const void* src, int64_t bytes, void* sink, pa_stream stream) {

@@ -193,6 +193,20 @@ __global__ __launch_bounds__(kThreads) void stream_copy_kernel(uint4* __restrict
   for (; i < n16; i += stride) dst[i] = src[i];
 }
 
+// Copies n16 16-byte words from pinned host memory (read directly over the
+// host link) to device memory, on the compute queue. The reads are
+// system-scope atomic loads, so no cache can serve a stale copy of a staging
+// buffer the host has rewritten since an earlier step.
+__global__ __launch_bounds__(kThreads) void stage_copy_kernel(uint4* __restrict__ dst,
+                                                              const uint64_t* __restrict__ src, int64_t n16) {
+  const int64_t stride = int64_t(gridDim.x) * kThreads;
+  for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < n16; i += stride) {
+    const uint64_t lo = __hip_atomic_load(src + 2 * i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    const uint64_t hi = __hip_atomic_load(src + 2 * i + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    dst[i] = make_uint4(uint32_t(lo), uint32_t(lo >> 32), uint32_t(hi), uint32_t(hi >> 32));
+  }
+}
+
 // Reads n16 16-byte words and folds them into a checksum; the store that
 // keeps the loads alive fires only for one checksum value in 2^32.
 __global__ __launch_bounds__(kThreads) void stream_read_kernel(const uint4* __restrict__ src, int64_t n16,
@@ -289,6 +303,17 @@ int launch_stream_copy(void* dst, const void* src, int64_t bytes, void* stream) 
   hipLaunchKernelGGL(stream_copy_kernel, dim3(unsigned(blocks)), dim3(kThreads), 0,
                      static_cast<hipStream_t>(stream), static_cast<uint4*>(dst),
                      static_cast<const uint4*>(src), n16);
+  return int(hipGetLastError());
+}
+
+int launch_stage_copy(void* dst, const void* src_device_view, int64_t bytes, void* stream) {
+  const int64_t n16 = bytes / 16;
+  if (n16 == 0) return 0;
+  int64_t blocks = (n16 + kThreads - 1) / kThreads;
+  if (blocks > 1024) blocks = 1024;
+  hipLaunchKernelGGL(stage_copy_kernel, dim3(unsigned(blocks)), dim3(kThreads), 0,
+                     static_cast<hipStream_t>(stream), static_cast<uint4*>(dst),
+                     static_cast<const uint64_t*>(src_device_view), n16);
   return int(hipGetLastError());
 }
 

@@ -122,6 +122,12 @@ struct Params {
   float* ws_l;
   float* ws_o;
   int32_t* err;
+  // Fused write (float pools): row s of k_new / v_new is sequence s's newest
+  // token, stored at slots[s]; null slots = no write.
+  const void* k_new;
+  const void* v_new;
+  const int64_t* slots;
+  int32_t new_is_f32;
 };
 
 // Bijection from dispatch order g to work item w: inside every chunk of
@@ -208,14 +214,50 @@ __device__ __forceinline__ void axpy16(float p, const uint4& r, float (&acc)[EPC
   }
 }
 
+// W consecutive 32-bit words from a 16-byte aligned address (8-byte aligned
+// when W == 2), with the widest loads that fit.
+template <typename T, int W>
+__device__ __forceinline__ void load_words(const T* src, uint32_t (&w)[W]) {
+  if constexpr (W % 4 == 0) {
+#pragma unroll
+    for (int j = 0; j < W / 4; ++j) {
+      const uint4 r = reinterpret_cast<const uint4*>(src)[j];
+      w[4 * j] = r.x;
+      w[4 * j + 1] = r.y;
+      w[4 * j + 2] = r.z;
+      w[4 * j + 3] = r.w;
+    }
+  } else {
+    static_assert(W == 2, "chunk shape");
+    const uint2 r = *reinterpret_cast<const uint2*>(src);
+    w[0] = r.x;
+    w[1] = r.y;
+  }
+}
+
+// Element e of a chunk of T values packed in 32-bit words, as float (exact).
+template <typename T, int W>
+__device__ __forceinline__ float word_elem(const uint32_t (&w)[W], int e) {
+  if constexpr (sizeof(T) == 4) {
+    return __builtin_bit_cast(float, w[e]);
+  } else {
+    return e % 2 ? hi_f16(w[e / 2]) : lo_f16(w[e / 2]);
+  }
+}
+
 template <typename QT>
 __device__ __forceinline__ QT to_out(float x) {
   return QT(x);   // fp32 -> fp16 conversion rounds to nearest even
 }
 
-template <typename KV, typename QT, int D, bool kPaged>
+// NEW: element type of the fused-write source rows (void = no fused write).
+template <typename KV, typename QT, int D, bool kPaged, typename NEW>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PA_DECODE_MIN_WAVES)))
-void decode_kernel(Params p) {
+void decode_kernel(Params p, const int32_t* __restrict__ tables, const int32_t* __restrict__ seq_ctx,
+                   const int64_t* __restrict__ new_slots) {
+  // tables / seq_ctx / new_slots are p.tables / p.ctx / p.slots, passed as
+  // restrict arguments so the compiler knows the kernel's stores (pool,
+  // output) never alias them and keeps reading them through the scalar cache.
   using G = Geo<KV, D>;
   constexpr int CPT = G::kCPT, TPI = G::kTPI, NLD = G::kNLD, EPC = G::kEPC;
   constexpr bool kInt8 = std::is_same<KV, int8_t>::value;
@@ -251,13 +293,13 @@ void decode_kernel(Params p) {
   const int blk_begin = part * p.partition_blocks;
   // This wave's blocks are first, first + 4, first + 8, ... (k-th at first + 4k).
   const int first = blk_begin + wave;
-  const int32_t* trow = kPaged ? p.tables + int64_t(s) * p.max_blocks : nullptr;
+  const int32_t* trow = kPaged ? tables + int64_t(s) * p.max_blocks : nullptr;
   const int64_t block_stride = int64_t(p.num_heads) * G::kTileBytes;
 
   // Loads that do not depend on the context length go out together with it:
   // the wave's first two table entries (inside the row; unused if past the
   // context) and its q slice. The first tile then waits for one round trip.
-  int ctx = p.ctx[s];
+  int ctx = seq_ctx[s];
   int e0 = 0, e1 = 0;
   if constexpr (kPaged) {
     e0 = first < p.max_blocks ? trow[first] : 0;
@@ -265,6 +307,21 @@ void decode_kernel(Params p) {
   }
   QSlice<KV, QT, EPC> qs;
   qs.load(reinterpret_cast<const QT*>(p.q) + sh * D + col * EPC);
+  // Fused write (float pools): the new row's slot and this lane's chunk of
+  // the row, fetched speculatively with the rest (used only by the wave that
+  // owns the sequence's last block).
+  constexpr bool kFusable = kPaged && !kInt8 && !std::is_same<NEW, void>::value;
+  using NewT = typename std::conditional<std::is_same<NEW, void>::value, float, NEW>::type;
+  constexpr int kNewWords = EPC * int(sizeof(NewT)) / 4;        // 32-bit words per lane chunk
+  int64_t new_slot = -1;
+  uint32_t rk[kNewWords], rv[kNewWords];                       // raw chunk, converted later
+  if constexpr (kFusable) {
+    new_slot = new_slots[s];
+    const NewT* ksrc = static_cast<const NewT*>(p.k_new) + sh * D + col * EPC;
+    const NewT* vsrc = static_cast<const NewT*>(p.v_new) + sh * D + col * EPC;
+    load_words(ksrc, rk);
+    load_words(vsrc, rv);
+  }
 
   const bool bad_ctx = ctx < 0 || ctx > p.max_ctx;
   if (bad_ctx) ctx = ctx < 0 ? 0 : p.max_ctx;
@@ -308,6 +365,7 @@ void decode_kernel(Params p) {
   };
   struct TileRef {
     int b;
+    int phys;
     bool ok;
     float kscale, vscale;
   };
@@ -315,6 +373,7 @@ void decode_kernel(Params p) {
   auto fetch = [&](int k, int phys, uint4 (&kr)[NLD], uint4 (&vr)[NLD]) -> TileRef {
     TileRef t;
     t.b = first + k * kWaves;
+    t.phys = phys;
     const int64_t off = tile_offset(t.b, phys, &t.ok);
     load_tile(p.k, off, kr);
     load_tile(p.v, off, vr);
@@ -338,10 +397,61 @@ void decode_kernel(Params p) {
   // and scales through the scalar cache.
   bool bad_entry = false;
 
+  // Fused write of the sequence's new token: the owning wave's lanes that
+  // hold row new_off of the last tile patch the new row into the tile's
+  // registers when that tile comes (if its physical block is the slot's),
+  // and store the row after the loop.
+  int new_off = -1;
+  bool patched = false, bad_slot = false;
+  int64_t new_dst = 0;
+  uint4 nk = make_uint4(0u, 0u, 0u, 0u), nv = nk;
+  if constexpr (kFusable) {
+    if (new_slots != nullptr && new_slot >= 0) {
+      const bool owner = blk_end == nblk && nblk > 0 && wave == (nblk - 1 - blk_begin) % kWaves;
+      if (nblk == 0 || int(new_slot % kBlockSize) != (ctx - 1) % kBlockSize) {
+        bad_slot = part == 0 && wave == 0;       // reported once per (sequence, head)
+      } else if (owner) {
+        new_off = int(new_slot % kBlockSize);
+      }
+    }
+  }
+  // The new row in the pool's element type (issued after the first tile's
+  // loads so their latencies overlap).
+  auto convert_new_row = [&]() {
+    if constexpr (kFusable) {
+      if (new_off >= 0) {
+        KV kv_k[EPC], kv_v[EPC];
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) {
+          kv_k[e] = KV(word_elem<NewT>(rk, e));
+          kv_v[e] = KV(word_elem<NewT>(rv, e));
+        }
+        nk = *reinterpret_cast<const uint4*>(kv_k);
+        nv = *reinterpret_cast<const uint4*>(kv_v);
+      }
+    }
+  };
+
   // Online-softmax update with one tile.
-  auto process = [&](const TileRef& t, const uint4 (&kr)[NLD], uint4 (&vr)[NLD]) {
+  auto process = [&](const TileRef& t, uint4 (&kr)[NLD], uint4 (&vr)[NLD]) {
     bad_entry |= !t.ok;
     const int t0 = t.b * kBlockSize;
+    if (new_off >= 0 && t.b == nblk - 1) {
+      if (t.ok && int64_t(t.phys) == new_slot / kBlockSize) {
+        patched = true;
+        new_dst = int64_t(t.phys) * block_stride + int64_t(h) * G::kTileBytes +
+                  int64_t(new_off) * G::kRowBytes + col * 16;
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) {
+          if (i == new_off / TPI && grp == new_off % TPI) {
+            kr[i] = nk;
+            vr[i] = nv;
+          }
+        }
+      } else {
+        bad_slot = true;
+      }
+    }
     float sc[NLD];
 #pragma unroll
     for (int i = 0; i < NLD; ++i) sc[i] = group_sum<CPT>(dot16(kr[i], qs)) * (t.kscale * p.scale_log2);
@@ -376,6 +486,7 @@ void decode_kernel(Params p) {
   // tile in flight; the last one or two tiles are peeled off so that no load
   // is issued that nothing consumes.
   if (PA_DECODE_PREFETCH == 0) {
+    convert_new_row();
     int e = e0;
     for (int k = 0; k < iters; ++k) {
       const int e_next = k + 1 < iters ? (k == 0 ? e1 : entry(k + 1)) : 0;   // consumed next iteration
@@ -389,6 +500,7 @@ void decode_kernel(Params p) {
     const int last = iters - 1;
     int e_next = last >= 1 ? e1 : e0;
     TileRef ta = fetch(0, e0, ka, va);
+    convert_new_row();
     int k = 0;
     for (; k + 2 < iters; k += 2) {
       const int e1 = e_next;
@@ -408,6 +520,11 @@ void decode_kernel(Params p) {
     }
   }
 
+  if (patched && grp == new_off % TPI) {
+    *reinterpret_cast<uint4*>(const_cast<char*>(p.k) + new_dst) = nk;
+    *reinterpret_cast<uint4*>(const_cast<char*>(p.v) + new_dst) = nv;
+  }
+  if (bad_slot && lane == 0) flag_error(p.err, PA_DEV_BAD_SLOT);
   if (bad_entry && lane == 0) flag_error(p.err, PA_DEV_BAD_TABLE_ENTRY);
   if (bad_ctx && threadIdx.x == 0 && part == 0) flag_error(p.err, PA_DEV_BAD_CONTEXT);
 
@@ -485,7 +602,22 @@ __global__ __launch_bounds__(D) void reduce_kernel(Params p) {
 
 template <typename KV, typename QT, int D, bool kPaged>
 int launch_typed(const Params& p, int grid, int sh_count, hipStream_t st) {
-  hipLaunchKernelGGL((decode_kernel<KV, QT, D, kPaged>), dim3(grid), dim3(kThreads), 0, st, p);
+  if constexpr (kPaged && !std::is_same<KV, int8_t>::value) {
+    if (p.slots != nullptr) {
+      if (p.new_is_f32)
+        hipLaunchKernelGGL((decode_kernel<KV, QT, D, kPaged, float>), dim3(grid), dim3(kThreads), 0, st, p,
+                           p.tables, p.ctx, p.slots);
+      else
+        hipLaunchKernelGGL((decode_kernel<KV, QT, D, kPaged, _Float16>), dim3(grid), dim3(kThreads), 0, st, p,
+                           p.tables, p.ctx, p.slots);
+    } else {
+      hipLaunchKernelGGL((decode_kernel<KV, QT, D, kPaged, void>), dim3(grid), dim3(kThreads), 0, st, p,
+                         p.tables, p.ctx, p.slots);
+    }
+  } else {
+    hipLaunchKernelGGL((decode_kernel<KV, QT, D, kPaged, void>), dim3(grid), dim3(kThreads), 0, st, p, p.tables,
+                       p.ctx, p.slots);
+  }
   if (p.num_partitions > 1)
     hipLaunchKernelGGL((reduce_kernel<QT, D>), dim3(sh_count), dim3(D), 0, st, p);
   return int(hipGetLastError());
@@ -531,6 +663,10 @@ int launch_decode(const DecodeArgs& a, void* stream) {
   p.ws_l = a.ws_l;
   p.ws_o = a.ws_o;
   p.err = device_error_ptr();
+  p.k_new = a.k_new;
+  p.v_new = a.v_new;
+  p.slots = a.slots;
+  p.new_is_f32 = a.new_dtype == PA_F32 ? 1 : 0;
   const int sh_count = a.num_seqs * a.num_heads;
   const int grid = sh_count * a.num_partitions;
   if (grid == 0) return 0;

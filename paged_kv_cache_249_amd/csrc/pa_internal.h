@@ -63,6 +63,11 @@ struct DecodeArgs {
   float* ws_m;
   float* ws_l;
   float* ws_o;
+  // Fused write (pa_write_decode): nullptr slots = none.
+  const void* k_new;
+  const void* v_new;
+  pa_dtype new_dtype;
+  const int64_t* slots;
 };
 
 int launch_decode(const DecodeArgs& a, void* stream);
@@ -71,6 +76,7 @@ int launch_write_kv(const pa_pool* p, const void* k_new, const void* v_new, pa_d
 int launch_copy_blocks(const pa_pool* p, const int32_t* pairs, int32_t n, void* stream);
 int launch_stream_copy(void* dst, const void* src, int64_t bytes, void* stream);
 int launch_stream_read(const void* src, int64_t bytes, void* sink, void* stream);
+int launch_stage_copy(void* dst, const void* src_device_view, int64_t bytes, void* stream);
 int read_and_clear_device_error(void* stream, int32_t* value);
 
 // Device address of the sticky error word on the current device (nullptr if

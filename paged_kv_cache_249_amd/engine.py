@@ -4,15 +4,20 @@ A step appends one token to each sequence of a batch and attends with it:
 
 1. host block manager (native): one slot per sequence, copy-on-write pairs,
    ring evictions, then the batch's table rows and live context lengths —
-   all written into pinned staging buffers by two library calls;
-2. asynchronous uploads of those buffers on the step's stream;
+   all written into a pinned staging buffer by two library calls, plus the
+   longest-first dispatch order;
+2. ``pa_stage_copy`` uploads that buffer with one small kernel on the step's
+   stream (``overlap_uploads=True`` moves it to an auxiliary stream that the
+   step's kernels wait on with an event; measured, the cross-stream wait costs
+   about what the overlap saves, so it is off by default);
 3. ``pa_copy_blocks`` for the copy-on-write pairs (only when there are any);
-4. ``pa_write_kv`` of the new K/V rows into their slots;
-5. ``pa_decode`` (single pass, or split-K partitions plus the reduce kernel).
+4. ``pa_write_kv`` of the new K/V rows into their slots and
+5. ``pa_decode_ordered`` (single pass, or split-K partitions plus the reduce
+   kernel) — for float pools both in one launch, ``pa_write_decode``.
 
-The host never waits for the device inside a step: staging buffers rotate
-through a small ring guarded by events, so the host prepares step k+1 while
-the device still runs step k.
+The host never waits for the device inside a step: pinned staging buffers
+rotate through a small ring guarded by events, and two device staging buffers
+alternate so an upload never overwrites the tables a running decode reads.
 """
 
 from __future__ import annotations
@@ -27,9 +32,11 @@ class PagedDecodeEngine:
     def __init__(self, num_blocks: int, num_heads: int, head_dim: int, kv_dtype: int,
                  max_seqs: int, max_blocks_per_seq: int, *, window_blocks: int = 0,
                  free_order=None, device="cuda", partition_tokens: int = 0,
-                 pool_fill=None, staging_depth: int = 3, longest_first: bool = True):
+                 pool_fill=None, staging_depth: int = 3, longest_first: bool = True,
+                 overlap_uploads: bool = False, fuse_write: bool = True):
         self.device = torch.device(device)
         self.num_heads, self.head_dim = num_heads, head_dim
+        self.kv_dtype = kv_dtype
         self.pool = N.new_pool(num_blocks, num_heads, head_dim, kv_dtype, device=self.device, fill=pool_fill)
         self.bm = N.BlockManager(num_blocks, N.BLOCK_SIZE, free_order=free_order, window_blocks=window_blocks)
         self.max_seqs = max_seqs
@@ -38,41 +45,64 @@ class PagedDecodeEngine:
         # Dispatch sequences longest first (pa_decode_ordered): the host knows
         # every context length, so the schedule costs one argsort per step.
         self.longest_first = longest_first
+        # Float pools write the new token inside the decode launch (pa_write_decode).
+        self.fuse_write = fuse_write and kv_dtype != N.PA_I8
         dev = self.device
-        # Everything a step uploads lives in one packed buffer so that a step
-        # makes a single host-to-device copy:
+        # Everything a step uploads lives in one packed buffer:
         #   slots int64 [max_seqs] | ctx int32 [max_seqs] | order int32 [max_seqs]
         #   | pairs int32 [max_seqs][2] | tables int32 [max_seqs][cap]
         self._off_ctx = 8 * max_seqs
         self._off_order = self._off_ctx + 4 * max_seqs
         self._off_pairs = self._off_order + 4 * max_seqs
         self._off_tables = self._off_pairs + 8 * max_seqs
-        self._stage_bytes = self._off_tables + 4 * max_seqs * self.cap
-        self._dev_stage = torch.zeros(self._stage_bytes, dtype=torch.uint8, device=dev)
-        self.slots, self.ctx, self.order, self.pairs, self.tables = self._views(self._dev_stage)
-        self.tables.fill_(-1)
+        self._stage_bytes = -(-(self._off_tables + 4 * max_seqs * self.cap) // 16) * 16
+        self._dev = []
+        for _ in range(2):
+            v = self._views(torch.zeros(self._stage_bytes, dtype=torch.uint8, device=dev))
+            v["tables"].fill_(-1)
+            v["released"] = None          # event: the last kernel reading this buffer is done
+            self._dev.append(v)
+        self._cur = 0
         self.workspace = None
         self._ws_bytes = 0
         self._staging = []
         for _ in range(staging_depth):
-            buf = torch.empty(self._stage_bytes, dtype=torch.uint8, pin_memory=True)
-            slots, ctx, order, pairs, tables = self._views(buf)
-            self._staging.append({"buf": buf, "slots": slots.numpy(), "ctx": ctx.numpy(),
-                                  "order": order.numpy(), "pairs": pairs.numpy(),
-                                  "tables": tables.numpy(), "event": None})
+            v = self._views(torch.empty(self._stage_bytes, dtype=torch.uint8, pin_memory=True))
+            v = {k: (t if k == "buf" else t.numpy()) for k, t in v.items()}
+            v["event"] = None             # event: the upload that last read this buffer is done
+            self._staging.append(v)
         self._next = 0
+        self._aux = torch.cuda.Stream(device=dev) if overlap_uploads else None
         self.last_ctx = np.zeros(0, dtype=np.int32)
         self.last_pairs = 0
 
     def _views(self, buf):
-        """(slots, ctx, order, pairs, tables) views of a packed staging buffer."""
         m = self.max_seqs
-        slots = buf[:self._off_ctx].view(torch.int64)
-        ctx = buf[self._off_ctx:self._off_order].view(torch.int32)
-        order = buf[self._off_order:self._off_pairs].view(torch.int32)
-        pairs = buf[self._off_pairs:self._off_tables].view(torch.int32).view(m, 2)
-        tables = buf[self._off_tables:self._stage_bytes].view(torch.int32).view(m, self.cap)
-        return slots, ctx, order, pairs, tables
+        return {
+            "buf": buf,
+            "slots": buf[:self._off_ctx].view(torch.int64),
+            "ctx": buf[self._off_ctx:self._off_order].view(torch.int32),
+            "order": buf[self._off_order:self._off_pairs].view(torch.int32),
+            "pairs": buf[self._off_pairs:self._off_tables].view(torch.int32).view(m, 2),
+            "tables": buf[self._off_tables:self._off_tables + 4 * m * self.cap].view(torch.int32).view(m, self.cap),
+        }
+
+    # Device views of the staging buffer the latest step used.
+    @property
+    def slots(self):
+        return self._dev[self._cur]["slots"]
+
+    @property
+    def tables(self):
+        return self._dev[self._cur]["tables"]
+
+    @property
+    def ctx(self):
+        return self._dev[self._cur]["ctx"]
+
+    @property
+    def order(self):
+        return self._dev[self._cur]["order"]
 
     # -- setup -----------------------------------------------------------------
     def add_sequence(self, seq: int, k_rows=None, v_rows=None, prefill_tokens: int | None = None):
@@ -89,8 +119,8 @@ class PagedDecodeEngine:
     def free_sequence(self, seq: int) -> None:
         self.bm.free_seq(seq)
 
-    def _workspace_for(self, n: int, max_ctx: int):
-        need = N.pa_decode_workspace_bytes(self.pool, n, max_ctx, self.partition_tokens)
+    def _workspace_for(self, n: int, max_ctx: int, ptok: int):
+        need = N.pa_decode_workspace_bytes(self.pool, n, max_ctx, ptok)
         if need > self._ws_bytes:
             # Grow geometrically so that a growing context does not reallocate every step.
             self._ws_bytes = max(need, int(self._ws_bytes * 1.5))
@@ -112,7 +142,7 @@ class PagedDecodeEngine:
         st = self._staging[self._next]
         self._next = (self._next + 1) % len(self._staging)
         if st["event"] is not None:
-            st["event"].synchronize()         # the uploads that last read this buffer are done
+            st["event"].synchronize()         # the upload that last read this buffer is done
         _, pairs = self.bm.append_batch(seqs, slots_out=st["slots"], pairs_out=st["pairs"])
         npairs = int(pairs.shape[0])
         tables_np = st["tables"][:n]
@@ -127,25 +157,44 @@ class PagedDecodeEngine:
         self.last_slots = st["slots"][:n].copy()
 
         cur = torch.cuda.current_stream(self.device) if stream is None else stream
+        self._cur ^= 1
+        dv = self._dev[self._cur]
+        # Everything up to the end of this batch's table rows, in one upload.
+        upto = self._off_tables + 4 * n * self.cap if decode else self._off_tables
+        upto = -(-upto // 16) * 16
+        up = self._aux if self._aux is not None else cur
+        if dv["released"] is not None and up is not cur:
+            up.wait_event(dv["released"])     # no kernel still reads this device buffer
+        N.pa_stage_copy(dv["buf"], st["buf"], upto, stream=up)
+        uploaded = torch.cuda.Event()
+        uploaded.record(up)
+        st["event"] = uploaded
+        if up is not cur:
+            cur.wait_event(uploaded)
         with torch.cuda.stream(cur):
-            # One copy: everything up to the end of this batch's table rows.
-            upto = self._off_tables + 4 * n * self.cap if decode else self._off_tables
-            self._dev_stage[:upto].copy_(st["buf"][:upto], non_blocking=True)
-            ev = torch.cuda.Event()
-            ev.record(cur)
-            st["event"] = ev
             if npairs:
-                N.pa_copy_blocks(self.pool, self.pairs[:npairs], stream=cur)
-            N.pa_write_kv(self.pool, k_new, v_new, self.slots[:n], stream=cur)
+                N.pa_copy_blocks(self.pool, dv["pairs"][:npairs], stream=cur)
+            fused = decode and self.fuse_write
+            if not fused:
+                N.pa_write_kv(self.pool, k_new, v_new, dv["slots"][:n], stream=cur)
             if decode:
-                ws = self._workspace_for(n, max_ctx) if self.partition_tokens else None
+                ptok = self.partition_tokens
+                ws = self._workspace_for(n, max_ctx, ptok) if ptok else None
+                order = dv["order"][:n] if self.longest_first else None
                 if decode_events is not None:
                     decode_events[0].record(cur)
-                N.pa_decode(self.pool, q, out, self.tables[:n], self.ctx[:n], max_ctx,
-                            partition_tokens=self.partition_tokens, workspace=ws, stream=cur,
-                            seq_order=self.order[:n] if self.longest_first else None)
+                if fused:
+                    N.pa_write_decode(self.pool, k_new, v_new, dv["slots"][:n], q, out, dv["tables"][:n],
+                                      dv["ctx"][:n], max_ctx, partition_tokens=ptok, workspace=ws,
+                                      stream=cur, seq_order=order)
+                else:
+                    N.pa_decode(self.pool, q, out, dv["tables"][:n], dv["ctx"][:n], max_ctx,
+                                partition_tokens=ptok, workspace=ws, stream=cur, seq_order=order)
                 if decode_events is not None:
                     decode_events[1].record(cur)
+            done = torch.cuda.Event()
+            done.record(cur)
+            dv["released"] = done
 
     def decode(self, seqs, q, out, *, partition_tokens=None, stream=None, longest_first=None) -> None:
         """Decode the batch as it stands (no append): tables and contexts uploaded first."""
@@ -156,16 +205,20 @@ class PagedDecodeEngine:
         ptok = self.partition_tokens if partition_tokens is None else partition_tokens
         lf = self.longest_first if longest_first is None else longest_first
         cur = torch.cuda.current_stream(self.device) if stream is None else stream
+        dv = self._dev[self._cur]
         with torch.cuda.stream(cur):
-            self.tables[:n].copy_(torch.from_numpy(tables))
-            self.ctx[:n].copy_(torch.from_numpy(ctx))
+            dv["tables"][:n].copy_(torch.from_numpy(tables))
+            dv["ctx"][:n].copy_(torch.from_numpy(ctx))
             if lf:
-                self.order[:n].copy_(torch.from_numpy(np.argsort(-ctx, kind="stable").astype(np.int32)))
+                dv["order"][:n].copy_(torch.from_numpy(np.argsort(-ctx, kind="stable").astype(np.int32)))
             ws = None
             if ptok:
                 need = N.pa_decode_workspace_bytes(self.pool, n, max_ctx, ptok)
                 ws = torch.empty(need // 4 + 1, dtype=torch.float32, device=self.device)
-            N.pa_decode(self.pool, q, out, self.tables[:n], self.ctx[:n], max_ctx,
+            N.pa_decode(self.pool, q, out, dv["tables"][:n], dv["ctx"][:n], max_ctx,
                         partition_tokens=ptok, workspace=ws, stream=cur,
-                        seq_order=self.order[:n] if lf else None)
+                        seq_order=dv["order"][:n] if lf else None)
+            done = torch.cuda.Event()
+            done.record(cur)
+            dv["released"] = done
         self.last_ctx = ctx

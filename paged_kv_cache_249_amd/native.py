@@ -65,11 +65,14 @@ _SIGS = {
     "pa_decode": ([_vp, _vp, _i32, _vp, _vp, _i32, _vp, _i32, _i32, _f32, _i32, _vp, _i64, _vp], _i32),
     "pa_decode_ordered": ([_vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _f32, _i32, _vp, _i64, _vp],
                           _i32),
+    "pa_write_decode": ([_vp, _vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _f32, _i32,
+                         _vp, _i64, _vp], _i32),
     "pa_check_errors": ([_vp, _pi32], _i32),
     "pa_decode_contiguous": ([_vp, _vp, _i32, _i32, _i32, _i32, _vp, _i32, _vp, _vp, _vp, _i32, _f32, _i32,
                               _vp, _i64, _vp], _i32),
     "pa_stream_copy": ([_vp, _vp, _i64, _vp], _i32),
     "pa_stream_read": ([_vp, _i64, _vp, _vp], _i32),
+    "pa_stage_copy": ([_vp, _vp, _i64, _vp], _i32),
     "pa_bm_create": ([_i32, _i32, _vp, _i32, C.POINTER(_vp)], _i32),
     "pa_bm_destroy": ([_vp], _i32),
     "pa_bm_add_seq": ([_vp, _i64, _i32, _vp], _i32),
@@ -143,6 +146,7 @@ class Pool:
 
     def __init__(self, handle, num_blocks, block_size, num_heads, head_dim, kv_dtype,
                  k_cache, v_cache, k_scale, v_scale):
+        self._lib = lib
         self.handle = handle
         self.num_blocks = num_blocks
         self.block_size = block_size
@@ -153,8 +157,10 @@ class Pool:
         self.k_scale, self.v_scale = k_scale, v_scale
 
     def __del__(self):
-        if getattr(self, "handle", None):
-            lib.pa_free_pool(self.handle)
+        # Module globals may already be gone at interpreter shutdown: use the
+        # library reference the object kept.
+        if getattr(self, "handle", None) and getattr(self, "_lib", None) is not None:
+            self._lib.pa_free_pool(self.handle)
             self.handle = None
 
 
@@ -268,6 +274,30 @@ def pa_decode(pool: Pool, q, out, block_tables, context_lens, max_context_len: i
                                  ws_bytes, _stream(stream, q)), "pa_decode_ordered")
 
 
+def pa_write_decode(pool: Pool, k_new, v_new, slot_mapping, q, out, block_tables, context_lens,
+                    max_context_len: int, sm_scale: float = 0.0, partition_tokens: int = 0,
+                    workspace=None, stream=None, seq_order=None) -> None:
+    """pa_write_kv + pa_decode_ordered in one launch (float pools; row s = sequence s's newest token)."""
+    torch = _torch()
+    S = int(q.shape[0])
+    if tuple(q.shape) != (S, pool.num_heads, pool.head_dim) or out.shape != q.shape or out.dtype != q.dtype:
+        raise PagedKVError(PA_ERR_INVALID_ARG, "q/out shape or dtype mismatch")
+    if tuple(k_new.shape) != tuple(q.shape) or v_new.shape != k_new.shape or v_new.dtype != k_new.dtype:
+        raise PagedKVError(PA_ERR_INVALID_ARG, "new rows must be [S][heads][head_dim] like q")
+    if slot_mapping.numel() < S or block_tables.dim() != 2 or block_tables.shape[0] < S or \
+            context_lens.numel() < S or (seq_order is not None and seq_order.numel() < S):
+        raise PagedKVError(PA_ERR_INVALID_ARG, "slots/tables/contexts/order do not cover the batch")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.pa_write_decode(pool.handle, _ptr(k_new, "k_new"), _ptr(v_new, "v_new"), dtype_code(k_new.dtype),
+                               _ptr(slot_mapping, "slot_mapping", torch.int64), _ptr(q, "q"),
+                               dtype_code(q.dtype), _ptr(out, "out"),
+                               _ptr(block_tables, "block_tables", torch.int32), int(block_tables.shape[1]),
+                               _ptr(context_lens, "context_lens", torch.int32),
+                               _ptr(seq_order, "seq_order", torch.int32), S, int(max_context_len),
+                               float(sm_scale), int(partition_tokens), _ptr(workspace, "workspace"),
+                               ws_bytes, _stream(stream, q)), "pa_write_decode")
+
+
 def pa_decode_contiguous(k, v, q, out, context_lens, sm_scale: float = 0.0,
                          partition_tokens: int = 0, workspace=None, stream=None, seq_order=None) -> None:
     """Decode over a contiguous cache ``[S][heads][max_tokens][head_dim]`` (measurement twin)."""
@@ -308,6 +338,17 @@ def pa_stream_copy(dst, src, stream=None) -> None:
            "pa_stream_copy")
 
 
+def pa_stage_copy(dst, host_src, nbytes=None, stream=None) -> None:
+    """Copy pinned host ``host_src`` into device ``dst`` with a compute kernel."""
+    n = host_src.numel() * host_src.element_size() if nbytes is None else int(nbytes)
+    if host_src.is_cuda or not host_src.is_pinned():
+        raise PagedKVError(PA_ERR_INVALID_ARG, "host_src must be pinned host memory")
+    if dst.numel() * dst.element_size() < n or host_src.numel() * host_src.element_size() < n:
+        raise PagedKVError(PA_ERR_INVALID_ARG, "copy larger than a buffer")
+    _check(lib.pa_stage_copy(_ptr(dst, "dst"), _ptr(host_src, "host_src", device=False), n,
+                             _stream(stream, dst)), "pa_stage_copy")
+
+
 def pa_stream_read(src, sink, stream=None) -> None:
     """Read every byte of ``src`` once (bandwidth probe); ``sink`` >= 4096 bytes."""
     if sink.numel() * sink.element_size() < 4096:
@@ -335,13 +376,14 @@ class BlockManager:
                 raise PagedKVError(PA_ERR_INVALID_ARG, "free_order length != num_blocks")
         _check(lib.pa_bm_create(num_blocks, block_size, None if order is None else _np_ptr(order),
                                 window_blocks, C.byref(h)), "pa_bm_create")
+        self._lib = lib
         self.handle = h.value
         self.num_blocks = num_blocks
         self.block_size = block_size
 
     def __del__(self):
-        if getattr(self, "handle", None):
-            lib.pa_bm_destroy(self.handle)
+        if getattr(self, "handle", None) and getattr(self, "_lib", None) is not None:
+            self._lib.pa_bm_destroy(self.handle)
             self.handle = None
 
     def add_seq(self, seq: int, prefill_tokens: int) -> np.ndarray:

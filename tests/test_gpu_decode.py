@@ -278,3 +278,63 @@ def test_out_of_range_indices_are_flagged_not_followed():
     assert pk.pa_check_errors() & pk.PA_DEV_BAD_PAIR
     assert torch.equal(before, b.kd)
     assert pk.pa_check_errors() == 0
+
+
+@pytest.mark.parametrize("kv,src,D,ptok", [("f16", torch.float16, 128, 0), ("f16", torch.float32, 128, 64),
+                                           ("f32", torch.float32, 64, 0), ("f32", torch.float16, 64, 32),
+                                           ("f16", torch.float16, 64, 16)])
+def test_fused_write_decode_matches_write_then_decode(kv, src, D, ptok):
+    # pa_write_decode must leave the pool byte-identical to pa_write_kv and
+    # produce the same outputs as pa_write_kv followed by pa_decode.
+    pk = _pk()
+    ctx = [300, 47, 1024, 16, 1, 129, 513]
+    H = 4
+    a = Batch(ctx, H, D, kv, "f16", seed=66)
+    b = Batch(ctx, H, D, kv, "f16", seed=66)
+    S = len(ctx)
+    slots = np.array([a.tables[s][(c - 1) // 16] * 16 + (c - 1) % 16 for s, c in enumerate(ctx)], np.int64)
+    k_new = torch.from_numpy(W.normal_np((S, H, D), 66, 1) * 2).to(src).to(DEV)
+    v_new = torch.from_numpy(W.normal_np((S, H, D), 66, 2) * 2).to(src).to(DEV)
+    slots_d = torch.from_numpy(slots).to(DEV)
+    order = torch.from_numpy(np.argsort(-np.array(ctx), kind="stable").astype(np.int32)).to(DEV)
+    maxc = max(ctx)
+    ws = None
+    if ptok:
+        nb = pk.pa_decode_workspace_bytes(a.pool, S, maxc, ptok)
+        ws = torch.empty(nb // 4, dtype=torch.float32, device=DEV)
+    out_a = torch.empty_like(a.qd)
+    pk.pa_write_kv(a.pool, k_new, v_new, slots_d)
+    pk.pa_decode(a.pool, a.qd, out_a, a.tabd, a.ctxd, maxc, partition_tokens=ptok, workspace=ws, seq_order=order)
+    out_b = torch.empty_like(b.qd)
+    pk.pa_write_decode(b.pool, k_new, v_new, slots_d, b.qd, out_b, b.tabd, b.ctxd, maxc, partition_tokens=ptok,
+                       workspace=ws, seq_order=order)
+    torch.cuda.synchronize()
+    assert pk.pa_check_errors() == 0
+    assert torch.equal(a.kd.view(torch.uint8), b.kd.view(torch.uint8))
+    assert torch.equal(a.vd.view(torch.uint8), b.vd.view(torch.uint8))
+    assert torch.equal(out_a.view(torch.int16), out_b.view(torch.int16))
+    # And against the oracle, with the new rows written on the host side.
+    kp, vp = a.k_pool.copy(), a.v_pool.copy()
+    OC.write_kv(kp, vp, k_new.cpu().numpy(), v_new.cpu().numpy(), slots)
+    ref = OA.paged_decode(a.q, kp, vp, a.tables, ctx)
+    assert_close(out_b.cpu().numpy(), ref, F16_ATOL, F16_RTOL, f"fused {kv} {src} D={D} ptok={ptok}")
+
+
+def test_fused_write_rejects_a_slot_that_is_not_the_newest_token():
+    pk = _pk()
+    ctx = [40, 20]
+    b = Batch(ctx, 2, 64, "f16", "f16", seed=67)
+    before_k = b.kd.clone()
+    slots = torch.tensor([b.tables[0][0] * 16 + 3, -1], dtype=torch.int64, device=DEV)   # not token 39
+    rows = torch.ones((2, 2, 64), dtype=torch.float16, device=DEV)
+    out = torch.empty_like(b.qd)
+    pk.pa_write_decode(b.pool, rows, rows, slots, b.qd, out, b.tabd, b.ctxd, 40)
+    torch.cuda.synchronize()
+    assert pk.pa_check_errors() & pk.PA_DEV_BAD_SLOT
+    assert torch.equal(before_k, b.kd)                       # nothing written
+    assert_close(out.cpu().numpy(), b.oracle(), F16_ATOL, F16_RTOL, "decode unaffected")
+    c = Batch([5], 2, 64, "f16", "f16", seed=68)
+    i8 = pk.new_pool(4, 2, 64, pk.PA_I8, device=DEV)
+    with pytest.raises(pk.PagedKVError) as e:
+        pk.pa_write_decode(i8, rows[:1], rows[:1], slots[:1], c.qd, torch.empty_like(c.qd), c.tabd, c.ctxd, 5)
+    assert e.value.status == pk.PA_ERR_UNSUPPORTED
