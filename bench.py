@@ -67,7 +67,13 @@ PROFILE_CMDS = {
              "-- python bench.py --profile-run --steps 5 --warmup 3 > gpurun_out/prof_fetch.log",
     "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/prof_write -o write "
              "-- python bench.py --profile-run --steps 5 --warmup 3 > gpurun_out/prof_write.log",
+    "occupancy": "rocprofv3 --pmc OccupancyPercent LdsBankConflict SQ_INSTS_LDS SQ_WAVES --output-format csv "
+                 "-d gpurun_out/prof_occ -o occ -- python bench.py --profile-run --steps 5 --warmup 3 "
+                 "> gpurun_out/prof_occ.log",
+    "occupancy_level": "rocprofv3 --pmc MeanOccupancyPerCU --output-format csv -d gpurun_out/prof_level "
+                       "-o level -- python bench.py --profile-run --steps 5 --warmup 3 > gpurun_out/prof_level.log",
 }
+OCC_FILE = os.path.join(ROOT, "profiles", "decode_opt13b_occupancy_lds.txt")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_opt13b_hbm_traffic.txt")
 STATS_FILE = os.path.join(ROOT, "profiles", "decode_opt13b_kernel_stats.txt")
 DECODE_SOURCE = os.path.join(ROOT, "paged_kv_cache_249_amd", "csrc", "decode.hip")
@@ -152,6 +158,22 @@ def summarize_profiles(raw_dir: str) -> int:
         f.write("\n".join(out) + "\n")
     print(STATS_FILE)
     print(TRAFFIC_FILE)
+
+    # Occupancy and LDS bank conflicts of the decode kernel (two more passes).
+    if os.path.isdir(os.path.join(raw_dir, "prof_occ")) and os.path.isdir(os.path.join(raw_dir, "prof_level")):
+        occ = {c: per_kernel("prof_occ", c) for c in ("OccupancyPercent", "LdsBankConflict", "SQ_INSTS_LDS",
+                                                      "SQ_WAVES")}
+        occ["MeanOccupancyPerCU"] = per_kernel("prof_level", "MeanOccupancyPerCU")
+        lines = ["# Occupancy and LDS bank conflicts (rocprofv3 derived counters, mean per dispatch)", "",
+                 "commands:", "  " + PROFILE_CMDS["occupancy"], "  " + PROFILE_CMDS["occupancy_level"], "",
+                 "OccupancyPercent: resident wave-cycles as a percentage of the CU wave slots over the",
+                 "dispatch; MeanOccupancyPerCU: mean resident waves per CU; LdsBankConflict: bank",
+                 "conflict cycles per LDS access cycle.", ""]
+        for k in sorted(occ["OccupancyPercent"]):
+            lines.append(f"{k:<58} " + "  ".join(f"{c} {occ[c].get(k, float('nan')):.4g}" for c in occ))
+        with open(OCC_FILE, "w") as f:
+            f.write("\n".join(lines) + "\n")
+        print(OCC_FILE)
     return 0
 
 
@@ -170,19 +192,19 @@ def recorded_traffic():
 # CPU baseline: the oracle on a bounded sample (run in a child process so the
 # thread count is fixed before numpy loads).
 def cpu_baseline_child(seconds: float) -> None:
+    """Whole passes of the oracle over the 64-sequence batch until ``seconds``
+    of decode time are spent (setup — generation and the scatter into each
+    sequence's pool — is not timed)."""
     import numpy as np
     import workloads as W
     from oracle import attention as OA
     from oracle import cache_ops as OC
-    from oracle import paging as OP
     from oracle.block_manager import BlockManager
 
     wl = W.opt13b()
     H, D = wl.num_heads, wl.head_dim
     bm = BlockManager(wl.num_blocks, 16, free_order=W.free_order(wl.seed, wl.num_blocks))
-    done_bytes = 0
-    seqs = 0
-    spent = 0.0
+    batch = []
     for s, ctx in enumerate(wl.context_lens):
         K = W.normal_np((ctx, H, D), wl.seed, W.STREAM_K, s, dtype=np.float16)
         V = W.normal_np((ctx, H, D), wl.seed, W.STREAM_V, s, dtype=np.float16)
@@ -194,14 +216,20 @@ def cpu_baseline_child(seconds: float) -> None:
         table, _ = bm.table(s)
         local = {b: i for i, b in enumerate(table)}       # compact pool for this sequence
         OC.write_kv(kp, vp, K, V, [local[int(x) // 16] * 16 + int(x) % 16 for x in slots])
-        t0 = time.perf_counter()
-        OA.paged_decode(q, kp, vp, [list(range(nb))], [ctx])
-        spent += time.perf_counter() - t0
-        done_bytes += ctx * H * D * 2 * 2
-        seqs += 1
-        if spent >= seconds:
-            break
-    print(json.dumps({"seconds": spent, "bytes": done_bytes, "seqs": seqs}))
+        batch.append((q, kp, vp, nb, ctx))
+    done_bytes = 0
+    seqs = 0
+    passes = 0
+    spent = 0.0
+    while spent < seconds:
+        for q, kp, vp, nb, ctx in batch:
+            t0 = time.perf_counter()
+            OA.paged_decode(q, kp, vp, [list(range(nb))], [ctx])
+            spent += time.perf_counter() - t0
+            done_bytes += ctx * H * D * 2 * 2
+            seqs += 1
+        passes += 1
+    print(json.dumps({"seconds": spent, "bytes": done_bytes, "seqs": seqs, "passes": passes}))
 
 
 def cpu_baseline(seconds: float) -> dict:
@@ -215,9 +243,9 @@ def cpu_baseline(seconds: float) -> dict:
     d = json.loads(r.stdout.strip().splitlines()[-1])
     return {"value": round(d["bytes"] / d["seconds"] / 1e9, 4), "unit": "GB/s", "cores": 1,
             "kind": "oracle",
-            "sample": f"fp64 numpy oracle (gather through the block table + attention) over the first "
-                      f"{d['seqs']} of the 64 sequences, all 40 heads; {d['bytes'] / 1e6:.1f} MB of KV "
-                      f"in {d['seconds']:.2f} s on one thread",
+            "sample": f"fp64 numpy oracle (gather through the block table + attention), {d['passes']} "
+                      f"whole passes over the 64-sequence batch, all 40 heads: {d['bytes'] / 1e6:.1f} MB "
+                      f"of KV in {d['seconds']:.2f} s on one thread",
             "seqs_per_s": round(d["seqs"] / d["seconds"], 4)}
 
 
@@ -510,6 +538,7 @@ def extras(eng, wl, q, ptok, dev):
     res["paged_gbs"] = round(nbytes / t_paged / 1e9, 1)
     res["paged_vs_contiguous_overhead"] = round(t_paged / t_contig - 1.0, 4)
     del kc, vc
+    res["block_size_sweep"] = block_size_sweep(pk, W, torch, np, wl, ctx, q, out, order, t_contig, nbytes, dev)
     # Streaming copy probe: achievable HBM bandwidth (read + write bytes).
     n = 1 << 30
     a = torch.empty(n, dtype=torch.uint8, device=dev)
@@ -520,6 +549,41 @@ def extras(eng, wl, q, ptok, dev):
     sink = torch.zeros(1024, dtype=torch.int32, device=dev)
     t_read = _time_calls(lambda: pk.pa_stream_read(big, sink))
     res["stream_read_gbs"] = round(big.numel() / t_read / 1e9, 1)
+    return res
+
+
+def block_size_sweep(pk, W, torch, np, wl, ctx, q, out, order, t_contig, nbytes, dev):
+    """The same contexts in pools of 16-, 32- and 64-token blocks: decode rate
+    and overhead against the contiguous twin, the slots lost to partly filled
+    last blocks, and the cost of one copy-on-write block copy."""
+    S, H, D = wl.num_seqs, wl.num_heads, wl.head_dim
+    res = {}
+    for bs in pk.BLOCK_SIZES:
+        need = int(sum(-(-int(c) // bs) for c in ctx))
+        nb = -(-5 * need // 4)
+        bm = pk.BlockManager(nb, bs, free_order=W.free_order(wl.seed, nb))
+        for s, c in enumerate(ctx):
+            bm.add_seq(s, int(c))
+        cap = -(-int(ctx.max()) // bs)
+        tables, _ = bm.export(np.arange(S), cap)
+        pool = pk.new_pool(nb, H, D, pk.PA_F16, device=dev, block_size=bs)
+        pool.k_cache.normal_()
+        pool.v_cache.normal_()
+        tabd = torch.from_numpy(tables).to(dev)
+        ctxd = torch.from_numpy(ctx).to(dev)
+        maxc = int(ctx.max())
+        t = _time_calls(lambda: pk.pa_decode(pool, q, out, tabd, ctxd, maxc, seq_order=order))
+        pairs = torch.tensor([[0, 1]], dtype=torch.int32, device=dev)
+        t_cow = _time_calls(lambda: pk.pa_copy_blocks(pool, pairs))
+        slots = need * bs
+        res[str(bs)] = {"decode_gbs": round(nbytes / t / 1e9, 1),
+                        "overhead_vs_contiguous": round(t / t_contig - 1.0, 4),
+                        "table_entries": need,
+                        "unused_slot_fraction": round(1.0 - int(ctx.sum()) / slots, 4),
+                        "cow_copy_us": round(t_cow * 1e6, 2),
+                        "cow_copy_bytes": 2 * H * bs * D * 2}
+        del pool
+        torch.cuda.empty_cache()
     return res
 
 

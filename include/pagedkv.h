@@ -2,8 +2,9 @@
  * pagedkv.h — C ABI of the paged KV cache and paged decode attention library
  * for AMD Instinct MI355X (gfx950).
  *
- * The method: each sequence's KV cache is cut into fixed blocks of 16 tokens
- * that live anywhere in one shared physical pool; a per-sequence block table
+ * The method: each sequence's KV cache is cut into fixed blocks of tokens
+ * (16 by default; 32 and 64 are supported too) that live anywhere in one
+ * shared physical pool; a per-sequence block table
  * maps logical block -> physical block, and the attention of one new query
  * token per sequence reads its context through that table
  * ("PagedAttention — 把 KV cache 当虚拟内存页来管理", 是什么 and 实践案例 / 案例 2;
@@ -33,7 +34,12 @@
  *     block tables  int32 [num_seqs][max_blocks], logical order
  *     context lens  int32 [num_seqs]
  *     slot mapping  int64 [n], slot = physical_block * block_size + offset
- * - Supported geometry: block_size 16, head_dim 64 or 128, num_heads >= 1.
+ * - Supported geometry: block_size 16, 32 or 64, head_dim 64 or 128,
+ *   num_heads >= 1. Pages of 16, 32 or 64 tokens are the sizes "KV Cache与长上
+ *   下文管理" lists (the section on the second problem paging solves); the
+ *   study note "PagedAttention — 把 KV cache 当虚拟内存页来管理" (踩过的坑) calls
+ *   16 the default compromise between table-lookup and copy overhead and
+ *   fragmentation. A pool, its block manager and its tables share one size.
  *
  * The block manager (pa_bm_*) is host-only: it touches no device memory and
  * needs no GPU.
@@ -69,8 +75,8 @@ enum {
   PA_DEV_BAD_SLOT = 2,         /* a slot outside the pool                      */
   PA_DEV_BAD_PAIR = 4,         /* a copy pair outside the pool                 */
   PA_DEV_BAD_CONTEXT = 8,      /* context_lens[s] < 0 or > the stated maximum  */
-  PA_DEV_BAD_RUN = 16          /* int8 write: one block hit by more than 16 rows
-                                  of one run (duplicate slots)                 */
+  PA_DEV_BAD_RUN = 16          /* int8 write: one block hit by more than
+                                  block_size rows of one run (duplicate slots) */
 };
 
 /* Text of the last failing call on this thread ("" if none). Never NULL. */
@@ -92,7 +98,7 @@ typedef struct pa_pool pa_pool;
 /* Bytes the caller must allocate for one of K or V (*kv_bytes) and for one of
  * the int8 scale arrays (*scale_bytes, 0 unless kv_dtype == PA_I8).
  * Errors: PA_ERR_INVALID_ARG (null outputs, non-positive sizes),
- * PA_ERR_UNSUPPORTED (block_size != 16, head_dim not 64/128). */
+ * PA_ERR_UNSUPPORTED (block_size not 16/32/64, head_dim not 64/128). */
 pa_status pa_pool_bytes(int32_t num_blocks, int32_t block_size, int32_t num_heads,
                         int32_t head_dim, pa_dtype kv_dtype, int64_t* kv_bytes,
                         int64_t* scale_bytes);
@@ -153,25 +159,26 @@ pa_status pa_copy_blocks(pa_pool* pool, const int32_t* pairs, int32_t n, pa_stre
  * Paged decode attention.
  *
  * For each sequence s and head h, with ctx = context_lens[s] and
- * k_t = K[table[s][t / 16]][h][t % 16] (int8: code * scale[block][h]):
+ * k_t = K[table[s][t / B]][h][t % B] with B = the pool's block_size (int8:
+ * code * scale[block][h]):
  *     out[s][h] = sum_{t < ctx} softmax_t(q[s][h] . k_t * sm_scale) v_t
  * ("One Deep Concept #01", §2 Background: softmax(Q K^T / sqrt(d)) V; the
  * table indirection of "PagedAttention — 把 KV cache 当虚拟内存页来管理",
  * 实践案例 / 案例 2). Accumulation is fp32; out is stored in q_dtype (round to
  * nearest even for PA_F16). ctx == 0 gives zeros. Only the first
- * ceil(ctx / 16) table entries of a row are read; tokens at t >= ctx are
+ * ceil(ctx / B) table entries of a row are read; tokens at t >= ctx are
  * never used, whatever the pool holds there.
  *
  * q_dtype: PA_F32 or PA_F16 (q and out). sm_scale <= 0 selects 1/sqrt(head_dim).
  * partition_tokens == 0: one workgroup per (sequence, head) covers the whole
  * context (single pass; workspace may be NULL).
- * partition_tokens  > 0 (a multiple of 16): split-K. Every (sequence, head,
+ * partition_tokens  > 0 (a multiple of B): split-K. Every (sequence, head,
  * partition of partition_tokens tokens) is decoded on its own and writes its
  * partial (m, l, o) into workspace; a second kernel merges them by
  * log-sum-exp. Sequences with a single partition are written directly.
  * max_context_len bounds every context_lens[s] (larger values are clamped and
  * flagged with PA_DEV_BAD_CONTEXT); max_blocks is the row stride of
- * block_tables and must be >= ceil(max_context_len / 16).
+ * block_tables and must be >= ceil(max_context_len / B).
  * Errors: PA_ERR_INVALID_ARG (null pointers, bad sizes, workspace too small),
  * PA_ERR_UNSUPPORTED, PA_ERR_HIP.
  */
@@ -289,8 +296,10 @@ pa_status pa_stream_read(const void* src, int64_t bytes, void* sink, pa_stream s
  * ------------------------------------------------------------------------- */
 typedef struct pa_bm pa_bm;
 
-/* free_order: NULL or a permutation of [0, num_blocks) (host int32).
- * Errors: PA_ERR_INVALID_ARG (sizes, not a permutation), PA_ERR_UNSUPPORTED. */
+/* block_size: 16, 32 or 64 (the pool's). free_order: NULL or a permutation
+ * of [0, num_blocks) (host int32).
+ * Errors: PA_ERR_INVALID_ARG (sizes, not a permutation), PA_ERR_UNSUPPORTED
+ * (block size). */
 pa_status pa_bm_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order,
                        int32_t window_blocks, pa_bm** out);
 pa_status pa_bm_destroy(pa_bm* bm);

@@ -82,7 +82,7 @@ pa_status check_geometry(const char* fn, int32_t num_blocks, int32_t block_size,
     return fail(PA_ERR_INVALID_ARG, "%s: sizes must be positive (blocks=%d bs=%d heads=%d dim=%d)", fn,
                 num_blocks, block_size, num_heads, head_dim);
   if (!pa::geometry_supported(block_size, head_dim))
-    return fail(PA_ERR_UNSUPPORTED, "%s: block_size=%d head_dim=%d (supported: 16 and 64/128)", fn,
+    return fail(PA_ERR_UNSUPPORTED, "%s: block_size=%d head_dim=%d (supported: 16/32/64 and 64/128)", fn,
                 block_size, head_dim);
   if (kv_dtype != PA_F32 && kv_dtype != PA_F16 && kv_dtype != PA_I8)
     return fail(PA_ERR_UNSUPPORTED, "%s: kv dtype %d", fn, int(kv_dtype));
@@ -175,8 +175,9 @@ static int64_t workspace_bytes_for(int64_t S, int64_t H, int64_t D, int64_t P) {
 pa_status pa_decode_workspace_bytes(const pa_pool* pool, int32_t num_seqs, int32_t max_context_len,
                                     int32_t partition_tokens, int64_t* bytes) {
   if (!pool || !bytes) return fail(PA_ERR_INVALID_ARG, "pa_decode_workspace_bytes: NULL argument");
-  if (num_seqs < 0 || max_context_len < 0 || partition_tokens < 0 || partition_tokens % pa::kBlockSize)
-    return fail(PA_ERR_INVALID_ARG, "pa_decode_workspace_bytes: bad sizes");
+  if (num_seqs < 0 || max_context_len < 0 || partition_tokens < 0 || partition_tokens % pool->block_size)
+    return fail(PA_ERR_INVALID_ARG, "pa_decode_workspace_bytes: bad sizes (partition_tokens=%d, block_size=%d)",
+                partition_tokens, pool->block_size);
   *bytes = workspace_bytes_for(num_seqs, pool->num_heads, pool->head_dim,
                                num_partitions(max_context_len, partition_tokens));
   return PA_OK;
@@ -188,8 +189,9 @@ static pa_status decode_common(const char* fn, pa::DecodeArgs& a, void* workspac
   if (a.q_dtype != PA_F32 && a.q_dtype != PA_F16)
     return fail(PA_ERR_UNSUPPORTED, "%s: q dtype %d (F32 or F16)", fn, int(a.q_dtype));
   if (a.num_seqs < 0 || a.max_ctx < 0) return fail(PA_ERR_INVALID_ARG, "%s: negative size", fn);
-  if (a.partition_tokens < 0 || a.partition_tokens % pa::kBlockSize)
-    return fail(PA_ERR_INVALID_ARG, "%s: partition_tokens=%d (0 or a multiple of 16)", fn, a.partition_tokens);
+  if (a.partition_tokens < 0 || a.partition_tokens % a.block_size)
+    return fail(PA_ERR_INVALID_ARG, "%s: partition_tokens=%d (0 or a multiple of the block size %d)", fn,
+                a.partition_tokens, a.block_size);
   if (a.q_dtype == PA_F16 && !aligned16(a.q))
     return fail(PA_ERR_INVALID_ARG, "%s: fp16 q must be 16-byte aligned", fn);
   if (!(a.sm_scale > 0.f) || std::isinf(a.sm_scale)) a.sm_scale = 1.0f / std::sqrt(float(a.head_dim));
@@ -229,7 +231,7 @@ pa_status pa_decode_ordered(pa_pool* pool, const void* q, pa_dtype q_dtype, void
   if (!pool) return fail(PA_ERR_INVALID_ARG, "pa_decode: pool is NULL");
   if (!block_tables) return fail(PA_ERR_INVALID_ARG, "pa_decode: block_tables is NULL");
   if (max_context_len < 0 || max_blocks < 0 ||
-      int64_t(max_blocks) * pa::kBlockSize < int64_t(max_context_len))
+      int64_t(max_blocks) * pool->block_size < int64_t(max_context_len))
     return fail(PA_ERR_INVALID_ARG, "pa_decode: max_blocks=%d cannot hold max_context_len=%d", max_blocks,
                 max_context_len);
   pa::DecodeArgs a{};
@@ -243,6 +245,7 @@ pa_status pa_decode_ordered(pa_pool* pool, const void* q, pa_dtype q_dtype, void
   a.kv_dtype = pool->kv_dtype;
   a.tables = block_tables;
   a.max_blocks = max_blocks;
+  a.block_size = pool->block_size;
   a.max_tokens = 0;
   a.ctx = context_lens;
   a.order = seq_order;
@@ -272,7 +275,7 @@ pa_status pa_write_decode(pa_pool* pool, const void* k_new, const void* v_new, p
   if (!aligned16(k_new) || !aligned16(v_new))
     return fail(PA_ERR_INVALID_ARG, "pa_write_decode: new rows must be 16-byte aligned");
   if (!block_tables) return fail(PA_ERR_INVALID_ARG, "pa_write_decode: block_tables is NULL");
-  if (max_context_len < 0 || max_blocks < 0 || int64_t(max_blocks) * pa::kBlockSize < int64_t(max_context_len))
+  if (max_context_len < 0 || max_blocks < 0 || int64_t(max_blocks) * pool->block_size < int64_t(max_context_len))
     return fail(PA_ERR_INVALID_ARG, "pa_write_decode: max_blocks=%d cannot hold max_context_len=%d", max_blocks,
                 max_context_len);
   pa::DecodeArgs a{};
@@ -284,6 +287,7 @@ pa_status pa_write_decode(pa_pool* pool, const void* k_new, const void* v_new, p
   a.kv_dtype = pool->kv_dtype;
   a.tables = block_tables;
   a.max_blocks = max_blocks;
+  a.block_size = pool->block_size;
   a.ctx = context_lens;
   a.order = seq_order;
   a.num_seqs = num_seqs;
@@ -308,7 +312,7 @@ pa_status pa_decode_contiguous(const void* k, const void* v, pa_dtype kv_dtype, 
   if (!k || !v) return fail(PA_ERR_INVALID_ARG, "pa_decode_contiguous: NULL cache");
   if (kv_dtype != PA_F32 && kv_dtype != PA_F16)
     return fail(PA_ERR_UNSUPPORTED, "pa_decode_contiguous: float KV only");
-  if (num_heads <= 0 || max_tokens < 0 || max_tokens % pa::kBlockSize)
+  if (num_heads <= 0 || max_tokens < 0 || max_tokens % pa::kTileRows)
     return fail(PA_ERR_INVALID_ARG, "pa_decode_contiguous: heads=%d max_tokens=%d (a multiple of 16)",
                 num_heads, max_tokens);
   if (head_dim != 64 && head_dim != 128) return fail(PA_ERR_UNSUPPORTED, "pa_decode_contiguous: head_dim %d", head_dim);
@@ -321,6 +325,7 @@ pa_status pa_decode_contiguous(const void* k, const void* v, pa_dtype kv_dtype, 
   a.v = v;
   a.kv_dtype = kv_dtype;
   a.tables = nullptr;
+  a.block_size = pa::kTileRows;
   a.max_tokens = max_tokens;
   a.ctx = context_lens;
   a.order = seq_order;

@@ -157,8 +157,8 @@ pa_status pa_bm_create(int32_t num_blocks, int32_t block_size, const int32_t* fr
   if (num_blocks <= 0 || block_size <= 0 || window_blocks < 0)
     return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_create: num_blocks=%d block_size=%d window=%d",
                     num_blocks, block_size, window_blocks);
-  if (block_size != pa::kBlockSize)
-    return pa::fail(PA_ERR_UNSUPPORTED, "pa_bm_create: block_size %d (only 16)", block_size);
+  if (!pa::block_size_supported(block_size))
+    return pa::fail(PA_ERR_UNSUPPORTED, "pa_bm_create: block_size %d (16, 32 or 64)", block_size);
   pa_bm* bm = new (std::nothrow) pa_bm();
   if (!bm) return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_create: out of host memory");
   bm->num_blocks = num_blocks;

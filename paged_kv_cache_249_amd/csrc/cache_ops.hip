@@ -2,8 +2,8 @@
 // copy-on-write block copies, and a plain streaming copy.
 //
 // write_kv (reshape-and-cache): row i of the new K/V goes to slot
-// slots[i] = block * 16 + offset, the lookup of "PagedAttention — 把 KV cache
-// 当虚拟内存页来管理", 实践案例 / 案例 2. Writing new tokens into pages is also the
+// slots[i] = block * B + offset for a block size B of 16, 32 or 64, the
+// lookup of "PagedAttention — 把 KV cache 当虚拟内存页来管理", 实践案例 / 案例 2. Writing new tokens into pages is also the
 // only data movement of the sliding window ("KV Cache与长上下文管理", the section
 // on the second problem paging solves: the new token is written into the page
 // the oldest data occupied).
@@ -12,7 +12,7 @@
 // and V separately (FP16 -> INT8 compression is listed in "KV Cache与长上下文管理",
 // section 二.3, without a scheme; the group rule below is this library's and
 // is stated in pagedkv.h). One wave handles one run of adjacent slot entries
-// that hit the same block (at most 16 rows), for one head and one tensor.
+// that hit the same block (at most B rows), for one head and one tensor.
 //
 // copy_blocks: whole-block copies, the copy-on-write unit of the study note's
 // 实践案例 / 案例 3.
@@ -42,7 +42,7 @@ __global__ __launch_bounds__(kThreads) void write_kv_kernel(const SRC* __restric
                                                             DST* __restrict__ k_pool,
                                                             DST* __restrict__ v_pool,
                                                             const int64_t* __restrict__ slots, int n,
-                                                            int H, int num_blocks, int32_t* err) {
+                                                            int H, int num_blocks, int bshift, int32_t* err) {
   constexpr int kEPT = 16 / int(sizeof(DST));   // elements per thread
   constexpr int kCPR = D / kEPT;                // threads per (row, head)
   const int64_t idx = int64_t(blockIdx.x) * kThreads + threadIdx.x;
@@ -54,14 +54,14 @@ __global__ __launch_bounds__(kThreads) void write_kv_kernel(const SRC* __restric
   const int h = int(row % H);
   const int64_t slot = slots[i];
   if (slot < 0) return;
-  const int64_t blk = slot / kBlockSize;
-  const int off = int(slot % kBlockSize);
+  const int64_t blk = slot >> bshift;
+  const int off = int(slot & ((int64_t(1) << bshift) - 1));
   if (blk >= num_blocks) {
     flag_error(err, PA_DEV_BAD_SLOT);
     return;
   }
   const SRC* src = (blockIdx.y == 0 ? k_new : v_new) + row * D + chunk * kEPT;
-  DST* dst = (blockIdx.y == 0 ? k_pool : v_pool) + ((blk * H + h) * kBlockSize + off) * D + chunk * kEPT;
+  DST* dst = (blockIdx.y == 0 ? k_pool : v_pool) + (((blk * H + h) << bshift) + off) * D + chunk * kEPT;
   DST vals[kEPT];
 #pragma unroll
   for (int e = 0; e < kEPT; ++e) vals[e] = DST(ld_f(src + e));
@@ -74,8 +74,9 @@ template <typename SRC, int D>
 __global__ __launch_bounds__(kThreads) void write_kv_i8_kernel(
     const SRC* __restrict__ k_new, const SRC* __restrict__ v_new, int8_t* __restrict__ k_pool,
     int8_t* __restrict__ v_pool, _Float16* __restrict__ k_scale, _Float16* __restrict__ v_scale,
-    const int64_t* __restrict__ slots, int n, int H, int num_blocks, int32_t* err) {
+    const int64_t* __restrict__ slots, int n, int H, int num_blocks, int bshift, int32_t* err) {
   constexpr int kDPL = D / kWave;   // dims per lane
+  const int bs = 1 << bshift;
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t wid = int64_t(blockIdx.x) * (kThreads / kWave) + wave_uniform(threadIdx.x / kWave);
   if (wid >= int64_t(n) * H) return;
@@ -83,14 +84,14 @@ __global__ __launch_bounds__(kThreads) void write_kv_i8_kernel(
   const int h = int(wid % H);
   const int64_t slot = slots[i];
   if (slot < 0) return;
-  const int64_t blk = slot / kBlockSize;
+  const int64_t blk = slot >> bshift;
   if (blk >= num_blocks) {
     if (lane == 0) flag_error(err, PA_DEV_BAD_SLOT);
     return;
   }
   if (i > 0) {
     const int64_t prev = slots[i - 1];
-    if (prev >= 0 && prev / kBlockSize == blk) return;   // not the first row of its run
+    if (prev >= 0 && (prev >> bshift) == blk) return;   // not the first row of its run
   }
   const bool is_v = blockIdx.y != 0;
   const SRC* src = is_v ? v_new : k_new;
@@ -98,20 +99,20 @@ __global__ __launch_bounds__(kThreads) void write_kv_i8_kernel(
   _Float16* scale = is_v ? v_scale : k_scale;
 
   // The run: rows i .. i+R-1 hitting block blk.
-  uint32_t mask = 0;
+  uint64_t mask = 0;
   int R = 0;
   bool dup = false;
-  while (R < kBlockSize && i + R < n) {
+  while (R < bs && i + R < n) {
     const int64_t sl = slots[i + R];
-    if (sl < 0 || sl / kBlockSize != blk) break;
-    const uint32_t bit = 1u << int(sl % kBlockSize);
+    if (sl < 0 || (sl >> bshift) != blk) break;
+    const uint64_t bit = uint64_t(1) << int(sl & (bs - 1));
     dup |= (mask & bit) != 0;
     mask |= bit;
     ++R;
   }
-  if (i + R < n && R == kBlockSize) {
+  if (i + R < n && R == bs) {
     const int64_t sl = slots[i + R];
-    dup |= sl >= 0 && sl / kBlockSize == blk;
+    dup |= sl >= 0 && (sl >> bshift) == blk;
   }
   if (dup && lane == 0) flag_error(err, PA_DEV_BAD_RUN);
 
@@ -126,11 +127,11 @@ __global__ __launch_bounds__(kThreads) void write_kv_i8_kernel(
   const int64_t sidx = blk * H + h;
   const float s_old = (mask & 1u) ? 0.f : float(scale[sidx]);
   const float s = fmaxf(s_old, s_new);
-  int8_t* tile = pool + sidx * kBlockSize * D;
+  int8_t* tile = pool + (sidx << bshift) * D;
 
   if (s_old > 0.f && s > s_old) {
-    for (int o = 0; o < kBlockSize; ++o) {
-      if (mask & (1u << o)) continue;
+    for (int o = 0; o < bs; ++o) {
+      if (mask & (uint64_t(1) << o)) continue;
 #pragma unroll
       for (int e = 0; e < kDPL; ++e) {
         int8_t* c = tile + o * D + lane * kDPL + e;
@@ -140,7 +141,7 @@ __global__ __launch_bounds__(kThreads) void write_kv_i8_kernel(
     }
   }
   for (int r = 0; r < R; ++r) {
-    const int o = int(slots[i + r] % kBlockSize);
+    const int o = int(slots[i + r] & (bs - 1));
     const SRC* x = src + ((i + r) * H + h) * D + lane * kDPL;
 #pragma unroll
     for (int e = 0; e < kDPL; ++e) {
@@ -236,12 +237,12 @@ int launch_write_float(const pa_pool* p, const void* k_new, const void* v_new, c
     hipLaunchKernelGGL((write_kv_kernel<DST, SRC, 64>), grid, dim3(kThreads), 0, st,
                        static_cast<const SRC*>(k_new), static_cast<const SRC*>(v_new),
                        static_cast<DST*>(p->k_cache), static_cast<DST*>(p->v_cache), slots, n,
-                       p->num_heads, p->num_blocks, device_error_ptr());
+                       p->num_heads, p->num_blocks, block_shift(p->block_size), device_error_ptr());
   else
     hipLaunchKernelGGL((write_kv_kernel<DST, SRC, 128>), grid, dim3(kThreads), 0, st,
                        static_cast<const SRC*>(k_new), static_cast<const SRC*>(v_new),
                        static_cast<DST*>(p->k_cache), static_cast<DST*>(p->v_cache), slots, n,
-                       p->num_heads, p->num_blocks, device_error_ptr());
+                       p->num_heads, p->num_blocks, block_shift(p->block_size), device_error_ptr());
   return int(hipGetLastError());
 }
 
@@ -255,7 +256,7 @@ int launch_write_i8(const pa_pool* p, const void* k_new, const void* v_new, cons
                        static_cast<const SRC*>(v_new), static_cast<int8_t*>(p->k_cache),
                        static_cast<int8_t*>(p->v_cache), static_cast<_Float16*>(p->k_scale),
                        static_cast<_Float16*>(p->v_scale), slots, n, p->num_heads, p->num_blocks,
-                       device_error_ptr());
+                       block_shift(p->block_size), device_error_ptr());
   };
   if (p->head_dim == 64)
     args(write_kv_i8_kernel<SRC, 64>);
@@ -286,7 +287,7 @@ int launch_write_kv(const pa_pool* p, const void* k_new, const void* v_new, pa_d
 
 int launch_copy_blocks(const pa_pool* p, const int32_t* pairs, int32_t n, void* stream) {
   if (n == 0) return 0;
-  const int64_t block_bytes = int64_t(p->num_heads) * kBlockSize * p->head_dim * elem_bytes(p->kv_dtype);
+  const int64_t block_bytes = int64_t(p->num_heads) * p->block_size * p->head_dim * elem_bytes(p->kv_dtype);
   const dim3 grid(unsigned((block_bytes / 16 + kThreads - 1) / kThreads), unsigned(n), 2);
   hipLaunchKernelGGL(copy_blocks_kernel, grid, dim3(kThreads), 0, static_cast<hipStream_t>(stream), pairs,
                      n, static_cast<char*>(p->k_cache), static_cast<char*>(p->v_cache), block_bytes,

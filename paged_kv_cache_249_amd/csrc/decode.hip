@@ -4,25 +4,30 @@
 // the sequence's first ctx[s] tokens ("One Deep Concept #01 — PagedAttention:
 // From Operating System Virtual Memory to Large Language Model Memory
 // Systems", §2 Background), where token t lives in physical block
-// table[s][t / 16] at offset t % 16 ("PagedAttention — 把 KV cache 当虚拟内存页来
-// 管理", 实践案例 / 案例 2). Decode reads a lot and computes little (same note,
-// 学到什么), so the kernel is built around HBM streaming, not matrix cores.
+// table[s][t / B] at offset t % B ("PagedAttention — 把 KV cache 当虚拟内存页来
+// 管理", 实践案例 / 案例 2, with B = 16; the same pages list 32 and 64 as the
+// other common block sizes). Decode reads a lot and computes little (same
+// note, 学到什么), so the kernel is built around HBM streaming, not matrix cores.
+//
+// Units. One (block, head) tile is B rows of head_dim elements, contiguous in
+// the pool. The kernel walks every tile as B / 16 units of 16 rows, so one
+// code path serves all block sizes; unit u of a sequence lives in table entry
+// u / (B / 16), slice u % (B / 16) of that tile.
 //
 // Work decomposition. One workgroup (4 waves) per (sequence, head, partition).
-// A partition is a run of whole 16-token blocks; in single-pass mode it covers
-// the whole context. Inside the workgroup each wave owns whole blocks (block
-// j of the partition goes to wave j % 4) and keeps its own online-softmax
-// state, so the hot loop has no barriers.
+// A partition is a run of whole blocks; in single-pass mode it covers the
+// whole context. Inside the workgroup each wave owns whole units (unit j of
+// the partition goes to wave j % 4) and keeps its own online-softmax state,
+// so the hot loop has no barriers.
 //
-// Tile mapping. One (block, head) tile is 16 rows of head_dim elements,
-// contiguous in the pool. A wave reads it with NLD 16-byte loads per lane;
-// load i of lane l covers bytes [i*1024 + 16*l, +16) of the tile, so every
+// Tile mapping. A wave reads one 16-row unit with NLD 16-byte loads per lane;
+// load i of lane l covers bytes [i*1024 + 16*l, +16) of the unit, so every
 // load instruction moves 1 KiB contiguous. In bytes-per-row terms, the 16
 // rows split into groups of TPI = 64 / CPT rows per load, CPT lanes per row
 // (CPT = row bytes / 16). Lane l therefore always sees the same CPT-th slice
 // of head_dim (its "column", l % CPT) of rows i*TPI + l / CPT.
 //
-// Per block, per lane: the partial dot of its slice with q for each of its NLD
+// Per unit, per lane: the partial dot of its slice with q for each of its NLD
 // rows, summed over the CPT lanes of the row with DPP row operations (no LDS);
 // then an fp32 online-softmax update on the lane's own rows in base 2
 // (logits pre-multiplied by log2 e), and acc[e] += p * v for its slice. Lanes
@@ -30,7 +35,7 @@
 // which merges all (wave, row-group) streams of the workgroup through LDS with
 // the log-sum-exp identity.
 //
-// Masking: only the last block of a sequence can be partial. Rows at t >= ctx
+// Masking: only the last unit of a sequence can be partial. Rows at t >= ctx
 // get logit -inf and their raw K/V registers are zeroed before use, so stale
 // or NaN data in unused slots never reaches the result. A table entry outside
 // the pool flags the device error word and its block is treated as empty.
@@ -93,9 +98,9 @@ struct Geo {
   static constexpr int kRowBytes = D * int(sizeof(KV));
   static constexpr int kCPT = kRowBytes / 16;      // lanes per row
   static constexpr int kTPI = kWave / kCPT;        // rows per wave-wide load
-  static constexpr int kNLD = kBlockSize / kTPI;   // loads per lane per tile
+  static constexpr int kNLD = kTileRows / kTPI;    // loads per lane per unit
   static constexpr int kEPC = 16 / int(sizeof(KV));  // elements per lane per row
-  static constexpr int kTileBytes = kBlockSize * kRowBytes;
+  static constexpr int kTileBytes = kTileRows * kRowBytes;   // one 16-row unit
   static_assert(kCPT >= 4 && kCPT <= 32, "unsupported row size");
 };
 
@@ -115,7 +120,8 @@ struct Params {
   int32_t num_heads;
   int32_t num_blocks;
   int32_t max_ctx;
-  int32_t partition_blocks;
+  int32_t partition_units;  // 16-row units per partition
+  int32_t unit_shift;       // log2(block_size / 16)
   int32_t num_partitions;
   float scale_log2;
   float* ws_m;
@@ -290,20 +296,24 @@ void decode_kernel(Params p, const int32_t* __restrict__ tables, const int32_t* 
   const int grp = lane / CPT;
   const int col = lane % CPT;
   const int64_t sh = int64_t(s) * p.num_heads + h;
-  const int blk_begin = part * p.partition_blocks;
-  // This wave's blocks are first, first + 4, first + 8, ... (k-th at first + 4k).
-  const int first = blk_begin + wave;
+  const int ushift = p.unit_shift;
+  const int bshift = ushift + 4;                                  // log2(block size)
+  const int64_t head_stride = int64_t(G::kTileBytes) << ushift;   // one (block, head) tile
+  const int64_t block_stride = int64_t(p.num_heads) * head_stride;
+  const int unit_begin = part * p.partition_units;
+  // This wave's units are first, first + 4, first + 8, ... (k-th at first + 4k).
+  const int first = unit_begin + wave;
   const int32_t* trow = kPaged ? tables + int64_t(s) * p.max_blocks : nullptr;
-  const int64_t block_stride = int64_t(p.num_heads) * G::kTileBytes;
 
   // Loads that do not depend on the context length go out together with it:
-  // the wave's first two table entries (inside the row; unused if past the
-  // context) and its q slice. The first tile then waits for one round trip.
+  // the table entries of the wave's first two units (inside the row; unused
+  // if past the context) and its q slice. The first unit then waits for one
+  // round trip.
   int ctx = seq_ctx[s];
   int e0 = 0, e1 = 0;
   if constexpr (kPaged) {
-    e0 = first < p.max_blocks ? trow[first] : 0;
-    e1 = first + kWaves < p.max_blocks ? trow[first + kWaves] : 0;
+    e0 = (first >> ushift) < p.max_blocks ? trow[first >> ushift] : 0;
+    e1 = ((first + kWaves) >> ushift) < p.max_blocks ? trow[(first + kWaves) >> ushift] : 0;
   }
   QSlice<KV, QT, EPC> qs;
   qs.load(reinterpret_cast<const QT*>(p.q) + sh * D + col * EPC);
@@ -325,36 +335,38 @@ void decode_kernel(Params p, const int32_t* __restrict__ tables, const int32_t* 
 
   const bool bad_ctx = ctx < 0 || ctx > p.max_ctx;
   if (bad_ctx) ctx = ctx < 0 ? 0 : p.max_ctx;
-  const int nblk = (ctx + kBlockSize - 1) / kBlockSize;
-  const int seq_parts = nblk == 0 ? 1 : (nblk + p.partition_blocks - 1) / p.partition_blocks;
+  const int nunits = (ctx + kTileRows - 1) / kTileRows;
+  const int seq_parts = nunits == 0 ? 1 : (nunits + p.partition_units - 1) / p.partition_units;
   if (part >= seq_parts) return;
-  const int blk_end = min(blk_begin + p.partition_blocks, nblk);
-  const int iters = first < blk_end ? (blk_end - first + kWaves - 1) / kWaves : 0;
+  const int unit_end = min(unit_begin + p.partition_units, nunits);
+  const int iters = first < unit_end ? (unit_end - first + kWaves - 1) / kWaves : 0;
 
-  // Table entry of the wave's k-th block. Reads are wave-uniform and the loop
+  // Table entry of the wave's k-th unit. Reads are wave-uniform and the loop
   // stores nothing, so they go through the scalar cache and are counted apart
   // from the vector loads: each is issued half an iteration before it is used.
   auto entry = [&](int k) -> int {
     if constexpr (kPaged) {
-      return trow[first + kWaves * k];
+      return trow[(first + kWaves * k) >> ushift];
     } else {
       return 0;
     }
   };
-  // Byte offset of the tile of (block b, head h); *ok is false for a table
-  // entry outside the pool (the tile is then read from block 0 and masked).
+  // Byte offset of unit b of head h (its table entry is phys); *ok is false
+  // for an entry outside the pool (the unit is then read from block 0 and
+  // masked).
   auto tile_offset = [&](int b, int phys, bool* ok) -> int64_t {
     if constexpr (kPaged) {
       *ok = unsigned(phys) < unsigned(p.num_blocks);
-      return (*ok ? int64_t(phys) : 0) * block_stride + int64_t(h) * G::kTileBytes;
+      return (*ok ? int64_t(phys) : 0) * block_stride + int64_t(h) * head_stride +
+             int64_t(b & ((1 << ushift) - 1)) * G::kTileBytes;
     } else {
       *ok = true;
-      return (sh * p.max_tokens + int64_t(b) * kBlockSize) * G::kRowBytes;
+      return (sh * p.max_tokens + int64_t(b) * kTileRows) * G::kRowBytes;
     }
   };
-  // A tile is read through a buffer resource built per tile (uniform base in
+  // A unit is read through a buffer resource built per unit (uniform base in
   // SGPRs, loop-invariant lane offset): no 64-bit vector address arithmetic in
-  // the loop, and the hardware clamps any access outside the tile to zero.
+  // the loop, and the hardware clamps any access outside the unit to zero.
   auto load_tile = [&](const char* base, int64_t off, uint4 (&r)[NLD]) {
     const __amdgpu_buffer_rsrc_t rs =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base + off), 0, G::kTileBytes, kRsrcWord3);
@@ -369,7 +381,7 @@ void decode_kernel(Params p, const int32_t* __restrict__ tables, const int32_t* 
     bool ok;
     float kscale, vscale;
   };
-  // Issue the loads of the wave's k-th tile (table entry phys) into (kr, vr).
+  // Issue the loads of the wave's k-th unit (table entry phys) into (kr, vr).
   auto fetch = [&](int k, int phys, uint4 (&kr)[NLD], uint4 (&vr)[NLD]) -> TileRef {
     TileRef t;
     t.b = first + k * kWaves;
@@ -398,20 +410,21 @@ void decode_kernel(Params p, const int32_t* __restrict__ tables, const int32_t* 
   bool bad_entry = false;
 
   // Fused write of the sequence's new token: the owning wave's lanes that
-  // hold row new_off of the last tile patch the new row into the tile's
-  // registers when that tile comes (if its physical block is the slot's),
+  // hold row new_row of the last unit patch the new row into the unit's
+  // registers when that unit comes (if its physical block is the slot's),
   // and store the row after the loop.
-  int new_off = -1;
+  int new_row = -1;
   bool patched = false, bad_slot = false;
   int64_t new_dst = 0;
   uint4 nk = make_uint4(0u, 0u, 0u, 0u), nv = nk;
+  const int64_t in_block = (int64_t(1) << bshift) - 1;   // offset mask inside a block
   if constexpr (kFusable) {
     if (new_slots != nullptr && new_slot >= 0) {
-      const bool owner = blk_end == nblk && nblk > 0 && wave == (nblk - 1 - blk_begin) % kWaves;
-      if (nblk == 0 || int(new_slot % kBlockSize) != (ctx - 1) % kBlockSize) {
+      const bool owner = unit_end == nunits && nunits > 0 && wave == (nunits - 1 - unit_begin) % kWaves;
+      if (nunits == 0 || (new_slot & in_block) != ((ctx - 1) & in_block)) {
         bad_slot = part == 0 && wave == 0;       // reported once per (sequence, head)
       } else if (owner) {
-        new_off = int(new_slot % kBlockSize);
+        new_row = (ctx - 1) % kTileRows;
       }
     }
   }
@@ -419,7 +432,7 @@ void decode_kernel(Params p, const int32_t* __restrict__ tables, const int32_t* 
   // loads so their latencies overlap).
   auto convert_new_row = [&]() {
     if constexpr (kFusable) {
-      if (new_off >= 0) {
+      if (new_row >= 0) {
         KV kv_k[EPC], kv_v[EPC];
 #pragma unroll
         for (int e = 0; e < EPC; ++e) {
@@ -432,18 +445,18 @@ void decode_kernel(Params p, const int32_t* __restrict__ tables, const int32_t* 
     }
   };
 
-  // Online-softmax update with one tile.
+  // Online-softmax update with one unit.
   auto process = [&](const TileRef& t, uint4 (&kr)[NLD], uint4 (&vr)[NLD]) {
     bad_entry |= !t.ok;
-    const int t0 = t.b * kBlockSize;
-    if (new_off >= 0 && t.b == nblk - 1) {
-      if (t.ok && int64_t(t.phys) == new_slot / kBlockSize) {
+    const int t0 = t.b * kTileRows;
+    if (new_row >= 0 && t.b == nunits - 1) {
+      if (t.ok && int64_t(t.phys) == (new_slot >> bshift)) {
         patched = true;
-        new_dst = int64_t(t.phys) * block_stride + int64_t(h) * G::kTileBytes +
-                  int64_t(new_off) * G::kRowBytes + col * 16;
+        new_dst = int64_t(t.phys) * block_stride + int64_t(h) * head_stride +
+                  (new_slot & in_block) * G::kRowBytes + col * 16;
 #pragma unroll
         for (int i = 0; i < NLD; ++i) {
-          if (i == new_off / TPI && grp == new_off % TPI) {
+          if (i == new_row / TPI && grp == new_row % TPI) {
             kr[i] = nk;
             vr[i] = nv;
           }
@@ -455,7 +468,7 @@ void decode_kernel(Params p, const int32_t* __restrict__ tables, const int32_t* 
     float sc[NLD];
 #pragma unroll
     for (int i = 0; i < NLD; ++i) sc[i] = group_sum<CPT>(dot16(kr[i], qs)) * (t.kscale * p.scale_log2);
-    if (t0 + kBlockSize > ctx || !t.ok) {
+    if (t0 + kTileRows > ctx || !t.ok) {
 #pragma unroll
       for (int i = 0; i < NLD; ++i) {
         if (!t.ok || t0 + i * TPI + grp >= ctx) {
@@ -485,7 +498,11 @@ void decode_kernel(Params p, const int32_t* __restrict__ tables, const int32_t* 
   // always issued before the current tile is used, so every wait leaves one
   // tile in flight; the last one or two tiles are peeled off so that no load
   // is issued that nothing consumes.
-  if (PA_DECODE_PREFETCH == 0) {
+  // Double buffering holds 4 * NLD 16-byte registers of tiles per lane; with
+  // 8 loads per unit (fp32 rows of 128) that would spill, and 8 loads per
+  // lane already keep enough bytes in flight, so those run single-buffered.
+  constexpr bool kDouble = PA_DECODE_PREFETCH != 0 && NLD <= 4;
+  if (!kDouble) {
     convert_new_row();
     int e = e0;
     for (int k = 0; k < iters; ++k) {
@@ -520,7 +537,7 @@ void decode_kernel(Params p, const int32_t* __restrict__ tables, const int32_t* 
     }
   }
 
-  if (patched && grp == new_off % TPI) {
+  if (patched && grp == new_row % TPI) {
     *reinterpret_cast<uint4*>(const_cast<char*>(p.k) + new_dst) = nk;
     *reinterpret_cast<uint4*>(const_cast<char*>(p.v) + new_dst) = nv;
   }
@@ -574,8 +591,8 @@ __global__ __launch_bounds__(D) void reduce_kernel(Params p) {
   const int s = sh / p.num_heads;
   int ctx = p.ctx[s];
   ctx = ctx < 0 ? 0 : (ctx > p.max_ctx ? p.max_ctx : ctx);
-  const int nblk = (ctx + kBlockSize - 1) / kBlockSize;
-  const int parts = nblk == 0 ? 1 : (nblk + p.partition_blocks - 1) / p.partition_blocks;
+  const int nunits = (ctx + kTileRows - 1) / kTileRows;
+  const int parts = nunits == 0 ? 1 : (nunits + p.partition_units - 1) / p.partition_units;
   if (parts <= 1) return;
   const float* m = p.ws_m + int64_t(sh) * p.num_partitions;
   const float* l = p.ws_l + int64_t(sh) * p.num_partitions;
@@ -655,8 +672,9 @@ int launch_decode(const DecodeArgs& a, void* stream) {
   p.num_blocks = a.num_blocks;
   p.max_ctx = a.max_ctx;
   // Single pass: one partition large enough for any context.
-  p.partition_blocks = a.partition_tokens > 0 ? a.partition_tokens / kBlockSize
-                                               : (a.max_ctx + kBlockSize - 1) / kBlockSize + 1;
+  p.partition_units = a.partition_tokens > 0 ? a.partition_tokens / kTileRows
+                                              : (a.max_ctx + kTileRows - 1) / kTileRows + 1;
+  p.unit_shift = block_shift(a.block_size) - 4;
   p.num_partitions = a.num_partitions;
   p.scale_log2 = a.sm_scale * kLog2e;
   p.ws_m = a.ws_m;

@@ -21,7 +21,18 @@ struct pa_pool {
 
 namespace pa {
 
-constexpr int kBlockSize = 16;
+// Rows a decode wave loads as one unit: a 16-row slice of a (block, head)
+// tile. Blocks of 32 or 64 tokens are 2 or 4 such slices, contiguous.
+constexpr int kTileRows = 16;
+
+inline bool block_size_supported(int32_t block_size) {
+  return block_size == 16 || block_size == 32 || block_size == 64;
+}
+
+// log2(block_size) for a supported block size.
+inline int block_shift(int32_t block_size) {
+  return block_size == 16 ? 4 : block_size == 32 ? 5 : 6;
+}
 
 // Records the message of a failing call for pa_last_error() and returns st.
 pa_status fail(pa_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
@@ -32,7 +43,7 @@ inline int64_t elem_bytes(pa_dtype t) {
 }
 
 inline bool geometry_supported(int32_t block_size, int32_t head_dim) {
-  return block_size == kBlockSize && (head_dim == 64 || head_dim == 128);
+  return block_size_supported(block_size) && (head_dim == 64 || head_dim == 128);
 }
 
 // Kernel launchers (decode.hip, cache_ops.hip). Arguments are validated by the
@@ -49,6 +60,7 @@ struct DecodeArgs {
   pa_dtype kv_dtype;
   const int32_t* tables;  // nullptr => contiguous layout
   int32_t max_blocks;     // table row stride
+  int32_t block_size;     // tokens per block (16 for the contiguous layout)
   int64_t max_tokens;     // contiguous layout: tokens per (seq, head) row
   const int32_t* ctx;
   const int32_t* order;   // optional schedule (permutation of the batch), may be null

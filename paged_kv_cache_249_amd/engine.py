@@ -33,12 +33,14 @@ class PagedDecodeEngine:
                  max_seqs: int, max_blocks_per_seq: int, *, window_blocks: int = 0,
                  free_order=None, device="cuda", partition_tokens: int = 0,
                  pool_fill=None, staging_depth: int = 3, longest_first: bool = True,
-                 overlap_uploads: bool = False, fuse_write: bool = True):
+                 overlap_uploads: bool = False, fuse_write: bool = True, block_size: int = N.BLOCK_SIZE):
         self.device = torch.device(device)
         self.num_heads, self.head_dim = num_heads, head_dim
         self.kv_dtype = kv_dtype
-        self.pool = N.new_pool(num_blocks, num_heads, head_dim, kv_dtype, device=self.device, fill=pool_fill)
-        self.bm = N.BlockManager(num_blocks, N.BLOCK_SIZE, free_order=free_order, window_blocks=window_blocks)
+        self.block_size = block_size
+        self.pool = N.new_pool(num_blocks, num_heads, head_dim, kv_dtype, device=self.device, fill=pool_fill,
+                               block_size=block_size)
+        self.bm = N.BlockManager(num_blocks, block_size, free_order=free_order, window_blocks=window_blocks)
         self.max_seqs = max_seqs
         self.cap = max_blocks_per_seq
         self.partition_tokens = partition_tokens

@@ -34,7 +34,8 @@ PA_DEV_BAD_PAIR = 4
 PA_DEV_BAD_CONTEXT = 8
 PA_DEV_BAD_RUN = 16
 
-BLOCK_SIZE = 16
+BLOCK_SIZE = 16                      # the default; pools and managers also take 32 and 64
+BLOCK_SIZES = (16, 32, 64)
 
 
 class PagedKVError(RuntimeError):
@@ -173,7 +174,7 @@ def pa_pool_bytes(num_blocks: int, block_size: int, num_heads: int, head_dim: in
 
 def pa_alloc_pool(num_blocks, block_size, num_heads, head_dim, kv_dtype, k_cache, v_cache,
                   k_scale=None, v_scale=None) -> Pool:
-    """Bind caller-owned tensors (``[num_blocks][heads][16][head_dim]``) as a pool."""
+    """Bind caller-owned tensors (``[num_blocks][heads][block_size][head_dim]``) as a pool."""
     kvb, scb = pa_pool_bytes(num_blocks, block_size, num_heads, head_dim, kv_dtype)
     for name, t, nb in (("k_cache", k_cache, kvb), ("v_cache", v_cache, kvb),
                         ("k_scale", k_scale, scb), ("v_scale", v_scale, scb)):

@@ -41,12 +41,18 @@ def test_pool_bytes():
     assert kv == 64 * 8 * 16 * 64 * 4 and sc == 0
     kv, sc = pk.pa_pool_bytes(10, 16, 32, 128, pk.PA_I8)
     assert kv == 10 * 32 * 16 * 128 and sc == 10 * 32 * 2
+    for bs in (32, 64):
+        kv, sc = pk.pa_pool_bytes(10, bs, 40, 128, pk.PA_F16)
+        assert kv == 10 * 40 * bs * 128 * 2 and sc == 0
+        kv, sc = pk.pa_pool_bytes(10, bs, 32, 128, pk.PA_I8)
+        assert kv == 10 * 32 * bs * 128 and sc == 10 * 32 * 2
 
 
 @pytest.mark.parametrize("args,status", [
     ((0, 16, 8, 64, 1), -1),
     ((4, 16, 0, 64, 1), -1),
-    ((4, 32, 8, 64, 1), -2),
+    ((4, 48, 8, 64, 1), -2),
+    ((4, 128, 8, 64, 1), -2),
     ((4, 16, 8, 96, 1), -2),
     ((4, 16, 8, 64, 7), -2),
 ])
@@ -115,6 +121,20 @@ def test_device_calls_validate_before_launching():
                            None) == pk.PA_ERR_INVALID_ARG
         # unsupported q dtype
         assert L.pa_decode(h, q, pk.PA_I8, out, tab, 8, ctx, 4, 100, 0.0, 0, None, 0, None) == pk.PA_ERR_UNSUPPORTED
+        # A 64-token pool: partitions are whole blocks, tables hold ceil(ctx / 64).
+        h64 = C.c_void_p()
+        assert L.pa_alloc_pool(8, 64, 2, 64, pk.PA_F16, p(0x10000000), p(0x10100000), None, None,
+                               C.byref(h64)) == 0
+        try:
+            assert L.pa_decode(h64, q, pk.PA_F16, out, tab, 2, ctx, 4, 128, 0.0, 32, ws, 1 << 20,
+                               None) == pk.PA_ERR_INVALID_ARG
+            assert L.pa_decode_workspace_bytes(h64, 4, 100, 32, C.byref(need)) == pk.PA_ERR_INVALID_ARG
+            assert L.pa_decode_workspace_bytes(h64, 4, 100, 64, C.byref(need)) == 0
+            assert need.value == 4 * 2 * 2 * (2 + 64) * 4
+            assert L.pa_decode(h64, q, pk.PA_F16, out, tab, 1, ctx, 4, 65, 0.0, 0, None, 0,
+                               None) == pk.PA_ERR_INVALID_ARG
+        finally:
+            L.pa_free_pool(h64)
         # num_seqs == 0 launches nothing and succeeds.
         assert L.pa_decode(h, q, pk.PA_F16, out, tab, 8, ctx, 0, 100, 0.0, 0, None, 0, None) == 0
         # Single pass needs no workspace.

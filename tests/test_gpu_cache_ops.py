@@ -22,11 +22,11 @@ def _bytes(t):
     return t.detach().cpu().contiguous().view(torch.uint8).numpy().reshape(-1)
 
 
-def _random_pool(pk, NB, H, D, code, seed):
+def _random_pool(pk, NB, H, D, code, seed, bs=16):
     """Pool tensors filled with random bits (stale data) and their host copies."""
     g = torch.Generator(device="cpu").manual_seed(seed)
     dt = pk.torch_dtype(code)
-    nbytes = NB * H * 16 * D * torch.empty(0, dtype=dt).element_size()
+    nbytes = NB * H * bs * D * torch.empty(0, dtype=dt).element_size()
     raw_k = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, generator=g)
     raw_v = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, generator=g)
     if code == pk.PA_F16:
@@ -36,65 +36,68 @@ def _random_pool(pk, NB, H, D, code, seed):
     if code == pk.PA_F32:
         raw_k.view(torch.int32).bitwise_and_(0x3effffff)
         raw_v.view(torch.int32).bitwise_and_(0x3effffff)
-    k = raw_k.view(dt).view(NB, H, 16, D).to(DEV)
-    v = raw_v.view(dt).view(NB, H, 16, D).to(DEV)
+    k = raw_k.view(dt).view(NB, H, bs, D).to(DEV)
+    v = raw_v.view(dt).view(NB, H, bs, D).to(DEV)
     ks = vs = None
     if code == pk.PA_I8:
         ks = (torch.rand((NB, H), generator=g) * 0.05).to(torch.float16).to(DEV)
         vs = (torch.rand((NB, H), generator=g) * 0.05).to(torch.float16).to(DEV)
-    pool = pk.pa_alloc_pool(NB, 16, H, D, code, k, v, ks, vs)
+    pool = pk.pa_alloc_pool(NB, bs, H, D, code, k, v, ks, vs)
     host = [k.cpu().numpy().copy(), v.cpu().numpy().copy()]
     if ks is not None:
         host += [ks.cpu().numpy().copy(), vs.cpu().numpy().copy()]
     return pool, host
 
 
-@pytest.mark.parametrize("pool_code,src_dtype,D", [
-    ("f32", torch.float32, 64), ("f16", torch.float16, 128), ("f16", torch.float32, 128),
-    ("f32", torch.float16, 128), ("f16", torch.float16, 64)])
-def test_write_kv_float_bit_exact(pool_code, src_dtype, D):
+@pytest.mark.parametrize("pool_code,src_dtype,D,bs", [
+    ("f32", torch.float32, 64, 16), ("f16", torch.float16, 128, 16), ("f16", torch.float32, 128, 16),
+    ("f32", torch.float16, 128, 16), ("f16", torch.float16, 64, 16), ("f16", torch.float16, 128, 32),
+    ("f16", torch.float32, 128, 64), ("f32", torch.float16, 64, 64)])
+def test_write_kv_float_bit_exact(pool_code, src_dtype, D, bs):
     pk = _pk()
     code = {"f32": pk.PA_F32, "f16": pk.PA_F16}[pool_code]
     NB, H, n = 37, 5, 203
-    pool, (hk, hv) = _random_pool(pk, NB, H, D, code, 1)
+    pool, (hk, hv) = _random_pool(pk, NB, H, D, code, 1, bs)
     rng = W.rng(31, D)
-    slots = rng.permutation(NB * 16)[:n].astype(np.int64)
+    slots = rng.permutation(NB * bs)[:n].astype(np.int64)
     slots[::17] = -1                                     # some rows are skipped
     k_new = torch.from_numpy(W.normal_np((n, H, D), 31, 1, D) * 3).to(src_dtype)
     v_new = torch.from_numpy(W.normal_np((n, H, D), 31, 2, D) * 3).to(src_dtype)
-    print(f"write_kv {pool_code} src={src_dtype} D={D} n={n}", flush=True)
+    print(f"write_kv {pool_code} src={src_dtype} D={D} n={n} bs={bs}", flush=True)
     pk.pa_write_kv(pool, k_new.to(DEV), v_new.to(DEV), torch.from_numpy(slots).to(DEV))
     torch.cuda.synchronize()
-    OC.write_kv(hk, hv, k_new.numpy(), v_new.numpy(), slots)
+    OC.write_kv(hk, hv, k_new.numpy(), v_new.numpy(), slots, block_size=bs)
     assert np.array_equal(_bytes(pool.k_cache), hk.view(np.uint8).reshape(-1))
     assert np.array_equal(_bytes(pool.v_cache), hv.view(np.uint8).reshape(-1))
     assert pk.pa_check_errors() == 0
 
 
-def _int8_case(pk, D, src_dtype, seed):
+def _int8_case(pk, D, src_dtype, seed, bs=16):
     NB, H = 24, 3
-    pool, host = _random_pool(pk, NB, H, D, pk.PA_I8, seed)
+    pool, host = _random_pool(pk, NB, H, D, pk.PA_I8, seed, bs)
     rng = W.rng(seed, 5)
     return pool, host, rng, NB, H
 
 
-@pytest.mark.parametrize("D,src_dtype", [(128, torch.float32), (64, torch.float16), (128, torch.float16)])
-def test_write_kv_int8_bit_exact(D, src_dtype):
+@pytest.mark.parametrize("D,src_dtype,bs", [(128, torch.float32, 16), (64, torch.float16, 16),
+                                            (128, torch.float16, 16), (128, torch.float16, 32),
+                                            (64, torch.float32, 64)])
+def test_write_kv_int8_bit_exact(D, src_dtype, bs):
     pk = _pk()
-    pool, (hk, hv, hks, hvs), rng, NB, H = _int8_case(pk, D, src_dtype, 7)
+    pool, (hk, hv, hks, hvs), rng, NB, H = _int8_case(pk, D, src_dtype, 7, bs)
     order = rng.permutation(NB)
     # Three sequences: prefill (whole and partial blocks, one call each), then
     # one-token decode calls; magnitudes grow now and then to force the
     # re-coding of rows already in a block.
-    seqs = [(order[0:4], 50), (order[4:8], 16), (order[8:12], 7)]
+    seqs = [(order[0:4], 50 * bs // 16), (order[4:8], bs), (order[8:12], 7)]
     lens = []
     calls = []
     for table, plen in seqs:
-        slots = np.array([table[t // 16] * 16 + t % 16 for t in range(plen)], np.int64)
+        slots = np.array([table[t // bs] * bs + t % bs for t in range(plen)], np.int64)
         calls.append(slots)
         lens.append(plen)
     for step in range(12):
-        calls.append(np.array([tb[(lens[i] + 0) // 16] * 16 + lens[i] % 16 for i, (tb, _) in enumerate(seqs)],
+        calls.append(np.array([tb[lens[i] // bs] * bs + lens[i] % bs for i, (tb, _) in enumerate(seqs)],
                               np.int64))
         lens = [x + 1 for x in lens]
     for ci, slots in enumerate(calls):
@@ -102,9 +105,9 @@ def test_write_kv_int8_bit_exact(D, src_dtype):
         amp = 1.0 + (3.0 if ci % 4 == 3 else 0.0) + 0.1 * ci
         k_new = torch.from_numpy(W.normal_np((n, H, D), 7, 10 + ci) * amp).to(src_dtype)
         v_new = torch.from_numpy(W.normal_np((n, H, D), 7, 100 + ci) * amp).to(src_dtype)
-        print(f"int8 write call {ci} n={n} D={D}", flush=True)
+        print(f"int8 write call {ci} n={n} D={D} bs={bs}", flush=True)
         pk.pa_write_kv(pool, k_new.to(DEV), v_new.to(DEV), torch.from_numpy(slots).to(DEV))
-        OC.write_kv_int8(hk, hks, hv, hvs, k_new.float().numpy(), v_new.float().numpy(), slots)
+        OC.write_kv_int8(hk, hks, hv, hvs, k_new.float().numpy(), v_new.float().numpy(), slots, block_size=bs)
     torch.cuda.synchronize()
     assert np.array_equal(pool.k_scale.cpu().numpy().view(np.uint16), hks.view(np.uint16))
     assert np.array_equal(pool.v_scale.cpu().numpy().view(np.uint16), hvs.view(np.uint16))
@@ -113,16 +116,17 @@ def test_write_kv_int8_bit_exact(D, src_dtype):
     assert pk.pa_check_errors() == 0
 
 
-@pytest.mark.parametrize("code,D", [("f16", 128), ("i8", 128), ("f32", 64)])
-def test_copy_blocks_bit_exact(code, D):
+@pytest.mark.parametrize("code,D,bs", [("f16", 128, 16), ("i8", 128, 16), ("f32", 64, 16), ("f16", 128, 64),
+                                       ("i8", 64, 32)])
+def test_copy_blocks_bit_exact(code, D, bs):
     pk = _pk()
     c = {"f32": pk.PA_F32, "f16": pk.PA_F16, "i8": pk.PA_I8}[code]
     NB, H = 50, 40 if D == 128 else 8
-    pool, host = _random_pool(pk, NB, H, D, c, 3)
+    pool, host = _random_pool(pk, NB, H, D, c, 3, bs)
     rng = W.rng(33, 0)
     perm = rng.permutation(NB)
     pairs = np.stack([perm[:24], perm[24:48]], axis=1).astype(np.int32)   # disjoint src / dst
-    print(f"copy_blocks {code} D={D} pairs={len(pairs)}", flush=True)
+    print(f"copy_blocks {code} D={D} bs={bs} pairs={len(pairs)}", flush=True)
     pk.pa_copy_blocks(pool, torch.from_numpy(pairs).to(DEV))
     torch.cuda.synchronize()
     OC.copy_blocks(host, pairs)

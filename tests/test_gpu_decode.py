@@ -39,16 +39,16 @@ class Batch:
     """A batch laid out through the oracle's own paging (tables from a seeded
     permutation) and mirrored into device buffers."""
 
-    def __init__(self, ctx, H, D, kv="f16", q="f16", seed=0, num_blocks=None, poison=False):
+    def __init__(self, ctx, H, D, kv="f16", q="f16", seed=0, num_blocks=None, poison=False, bs=16):
         pk = _pk()
         self.ctx = list(ctx)
-        self.H, self.D = H, D
-        need = sum(-(-c // 16) for c in ctx)
+        self.H, self.D, self.bs = H, D, bs
+        need = sum(-(-c // bs) for c in ctx)
         self.NB = num_blocks or need + 7
         order = W.free_order(seed, self.NB)
         self.tables, used = [], 0
         for c in ctx:
-            nb = -(-c // 16)
+            nb = -(-c // bs)
             self.tables.append(order[used:used + nb])
             used += nb
         self.max_blocks = max(1, max(len(t) for t in self.tables))
@@ -59,17 +59,17 @@ class Batch:
         np_kv = {"f32": np.float32, "f16": np.float16}[kv]
         np_q = {"f32": np.float32, "f16": np.float16}[q]
         fill = np.nan if poison else 0.0
-        self.k_pool = np.full((self.NB, H, 16, D), fill, np_kv)
-        self.v_pool = np.full((self.NB, H, 16, D), fill, np_kv)
+        self.k_pool = np.full((self.NB, H, bs, D), fill, np_kv)
+        self.v_pool = np.full((self.NB, H, bs, D), fill, np_kv)
         for s, c in enumerate(ctx):
             K = W.normal_np((c, H, D), seed, W.STREAM_K, s, dtype=np_kv)
             V = W.normal_np((c, H, D), seed, W.STREAM_V, s, dtype=np_kv)
-            OC.write_kv(self.k_pool, self.v_pool, K, V, OP.slots(c, self.tables[s]))
+            OC.write_kv(self.k_pool, self.v_pool, K, V, OP.slots(c, self.tables[s], bs), block_size=bs)
         self.q = W.normal_np((len(ctx), H, D), seed, W.STREAM_Q, dtype=np_q)
         code = {"f32": pk.PA_F32, "f16": pk.PA_F16}[kv]
         self.kd = torch.from_numpy(self.k_pool).to(DEV)
         self.vd = torch.from_numpy(self.v_pool).to(DEV)
-        self.pool = pk.pa_alloc_pool(self.NB, 16, H, D, code, self.kd, self.vd)
+        self.pool = pk.pa_alloc_pool(self.NB, bs, H, D, code, self.kd, self.vd)
         self.qd = torch.from_numpy(self.q).to(DEV)
         self.tabd = torch.from_numpy(tab).to(DEV)
         self.ctxd = torch.tensor(ctx, dtype=torch.int32, device=DEV)
@@ -89,7 +89,7 @@ class Batch:
         return out.cpu().numpy(), ws
 
     def oracle(self):
-        return OA.paged_decode(self.q, self.k_pool, self.v_pool, self.tables, self.ctx)
+        return OA.paged_decode(self.q, self.k_pool, self.v_pool, self.tables, self.ctx, block_size=self.bs)
 
 
 @pytest.mark.parametrize("ptok", [0, 16, 32, 64])
@@ -338,3 +338,96 @@ def test_fused_write_rejects_a_slot_that_is_not_the_newest_token():
     with pytest.raises(pk.PagedKVError) as e:
         pk.pa_write_decode(i8, rows[:1], rows[:1], slots[:1], c.qd, torch.empty_like(c.qd), c.tabd, c.ctxd, 5)
     assert e.value.status == pk.PA_ERR_UNSUPPORTED
+
+
+# ---------------------------------------------------------------------------
+# Block sizes 32 and 64: the same kernels walk each block as 16-row units.
+
+@pytest.mark.parametrize("bs", [32, 64])
+@pytest.mark.parametrize("D", [64, 128])
+def test_block_size_ragged_edges(bs, D):
+    print(f"block size {bs} edges D={D}", flush=True)
+    b = Batch(EDGE_CTX, 6, D, "f16", "f16", seed=80 + D + bs, bs=bs)
+    ref = b.oracle()
+    for ptok in (0, bs, 4 * bs, 512):
+        got, _ = b.gpu(ptok)
+        assert_close(got, ref, F16_ATOL, F16_RTOL, f"bs={bs} D={D} ptok={ptok}")
+
+
+@pytest.mark.parametrize("bs", [32, 64])
+@pytest.mark.parametrize("kv,q,D", [("f32", "f32", 128), ("f32", "f16", 64), ("f16", "f32", 128)])
+def test_block_size_dtype_combinations(bs, kv, q, D):
+    print(f"block size {bs} dtypes kv={kv} q={q} D={D}", flush=True)
+    b = Batch([5, 47, 300, 129, 64], 4, D, kv, q, seed=81, bs=bs)
+    ref = b.oracle()
+    for ptok in (0, 2 * bs):
+        got, _ = b.gpu(ptok)
+        atol, rtol = (F32_ATOL, F32_RTOL) if (kv, q) == ("f32", "f32") else (F16_ATOL, F16_RTOL)
+        if q == "f32" and kv == "f16":
+            atol, rtol = 1e-4, 1e-4
+        assert_close(got, ref, atol, rtol, f"bs={bs} {kv}/{q}/{D} ptok={ptok}")
+
+
+@pytest.mark.parametrize("bs", [32, 64])
+def test_block_size_poison_and_permutation(bs):
+    # Unused slots hold NaN and physical blocks are relabelled: outputs stay
+    # bit-identical to the clean, unpermuted pool's.
+    ctx = [17, 33, 50, 100, 1, 255, 64]
+    clean = Batch(ctx, 8, 128, "f16", "f16", seed=82, bs=bs)
+    dirty = Batch(ctx, 8, 128, "f16", "f16", seed=82, poison=True, bs=bs)
+    perm = W.relabel(82, dirty.NB)
+    k2 = np.empty_like(dirty.k_pool)
+    v2 = np.empty_like(dirty.v_pool)
+    k2[perm] = dirty.k_pool
+    v2[perm] = dirty.v_pool
+    dirty.kd.copy_(torch.from_numpy(k2))
+    dirty.vd.copy_(torch.from_numpy(v2))
+    tab2 = torch.from_numpy(np.where(dirty.tab >= 0, perm[np.maximum(dirty.tab, 0)], -1).astype(np.int32)).to(DEV)
+    for ptok in (0, bs):
+        a, _ = clean.gpu(ptok)
+        c, _ = dirty.gpu(ptok, tab2)
+        assert np.array_equal(a.view(np.uint16), c.view(np.uint16)), f"bs={bs} ptok={ptok}"
+
+
+@pytest.mark.parametrize("bs,kv,src,ptok", [(32, "f16", torch.float16, 0), (64, "f16", torch.float32, 128),
+                                            (64, "f32", torch.float16, 0)])
+def test_block_size_fused_write_decode(bs, kv, src, ptok):
+    pk = _pk()
+    ctx = [300, 47, 1024, 16, 1, 129, 513, 64]
+    H, D = 4, 128
+    a = Batch(ctx, H, D, kv, "f16", seed=83, bs=bs)
+    b = Batch(ctx, H, D, kv, "f16", seed=83, bs=bs)
+    S = len(ctx)
+    slots = np.array([a.tables[s][(c - 1) // bs] * bs + (c - 1) % bs for s, c in enumerate(ctx)], np.int64)
+    k_new = torch.from_numpy(W.normal_np((S, H, D), 83, 1) * 2).to(src).to(DEV)
+    v_new = torch.from_numpy(W.normal_np((S, H, D), 83, 2) * 2).to(src).to(DEV)
+    slots_d = torch.from_numpy(slots).to(DEV)
+    maxc = max(ctx)
+    ws = None
+    if ptok:
+        nb = pk.pa_decode_workspace_bytes(a.pool, S, maxc, ptok)
+        ws = torch.empty(nb // 4, dtype=torch.float32, device=DEV)
+    out_a = torch.empty_like(a.qd)
+    pk.pa_write_kv(a.pool, k_new, v_new, slots_d)
+    pk.pa_decode(a.pool, a.qd, out_a, a.tabd, a.ctxd, maxc, partition_tokens=ptok, workspace=ws)
+    out_b = torch.empty_like(b.qd)
+    pk.pa_write_decode(b.pool, k_new, v_new, slots_d, b.qd, out_b, b.tabd, b.ctxd, maxc, partition_tokens=ptok,
+                       workspace=ws)
+    torch.cuda.synchronize()
+    assert pk.pa_check_errors() == 0
+    assert torch.equal(a.kd.view(torch.uint8), b.kd.view(torch.uint8))
+    assert torch.equal(a.vd.view(torch.uint8), b.vd.view(torch.uint8))
+    assert torch.equal(out_a.view(torch.int16), out_b.view(torch.int16))
+    kp, vp = a.k_pool.copy(), a.v_pool.copy()
+    OC.write_kv(kp, vp, k_new.cpu().numpy(), v_new.cpu().numpy(), slots, block_size=bs)
+    assert np.array_equal(a.kd.cpu().numpy().view(np.uint8), kp.view(np.uint8))
+    ref = OA.paged_decode(a.q, kp, vp, a.tables, ctx, block_size=bs)
+    assert_close(out_b.cpu().numpy(), ref, F16_ATOL, F16_RTOL, f"fused bs={bs} {kv} {src} ptok={ptok}")
+
+
+def test_block_size_rejects_partitions_that_split_a_block():
+    pk = _pk()
+    b = Batch([100, 40], 2, 64, "f16", "f16", seed=84, bs=64)
+    with pytest.raises(pk.PagedKVError) as e:
+        b.gpu(32)
+    assert e.value.status == pk.PA_ERR_INVALID_ARG

@@ -213,3 +213,34 @@ def test_kv_bytes_per_token_matches_the_note(load_golden):
     assert abs(per_request - g["printed_gb_per_2048_tokens_approx"]) < 0.05
     # One layer of the OPT-13B shape (40 heads x 128 = 5120) keeps 20,480 B per token.
     assert C.kv_bytes_per_token(1, 40 * 128, 2) == 20_480
+
+
+@pytest.mark.parametrize("bs", [16, 32, 64])
+def test_paged_decode_at_any_block_size_equals_contiguous_attention(bs):
+    # Pages of 16, 32 or 64 tokens only change where rows live: scattered
+    # through random tables into a pool whose other slots hold NaN, every
+    # sequence must give exactly the attention over its contiguous rows.
+    rng = W.rng(13, bs)
+    H, D, NB = 2, 8, 12
+    ctxs = [1, bs - 1, bs, bs + 1, 3 * bs - 5]
+    perm = rng.permutation(NB)
+    kp = np.full((NB, H, bs, D), np.nan)
+    vp = np.full((NB, H, bs, D), np.nan)
+    tables, ks, vs, used = [], [], [], 0
+    for ctx in ctxs:
+        nb = -(-ctx // bs)
+        table = perm[used:used + nb]
+        used += nb
+        K = rng.standard_normal((ctx, H, D))
+        V = rng.standard_normal((ctx, H, D))
+        C.write_kv(kp, vp, K, V, P.slots(ctx, table, bs), block_size=bs)
+        tables.append(table)
+        ks.append(K)
+        vs.append(V)
+    q = rng.standard_normal((len(ctxs), H, D))
+    out = A.paged_decode(q, kp, vp, tables, ctxs, block_size=bs)
+    for s in range(len(ctxs)):
+        np.testing.assert_array_equal(out[s], A.attend(q[s], ks[s], vs[s], A.default_scale(D)))
+    # The written slots are exactly the table's blocks at offsets t % bs.
+    t = ctxs[-1] - 1
+    assert P.slot(t, tables[-1], bs) == tables[-1][t // bs] * bs + t % bs
