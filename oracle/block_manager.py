@@ -33,6 +33,19 @@ Readings of what the pages leave open (this project's choices):
   count drops by one and a fresh block comes from the free list. The table row
   stays in logical order (front dropped, id pushed to the back). The live
   context is ``tokens appended - block_size * blocks evicted``.
+* Swapping ("KV Cache与长上下文管理", the fourth point: only a paged cache can
+  swap page by page, cold pages to host memory and back on demand, instead of
+  moving a whole contiguous cache). The unit here is one sequence's live
+  blocks: ``swap_out`` gives each of them a block of a host pool (a FIFO free
+  list of its own, ascending ids unless an order is given), in logical order,
+  and returns the ``(device, host)`` copy pairs; a device block that no one
+  else holds returns to the device free list (tail, logical order), a shared
+  one only loses a count, so the sequences still holding it are untouched.
+  ``swap_in`` takes one device block per host block from the device free list
+  and returns the ``(host, device)`` pairs; the host blocks return to the tail
+  of the host free list. Blocks shared before a swap-out come back as private
+  copies. A swapped-out sequence cannot append, fork or be exported for decode;
+  freeing it returns its host blocks.
 * Every call is atomic: on error nothing changes.
 """
 
@@ -69,6 +82,7 @@ class _Seq:
     table: list = field(default_factory=list)   # live physical blocks, logical order
     tokens: int = 0                              # tokens appended in total
     evicted: int = 0                             # blocks dropped by the ring
+    swapped: bool = False                        # table holds host-pool block ids
 
 
 class BlockManager:
@@ -85,6 +99,8 @@ class BlockManager:
         self.free = deque(order)
         self.ref = [0] * num_blocks
         self.seqs: dict[int, _Seq] = {}
+        self.num_host_blocks = 0
+        self.host_free: deque = deque()
 
     # -- queries -------------------------------------------------------------
     def num_free(self) -> int:
@@ -108,7 +124,7 @@ class BlockManager:
         rows = np.full((len(seqs), cap), -1, dtype=np.int32)
         ctx = np.zeros(len(seqs), dtype=np.int32)
         for i, s in enumerate(seqs):
-            st = self._get(s)
+            st = self._resident(s)
             if len(st.table) > cap:
                 raise OutOfRange("table row longer than cap")
         for i, s in enumerate(seqs):
@@ -142,7 +158,7 @@ class BlockManager:
 
     def fork(self, parent: int, child: int) -> None:
         """``child`` shares every block of ``parent`` (each count rises by one)."""
-        p = self._get(parent)
+        p = self._resident(parent)
         if child in self.seqs:
             raise StateError("child exists")
         for b in p.table:
@@ -154,7 +170,7 @@ class BlockManager:
 
         ``copy_src``/``copy_dst`` are -1 when no block has to be copied first.
         """
-        st = self._get(seq)
+        st = self._resident(seq)
         bs = self.block_size
         offset = st.tokens % bs
         src = dst = -1
@@ -194,14 +210,77 @@ class BlockManager:
 
     def free_seq(self, seq: int) -> None:
         st = self._get(seq)
+        if st.swapped:
+            self.host_free.extend(st.table)
+        else:
+            for b in st.table:
+                self.ref[b] -= 1
+                if self.ref[b] == 0:
+                    self.free.append(b)
+        del self.seqs[seq]
+
+    # -- swapping ------------------------------------------------------------
+    def set_host_blocks(self, num_host_blocks: int, free_order=None) -> None:
+        """Give the manager a host pool of ``num_host_blocks`` blocks (once)."""
+        if self.num_host_blocks:
+            raise StateError("host pool already set")
+        if num_host_blocks <= 0:
+            raise InvalidArg("host pool size")
+        order = list(range(num_host_blocks)) if free_order is None else [int(b) for b in free_order]
+        if sorted(order) != list(range(num_host_blocks)):
+            raise InvalidArg("host free order must be a permutation of the host pool")
+        self.num_host_blocks = num_host_blocks
+        self.host_free = deque(order)
+
+    def num_host_free(self) -> int:
+        return len(self.host_free)
+
+    def is_swapped(self, seq: int) -> bool:
+        return self._get(seq).swapped
+
+    def swap_out(self, seq: int):
+        """Move ``seq``'s live blocks to the host pool; returns ``[(device, host)]``."""
+        st = self._resident(seq)
+        if not self.num_host_blocks:
+            raise StateError("no host pool")
+        if len(st.table) > len(self.host_free):
+            raise OutOfBlocks("host pool exhausted")
+        pairs = []
         for b in st.table:
+            hb = self.host_free.popleft()
+            pairs.append((b, hb))
             self.ref[b] -= 1
             if self.ref[b] == 0:
                 self.free.append(b)
-        del self.seqs[seq]
+        st.table = [hb for _, hb in pairs]
+        st.swapped = True
+        return pairs
+
+    def swap_in(self, seq: int):
+        """Bring ``seq``'s blocks back into the device pool; returns ``[(host, device)]``."""
+        st = self._get(seq)
+        if not st.swapped:
+            raise StateError("sequence is resident")
+        if len(st.table) > len(self.free):
+            raise OutOfBlocks("pool exhausted")
+        pairs = []
+        for hb in st.table:
+            b = self.free.popleft()
+            self.ref[b] = 1
+            pairs.append((hb, b))
+            self.host_free.append(hb)
+        st.table = [b for _, b in pairs]
+        st.swapped = False
+        return pairs
 
     # -- helpers -------------------------------------------------------------
     def _get(self, seq: int) -> _Seq:
         if seq not in self.seqs:
             raise StateError("unknown sequence")
         return self.seqs[seq]
+
+    def _resident(self, seq: int) -> _Seq:
+        st = self._get(seq)
+        if st.swapped:
+            raise StateError("sequence is swapped out")
+        return st

@@ -10,6 +10,9 @@ Pool layout used throughout: ``pool[block][head][offset][dim]``; a slot is
   rounded to nearest even into the pool dtype. Negative slots are skipped.
 * :func:`copy_blocks` — copy-on-write copies whole blocks: the note's 案例 3
   says the copy unit is one block, not the whole prompt.
+* :func:`swap_blocks` — swapping moves whole blocks between the device pool
+  and a host pool of the same per-block layout ("KV Cache与长上下文管理", the
+  fourth point on what paging makes possible: page-by-page swap in and out).
 * :func:`write_kv_int8` — FP16 -> INT8 cache compression is listed by "KV
   Cache与长上下文管理" (section 二.3 and its summary list) without a scheme. The
   scheme here is this project's reading: symmetric int8 codes in [-127, 127]
@@ -57,6 +60,24 @@ def copy_blocks(pools, pairs) -> None:
     for src, dst in np.asarray(pairs, dtype=np.int64).reshape(-1, 2):
         for p in pools:
             p[dst] = p[src].copy()
+
+
+def swap_blocks(device_pools, host_pools, pairs, direction: str) -> None:
+    """Copy whole blocks between two pools of the same per-block layout.
+
+    ``direction == "out"``: ``host[h] = device[d]`` for every ``(d, h)``;
+    ``direction == "in"``: ``device[d] = host[h]`` for every ``(h, d)``.
+    ``device_pools`` / ``host_pools`` are matching lists (K, V and, for int8,
+    the two scale arrays) whose first axis is the block id.
+    """
+    if direction not in ("out", "in"):
+        raise ValueError(direction)
+    for a, b in np.asarray(pairs, dtype=np.int64).reshape(-1, 2):
+        for dp, hp in zip(device_pools, host_pools):
+            if direction == "out":
+                hp[b] = dp[a].copy()
+            else:
+                dp[b] = hp[a].copy()
 
 
 def _quantise_group(codes: np.ndarray, scales: np.ndarray, b: int, h: int,

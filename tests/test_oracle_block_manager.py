@@ -115,7 +115,11 @@ def test_ring_with_a_shared_oldest_block_takes_a_fresh_one():
 
 def _invariants(bm: BlockManager):
     refs = [0] * bm.num_blocks
+    host_held = []
     for st in bm.seqs.values():
+        if st.swapped:
+            host_held += st.table
+            continue
         for b in st.table:
             refs[b] += 1
     assert refs == bm.ref
@@ -123,26 +127,35 @@ def _invariants(bm: BlockManager):
     used = {b for b in range(bm.num_blocks) if bm.ref[b] > 0}
     assert len(free) == len(bm.free)
     assert free.isdisjoint(used) and free | used == set(range(bm.num_blocks))
+    # Host blocks: each held by exactly one swapped sequence, or free.
+    assert len(set(host_held)) == len(host_held)
+    assert len(set(bm.host_free)) == len(bm.host_free)
+    assert set(host_held).isdisjoint(bm.host_free)
+    assert set(host_held) | set(bm.host_free) == set(range(bm.num_host_blocks))
 
 
+@pytest.mark.parametrize("bs", [16, 32])
 @pytest.mark.parametrize("seed", range(6))
-def test_random_operation_sequences_keep_the_invariants(seed):
+def test_random_operation_sequences_keep_the_invariants(seed, bs):
     rng = W.rng(seed, 77)
     window = int(rng.integers(0, 2)) * int(rng.integers(2, 6))
-    bm = BlockManager(48, 16, free_order=W.free_order(seed, 48), window_blocks=window)
+    bm = BlockManager(48, bs, free_order=W.free_order(seed, 48), window_blocks=window)
+    bm.set_host_blocks(40, W.free_order(seed + 100, 40))
     content = {}          # slot -> token id written there (models the pool)
+    host = {}             # host slot -> token id (models the host pool)
     owner_tokens = {}     # seq -> list of token ids in logical order
     next_id = 0
     serial = 0            # unique id of every appended token
-    live = []
+    live = []             # resident sequences
+    swapped = []
     for _ in range(600):
-        op = rng.integers(0, 10)
+        op = rng.integers(0, 12)
         try:
             if op == 0 or not live:
                 s = next_id
                 n = int(rng.integers(0, 40))
                 if window:
-                    n = min(n, window * 16)
+                    n = min(n, window * bs)
                 slots = bm.add_seq(s, n)
                 ids = list(range(next_id * 1000, next_id * 1000 + n))
                 for sl, tid in zip(slots, ids):
@@ -161,6 +174,36 @@ def test_random_operation_sequences_keep_the_invariants(seed):
                 s = live.pop(int(rng.integers(len(live))))
                 bm.free_seq(s)
                 del owner_tokens[s]
+            elif op == 10:
+                s = live[int(rng.integers(len(live)))]
+                pairs = bm.swap_out(s)
+                for d, h in pairs:                      # the copy the pairs ask for
+                    for o in range(bs):
+                        host.pop(h * bs + o, None)
+                        if d * bs + o in content:
+                            host[h * bs + o] = content[d * bs + o]
+                live.remove(s)
+                swapped.append(s)
+                with pytest.raises(StateError):
+                    bm.append(s)
+                with pytest.raises(StateError):
+                    bm.export([s], 64)
+            elif op == 11 and swapped:
+                s = swapped[int(rng.integers(len(swapped)))]
+                pairs = bm.swap_in(s)
+                for h, d in pairs:
+                    # A device block taken for a swap-in was free: no live sequence reads it.
+                    assert bm.ref[d] == 1
+                    for o in range(bs):
+                        content.pop(d * bs + o, None)
+                        if h * bs + o in host:
+                            content[d * bs + o] = host[h * bs + o]
+                swapped.remove(s)
+                live.append(s)
+            elif op == 9 and swapped:
+                s = swapped.pop(int(rng.integers(len(swapped))))
+                bm.free_seq(s)
+                del owner_tokens[s]
             else:
                 s = live[int(rng.integers(len(live)))]
                 shared_before = {b: bm.ref[b] for b in range(bm.num_blocks)}
@@ -168,11 +211,11 @@ def test_random_operation_sequences_keep_the_invariants(seed):
                 if src >= 0:
                     # Copy-on-write only when the block was shared.
                     assert shared_before[src] > 1
-                    for o in range(16):
-                        if src * 16 + o in content:
-                            content[dst * 16 + o] = content[src * 16 + o]
+                    for o in range(bs):
+                        if src * bs + o in content:
+                            content[dst * bs + o] = content[src * bs + o]
                 # The block written into is never shared at write time.
-                assert bm.ref[slot // 16] == 1
+                assert bm.ref[slot // bs] == 1
                 tid = 10 ** 9 + serial
                 serial += 1
                 content[slot] = tid
@@ -184,8 +227,12 @@ def test_random_operation_sequences_keep_the_invariants(seed):
         for s in live:
             row, ctx = bm.table(s)
             toks = owner_tokens[s][len(owner_tokens[s]) - ctx:]
-            got = [content.get(row[t // 16] * 16 + t % 16) for t in range(ctx)]
+            got = [content.get(row[t // bs] * bs + t % bs) for t in range(ctx)]
             assert got == toks
+        for s in swapped:
+            row, ctx = bm.table(s)
+            toks = owner_tokens[s][len(owner_tokens[s]) - ctx:]
+            assert [host.get(row[t // bs] * bs + t % bs) for t in range(ctx)] == toks
 
 
 def test_calls_are_atomic_on_error():
@@ -217,3 +264,43 @@ def test_calls_are_atomic_on_error():
     assert bm.num_free() == 0
     bm.free_seq(1)
     assert list(bm.free) == [0, 1, 2]
+
+
+def test_swap_round_trip_and_shared_blocks():
+    bm = BlockManager(8, 16, free_order=range(8))
+    bm.add_seq(0, 40)                        # blocks 0, 1, 2
+    bm.fork(0, 1)                            # all three shared
+    with pytest.raises(StateError):
+        bm.swap_out(0)                       # no host pool yet
+    bm.set_host_blocks(4)
+    with pytest.raises(StateError):
+        bm.set_host_blocks(4)
+    pairs = bm.swap_out(1)
+    assert pairs == [(0, 0), (1, 1), (2, 2)]
+    # The resident sharer is untouched; the blocks only lost one count.
+    assert bm.table(0) == ([0, 1, 2], 40) and [bm.ref_count(b) for b in (0, 1, 2)] == [1, 1, 1]
+    assert bm.table(1) == ([0, 1, 2], 40) and bm.is_swapped(1)
+    assert bm.num_host_free() == 1 and bm.num_free() == 5
+    with pytest.raises(StateError):
+        bm.fork(1, 2)
+    with pytest.raises(StateError):
+        bm.swap_in(0)
+    bm.add_seq(2, 20)                        # device blocks 3, 4
+    snap = copy.deepcopy(bm.__dict__)
+    with pytest.raises(OutOfBlocks):
+        bm.swap_out(2)                       # 2 host blocks needed, 1 free
+    assert bm.__dict__ == snap and not bm.is_swapped(2)
+    bm.free_seq(2)                           # device free list: 5 6 7 3 4
+    snap = copy.deepcopy(bm.__dict__)
+    back = bm.swap_in(1)                     # private copies, from the device free list head
+    assert back == [(0, 5), (1, 6), (2, 7)]
+    assert bm.table(1) == ([5, 6, 7], 40) and list(bm.host_free) == [3, 0, 1, 2]
+    assert [bm.ref_count(b) for b in (0, 1, 2, 5, 6, 7)] == [1] * 6
+    bm.__dict__.update(copy.deepcopy(snap))
+    # Freeing a swapped-out sequence returns its host blocks to the tail.
+    bm.free_seq(1)
+    assert list(bm.host_free) == [3, 0, 1, 2]
+    # Swap-out of a sole owner releases its device blocks in logical order.
+    bm.swap_out(0)
+    assert list(bm.free)[-3:] == [0, 1, 2]
+    _invariants(bm)

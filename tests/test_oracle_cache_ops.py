@@ -147,3 +147,33 @@ def test_int8_attention_error_within_two_hundredths():
     out_q = A.paged_decode(q[None], kc, vc, [table], [T], k_scale=ks, v_scale=vs)[0]
     out_f = A.attend(q, K, V, A.default_scale(D))
     assert np.abs(out_q - out_f).max() < 2e-2
+
+
+def test_swap_round_trip_is_a_relabelling():
+    # Out to host blocks and back into other device blocks: every moved block
+    # arrives bit for bit, blocks not named stay as they were, and decode
+    # through the updated tables gives exactly the same result.
+    from oracle import attention as A
+    from oracle import paging as P
+    rng = W.rng(21, 0)
+    NB, NH, H, D, bs = 12, 6, 2, 8, 16
+    kp = rng.standard_normal((NB, H, bs, D)).astype(np.float16)
+    vp = rng.standard_normal((NB, H, bs, D)).astype(np.float16)
+    ks = rng.standard_normal((NB, H)).astype(np.float16)
+    hk = np.zeros((NH, H, bs, D), np.float16)
+    hv = np.zeros_like(hk)
+    hs = np.zeros((NH, H), np.float16)
+    table, ctx = [7, 2, 9], 40
+    q = rng.standard_normal((1, H, D))
+    before = A.paged_decode(q, kp, vp, [table], [ctx])
+    C.swap_blocks([kp, vp, ks], [hk, hv, hs], [(7, 4), (2, 0), (9, 5)], "out")
+    assert np.array_equal(hk[[4, 0, 5]], kp[[7, 2, 9]]) and np.array_equal(hs[[4, 0, 5]], ks[[7, 2, 9]])
+    untouched = kp[[0, 1, 3]].copy()
+    kp[[7, 2, 9]] = np.nan                    # the device blocks are reused meanwhile
+    C.swap_blocks([kp, vp, ks], [hk, hv, hs], [(4, 3), (0, 11), (5, 1)], "in")
+    assert np.array_equal(kp[[3, 11, 1]], hk[[4, 0, 5]])
+    assert np.array_equal(kp[0], untouched[0])
+    after = A.paged_decode(q, kp, vp, [[3, 11, 1]], [ctx])
+    assert np.array_equal(before, after)
+    with pytest.raises(ValueError):
+        C.swap_blocks([kp], [hk], [(0, 0)], "sideways")
