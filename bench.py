@@ -539,6 +539,7 @@ def extras(eng, wl, q, ptok, dev):
     res["paged_vs_contiguous_overhead"] = round(t_paged / t_contig - 1.0, 4)
     del kc, vc
     res["block_size_sweep"] = block_size_sweep(pk, W, torch, np, wl, ctx, q, out, order, t_contig, nbytes, dev)
+    res["swap"] = swap_probe(pk, torch, np, eng, q, dev)
     # Streaming copy probe: achievable HBM bandwidth (read + write bytes).
     n = 1 << 30
     a = torch.empty(n, dtype=torch.uint8, device=dev)
@@ -550,6 +551,38 @@ def extras(eng, wl, q, ptok, dev):
     t_read = _time_calls(lambda: pk.pa_stream_read(big, sink))
     res["stream_read_gbs"] = round(big.numel() / t_read / 1e9, 1)
     return res
+
+
+def swap_probe(pk, torch, np, eng, q, dev, nseq=16, rounds=3):
+    """Swap the first ``nseq`` sequences out to pinned host memory and back in,
+    ``rounds`` times: rate of each direction over the host link, and whether
+    decode afterwards is bit-identical to decode before."""
+    S = eng.max_seqs
+    seqs = np.arange(S)
+    before = torch.empty_like(q)
+    eng.decode(seqs, q, before)
+    need = sum(len(eng.bm.table(s)[0]) for s in range(nseq))
+    eng.enable_swap(need)
+    block_bytes = 2 * eng.pool.k_cache[0].numel() * eng.pool.k_cache.element_size()   # K and V
+    t = {"out": [], "in": []}
+    for _ in range(rounds):
+        for d in ("out", "in"):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            a.record()
+            pairs = (eng.swap_out if d == "out" else eng.swap_in)(list(range(nseq)))
+            b.record()
+            torch.cuda.synchronize()
+            t[d].append(a.elapsed_time(b) / 1e3)
+    after = torch.empty_like(q)
+    eng.decode(seqs, q, after)
+    torch.cuda.synchronize()
+    moved = pairs.shape[0] * block_bytes
+    return {"seqs": nseq, "blocks": int(pairs.shape[0]), "bytes": int(moved),
+            "out_gbs": round(moved / sorted(t["out"])[rounds // 2] / 1e9, 2),
+            "in_gbs": round(moved / sorted(t["in"])[rounds // 2] / 1e9, 2),
+            "decode_bit_identical_after_round_trip": bool(torch.equal(before.view(torch.int16),
+                                                                      after.view(torch.int16)))}
 
 
 def block_size_sweep(pk, W, torch, np, wl, ctx, q, out, order, t_contig, nbytes, dev):

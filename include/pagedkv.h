@@ -156,6 +156,30 @@ pa_status pa_write_kv(pa_pool* pool, const void* k_new, const void* v_new, pa_dt
 pa_status pa_copy_blocks(pa_pool* pool, const int32_t* pairs, int32_t n, pa_stream stream);
 
 /* ----------------------------------------------------------------------------
+ * Copy whole blocks between the device pool and a host pool (swap).
+ *
+ * Page-by-page swapping to host memory and back is what paging makes
+ * possible ("KV Cache与长上下文管理", the fourth point). The host pool is
+ * caller-owned pinned host memory (hipHostMalloc, or a pinned tensor) with
+ * the pool's per-block layout: host_k / host_v [num_host_blocks][num_heads]
+ * [block_size][head_dim] of the pool's dtype, 16-byte aligned; host_k_scale /
+ * host_v_scale [num_host_blocks][num_heads] fp16 for int8 pools, NULL
+ * otherwise. pairs ([n][2] device int32): PA_SWAP_OUT copies device block
+ * pairs[i][0] to host block pairs[i][1]; PA_SWAP_IN copies host block
+ * pairs[i][0] to device block pairs[i][1] (K, V and int8 scales). One kernel
+ * reads or writes the host pool directly over the host link; no destination
+ * may appear twice in one call. An id outside its pool flags
+ * PA_DEV_BAD_PAIR and the pair is skipped. The host sees swapped-out data
+ * once the stream has reached the end of the call.
+ * n == 0 is a no-op. Errors: PA_ERR_INVALID_ARG (NULL, misaligned, memory
+ * that is not pinned host memory, scales given or missing, bad direction,
+ * n > 65535), PA_ERR_HIP. */
+enum { PA_SWAP_OUT = 0, PA_SWAP_IN = 1 };
+pa_status pa_swap_blocks(pa_pool* pool, void* host_k, void* host_v, void* host_k_scale,
+                         void* host_v_scale, int32_t num_host_blocks, const int32_t* pairs, int32_t n,
+                         int32_t direction, pa_stream stream);
+
+/* ----------------------------------------------------------------------------
  * Paged decode attention.
  *
  * For each sequence s and head h, with ctx = context_lens[s] and
@@ -311,12 +335,12 @@ pa_status pa_bm_destroy(pa_bm* bm);
 pa_status pa_bm_add_seq(pa_bm* bm, int64_t seq, int32_t prefill_tokens, int64_t* slots_out);
 
 /* child shares every block of parent; each count rises by one.
- * Errors: PA_ERR_STATE (unknown parent, existing child). */
+ * Errors: PA_ERR_STATE (unknown or swapped-out parent, existing child). */
 pa_status pa_bm_fork(pa_bm* bm, int64_t parent, int64_t child);
 
 /* Make room for one token of seq. *slot_out receives its slot; *copy_src /
  * *copy_dst receive the block pair to copy first, or -1 / -1.
- * Errors: PA_ERR_STATE, PA_ERR_OUT_OF_BLOCKS. */
+ * Errors: PA_ERR_STATE (unknown or swapped-out seq), PA_ERR_OUT_OF_BLOCKS. */
 pa_status pa_bm_append(pa_bm* bm, int64_t seq, int64_t* slot_out, int32_t* copy_src,
                        int32_t* copy_dst);
 
@@ -326,18 +350,20 @@ pa_status pa_bm_append(pa_bm* bm, int64_t seq, int64_t* slot_out, int32_t* copy_
 pa_status pa_bm_append_batch(pa_bm* bm, const int64_t* seqs, int32_t n, int64_t* slots_out,
                              int32_t* pairs_out, int32_t* n_pairs);
 
-/* Release seq; blocks whose count reaches zero return to the free list.
+/* Release seq; blocks whose count reaches zero return to the free list (a
+ * swapped-out seq returns its host blocks to the host free list).
  * Errors: PA_ERR_STATE. */
 pa_status pa_bm_free_seq(pa_bm* bm, int64_t seq);
 
 /* Table row (logical order) and live context length of seq. row may be NULL
- * to query sizes only. Errors: PA_ERR_STATE, PA_ERR_OUT_OF_RANGE (cap too
- * small). */
+ * to query sizes only. While seq is swapped out the row holds its host-pool
+ * block ids. Errors: PA_ERR_STATE, PA_ERR_OUT_OF_RANGE (cap too small). */
 pa_status pa_bm_table(const pa_bm* bm, int64_t seq, int32_t* row, int32_t cap,
                       int32_t* n_blocks, int32_t* ctx_len);
 
 /* Rows of seqs[0..n) into tables [n][cap] (unused entries -1) and their live
- * context lengths into ctx_out [n]. Errors: PA_ERR_STATE, PA_ERR_OUT_OF_RANGE. */
+ * context lengths into ctx_out [n]. Errors: PA_ERR_STATE (unknown or
+ * swapped-out seq), PA_ERR_OUT_OF_RANGE. */
 pa_status pa_bm_export(const pa_bm* bm, const int64_t* seqs, int32_t n, int32_t* tables,
                        int32_t cap, int32_t* ctx_out);
 
@@ -345,6 +371,39 @@ pa_status pa_bm_ref_count(const pa_bm* bm, int32_t block, int32_t* out);
 pa_status pa_bm_num_free(const pa_bm* bm, int32_t* out);
 /* The free list in order (head first) into out [cap]; *n receives its length. */
 pa_status pa_bm_free_list(const pa_bm* bm, int32_t* out, int32_t cap, int32_t* n);
+
+/* ----------------------------------------------------------------------------
+ * Swapping whole sequences between the device pool and a host pool.
+ *
+ * Only a paged cache can swap page by page: cold pages go to host memory and
+ * come back on demand, instead of moving a whole contiguous cache ("KV Cache与
+ * 长上下文管理", the fourth point on what paging makes possible). The unit here
+ * is one sequence's live blocks.
+ *
+ * pa_bm_set_host_pool gives the manager a host pool of num_host_blocks blocks
+ * (once; host_free_order NULL = ascending ids, else a permutation; the host
+ * free list is FIFO like the device one).
+ * pa_bm_swap_out: every live block of seq, in logical order, takes the head
+ * of the host free list; pairs_out [cap][2] receives the (device, host) pairs
+ * to copy (pa_swap_blocks, PA_SWAP_OUT) and *n_pairs their number. A device
+ * block whose count reaches zero returns to the device free list (tail, in
+ * logical order); a block still held by other sequences only loses a count.
+ * pa_bm_swap_in: every host block of seq takes the head of the device free
+ * list (count one); pairs_out receives the (host, device) pairs (PA_SWAP_IN)
+ * and the host blocks return to the tail of the host free list. Blocks that
+ * were shared before the swap-out come back as private copies.
+ * Copy the pairs before the freed blocks are reused (same stream order).
+ * Errors: PA_ERR_STATE (unknown seq, wrong state, no host pool, host pool set
+ * twice), PA_ERR_OUT_OF_BLOCKS (not enough free blocks on the receiving
+ * side; nothing changes), PA_ERR_OUT_OF_RANGE (cap too small),
+ * PA_ERR_INVALID_ARG. */
+pa_status pa_bm_set_host_pool(pa_bm* bm, int32_t num_host_blocks, const int32_t* host_free_order);
+pa_status pa_bm_swap_out(pa_bm* bm, int64_t seq, int32_t* pairs_out, int32_t cap, int32_t* n_pairs);
+pa_status pa_bm_swap_in(pa_bm* bm, int64_t seq, int32_t* pairs_out, int32_t cap, int32_t* n_pairs);
+/* *out = 1 if seq is swapped out, else 0. Errors: PA_ERR_STATE (unknown seq). */
+pa_status pa_bm_is_swapped(const pa_bm* bm, int64_t seq, int32_t* out);
+/* The host free list in order (head first) into out [cap]; *n its length. */
+pa_status pa_bm_host_free_list(const pa_bm* bm, int32_t* out, int32_t cap, int32_t* n);
 
 #ifdef __cplusplus
 }

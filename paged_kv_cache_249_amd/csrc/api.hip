@@ -161,6 +161,51 @@ pa_status pa_copy_blocks(pa_pool* pool, const int32_t* pairs, int32_t n, pa_stre
   return hip_status("pa_copy_blocks", pa::launch_copy_blocks(pool, pairs, n, stream));
 }
 
+// Device view of pinned host memory, or nullptr (with *e set) if it has none.
+// A failed lookup is cleared from the runtime's last-error slot so that it
+// is not reported again by the next launch check.
+static void* host_view(void* host, hipError_t* e) {
+  void* view = nullptr;
+  *e = hipHostGetDevicePointer(&view, host, 0);
+  if (*e != hipSuccess || !view) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  return view;
+}
+
+pa_status pa_swap_blocks(pa_pool* pool, void* host_k, void* host_v, void* host_k_scale, void* host_v_scale,
+                         int32_t num_host_blocks, const int32_t* pairs, int32_t n, int32_t direction,
+                         pa_stream stream) {
+  if (!pool) return fail(PA_ERR_INVALID_ARG, "pa_swap_blocks: pool is NULL");
+  if (direction != PA_SWAP_OUT && direction != PA_SWAP_IN)
+    return fail(PA_ERR_INVALID_ARG, "pa_swap_blocks: direction %d", direction);
+  if (n < 0 || num_host_blocks < 0) return fail(PA_ERR_INVALID_ARG, "pa_swap_blocks: negative size");
+  if (n == 0) return PA_OK;
+  if (!pairs) return fail(PA_ERR_INVALID_ARG, "pa_swap_blocks: pairs is NULL");
+  if (n > 65535) return fail(PA_ERR_INVALID_ARG, "pa_swap_blocks: n=%d > 65535 pairs per call", n);
+  if (!host_k || !host_v || !aligned16(host_k) || !aligned16(host_v))
+    return fail(PA_ERR_INVALID_ARG, "pa_swap_blocks: host K/V must be non-NULL and 16-byte aligned");
+  const bool i8 = pool->kv_dtype == PA_I8;
+  if (i8 != (host_k_scale != nullptr && host_v_scale != nullptr) || (!i8 && (host_k_scale || host_v_scale)))
+    return fail(PA_ERR_INVALID_ARG, "pa_swap_blocks: host scales are required for int8 pools and only for them");
+  pa::SwapHost h{};
+  hipError_t e = hipSuccess;
+  h.num_blocks = num_host_blocks;
+  void* in[4] = {host_k, host_v, host_k_scale, host_v_scale};
+  void** view[4] = {&h.k, &h.v, &h.k_scale, &h.v_scale};
+  for (int i = 0; i < 4; ++i) {
+    if (!in[i]) continue;
+    *view[i] = host_view(in[i], &e);
+    if (!*view[i])
+      return fail(PA_ERR_INVALID_ARG, "pa_swap_blocks: host buffer %d is not pinned host memory (%s)", i,
+                  hipGetErrorString(e));
+  }
+  if (!aligned16(h.k) || !aligned16(h.v))
+    return fail(PA_ERR_INVALID_ARG, "pa_swap_blocks: device view of the host pool is unaligned");
+  return hip_status("pa_swap_blocks", pa::launch_swap_blocks(pool, h, pairs, n, direction == PA_SWAP_OUT, stream));
+}
+
 static int64_t num_partitions(int32_t max_ctx, int32_t partition_tokens) {
   if (partition_tokens <= 0) return 1;
   const int64_t p = (int64_t(max_ctx) + partition_tokens - 1) / partition_tokens;
@@ -353,9 +398,9 @@ pa_status pa_stage_copy(void* dst, const void* host_src, int64_t bytes, pa_strea
   if (!dst || !host_src || bytes < 0 || bytes % 16 || !aligned16(dst) || !aligned16(host_src))
     return fail(PA_ERR_INVALID_ARG, "pa_stage_copy: bad arguments");
   if (bytes == 0) return PA_OK;
-  void* view = nullptr;
-  hipError_t e = hipHostGetDevicePointer(&view, const_cast<void*>(host_src), 0);
-  if (e != hipSuccess || !view)
+  hipError_t e = hipSuccess;
+  void* view = host_view(const_cast<void*>(host_src), &e);
+  if (!view)
     return fail(PA_ERR_INVALID_ARG, "pa_stage_copy: source is not pinned host memory (%s)", hipGetErrorString(e));
   if (!aligned16(view)) return fail(PA_ERR_INVALID_ARG, "pa_stage_copy: device view of the source is unaligned");
   return hip_status("pa_stage_copy", pa::launch_stage_copy(dst, view, bytes, stream));

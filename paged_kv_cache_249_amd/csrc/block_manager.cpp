@@ -15,6 +15,14 @@
 //    its physical id for the new one; only the table row changes (front
 //    dropped, id appended). An oldest block still shared by another sequence
 //    cannot be overwritten: its count drops and a fresh block is taken.
+//  * Swapping ("KV Cache与长上下文管理", the fourth point: a paged cache can move
+//    page by page between device and host memory). The unit is a sequence's
+//    live blocks. Swap-out gives each a block of a host pool (FIFO free list
+//    of its own), in logical order, and reports (device, host) copy pairs; a
+//    device block no one else holds returns to the device free list, a shared
+//    one only loses a count. Swap-in takes device blocks from the free list
+//    and reports (host, device) pairs; host blocks return to the host list.
+//    A swapped-out sequence cannot append, fork or be exported.
 //  * Every call is atomic; batched appends roll back through an undo log.
 #include <algorithm>
 #include <deque>
@@ -30,6 +38,7 @@ struct Seq {
   std::deque<int32_t> table;  // live physical blocks in logical order
   int64_t tokens = 0;         // tokens appended in total
   int64_t evicted = 0;        // blocks dropped by the ring
+  bool swapped = false;       // table holds host-pool block ids
 };
 
 enum class Kind : int8_t { kInPlace, kFresh, kRingReuse, kRingFresh, kCow };
@@ -50,6 +59,8 @@ struct pa_bm {
   std::deque<int32_t> free_list;
   std::vector<int32_t> ref;
   std::unordered_map<int64_t, Seq> seqs;
+  int32_t num_host_blocks = 0;
+  std::deque<int32_t> host_free;
 
   int64_t live_tokens(const Seq& s) const { return s.tokens - int64_t(block_size) * s.evicted; }
 
@@ -70,6 +81,7 @@ struct pa_bm {
     auto it = seqs.find(id);
     if (it == seqs.end()) return pa::fail(PA_ERR_STATE, "pa_bm_append: unknown sequence %lld", (long long)id);
     Seq& s = it->second;
+    if (s.swapped) return pa::fail(PA_ERR_STATE, "pa_bm_append: sequence %lld is swapped out", (long long)id);
     const int32_t offset = int32_t(s.tokens % block_size);
     *src = -1;
     *dst = -1;
@@ -212,6 +224,8 @@ pa_status pa_bm_fork(pa_bm* bm, int64_t parent, int64_t child) {
   if (!bm) return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_fork: bm is NULL");
   auto it = bm->seqs.find(parent);
   if (it == bm->seqs.end()) return pa::fail(PA_ERR_STATE, "pa_bm_fork: unknown parent %lld", (long long)parent);
+  if (it->second.swapped)
+    return pa::fail(PA_ERR_STATE, "pa_bm_fork: parent %lld is swapped out", (long long)parent);
   if (bm->seqs.count(child)) return pa::fail(PA_ERR_STATE, "pa_bm_fork: child %lld exists", (long long)child);
   Seq c = it->second;
   for (int32_t b : c.table) bm->ref[b] += 1;
@@ -255,11 +269,106 @@ pa_status pa_bm_free_seq(pa_bm* bm, int64_t seq) {
   if (!bm) return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_free_seq: bm is NULL");
   auto it = bm->seqs.find(seq);
   if (it == bm->seqs.end()) return pa::fail(PA_ERR_STATE, "pa_bm_free_seq: unknown sequence %lld", (long long)seq);
-  for (int32_t b : it->second.table) {
-    bm->ref[b] -= 1;
-    if (bm->ref[b] == 0) bm->free_list.push_back(b);
+  if (it->second.swapped) {
+    for (int32_t hb : it->second.table) bm->host_free.push_back(hb);
+  } else {
+    for (int32_t b : it->second.table) {
+      bm->ref[b] -= 1;
+      if (bm->ref[b] == 0) bm->free_list.push_back(b);
+    }
   }
   bm->seqs.erase(it);
+  return PA_OK;
+}
+
+pa_status pa_bm_set_host_pool(pa_bm* bm, int32_t num_host_blocks, const int32_t* host_free_order) {
+  if (!bm) return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_set_host_pool: bm is NULL");
+  if (bm->num_host_blocks > 0) return pa::fail(PA_ERR_STATE, "pa_bm_set_host_pool: host pool already set");
+  if (num_host_blocks <= 0)
+    return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_set_host_pool: num_host_blocks=%d", num_host_blocks);
+  std::deque<int32_t> order;
+  if (host_free_order) {
+    std::vector<char> seen(num_host_blocks, 0);
+    for (int32_t i = 0; i < num_host_blocks; ++i) {
+      const int32_t b = host_free_order[i];
+      if (b < 0 || b >= num_host_blocks || seen[b])
+        return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_set_host_pool: order is not a permutation (entry %d)", i);
+      seen[b] = 1;
+      order.push_back(b);
+    }
+  } else {
+    for (int32_t b = 0; b < num_host_blocks; ++b) order.push_back(b);
+  }
+  bm->num_host_blocks = num_host_blocks;
+  bm->host_free = std::move(order);
+  return PA_OK;
+}
+
+pa_status pa_bm_swap_out(pa_bm* bm, int64_t seq, int32_t* pairs_out, int32_t cap, int32_t* n_pairs) {
+  if (!bm || !n_pairs || cap < 0 || (cap > 0 && !pairs_out))
+    return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_swap_out: bad arguments");
+  auto it = bm->seqs.find(seq);
+  if (it == bm->seqs.end()) return pa::fail(PA_ERR_STATE, "pa_bm_swap_out: unknown sequence %lld", (long long)seq);
+  Seq& s = it->second;
+  if (s.swapped) return pa::fail(PA_ERR_STATE, "pa_bm_swap_out: sequence %lld is swapped out", (long long)seq);
+  if (bm->num_host_blocks == 0) return pa::fail(PA_ERR_STATE, "pa_bm_swap_out: no host pool");
+  const int32_t nb = int32_t(s.table.size());
+  if (cap < nb) return pa::fail(PA_ERR_OUT_OF_RANGE, "pa_bm_swap_out: cap %d < %d blocks", cap, nb);
+  if (size_t(nb) > bm->host_free.size())
+    return pa::fail(PA_ERR_OUT_OF_BLOCKS, "pa_bm_swap_out: needs %d host blocks, %zu free", nb,
+                    bm->host_free.size());
+  for (int32_t i = 0; i < nb; ++i) {
+    const int32_t b = s.table[i];
+    const int32_t hb = bm->host_free.front();
+    bm->host_free.pop_front();
+    pairs_out[2 * i] = b;
+    pairs_out[2 * i + 1] = hb;
+    bm->ref[b] -= 1;
+    if (bm->ref[b] == 0) bm->free_list.push_back(b);
+    s.table[i] = hb;
+  }
+  s.swapped = true;
+  *n_pairs = nb;
+  return PA_OK;
+}
+
+pa_status pa_bm_swap_in(pa_bm* bm, int64_t seq, int32_t* pairs_out, int32_t cap, int32_t* n_pairs) {
+  if (!bm || !n_pairs || cap < 0 || (cap > 0 && !pairs_out))
+    return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_swap_in: bad arguments");
+  auto it = bm->seqs.find(seq);
+  if (it == bm->seqs.end()) return pa::fail(PA_ERR_STATE, "pa_bm_swap_in: unknown sequence %lld", (long long)seq);
+  Seq& s = it->second;
+  if (!s.swapped) return pa::fail(PA_ERR_STATE, "pa_bm_swap_in: sequence %lld is resident", (long long)seq);
+  const int32_t nb = int32_t(s.table.size());
+  if (cap < nb) return pa::fail(PA_ERR_OUT_OF_RANGE, "pa_bm_swap_in: cap %d < %d blocks", cap, nb);
+  if (size_t(nb) > bm->free_list.size())
+    return pa::fail(PA_ERR_OUT_OF_BLOCKS, "pa_bm_swap_in: needs %d blocks, %zu free", nb, bm->free_list.size());
+  for (int32_t i = 0; i < nb; ++i) {
+    const int32_t hb = s.table[i];
+    const int32_t b = bm->take_free();
+    pairs_out[2 * i] = hb;
+    pairs_out[2 * i + 1] = b;
+    bm->host_free.push_back(hb);
+    s.table[i] = b;
+  }
+  s.swapped = false;
+  *n_pairs = nb;
+  return PA_OK;
+}
+
+pa_status pa_bm_is_swapped(const pa_bm* bm, int64_t seq, int32_t* out) {
+  if (!bm || !out) return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_is_swapped: NULL argument");
+  auto it = bm->seqs.find(seq);
+  if (it == bm->seqs.end()) return pa::fail(PA_ERR_STATE, "pa_bm_is_swapped: unknown sequence %lld", (long long)seq);
+  *out = it->second.swapped ? 1 : 0;
+  return PA_OK;
+}
+
+pa_status pa_bm_host_free_list(const pa_bm* bm, int32_t* out, int32_t cap, int32_t* n) {
+  if (!bm || !n || (cap > 0 && !out)) return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_host_free_list: NULL argument");
+  *n = int32_t(bm->host_free.size());
+  if (cap < *n) return pa::fail(PA_ERR_OUT_OF_RANGE, "pa_bm_host_free_list: cap %d < %d", cap, *n);
+  std::copy(bm->host_free.begin(), bm->host_free.end(), out);
   return PA_OK;
 }
 
@@ -288,6 +397,8 @@ pa_status pa_bm_export(const pa_bm* bm, const int64_t* seqs, int32_t n, int32_t*
     auto it = bm->seqs.find(seqs[i]);
     if (it == bm->seqs.end())
       return pa::fail(PA_ERR_STATE, "pa_bm_export: unknown sequence %lld", (long long)seqs[i]);
+    if (it->second.swapped)
+      return pa::fail(PA_ERR_STATE, "pa_bm_export: sequence %lld is swapped out", (long long)seqs[i]);
     if (int32_t(it->second.table.size()) > cap)
       return pa::fail(PA_ERR_OUT_OF_RANGE, "pa_bm_export: sequence %lld holds %zu blocks > cap %d",
                       (long long)seqs[i], it->second.table.size(), cap);

@@ -16,6 +16,10 @@
 //
 // copy_blocks: whole-block copies, the copy-on-write unit of the study note's
 // 实践案例 / 案例 3.
+//
+// swap_blocks: whole blocks between the device pool and a pool in pinned host
+// memory, page by page ("KV Cache与长上下文管理", the fourth point on what paging
+// makes possible), read or written by the kernel directly over the host link.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -178,6 +182,56 @@ __global__ __launch_bounds__(kThreads) void copy_blocks_kernel(const int32_t* __
   }
 }
 
+// One workgroup per 4 KiB of one block of one tensor. A thread moves two
+// 8-byte words 512 bytes apart, so each load and store instruction of a wave
+// covers 512 contiguous bytes on both sides. Host memory is accessed with
+// system-scope loads and stores: no GPU cache serves a stale copy of it or
+// holds back a write to it.
+constexpr int kSwapWordsPerGroup = 2 * kThreads;   // 8-byte words per workgroup
+
+__global__ __launch_bounds__(kThreads) void swap_blocks_kernel(
+    const int32_t* __restrict__ pairs, uint64_t* dev_k, uint64_t* dev_v, uint64_t* host_k, uint64_t* host_v,
+    int64_t block_words, uint16_t* dev_ks, uint16_t* dev_vs, uint16_t* host_ks, uint16_t* host_vs, int H,
+    int num_blocks, int num_host_blocks, int out_dir, int32_t* err) {
+  const int pair = blockIdx.y;
+  const int a = pairs[2 * pair];
+  const int b = pairs[2 * pair + 1];
+  const int dblk = out_dir ? a : b;
+  const int hblk = out_dir ? b : a;
+  if (unsigned(dblk) >= unsigned(num_blocks) || unsigned(hblk) >= unsigned(num_host_blocks)) {
+    if (blockIdx.x == 0 && blockIdx.z == 0 && threadIdx.x == 0) flag_error(err, PA_DEV_BAD_PAIR);
+    return;
+  }
+  uint64_t* dev = (blockIdx.z == 0 ? dev_k : dev_v) + int64_t(dblk) * block_words;
+  uint64_t* host = (blockIdx.z == 0 ? host_k : host_v) + int64_t(hblk) * block_words;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t w0 = int64_t(blockIdx.x) * kSwapWordsPerGroup + (threadIdx.x / kWave) * (2 * kWave) + lane;
+  const int64_t w1 = w0 + kWave;
+  if (w1 < block_words) {
+    if (out_dir) {
+      const uint64_t x0 = dev[w0];
+      const uint64_t x1 = dev[w1];
+      __hip_atomic_store(host + w0, x0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      __hip_atomic_store(host + w1, x1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    } else {
+      const uint64_t x0 = __hip_atomic_load(host + w0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      const uint64_t x1 = __hip_atomic_load(host + w1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      dev[w0] = x0;
+      dev[w1] = x1;
+    }
+  }
+  if (dev_ks && blockIdx.x == 0) {
+    uint16_t* ds = (blockIdx.z == 0 ? dev_ks : dev_vs) + int64_t(dblk) * H;
+    uint16_t* hs = (blockIdx.z == 0 ? host_ks : host_vs) + int64_t(hblk) * H;
+    for (int hh = threadIdx.x; hh < H; hh += kThreads) {
+      if (out_dir)
+        __hip_atomic_store(hs + hh, ds[hh], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      else
+        ds[hh] = __hip_atomic_load(hs + hh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
+  }
+}
+
 __global__ __launch_bounds__(kThreads) void stream_copy_kernel(uint4* __restrict__ dst,
                                                                const uint4* __restrict__ src,
                                                                int64_t n16) {
@@ -293,6 +347,21 @@ int launch_copy_blocks(const pa_pool* p, const int32_t* pairs, int32_t n, void* 
                      n, static_cast<char*>(p->k_cache), static_cast<char*>(p->v_cache), block_bytes,
                      static_cast<_Float16*>(p->k_scale), static_cast<_Float16*>(p->v_scale),
                      p->num_heads, p->num_blocks, device_error_ptr());
+  return int(hipGetLastError());
+}
+
+int launch_swap_blocks(const pa_pool* p, const SwapHost& h, const int32_t* pairs, int32_t n, bool out_dir,
+                       void* stream) {
+  if (n == 0) return 0;
+  const int64_t block_bytes = int64_t(p->num_heads) * p->block_size * p->head_dim * elem_bytes(p->kv_dtype);
+  const int64_t words = block_bytes / 8;   // whole 1 KiB wave chunks for every supported geometry
+  const dim3 grid(unsigned((words + kSwapWordsPerGroup - 1) / kSwapWordsPerGroup), unsigned(n), 2);
+  hipLaunchKernelGGL(swap_blocks_kernel, grid, dim3(kThreads), 0, static_cast<hipStream_t>(stream), pairs,
+                     static_cast<uint64_t*>(p->k_cache), static_cast<uint64_t*>(p->v_cache),
+                     static_cast<uint64_t*>(h.k), static_cast<uint64_t*>(h.v), words,
+                     static_cast<uint16_t*>(p->k_scale), static_cast<uint16_t*>(p->v_scale),
+                     static_cast<uint16_t*>(h.k_scale), static_cast<uint16_t*>(h.v_scale), p->num_heads,
+                     p->num_blocks, h.num_blocks, out_dir ? 1 : 0, device_error_ptr());
   return int(hipGetLastError());
 }
 

@@ -86,6 +86,16 @@ int launch_decode(const DecodeArgs& a, void* stream);
 int launch_write_kv(const pa_pool* p, const void* k_new, const void* v_new, pa_dtype src,
                     const int64_t* slots, int32_t n, void* stream);
 int launch_copy_blocks(const pa_pool* p, const int32_t* pairs, int32_t n, void* stream);
+// Device views of a host pool (pinned host memory) for launch_swap_blocks.
+struct SwapHost {
+  void* k;
+  void* v;
+  void* k_scale;   // int8 pools only
+  void* v_scale;
+  int32_t num_blocks;
+};
+int launch_swap_blocks(const pa_pool* p, const SwapHost& h, const int32_t* pairs, int32_t n, bool out_dir,
+                       void* stream);
 int launch_stream_copy(void* dst, const void* src, int64_t bytes, void* stream);
 int launch_stream_read(const void* src, int64_t bytes, void* sink, void* stream);
 int launch_stage_copy(void* dst, const void* src_device_view, int64_t bytes, void* stream);

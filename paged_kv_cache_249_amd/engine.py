@@ -121,6 +121,43 @@ class PagedDecodeEngine:
     def free_sequence(self, seq: int) -> None:
         self.bm.free_seq(seq)
 
+    # -- swapping --------------------------------------------------------------
+    def enable_swap(self, host_blocks: int, host_free_order=None) -> None:
+        """Give the engine a host pool of ``host_blocks`` blocks in pinned memory."""
+        self.host = N.HostPool(self.pool, host_blocks)
+        self.bm.set_host_pool(host_blocks, host_free_order)
+
+    def swap_out(self, seqs, stream=None) -> np.ndarray:
+        """Move the blocks of ``seqs`` to the host pool; returns the (device, host) pairs."""
+        return self._swap(seqs, True, stream)
+
+    def swap_in(self, seqs, stream=None) -> np.ndarray:
+        """Bring ``seqs`` back into the device pool; returns the (host, device) pairs."""
+        return self._swap(seqs, False, stream)
+
+    def _swap(self, seqs, out: bool, stream) -> np.ndarray:
+        # The manager moves one sequence at a time; if one fails, the copies of
+        # those already moved are still issued before the error propagates.
+        done, err = [], None
+        for s in np.asarray(seqs, dtype=np.int64).reshape(-1):
+            try:
+                done.append(self.bm.swap_out(int(s)) if out else self.bm.swap_in(int(s)))
+            except N.PagedKVError as e:
+                err = e
+                break
+        pairs = np.concatenate(done) if done else np.zeros((0, 2), np.int32)
+        if pairs.shape[0]:
+            cur = torch.cuda.current_stream(self.device) if stream is None else stream
+            host = torch.from_numpy(np.ascontiguousarray(pairs, dtype=np.int32)).pin_memory()
+            with torch.cuda.stream(cur):
+                dev = host.to(self.device, non_blocking=True)
+                for i in range(0, pairs.shape[0], 65535):
+                    N.pa_swap_blocks(self.pool, self.host, dev[i:i + 65535],
+                                     N.PA_SWAP_OUT if out else N.PA_SWAP_IN, stream=cur)
+        if err is not None:
+            raise err
+        return pairs
+
     def _workspace_for(self, n: int, max_ctx: int, ptok: int):
         need = N.pa_decode_workspace_bytes(self.pool, n, max_ctx, ptok)
         if need > self._ws_bytes:

@@ -33,6 +33,7 @@ PA_DEV_BAD_SLOT = 2
 PA_DEV_BAD_PAIR = 4
 PA_DEV_BAD_CONTEXT = 8
 PA_DEV_BAD_RUN = 16
+PA_SWAP_OUT, PA_SWAP_IN = 0, 1
 
 BLOCK_SIZE = 16                      # the default; pools and managers also take 32 and 64
 BLOCK_SIZES = (16, 32, 64)
@@ -62,6 +63,7 @@ _SIGS = {
     "pa_free_pool": ([_vp], _i32),
     "pa_write_kv": ([_vp, _vp, _vp, _i32, _vp, _i32, _vp], _i32),
     "pa_copy_blocks": ([_vp, _vp, _i32, _vp], _i32),
+    "pa_swap_blocks": ([_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _vp], _i32),
     "pa_decode_workspace_bytes": ([_vp, _i32, _i32, _i32, _pi64], _i32),
     "pa_decode": ([_vp, _vp, _i32, _vp, _vp, _i32, _vp, _i32, _i32, _f32, _i32, _vp, _i64, _vp], _i32),
     "pa_decode_ordered": ([_vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _f32, _i32, _vp, _i64, _vp],
@@ -86,6 +88,11 @@ _SIGS = {
     "pa_bm_ref_count": ([_vp, _i32, _pi32], _i32),
     "pa_bm_num_free": ([_vp, _pi32], _i32),
     "pa_bm_free_list": ([_vp, _vp, _i32, _pi32], _i32),
+    "pa_bm_set_host_pool": ([_vp, _i32, _vp], _i32),
+    "pa_bm_swap_out": ([_vp, _i64, _vp, _i32, _pi32], _i32),
+    "pa_bm_swap_in": ([_vp, _i64, _vp, _i32, _pi32], _i32),
+    "pa_bm_is_swapped": ([_vp, _i64, _pi32], _i32),
+    "pa_bm_host_free_list": ([_vp, _vp, _i32, _pi32], _i32),
 }
 for _name, (_args, _ret) in _SIGS.items():
     _fn = getattr(lib, _name)
@@ -234,6 +241,36 @@ def pa_copy_blocks(pool: Pool, pairs, stream=None) -> None:
     n = int(pairs.shape[0]) if pairs.numel() else 0
     _check(lib.pa_copy_blocks(pool.handle, _ptr(pairs, "pairs", torch.int32), n,
                               _stream(stream, pairs)), "pa_copy_blocks")
+
+
+class HostPool:
+    """A host pool in pinned host memory with a device pool's per-block layout."""
+
+    def __init__(self, pool: Pool, num_blocks: int):
+        torch = _torch()
+        self.num_blocks = num_blocks
+        shape = (num_blocks, pool.num_heads, pool.block_size, pool.head_dim)
+        dt = torch_dtype(pool.kv_dtype)
+        self.k = torch.zeros(shape, dtype=dt, pin_memory=True)
+        self.v = torch.zeros(shape, dtype=dt, pin_memory=True)
+        self.k_scale = self.v_scale = None
+        if pool.kv_dtype == PA_I8:
+            self.k_scale = torch.zeros((num_blocks, pool.num_heads), dtype=torch.float16, pin_memory=True)
+            self.v_scale = torch.zeros((num_blocks, pool.num_heads), dtype=torch.float16, pin_memory=True)
+
+
+def pa_swap_blocks(pool: Pool, host: HostPool, pairs, direction: int, stream=None) -> None:
+    """Copy whole blocks for an int32 ``[n][2]`` device tensor of pairs:
+    (device, host) for ``PA_SWAP_OUT``, (host, device) for ``PA_SWAP_IN``."""
+    torch = _torch()
+    n = int(pairs.shape[0]) if pairs.numel() else 0
+    for t in (host.k, host.v):
+        if not t.is_pinned():
+            raise PagedKVError(PA_ERR_INVALID_ARG, "host pool must be pinned")
+    hp = lambda t: None if t is None else t.data_ptr()
+    _check(lib.pa_swap_blocks(pool.handle, hp(host.k), hp(host.v), hp(host.k_scale), hp(host.v_scale),
+                              host.num_blocks, _ptr(pairs, "pairs", torch.int32), n, direction,
+                              _stream(stream, pairs)), "pa_swap_blocks")
 
 
 def pa_decode_workspace_bytes(pool: Pool, num_seqs: int, max_context_len: int,
@@ -449,4 +486,44 @@ class BlockManager:
         out = np.empty(max(n, 1), dtype=np.int32)
         got = C.c_int32()
         _check(lib.pa_bm_free_list(self.handle, _np_ptr(out), out.size, C.byref(got)), "pa_bm_free_list")
+        return out[:got.value].tolist()
+
+    # -- swapping --------------------------------------------------------------
+    def set_host_pool(self, num_host_blocks: int, free_order=None) -> None:
+        order = None
+        if free_order is not None:
+            order = np.ascontiguousarray(np.asarray(free_order, dtype=np.int32))
+            if order.size != num_host_blocks:
+                raise PagedKVError(PA_ERR_INVALID_ARG, "host free_order length != num_host_blocks")
+        _check(lib.pa_bm_set_host_pool(self.handle, num_host_blocks, None if order is None else _np_ptr(order)),
+               "pa_bm_set_host_pool")
+        self.num_host_blocks = num_host_blocks
+
+    def _swap(self, fn, seq: int, pairs_out=None) -> np.ndarray:
+        nb = C.c_int32()
+        _check(lib.pa_bm_table(self.handle, seq, None, 0, C.byref(nb), None), fn.__name__)
+        out = pairs_out if pairs_out is not None else np.empty((max(nb.value, 1), 2), dtype=np.int32)
+        got = C.c_int32()
+        _check(fn(self.handle, seq, _np_ptr(out), out.shape[0], C.byref(got)), fn.__name__)
+        return out[:got.value]
+
+    def swap_out(self, seq: int, pairs_out=None) -> np.ndarray:
+        """(device, host) pairs to copy with ``PA_SWAP_OUT``."""
+        return self._swap(lib.pa_bm_swap_out, seq, pairs_out)
+
+    def swap_in(self, seq: int, pairs_out=None) -> np.ndarray:
+        """(host, device) pairs to copy with ``PA_SWAP_IN``."""
+        return self._swap(lib.pa_bm_swap_in, seq, pairs_out)
+
+    def is_swapped(self, seq: int) -> bool:
+        out = C.c_int32()
+        _check(lib.pa_bm_is_swapped(self.handle, seq, C.byref(out)), "pa_bm_is_swapped")
+        return bool(out.value)
+
+    def host_free_list(self):
+        cap = max(getattr(self, "num_host_blocks", 0), 1)
+        out = np.empty(cap, dtype=np.int32)
+        got = C.c_int32()
+        _check(lib.pa_bm_host_free_list(self.handle, _np_ptr(out), out.size, C.byref(got)),
+               "pa_bm_host_free_list")
         return out[:got.value].tolist()
