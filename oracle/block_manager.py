@@ -46,6 +46,17 @@ Readings of what the pages leave open (this project's choices):
   of the host free list. Blocks shared before a swap-out come back as private
   copies. A swapped-out sequence cannot append, fork or be exported for decode;
   freeing it returns its host blocks.
+* Prefix caching ("KV Cache与长上下文管理", section 二, item 2: a system prompt
+  or a common history prefix is stored once and reused by many users).
+  ``add_seq_prefix`` registers a sequence from its token ids. Every full block
+  is looked up under the key (physical block before it, or -1 for the first;
+  the block's token ids): a live block registered under that key is shared
+  (its count rises by one) and its tokens get slot -1 (nothing to write);
+  otherwise a fresh block is taken and registered. Keying on the previous
+  physical block makes a match imply that the whole prefix matches. The
+  partly filled last block is never shared. A block leaves the index when its
+  count drops to zero. Only managers without a ring use it (an evicted or
+  reused block would leave stale keys behind).
 * Every call is atomic: on error nothing changes.
 """
 
@@ -77,6 +88,10 @@ class StateError(BMError):
     code = -5
 
 
+class Unsupported(BMError):
+    code = -2
+
+
 @dataclass
 class _Seq:
     table: list = field(default_factory=list)   # live physical blocks, logical order
@@ -101,6 +116,8 @@ class BlockManager:
         self.seqs: dict[int, _Seq] = {}
         self.num_host_blocks = 0
         self.host_free: deque = deque()
+        self.prefix: dict = {}          # (previous block or -1, token ids) -> block
+        self.prefix_key: dict = {}      # block -> its key in self.prefix
 
     # -- queries -------------------------------------------------------------
     def num_free(self) -> int:
@@ -155,6 +172,61 @@ class BlockManager:
         bs = self.block_size
         return np.array([st.table[t // bs] * bs + t % bs for t in range(prefill_tokens)],
                         dtype=np.int64)
+
+    def add_seq_prefix(self, seq: int, tokens):
+        """Register ``seq`` from its token ids, sharing cached full blocks.
+
+        Returns ``(slots, shared_blocks)``: the slots of the tokens to write
+        (-1 for tokens of shared blocks) and how many leading blocks were shared.
+        """
+        if self.window:
+            raise Unsupported("prefix caching with a ring")
+        if seq in self.seqs:
+            raise StateError("sequence exists")
+        tokens = [int(t) for t in tokens]
+        bs = self.block_size
+        n = len(tokens)
+        nb = -(-n // bs)
+        plan, prev = [], -1
+        for i in range(nb):
+            chunk = tuple(tokens[i * bs:(i + 1) * bs])
+            hit = self.prefix.get((prev, chunk)) if len(chunk) == bs else None
+            if hit is None:
+                break
+            plan.append(hit)
+            prev = hit
+        shared = len(plan)
+        if nb - shared > len(self.free):
+            raise OutOfBlocks("pool exhausted")
+        st = _Seq()
+        prev = -1
+        for i in range(nb):
+            chunk = tuple(tokens[i * bs:(i + 1) * bs])
+            if i < shared:
+                b = plan[i]
+                self.ref[b] += 1
+            else:
+                b = self.free.popleft()
+                self.ref[b] = 1
+                if len(chunk) == bs:
+                    self.prefix[(prev, chunk)] = b
+                    self.prefix_key[b] = (prev, chunk)
+            st.table.append(b)
+            prev = b
+        st.tokens = n
+        self.seqs[seq] = st
+        slots = np.array([-1 if t // bs < shared else st.table[t // bs] * bs + t % bs for t in range(n)],
+                         dtype=np.int64)
+        return slots, shared
+
+    def _release(self, b: int) -> None:
+        """Drop one count of device block ``b``; at zero it is free and unindexed."""
+        self.ref[b] -= 1
+        if self.ref[b] == 0:
+            self.free.append(b)
+            key = self.prefix_key.pop(b, None)
+            if key is not None:
+                del self.prefix[key]
 
     def fork(self, parent: int, child: int) -> None:
         """``child`` shares every block of ``parent`` (each count rises by one)."""
@@ -214,9 +286,7 @@ class BlockManager:
             self.host_free.extend(st.table)
         else:
             for b in st.table:
-                self.ref[b] -= 1
-                if self.ref[b] == 0:
-                    self.free.append(b)
+                self._release(b)
         del self.seqs[seq]
 
     # -- swapping ------------------------------------------------------------
@@ -249,9 +319,7 @@ class BlockManager:
         for b in st.table:
             hb = self.host_free.popleft()
             pairs.append((b, hb))
-            self.ref[b] -= 1
-            if self.ref[b] == 0:
-                self.free.append(b)
+            self._release(b)
         st.table = [hb for _, hb in pairs]
         st.swapped = True
         return pairs

@@ -6,7 +6,7 @@ import numpy as np
 import pytest
 
 import workloads as W
-from oracle.block_manager import BlockManager, InvalidArg, OutOfBlocks, OutOfRange, StateError
+from oracle.block_manager import BlockManager, InvalidArg, OutOfBlocks, OutOfRange, StateError, Unsupported
 
 
 def test_cow_worked_example(load_golden):
@@ -132,6 +132,10 @@ def _invariants(bm: BlockManager):
     assert len(set(bm.host_free)) == len(bm.host_free)
     assert set(host_held).isdisjoint(bm.host_free)
     assert set(host_held) | set(bm.host_free) == set(range(bm.num_host_blocks))
+    # The prefix index only names live blocks, each under the key it was built with.
+    for key, b in bm.prefix.items():
+        assert bm.ref[b] > 0 and bm.prefix_key[b] == key
+        assert key[0] == -1 or bm.ref[key[0]] > 0
 
 
 @pytest.mark.parametrize("bs", [16, 32])
@@ -200,6 +204,20 @@ def test_random_operation_sequences_keep_the_invariants(seed, bs):
                             content[d * bs + o] = host[h * bs + o]
                 swapped.remove(s)
                 live.append(s)
+            elif op == 8 and not window:
+                # A prompt built from a few shared templates, so full blocks repeat.
+                s = next_id
+                t = int(rng.integers(0, 3))
+                n = int(rng.integers(0, 70))
+                toks = [5000 + 100 * t + (i % 37) * 1000 * (1 + (i // 37) % 2) + i for i in range(n)]
+                slots, shared = bm.add_seq_prefix(s, toks)
+                assert (slots[:shared * bs] == -1).all() and (slots[shared * bs:] >= 0).all()
+                for sl, tid in zip(slots, toks):
+                    if sl >= 0:
+                        content[int(sl)] = tid
+                owner_tokens[s] = list(toks)
+                live.append(s)
+                next_id += 1
             elif op == 9 and swapped:
                 s = swapped.pop(int(rng.integers(len(swapped))))
                 bm.free_seq(s)
@@ -304,3 +322,58 @@ def test_swap_round_trip_and_shared_blocks():
     bm.swap_out(0)
     assert list(bm.free)[-3:] == [0, 1, 2]
     _invariants(bm)
+
+
+def test_prefix_caching_shares_whole_matching_prefixes():
+    bs = 16
+    bm = BlockManager(32, bs, free_order=range(32))
+    A = list(range(100, 150))                    # 3 full blocks + 2 tokens
+    slots, shared = bm.add_seq_prefix(0, A)
+    assert shared == 0 and (slots >= 0).all() and bm.table(0) == ([0, 1, 2, 3], 50)
+    slots, shared = bm.add_seq_prefix(1, A)
+    assert shared == 3 and (slots[:48] == -1).all()
+    assert bm.table(1) == ([0, 1, 2, 4], 50) and slots[48] == 4 * bs
+    assert [bm.ref_count(b) for b in range(5)] == [2, 2, 2, 1, 1]
+    # Same first block, different second: only the first is shared.
+    B = A[:16] + [7] * 16 + A[32:48]
+    _, shared = bm.add_seq_prefix(2, B)
+    assert shared == 1 and bm.table(2)[0] == [0, 5, 6]
+    # A different first block breaks the chain even if later blocks match.
+    C = [9] * 16 + A[16:48]
+    _, shared = bm.add_seq_prefix(3, C)
+    assert shared == 0 and bm.table(3)[0] == [7, 8, 9]
+    # A full shared last block: the next append opens a fresh block, no copy.
+    _, shared = bm.add_seq_prefix(4, A[:32])
+    assert shared == 2
+    slot, src, dst = bm.append(4)
+    assert (src, dst) == (-1, -1) and slot == 10 * bs and bm.ref_count(1) == 3
+    # Freed blocks leave the index: after every holder of A's blocks is gone,
+    # A is built from scratch again.
+    for s in (0, 1, 2, 4):
+        bm.free_seq(s)
+    assert all(bm.ref_count(b) == 0 for b in (0, 1, 2))
+    _, shared = bm.add_seq_prefix(5, A)
+    assert shared == 0
+    _invariants(bm)
+    # Atomic on error, and not offered with a ring.
+    snap = copy.deepcopy(bm.__dict__)
+    with pytest.raises(OutOfBlocks):
+        bm.add_seq_prefix(6, list(range(10**6, 10**6 + 40 * bs)))
+    assert bm.__dict__ == snap
+    with pytest.raises(StateError):
+        bm.add_seq_prefix(5, A)
+    with pytest.raises(Unsupported):
+        BlockManager(8, 16, window_blocks=2).add_seq_prefix(0, A)
+
+
+def test_prefix_caching_saves_the_shared_prompt_blocks():
+    # Eight prompts of 1024 tokens, four samples each ("KV Cache与长上下文管理",
+    # section 二 item 2: a common prefix is stored once): 8 x 64 prompt blocks
+    # instead of 32 x 64.
+    bm = BlockManager(4096, 16, free_order=W.free_order(3, 4096))
+    for p in range(8):
+        prompt = [p * 10**6 + i for i in range(1024)]
+        for j in range(4):
+            _, shared = bm.add_seq_prefix(p * 4 + j, prompt)
+            assert shared == (0 if j == 0 else 64)
+    assert 4096 - bm.num_free() == 8 * 64
