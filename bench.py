@@ -540,6 +540,7 @@ def extras(eng, wl, q, ptok, dev):
     del kc, vc
     res["block_size_sweep"] = block_size_sweep(pk, W, torch, np, wl, ctx, q, out, order, t_contig, nbytes, dev)
     res["swap"] = swap_probe(pk, torch, np, eng, q, dev)
+    res["prefix_cache"] = prefix_probe(pk, W, np)
     # Streaming copy probe: achievable HBM bandwidth (read + write bytes).
     n = 1 << 30
     a = torch.empty(n, dtype=torch.uint8, device=dev)
@@ -551,6 +552,25 @@ def extras(eng, wl, q, ptok, dev):
     t_read = _time_calls(lambda: pk.pa_stream_read(big, sink))
     res["stream_read_gbs"] = round(big.numel() / t_read / 1e9, 1)
     return res
+
+
+def prefix_probe(pk, W, np):
+    """Host side of prefix caching at the shared-prefix workload's shape:
+    8 prompts x 4 samples of 1024 tokens registered from their token ids."""
+    wl = W.shared_prefix()
+    P, Sm, pt = wl.prompts, wl.samples, wl.prompt_tokens
+    bm = pk.BlockManager(wl.num_blocks, 16, free_order=W.free_order(wl.seed, wl.num_blocks))
+    prompts = [np.arange(pt, dtype=np.int32) + p * 10**6 for p in range(P)]
+    t0 = time.perf_counter()
+    shared = 0
+    for p in range(P):
+        for j in range(Sm):
+            shared += bm.add_seq_prefix(p * Sm + j, prompts[p])[1]
+    dt = time.perf_counter() - t0
+    used = wl.num_blocks - bm.num_free()
+    return {"sequences": P * Sm, "prompt_tokens": pt, "blocks_used": used,
+            "blocks_without_sharing": P * Sm * -(-pt // 16), "shared_blocks": shared,
+            "host_us_per_sequence": round(dt / (P * Sm) * 1e6, 1)}
 
 
 def swap_probe(pk, torch, np, eng, q, dev, nseq=16, rounds=3):

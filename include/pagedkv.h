@@ -334,6 +334,22 @@ pa_status pa_bm_destroy(pa_bm* bm);
  * more blocks than the window), PA_ERR_OUT_OF_BLOCKS. */
 pa_status pa_bm_add_seq(pa_bm* bm, int64_t seq, int32_t prefill_tokens, int64_t* slots_out);
 
+/* Prefix caching: register seq from its n token ids (host int32), sharing
+ * cached blocks. A system prompt or a common prefix is stored once and reused
+ * ("KV Cache与长上下文管理", section 二 item 2). Each leading full block is looked
+ * up under the key (previous physical block of the sequence or -1, the
+ * block's block_size token ids); a live block under that key is shared (count
+ * + 1). From the first miss on, blocks are fresh; fresh full blocks enter the
+ * index. A key names the whole prefix, since it includes the block before.
+ * The partly filled last block is never shared. A block leaves the index when
+ * its count reaches zero. slots_out [n] receives each token's slot, -1 for
+ * tokens of shared blocks (pa_write_kv skips them); *shared_blocks the number
+ * of shared blocks. Errors: PA_ERR_STATE (seq exists), PA_ERR_UNSUPPORTED
+ * (manager with a ring), PA_ERR_OUT_OF_BLOCKS (nothing changes),
+ * PA_ERR_INVALID_ARG. */
+pa_status pa_bm_add_seq_prefix(pa_bm* bm, int64_t seq, const int32_t* tokens, int32_t n,
+                               int64_t* slots_out, int32_t* shared_blocks);
+
 /* child shares every block of parent; each count rises by one.
  * Errors: PA_ERR_STATE (unknown or swapped-out parent, existing child). */
 pa_status pa_bm_fork(pa_bm* bm, int64_t parent, int64_t child);

@@ -23,8 +23,16 @@
 //    one only loses a count. Swap-in takes device blocks from the free list
 //    and reports (host, device) pairs; host blocks return to the host list.
 //    A swapped-out sequence cannot append, fork or be exported.
+//  * Prefix caching ("KV Cache与长上下文管理", section 二 item 2: a common prefix
+//    is stored once and reused). A sequence registered from its token ids
+//    shares every leading full block found under the key (previous physical
+//    block or -1, the block's token ids); the rest are fresh and registered.
+//    Keying on the previous block makes a match imply the whole prefix
+//    matches. A block leaves the index when its count reaches zero. Not
+//    offered with a ring (evicted blocks would leave stale keys).
 //  * Every call is atomic; batched appends roll back through an undo log.
 #include <algorithm>
+#include <cstring>
 #include <deque>
 #include <new>
 #include <unordered_map>
@@ -42,6 +50,30 @@ struct Seq {
 };
 
 enum class Kind : int8_t { kInPlace, kFresh, kRingReuse, kRingFresh, kCow };
+
+// Key of a full block in the prefix index: the physical block before it in
+// the sequence (-1 for the first) and the block's token ids.
+struct PrefixKey {
+  int32_t prev;
+  std::vector<int32_t> tokens;
+  bool operator==(const PrefixKey& o) const { return prev == o.prev && tokens == o.tokens; }
+};
+
+struct PrefixKeyHash {
+  size_t operator()(const PrefixKey& k) const {
+    // FNV-1a over the previous block id and the token ids.
+    uint64_t h = 1469598103934665603ull;
+    auto mix = [&h](uint32_t x) {
+      for (int i = 0; i < 4; ++i) {
+        h ^= (x >> (8 * i)) & 0xffu;
+        h *= 1099511628211ull;
+      }
+    };
+    mix(uint32_t(k.prev));
+    for (int32_t t : k.tokens) mix(uint32_t(t));
+    return size_t(h);
+  }
+};
 
 struct Undo {
   int64_t seq;
@@ -61,6 +93,22 @@ struct pa_bm {
   std::unordered_map<int64_t, Seq> seqs;
   int32_t num_host_blocks = 0;
   std::deque<int32_t> host_free;
+  std::unordered_map<PrefixKey, int32_t, PrefixKeyHash> prefix;   // key -> block
+  std::unordered_map<int32_t, PrefixKey> prefix_key;               // block -> its key
+
+  // Drop one count of device block b; at zero it returns to the free list
+  // (tail) and leaves the prefix index.
+  void release(int32_t b) {
+    ref[b] -= 1;
+    if (ref[b] == 0) {
+      free_list.push_back(b);
+      auto it = prefix_key.find(b);
+      if (it != prefix_key.end()) {
+        prefix.erase(it->second);
+        prefix_key.erase(it);
+      }
+    }
+  }
 
   int64_t live_tokens(const Seq& s) const { return s.tokens - int64_t(block_size) * s.evicted; }
 
@@ -220,6 +268,55 @@ pa_status pa_bm_add_seq(pa_bm* bm, int64_t seq, int32_t prefill_tokens, int64_t*
   return PA_OK;
 }
 
+pa_status pa_bm_add_seq_prefix(pa_bm* bm, int64_t seq, const int32_t* tokens, int32_t n, int64_t* slots_out,
+                               int32_t* shared_blocks) {
+  if (!bm || n < 0 || (n > 0 && (!tokens || !slots_out)) || !shared_blocks)
+    return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_add_seq_prefix: bad arguments");
+  if (bm->window > 0) return pa::fail(PA_ERR_UNSUPPORTED, "pa_bm_add_seq_prefix: prefix caching with a ring");
+  if (bm->seqs.count(seq))
+    return pa::fail(PA_ERR_STATE, "pa_bm_add_seq_prefix: sequence %lld exists", (long long)seq);
+  const int32_t bs = bm->block_size;
+  const int32_t nb = (n + bs - 1) / bs;
+  // Leading full blocks already in the index.
+  std::vector<int32_t> hits;
+  PrefixKey key{-1, {}};
+  for (int32_t i = 0; i < nb && (i + 1) * bs <= n; ++i) {
+    key.tokens.assign(tokens + int64_t(i) * bs, tokens + int64_t(i + 1) * bs);
+    auto it = bm->prefix.find(key);
+    if (it == bm->prefix.end()) break;
+    hits.push_back(it->second);
+    key.prev = it->second;
+  }
+  const int32_t shared = int32_t(hits.size());
+  if (size_t(nb - shared) > bm->free_list.size())
+    return pa::fail(PA_ERR_OUT_OF_BLOCKS, "pa_bm_add_seq_prefix: needs %d blocks, %zu free", nb - shared,
+                    bm->free_list.size());
+  Seq s;
+  int32_t prev = -1;
+  for (int32_t i = 0; i < nb; ++i) {
+    int32_t b;
+    if (i < shared) {
+      b = hits[i];
+      bm->ref[b] += 1;
+    } else {
+      b = bm->take_free();
+      if ((i + 1) * bs <= n) {
+        PrefixKey k{prev, std::vector<int32_t>(tokens + int64_t(i) * bs, tokens + int64_t(i + 1) * bs)};
+        bm->prefix_key.emplace(b, k);
+        bm->prefix.emplace(std::move(k), b);
+      }
+    }
+    s.table.push_back(b);
+    prev = b;
+  }
+  s.tokens = n;
+  for (int32_t t = 0; t < n; ++t)
+    slots_out[t] = t / bs < shared ? -1 : int64_t(s.table[t / bs]) * bs + t % bs;
+  bm->seqs.emplace(seq, std::move(s));
+  *shared_blocks = shared;
+  return PA_OK;
+}
+
 pa_status pa_bm_fork(pa_bm* bm, int64_t parent, int64_t child) {
   if (!bm) return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_fork: bm is NULL");
   auto it = bm->seqs.find(parent);
@@ -272,10 +369,7 @@ pa_status pa_bm_free_seq(pa_bm* bm, int64_t seq) {
   if (it->second.swapped) {
     for (int32_t hb : it->second.table) bm->host_free.push_back(hb);
   } else {
-    for (int32_t b : it->second.table) {
-      bm->ref[b] -= 1;
-      if (bm->ref[b] == 0) bm->free_list.push_back(b);
-    }
+    for (int32_t b : it->second.table) bm->release(b);
   }
   bm->seqs.erase(it);
   return PA_OK;
@@ -323,8 +417,7 @@ pa_status pa_bm_swap_out(pa_bm* bm, int64_t seq, int32_t* pairs_out, int32_t cap
     bm->host_free.pop_front();
     pairs_out[2 * i] = b;
     pairs_out[2 * i + 1] = hb;
-    bm->ref[b] -= 1;
-    if (bm->ref[b] == 0) bm->free_list.push_back(b);
+    bm->release(b);
     s.table[i] = hb;
   }
   s.swapped = true;

@@ -115,6 +115,15 @@ class PagedDecodeEngine:
             N.pa_write_kv(self.pool, k_rows, v_rows, torch.from_numpy(slots).to(self.device))
         return slots
 
+    def add_sequence_prefix(self, seq: int, tokens, k_rows, v_rows):
+        """Register ``seq`` from its token ids, sharing cached full blocks
+        (prefix caching), and write the rows of the tokens not shared.
+        Returns the number of shared blocks."""
+        slots, shared = self.bm.add_seq_prefix(seq, tokens)
+        if slots.size and shared * self.block_size < slots.size:
+            N.pa_write_kv(self.pool, k_rows, v_rows, torch.from_numpy(slots).to(self.device))
+        return shared
+
     def fork(self, parent: int, child: int) -> None:
         self.bm.fork(parent, child)
 

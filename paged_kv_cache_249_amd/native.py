@@ -88,6 +88,7 @@ _SIGS = {
     "pa_bm_ref_count": ([_vp, _i32, _pi32], _i32),
     "pa_bm_num_free": ([_vp, _pi32], _i32),
     "pa_bm_free_list": ([_vp, _vp, _i32, _pi32], _i32),
+    "pa_bm_add_seq_prefix": ([_vp, _i64, _vp, _i32, _vp, _pi32], _i32),
     "pa_bm_set_host_pool": ([_vp, _i32, _vp], _i32),
     "pa_bm_swap_out": ([_vp, _i64, _vp, _i32, _pi32], _i32),
     "pa_bm_swap_in": ([_vp, _i64, _vp, _i32, _pi32], _i32),
@@ -429,6 +430,16 @@ class BlockManager:
         _check(lib.pa_bm_add_seq(self.handle, seq, prefill_tokens,
                                  _np_ptr(slots) if slots.size else None), "pa_bm_add_seq")
         return slots
+
+    def add_seq_prefix(self, seq: int, tokens):
+        """Register ``seq`` from its token ids sharing cached full blocks:
+        returns (slots with -1 for shared tokens, number of shared blocks)."""
+        toks = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32).reshape(-1))
+        slots = np.empty(max(toks.size, 1), dtype=np.int64)
+        shared = C.c_int32()
+        _check(lib.pa_bm_add_seq_prefix(self.handle, seq, _np_ptr(toks) if toks.size else None, toks.size,
+                                        _np_ptr(slots), C.byref(shared)), "pa_bm_add_seq_prefix")
+        return slots[:toks.size], shared.value
 
     def fork(self, parent: int, child: int) -> None:
         _check(lib.pa_bm_fork(self.handle, parent, child), "pa_bm_fork")
