@@ -26,6 +26,9 @@ Sources, cited by page title and section:
   (fragmentation), and the quantisation list (FP16 -> INT8).
 * "PagedAttention的终极用途" (staroceans.org video script), part 三: the same
   sliding-window-by-table-edit statement.
+* "PagedAttention 的技术溯源与演进脉络" (mjmagnets.cn), §4.1 item 2: mixed-
+  precision page management (FP16 hot pages, INT8 rarely used pages, host
+  backup for cold pages).
 
 Modules:
 
@@ -35,12 +38,16 @@ Modules:
 * :mod:`oracle.cache_ops` — scatter of new K/V rows into slots, block copy, and
   the int8 quantise-on-write rule.
 * :mod:`oracle.block_manager` — free list, reference counts, copy-on-write on
-  append and the sliding-window ring, as a plain Python model.
+  append, the sliding-window ring, swapping to a host pool and prefix caching,
+  as a plain Python model.
+* :mod:`oracle.mixed` — mixed-precision pages: an fp16 hot tail block per
+  sequence, int8 cold blocks demoted from it, and decode over both.
 
 Parity unpinned (checked only against this oracle's own definition, because
 the pages fix no value for it): the merge rule used when int8 rows are written
 into a block that already holds rows (requantisation on a grown scale), and the
-choice of which free block is handed out (a FIFO over a seeded permutation).
+choice of which free block is handed out (a FIFO over a seeded permutation),
+the swap and prefix-caching policies, and the hot/cold split of mixed pages.
 """
 
-from . import attention, block_manager, cache_ops, paging  # noqa: F401
+from . import attention, block_manager, cache_ops, mixed, paging  # noqa: F401
