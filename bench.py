@@ -541,6 +541,7 @@ def extras(eng, wl, q, ptok, dev):
     res["block_size_sweep"] = block_size_sweep(pk, W, torch, np, wl, ctx, q, out, order, t_contig, nbytes, dev)
     res["swap"] = swap_probe(pk, torch, np, eng, q, dev)
     res["prefix_cache"] = prefix_probe(pk, W, np)
+    res["mixed_precision"] = mixed_probe(pk, W, torch, np, wl, ctx, q, t_paged, nbytes, dev)
     # Streaming copy probe: achievable HBM bandwidth (read + write bytes).
     n = 1 << 30
     a = torch.empty(n, dtype=torch.uint8, device=dev)
@@ -552,6 +553,37 @@ def extras(eng, wl, q, ptok, dev):
     t_read = _time_calls(lambda: pk.pa_stream_read(big, sink))
     res["stream_read_gbs"] = round(big.numel() / t_read / 1e9, 1)
     return res
+
+
+def mixed_probe(pk, W, torch, np, wl, ctx, q, t_fp16, fp16_bytes, dev):
+    """The same contexts stored as mixed-precision pages (int8 cold blocks,
+    one fp16 hot block per sequence): decode time and bytes against the
+    all-fp16 paged decode of the same batch."""
+    from paged_kv_cache_249_amd.engine import MixedDecodeEngine
+    S, H, D = wl.num_seqs, wl.num_heads, wl.head_dim
+    n_cold = [max(0, -(-int(c) // 16) - 1) for c in ctx]
+    nc = -(-5 * sum(n_cold) // 4)
+    eng = MixedDecodeEngine(nc, S, H, D, S, max(n_cold) + 1, cold_order=W.free_order(wl.seed, nc), device=dev)
+    for s, c in enumerate(ctx):
+        k = W.normal_torch((int(c), H, D), wl.seed, W.STREAM_K, s, dtype=torch.float16, device=dev)
+        v = W.normal_torch((int(c), H, D), wl.seed, W.STREAM_V, s, dtype=torch.float16, device=dev)
+        eng.add_sequence(s, k, v)
+        del k, v
+    tables, hot, cl = eng.mbm.export(np.arange(S), eng.cap)
+    tabd, hotd, ctxd = (torch.from_numpy(a).to(dev) for a in (tables, hot, cl))
+    order = torch.from_numpy(np.argsort(-cl, kind="stable").astype(np.int32)).to(dev)
+    out = torch.empty_like(q)
+    maxc = int(cl.max())
+    t = _time_calls(lambda: pk.pa_decode_mixed(eng.cold, eng.hot, q, out, tabd, hotd, ctxd, maxc,
+                                               seq_order=order))
+    cold_tokens = 16 * sum(n_cold)
+    hot_tokens = int(cl.sum()) - cold_tokens
+    nbytes = cold_tokens * H * D * 2 + sum(n_cold) * H * 2 * 2 + hot_tokens * H * D * 2 * 2
+    del eng
+    torch.cuda.empty_cache()
+    return {"decode_us": round(t * 1e6, 2), "bytes": int(nbytes), "gbs": round(nbytes / t / 1e9, 1),
+            "fp16_decode_us": round(t_fp16 * 1e6, 2), "fp16_bytes": int(fp16_bytes),
+            "speedup_vs_fp16": round(t_fp16 / t, 3), "cold_token_fraction": round(cold_tokens / int(cl.sum()), 4)}
 
 
 def prefix_probe(pk, W, np):

@@ -421,6 +421,78 @@ pa_status pa_bm_is_swapped(const pa_bm* bm, int64_t seq, int32_t* out);
 /* The host free list in order (head first) into out [cap]; *n its length. */
 pa_status pa_bm_host_free_list(const pa_bm* bm, int32_t* out, int32_t cap, int32_t* n);
 
+/* ----------------------------------------------------------------------------
+ * Mixed-precision pages: an fp16 hot block per sequence, int8 cold blocks.
+ *
+ * Pages used often stay in FP16 and pages used rarely are stored as INT8
+ * ("PagedAttention 的技术溯源与演进脉络", §4.1 item 2, mixed-precision page
+ * management; FP16 -> INT8 halves the KV bytes, "KV Cache与长上下文管理",
+ * section 二.3). Here the hot page of a sequence is its newest block, the one
+ * each decode step writes. Two pools with block_size 16 and the same heads and
+ * head_dim: a PA_F16 "hot" pool (one block per sequence for its whole life)
+ * and a PA_I8 "cold" pool (with its scales). A sequence of ctx tokens holds
+ * n_cold = max(0, ceil(ctx / 16) - 1) cold blocks (tokens [0, 16 n_cold)) and
+ * its hot block (tokens [16 n_cold, ctx)).
+ *
+ * The manager (pa_mbm_*, host only, FIFO free lists in caller-given orders,
+ * freed blocks to the tail, every call atomic):
+ *  - pa_mbm_add_seq: prefill of n tokens; cold_slots_out / hot_slots_out [n]
+ *    give each token's slot in the cold or the hot pool (-1 in the other):
+ *    write them with pa_write_kv on each pool (a whole cold block in one call
+ *    is quantised as one group: the demotion rule below).
+ *  - pa_mbm_append_batch: one token per sequence; hot_slots_out [n] is its
+ *    slot in the hot pool; when a sequence's hot block is full (a multiple of
+ *    16 tokens, > 0) the block is demoted first: a fresh cold block is taken
+ *    and the (hot, cold) pair reported in demote_pairs_out [n][2] (*n_pairs of
+ *    them), and the token goes to offset 0 of the same hot block.
+ *  - pa_mbm_fork: child shares the parent's cold blocks (counts + 1) and takes
+ *    a fresh hot block; *copy_src / *copy_dst is the hot pair to copy
+ *    (pa_copy_blocks on the hot pool).
+ *  - pa_mbm_export: cold tables [n][cap] (-1 padded), hot blocks [n], context
+ *    lengths [n].
+ * Errors: PA_ERR_STATE (unknown / existing sequence), PA_ERR_OUT_OF_BLOCKS,
+ * PA_ERR_OUT_OF_RANGE (cap), PA_ERR_INVALID_ARG. */
+typedef struct pa_mbm pa_mbm;
+pa_status pa_mbm_create(int32_t num_cold, int32_t num_hot, const int32_t* cold_order,
+                        const int32_t* hot_order, pa_mbm** out);
+pa_status pa_mbm_destroy(pa_mbm* m);
+pa_status pa_mbm_add_seq(pa_mbm* m, int64_t seq, int32_t prefill_tokens, int64_t* cold_slots_out,
+                         int64_t* hot_slots_out);
+pa_status pa_mbm_append_batch(pa_mbm* m, const int64_t* seqs, int32_t n, int64_t* hot_slots_out,
+                              int32_t* demote_pairs_out, int32_t* n_pairs);
+pa_status pa_mbm_fork(pa_mbm* m, int64_t parent, int64_t child, int32_t* copy_src, int32_t* copy_dst);
+pa_status pa_mbm_free_seq(pa_mbm* m, int64_t seq);
+pa_status pa_mbm_export(const pa_mbm* m, const int64_t* seqs, int32_t n, int32_t* cold_tables,
+                        int32_t cap, int32_t* hot_out, int32_t* ctx_out);
+pa_status pa_mbm_ref_count(const pa_mbm* m, int32_t cold_block, int32_t* out);
+/* Free lists in order (head first); either output may be NULL to query sizes. */
+pa_status pa_mbm_free_lists(const pa_mbm* m, int32_t* cold_out, int32_t cold_cap, int32_t* n_cold,
+                            int32_t* hot_out, int32_t hot_cap, int32_t* n_hot);
+
+/* Demote hot blocks: for every (hot, cold) pair ([n][2] device int32) and
+ * head, the hot block's 16 fp16 rows of K (and of V) are quantised as one
+ * group into the cold block: s = fp16(max|x| / 127) (IEEE fp32 divide, RNE),
+ * codes clamp(rne(x / s), -127, 127) (0 if s == 0) — the pa_write_kv int8
+ * rule for a whole block written at once. Ids outside their pools flag
+ * PA_DEV_BAD_PAIR and are skipped. Errors: PA_ERR_INVALID_ARG (pool kinds or
+ * geometry do not match), PA_ERR_HIP. */
+pa_status pa_demote_blocks(pa_pool* hot_pool, pa_pool* cold_pool, const int32_t* pairs, int32_t n,
+                           pa_stream stream);
+
+/* Paged decode over mixed-precision pages: as pa_decode_ordered, where token t
+ * of sequence s is cold row K[cold_tables[s][t / 16]][h][t % 16] * scale for
+ * t < 16 n_cold, and hot row Khot[hot_blocks[s]][h][t - 16 n_cold] otherwise.
+ * partition_tokens: 0 or a multiple of 16; workspace as pa_decode. A hot block
+ * id outside the hot pool flags PA_DEV_BAD_TABLE_ENTRY and its rows are
+ * masked. Errors: as pa_decode, plus PA_ERR_INVALID_ARG when the pools are not
+ * an int8 cold pool and an fp16 hot pool of block size 16 with equal heads and
+ * head_dim. */
+pa_status pa_decode_mixed(pa_pool* cold_pool, pa_pool* hot_pool, const void* q, pa_dtype q_dtype, void* out,
+                          const int32_t* cold_tables, int32_t max_blocks, const int32_t* hot_blocks,
+                          const int32_t* context_lens, const int32_t* seq_order, int32_t num_seqs,
+                          int32_t max_context_len, float sm_scale, int32_t partition_tokens,
+                          void* workspace, int64_t workspace_bytes, pa_stream stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -349,6 +349,67 @@ pa_status pa_write_decode(pa_pool* pool, const void* k_new, const void* v_new, p
   return decode_common("pa_write_decode", a, workspace, workspace_bytes, stream);
 }
 
+// The two pools of mixed-precision pages: int8 cold, fp16 hot, 16-token
+// blocks, equal heads and head_dim.
+static pa_status check_mixed_pools(const char* fn, const pa_pool* cold, const pa_pool* hot) {
+  if (!cold || !hot) return fail(PA_ERR_INVALID_ARG, "%s: pool is NULL", fn);
+  if (cold->kv_dtype != PA_I8 || hot->kv_dtype != PA_F16 || cold->block_size != 16 || hot->block_size != 16 ||
+      cold->num_heads != hot->num_heads || cold->head_dim != hot->head_dim)
+    return fail(PA_ERR_INVALID_ARG, "%s: needs an int8 cold pool and an fp16 hot pool of 16-token blocks with "
+                "equal heads and head_dim", fn);
+  return PA_OK;
+}
+
+pa_status pa_demote_blocks(pa_pool* hot_pool, pa_pool* cold_pool, const int32_t* pairs, int32_t n,
+                           pa_stream stream) {
+  pa_status st = check_mixed_pools("pa_demote_blocks", cold_pool, hot_pool);
+  if (st != PA_OK) return st;
+  if (n < 0) return fail(PA_ERR_INVALID_ARG, "pa_demote_blocks: n=%d", n);
+  if (n == 0) return PA_OK;
+  if (!pairs) return fail(PA_ERR_INVALID_ARG, "pa_demote_blocks: pairs is NULL");
+  if (n > 65535) return fail(PA_ERR_INVALID_ARG, "pa_demote_blocks: n=%d > 65535 pairs per call", n);
+  return hip_status("pa_demote_blocks", pa::launch_demote_blocks(hot_pool, cold_pool, pairs, n, stream));
+}
+
+pa_status pa_decode_mixed(pa_pool* cold_pool, pa_pool* hot_pool, const void* q, pa_dtype q_dtype, void* out,
+                          const int32_t* cold_tables, int32_t max_blocks, const int32_t* hot_blocks,
+                          const int32_t* context_lens, const int32_t* seq_order, int32_t num_seqs,
+                          int32_t max_context_len, float sm_scale, int32_t partition_tokens, void* workspace,
+                          int64_t workspace_bytes, pa_stream stream) {
+  pa_status st = check_mixed_pools("pa_decode_mixed", cold_pool, hot_pool);
+  if (st != PA_OK) return st;
+  if (!cold_tables || !hot_blocks) return fail(PA_ERR_INVALID_ARG, "pa_decode_mixed: tables are NULL");
+  if (max_context_len < 0 || max_blocks < 0 || int64_t(max_blocks) * 16 + 16 < int64_t(max_context_len))
+    return fail(PA_ERR_INVALID_ARG, "pa_decode_mixed: max_blocks=%d cannot hold max_context_len=%d", max_blocks,
+                max_context_len);
+  pa::DecodeArgs a{};
+  a.q = q;
+  a.q_dtype = q_dtype;
+  a.out = out;
+  a.k = cold_pool->k_cache;
+  a.v = cold_pool->v_cache;
+  a.k_scale = cold_pool->k_scale;
+  a.v_scale = cold_pool->v_scale;
+  a.kv_dtype = PA_I8;
+  a.tables = cold_tables;
+  a.max_blocks = max_blocks;
+  a.block_size = 16;
+  a.ctx = context_lens;
+  a.order = seq_order;
+  a.num_seqs = num_seqs;
+  a.num_heads = cold_pool->num_heads;
+  a.head_dim = cold_pool->head_dim;
+  a.num_blocks = cold_pool->num_blocks;
+  a.max_ctx = max_context_len;
+  a.sm_scale = sm_scale;
+  a.partition_tokens = partition_tokens;
+  a.hot_k = hot_pool->k_cache;
+  a.hot_v = hot_pool->v_cache;
+  a.hot_blocks = hot_blocks;
+  a.num_hot = hot_pool->num_blocks;
+  return decode_common("pa_decode_mixed", a, workspace, workspace_bytes, stream);
+}
+
 pa_status pa_decode_contiguous(const void* k, const void* v, pa_dtype kv_dtype, int32_t num_heads,
                                int32_t head_dim, int32_t max_tokens, const void* q, pa_dtype q_dtype,
                                void* out, const int32_t* context_lens, const int32_t* seq_order,

@@ -158,6 +158,58 @@ __global__ __launch_bounds__(kThreads) void write_kv_i8_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Demotion of full fp16 hot blocks into int8 cold blocks (mixed-precision
+// pages): one wave per (pair, head, tensor). The (block, head) tile of 16
+// fp16 rows is 16 * D contiguous values; lane l quantises the kPer values
+// starting at l * kPer. The arithmetic is write_kv_i8_kernel's for a group
+// that writes the whole block (so the earlier scale plays no part).
+template <int D>
+__global__ __launch_bounds__(kThreads) void demote_kernel(const int32_t* __restrict__ pairs, int n,
+                                                          const _Float16* __restrict__ hot_k,
+                                                          const _Float16* __restrict__ hot_v,
+                                                          int8_t* __restrict__ cold_k, int8_t* __restrict__ cold_v,
+                                                          _Float16* __restrict__ k_scale,
+                                                          _Float16* __restrict__ v_scale, int H, int num_hot,
+                                                          int num_cold, int32_t* err) {
+  constexpr int kRows = 16;
+  constexpr int kPer = kRows * D / kWave;   // values per lane: 32 (D = 128) or 16 (D = 64)
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t wid = int64_t(blockIdx.x) * (kThreads / kWave) + wave_uniform(threadIdx.x / kWave);
+  if (wid >= int64_t(n) * H) return;
+  const int pair = int(wid / H);
+  const int h = int(wid % H);
+  const bool is_v = blockIdx.y != 0;
+  const int src = pairs[2 * pair];
+  const int dst = pairs[2 * pair + 1];
+  if (unsigned(src) >= unsigned(num_hot) || unsigned(dst) >= unsigned(num_cold)) {
+    if (lane == 0 && h == 0 && !is_v) flag_error(err, PA_DEV_BAD_PAIR);
+    return;
+  }
+  const _Float16* x = (is_v ? hot_v : hot_k) + (int64_t(src) * H + h) * kRows * D + lane * kPer;
+  _Float16 vals[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer / 8; ++j)
+    *reinterpret_cast<uint4*>(vals + 8 * j) = reinterpret_cast<const uint4*>(x)[j];
+  float a = 0.f;
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) a = fmaxf(a, fabsf(float(vals[e])));
+  a = wave_max(a);
+  const float s = float(_Float16(a / 127.0f));
+  int8_t codes[kPer];
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) {
+    float qf = 0.f;
+    if (s > 0.f) qf = fminf(fmaxf(__builtin_rintf(float(vals[e]) / s), -127.f), 127.f);
+    codes[e] = int8_t(qf);
+  }
+  int8_t* y = (is_v ? cold_v : cold_k) + (int64_t(dst) * H + h) * kRows * D + lane * kPer;
+#pragma unroll
+  for (int j = 0; j < kPer / 16; ++j)
+    reinterpret_cast<uint4*>(y)[j] = *reinterpret_cast<const uint4*>(codes + 16 * j);
+  if (lane == 0) (is_v ? v_scale : k_scale)[int64_t(dst) * H + h] = _Float16(s);
+}
+
+// ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void copy_blocks_kernel(const int32_t* __restrict__ pairs, int n,
                                                                char* __restrict__ k, char* __restrict__ v,
                                                                int64_t block_bytes, _Float16* ks,
@@ -337,6 +389,24 @@ int launch_write_kv(const pa_pool* p, const void* k_new, const void* v_new, pa_d
                            : launch_write_i8<_Float16>(p, k_new, v_new, slots, n, st);
   }
   return int(hipErrorInvalidValue);
+}
+
+int launch_demote_blocks(const pa_pool* hot, const pa_pool* cold, const int32_t* pairs, int32_t n, void* stream) {
+  if (n == 0) return 0;
+  const int64_t waves = int64_t(n) * hot->num_heads;
+  const dim3 grid(unsigned((waves + (kThreads / kWave) - 1) / (kThreads / kWave)), 2);
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, static_cast<hipStream_t>(stream), pairs, n,
+                       static_cast<const _Float16*>(hot->k_cache), static_cast<const _Float16*>(hot->v_cache),
+                       static_cast<int8_t*>(cold->k_cache), static_cast<int8_t*>(cold->v_cache),
+                       static_cast<_Float16*>(cold->k_scale), static_cast<_Float16*>(cold->v_scale),
+                       hot->num_heads, hot->num_blocks, cold->num_blocks, device_error_ptr());
+  };
+  if (hot->head_dim == 64)
+    go(demote_kernel<64>);
+  else
+    go(demote_kernel<128>);
+  return int(hipGetLastError());
 }
 
 int launch_copy_blocks(const pa_pool* p, const int32_t* pairs, int32_t n, void* stream) {

@@ -45,6 +45,12 @@
 // reduce kernel merges partitions as out = sum w_p o_p / sum w_p with
 // w_p = exp(m_p - M) l_p. Sequences with one partition are written directly.
 //
+// Mixed-precision pages. With an fp16 hot pool, the table holds the int8
+// cold blocks and the last unit of every sequence comes from its hot block:
+// the wave that owns that unit reads its fp16 rows after the loop, in the
+// int8 lane layout (each lane 16 values of a row), and folds them into the
+// same softmax stream.
+//
 // XCD-aware order: work item w enumerates (partition, head, sequence) with the
 // sequence fastest (or, when the caller passes a schedule, (partition,
 // scheduled sequence, head) with the head fastest, e.g. longest first). Workgroup ids are dealt to the 8 XCDs round-robin; groups
@@ -134,6 +140,11 @@ struct Params {
   const void* v_new;
   const int64_t* slots;
   int32_t new_is_f32;
+  // Mixed-precision pages: fp16 hot pool and each sequence's hot block.
+  const char* hot_k;
+  const char* hot_v;
+  const int32_t* hot_blocks;
+  int32_t num_hot;
 };
 
 // Bijection from dispatch order g to work item w: inside every chunk of
@@ -257,7 +268,8 @@ __device__ __forceinline__ QT to_out(float x) {
 }
 
 // NEW: element type of the fused-write source rows (void = no fused write).
-template <typename KV, typename QT, int D, bool kPaged, typename NEW>
+// kMixed: int8 cold pool through the table plus an fp16 hot block per sequence.
+template <typename KV, typename QT, int D, bool kPaged, typename NEW, bool kMixed = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PA_DECODE_MIN_WAVES)))
 void decode_kernel(Params p, const int32_t* __restrict__ tables, const int32_t* __restrict__ seq_ctx,
                    const int64_t* __restrict__ new_slots) {
@@ -333,12 +345,17 @@ void decode_kernel(Params p, const int32_t* __restrict__ tables, const int32_t* 
     load_words(vsrc, rv);
   }
 
+  static_assert(!kMixed || (kInt8 && kPaged && std::is_same<NEW, void>::value), "mixed pages: int8 cold pool");
+  int hot_blk = 0;
+  if constexpr (kMixed) hot_blk = p.hot_blocks[s];
   const bool bad_ctx = ctx < 0 || ctx > p.max_ctx;
   if (bad_ctx) ctx = ctx < 0 ? 0 : p.max_ctx;
   const int nunits = (ctx + kTileRows - 1) / kTileRows;
   const int seq_parts = nunits == 0 ? 1 : (nunits + p.partition_units - 1) / p.partition_units;
   if (part >= seq_parts) return;
-  const int unit_end = min(unit_begin + p.partition_units, nunits);
+  // Units read through the table (mixed pages: all but the last, hot one).
+  const int table_units = kMixed ? max(nunits - 1, 0) : nunits;
+  const int unit_end = min(unit_begin + p.partition_units, table_units);
   const int iters = first < unit_end ? (unit_end - first + kWaves - 1) / kWaves : 0;
 
   // Table entry of the wave's k-th unit. Reads are wave-uniform and the loop
@@ -537,6 +554,72 @@ void decode_kernel(Params p, const int32_t* __restrict__ tables, const int32_t* 
     }
   }
 
+  // Mixed pages: the hot unit, by the wave that owns it.
+  if constexpr (kMixed) {
+    const int hu = nunits - 1;
+    if (nunits > 0 && hu >= unit_begin && hu < unit_begin + p.partition_units &&
+        wave == (hu - unit_begin) % kWaves) {
+      constexpr int kHW = EPC * 2 / 16;   // 16-byte words of fp16 per lane and row
+      const bool ok = unsigned(hot_blk) < unsigned(p.num_hot);
+      bad_entry |= !ok;
+      const int64_t tile = (int64_t(ok ? hot_blk : 0) * p.num_heads + h) * kTileRows * D * 2;
+      uint4 hk[NLD][kHW], hv[NLD][kHW];
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) {
+        const int64_t off = tile + int64_t(i * TPI + grp) * D * 2 + col * EPC * 2;
+#pragma unroll
+        for (int j = 0; j < kHW; ++j) {
+          hk[i][j] = *reinterpret_cast<const uint4*>(p.hot_k + off + 16 * j);
+          hv[i][j] = *reinterpret_cast<const uint4*>(p.hot_v + off + 16 * j);
+        }
+      }
+      const int t0 = hu * kTileRows;
+      float sc[NLD];
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) {
+        float d = 0.f;
+#pragma unroll
+        for (int j = 0; j < kHW; ++j) {
+          const uint32_t w[4] = {hk[i][j].x, hk[i][j].y, hk[i][j].z, hk[i][j].w};
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            d = fmaf(lo_f16(w[c]), qs.f[8 * j + 2 * c], d);
+            d = fmaf(hi_f16(w[c]), qs.f[8 * j + 2 * c + 1], d);
+          }
+        }
+        sc[i] = group_sum<CPT>(d) * p.scale_log2;
+        if (!ok || t0 + i * TPI + grp >= ctx) {
+          sc[i] = -INFINITY;
+#pragma unroll
+          for (int j = 0; j < kHW; ++j) hv[i][j] = make_uint4(0u, 0u, 0u, 0u);
+        }
+      }
+      float bmax = sc[0];
+#pragma unroll
+      for (int i = 1; i < NLD; ++i) bmax = fmaxf(bmax, sc[i]);
+      const float mn = fmaxf(m, bmax);
+      const float alpha = __builtin_amdgcn_exp2f(m - mn);
+      l *= alpha;
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) acc[e] *= alpha;
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) {
+        const float pi = __builtin_amdgcn_exp2f(sc[i] - mn);
+        l += pi;
+#pragma unroll
+        for (int j = 0; j < kHW; ++j) {
+          const uint32_t w[4] = {hv[i][j].x, hv[i][j].y, hv[i][j].z, hv[i][j].w};
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            acc[8 * j + 2 * c] = fmaf(pi, lo_f16(w[c]), acc[8 * j + 2 * c]);
+            acc[8 * j + 2 * c + 1] = fmaf(pi, hi_f16(w[c]), acc[8 * j + 2 * c + 1]);
+          }
+        }
+      }
+      m = mn;
+    }
+  }
+
   if (patched && grp == new_row % TPI) {
     *reinterpret_cast<uint4*>(const_cast<char*>(p.k) + new_dst) = nk;
     *reinterpret_cast<uint4*>(const_cast<char*>(p.v) + new_dst) = nv;
@@ -619,7 +702,14 @@ __global__ __launch_bounds__(D) void reduce_kernel(Params p) {
 
 template <typename KV, typename QT, int D, bool kPaged>
 int launch_typed(const Params& p, int grid, int sh_count, hipStream_t st) {
-  if constexpr (kPaged && !std::is_same<KV, int8_t>::value) {
+  if constexpr (kPaged && std::is_same<KV, int8_t>::value) {
+    if (p.hot_blocks != nullptr)
+      hipLaunchKernelGGL((decode_kernel<KV, QT, D, kPaged, void, true>), dim3(grid), dim3(kThreads), 0, st, p,
+                         p.tables, p.ctx, p.slots);
+    else
+      hipLaunchKernelGGL((decode_kernel<KV, QT, D, kPaged, void>), dim3(grid), dim3(kThreads), 0, st, p, p.tables,
+                         p.ctx, p.slots);
+  } else if constexpr (kPaged) {
     if (p.slots != nullptr) {
       if (p.new_is_f32)
         hipLaunchKernelGGL((decode_kernel<KV, QT, D, kPaged, float>), dim3(grid), dim3(kThreads), 0, st, p,
@@ -685,6 +775,10 @@ int launch_decode(const DecodeArgs& a, void* stream) {
   p.v_new = a.v_new;
   p.slots = a.slots;
   p.new_is_f32 = a.new_dtype == PA_F32 ? 1 : 0;
+  p.hot_k = static_cast<const char*>(a.hot_k);
+  p.hot_v = static_cast<const char*>(a.hot_v);
+  p.hot_blocks = a.hot_blocks;
+  p.num_hot = a.num_hot;
   const int sh_count = a.num_seqs * a.num_heads;
   const int grid = sh_count * a.num_partitions;
   if (grid == 0) return 0;

@@ -80,12 +80,19 @@ struct DecodeArgs {
   const void* v_new;
   pa_dtype new_dtype;
   const int64_t* slots;
+  // Mixed-precision pages (pa_decode_mixed): nullptr hot_blocks = none. The
+  // pool above (k, v, scales) is then the int8 cold pool.
+  const void* hot_k;
+  const void* hot_v;
+  const int32_t* hot_blocks;
+  int32_t num_hot;
 };
 
 int launch_decode(const DecodeArgs& a, void* stream);
 int launch_write_kv(const pa_pool* p, const void* k_new, const void* v_new, pa_dtype src,
                     const int64_t* slots, int32_t n, void* stream);
 int launch_copy_blocks(const pa_pool* p, const int32_t* pairs, int32_t n, void* stream);
+int launch_demote_blocks(const pa_pool* hot, const pa_pool* cold, const int32_t* pairs, int32_t n, void* stream);
 // Device views of a host pool (pinned host memory) for launch_swap_blocks.
 struct SwapHost {
   void* k;

@@ -28,6 +28,93 @@ import torch
 from . import native as N
 
 
+class _Staging:
+    """Upload of a step's small arrays in one packed buffer.
+
+    ``fields`` is an ordered list of ``(name, torch dtype, per-sequence
+    shape)``; the last field is the only one whose upload is cut to the batch
+    (the table rows). Pinned host copies rotate through a ring guarded by
+    events, and two device copies alternate, each released by an event after
+    the last kernel that reads it.
+    """
+
+    def __init__(self, fields, max_seqs: int, device, depth: int, aux_stream: bool):
+        self.fields, self.max_seqs, self.device = fields, max_seqs, device
+        self.off, o = {}, 0
+        for name, dt, shape in fields:
+            self.off[name] = o
+            o += max_seqs * int(np.prod(shape, dtype=np.int64)) * torch.empty(0, dtype=dt).element_size()
+            o = -(-o // 8) * 8
+        self.bytes = -(-o // 16) * 16
+        self.dev = []
+        for _ in range(2):
+            v = self._views(torch.zeros(self.bytes, dtype=torch.uint8, device=device))
+            v["released"] = None          # event: the last kernel reading this buffer is done
+            self.dev.append(v)
+        self.cur = 0
+        self.ring = []
+        for _ in range(depth):
+            v = self._views(torch.empty(self.bytes, dtype=torch.uint8, pin_memory=True))
+            v = {k: (t if k == "buf" else t.numpy()) for k, t in v.items()}
+            v["event"] = None             # event: the upload that last read this buffer is done
+            self.ring.append(v)
+        self.next = 0
+        self.aux = torch.cuda.Stream(device=device) if aux_stream else None
+
+    def _views(self, buf):
+        m, out = self.max_seqs, {"buf": buf}
+        for name, dt, shape in self.fields:
+            size = torch.empty(0, dtype=dt).element_size() * m * int(np.prod(shape, dtype=np.int64))
+            o = self.off[name]
+            out[name] = buf[o:o + size].view(dt).view(m, *shape) if shape else buf[o:o + size].view(dt)
+        return out
+
+    def host(self):
+        """The next pinned buffer, once the upload that last read it is done."""
+        st = self.ring[self.next]
+        self.next = (self.next + 1) % len(self.ring)
+        if st["event"] is not None:
+            st["event"].synchronize()
+        return st
+
+    def upload(self, st, n: int, stream):
+        """Copy ``st`` (the last field up to row ``n``) into the next device
+        buffer; kernels on ``stream`` issued afterwards see it."""
+        name, dt, shape = self.fields[-1]
+        row = torch.empty(0, dtype=dt).element_size() * int(np.prod(shape, dtype=np.int64))
+        upto = -(-(self.off[name] + row * n) // 16) * 16
+        self.cur ^= 1
+        dv = self.dev[self.cur]
+        up = self.aux if self.aux is not None else stream
+        if dv["released"] is not None and up is not stream:
+            up.wait_event(dv["released"])     # no kernel still reads this device buffer
+        N.pa_stage_copy(dv["buf"], st["buf"], upto, stream=up)
+        uploaded = torch.cuda.Event()
+        uploaded.record(up)
+        st["event"] = uploaded
+        if up is not stream:
+            stream.wait_event(uploaded)
+        return dv
+
+    def release(self, dv, stream) -> None:
+        done = torch.cuda.Event()
+        done.record(stream)
+        dv["released"] = done
+
+
+class _Workspace:
+    """Split-K workspace on the device, grown geometrically."""
+
+    def __init__(self, device):
+        self.device, self.buf, self.bytes = device, None, 0
+
+    def get(self, need: int):
+        if need > self.bytes:
+            self.bytes = max(need, int(self.bytes * 1.5))
+            self.buf = torch.empty(self.bytes // 4 + 1, dtype=torch.float32, device=self.device)
+        return self.buf
+
+
 class PagedDecodeEngine:
     def __init__(self, num_blocks: int, num_heads: int, head_dim: int, kv_dtype: int,
                  max_seqs: int, max_blocks_per_seq: int, *, window_blocks: int = 0,
@@ -49,62 +136,36 @@ class PagedDecodeEngine:
         self.longest_first = longest_first
         # Float pools write the new token inside the decode launch (pa_write_decode).
         self.fuse_write = fuse_write and kv_dtype != N.PA_I8
-        dev = self.device
-        # Everything a step uploads lives in one packed buffer:
-        #   slots int64 [max_seqs] | ctx int32 [max_seqs] | order int32 [max_seqs]
-        #   | pairs int32 [max_seqs][2] | tables int32 [max_seqs][cap]
-        self._off_ctx = 8 * max_seqs
-        self._off_order = self._off_ctx + 4 * max_seqs
-        self._off_pairs = self._off_order + 4 * max_seqs
-        self._off_tables = self._off_pairs + 8 * max_seqs
-        self._stage_bytes = -(-(self._off_tables + 4 * max_seqs * self.cap) // 16) * 16
-        self._dev = []
-        for _ in range(2):
-            v = self._views(torch.zeros(self._stage_bytes, dtype=torch.uint8, device=dev))
+        # Everything a step uploads lives in one packed buffer.
+        self._stage = _Staging([("slots", torch.int64, ()), ("ctx", torch.int32, ()), ("order", torch.int32, ()),
+                                ("pairs", torch.int32, (2,)), ("tables", torch.int32, (self.cap,))],
+                               max_seqs, self.device, staging_depth, overlap_uploads)
+        for v in self._stage.dev:
             v["tables"].fill_(-1)
-            v["released"] = None          # event: the last kernel reading this buffer is done
-            self._dev.append(v)
-        self._cur = 0
-        self.workspace = None
-        self._ws_bytes = 0
-        self._staging = []
-        for _ in range(staging_depth):
-            v = self._views(torch.empty(self._stage_bytes, dtype=torch.uint8, pin_memory=True))
-            v = {k: (t if k == "buf" else t.numpy()) for k, t in v.items()}
-            v["event"] = None             # event: the upload that last read this buffer is done
-            self._staging.append(v)
-        self._next = 0
-        self._aux = torch.cuda.Stream(device=dev) if overlap_uploads else None
+        self._ws = _Workspace(self.device)
         self.last_ctx = np.zeros(0, dtype=np.int32)
         self.last_pairs = 0
 
-    def _views(self, buf):
-        m = self.max_seqs
-        return {
-            "buf": buf,
-            "slots": buf[:self._off_ctx].view(torch.int64),
-            "ctx": buf[self._off_ctx:self._off_order].view(torch.int32),
-            "order": buf[self._off_order:self._off_pairs].view(torch.int32),
-            "pairs": buf[self._off_pairs:self._off_tables].view(torch.int32).view(m, 2),
-            "tables": buf[self._off_tables:self._off_tables + 4 * m * self.cap].view(torch.int32).view(m, self.cap),
-        }
+    @property
+    def workspace(self):
+        return self._ws.buf
 
     # Device views of the staging buffer the latest step used.
     @property
     def slots(self):
-        return self._dev[self._cur]["slots"]
+        return self._stage.dev[self._stage.cur]["slots"]
 
     @property
     def tables(self):
-        return self._dev[self._cur]["tables"]
+        return self._stage.dev[self._stage.cur]["tables"]
 
     @property
     def ctx(self):
-        return self._dev[self._cur]["ctx"]
+        return self._stage.dev[self._stage.cur]["ctx"]
 
     @property
     def order(self):
-        return self._dev[self._cur]["order"]
+        return self._stage.dev[self._stage.cur]["order"]
 
     # -- setup -----------------------------------------------------------------
     def add_sequence(self, seq: int, k_rows=None, v_rows=None, prefill_tokens: int | None = None):
@@ -168,12 +229,7 @@ class PagedDecodeEngine:
         return pairs
 
     def _workspace_for(self, n: int, max_ctx: int, ptok: int):
-        need = N.pa_decode_workspace_bytes(self.pool, n, max_ctx, ptok)
-        if need > self._ws_bytes:
-            # Grow geometrically so that a growing context does not reallocate every step.
-            self._ws_bytes = max(need, int(self._ws_bytes * 1.5))
-            self.workspace = torch.empty(self._ws_bytes // 4 + 1, dtype=torch.float32, device=self.device)
-        return self.workspace
+        return self._ws.get(N.pa_decode_workspace_bytes(self.pool, n, max_ctx, ptok))
 
     # -- the step ---------------------------------------------------------------
     def step(self, seqs, k_new, v_new, q, out, *, decode: bool = True, stream=None,
@@ -187,10 +243,7 @@ class PagedDecodeEngine:
         n = seqs.size
         if n > self.max_seqs:
             raise N.PagedKVError(N.PA_ERR_INVALID_ARG, f"batch of {n} > max_seqs {self.max_seqs}")
-        st = self._staging[self._next]
-        self._next = (self._next + 1) % len(self._staging)
-        if st["event"] is not None:
-            st["event"].synchronize()         # the upload that last read this buffer is done
+        st = self._stage.host()
         _, pairs = self.bm.append_batch(seqs, slots_out=st["slots"], pairs_out=st["pairs"])
         npairs = int(pairs.shape[0])
         tables_np = st["tables"][:n]
@@ -205,20 +258,8 @@ class PagedDecodeEngine:
         self.last_slots = st["slots"][:n].copy()
 
         cur = torch.cuda.current_stream(self.device) if stream is None else stream
-        self._cur ^= 1
-        dv = self._dev[self._cur]
         # Everything up to the end of this batch's table rows, in one upload.
-        upto = self._off_tables + 4 * n * self.cap if decode else self._off_tables
-        upto = -(-upto // 16) * 16
-        up = self._aux if self._aux is not None else cur
-        if dv["released"] is not None and up is not cur:
-            up.wait_event(dv["released"])     # no kernel still reads this device buffer
-        N.pa_stage_copy(dv["buf"], st["buf"], upto, stream=up)
-        uploaded = torch.cuda.Event()
-        uploaded.record(up)
-        st["event"] = uploaded
-        if up is not cur:
-            cur.wait_event(uploaded)
+        dv = self._stage.upload(st, n if decode else 0, cur)
         with torch.cuda.stream(cur):
             if npairs:
                 N.pa_copy_blocks(self.pool, dv["pairs"][:npairs], stream=cur)
@@ -240,9 +281,7 @@ class PagedDecodeEngine:
                                 partition_tokens=ptok, workspace=ws, stream=cur, seq_order=order)
                 if decode_events is not None:
                     decode_events[1].record(cur)
-            done = torch.cuda.Event()
-            done.record(cur)
-            dv["released"] = done
+            self._stage.release(dv, cur)
 
     def decode(self, seqs, q, out, *, partition_tokens=None, stream=None, longest_first=None) -> None:
         """Decode the batch as it stands (no append): tables and contexts uploaded first."""
@@ -253,7 +292,7 @@ class PagedDecodeEngine:
         ptok = self.partition_tokens if partition_tokens is None else partition_tokens
         lf = self.longest_first if longest_first is None else longest_first
         cur = torch.cuda.current_stream(self.device) if stream is None else stream
-        dv = self._dev[self._cur]
+        dv = self._stage.dev[self._stage.cur]
         with torch.cuda.stream(cur):
             dv["tables"][:n].copy_(torch.from_numpy(tables))
             dv["ctx"][:n].copy_(torch.from_numpy(ctx))
@@ -266,7 +305,90 @@ class PagedDecodeEngine:
             N.pa_decode(self.pool, q, out, dv["tables"][:n], dv["ctx"][:n], max_ctx,
                         partition_tokens=ptok, workspace=ws, stream=cur,
                         seq_order=dv["order"][:n] if lf else None)
-            done = torch.cuda.Event()
-            done.record(cur)
-            dv["released"] = done
+            self._stage.release(dv, cur)
         self.last_ctx = ctx
+
+
+class MixedDecodeEngine:
+    """Decode steps over mixed-precision pages: an fp16 hot block per
+    sequence (its newest tokens), int8 cold blocks for everything older.
+
+    A step: the manager appends one token per sequence (demoting full hot
+    blocks into fresh cold blocks) and exports cold tables, hot blocks and
+    contexts into the pinned staging buffer; one upload; ``pa_demote_blocks``
+    for the demoted blocks; ``pa_write_kv`` of the new rows into the hot pool;
+    ``pa_decode_mixed``.
+    """
+
+    def __init__(self, num_cold: int, num_hot: int, num_heads: int, head_dim: int, max_seqs: int,
+                 max_cold_per_seq: int, *, cold_order=None, hot_order=None, device="cuda",
+                 partition_tokens: int = 0, staging_depth: int = 3, longest_first: bool = True):
+        self.device = torch.device(device)
+        self.num_heads, self.head_dim = num_heads, head_dim
+        self.cold = N.new_pool(num_cold, num_heads, head_dim, N.PA_I8, device=self.device, fill=0)
+        self.hot = N.new_pool(num_hot, num_heads, head_dim, N.PA_F16, device=self.device, fill=0.0)
+        self.mbm = N.MixedBlockManager(num_cold, num_hot, cold_order, hot_order)
+        self.max_seqs = max_seqs
+        self.cap = max_cold_per_seq
+        self.partition_tokens = partition_tokens
+        self.longest_first = longest_first
+        self._stage = _Staging([("slots", torch.int64, ()), ("ctx", torch.int32, ()), ("order", torch.int32, ()),
+                                ("hot", torch.int32, ()), ("pairs", torch.int32, (2,)),
+                                ("tables", torch.int32, (self.cap,))],
+                               max_seqs, self.device, staging_depth, False)
+        for v in self._stage.dev:
+            v["tables"].fill_(-1)
+        self._ws = _Workspace(self.device)
+        self.last_ctx = np.zeros(0, dtype=np.int32)
+        self.last_pairs = 0
+
+    def add_sequence(self, seq: int, k_rows, v_rows) -> None:
+        """Register ``seq`` with prefill rows ``[n][heads][head_dim]``: full
+        blocks but the last are quantised into the cold pool, the rest goes to
+        the sequence's hot block."""
+        n = int(k_rows.shape[0])
+        cold, hot = self.mbm.add_seq(seq, n)
+        if n:
+            if (cold >= 0).any():
+                N.pa_write_kv(self.cold, k_rows, v_rows, torch.from_numpy(cold).to(self.device))
+            N.pa_write_kv(self.hot, k_rows, v_rows, torch.from_numpy(hot).to(self.device))
+
+    def fork(self, parent: int, child: int) -> None:
+        src, dst = self.mbm.fork(parent, child)
+        N.pa_copy_blocks(self.hot, torch.tensor([[src, dst]], dtype=torch.int32, device=self.device))
+
+    def free_sequence(self, seq: int) -> None:
+        self.mbm.free_seq(seq)
+
+    def step(self, seqs, k_new, v_new, q, out, *, decode: bool = True, stream=None, decode_events=None) -> None:
+        seqs = np.asarray(seqs, dtype=np.int64)
+        n = seqs.size
+        if n > self.max_seqs:
+            raise N.PagedKVError(N.PA_ERR_INVALID_ARG, f"batch of {n} > max_seqs {self.max_seqs}")
+        st = self._stage.host()
+        _, pairs = self.mbm.append_batch(seqs, slots_out=st["slots"], pairs_out=st["pairs"])
+        npairs = int(pairs.shape[0])
+        ctx_np = st["ctx"][:n]
+        self.mbm.export(seqs, self.cap, tables_out=st["tables"][:n], hot_out=st["hot"][:n], ctx_out=ctx_np)
+        max_ctx = int(ctx_np.max()) if n else 0
+        if decode and self.longest_first:
+            st["order"][:n] = np.argsort(-ctx_np, kind="stable")
+        self.last_ctx = ctx_np.copy()
+        self.last_pairs = npairs
+        cur = torch.cuda.current_stream(self.device) if stream is None else stream
+        dv = self._stage.upload(st, n if decode else 0, cur)
+        with torch.cuda.stream(cur):
+            if npairs:
+                N.pa_demote_blocks(self.hot, self.cold, dv["pairs"][:npairs], stream=cur)
+            N.pa_write_kv(self.hot, k_new, v_new, dv["slots"][:n], stream=cur)
+            if decode:
+                ptok = self.partition_tokens
+                ws = self._ws.get(N.pa_decode_workspace_bytes(self.cold, n, max_ctx, ptok)) if ptok else None
+                if decode_events is not None:
+                    decode_events[0].record(cur)
+                N.pa_decode_mixed(self.cold, self.hot, q, out, dv["tables"][:n], dv["hot"][:n], dv["ctx"][:n],
+                                  max_ctx, partition_tokens=ptok, workspace=ws, stream=cur,
+                                  seq_order=dv["order"][:n] if self.longest_first else None)
+                if decode_events is not None:
+                    decode_events[1].record(cur)
+            self._stage.release(dv, cur)

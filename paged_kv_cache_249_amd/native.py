@@ -90,6 +90,18 @@ _SIGS = {
     "pa_bm_free_list": ([_vp, _vp, _i32, _pi32], _i32),
     "pa_bm_add_seq_prefix": ([_vp, _i64, _vp, _i32, _vp, _pi32], _i32),
     "pa_bm_set_host_pool": ([_vp, _i32, _vp], _i32),
+    "pa_mbm_create": ([_i32, _i32, _vp, _vp, C.POINTER(_vp)], _i32),
+    "pa_mbm_destroy": ([_vp], _i32),
+    "pa_mbm_add_seq": ([_vp, _i64, _i32, _vp, _vp], _i32),
+    "pa_mbm_append_batch": ([_vp, _vp, _i32, _vp, _vp, _pi32], _i32),
+    "pa_mbm_fork": ([_vp, _i64, _i64, _pi32, _pi32], _i32),
+    "pa_mbm_free_seq": ([_vp, _i64], _i32),
+    "pa_mbm_export": ([_vp, _vp, _i32, _vp, _i32, _vp, _vp], _i32),
+    "pa_mbm_ref_count": ([_vp, _i32, _pi32], _i32),
+    "pa_mbm_free_lists": ([_vp, _vp, _i32, _pi32, _vp, _i32, _pi32], _i32),
+    "pa_demote_blocks": ([_vp, _vp, _vp, _i32, _vp], _i32),
+    "pa_decode_mixed": ([_vp, _vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _i32, _i32, _f32, _i32, _vp, _i64,
+                         _vp], _i32),
     "pa_bm_swap_out": ([_vp, _i64, _vp, _i32, _pi32], _i32),
     "pa_bm_swap_in": ([_vp, _i64, _vp, _i32, _pi32], _i32),
     "pa_bm_is_swapped": ([_vp, _i64, _pi32], _i32),
@@ -311,6 +323,38 @@ def pa_decode(pool: Pool, q, out, block_tables, context_lens, max_context_len: i
                                  _ptr(seq_order, "seq_order", torch.int32), S, int(max_context_len),
                                  float(sm_scale), int(partition_tokens), _ptr(workspace, "workspace"),
                                  ws_bytes, _stream(stream, q)), "pa_decode_ordered")
+
+
+def pa_demote_blocks(hot: Pool, cold: Pool, pairs, stream=None) -> None:
+    """Quantise full fp16 hot blocks into int8 cold blocks for int32 ``[n][2]``
+    device (hot, cold) pairs."""
+    torch = _torch()
+    n = int(pairs.shape[0]) if pairs.numel() else 0
+    _check(lib.pa_demote_blocks(hot.handle, cold.handle, _ptr(pairs, "pairs", torch.int32), n,
+                                _stream(stream, pairs)), "pa_demote_blocks")
+
+
+def pa_decode_mixed(cold: Pool, hot: Pool, q, out, cold_tables, hot_blocks, context_lens, max_context_len: int,
+                    sm_scale: float = 0.0, partition_tokens: int = 0, workspace=None, stream=None,
+                    seq_order=None) -> None:
+    """Decode over mixed-precision pages (int8 cold pool through ``cold_tables``,
+    each sequence's fp16 hot block ``hot_blocks[s]`` for its last tokens)."""
+    torch = _torch()
+    S = int(q.shape[0])
+    if tuple(q.shape) != (S, cold.num_heads, cold.head_dim) or out.shape != q.shape or out.dtype != q.dtype:
+        raise PagedKVError(PA_ERR_INVALID_ARG, "q/out shape or dtype mismatch")
+    if cold_tables.dim() != 2 or cold_tables.shape[0] < S or context_lens.numel() < S or hot_blocks.numel() < S:
+        raise PagedKVError(PA_ERR_INVALID_ARG, "tables/hot blocks/context_lens do not cover the batch")
+    if seq_order is not None and seq_order.numel() < S:
+        raise PagedKVError(PA_ERR_INVALID_ARG, "seq_order does not cover the batch")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.pa_decode_mixed(cold.handle, hot.handle, _ptr(q, "q"), dtype_code(q.dtype), _ptr(out, "out"),
+                               _ptr(cold_tables, "cold_tables", torch.int32), int(cold_tables.shape[1]),
+                               _ptr(hot_blocks, "hot_blocks", torch.int32),
+                               _ptr(context_lens, "context_lens", torch.int32),
+                               _ptr(seq_order, "seq_order", torch.int32), S, int(max_context_len), float(sm_scale),
+                               int(partition_tokens), _ptr(workspace, "workspace"), ws_bytes,
+                               _stream(stream, q)), "pa_decode_mixed")
 
 
 def pa_write_decode(pool: Pool, k_new, v_new, slot_mapping, q, out, block_tables, context_lens,
@@ -538,3 +582,84 @@ class BlockManager:
         _check(lib.pa_bm_host_free_list(self.handle, _np_ptr(out), out.size, C.byref(got)),
                "pa_bm_host_free_list")
         return out[:got.value].tolist()
+
+
+class MixedBlockManager:
+    """The library's host manager of mixed-precision pages (pa_mbm_*)."""
+
+    def __init__(self, num_cold: int, num_hot: int, cold_order=None, hot_order=None):
+        h = C.c_void_p()
+        orders = []
+        for o, n in ((cold_order, num_cold), (hot_order, num_hot)):
+            if o is None:
+                orders.append(None)
+                continue
+            a = np.ascontiguousarray(np.asarray(o, dtype=np.int32))
+            if a.size != n:
+                raise PagedKVError(PA_ERR_INVALID_ARG, "free order length != pool size")
+            orders.append(a)
+        self._orders = orders
+        _check(lib.pa_mbm_create(num_cold, num_hot, *(None if a is None else _np_ptr(a) for a in orders),
+                                 C.byref(h)), "pa_mbm_create")
+        self._lib = lib
+        self.handle = h.value
+        self.num_cold, self.num_hot = num_cold, num_hot
+
+    def __del__(self):
+        if getattr(self, "handle", None) and getattr(self, "_lib", None) is not None:
+            self._lib.pa_mbm_destroy(self.handle)
+            self.handle = None
+
+    def add_seq(self, seq: int, prefill_tokens: int):
+        """(cold_slots, hot_slots), each [prefill_tokens], -1 for the other pool's tokens."""
+        cold = np.empty(max(prefill_tokens, 1), dtype=np.int64)
+        hot = np.empty(max(prefill_tokens, 1), dtype=np.int64)
+        _check(lib.pa_mbm_add_seq(self.handle, seq, prefill_tokens, _np_ptr(cold), _np_ptr(hot)), "pa_mbm_add_seq")
+        return cold[:max(prefill_tokens, 0)], hot[:max(prefill_tokens, 0)]
+
+    def append_batch(self, seqs, slots_out=None, pairs_out=None):
+        """(hot slots [n], demote pairs [k][2]) for one token per sequence."""
+        seqs = np.ascontiguousarray(np.asarray(seqs, dtype=np.int64))
+        n = seqs.size
+        slots = slots_out if slots_out is not None else np.empty(max(n, 1), dtype=np.int64)
+        pairs = pairs_out if pairs_out is not None else np.empty((max(n, 1), 2), dtype=np.int32)
+        npairs = C.c_int32()
+        _check(lib.pa_mbm_append_batch(self.handle, _np_ptr(seqs), n, _np_ptr(slots), _np_ptr(pairs),
+                                       C.byref(npairs)), "pa_mbm_append_batch")
+        return slots[:n], pairs[:npairs.value]
+
+    def append(self, seq: int):
+        slots, pairs = self.append_batch([seq])
+        src, dst = (int(pairs[0, 0]), int(pairs[0, 1])) if pairs.shape[0] else (-1, -1)
+        return int(slots[0]), src, dst
+
+    def fork(self, parent: int, child: int):
+        src, dst = C.c_int32(), C.c_int32()
+        _check(lib.pa_mbm_fork(self.handle, parent, child, C.byref(src), C.byref(dst)), "pa_mbm_fork")
+        return src.value, dst.value
+
+    def free_seq(self, seq: int) -> None:
+        _check(lib.pa_mbm_free_seq(self.handle, seq), "pa_mbm_free_seq")
+
+    def export(self, seqs, cap: int, tables_out=None, hot_out=None, ctx_out=None):
+        seqs = np.ascontiguousarray(np.asarray(seqs, dtype=np.int64))
+        n = seqs.size
+        tables = tables_out if tables_out is not None else np.empty((max(n, 1), max(cap, 1)), dtype=np.int32)
+        hot = hot_out if hot_out is not None else np.empty(max(n, 1), dtype=np.int32)
+        ctx = ctx_out if ctx_out is not None else np.empty(max(n, 1), dtype=np.int32)
+        _check(lib.pa_mbm_export(self.handle, _np_ptr(seqs), n, _np_ptr(tables), cap, _np_ptr(hot), _np_ptr(ctx)),
+               "pa_mbm_export")
+        return tables[:n, :cap], hot[:n], ctx[:n]
+
+    def ref_count(self, block: int) -> int:
+        v = C.c_int32()
+        _check(lib.pa_mbm_ref_count(self.handle, block, C.byref(v)), "pa_mbm_ref_count")
+        return v.value
+
+    def free_lists(self):
+        cold = np.empty(self.num_cold, dtype=np.int32)
+        hot = np.empty(self.num_hot, dtype=np.int32)
+        nc, nh = C.c_int32(), C.c_int32()
+        _check(lib.pa_mbm_free_lists(self.handle, _np_ptr(cold), cold.size, C.byref(nc), _np_ptr(hot), hot.size,
+                                     C.byref(nh)), "pa_mbm_free_lists")
+        return cold[:nc.value].tolist(), hot[:nh.value].tolist()

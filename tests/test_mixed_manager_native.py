@@ -1,0 +1,116 @@
+"""The library's mixed-precision page manager against the oracle's model
+(CPU only): the same random operations give the same slots, demote pairs,
+fork copies, tables, reference counts and free lists, and errors match."""
+
+import copy
+
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import block_manager as OBM
+from oracle import mixed as OM
+
+
+def _pair(nc, nh, seed):
+    import paged_kv_cache_249_amd as pk
+    co, ho = W.free_order(seed, nc), W.free_order(seed + 1, nh)
+    return OM.MixedBlockManager(nc, nh, co, ho), pk.MixedBlockManager(nc, nh, co, ho)
+
+
+def _both(fo, fn):
+    import paged_kv_cache_249_amd as pk
+    try:
+        ro = ("ok", fo())
+    except OBM.BMError as e:
+        ro = ("err", e.code)
+    try:
+        rn = ("ok", fn())
+    except pk.PagedKVError as e:
+        rn = ("err", e.status)
+    return ro, rn
+
+
+def _same(o, n, live):
+    cold, hot = n.free_lists()
+    assert list(o.cold_free) == cold and list(o.hot_free) == hot
+    assert [o.ref[b] for b in range(o.num_cold)] == [n.ref_count(b) for b in range(o.num_cold)]
+    if live:
+        ot, oh, oc = o.export(live, 16)
+        nt, nh, nc = n.export(live, 16)
+        assert np.array_equal(ot, nt) and np.array_equal(oh, nh) and np.array_equal(oc, nc)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_operations_match_the_oracle(seed):
+    rng = W.rng(seed, 93)
+    o, n = _pair(60, 14, seed)
+    live, nid = [], 0
+    for step in range(400):
+        op = int(rng.integers(0, 10))
+        if op == 0 or not live:
+            k = int(rng.integers(0, 90))
+            ro, rn = _both(lambda: [a.tolist() for a in o.add_seq(nid, k)],
+                           lambda: [a.tolist() for a in n.add_seq(nid, k)])
+            assert ro == rn, (step, ro, rn)
+            if ro[0] == "ok":
+                live.append(nid)
+            nid += 1
+        elif op == 1:
+            p = live[int(rng.integers(len(live)))]
+            ro, rn = _both(lambda: o.fork(p, nid), lambda: n.fork(p, nid))
+            assert ro == rn
+            if ro[0] == "ok":
+                live.append(nid)
+            nid += 1
+        elif op == 2:
+            s = live.pop(int(rng.integers(len(live))))
+            assert _both(lambda: o.free_seq(s), lambda: n.free_seq(s)) == (("ok", None), ("ok", None))
+        elif op == 3:
+            seqs = [live[int(rng.integers(len(live)))] for _ in range(int(rng.integers(1, 6)))]
+            snap = copy.deepcopy(o)
+            try:
+                res = [o.append(s) for s in seqs]
+                ro = ("ok", ([r[0] for r in res], [[r[1], r[2]] for r in res if r[1] >= 0]))
+            except OBM.BMError as e:
+                o = snap
+                ro = ("err", e.code)
+            import paged_kv_cache_249_amd as pk
+            try:
+                sl, pr = n.append_batch(seqs)
+                rn = ("ok", (sl.tolist(), pr.tolist()))
+            except pk.PagedKVError as e:
+                rn = ("err", e.status)
+            assert ro == rn, (step, ro, rn)
+        else:
+            s = live[int(rng.integers(len(live)))]
+            ro, rn = _both(lambda: o.append(s), lambda: n.append(s))
+            assert ro == rn, (step, ro, rn)
+        _same(o, n, live)
+
+
+def test_errors_match():
+    import paged_kv_cache_249_amd as pk
+    o, n = _pair(4, 2, 0)
+    cases = [
+        (lambda: o.add_seq(0, 40), lambda: n.add_seq(0, 40)),
+        (lambda: o.add_seq(0, 1), lambda: n.add_seq(0, 1)),            # exists
+        (lambda: o.add_seq(1, 16 * 4), lambda: n.add_seq(1, 16 * 4)),  # 3 cold needed, 2 free
+        (lambda: o.fork(0, 1), lambda: n.fork(0, 1)),
+        (lambda: o.fork(0, 2), lambda: n.fork(0, 2)),                  # hot pool exhausted
+        (lambda: o.fork(9, 3), lambda: n.fork(9, 3)),                  # unknown parent
+        (lambda: o.free_seq(9), lambda: n.free_seq(9)),
+        (lambda: o.export([0], 1), lambda: n.export([0], 1)),          # cap too small
+    ]
+    for fo, fn in cases:
+        ro, rn = _both(fo, fn)
+        assert ro[0] == rn[0]
+        if ro[0] == "err":
+            assert ro == rn
+    for _ in range(8):
+        ro, rn = _both(lambda: o.append(0), lambda: n.append(0))
+        assert ro == rn
+    _same(o, n, [0, 1])
+    with pytest.raises(pk.PagedKVError) as e:
+        pk.MixedBlockManager(4, 2, cold_order=[0, 0, 1, 2])
+    assert e.value.status == pk.PA_ERR_INVALID_ARG
