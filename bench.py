@@ -127,11 +127,14 @@ def summarize_profiles(raw_dir: str) -> int:
     # The kernel source hash as it was when the counters were taken (printed
     # by the profiled run into its log next to the raw output).
     shas = set()
+    algo = set()
     for sub in ("prof_fetch", "prof_write"):
         with open(os.path.join(raw_dir, sub + ".log")) as f:
             for line in f:
                 if line.startswith("{") and "decode_source_sha256" in line:
-                    shas.add(json.loads(line)["decode_source_sha256"])
+                    rec = json.loads(line)
+                    shas.add(rec["decode_source_sha256"])
+                    algo.add(rec["kv_bytes_per_decode"])
     if len(shas) != 1:
         raise SystemExit(f"profiled runs disagree on the kernel source: {shas}")
     profiled_sha = shas.pop()
@@ -153,6 +156,8 @@ def summarize_profiles(raw_dir: str) -> int:
             f"decode_fetch_bytes = {fetch[dec] * f_fac * 1024:.0f}",
             f"decode_write_bytes = {write[dec] * w_fac * 1024:.0f}",
             f"traffic_bytes_per_launch = {traffic:.0f}",
+            f"algorithmic_kv_bytes_per_launch = {max(algo)}",
+            f"traffic_over_algorithmic = {traffic / max(algo):.4f}",
             f"decode_source_sha256 = {profiled_sha}"]
     with open(TRAFFIC_FILE, "w") as f:
         f.write("\n".join(out) + "\n")
