@@ -19,6 +19,7 @@ oracle on a bounded sample of the same batch. Inputs are synthetic N(0,1).
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import math
 import os
@@ -286,8 +287,16 @@ def main():
     torch.cuda.synchronize()
     assert pk.pa_check_errors() == 0
 
+    # Warm-up steps carry timing events like the timed steps do: the first
+    # timed event pair of a process can stall the host for tens of ms.
     for i in range(Wm):
-        eng.step(seqs, knew[i % ring], vnew[i % ring], q, out)
+        ev = None
+        if i % EVENT_EVERY == EVENT_EVERY - 1 or i == Wm - 1:
+            ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        eng.step(seqs, knew[i % ring], vnew[i % ring], q, out, decode_events=ev)
+        if ev is not None:
+            torch.cuda.synchronize()
+            ev[0].elapsed_time(ev[1])
     torch.cuda.synchronize()
 
     if args.profile_run:
@@ -313,14 +322,23 @@ def main():
     kv_bytes = []
     torch.cuda.synchronize()
     host_s = 0.0
+    host_each = []
+    # A full Python garbage collection inside the loop stalls the host for
+    # tens of ms (the objects of torch's import): collect and freeze them
+    # first, and keep the collector off during the timed steps.
+    gc.collect()
+    gc.freeze()
+    gc.disable()
     t0 = time.perf_counter()
     for i in range(K):
         h0 = time.perf_counter()
         eng.step(seqs, knew[i % ring], vnew[i % ring], q, out, decode_events=events.get(i))
-        host_s += time.perf_counter() - h0
+        host_each.append(time.perf_counter() - h0)
         kv_bytes.append(kv_bytes_of(eng.last_ctx))
+    host_s = sum(host_each)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    gc.enable()
     dev_err = pk.pa_check_errors()
     wall = t1 - t0
     dec_ms = [events[i][0].elapsed_time(events[i][1]) for i in timed]
@@ -353,6 +371,9 @@ def main():
         "decode_steps_seqs_per_s": round(S * K / wall, 1),
         "decode_kernel_us": round(dec_avg_s * 1e6, 2),
         "host_us_per_step": round(host_s / K * 1e6, 1),
+        "host_us_first_steps": [round(x * 1e6, 1) for x in host_each[:5]],
+        "host_us_max": round(max(host_each) * 1e6, 1),
+        "host_us_argmax": int(np.argmax(host_each)),
         "decode_kernel_us_p10_p90": [round(float(np.percentile(dec_ms, 10)) * 1e3, 2),
                                      round(float(np.percentile(dec_ms, 90)) * 1e3, 2)],
         "kv_bytes_per_decode": int(bytes_avg),

@@ -216,16 +216,28 @@ pa_status pa_decode(pa_pool* pool, const void* q, pa_dtype q_dtype, void* out,
                     float sm_scale, int32_t partition_tokens, void* workspace,
                     int64_t workspace_bytes, pa_stream stream);
 
+/* Dispatch schedules for an ordered decode (seq_order not NULL):
+ * PA_SCHED_HEADS  — ranks one after the other, all heads of a rank together
+ *                   (each XCD takes 4 adjacent heads: 4 adjacent tiles of each
+ *                   block); the faster one when sequences share no blocks.
+ * PA_SCHED_SHARED — ranks in groups of 4, a group head by head (each XCD
+ *                   takes one head of 4 adjacent ranks), so samples that share
+ *                   blocks and sit next to each other in the order read them
+ *                   through one L2 at about the same time. */
+enum { PA_SCHED_HEADS = 0, PA_SCHED_SHARED = 1 };
+
 /* pa_decode with a schedule: seq_order (device int32 [num_seqs], a
  * permutation of the batch, or NULL for batch order) is the order in which
- * sequences are dispatched, all heads of a sequence together. Passing the
- * batch sorted by decreasing context length (longest first) shortens the
- * tail of a single-pass launch, whose per-sequence work is proportional to
- * the context. Results do not depend on the order. An entry outside
- * [0, num_seqs) flags PA_DEV_BAD_CONTEXT and that work is skipped. */
+ * sequences are dispatched; schedule is a PA_SCHED_* value (ignored without
+ * an order). Passing the batch sorted by decreasing context length (longest
+ * first) shortens the tail of a single-pass launch, whose per-sequence work
+ * is proportional to the context. Results do not depend on the order or the
+ * schedule. An entry outside [0, num_seqs) flags PA_DEV_BAD_CONTEXT and that
+ * work is skipped. */
 pa_status pa_decode_ordered(pa_pool* pool, const void* q, pa_dtype q_dtype, void* out,
                             const int32_t* block_tables, int32_t max_blocks,
-                            const int32_t* context_lens, const int32_t* seq_order, int32_t num_seqs,
+                            const int32_t* context_lens, const int32_t* seq_order, int32_t schedule,
+                            int32_t num_seqs,
                             int32_t max_context_len, float sm_scale, int32_t partition_tokens,
                             void* workspace, int64_t workspace_bytes, pa_stream stream);
 
@@ -243,9 +255,10 @@ pa_status pa_decode_ordered(pa_pool* pool, const void* q, pa_dtype q_dtype, void
 pa_status pa_write_decode(pa_pool* pool, const void* k_new, const void* v_new, pa_dtype src_dtype,
                           const int64_t* slot_mapping, const void* q, pa_dtype q_dtype, void* out,
                           const int32_t* block_tables, int32_t max_blocks,
-                          const int32_t* context_lens, const int32_t* seq_order, int32_t num_seqs,
-                          int32_t max_context_len, float sm_scale, int32_t partition_tokens,
-                          void* workspace, int64_t workspace_bytes, pa_stream stream);
+                          const int32_t* context_lens, const int32_t* seq_order, int32_t schedule,
+                          int32_t num_seqs, int32_t max_context_len, float sm_scale,
+                          int32_t partition_tokens, void* workspace, int64_t workspace_bytes,
+                          pa_stream stream);
 
 /* Layout of the split-K workspace, for callers that inspect partials: with
  * P = ceil(max_context_len / partition_tokens), the workspace holds
@@ -388,6 +401,11 @@ pa_status pa_bm_num_free(const pa_bm* bm, int32_t* out);
 /* The free list in order (head first) into out [cap]; *n receives its length. */
 pa_status pa_bm_free_list(const pa_bm* bm, int32_t* out, int32_t cap, int32_t* n);
 
+/* *out = 1 if some block held by a resident sequence of seqs[0..n) has a
+ * count above one (shared with a fork or a prefix), else 0: the hint for
+ * choosing PA_SCHED_SHARED. Errors: PA_ERR_STATE (unknown sequence). */
+pa_status pa_bm_batch_shares(const pa_bm* bm, const int64_t* seqs, int32_t n, int32_t* out);
+
 /* ----------------------------------------------------------------------------
  * Swapping whole sequences between the device pool and a host pool.
  *
@@ -465,6 +483,8 @@ pa_status pa_mbm_free_seq(pa_mbm* m, int64_t seq);
 pa_status pa_mbm_export(const pa_mbm* m, const int64_t* seqs, int32_t n, int32_t* cold_tables,
                         int32_t cap, int32_t* hot_out, int32_t* ctx_out);
 pa_status pa_mbm_ref_count(const pa_mbm* m, int32_t cold_block, int32_t* out);
+/* As pa_bm_batch_shares, over the cold blocks. */
+pa_status pa_mbm_batch_shares(const pa_mbm* m, const int64_t* seqs, int32_t n, int32_t* out);
 /* Free lists in order (head first); either output may be NULL to query sizes. */
 pa_status pa_mbm_free_lists(const pa_mbm* m, int32_t* cold_out, int32_t cold_cap, int32_t* n_cold,
                             int32_t* hot_out, int32_t hot_cap, int32_t* n_hot);
@@ -482,14 +502,16 @@ pa_status pa_demote_blocks(pa_pool* hot_pool, pa_pool* cold_pool, const int32_t*
 /* Paged decode over mixed-precision pages: as pa_decode_ordered, where token t
  * of sequence s is cold row K[cold_tables[s][t / 16]][h][t % 16] * scale for
  * t < 16 n_cold, and hot row Khot[hot_blocks[s]][h][t - 16 n_cold] otherwise.
- * partition_tokens: 0 or a multiple of 16; workspace as pa_decode. A hot block
+ * partition_tokens: 0 or a multiple of 16; workspace, seq_order and schedule
+ * as pa_decode_ordered. A hot block
  * id outside the hot pool flags PA_DEV_BAD_TABLE_ENTRY and its rows are
  * masked. Errors: as pa_decode, plus PA_ERR_INVALID_ARG when the pools are not
  * an int8 cold pool and an fp16 hot pool of block size 16 with equal heads and
  * head_dim. */
 pa_status pa_decode_mixed(pa_pool* cold_pool, pa_pool* hot_pool, const void* q, pa_dtype q_dtype, void* out,
                           const int32_t* cold_tables, int32_t max_blocks, const int32_t* hot_blocks,
-                          const int32_t* context_lens, const int32_t* seq_order, int32_t num_seqs,
+                          const int32_t* context_lens, const int32_t* seq_order, int32_t schedule,
+                          int32_t num_seqs,
                           int32_t max_context_len, float sm_scale, int32_t partition_tokens,
                           void* workspace, int64_t workspace_bytes, pa_stream stream);
 

@@ -234,6 +234,8 @@ static pa_status decode_common(const char* fn, pa::DecodeArgs& a, void* workspac
   if (a.q_dtype != PA_F32 && a.q_dtype != PA_F16)
     return fail(PA_ERR_UNSUPPORTED, "%s: q dtype %d (F32 or F16)", fn, int(a.q_dtype));
   if (a.num_seqs < 0 || a.max_ctx < 0) return fail(PA_ERR_INVALID_ARG, "%s: negative size", fn);
+  if (a.schedule != PA_SCHED_HEADS && a.schedule != PA_SCHED_SHARED)
+    return fail(PA_ERR_INVALID_ARG, "%s: schedule %d", fn, a.schedule);
   if (a.partition_tokens < 0 || a.partition_tokens % a.block_size)
     return fail(PA_ERR_INVALID_ARG, "%s: partition_tokens=%d (0 or a multiple of the block size %d)", fn,
                 a.partition_tokens, a.block_size);
@@ -264,13 +266,14 @@ pa_status pa_decode(pa_pool* pool, const void* q, pa_dtype q_dtype, void* out, c
                     int32_t max_blocks, const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
                     float sm_scale, int32_t partition_tokens, void* workspace, int64_t workspace_bytes,
                     pa_stream stream) {
-  return pa_decode_ordered(pool, q, q_dtype, out, block_tables, max_blocks, context_lens, nullptr, num_seqs,
-                           max_context_len, sm_scale, partition_tokens, workspace, workspace_bytes, stream);
+  return pa_decode_ordered(pool, q, q_dtype, out, block_tables, max_blocks, context_lens, nullptr, PA_SCHED_HEADS,
+                           num_seqs, max_context_len, sm_scale, partition_tokens, workspace, workspace_bytes, stream);
 }
 
 pa_status pa_decode_ordered(pa_pool* pool, const void* q, pa_dtype q_dtype, void* out,
                             const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens,
-                            const int32_t* seq_order, int32_t num_seqs, int32_t max_context_len, float sm_scale,
+                            const int32_t* seq_order, int32_t schedule, int32_t num_seqs, int32_t max_context_len,
+                            float sm_scale,
                             int32_t partition_tokens, void* workspace, int64_t workspace_bytes,
                             pa_stream stream) {
   if (!pool) return fail(PA_ERR_INVALID_ARG, "pa_decode: pool is NULL");
@@ -294,6 +297,7 @@ pa_status pa_decode_ordered(pa_pool* pool, const void* q, pa_dtype q_dtype, void
   a.max_tokens = 0;
   a.ctx = context_lens;
   a.order = seq_order;
+  a.schedule = schedule;
   a.num_seqs = num_seqs;
   a.num_heads = pool->num_heads;
   a.head_dim = pool->head_dim;
@@ -307,7 +311,8 @@ pa_status pa_decode_ordered(pa_pool* pool, const void* q, pa_dtype q_dtype, void
 pa_status pa_write_decode(pa_pool* pool, const void* k_new, const void* v_new, pa_dtype src_dtype,
                           const int64_t* slot_mapping, const void* q, pa_dtype q_dtype, void* out,
                           const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens,
-                          const int32_t* seq_order, int32_t num_seqs, int32_t max_context_len, float sm_scale,
+                          const int32_t* seq_order, int32_t schedule, int32_t num_seqs, int32_t max_context_len,
+                          float sm_scale,
                           int32_t partition_tokens, void* workspace, int64_t workspace_bytes,
                           pa_stream stream) {
   if (!pool) return fail(PA_ERR_INVALID_ARG, "pa_write_decode: pool is NULL");
@@ -335,6 +340,7 @@ pa_status pa_write_decode(pa_pool* pool, const void* k_new, const void* v_new, p
   a.block_size = pool->block_size;
   a.ctx = context_lens;
   a.order = seq_order;
+  a.schedule = schedule;
   a.num_seqs = num_seqs;
   a.num_heads = pool->num_heads;
   a.head_dim = pool->head_dim;
@@ -373,7 +379,8 @@ pa_status pa_demote_blocks(pa_pool* hot_pool, pa_pool* cold_pool, const int32_t*
 
 pa_status pa_decode_mixed(pa_pool* cold_pool, pa_pool* hot_pool, const void* q, pa_dtype q_dtype, void* out,
                           const int32_t* cold_tables, int32_t max_blocks, const int32_t* hot_blocks,
-                          const int32_t* context_lens, const int32_t* seq_order, int32_t num_seqs,
+                          const int32_t* context_lens, const int32_t* seq_order, int32_t schedule,
+                          int32_t num_seqs,
                           int32_t max_context_len, float sm_scale, int32_t partition_tokens, void* workspace,
                           int64_t workspace_bytes, pa_stream stream) {
   pa_status st = check_mixed_pools("pa_decode_mixed", cold_pool, hot_pool);
@@ -396,6 +403,7 @@ pa_status pa_decode_mixed(pa_pool* cold_pool, pa_pool* hot_pool, const void* q, 
   a.block_size = 16;
   a.ctx = context_lens;
   a.order = seq_order;
+  a.schedule = schedule;
   a.num_seqs = num_seqs;
   a.num_heads = cold_pool->num_heads;
   a.head_dim = cold_pool->head_dim;
@@ -435,6 +443,7 @@ pa_status pa_decode_contiguous(const void* k, const void* v, pa_dtype kv_dtype, 
   a.max_tokens = max_tokens;
   a.ctx = context_lens;
   a.order = seq_order;
+  a.schedule = PA_SCHED_HEADS;
   a.num_seqs = num_seqs;
   a.num_heads = num_heads;
   a.head_dim = head_dim;

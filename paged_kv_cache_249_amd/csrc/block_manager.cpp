@@ -514,6 +514,25 @@ pa_status pa_bm_ref_count(const pa_bm* bm, int32_t block, int32_t* out) {
   return PA_OK;
 }
 
+pa_status pa_bm_batch_shares(const pa_bm* bm, const int64_t* seqs, int32_t n, int32_t* out) {
+  if (!bm || !out || n < 0 || (n > 0 && !seqs)) return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_batch_shares: bad arguments");
+  int32_t shares = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = bm->seqs.find(seqs[i]);
+    if (it == bm->seqs.end())
+      return pa::fail(PA_ERR_STATE, "pa_bm_batch_shares: unknown sequence %lld", (long long)seqs[i]);
+    if (it->second.swapped || shares) continue;
+    for (int32_t b : it->second.table) {
+      if (bm->ref[b] > 1) {
+        shares = 1;
+        break;
+      }
+    }
+  }
+  *out = shares;
+  return PA_OK;
+}
+
 pa_status pa_bm_num_free(const pa_bm* bm, int32_t* out) {
   if (!bm || !out) return pa::fail(PA_ERR_INVALID_ARG, "pa_bm_num_free: NULL argument");
   *out = int32_t(bm->free_list.size());

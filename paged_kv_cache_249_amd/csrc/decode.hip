@@ -51,13 +51,17 @@
 // int8 lane layout (each lane 16 values of a row), and folds them into the
 // same softmax stream.
 //
-// XCD-aware order: work item w enumerates (partition, head, sequence) with the
-// sequence fastest (or, when the caller passes a schedule, (partition,
-// scheduled sequence, head) with the head fastest, e.g. longest first). Workgroup ids are dealt to the 8 XCDs round-robin; groups
-// of 4 consecutive work items are steered onto one XCD, so the 4 sequences
-// next to each other in the batch (e.g. samples sharing a prompt's blocks)
-// read those blocks through the same L2 at about the same time, while the
-// deal stays interleaved at that granularity for load balance.
+// XCD-aware order. Workgroup ids are dealt to the 8 XCDs round-robin; groups
+// of 4 consecutive work items are steered onto one XCD, while the deal stays
+// interleaved at that granularity for load balance. Without a dispatch order,
+// work item w enumerates (partition, head, sequence) with the sequence
+// fastest. With one (e.g. longest first) the items of each partition follow
+// the order's ranks, in one of two schedules: PA_SCHED_HEADS runs all heads
+// of a sequence together (an XCD takes 4 adjacent heads, 4 adjacent tiles of
+// each block: the faster layout when nothing is shared), PA_SCHED_SHARED
+// takes ranks in groups of 4 and runs a group head by head (an XCD takes one
+// head of 4 adjacent ranks, so samples that share blocks read them through
+// one L2 at about the same time).
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -121,6 +125,7 @@ struct Params {
   int64_t max_tokens;       // contiguous layout row length
   const int32_t* ctx;
   const int32_t* order;     // optional schedule: the r-th sequence dispatched is order[r]
+  int32_t sched;            // PA_SCHED_HEADS or PA_SCHED_SHARED (with order)
   int32_t max_blocks;
   int32_t num_seqs;
   int32_t num_heads;
@@ -285,15 +290,22 @@ void decode_kernel(Params p, const int32_t* __restrict__ tables, const int32_t* 
   int s, h;
   const int part = w / (p.num_seqs * p.num_heads);
   if (p.order) {
-    // Scheduled: ranks of the caller's order (e.g. longest first) in groups
-    // of kXcdGroup; a group's items run head by head, so the group's
-    // sequences with one head form kXcdGroup consecutive items (one XCD).
     const int r = w % (p.num_seqs * p.num_heads);
-    const int g = r / (kXcdGroup * p.num_heads);
-    const int gs = min(kXcdGroup, p.num_seqs - g * kXcdGroup);
-    const int q_in = r - g * kXcdGroup * p.num_heads;
-    h = q_in / gs;
-    s = p.order[g * kXcdGroup + q_in % gs];
+    int rank;
+    if (p.sched == PA_SCHED_HEADS) {
+      // Ranks one after the other, all heads of a rank together.
+      rank = r / p.num_heads;
+      h = r - rank * p.num_heads;
+    } else {
+      // Ranks in groups of kXcdGroup, a group's items head by head, so the
+      // group's sequences with one head form kXcdGroup consecutive items.
+      const int g = r / (kXcdGroup * p.num_heads);
+      const int gs = min(kXcdGroup, p.num_seqs - g * kXcdGroup);
+      const int q_in = r - g * kXcdGroup * p.num_heads;
+      h = q_in / gs;
+      rank = g * kXcdGroup + q_in % gs;
+    }
+    s = p.order[rank];
     if (unsigned(s) >= unsigned(p.num_seqs)) {
       if (threadIdx.x == 0) flag_error(p.err, PA_DEV_BAD_CONTEXT);
       return;
@@ -756,6 +768,7 @@ int launch_decode(const DecodeArgs& a, void* stream) {
   p.max_tokens = a.max_tokens;
   p.ctx = a.ctx;
   p.order = a.order;
+  p.sched = a.schedule;
   p.max_blocks = a.max_blocks;
   p.num_seqs = a.num_seqs;
   p.num_heads = a.num_heads;

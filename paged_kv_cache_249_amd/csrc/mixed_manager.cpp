@@ -246,6 +246,22 @@ pa_status pa_mbm_ref_count(const pa_mbm* m, int32_t cold_block, int32_t* out) {
   return PA_OK;
 }
 
+pa_status pa_mbm_batch_shares(const pa_mbm* m, const int64_t* seqs, int32_t n, int32_t* out) {
+  if (!m || !out || n < 0 || (n > 0 && !seqs)) return pa::fail(PA_ERR_INVALID_ARG, "pa_mbm_batch_shares: bad arguments");
+  int32_t shares = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = m->seqs.find(seqs[i]);
+    if (it == m->seqs.end())
+      return pa::fail(PA_ERR_STATE, "pa_mbm_batch_shares: unknown sequence %lld", (long long)seqs[i]);
+    for (int32_t b : it->second.cold) {
+      if (shares) break;
+      if (m->ref[b] > 1) shares = 1;
+    }
+  }
+  *out = shares;
+  return PA_OK;
+}
+
 pa_status pa_mbm_free_lists(const pa_mbm* m, int32_t* cold_out, int32_t cold_cap, int32_t* n_cold,
                             int32_t* hot_out, int32_t hot_cap, int32_t* n_hot) {
   if (!m || !n_cold || !n_hot) return pa::fail(PA_ERR_INVALID_ARG, "pa_mbm_free_lists: NULL argument");

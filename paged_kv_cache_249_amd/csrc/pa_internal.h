@@ -64,6 +64,7 @@ struct DecodeArgs {
   int64_t max_tokens;     // contiguous layout: tokens per (seq, head) row
   const int32_t* ctx;
   const int32_t* order;   // optional schedule (permutation of the batch), may be null
+  int32_t schedule;       // PA_SCHED_*: how ordered (rank, head) items map to XCDs
   int32_t num_seqs;
   int32_t num_heads;
   int32_t head_dim;

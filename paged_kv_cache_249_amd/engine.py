@@ -250,6 +250,8 @@ class PagedDecodeEngine:
         ctx_np = st["ctx"][:n]
         self.bm.export(seqs, self.cap, tables_out=tables_np, ctx_out=ctx_np)
         max_ctx = int(ctx_np.max()) if n else 0
+        # Samples that share blocks go through one L2 together (PA_SCHED_SHARED).
+        sched = N.PA_SCHED_SHARED if decode and self.bm.batch_shares(seqs) else N.PA_SCHED_HEADS
         if decode and self.longest_first:
             st["order"][:n] = np.argsort(-ctx_np, kind="stable")
         self.last_ctx = ctx_np.copy()
@@ -275,10 +277,11 @@ class PagedDecodeEngine:
                 if fused:
                     N.pa_write_decode(self.pool, k_new, v_new, dv["slots"][:n], q, out, dv["tables"][:n],
                                       dv["ctx"][:n], max_ctx, partition_tokens=ptok, workspace=ws,
-                                      stream=cur, seq_order=order)
+                                      stream=cur, seq_order=order, schedule=sched)
                 else:
                     N.pa_decode(self.pool, q, out, dv["tables"][:n], dv["ctx"][:n], max_ctx,
-                                partition_tokens=ptok, workspace=ws, stream=cur, seq_order=order)
+                                partition_tokens=ptok, workspace=ws, stream=cur, seq_order=order,
+                                schedule=sched)
                 if decode_events is not None:
                     decode_events[1].record(cur)
             self._stage.release(dv, cur)
@@ -291,6 +294,7 @@ class PagedDecodeEngine:
         max_ctx = int(ctx.max()) if n else 0
         ptok = self.partition_tokens if partition_tokens is None else partition_tokens
         lf = self.longest_first if longest_first is None else longest_first
+        sched = N.PA_SCHED_SHARED if self.bm.batch_shares(seqs) else N.PA_SCHED_HEADS
         cur = torch.cuda.current_stream(self.device) if stream is None else stream
         dv = self._stage.dev[self._stage.cur]
         with torch.cuda.stream(cur):
@@ -304,7 +308,7 @@ class PagedDecodeEngine:
                 ws = torch.empty(need // 4 + 1, dtype=torch.float32, device=self.device)
             N.pa_decode(self.pool, q, out, dv["tables"][:n], dv["ctx"][:n], max_ctx,
                         partition_tokens=ptok, workspace=ws, stream=cur,
-                        seq_order=dv["order"][:n] if lf else None)
+                        seq_order=dv["order"][:n] if lf else None, schedule=sched)
             self._stage.release(dv, cur)
         self.last_ctx = ctx
 
@@ -373,6 +377,7 @@ class MixedDecodeEngine:
         max_ctx = int(ctx_np.max()) if n else 0
         if decode and self.longest_first:
             st["order"][:n] = np.argsort(-ctx_np, kind="stable")
+        sched = N.PA_SCHED_SHARED if decode and self.mbm.batch_shares(seqs) else N.PA_SCHED_HEADS
         self.last_ctx = ctx_np.copy()
         self.last_pairs = npairs
         cur = torch.cuda.current_stream(self.device) if stream is None else stream
@@ -388,7 +393,7 @@ class MixedDecodeEngine:
                     decode_events[0].record(cur)
                 N.pa_decode_mixed(self.cold, self.hot, q, out, dv["tables"][:n], dv["hot"][:n], dv["ctx"][:n],
                                   max_ctx, partition_tokens=ptok, workspace=ws, stream=cur,
-                                  seq_order=dv["order"][:n] if self.longest_first else None)
+                                  seq_order=dv["order"][:n] if self.longest_first else None, schedule=sched)
                 if decode_events is not None:
                     decode_events[1].record(cur)
             self._stage.release(dv, cur)

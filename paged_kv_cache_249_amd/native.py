@@ -34,6 +34,7 @@ PA_DEV_BAD_PAIR = 4
 PA_DEV_BAD_CONTEXT = 8
 PA_DEV_BAD_RUN = 16
 PA_SWAP_OUT, PA_SWAP_IN = 0, 1
+PA_SCHED_HEADS, PA_SCHED_SHARED = 0, 1
 
 BLOCK_SIZE = 16                      # the default; pools and managers also take 32 and 64
 BLOCK_SIZES = (16, 32, 64)
@@ -66,10 +67,10 @@ _SIGS = {
     "pa_swap_blocks": ([_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _vp], _i32),
     "pa_decode_workspace_bytes": ([_vp, _i32, _i32, _i32, _pi64], _i32),
     "pa_decode": ([_vp, _vp, _i32, _vp, _vp, _i32, _vp, _i32, _i32, _f32, _i32, _vp, _i64, _vp], _i32),
-    "pa_decode_ordered": ([_vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _f32, _i32, _vp, _i64, _vp],
-                          _i32),
-    "pa_write_decode": ([_vp, _vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _f32, _i32,
-                         _vp, _i64, _vp], _i32),
+    "pa_decode_ordered": ([_vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _f32, _i32, _vp, _i64,
+                           _vp], _i32),
+    "pa_write_decode": ([_vp, _vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _f32,
+                         _i32, _vp, _i64, _vp], _i32),
     "pa_check_errors": ([_vp, _pi32], _i32),
     "pa_decode_contiguous": ([_vp, _vp, _i32, _i32, _i32, _i32, _vp, _i32, _vp, _vp, _vp, _i32, _f32, _i32,
                               _vp, _i64, _vp], _i32),
@@ -100,8 +101,10 @@ _SIGS = {
     "pa_mbm_ref_count": ([_vp, _i32, _pi32], _i32),
     "pa_mbm_free_lists": ([_vp, _vp, _i32, _pi32, _vp, _i32, _pi32], _i32),
     "pa_demote_blocks": ([_vp, _vp, _vp, _i32, _vp], _i32),
-    "pa_decode_mixed": ([_vp, _vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _i32, _i32, _f32, _i32, _vp, _i64,
-                         _vp], _i32),
+    "pa_decode_mixed": ([_vp, _vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _i32, _i32, _i32, _f32, _i32, _vp,
+                         _i64, _vp], _i32),
+    "pa_bm_batch_shares": ([_vp, _vp, _i32, _pi32], _i32),
+    "pa_mbm_batch_shares": ([_vp, _vp, _i32, _pi32], _i32),
     "pa_bm_swap_out": ([_vp, _i64, _vp, _i32, _pi32], _i32),
     "pa_bm_swap_in": ([_vp, _i64, _vp, _i32, _pi32], _i32),
     "pa_bm_is_swapped": ([_vp, _i64, _pi32], _i32),
@@ -296,10 +299,11 @@ def pa_decode_workspace_bytes(pool: Pool, num_seqs: int, max_context_len: int,
 
 def pa_decode(pool: Pool, q, out, block_tables, context_lens, max_context_len: int,
               sm_scale: float = 0.0, partition_tokens: int = 0, workspace=None, stream=None,
-              seq_order=None) -> None:
+              seq_order=None, schedule: int = PA_SCHED_HEADS) -> None:
     """Paged decode: ``q``/``out`` ``[S][heads][head_dim]``, tables int32 ``[S][max_blocks]``.
 
-    ``seq_order`` (int32 ``[S]`` device permutation) selects pa_decode_ordered.
+    ``seq_order`` (int32 ``[S]`` device permutation) selects pa_decode_ordered
+    with ``schedule`` (``PA_SCHED_HEADS`` or ``PA_SCHED_SHARED``).
     """
     torch = _torch()
     S = int(q.shape[0])
@@ -320,9 +324,9 @@ def pa_decode(pool: Pool, q, out, block_tables, context_lens, max_context_len: i
     _check(lib.pa_decode_ordered(pool.handle, _ptr(q, "q"), dtype_code(q.dtype), _ptr(out, "out"),
                                  _ptr(block_tables, "block_tables", torch.int32), int(block_tables.shape[1]),
                                  _ptr(context_lens, "context_lens", torch.int32),
-                                 _ptr(seq_order, "seq_order", torch.int32), S, int(max_context_len),
-                                 float(sm_scale), int(partition_tokens), _ptr(workspace, "workspace"),
-                                 ws_bytes, _stream(stream, q)), "pa_decode_ordered")
+                                 _ptr(seq_order, "seq_order", torch.int32), int(schedule), S,
+                                 int(max_context_len), float(sm_scale), int(partition_tokens),
+                                 _ptr(workspace, "workspace"), ws_bytes, _stream(stream, q)), "pa_decode_ordered")
 
 
 def pa_demote_blocks(hot: Pool, cold: Pool, pairs, stream=None) -> None:
@@ -336,7 +340,7 @@ def pa_demote_blocks(hot: Pool, cold: Pool, pairs, stream=None) -> None:
 
 def pa_decode_mixed(cold: Pool, hot: Pool, q, out, cold_tables, hot_blocks, context_lens, max_context_len: int,
                     sm_scale: float = 0.0, partition_tokens: int = 0, workspace=None, stream=None,
-                    seq_order=None) -> None:
+                    seq_order=None, schedule: int = PA_SCHED_HEADS) -> None:
     """Decode over mixed-precision pages (int8 cold pool through ``cold_tables``,
     each sequence's fp16 hot block ``hot_blocks[s]`` for its last tokens)."""
     torch = _torch()
@@ -352,14 +356,14 @@ def pa_decode_mixed(cold: Pool, hot: Pool, q, out, cold_tables, hot_blocks, cont
                                _ptr(cold_tables, "cold_tables", torch.int32), int(cold_tables.shape[1]),
                                _ptr(hot_blocks, "hot_blocks", torch.int32),
                                _ptr(context_lens, "context_lens", torch.int32),
-                               _ptr(seq_order, "seq_order", torch.int32), S, int(max_context_len), float(sm_scale),
-                               int(partition_tokens), _ptr(workspace, "workspace"), ws_bytes,
+                               _ptr(seq_order, "seq_order", torch.int32), int(schedule), S, int(max_context_len),
+                               float(sm_scale), int(partition_tokens), _ptr(workspace, "workspace"), ws_bytes,
                                _stream(stream, q)), "pa_decode_mixed")
 
 
 def pa_write_decode(pool: Pool, k_new, v_new, slot_mapping, q, out, block_tables, context_lens,
                     max_context_len: int, sm_scale: float = 0.0, partition_tokens: int = 0,
-                    workspace=None, stream=None, seq_order=None) -> None:
+                    workspace=None, stream=None, seq_order=None, schedule: int = PA_SCHED_HEADS) -> None:
     """pa_write_kv + pa_decode_ordered in one launch (float pools; row s = sequence s's newest token)."""
     torch = _torch()
     S = int(q.shape[0])
@@ -376,9 +380,9 @@ def pa_write_decode(pool: Pool, k_new, v_new, slot_mapping, q, out, block_tables
                                dtype_code(q.dtype), _ptr(out, "out"),
                                _ptr(block_tables, "block_tables", torch.int32), int(block_tables.shape[1]),
                                _ptr(context_lens, "context_lens", torch.int32),
-                               _ptr(seq_order, "seq_order", torch.int32), S, int(max_context_len),
-                               float(sm_scale), int(partition_tokens), _ptr(workspace, "workspace"),
-                               ws_bytes, _stream(stream, q)), "pa_write_decode")
+                               _ptr(seq_order, "seq_order", torch.int32), int(schedule), S,
+                               int(max_context_len), float(sm_scale), int(partition_tokens),
+                               _ptr(workspace, "workspace"), ws_bytes, _stream(stream, q)), "pa_write_decode")
 
 
 def pa_decode_contiguous(k, v, q, out, context_lens, sm_scale: float = 0.0,
@@ -543,6 +547,13 @@ class BlockManager:
         _check(lib.pa_bm_free_list(self.handle, _np_ptr(out), out.size, C.byref(got)), "pa_bm_free_list")
         return out[:got.value].tolist()
 
+    def batch_shares(self, seqs) -> bool:
+        """Whether a resident sequence of ``seqs`` holds a block with a count above one."""
+        seqs = np.ascontiguousarray(np.asarray(seqs, dtype=np.int64))
+        out = C.c_int32()
+        _check(lib.pa_bm_batch_shares(self.handle, _np_ptr(seqs), seqs.size, C.byref(out)), "pa_bm_batch_shares")
+        return bool(out.value)
+
     # -- swapping --------------------------------------------------------------
     def set_host_pool(self, num_host_blocks: int, free_order=None) -> None:
         order = None
@@ -655,6 +666,12 @@ class MixedBlockManager:
         v = C.c_int32()
         _check(lib.pa_mbm_ref_count(self.handle, block, C.byref(v)), "pa_mbm_ref_count")
         return v.value
+
+    def batch_shares(self, seqs) -> bool:
+        seqs = np.ascontiguousarray(np.asarray(seqs, dtype=np.int64))
+        out = C.c_int32()
+        _check(lib.pa_mbm_batch_shares(self.handle, _np_ptr(seqs), seqs.size, C.byref(out)), "pa_mbm_batch_shares")
+        return bool(out.value)
 
     def free_lists(self):
         cold = np.empty(self.num_cold, dtype=np.int32)

@@ -34,6 +34,8 @@ def _same_state(o, n, live, cap=64):
     if o.num_host_blocks:
         assert list(o.host_free) == n.host_free_list()
     resident = [s for s in live if not o.is_swapped(s)]
+    shares = any(o.ref_count(b) > 1 for s in resident for b in o.table(s)[0])
+    assert n.batch_shares(live) == shares
     if resident:
         ot, oc = o.export(resident, cap)
         nt, nc = n.export(resident, cap)

@@ -245,11 +245,15 @@ def test_schedule_does_not_change_results():
             if ptok:
                 nb = pk.pa_decode_workspace_bytes(b.pool, len(ctx), maxc, ptok)
                 ws = torch.empty(nb // 4, dtype=torch.float32, device=DEV)
-            pk.pa_decode(b.pool, b.qd, out, b.tabd, b.ctxd, maxc, partition_tokens=ptok, workspace=ws,
-                         seq_order=torch.from_numpy(order.astype(np.int32)).to(DEV))
-            torch.cuda.synchronize()
-            assert pk.pa_check_errors() == 0
-            assert np.array_equal(out.cpu().numpy().view(np.uint16), base.view(np.uint16))
+            for sched in (pk.PA_SCHED_HEADS, pk.PA_SCHED_SHARED):
+                pk.pa_decode(b.pool, b.qd, out, b.tabd, b.ctxd, maxc, partition_tokens=ptok, workspace=ws,
+                             seq_order=torch.from_numpy(order.astype(np.int32)).to(DEV), schedule=sched)
+                torch.cuda.synchronize()
+                assert pk.pa_check_errors() == 0
+                assert np.array_equal(out.cpu().numpy().view(np.uint16), base.view(np.uint16))
+    with pytest.raises(pk.PagedKVError) as e:
+        pk.pa_decode(b.pool, b.qd, out, b.tabd, b.ctxd, maxc, seq_order=b.ctxd, schedule=7)
+    assert e.value.status == pk.PA_ERR_INVALID_ARG
 
 
 def test_out_of_range_indices_are_flagged_not_followed():

@@ -35,6 +35,7 @@ def _same(o, n, live):
     cold, hot = n.free_lists()
     assert list(o.cold_free) == cold and list(o.hot_free) == hot
     assert [o.ref[b] for b in range(o.num_cold)] == [n.ref_count(b) for b in range(o.num_cold)]
+    assert n.batch_shares(live) == any(o.ref[b] > 1 for s in live for b in o.seqs[s].cold)
     if live:
         ot, oh, oc = o.export(live, 16)
         nt, nh, nc = n.export(live, 16)
