@@ -304,6 +304,13 @@ pa_status pa_decode_contiguous(const void* k, const void* v, pa_dtype kv_dtype, 
 
 pa_status pa_stream_copy(void* dst, const void* src, int64_t bytes, pa_stream stream);
 
+/* *device_view = the address at which kernels reach the pinned host memory
+ * at host (hipHostMalloc, or a pinned tensor). Device calls accept such
+ * addresses wherever they read small step data (tables, contexts, order,
+ * slots, pairs): the kernels then read host memory in place over the host
+ * link. Errors: PA_ERR_INVALID_ARG (NULL, or memory that is not pinned). */
+pa_status pa_host_view(void* host, void** device_view);
+
 /* Reads bytes (a multiple of 16, 16-byte aligned) with a plain streaming
  * kernel and folds them into a checksum: the read-only bandwidth probe. sink
  * is device memory of at least 4096 bytes that may receive a word. */

@@ -476,6 +476,15 @@ pa_status pa_stage_copy(void* dst, const void* host_src, int64_t bytes, pa_strea
   return hip_status("pa_stage_copy", pa::launch_stage_copy(dst, view, bytes, stream));
 }
 
+pa_status pa_host_view(void* host, void** device_view) {
+  if (!host || !device_view) return fail(PA_ERR_INVALID_ARG, "pa_host_view: NULL argument");
+  hipError_t e = hipSuccess;
+  *device_view = host_view(host, &e);
+  if (!*device_view)
+    return fail(PA_ERR_INVALID_ARG, "pa_host_view: not pinned host memory (%s)", hipGetErrorString(e));
+  return PA_OK;
+}
+
 pa_status pa_stream_read(const void* src, int64_t bytes, void* sink, pa_stream stream) {
   if (!src || !sink || bytes < 0 || bytes % 16 || !aligned16(src))
     return fail(PA_ERR_INVALID_ARG, "pa_stream_read: bad arguments");

@@ -6,18 +6,22 @@ A step appends one token to each sequence of a batch and attends with it:
    ring evictions, then the batch's table rows and live context lengths —
    all written into a pinned staging buffer by two library calls, plus the
    longest-first dispatch order;
-2. ``pa_stage_copy`` uploads that buffer with one small kernel on the step's
-   stream (``overlap_uploads=True`` moves it to an auxiliary stream that the
-   step's kernels wait on with an event; measured, the cross-stream wait costs
-   about what the overlap saves, so it is off by default);
+2. the step's kernels read that buffer in place over the host link (the
+   default where pinned memory has the same address on the device: no upload
+   and one kernel boundary less per step), or ``pa_stage_copy`` uploads it
+   with one small kernel first (``host_tables=False``; ``overlap_uploads=True``
+   then moves the upload to an auxiliary stream that the step's kernels wait
+   on with an event; measured, that wait costs about what the overlap saves);
 3. ``pa_copy_blocks`` for the copy-on-write pairs (only when there are any);
 4. ``pa_write_kv`` of the new K/V rows into their slots and
 5. ``pa_decode_ordered`` (single pass, or split-K partitions plus the reduce
    kernel) — for float pools both in one launch, ``pa_write_decode``.
 
 The host never waits for the device inside a step: pinned staging buffers
-rotate through a small ring guarded by events, and two device staging buffers
-alternate so an upload never overwrites the tables a running decode reads.
+rotate through a small ring guarded by events (a buffer is rewritten only
+after the last kernel that reads it is done), and with uploads two device
+staging buffers alternate so an upload never overwrites the tables a
+running decode reads.
 """
 
 from __future__ import annotations
@@ -54,9 +58,10 @@ class _Staging:
         self.cur = 0
         self.ring = []
         for _ in range(depth):
-            v = self._views(torch.empty(self.bytes, dtype=torch.uint8, pin_memory=True))
-            v = {k: (t if k == "buf" else t.numpy()) for k, t in v.items()}
-            v["event"] = None             # event: the upload that last read this buffer is done
+            tv = self._views(torch.empty(self.bytes, dtype=torch.uint8, pin_memory=True))
+            v = {k: (t if k == "buf" else t.numpy()) for k, t in tv.items()}
+            v["t"] = tv                   # the same pinned memory as tensors
+            v["event"] = None             # event: the last kernel that reads this buffer is done
             self.ring.append(v)
         self.next = 0
         self.aux = torch.cuda.Stream(device=device) if aux_stream else None
@@ -101,6 +106,17 @@ class _Staging:
         done.record(stream)
         dv["released"] = done
 
+    def in_place_ok(self) -> bool:
+        """Whether kernels can read the pinned buffers at their host
+        addresses (the tensors handed to them carry those addresses)."""
+        return all(N.pa_host_view(st["buf"]) == st["buf"].data_ptr() for st in self.ring)
+
+    def release_host(self, st, stream) -> None:
+        """The kernels read ``st`` in place: it may be rewritten once they are done."""
+        done = torch.cuda.Event()
+        done.record(stream)
+        st["event"] = done
+
 
 class _Workspace:
     """Split-K workspace on the device, grown geometrically."""
@@ -120,7 +136,8 @@ class PagedDecodeEngine:
                  max_seqs: int, max_blocks_per_seq: int, *, window_blocks: int = 0,
                  free_order=None, device="cuda", partition_tokens: int = 0,
                  pool_fill=None, staging_depth: int = 3, longest_first: bool = True,
-                 overlap_uploads: bool = False, fuse_write: bool = True, block_size: int = N.BLOCK_SIZE):
+                 overlap_uploads: bool = False, fuse_write: bool = True, block_size: int = N.BLOCK_SIZE,
+                 host_tables=None):
         self.device = torch.device(device)
         self.num_heads, self.head_dim = num_heads, head_dim
         self.kv_dtype = kv_dtype
@@ -142,6 +159,9 @@ class PagedDecodeEngine:
                                max_seqs, self.device, staging_depth, overlap_uploads)
         for v in self._stage.dev:
             v["tables"].fill_(-1)
+        self.host_tables = self._stage.in_place_ok() if host_tables is None else host_tables
+        if self.host_tables and not self._stage.in_place_ok():
+            raise N.PagedKVError(N.PA_ERR_UNSUPPORTED, "pinned memory has a different device address")
         self._ws = _Workspace(self.device)
         self.last_ctx = np.zeros(0, dtype=np.int32)
         self.last_pairs = 0
@@ -260,8 +280,9 @@ class PagedDecodeEngine:
         self.last_slots = st["slots"][:n].copy()
 
         cur = torch.cuda.current_stream(self.device) if stream is None else stream
-        # Everything up to the end of this batch's table rows, in one upload.
-        dv = self._stage.upload(st, n if decode else 0, cur)
+        # Everything up to the end of this batch's table rows, in one upload
+        # (or none: the kernels read the pinned buffer in place).
+        dv = st["t"] if self.host_tables else self._stage.upload(st, n if decode else 0, cur)
         with torch.cuda.stream(cur):
             if npairs:
                 N.pa_copy_blocks(self.pool, dv["pairs"][:npairs], stream=cur)
@@ -284,7 +305,10 @@ class PagedDecodeEngine:
                                 schedule=sched)
                 if decode_events is not None:
                     decode_events[1].record(cur)
-            self._stage.release(dv, cur)
+            if self.host_tables:
+                self._stage.release_host(st, cur)
+            else:
+                self._stage.release(dv, cur)
 
     def decode(self, seqs, q, out, *, partition_tokens=None, stream=None, longest_first=None) -> None:
         """Decode the batch as it stands (no append): tables and contexts uploaded first."""
@@ -326,7 +350,7 @@ class MixedDecodeEngine:
 
     def __init__(self, num_cold: int, num_hot: int, num_heads: int, head_dim: int, max_seqs: int,
                  max_cold_per_seq: int, *, cold_order=None, hot_order=None, device="cuda",
-                 partition_tokens: int = 0, staging_depth: int = 3, longest_first: bool = True):
+                 partition_tokens: int = 0, staging_depth: int = 3, longest_first: bool = True, host_tables=None):
         self.device = torch.device(device)
         self.num_heads, self.head_dim = num_heads, head_dim
         self.cold = N.new_pool(num_cold, num_heads, head_dim, N.PA_I8, device=self.device, fill=0)
@@ -342,6 +366,7 @@ class MixedDecodeEngine:
                                max_seqs, self.device, staging_depth, False)
         for v in self._stage.dev:
             v["tables"].fill_(-1)
+        self.host_tables = self._stage.in_place_ok() if host_tables is None else host_tables
         self._ws = _Workspace(self.device)
         self.last_ctx = np.zeros(0, dtype=np.int32)
         self.last_pairs = 0
@@ -381,7 +406,7 @@ class MixedDecodeEngine:
         self.last_ctx = ctx_np.copy()
         self.last_pairs = npairs
         cur = torch.cuda.current_stream(self.device) if stream is None else stream
-        dv = self._stage.upload(st, n if decode else 0, cur)
+        dv = st["t"] if self.host_tables else self._stage.upload(st, n if decode else 0, cur)
         with torch.cuda.stream(cur):
             if npairs:
                 N.pa_demote_blocks(self.hot, self.cold, dv["pairs"][:npairs], stream=cur)
@@ -396,4 +421,7 @@ class MixedDecodeEngine:
                                   seq_order=dv["order"][:n] if self.longest_first else None, schedule=sched)
                 if decode_events is not None:
                     decode_events[1].record(cur)
-            self._stage.release(dv, cur)
+            if self.host_tables:
+                self._stage.release_host(st, cur)
+            else:
+                self._stage.release(dv, cur)

@@ -77,6 +77,7 @@ _SIGS = {
     "pa_stream_copy": ([_vp, _vp, _i64, _vp], _i32),
     "pa_stream_read": ([_vp, _i64, _vp, _vp], _i32),
     "pa_stage_copy": ([_vp, _vp, _i64, _vp], _i32),
+    "pa_host_view": ([_vp, C.POINTER(_vp)], _i32),
     "pa_bm_create": ([_i32, _i32, _vp, _i32, C.POINTER(_vp)], _i32),
     "pa_bm_destroy": ([_vp], _i32),
     "pa_bm_add_seq": ([_vp, _i64, _i32, _vp], _i32),
@@ -150,8 +151,8 @@ def _ptr(t, name: str, dtype=None, device=True):
         raise PagedKVError(PA_ERR_INVALID_ARG, f"{name}: dtype {t.dtype}, expected {dtype}")
     if not t.is_contiguous():
         raise PagedKVError(PA_ERR_INVALID_ARG, f"{name}: must be contiguous")
-    if device and not t.is_cuda:
-        raise PagedKVError(PA_ERR_INVALID_ARG, f"{name}: must be a device tensor")
+    if device and not (t.is_cuda or t.is_pinned()):
+        raise PagedKVError(PA_ERR_INVALID_ARG, f"{name}: must be a device tensor or pinned host memory")
     return t.data_ptr()
 
 
@@ -423,6 +424,13 @@ def pa_stream_copy(dst, src, stream=None) -> None:
         raise PagedKVError(PA_ERR_INVALID_ARG, "dst too small")
     _check(lib.pa_stream_copy(_ptr(dst, "dst"), _ptr(src, "src"), nbytes, _stream(stream, src)),
            "pa_stream_copy")
+
+
+def pa_host_view(t) -> int:
+    """The address kernels use for the pinned host tensor ``t``."""
+    out = C.c_void_p()
+    _check(lib.pa_host_view(C.c_void_p(t.data_ptr()), C.byref(out)), "pa_host_view")
+    return out.value or 0
 
 
 def pa_stage_copy(dst, host_src, nbytes=None, stream=None) -> None:

@@ -36,12 +36,12 @@ def _contexts():
     return [int(c) for c in g.integers(20, 300, size=PARENTS)]
 
 
-def _run(pk, Engine, overlap, fuse, longest_first, ptok, bs):
+def _run(pk, Engine, overlap, fuse, longest_first, ptok, bs, host_tables):
     ctx0 = _contexts()
     order = W.free_order(SEED, NB)
     eng = Engine(NB, H, D, pk.PA_F16, S, 64, free_order=order, device=DEV, partition_tokens=ptok,
                  pool_fill=0.0, overlap_uploads=overlap, fuse_write=fuse, longest_first=longest_first,
-                 block_size=bs)
+                 block_size=bs, host_tables=host_tables)
     rows = {}
     for s, c in enumerate(ctx0):
         K = W.normal_torch((c, H, D), SEED, W.STREAM_K, s, dtype=torch.float16, device=DEV)
@@ -75,9 +75,13 @@ def test_step_options_are_bit_identical(ptok, bs):
     import paged_kv_cache_249_amd as pk
     from paged_kv_cache_249_amd.engine import PagedDecodeEngine as Engine
     base = None
-    for overlap, fuse, lf in itertools.product([False, True], [True, False], [True, False]):
-        print(f"engine options overlap={overlap} fuse={fuse} longest_first={lf} ptok={ptok} bs={bs}", flush=True)
-        r = _run(pk, Engine, overlap, fuse, lf, ptok, bs)
+    # The step data uploaded by a kernel (host_tables False) or read in place.
+    combos = list(itertools.product([False, True], [True, False], [True, False], [False]))
+    combos += [(False, True, True, True), (False, False, False, True)]
+    for overlap, fuse, lf, ht in combos:
+        print(f"engine options overlap={overlap} fuse={fuse} longest_first={lf} host_tables={ht} ptok={ptok} "
+              f"bs={bs}", flush=True)
+        r = _run(pk, Engine, overlap, fuse, lf, ptok, bs, ht)
         if base is None:
             base = r
             continue
