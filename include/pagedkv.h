@@ -261,12 +261,14 @@ pa_status pa_write_decode(pa_pool* pool, const void* k_new, const void* v_new, p
                           pa_stream stream);
 
 /* Layout of the split-K workspace, for callers that inspect partials: with
- * P = ceil(max_context_len / partition_tokens), the workspace holds
+ * P = ceil(max_context_len / partition_tokens) and n = num_seqs * num_heads * P,
+ * the workspace holds
  *   m [num_seqs][num_heads][P] fp32   largest logit of the partition (natural units)
  *   l [num_seqs][num_heads][P] fp32   sum of exp(logit - m)
  *   o [num_seqs][num_heads][P][head_dim] fp32  attention over the partition alone
- * back to back, in that order. Entries of partitions past a sequence's context
- * are not written. */
+ * in that order, m and l each padded to a multiple of 4 floats (n rounded up)
+ * so that o is 16-byte aligned. Entries of partitions past a sequence's
+ * context are not written. */
 
 /* Upload a step's small host data (slots, table rows, context lengths, ...)
  * with a compute kernel that reads pinned host memory directly: host_src must

@@ -212,9 +212,14 @@ static int64_t num_partitions(int32_t max_ctx, int32_t partition_tokens) {
   return p < 1 ? 1 : p;
 }
 
+// m and l hold n = S * H * P floats each, padded to a multiple of 4 so that
+// o starts 16-byte aligned.
+static int64_t padded4(int64_t n) { return (n + 3) / 4 * 4; }
+
 static int64_t workspace_bytes_for(int64_t S, int64_t H, int64_t D, int64_t P) {
   if (P <= 1) return 0;
-  return S * H * P * (2 + D) * 4;
+  const int64_t n = S * H * P;
+  return (2 * padded4(n) + n * D) * 4;
 }
 
 pa_status pa_decode_workspace_bytes(const pa_pool* pool, int32_t num_seqs, int32_t max_context_len,
@@ -255,8 +260,8 @@ static pa_status decode_common(const char* fn, pa::DecodeArgs& a, void* workspac
     if (!aligned16(workspace)) return fail(PA_ERR_INVALID_ARG, "%s: workspace must be 16-byte aligned", fn);
     const int64_t n = int64_t(a.num_seqs) * a.num_heads * P;
     a.ws_m = static_cast<float*>(workspace);
-    a.ws_l = a.ws_m + n;
-    a.ws_o = a.ws_l + n;
+    a.ws_l = a.ws_m + padded4(n);
+    a.ws_o = a.ws_l + padded4(n);
   }
   if (a.num_seqs == 0) return PA_OK;
   return hip_status(fn, pa::launch_decode(a, stream));

@@ -98,6 +98,12 @@ constexpr int kRsrcWord3 = 0x00020000;  // buffer resource word 3 for raw dword 
 #ifndef PA_DECODE_PREFETCH
 #define PA_DECODE_PREFETCH 1
 #endif
+// Split launches with partitions of at most this many tokens give each wave
+// a partition of its own.
+#ifndef PA_DECODE_WAVE_PART_MAX
+#define PA_DECODE_WAVE_PART_MAX 512
+#endif
+constexpr int kWavePartMaxTokens = PA_DECODE_WAVE_PART_MAX;
 // Minimum waves per SIMD the register allocator must leave room for.
 #ifndef PA_DECODE_MIN_WAVES
 #define PA_DECODE_MIN_WAVES (PA_DECODE_PREFETCH ? 4 : 8)
@@ -274,7 +280,10 @@ __device__ __forceinline__ QT to_out(float x) {
 
 // NEW: element type of the fused-write source rows (void = no fused write).
 // kMixed: int8 cold pool through the table plus an fp16 hot block per sequence.
-template <typename KV, typename QT, int D, bool kPaged, typename NEW, bool kMixed = false>
+// kWavePart: each wave owns one whole partition (a workgroup covers kWaves
+// consecutive partitions of one (sequence, head)); otherwise the kWaves waves
+// share one partition.
+template <typename KV, typename QT, int D, bool kPaged, typename NEW, bool kMixed = false, bool kWavePart = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PA_DECODE_MIN_WAVES)))
 void decode_kernel(Params p, const int32_t* __restrict__ tables, const int32_t* __restrict__ seq_ctx,
                    const int64_t* __restrict__ new_slots) {
@@ -285,10 +294,12 @@ void decode_kernel(Params p, const int32_t* __restrict__ tables, const int32_t* 
   constexpr int CPT = G::kCPT, TPI = G::kTPI, NLD = G::kNLD, EPC = G::kEPC;
   constexpr bool kInt8 = std::is_same<KV, int8_t>::value;
 
-  const int total = p.num_seqs * p.num_heads * p.num_partitions;
+  constexpr int kPartsPerGroup = kWavePart ? kWaves : 1;
+  const int groups = (p.num_partitions + kPartsPerGroup - 1) / kPartsPerGroup;
+  const int total = p.num_seqs * p.num_heads * groups;
   const int w = xcd_remap(int(blockIdx.x), total);
   int s, h;
-  const int part = w / (p.num_seqs * p.num_heads);
+  const int pgroup = w / (p.num_seqs * p.num_heads);
   if (p.order) {
     const int r = w % (p.num_seqs * p.num_heads);
     int rank;
@@ -317,6 +328,7 @@ void decode_kernel(Params p, const int32_t* __restrict__ tables, const int32_t* 
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = wave_uniform(threadIdx.x / kWave);
+  const int part = kWavePart ? pgroup * kWaves + wave : pgroup;
   const int grp = lane / CPT;
   const int col = lane % CPT;
   const int64_t sh = int64_t(s) * p.num_heads + h;
@@ -325,8 +337,10 @@ void decode_kernel(Params p, const int32_t* __restrict__ tables, const int32_t* 
   const int64_t head_stride = int64_t(G::kTileBytes) << ushift;   // one (block, head) tile
   const int64_t block_stride = int64_t(p.num_heads) * head_stride;
   const int unit_begin = part * p.partition_units;
-  // This wave's units are first, first + 4, first + 8, ... (k-th at first + 4k).
-  const int first = unit_begin + wave;
+  // This wave's units are first, first + ustride, first + 2 ustride, ...:
+  // every kWaves-th unit of the shared partition, or all of its own one.
+  constexpr int ustride = kWavePart ? 1 : kWaves;
+  const int first = unit_begin + (kWavePart ? 0 : wave);
   const int32_t* trow = kPaged ? tables + int64_t(s) * p.max_blocks : nullptr;
 
   // Loads that do not depend on the context length go out together with it:
@@ -337,7 +351,7 @@ void decode_kernel(Params p, const int32_t* __restrict__ tables, const int32_t* 
   int e0 = 0, e1 = 0;
   if constexpr (kPaged) {
     e0 = (first >> ushift) < p.max_blocks ? trow[first >> ushift] : 0;
-    e1 = ((first + kWaves) >> ushift) < p.max_blocks ? trow[(first + kWaves) >> ushift] : 0;
+    e1 = ((first + ustride) >> ushift) < p.max_blocks ? trow[(first + ustride) >> ushift] : 0;
   }
   QSlice<KV, QT, EPC> qs;
   qs.load(reinterpret_cast<const QT*>(p.q) + sh * D + col * EPC);
@@ -368,14 +382,14 @@ void decode_kernel(Params p, const int32_t* __restrict__ tables, const int32_t* 
   // Units read through the table (mixed pages: all but the last, hot one).
   const int table_units = kMixed ? max(nunits - 1, 0) : nunits;
   const int unit_end = min(unit_begin + p.partition_units, table_units);
-  const int iters = first < unit_end ? (unit_end - first + kWaves - 1) / kWaves : 0;
+  const int iters = first < unit_end ? (unit_end - first + ustride - 1) / ustride : 0;
 
   // Table entry of the wave's k-th unit. Reads are wave-uniform and the loop
   // stores nothing, so they go through the scalar cache and are counted apart
   // from the vector loads: each is issued half an iteration before it is used.
   auto entry = [&](int k) -> int {
     if constexpr (kPaged) {
-      return trow[(first + kWaves * k) >> ushift];
+      return trow[(first + ustride * k) >> ushift];
     } else {
       return 0;
     }
@@ -413,7 +427,7 @@ void decode_kernel(Params p, const int32_t* __restrict__ tables, const int32_t* 
   // Issue the loads of the wave's k-th unit (table entry phys) into (kr, vr).
   auto fetch = [&](int k, int phys, uint4 (&kr)[NLD], uint4 (&vr)[NLD]) -> TileRef {
     TileRef t;
-    t.b = first + k * kWaves;
+    t.b = first + k * ustride;
     t.phys = phys;
     const int64_t off = tile_offset(t.b, phys, &t.ok);
     load_tile(p.k, off, kr);
@@ -449,7 +463,8 @@ void decode_kernel(Params p, const int32_t* __restrict__ tables, const int32_t* 
   const int64_t in_block = (int64_t(1) << bshift) - 1;   // offset mask inside a block
   if constexpr (kFusable) {
     if (new_slots != nullptr && new_slot >= 0) {
-      const bool owner = unit_end == nunits && nunits > 0 && wave == (nunits - 1 - unit_begin) % kWaves;
+      const bool owner = unit_end == nunits && nunits > 0 && nunits - 1 >= first &&
+                         (nunits - 1 - first) % ustride == 0;
       if (nunits == 0 || (new_slot & in_block) != ((ctx - 1) & in_block)) {
         bad_slot = part == 0 && wave == 0;       // reported once per (sequence, head)
       } else if (owner) {
@@ -569,8 +584,7 @@ void decode_kernel(Params p, const int32_t* __restrict__ tables, const int32_t* 
   // Mixed pages: the hot unit, by the wave that owns it.
   if constexpr (kMixed) {
     const int hu = nunits - 1;
-    if (nunits > 0 && hu >= unit_begin && hu < unit_begin + p.partition_units &&
-        wave == (hu - unit_begin) % kWaves) {
+    if (nunits > 0 && hu >= first && hu < unit_begin + p.partition_units && (hu - first) % ustride == 0) {
       constexpr int kHW = EPC * 2 / 16;   // 16-byte words of fp16 per lane and row
       const bool ok = unsigned(hot_blk) < unsigned(p.num_hot);
       bad_entry |= !ok;
@@ -640,6 +654,40 @@ void decode_kernel(Params p, const int32_t* __restrict__ tables, const int32_t* 
   if (bad_entry && lane == 0) flag_error(p.err, PA_DEV_BAD_TABLE_ENTRY);
   if (bad_ctx && threadIdx.x == 0 && part == 0) flag_error(p.err, PA_DEV_BAD_CONTEXT);
 
+  if constexpr (kWavePart) {
+    // Epilogue of a wave-owned partition: merge the wave's TPI row-group
+    // streams across lanes (the lanes of one column, CPT apart) by the
+    // log-sum-exp identity; no workgroup barrier.
+#pragma unroll
+    for (int mask = CPT; mask < kWave; mask <<= 1) {
+      const float m2 = __shfl_xor(m, mask);
+      const float l2 = __shfl_xor(l, mask);
+      const float mn = fmaxf(m, m2);
+      const float a = __builtin_amdgcn_exp2f(m - mn);
+      const float b = __builtin_amdgcn_exp2f(m2 - mn);
+      l = l * a + l2 * b;
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) acc[e] = acc[e] * a + __shfl_xor(acc[e], mask) * b;
+      m = mn;
+    }
+    if (grp == 0) {
+      if (seq_parts == 1) {
+#pragma unroll
+        for (int e = 0; e < EPC; ++e)
+          reinterpret_cast<QT*>(p.out)[sh * D + col * EPC + e] = to_out<QT>(l > 0.f ? acc[e] / l : 0.f);
+      } else {
+        const int64_t slot = sh * p.num_partitions + part;
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) p.ws_o[slot * D + col * EPC + e] = l > 0.f ? acc[e] / l : 0.f;
+        if (col == 0) {
+          p.ws_m[slot] = m * kLn2;
+          p.ws_l[slot] = l;
+        }
+      }
+    }
+    return;
+  }
+
   // Epilogue: merge the kWaves * TPI softmax streams of the workgroup.
   constexpr int kStreams = kWaves * TPI;
   __shared__ float s_m[kStreams];
@@ -680,8 +728,22 @@ void decode_kernel(Params p, const int32_t* __restrict__ tables, const int32_t* 
 }
 
 // Merge the partitions of every (sequence, head) that has more than one.
+// One workgroup per (sequence, head): thread t reads 4 adjacent dims (16
+// bytes) of every kLanes-th partition, kLanes = 256 / (D / 4) partitions at a
+// time with 4 loads each in flight, and the partial sums meet in LDS.
+#ifndef PA_REDUCE_THREADS
+#define PA_REDUCE_THREADS 256
+#endif
+#ifndef PA_REDUCE_UNROLL
+#define PA_REDUCE_UNROLL 4
+#endif
+constexpr int kReduceThreads = PA_REDUCE_THREADS;
+
 template <typename QT, int D>
-__global__ __launch_bounds__(D) void reduce_kernel(Params p) {
+__global__ __launch_bounds__(kReduceThreads) void reduce_kernel(Params p) {
+  constexpr int kQuads = D / 4;                       // threads per partition row
+  constexpr int kLanes = kReduceThreads / kQuads;     // partitions read at a time
+  constexpr int kUnroll = PA_REDUCE_UNROLL;
   const int sh = blockIdx.x;
   const int s = sh / p.num_heads;
   int ctx = p.ctx[s];
@@ -691,67 +753,107 @@ __global__ __launch_bounds__(D) void reduce_kernel(Params p) {
   if (parts <= 1) return;
   const float* m = p.ws_m + int64_t(sh) * p.num_partitions;
   const float* l = p.ws_l + int64_t(sh) * p.num_partitions;
-  const float* o = p.ws_o + int64_t(sh) * p.num_partitions * D;
+  const float4* o = reinterpret_cast<const float4*>(p.ws_o + int64_t(sh) * p.num_partitions * D);
 
+  __shared__ float s_max[kReduceThreads / kWave];
+  __shared__ float s_l[kLanes];
+  __shared__ float4 s_o[kLanes][kQuads];
   float M = kNegBig;
-  for (int i = threadIdx.x; i < parts; i += D) M = fmaxf(M, m[i]);
+  for (int i = threadIdx.x; i < parts; i += kReduceThreads) M = fmaxf(M, m[i]);
   M = wave_max(M);
-  __shared__ float s_max[D / kWave];
   if ((threadIdx.x & (kWave - 1)) == 0) s_max[threadIdx.x / kWave] = M;
   __syncthreads();
 #pragma unroll
-  for (int i = 0; i < D / kWave; ++i) M = fmaxf(M, s_max[i]);
+  for (int i = 0; i < kReduceThreads / kWave; ++i) M = fmaxf(M, s_max[i]);
 
-  const int d = threadIdx.x;
-  float L = 0.f, O = 0.f;
-  for (int i = 0; i < parts; ++i) {
+  const int dq = threadIdx.x % kQuads;
+  const int lane_p = threadIdx.x / kQuads;
+  float L = 0.f;
+  float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
+  auto add = [&](int i, const float4& x) {
     const float wgt = __builtin_amdgcn_exp2f((m[i] - M) * kLog2e) * l[i];
     L += wgt;
-    O = fmaf(wgt, o[int64_t(i) * D + d], O);
+    O.x = fmaf(wgt, x.x, O.x);
+    O.y = fmaf(wgt, x.y, O.y);
+    O.z = fmaf(wgt, x.z, O.z);
+    O.w = fmaf(wgt, x.w, O.w);
+  };
+  int i = lane_p;
+  for (; i + (kUnroll - 1) * kLanes < parts; i += kUnroll * kLanes) {
+    float4 x[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) x[u] = o[int64_t(i + u * kLanes) * kQuads + dq];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) add(i + u * kLanes, x[u]);
   }
-  reinterpret_cast<QT*>(p.out)[int64_t(sh) * D + d] = to_out<QT>(O / L);
+  for (; i < parts; i += kLanes) add(i, o[int64_t(i) * kQuads + dq]);
+  s_o[lane_p][dq] = O;
+  if (dq == 0) s_l[lane_p] = L;
+  __syncthreads();
+  if (threadIdx.x < D) {
+    const int d = threadIdx.x;
+    float Lt = 0.f, Ot = 0.f;
+#pragma unroll
+    for (int j = 0; j < kLanes; ++j) {
+      Lt += s_l[j];
+      const float4 v = s_o[j][d / 4];
+      Ot += (d % 4 == 0) ? v.x : (d % 4 == 1) ? v.y : (d % 4 == 2) ? v.z : v.w;
+    }
+    reinterpret_cast<QT*>(p.out)[int64_t(sh) * D + d] = to_out<QT>(Ot / Lt);
+  }
 }
 
-template <typename KV, typename QT, int D, bool kPaged>
-int launch_typed(const Params& p, int grid, int sh_count, hipStream_t st) {
+template <typename KV, typename QT, int D, bool kPaged, bool kWP>
+void launch_kernels(const Params& p, int grid, hipStream_t st) {
   if constexpr (kPaged && std::is_same<KV, int8_t>::value) {
     if (p.hot_blocks != nullptr)
-      hipLaunchKernelGGL((decode_kernel<KV, QT, D, kPaged, void, true>), dim3(grid), dim3(kThreads), 0, st, p,
+      hipLaunchKernelGGL((decode_kernel<KV, QT, D, kPaged, void, true, kWP>), dim3(grid), dim3(kThreads), 0, st, p,
                          p.tables, p.ctx, p.slots);
     else
-      hipLaunchKernelGGL((decode_kernel<KV, QT, D, kPaged, void>), dim3(grid), dim3(kThreads), 0, st, p, p.tables,
-                         p.ctx, p.slots);
+      hipLaunchKernelGGL((decode_kernel<KV, QT, D, kPaged, void, false, kWP>), dim3(grid), dim3(kThreads), 0, st, p,
+                         p.tables, p.ctx, p.slots);
   } else if constexpr (kPaged) {
     if (p.slots != nullptr) {
       if (p.new_is_f32)
-        hipLaunchKernelGGL((decode_kernel<KV, QT, D, kPaged, float>), dim3(grid), dim3(kThreads), 0, st, p,
-                           p.tables, p.ctx, p.slots);
+        hipLaunchKernelGGL((decode_kernel<KV, QT, D, kPaged, float, false, kWP>), dim3(grid), dim3(kThreads), 0, st,
+                           p, p.tables, p.ctx, p.slots);
       else
-        hipLaunchKernelGGL((decode_kernel<KV, QT, D, kPaged, _Float16>), dim3(grid), dim3(kThreads), 0, st, p,
-                           p.tables, p.ctx, p.slots);
+        hipLaunchKernelGGL((decode_kernel<KV, QT, D, kPaged, _Float16, false, kWP>), dim3(grid), dim3(kThreads), 0,
+                           st, p, p.tables, p.ctx, p.slots);
     } else {
-      hipLaunchKernelGGL((decode_kernel<KV, QT, D, kPaged, void>), dim3(grid), dim3(kThreads), 0, st, p,
+      hipLaunchKernelGGL((decode_kernel<KV, QT, D, kPaged, void, false, kWP>), dim3(grid), dim3(kThreads), 0, st, p,
                          p.tables, p.ctx, p.slots);
     }
   } else {
-    hipLaunchKernelGGL((decode_kernel<KV, QT, D, kPaged, void>), dim3(grid), dim3(kThreads), 0, st, p, p.tables,
-                       p.ctx, p.slots);
+    hipLaunchKernelGGL((decode_kernel<KV, QT, D, kPaged, void, false, kWP>), dim3(grid), dim3(kThreads), 0, st, p,
+                       p.tables, p.ctx, p.slots);
   }
+}
+
+template <typename KV, typename QT, int D, bool kPaged>
+int launch_typed(const Params& p, int sh_count, hipStream_t st) {
+  // Short partitions of a split launch: one partition per wave, so a
+  // workgroup's start-up and epilogue are paid once per kWaves partitions.
+  const bool wave_part = p.num_partitions > 1 && p.partition_units * kTileRows <= kWavePartMaxTokens;
+  if (wave_part)
+    launch_kernels<KV, QT, D, kPaged, true>(p, sh_count * ((p.num_partitions + kWaves - 1) / kWaves), st);
+  else
+    launch_kernels<KV, QT, D, kPaged, false>(p, sh_count * p.num_partitions, st);
   if (p.num_partitions > 1)
-    hipLaunchKernelGGL((reduce_kernel<QT, D>), dim3(sh_count), dim3(D), 0, st, p);
+    hipLaunchKernelGGL((reduce_kernel<QT, D>), dim3(sh_count), dim3(kReduceThreads), 0, st, p);
   return int(hipGetLastError());
 }
 
 template <typename KV, typename QT, bool kPaged>
-int launch_d(const Params& p, int D, int grid, int sh_count, hipStream_t st) {
-  return D == 64 ? launch_typed<KV, QT, 64, kPaged>(p, grid, sh_count, st)
-                 : launch_typed<KV, QT, 128, kPaged>(p, grid, sh_count, st);
+int launch_d(const Params& p, int D, int sh_count, hipStream_t st) {
+  return D == 64 ? launch_typed<KV, QT, 64, kPaged>(p, sh_count, st)
+                 : launch_typed<KV, QT, 128, kPaged>(p, sh_count, st);
 }
 
 template <typename KV, bool kPaged>
-int launch_q(const Params& p, pa_dtype qd, int D, int grid, int sh_count, hipStream_t st) {
-  return qd == PA_F32 ? launch_d<KV, float, kPaged>(p, D, grid, sh_count, st)
-                      : launch_d<KV, _Float16, kPaged>(p, D, grid, sh_count, st);
+int launch_q(const Params& p, pa_dtype qd, int D, int sh_count, hipStream_t st) {
+  return qd == PA_F32 ? launch_d<KV, float, kPaged>(p, D, sh_count, st)
+                      : launch_d<KV, _Float16, kPaged>(p, D, sh_count, st);
 }
 
 }  // namespace
@@ -793,19 +895,18 @@ int launch_decode(const DecodeArgs& a, void* stream) {
   p.hot_blocks = a.hot_blocks;
   p.num_hot = a.num_hot;
   const int sh_count = a.num_seqs * a.num_heads;
-  const int grid = sh_count * a.num_partitions;
-  if (grid == 0) return 0;
+  if (sh_count == 0) return 0;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const bool paged = a.tables != nullptr;
   switch (a.kv_dtype) {
     case PA_F32:
-      return paged ? launch_q<float, true>(p, a.q_dtype, a.head_dim, grid, sh_count, st)
-                   : launch_q<float, false>(p, a.q_dtype, a.head_dim, grid, sh_count, st);
+      return paged ? launch_q<float, true>(p, a.q_dtype, a.head_dim, sh_count, st)
+                   : launch_q<float, false>(p, a.q_dtype, a.head_dim, sh_count, st);
     case PA_F16:
-      return paged ? launch_q<_Float16, true>(p, a.q_dtype, a.head_dim, grid, sh_count, st)
-                   : launch_q<_Float16, false>(p, a.q_dtype, a.head_dim, grid, sh_count, st);
+      return paged ? launch_q<_Float16, true>(p, a.q_dtype, a.head_dim, sh_count, st)
+                   : launch_q<_Float16, false>(p, a.q_dtype, a.head_dim, sh_count, st);
     case PA_I8:
-      return launch_q<int8_t, true>(p, a.q_dtype, a.head_dim, grid, sh_count, st);
+      return launch_q<int8_t, true>(p, a.q_dtype, a.head_dim, sh_count, st);
   }
   return int(hipErrorInvalidValue);
 }

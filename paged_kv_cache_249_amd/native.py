@@ -408,7 +408,8 @@ def contiguous_workspace_bytes(num_seqs: int, num_heads: int, head_dim: int, max
     if partition_tokens <= 0:
         return 0
     P = max(1, -(-max_tokens // partition_tokens))
-    return 0 if P <= 1 else num_seqs * num_heads * P * (2 + head_dim) * 4
+    n = num_seqs * num_heads * P
+    return 0 if P <= 1 else (2 * (-(-n // 4) * 4) + n * head_dim) * 4
 
 
 def pa_check_errors(stream=None) -> int:

@@ -178,14 +178,16 @@ def test_split_partials_match_the_oracle():
     # plain definition the oracle computes directly.
     ctx = [700, 96, 513]
     ptok = 256
-    b = Batch(ctx, 4, 128, "f16", "f16", seed=62)
+    b = Batch(ctx, 3, 128, "f16", "f16", seed=62)
     _, ws = b.gpu(ptok)
-    S, H, D = len(ctx), 4, 128
+    S, H, D = len(ctx), 3, 128
     P = -(-max(ctx) // ptok)
     flat = ws.cpu().numpy()
-    m = flat[:S * H * P].reshape(S, H, P)
-    l = flat[S * H * P:2 * S * H * P].reshape(S, H, P)
-    o = flat[2 * S * H * P:2 * S * H * P + S * H * P * D].reshape(S, H, P, D)
+    n = S * H * P
+    n4 = -(-n // 4) * 4                      # m and l are padded to a multiple of 4
+    m = flat[:n].reshape(S, H, P)
+    l = flat[n4:n4 + n].reshape(S, H, P)
+    o = flat[2 * n4:2 * n4 + n * D].reshape(S, H, P, D)
     scale = 1.0 / math.sqrt(D)
     for s, c in enumerate(ctx):
         parts = -(-c // ptok)

@@ -183,9 +183,11 @@ def test_long_context_split_k_full_size():
     qh = q.cpu().numpy()
     P = T // ptok
     ws = eng.workspace.cpu().numpy()
-    m = ws[:S * H * P].reshape(S, H, P)
-    l = ws[S * H * P:2 * S * H * P].reshape(S, H, P)
-    o = ws[2 * S * H * P:2 * S * H * P + S * H * P * D].reshape(S, H, P, D)
+    n = S * H * P
+    n4 = -(-n // 4) * 4                      # m and l are padded to a multiple of 4
+    m = ws[:n].reshape(S, H, P)
+    l = ws[n4:n4 + n].reshape(S, H, P)
+    o = ws[2 * n4:2 * n4 + n * D].reshape(S, H, P, D)
     scale = 1.0 / math.sqrt(D)
     for s, heads in ((0, (0, 31)), (3, (17,)), (1, (5,))):
         for h in heads:
