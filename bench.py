@@ -52,6 +52,7 @@ def parse():
                     help="write profiles/*.txt from rocprofv3 output under DIR and exit")
     ap.add_argument("--cpu-baseline-only", action="store_true", help=argparse.SUPPRESS)
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help=argparse.SUPPRESS)
+    ap.add_argument("--cpu-workers", type=int, default=1, help=argparse.SUPPRESS)
     return ap.parse_args()
 
 
@@ -197,10 +198,22 @@ def recorded_traffic():
 # ---------------------------------------------------------------------------
 # CPU baseline: the oracle on a bounded sample (run in a child process so the
 # thread count is fixed before numpy loads).
-def cpu_baseline_child(seconds: float) -> None:
+_CPU_BATCH = None
+
+
+def _cpu_decode_one(i):
+    from oracle import attention as OA
+    q, kp, vp, nb, ctx = _CPU_BATCH[i]
+    OA.paged_decode(q, kp, vp, [list(range(nb))], [ctx])
+    return ctx
+
+
+def cpu_baseline_child(seconds: float, workers: int = 1) -> None:
     """Whole passes of the oracle over the 64-sequence batch until ``seconds``
     of decode time are spent (setup — generation and the scatter into each
-    sequence's pool — is not timed)."""
+    sequence's pool — is not timed). With ``workers`` > 1 the sequences of a
+    pass are shared by a pool of that many forked processes."""
+    global _CPU_BATCH
     import numpy as np
     import workloads as W
     from oracle import attention as OA
@@ -227,39 +240,69 @@ def cpu_baseline_child(seconds: float) -> None:
     seqs = 0
     passes = 0
     spent = 0.0
-    while spent < seconds:
-        for q, kp, vp, nb, ctx in batch:
-            t0 = time.perf_counter()
-            OA.paged_decode(q, kp, vp, [list(range(nb))], [ctx])
-            spent += time.perf_counter() - t0
-            done_bytes += ctx * H * D * 2 * 2
-            seqs += 1
-        passes += 1
-    print(json.dumps({"seconds": spent, "bytes": done_bytes, "seqs": seqs, "passes": passes}))
+    if workers > 1:
+        import multiprocessing as mp
+        _CPU_BATCH = batch
+        with mp.get_context("fork").Pool(workers) as pool:
+            while spent < seconds:
+                t0 = time.perf_counter()
+                ctxs = pool.map(_cpu_decode_one, range(len(batch)), chunksize=1)
+                spent += time.perf_counter() - t0
+                done_bytes += sum(ctxs) * H * D * 2 * 2
+                seqs += len(ctxs)
+                passes += 1
+    else:
+        while spent < seconds:
+            for q, kp, vp, nb, ctx in batch:
+                t0 = time.perf_counter()
+                OA.paged_decode(q, kp, vp, [list(range(nb))], [ctx])
+                spent += time.perf_counter() - t0
+                done_bytes += ctx * H * D * 2 * 2
+                seqs += 1
+            passes += 1
+    print(json.dumps({"seconds": spent, "bytes": done_bytes, "seqs": seqs, "passes": passes,
+                      "workers": workers}))
 
 
-def cpu_baseline(seconds: float) -> dict:
+def _cpu_run(seconds: float, workers: int) -> dict:
     env = dict(os.environ, OMP_NUM_THREADS="1", OPENBLAS_NUM_THREADS="1", MKL_NUM_THREADS="1",
                HIP_VISIBLE_DEVICES="", CUDA_VISIBLE_DEVICES="")
     r = subprocess.run([sys.executable, os.path.abspath(__file__), "--cpu-baseline-only",
-                        "--cpu-seconds", str(seconds)], capture_output=True, text=True, env=env,
-                       cwd=ROOT, timeout=600)
+                        "--cpu-seconds", str(seconds), "--cpu-workers", str(workers)], capture_output=True,
+                       text=True, env=env, cwd=ROOT, timeout=600)
     if r.returncode != 0:
         return {"error": r.stderr[-500:]}
-    d = json.loads(r.stdout.strip().splitlines()[-1])
-    return {"value": round(d["bytes"] / d["seconds"] / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle",
-            "sample": f"fp64 numpy oracle (gather through the block table + attention), {d['passes']} "
-                      f"whole passes over the 64-sequence batch, all 40 heads: {d['bytes'] / 1e6:.1f} MB "
-                      f"of KV in {d['seconds']:.2f} s on one thread",
-            "seqs_per_s": round(d["seqs"] / d["seconds"], 4)}
+    return json.loads(r.stdout.strip().splitlines()[-1])
+
+
+def cpu_baseline(seconds: float) -> dict:
+    """The oracle on one thread (the reported baseline) and on a pool of
+    processes over sequences (one thread each), up to 16 host cores."""
+    d = _cpu_run(seconds, 1)
+    if "error" in d:
+        return d
+    res = {"value": round(d["bytes"] / d["seconds"] / 1e9, 4), "unit": "GB/s", "cores": 1,
+           "kind": "oracle",
+           "sample": f"fp64 numpy oracle (gather through the block table + attention), {d['passes']} "
+                     f"whole passes over the 64-sequence batch, all 40 heads: {d['bytes'] / 1e6:.1f} MB "
+                     f"of KV in {d['seconds']:.2f} s on one thread",
+           "seqs_per_s": round(d["seqs"] / d["seconds"], 4)}
+    n = min(16, len(os.sched_getaffinity(0)))
+    if n > 1:
+        m = _cpu_run(seconds, n)
+        if "error" not in m:
+            res["multi_core"] = {"value": round(m["bytes"] / m["seconds"] / 1e9, 4), "unit": "GB/s", "cores": n,
+                                 "sample": f"{m['passes']} whole passes, sequences over {n} processes of one "
+                                           f"thread, {m['seconds']:.2f} s wall",
+                                 "seqs_per_s": round(m["seqs"] / m["seconds"], 4)}
+    return res
 
 
 # ---------------------------------------------------------------------------
 def main():
     args = parse()
     if args.cpu_baseline_only:
-        cpu_baseline_child(args.cpu_seconds)
+        cpu_baseline_child(args.cpu_seconds, args.cpu_workers)
         return 0
     if args.summarize_profiles:
         return summarize_profiles(args.summarize_profiles)
@@ -387,6 +430,8 @@ def main():
         ub = ws["unique_bytes_of"](eng.last_ctx)
         result["unique_kv_bytes_per_decode"] = ub
         result["unique_gbs"] = round(ub / dec_avg_s / 1e9, 2)
+        if not args.no_extras:
+            result["extras"] = shared_prefix_cache_probe(pk, torch, np, eng, q, dev, ub)
     if args.workload == "opt13b":
         if not args.no_extras:
             result["extras"] = extras(eng, wl, q, ptok, dev)
@@ -563,6 +608,16 @@ def extras(eng, wl, q, ptok, dev):
     res["contiguous_gbs"] = round(nbytes / t_contig / 1e9, 1)
     res["paged_gbs"] = round(nbytes / t_paged / 1e9, 1)
     res["paged_vs_contiguous_overhead"] = round(t_paged / t_contig - 1.0, 4)
+    # Identity placement: each sequence's blocks consecutive in the pool, to
+    # separate the cost of the table lookup from that of scattered blocks.
+    bmi = pk.BlockManager(eng.pool.num_blocks, 16)
+    for s_ in range(S):
+        bmi.add_seq(s_, int(ctx[s_]))
+    tab_id, _ = bmi.export(np.arange(S), eng.cap)
+    tab_idd = torch.from_numpy(tab_id).to(dev)
+    t_ident = _time_calls(lambda: pk.pa_decode(eng.pool, q, out, tab_idd, ctxd, maxc, seq_order=order))
+    res["paged_identity_placement_gbs"] = round(nbytes / t_ident / 1e9, 1)
+    res["identity_vs_contiguous_overhead"] = round(t_ident / t_contig - 1.0, 4)
     del kc, vc
     res["block_size_sweep"] = block_size_sweep(pk, W, torch, np, wl, ctx, q, out, order, t_contig, nbytes, dev)
     res["swap"] = swap_probe(pk, torch, np, eng, q, dev)
@@ -578,6 +633,12 @@ def extras(eng, wl, q, ptok, dev):
     sink = torch.zeros(1024, dtype=torch.int32, device=dev)
     t_read = _time_calls(lambda: pk.pa_stream_read(big, sink))
     res["stream_read_gbs"] = round(big.numel() / t_read / 1e9, 1)
+    # The achievable read rate for a read of the decode's size (same cache
+    # policy, one plain streaming kernel): the practical ceiling of the step.
+    same = big[:nbytes // 16 * 16]
+    t_same = _time_calls(lambda: pk.pa_stream_read(same, sink))
+    res["achievable_read_gbs_at_decode_size"] = round(same.numel() / t_same / 1e9, 1)
+    res["paged_frac_of_achievable"] = round(t_same / t_paged * same.numel() / nbytes, 4)
     return res
 
 
@@ -629,6 +690,41 @@ def prefix_probe(pk, W, np):
     return {"sequences": P * Sm, "prompt_tokens": pt, "blocks_used": used,
             "blocks_without_sharing": P * Sm * -(-pt // 16), "shared_blocks": shared,
             "host_us_per_sequence": round(dt / (P * Sm) * 1e6, 1)}
+
+
+def shared_prefix_cache_probe(pk, torch, np, eng, q, dev, unique_bytes):
+    """Decode of the shared-prefix batch with the last-level cache warm (the
+    previous decode's blocks still cached) and cold (a 1 GiB read of other
+    memory before every decode)."""
+    S = eng.max_seqs
+    seqs = np.arange(S)
+    out = torch.empty_like(q)
+    eng.decode(seqs, q, out)
+    torch.cuda.synchronize()
+    tabd = eng.tables[:S].clone()
+    ctxd = eng.ctx[:S].clone()
+    cl = ctxd.cpu().numpy()
+    order = torch.from_numpy(np.argsort(-cl, kind="stable").astype(np.int32)).to(dev)
+    maxc = int(cl.max())
+    sched = pk.PA_SCHED_SHARED if eng.bm.batch_shares(seqs) else pk.PA_SCHED_HEADS
+    run = lambda: pk.pa_decode(eng.pool, q, out, tabd, ctxd, maxc, seq_order=order, schedule=sched)
+    t_warm = _time_calls(run)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1024, dtype=torch.int32, device=dev)
+    ms = []
+    for _ in range(10):
+        pk.pa_stream_read(flush, sink)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        run()
+        b.record()
+        torch.cuda.synchronize()
+        ms.append(a.elapsed_time(b))
+    t_cold = sorted(ms)[len(ms) // 2] / 1e3
+    return {"decode_warm_us": round(t_warm * 1e6, 2), "decode_cold_us": round(t_cold * 1e6, 2),
+            "unique_gbs_warm": round(unique_bytes / t_warm / 1e9, 1),
+            "unique_gbs_cold": round(unique_bytes / t_cold / 1e9, 1),
+            "unique_frac_of_peak_cold": round(unique_bytes / t_cold / 1e9 / HBM_PEAK_GBS, 4)}
 
 
 def swap_probe(pk, torch, np, eng, q, dev, nseq=16, rounds=3):

@@ -314,8 +314,9 @@ pa_status pa_stream_copy(void* dst, const void* src, int64_t bytes, pa_stream st
 pa_status pa_host_view(void* host, void** device_view);
 
 /* Reads bytes (a multiple of 16, 16-byte aligned) with a plain streaming
- * kernel and folds them into a checksum: the read-only bandwidth probe. sink
- * is device memory of at least 4096 bytes that may receive a word. */
+ * kernel (non-temporal loads, the policy of the decode kernel's K/V reads)
+ * and folds them into a checksum: the achievable read bandwidth. sink is
+ * device memory of at least 4096 bytes that may receive a word. */
 pa_status pa_stream_read(const void* src, int64_t bytes, void* sink, pa_stream stream);
 
 /* ----------------------------------------------------------------------------

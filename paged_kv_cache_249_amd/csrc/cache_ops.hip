@@ -314,22 +314,32 @@ __global__ __launch_bounds__(kThreads) void stage_copy_kernel(uint4* __restrict_
   }
 }
 
-// Reads n16 16-byte words and folds them into a checksum; the store that
-// keeps the loads alive fires only for one checksum value in 2^32.
-__global__ __launch_bounds__(kThreads) void stream_read_kernel(const uint4* __restrict__ src, int64_t n16,
+// Reads a buffer chunk by chunk: workgroup b reads bytes [b * kReadChunk,
+// +kReadChunk) through a buffer resource (the hardware returns zeros past the
+// end of the buffer), four 16-byte non-temporal loads per lane in flight (the
+// cache policy of the decode kernel's K/V tiles), and folds them into a
+// checksum; the store that keeps the loads alive fires only for one checksum
+// value in 2^32.
+constexpr int kReadChunk = 65536;
+
+__global__ __launch_bounds__(kThreads) void stream_read_kernel(const char* src, int64_t bytes,
                                                                uint32_t* __restrict__ sink) {
   constexpr int kUnroll = 4;
-  const int64_t stride = int64_t(gridDim.x) * kThreads;
-  int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+  constexpr int kStep = kThreads * 16;
+  const int64_t base = int64_t(blockIdx.x) * kReadChunk;
+  const int64_t left = bytes - base;
+  const int n = int(left < kReadChunk ? left : kReadChunk);
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(src + base), 0, n, 0x00020000);
   uint32_t acc = 0;
-  for (; i + (kUnroll - 1) * stride < n16; i += kUnroll * stride) {
+  for (int off = threadIdx.x * 16; off < kReadChunk; off += kStep * kUnroll) {
     uint4 r[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) r[u] = src[i + u * stride];
+    for (int u = 0; u < kUnroll; ++u)
+      r[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + u * kStep, 0, 2));
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) acc ^= r[u].x ^ r[u].y ^ r[u].z ^ r[u].w;
   }
-  for (; i < n16; i += stride) acc ^= src[i].x ^ src[i].y ^ src[i].z ^ src[i].w;
   if (acc == 0x9E3779B9u) sink[blockIdx.x & 1023] = acc;
 }
 
@@ -458,12 +468,10 @@ int launch_stage_copy(void* dst, const void* src_device_view, int64_t bytes, voi
 }
 
 int launch_stream_read(const void* src, int64_t bytes, void* sink, void* stream) {
-  const int64_t n16 = bytes / 16;
-  if (n16 == 0) return 0;
-  int64_t blocks = (n16 + kThreads - 1) / kThreads;
-  if (blocks > 256 * 8) blocks = 256 * 8;
-  hipLaunchKernelGGL(stream_read_kernel, dim3(unsigned(blocks)), dim3(kThreads), 0,
-                     static_cast<hipStream_t>(stream), static_cast<const uint4*>(src), n16,
+  if (bytes == 0) return 0;
+  const int64_t chunks = (bytes + kReadChunk - 1) / kReadChunk;
+  hipLaunchKernelGGL(stream_read_kernel, dim3(unsigned(chunks)), dim3(kThreads), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const char*>(src), bytes,
                      static_cast<uint32_t*>(sink));
   return int(hipGetLastError());
 }

@@ -170,7 +170,8 @@ class PagedDecodeEngine:
     def workspace(self):
         return self._ws.buf
 
-    # Device views of the staging buffer the latest step used.
+    # Device views of the device staging buffer last written (by decode(), or
+    # by a step that uploads instead of reading the pinned buffer in place).
     @property
     def slots(self):
         return self._stage.dev[self._stage.cur]["slots"]
