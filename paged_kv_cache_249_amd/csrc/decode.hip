@@ -104,6 +104,21 @@ constexpr int kRsrcWord3 = 0x00020000;  // buffer resource word 3 for raw dword 
 #define PA_DECODE_WAVE_PART_MAX 512
 #endif
 constexpr int kWavePartMaxTokens = PA_DECODE_WAVE_PART_MAX;
+// Split launches with many partitions per sequence: a workgroup streams
+// several consecutive partitions, about kGroupTokens tokens, as long as the
+// launch keeps at least kMinGroups workgroups.
+#ifndef PA_DECODE_GROUP_TOKENS
+#define PA_DECODE_GROUP_TOKENS 8192
+#endif
+#ifndef PA_DECODE_MIN_GROUPS
+#define PA_DECODE_MIN_GROUPS 2048
+#endif
+constexpr int kGroupTokens = PA_DECODE_GROUP_TOKENS;
+constexpr int kMinGroups = PA_DECODE_MIN_GROUPS;
+// At most this many partitions per workgroup: their per-wave partials wait in
+// LDS, kWaves * (D + 2) floats each (33 KB at D = 128).
+constexpr int kMaxGroupParts = 16;
+
 // Minimum waves per SIMD the register allocator must leave room for.
 #ifndef PA_DECODE_MIN_WAVES
 #define PA_DECODE_MIN_WAVES (PA_DECODE_PREFETCH ? 4 : 8)
@@ -138,6 +153,7 @@ struct Params {
   int32_t num_blocks;
   int32_t max_ctx;
   int32_t partition_units;  // 16-row units per partition
+  int32_t parts_per_group;  // shared partitions: how many one workgroup streams
   int32_t unit_shift;       // log2(block_size / 16)
   int32_t num_partitions;
   float scale_log2;
@@ -281,8 +297,11 @@ __device__ __forceinline__ QT to_out(float x) {
 // NEW: element type of the fused-write source rows (void = no fused write).
 // kMixed: int8 cold pool through the table plus an fp16 hot block per sequence.
 // kWavePart: each wave owns one whole partition (a workgroup covers kWaves
-// consecutive partitions of one (sequence, head)); otherwise the kWaves waves
-// share one partition.
+// consecutive partitions of one (sequence, head)). Otherwise the kWaves waves
+// share each partition, taking every kWaves-th unit, and a workgroup streams
+// p.parts_per_group consecutive partitions, handing over each one's (m, l, o)
+// when its last units are done while the next partition's loads are already
+// in flight.
 template <typename KV, typename QT, int D, bool kPaged, typename NEW, bool kMixed = false, bool kWavePart = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PA_DECODE_MIN_WAVES)))
 void decode_kernel(Params p, const int32_t* __restrict__ tables, const int32_t* __restrict__ seq_ctx,
@@ -294,8 +313,8 @@ void decode_kernel(Params p, const int32_t* __restrict__ tables, const int32_t* 
   constexpr int CPT = G::kCPT, TPI = G::kTPI, NLD = G::kNLD, EPC = G::kEPC;
   constexpr bool kInt8 = std::is_same<KV, int8_t>::value;
 
-  constexpr int kPartsPerGroup = kWavePart ? kWaves : 1;
-  const int groups = (p.num_partitions + kPartsPerGroup - 1) / kPartsPerGroup;
+  const int parts_per_group = kWavePart ? kWaves : p.parts_per_group;
+  const int groups = (p.num_partitions + parts_per_group - 1) / parts_per_group;
   const int total = p.num_seqs * p.num_heads * groups;
   const int w = xcd_remap(int(blockIdx.x), total);
   int s, h;
@@ -328,7 +347,8 @@ void decode_kernel(Params p, const int32_t* __restrict__ tables, const int32_t* 
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = wave_uniform(threadIdx.x / kWave);
-  const int part = kWavePart ? pgroup * kWaves + wave : pgroup;
+  // The wave's partition (shared partitions: the workgroup's first one).
+  const int part = kWavePart ? pgroup * kWaves + wave : pgroup * parts_per_group;
   const int grp = lane / CPT;
   const int col = lane % CPT;
   const int64_t sh = int64_t(s) * p.num_heads + h;
@@ -342,6 +362,16 @@ void decode_kernel(Params p, const int32_t* __restrict__ tables, const int32_t* 
   constexpr int ustride = kWavePart ? 1 : kWaves;
   const int first = unit_begin + (kWavePart ? 0 : wave);
   const int32_t* trow = kPaged ? tables + int64_t(s) * p.max_blocks : nullptr;
+
+  // Shared partitions: the waves that are done are counted in LDS, and the
+  // last one merges the workgroup's partials. The count is zeroed before any
+  // load is issued, so this barrier waits for nothing but the other waves'
+  // start.
+  __shared__ int s_done;
+  if constexpr (!kWavePart) {
+    if (threadIdx.x == 0) s_done = 0;
+    __syncthreads();
+  }
 
   // Loads that do not depend on the context length go out together with it:
   // the table entries of the wave's first two units (inside the row; unused
@@ -381,7 +411,7 @@ void decode_kernel(Params p, const int32_t* __restrict__ tables, const int32_t* 
   if (part >= seq_parts) return;
   // Units read through the table (mixed pages: all but the last, hot one).
   const int table_units = kMixed ? max(nunits - 1, 0) : nunits;
-  const int unit_end = min(unit_begin + p.partition_units, table_units);
+  const int unit_end = min(unit_begin + (kWavePart ? 1 : parts_per_group) * p.partition_units, table_units);
   const int iters = first < unit_end ? (unit_end - first + ustride - 1) / ustride : 0;
 
   // Table entry of the wave's k-th unit. Reads are wave-uniform and the loop
@@ -489,6 +519,77 @@ void decode_kernel(Params p, const int32_t* __restrict__ tables, const int32_t* 
     }
   };
 
+  // Hand over the wave's partial result for partition pidx and restart its
+  // stream. The wave's TPI row-group streams meet first, across lanes (the
+  // lanes of one column, CPT apart), by the log-sum-exp identity. A wave that
+  // owns its partition then writes (m, l, o) — or the output when the
+  // sequence has one partition. Waves that share partitions park the partial
+  // in their own LDS slot; the workgroup's partitions are merged once, after
+  // the loop.
+  float* s_o = nullptr;       // [parts_per_group][kWaves][D] unnormalised o
+  float* s_m = nullptr;       // [parts_per_group][kWaves] running max (base 2)
+  float* s_l = nullptr;       // [parts_per_group][kWaves] softmax denominators
+  if constexpr (!kWavePart) {
+    extern __shared__ __align__(16) float lds_partials[];
+    s_o = lds_partials;
+    s_m = s_o + parts_per_group * kWaves * D;
+    s_l = s_m + parts_per_group * kWaves;
+  }
+  auto emit = [&](int pidx, int d, float M, float L, float O) {
+    const float res = L > 0.f ? O / L : 0.f;
+    if (seq_parts == 1) {
+      reinterpret_cast<QT*>(p.out)[sh * D + d] = to_out<QT>(res);
+    } else {
+      const int64_t slot = sh * p.num_partitions + pidx;
+      p.ws_o[slot * D + d] = res;
+      if (d == 0) {
+        p.ws_m[slot] = M * kLn2;
+        p.ws_l[slot] = L;
+      }
+    }
+  };
+  auto flush = [&](int pidx) {
+    float fm = m, fl = l, fa[EPC];
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) fa[e] = acc[e];
+#pragma unroll
+    for (int mask = CPT; mask < kWave; mask <<= 1) {
+      const float m2 = __shfl_xor(fm, mask);
+      const float l2 = __shfl_xor(fl, mask);
+      const float mn = fmaxf(fm, m2);
+      const float a = __builtin_amdgcn_exp2f(fm - mn);
+      const float b = __builtin_amdgcn_exp2f(m2 - mn);
+      fl = fl * a + l2 * b;
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) fa[e] = fa[e] * a + __shfl_xor(fa[e], mask) * b;
+      fm = mn;
+    }
+    if (grp == 0) {
+      if constexpr (kWavePart) {
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) emit(pidx, col * EPC + e, fm, fl, fa[e]);
+      } else {
+        const int slot = (pidx - part) * kWaves + wave;
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) s_o[slot * D + col * EPC + e] = fa[e];
+        if (col == 0) {
+          s_m[slot] = fm;
+          s_l[slot] = fl;
+        }
+      }
+    }
+    m = kNegBig;
+    l = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) acc[e] = 0.f;
+  };
+  // The unit that starts the workgroup's next partition (shared partitions).
+  // Partitions are a multiple of kWaves units whenever a workgroup streams
+  // more than one, so every wave holds units of each full partition and hands
+  // over every partition once: at its last unit of the partition, or after
+  // the loop for the last one (an empty stream if it holds none of it).
+  int next_flush = unit_begin + p.partition_units;
+
   // Online-softmax update with one unit.
   auto process = [&](const TileRef& t, uint4 (&kr)[NLD], uint4 (&vr)[NLD]) {
     bad_entry |= !t.ok;
@@ -536,6 +637,12 @@ void decode_kernel(Params p, const int32_t* __restrict__ tables, const int32_t* 
       axpy16<KV, EPC>(pi * t.vscale, vr[i], acc);
     }
     m = mn;
+    if constexpr (!kWavePart && !kMixed) {
+      if (t.b + ustride >= next_flush && next_flush < unit_end) {   // the wave's last unit of a partition
+        flush(next_flush / p.partition_units - 1);
+        next_flush += p.partition_units;
+      }
+    }
   };
 
   // Two register buffers in turn. Inside the loop the next tile's loads are
@@ -654,74 +761,68 @@ void decode_kernel(Params p, const int32_t* __restrict__ tables, const int32_t* 
   if (bad_entry && lane == 0) flag_error(p.err, PA_DEV_BAD_TABLE_ENTRY);
   if (bad_ctx && threadIdx.x == 0 && part == 0) flag_error(p.err, PA_DEV_BAD_CONTEXT);
 
-  if constexpr (kWavePart) {
-    // Epilogue of a wave-owned partition: merge the wave's TPI row-group
-    // streams across lanes (the lanes of one column, CPT apart) by the
-    // log-sum-exp identity; no workgroup barrier.
+  // The last (or only) partition: the one holding the last unit read through
+  // the table, else the first (an empty context, or mixed pages whose
+  // partition holds just the hot unit).
+  const int last = unit_end > unit_begin ? (unit_end - 1) / p.partition_units : part;
+  flush(last);
+  if constexpr (!kWavePart) {
+    // The last wave to park its partials merges every partition of the
+    // workgroup; the others end here. (With a workgroup barrier instead, every
+    // wave would wait for the slowest: over a long stream the waves drift
+    // apart, and waiting waves hold their slots.)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    int prev = 0;
+    if (lane == 0) prev = __hip_atomic_fetch_add(&s_done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    if (__shfl(prev, 0) != kWaves - 1) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    typedef float f4v __attribute__((ext_vector_type(4)));
+    constexpr int kQ = D / 4;
+    const int nparts = last - part + 1;
+    const int64_t slot0 = sh * p.num_partitions + part;
+    // (m, l) of partition `lane`, stored as whole runs of the workspace.
+    if (seq_parts != 1 && lane < nparts) {
+      const float* mm = s_m + lane * kWaves;
+      const float* ll = s_l + lane * kWaves;
+      float M = mm[0];
 #pragma unroll
-    for (int mask = CPT; mask < kWave; mask <<= 1) {
-      const float m2 = __shfl_xor(m, mask);
-      const float l2 = __shfl_xor(l, mask);
-      const float mn = fmaxf(m, m2);
-      const float a = __builtin_amdgcn_exp2f(m - mn);
-      const float b = __builtin_amdgcn_exp2f(m2 - mn);
-      l = l * a + l2 * b;
+      for (int w = 1; w < kWaves; ++w) M = fmaxf(M, mm[w]);
+      float L = 0.f;
 #pragma unroll
-      for (int e = 0; e < EPC; ++e) acc[e] = acc[e] * a + __shfl_xor(acc[e], mask) * b;
-      m = mn;
+      for (int w = 0; w < kWaves; ++w) L = fmaf(__builtin_amdgcn_exp2f(mm[w] - M), ll[w], L);
+      p.ws_m[slot0 + lane] = M * kLn2;
+      p.ws_l[slot0 + lane] = L;
     }
-    if (grp == 0) {
-      if (seq_parts == 1) {
+    // o: a lane merges 4 adjacent dims at a time (16-byte LDS reads and
+    // stores), so the merging wave, which holds the workgroup's slot, issues
+    // few instructions.
+    const f4v* o4 = reinterpret_cast<const f4v*>(s_o);
+    for (int i = lane; i < nparts * kQ; i += kWave) {
+      const int idx = i / kQ, c = i % kQ;
+      const float* mm = s_m + idx * kWaves;
+      const float* ll = s_l + idx * kWaves;
+      float M = mm[0];
 #pragma unroll
-        for (int e = 0; e < EPC; ++e)
-          reinterpret_cast<QT*>(p.out)[sh * D + col * EPC + e] = to_out<QT>(l > 0.f ? acc[e] / l : 0.f);
-      } else {
-        const int64_t slot = sh * p.num_partitions + part;
+      for (int w = 1; w < kWaves; ++w) M = fmaxf(M, mm[w]);
+      float L = 0.f;
+      f4v O = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) p.ws_o[slot * D + col * EPC + e] = l > 0.f ? acc[e] / l : 0.f;
-        if (col == 0) {
-          p.ws_m[slot] = m * kLn2;
-          p.ws_l[slot] = l;
-        }
+      for (int w = 0; w < kWaves; ++w) {
+        const float wgt = __builtin_amdgcn_exp2f(mm[w] - M);
+        L = fmaf(wgt, ll[w], L);
+        O += wgt * o4[(idx * kWaves + w) * kQ + c];
       }
-    }
-    return;
-  }
-
-  // Epilogue: merge the kWaves * TPI softmax streams of the workgroup.
-  constexpr int kStreams = kWaves * TPI;
-  __shared__ float s_m[kStreams];
-  __shared__ float s_l[kStreams];
-  __shared__ float s_acc[kStreams][D];
-  const int j = wave * TPI + grp;
-#pragma unroll
-  for (int e = 0; e < EPC; ++e) s_acc[j][col * EPC + e] = acc[e];
-  if (col == 0) {
-    s_m[j] = m;
-    s_l[j] = l;
-  }
-  __syncthreads();
-  if (threadIdx.x < D) {
-    const int d = threadIdx.x;
-    float M = kNegBig;
-#pragma unroll
-    for (int t = 0; t < kStreams; ++t) M = fmaxf(M, s_m[t]);
-    float L = 0.f, O = 0.f;
-#pragma unroll
-    for (int t = 0; t < kStreams; ++t) {
-      const float wgt = __builtin_amdgcn_exp2f(s_m[t] - M);
-      L = fmaf(wgt, s_l[t], L);
-      O = fmaf(wgt, s_acc[t][d], O);
-    }
-    const float res = L > 0.f ? O / L : 0.f;
-    if (seq_parts == 1) {
-      reinterpret_cast<QT*>(p.out)[sh * D + d] = to_out<QT>(res);
-    } else {
-      const int64_t slot = sh * p.num_partitions + part;
-      p.ws_o[slot * D + d] = res;
-      if (d == 0) {
-        p.ws_m[slot] = M * kLn2;
-        p.ws_l[slot] = L;
+      const f4v res = L > 0.f ? O / L : f4v{0.f, 0.f, 0.f, 0.f};
+      if (seq_parts == 1) {
+        QT* o = reinterpret_cast<QT*>(p.out) + sh * D + 4 * c;
+        o[0] = to_out<QT>(res.x);
+        o[1] = to_out<QT>(res.y);
+        o[2] = to_out<QT>(res.z);
+        o[3] = to_out<QT>(res.w);
+      } else {
+        // Written once and read once by the reduce: kept out of the caches
+        // that the tile stream runs through (plain stores cost the stream 3%).
+        __builtin_nontemporal_store(res, reinterpret_cast<f4v*>(p.ws_o) + (slot0 + idx) * kQ + c);
       }
     }
   }
@@ -805,40 +906,54 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(Params p) {
 
 template <typename KV, typename QT, int D, bool kPaged, bool kWP>
 void launch_kernels(const Params& p, int grid, hipStream_t st) {
+  // Shared partitions park per-wave partials in LDS until the workgroup merges them.
+  const size_t lds = kWP ? 0 : size_t(p.parts_per_group) * kWaves * (D + 2) * sizeof(float);
   if constexpr (kPaged && std::is_same<KV, int8_t>::value) {
     if (p.hot_blocks != nullptr)
-      hipLaunchKernelGGL((decode_kernel<KV, QT, D, kPaged, void, true, kWP>), dim3(grid), dim3(kThreads), 0, st, p,
+      hipLaunchKernelGGL((decode_kernel<KV, QT, D, kPaged, void, true, kWP>), dim3(grid), dim3(kThreads), lds, st, p,
                          p.tables, p.ctx, p.slots);
     else
-      hipLaunchKernelGGL((decode_kernel<KV, QT, D, kPaged, void, false, kWP>), dim3(grid), dim3(kThreads), 0, st, p,
+      hipLaunchKernelGGL((decode_kernel<KV, QT, D, kPaged, void, false, kWP>), dim3(grid), dim3(kThreads), lds, st, p,
                          p.tables, p.ctx, p.slots);
   } else if constexpr (kPaged) {
     if (p.slots != nullptr) {
       if (p.new_is_f32)
-        hipLaunchKernelGGL((decode_kernel<KV, QT, D, kPaged, float, false, kWP>), dim3(grid), dim3(kThreads), 0, st,
+        hipLaunchKernelGGL((decode_kernel<KV, QT, D, kPaged, float, false, kWP>), dim3(grid), dim3(kThreads), lds, st,
                            p, p.tables, p.ctx, p.slots);
       else
-        hipLaunchKernelGGL((decode_kernel<KV, QT, D, kPaged, _Float16, false, kWP>), dim3(grid), dim3(kThreads), 0,
+        hipLaunchKernelGGL((decode_kernel<KV, QT, D, kPaged, _Float16, false, kWP>), dim3(grid), dim3(kThreads), lds,
                            st, p, p.tables, p.ctx, p.slots);
     } else {
-      hipLaunchKernelGGL((decode_kernel<KV, QT, D, kPaged, void, false, kWP>), dim3(grid), dim3(kThreads), 0, st, p,
+      hipLaunchKernelGGL((decode_kernel<KV, QT, D, kPaged, void, false, kWP>), dim3(grid), dim3(kThreads), lds, st, p,
                          p.tables, p.ctx, p.slots);
     }
   } else {
-    hipLaunchKernelGGL((decode_kernel<KV, QT, D, kPaged, void, false, kWP>), dim3(grid), dim3(kThreads), 0, st, p,
+    hipLaunchKernelGGL((decode_kernel<KV, QT, D, kPaged, void, false, kWP>), dim3(grid), dim3(kThreads), lds, st, p,
                        p.tables, p.ctx, p.slots);
   }
 }
 
 template <typename KV, typename QT, int D, bool kPaged>
 int launch_typed(const Params& p, int sh_count, hipStream_t st) {
-  // Short partitions of a split launch: one partition per wave, so a
-  // workgroup's start-up and epilogue are paid once per kWaves partitions.
-  const bool wave_part = p.num_partitions > 1 && p.partition_units * kTileRows <= kWavePartMaxTokens;
-  if (wave_part)
-    launch_kernels<KV, QT, D, kPaged, true>(p, sh_count * ((p.num_partitions + kWaves - 1) / kWaves), st);
-  else
-    launch_kernels<KV, QT, D, kPaged, false>(p, sh_count * p.num_partitions, st);
+  // Many partitions per sequence: a workgroup streams several (start-up paid
+  // once, loads kept in flight across partition ends, and the kWaves waves
+  // read adjacent units, which HBM serves faster than kWaves distant runs).
+  // Otherwise short split partitions go a wave each (start-up and merge paid
+  // per wave, no barrier), longer ones a workgroup each.
+  const int P = p.num_partitions;
+  const int ptok = p.partition_units * kTileRows;
+  int ppg = 1;
+  if (P > 1 && p.hot_blocks == nullptr && p.partition_units % kWaves == 0)
+    ppg = max(1, min(min(kGroupTokens / ptok, kMaxGroupParts), int(int64_t(sh_count) * P / kMinGroups)));
+  if (ppg > 1) {
+    Params q = p;
+    q.parts_per_group = ppg;
+    launch_kernels<KV, QT, D, kPaged, false>(q, sh_count * ((P + ppg - 1) / ppg), st);
+  } else if (P > 1 && ptok <= kWavePartMaxTokens) {
+    launch_kernels<KV, QT, D, kPaged, true>(p, sh_count * ((P + kWaves - 1) / kWaves), st);
+  } else {
+    launch_kernels<KV, QT, D, kPaged, false>(p, sh_count * P, st);
+  }
   if (p.num_partitions > 1)
     hipLaunchKernelGGL((reduce_kernel<QT, D>), dim3(sh_count), dim3(kReduceThreads), 0, st, p);
   return int(hipGetLastError());
@@ -880,6 +995,7 @@ int launch_decode(const DecodeArgs& a, void* stream) {
   p.partition_units = a.partition_tokens > 0 ? a.partition_tokens / kTileRows
                                               : (a.max_ctx + kTileRows - 1) / kTileRows + 1;
   p.unit_shift = block_shift(a.block_size) - 4;
+  p.parts_per_group = 1;
   p.num_partitions = a.num_partitions;
   p.scale_log2 = a.sm_scale * kLog2e;
   p.ws_m = a.ws_m;

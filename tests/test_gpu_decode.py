@@ -1,6 +1,7 @@
 """GPU parity of paged decode (single pass and split-K) against the fp64
 oracle, through the C ABI, at sizes the oracle finishes in seconds."""
 
+import functools
 import math
 
 import numpy as np
@@ -197,6 +198,93 @@ def test_split_partials_match_the_oracle():
         V = OP.gather(b.v_pool, b.tables[s], c)
         for p in range(parts):
             om, ol, oo = OA.partition_partials(b.q[s], K, V, scale, p * ptok, min((p + 1) * ptok, c))
+            np.testing.assert_allclose(m[s, :, p], om, rtol=1e-4, atol=1e-4)
+            np.testing.assert_allclose(l[s, :, p], ol, rtol=1e-4, atol=1e-4)
+            assert_close(o[s, :, p], oo, 1e-4, 1e-4, f"o s={s} p={p}")
+
+
+STREAM_CTX = [1, 16, 17, 700, 2047, 2048, 2049, 4001]
+STREAM_H = 16
+
+
+@functools.lru_cache(maxsize=1)
+def _int8_stream_batch(H, D, seed):
+    """Int8 pools written by the oracle's quantise-on-write (whole contexts
+    at once), their tables, q and the oracle's decode over the codes."""
+    ctx = STREAM_CTX
+    NB = sum(-(-c // 16) for c in ctx) + 5
+    order = W.free_order(seed, NB)
+    tables, used = [], 0
+    for c in ctx:
+        tables.append(order[used:used + -(-c // 16)])
+        used += len(tables[-1])
+    kc = np.zeros((NB, H, 16, D), np.int8)
+    vc = np.zeros_like(kc)
+    ks = np.zeros((NB, H), np.float16)
+    vs = np.zeros_like(ks)
+    for s, c in enumerate(ctx):
+        K = W.normal_np((c, H, D), seed, W.STREAM_K, s)
+        V = W.normal_np((c, H, D), seed, W.STREAM_V, s)
+        OC.write_kv_int8(kc, ks, vc, vs, K, V, OP.slots(c, tables[s]))
+    q = W.normal_np((len(ctx), H, D), seed, W.STREAM_Q, dtype=np.float16)
+    ref = OA.paged_decode(q, kc, vc, tables, ctx, k_scale=ks, v_scale=vs)
+    return NB, tables, (kc, vc, ks, vs), q, ref
+
+
+@pytest.mark.parametrize("ptok", [32, 64, 128])
+@pytest.mark.parametrize("kv,D", [("f16", 128), ("f32", 64), ("i8", 128)])
+def test_many_partitions_per_sequence(kv, D, ptok):
+    # Many partitions per sequence (16 heads x 8 sequences, contexts up to
+    # 4001): a workgroup streams several partitions (64 and 128 tokens) or a
+    # wave owns one (32 tokens), and every partition's (m, l, o) is handed
+    # over separately, including ragged last partitions that some waves hold
+    # no unit of. The workspace starts as NaN, so a partial written to the
+    # wrong slot, or one never written, reaches the output; sampled partials
+    # are also checked against their plain definition.
+    pk = _pk()
+    print(f"many partitions kv={kv} D={D} ptok={ptok}", flush=True)
+    H, seed = STREAM_H, 64
+    if kv == "i8":
+        NB, tables, (kc, vc, ks, vs), q, ref = _int8_stream_batch(H, D, seed)
+        ctx = STREAM_CTX
+        pool = pk.new_pool(NB, H, D, pk.PA_I8, device=DEV)
+        for dst, src in ((pool.k_cache, kc), (pool.v_cache, vc), (pool.k_scale, ks), (pool.v_scale, vs)):
+            dst.copy_(torch.from_numpy(src))
+        tab = np.full((len(ctx), max(len(t) for t in tables)), -1, np.int32)
+        for i, t in enumerate(tables):
+            tab[i, :len(t)] = t
+        gather = lambda s, c: (OP.gather(kc, tables[s], c, 16, ks), OP.gather(vc, tables[s], c, 16, vs))
+    else:
+        b = Batch(STREAM_CTX, H, D, kv, "f16", seed=seed)
+        ctx, pool, q, tab = b.ctx, b.pool, b.q, b.tab
+        gather = lambda s, c: (OP.gather(b.k_pool, b.tables[s], c), OP.gather(b.v_pool, b.tables[s], c))
+        ref = b.oracle()
+    qd = torch.from_numpy(q).to(DEV)
+    out = torch.empty_like(qd)
+    S, maxc = len(ctx), max(ctx)
+    ws = torch.full((pk.pa_decode_workspace_bytes(pool, S, maxc, ptok) // 4,), float("nan"), device=DEV)
+    pk.pa_decode(pool, qd, out, torch.from_numpy(tab).to(DEV), torch.tensor(ctx, dtype=torch.int32, device=DEV),
+                 maxc, partition_tokens=ptok, workspace=ws)
+    torch.cuda.synchronize()
+    assert pk.pa_check_errors() == 0
+    assert_close(out.cpu().numpy(), ref, F16_ATOL, F16_RTOL, f"{kv} ptok={ptok}")
+    P = -(-maxc // ptok)
+    flat = ws.cpu().numpy()
+    n = S * H * P
+    n4 = -(-n // 4) * 4
+    m = flat[:n].reshape(S, H, P)
+    l = flat[n4:n4 + n].reshape(S, H, P)
+    o = flat[2 * n4:2 * n4 + n * D].reshape(S, H, P, D)
+    scale = 1.0 / math.sqrt(D)
+    rng = W.rng(seed, ptok)
+    for s, c in enumerate(ctx):
+        parts = -(-c // ptok)
+        if parts == 1:
+            continue
+        K, V = gather(s, c)
+        picks = sorted(set([0, 1, parts - 2, parts - 1] + rng.integers(0, parts, size=6).tolist()))
+        for p in picks:
+            om, ol, oo = OA.partition_partials(q[s], K, V, scale, p * ptok, min((p + 1) * ptok, c))
             np.testing.assert_allclose(m[s, :, p], om, rtol=1e-4, atol=1e-4)
             np.testing.assert_allclose(l[s, :, p], ol, rtol=1e-4, atol=1e-4)
             assert_close(o[s, :, p], oo, 1e-4, 1e-4, f"o s={s} p={p}")
