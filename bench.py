@@ -61,23 +61,36 @@ CALIBRATION_BYTES = 1 << 30
 EVENT_EVERY = 4
 
 # The profiler commands whose summaries live under profiles/ (run from the
-# repository root; raw output goes to gpurun_out/).
-PROFILE_CMDS = {
-    "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_trace -o trace "
-             "-- python bench.py --steps 20 --warmup 5 --no-cpu-baseline --no-extras",
-    "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/prof_fetch -o fetch "
-             "-- python bench.py --profile-run --steps 5 --warmup 3 > gpurun_out/prof_fetch.log",
-    "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/prof_write -o write "
-             "-- python bench.py --profile-run --steps 5 --warmup 3 > gpurun_out/prof_write.log",
-    "occupancy": "rocprofv3 --pmc OccupancyPercent LdsBankConflict SQ_INSTS_LDS SQ_WAVES --output-format csv "
-                 "-d gpurun_out/prof_occ -o occ -- python bench.py --profile-run --steps 5 --warmup 3 "
-                 "> gpurun_out/prof_occ.log",
-    "occupancy_level": "rocprofv3 --pmc MeanOccupancyPerCU --output-format csv -d gpurun_out/prof_level "
-                       "-o level -- python bench.py --profile-run --steps 5 --warmup 3 > gpurun_out/prof_level.log",
-}
-OCC_FILE = os.path.join(ROOT, "profiles", "decode_opt13b_occupancy_lds.txt")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_opt13b_hbm_traffic.txt")
-STATS_FILE = os.path.join(ROOT, "profiles", "decode_opt13b_kernel_stats.txt")
+# repository root; raw output goes to gpurun_out/). The headline workload's
+# raw folders are gpurun_out/prof_<pass>; another workload's carry its name.
+def profile_cmds(workload: str = "opt13b") -> dict:
+    tag = "" if workload == "opt13b" else "_" + workload
+    wl = "" if workload == "opt13b" else " --workload " + workload
+    run = f"-- python bench.py{wl} --profile-run --steps 5 --warmup 3"
+    return {
+        "trace": f"rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof{tag}_trace -o trace "
+                 f"-- python bench.py{wl} --steps 20 --warmup 5 --no-cpu-baseline --no-extras",
+        "fetch": f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/prof{tag}_fetch -o fetch "
+                 f"{run} > gpurun_out/prof{tag}_fetch.log",
+        "write": f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/prof{tag}_write -o write "
+                 f"{run} > gpurun_out/prof{tag}_write.log",
+        "occupancy": f"rocprofv3 --pmc OccupancyPercent LdsBankConflict SQ_INSTS_LDS SQ_WAVES --output-format csv "
+                     f"-d gpurun_out/prof{tag}_occ -o occ {run} > gpurun_out/prof{tag}_occ.log",
+        "occupancy_level": f"rocprofv3 --pmc MeanOccupancyPerCU --output-format csv -d gpurun_out/prof{tag}_level "
+                           f"-o level {run} > gpurun_out/prof{tag}_level.log",
+    }
+
+
+PROFILE_CMDS = profile_cmds()
+
+
+def profile_files(workload: str = "opt13b"):
+    """(kernel stats, HBM traffic, occupancy) summary paths for a workload."""
+    base = os.path.join(ROOT, "profiles", f"decode_{workload}_")
+    return base + "kernel_stats.txt", base + "hbm_traffic.txt", base + "occupancy_lds.txt"
+
+
+STATS_FILE, TRAFFIC_FILE, OCC_FILE = profile_files()
 DECODE_SOURCE = os.path.join(ROOT, "paged_kv_cache_249_amd", "csrc", "decode.hip")
 
 
@@ -95,10 +108,19 @@ def _short(name: str) -> str:
     return name[:60]
 
 
-def summarize_profiles(raw_dir: str) -> int:
+def summarize_profiles(raw_dir: str, workload: str = "opt13b") -> int:
     """Write profiles/*.txt from rocprofv3 CSV output (kernel stats, HBM bytes)."""
     import csv
     import glob
+
+    cmds = profile_cmds(workload)
+    stats_file, traffic_file, occ_file = profile_files(workload)
+    tag = "" if workload == "opt13b" else "_" + workload
+    titles = {"opt13b": "OPT-13B-shaped paged decode step",
+              "long_context": "long-context split-K step (4 x 131072 tokens, 512-token partitions)",
+              "int8_ring": "int8 sliding-window ring step (128 x 4096 tokens)",
+              "shared_prefix": "shared-prefix parallel sampling step (8 prompts x 4 samples)",
+              "tiny": "tiny fp32 decode step"}
 
     def find(sub, pattern):
         hits = glob.glob(os.path.join(raw_dir, sub, "**", pattern), recursive=True)
@@ -106,15 +128,15 @@ def summarize_profiles(raw_dir: str) -> int:
             raise SystemExit(f"no {pattern} under {os.path.join(raw_dir, sub)}")
         return hits[0]
 
-    stats = list(csv.DictReader(open(find("prof_trace", "*kernel_stats.csv"))))
-    lines = ["# rocprofv3 kernel statistics: OPT-13B-shaped paged decode step", "",
-             "command: " + PROFILE_CMDS["trace"], "",
+    stats = list(csv.DictReader(open(find(f"prof{tag}_trace", "*kernel_stats.csv"))))
+    lines = [f"# rocprofv3 kernel statistics: {titles[workload]}", "",
+             "command: " + cmds["trace"], "",
              f"{'kernel':<58} {'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'pct':>6}"]
     for r in stats:
         lines.append(f"{_short(r['Name']):<58} {int(r['Calls']):>6} {float(r['AverageNs']) / 1e3:>10.2f} "
                      f"{float(r['MinNs']) / 1e3:>10.2f} {float(r['MaxNs']) / 1e3:>10.2f} "
                      f"{float(r['Percentage']):>6.2f}")
-    with open(STATS_FILE, "w") as f:
+    with open(stats_file, "w") as f:
         f.write("\n".join(lines) + "\n")
 
     def per_kernel(sub, counter):
@@ -130,7 +152,7 @@ def summarize_profiles(raw_dir: str) -> int:
     # by the profiled run into its log next to the raw output).
     shas = set()
     algo = set()
-    for sub in ("prof_fetch", "prof_write"):
+    for sub in (f"prof{tag}_fetch", f"prof{tag}_write"):
         with open(os.path.join(raw_dir, sub + ".log")) as f:
             for line in f:
                 if line.startswith("{") and "decode_source_sha256" in line:
@@ -140,15 +162,15 @@ def summarize_profiles(raw_dir: str) -> int:
     if len(shas) != 1:
         raise SystemExit(f"profiled runs disagree on the kernel source: {shas}")
     profiled_sha = shas.pop()
-    fetch = per_kernel("prof_fetch", "FETCH_SIZE")
-    write = per_kernel("prof_write", "WRITE_SIZE")
+    fetch = per_kernel(f"prof{tag}_fetch", "FETCH_SIZE")
+    write = per_kernel(f"prof{tag}_write", "WRITE_SIZE")
     cal_kib = CALIBRATION_BYTES / 1024
     f_fac = cal_kib / fetch["stream_copy_kernel"]
     w_fac = cal_kib / write["stream_copy_kernel"]
     dec = next(k for k in fetch if k.startswith("decode_kernel"))
     traffic = (fetch[dec] * f_fac + write[dec] * w_fac) * 1024
     out = ["# HBM traffic of the decode kernel (rocprofv3 counters, KiB per dispatch)", "",
-           "commands:", "  " + PROFILE_CMDS["fetch"], "  " + PROFILE_CMDS["write"], "",
+           "commands:", "  " + cmds["fetch"], "  " + cmds["write"], "",
            f"calibration: stream_copy_kernel over {CALIBRATION_BYTES} B reads FETCH_SIZE "
            f"{fetch['stream_copy_kernel']:.1f} KiB (factor {f_fac:.4f}) and WRITE_SIZE "
            f"{write['stream_copy_kernel']:.1f} KiB (factor {w_fac:.4f})", ""]
@@ -161,33 +183,35 @@ def summarize_profiles(raw_dir: str) -> int:
             f"algorithmic_kv_bytes_per_launch = {max(algo)}",
             f"traffic_over_algorithmic = {traffic / max(algo):.4f}",
             f"decode_source_sha256 = {profiled_sha}"]
-    with open(TRAFFIC_FILE, "w") as f:
+    with open(traffic_file, "w") as f:
         f.write("\n".join(out) + "\n")
-    print(STATS_FILE)
-    print(TRAFFIC_FILE)
+    print(stats_file)
+    print(traffic_file)
 
     # Occupancy and LDS bank conflicts of the decode kernel (two more passes).
-    if os.path.isdir(os.path.join(raw_dir, "prof_occ")) and os.path.isdir(os.path.join(raw_dir, "prof_level")):
-        occ = {c: per_kernel("prof_occ", c) for c in ("OccupancyPercent", "LdsBankConflict", "SQ_INSTS_LDS",
-                                                      "SQ_WAVES")}
-        occ["MeanOccupancyPerCU"] = per_kernel("prof_level", "MeanOccupancyPerCU")
+    if os.path.isdir(os.path.join(raw_dir, f"prof{tag}_occ")) and os.path.isdir(
+            os.path.join(raw_dir, f"prof{tag}_level")):
+        occ = {c: per_kernel(f"prof{tag}_occ", c) for c in ("OccupancyPercent", "LdsBankConflict", "SQ_INSTS_LDS",
+                                                            "SQ_WAVES")}
+        occ["MeanOccupancyPerCU"] = per_kernel(f"prof{tag}_level", "MeanOccupancyPerCU")
         lines = ["# Occupancy and LDS bank conflicts (rocprofv3 derived counters, mean per dispatch)", "",
-                 "commands:", "  " + PROFILE_CMDS["occupancy"], "  " + PROFILE_CMDS["occupancy_level"], "",
+                 "commands:", "  " + cmds["occupancy"], "  " + cmds["occupancy_level"], "",
                  "OccupancyPercent: resident wave-cycles as a percentage of the CU wave slots over the",
                  "dispatch; MeanOccupancyPerCU: mean resident waves per CU; LdsBankConflict: bank",
                  "conflict cycles per LDS access cycle.", ""]
         for k in sorted(occ["OccupancyPercent"]):
             lines.append(f"{k:<58} " + "  ".join(f"{c} {occ[c].get(k, float('nan')):.4g}" for c in occ))
-        with open(OCC_FILE, "w") as f:
+        with open(occ_file, "w") as f:
             f.write("\n".join(lines) + "\n")
-        print(OCC_FILE)
+        print(occ_file)
     return 0
 
 
-def recorded_traffic():
+def recorded_traffic(workload: str = "opt13b"):
     """HBM bytes per decode launch from profiles/, or None if missing or stale."""
     try:
-        kv = dict(line.split(" = ", 1) for line in open(TRAFFIC_FILE).read().splitlines() if " = " in line)
+        kv = dict(line.split(" = ", 1) for line in open(profile_files(workload)[1]).read().splitlines()
+                  if " = " in line)
     except OSError:
         return None
     if kv.get("decode_source_sha256", "").strip() != _sha256(DECODE_SOURCE):
@@ -305,7 +329,7 @@ def main():
         cpu_baseline_child(args.cpu_seconds, args.cpu_workers)
         return 0
     if args.summarize_profiles:
-        return summarize_profiles(args.summarize_profiles)
+        return summarize_profiles(args.summarize_profiles, args.workload)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (pass --gpus 1)",
               file=sys.stderr)
@@ -422,7 +446,7 @@ def main():
         "kv_bytes_per_decode": int(bytes_avg),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": recorded_traffic() if args.workload == "opt13b" else None},
+                     "traffic": recorded_traffic(args.workload)},
         "device_error_bits": dev_err,
     }
 
