@@ -14,11 +14,13 @@
 // code path serves all block sizes; unit u of a sequence lives in table entry
 // u / (B / 16), slice u % (B / 16) of that tile.
 //
-// Work decomposition. One workgroup (4 waves) per (sequence, head, partition).
-// A partition is a run of whole blocks; in single-pass mode it covers the
-// whole context. Inside the workgroup each wave owns whole units (unit j of
-// the partition goes to wave j % 4) and keeps its own online-softmax state,
-// so the hot loop has no barriers.
+// Work decomposition. A partition is a run of whole blocks; in single-pass
+// mode it covers the whole context. A workgroup (4 waves) takes one
+// (sequence, head) and one or more consecutive partitions of it; its waves
+// own whole units (unit j goes to wave j % 4), so the 4 waves read adjacent
+// units, and each keeps its own online-softmax state: the hot loop has no
+// barriers. Short split partitions with few per sequence go a wave each
+// instead (a workgroup covers 4 of them).
 //
 // Tile mapping. A wave reads one 16-row unit with NLD 16-byte loads per lane;
 // load i of lane l covers bytes [i*1024 + 16*l, +16) of the unit, so every
@@ -31,9 +33,11 @@
 // rows, summed over the CPT lanes of the row with DPP row operations (no LDS);
 // then an fp32 online-softmax update on the lane's own rows in base 2
 // (logits pre-multiplied by log2 e), and acc[e] += p * v for its slice. Lanes
-// of different row groups are independent softmax streams until the epilogue,
-// which merges all (wave, row-group) streams of the workgroup through LDS with
-// the log-sum-exp identity.
+// of different row groups are independent softmax streams until a partition
+// ends for the wave: its streams then meet across lanes (log-sum-exp
+// identity) and the wave parks the partition's partial in LDS; the last wave
+// of the workgroup to finish (an LDS counter, no barrier) merges the parked
+// partials of every partition and writes them.
 //
 // Masking: only the last unit of a sequence can be partial. Rows at t >= ctx
 // get logit -inf and their raw K/V registers are zeroed before use, so stale
@@ -74,7 +78,7 @@
 namespace pa {
 namespace {
 
-// Waves per workgroup: each owns every kWaves-th block of the partition.
+// Waves per workgroup: each owns every kWaves-th unit of the workgroup's range.
 #ifndef PA_DECODE_WAVES
 #define PA_DECODE_WAVES 4
 #endif
@@ -304,9 +308,9 @@ __device__ __forceinline__ QT to_out(float x) {
 // kWavePart: each wave owns one whole partition (a workgroup covers kWaves
 // consecutive partitions of one (sequence, head)). Otherwise the kWaves waves
 // share each partition, taking every kWaves-th unit, and a workgroup streams
-// p.parts_per_group consecutive partitions, handing over each one's (m, l, o)
-// when its last units are done while the next partition's loads are already
-// in flight.
+// p.parts_per_group consecutive partitions; a wave parks its share of a
+// partition's (m, l, o) when its last unit of the partition is done, with the
+// next partition's loads already in flight.
 // kCached: temporal tile loads (blocks shared within the batch).
 template <typename KV, typename QT, int D, bool kPaged, typename NEW, bool kMixed = false, bool kWavePart = false,
           bool kCached = false>
@@ -422,8 +426,9 @@ void decode_kernel(Params p, const int32_t* __restrict__ tables, const int32_t* 
   const int iters = first < unit_end ? (unit_end - first + ustride - 1) / ustride : 0;
 
   // Table entry of the wave's k-th unit. Reads are wave-uniform and the loop
-  // stores nothing, so they go through the scalar cache and are counted apart
-  // from the vector loads: each is issued half an iteration before it is used.
+  // stores nothing to global memory, so they go through the scalar cache and
+  // are counted apart from the vector loads: each is issued half an iteration
+  // before it is used.
   auto entry = [&](int k) -> int {
     if constexpr (kPaged) {
       return trow[(first + ustride * k) >> ushift];
