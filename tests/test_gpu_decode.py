@@ -320,6 +320,32 @@ def test_contiguous_twin_matches_the_oracle():
         assert_close(out.cpu().numpy(), ref, F16_ATOL, F16_RTOL, f"contiguous ptok={ptok}")
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_contiguous_twin_many_partitions(D):
+    # Enough (sequence, head) pairs and partitions that a workgroup streams
+    # several 64-token partitions of the contiguous cache; ragged contexts.
+    pk = _pk()
+    ctx = [2048, 1, 700, 1999, 64, 1024, 2047, 333]
+    H, T = 32, 2048
+    S = len(ctx)
+    print(f"contiguous many partitions D={D}", flush=True)
+    K = W.normal_np((S, H, T, D), 71, 1, dtype=np.float16)
+    V = W.normal_np((S, H, T, D), 71, 2, dtype=np.float16)
+    q = W.normal_np((S, H, D), 71, 3, dtype=np.float16)
+    ref = np.stack([OA.attend(q[s], K[s, :, :c].transpose(1, 0, 2), V[s, :, :c].transpose(1, 0, 2),
+                              1 / math.sqrt(D)) for s, c in enumerate(ctx)])
+    kd, vd, qd = (torch.from_numpy(x).to(DEV) for x in (K, V, q))
+    ctxd = torch.tensor(ctx, dtype=torch.int32, device=DEV)
+    for ptok in (64, 128):
+        out = torch.empty_like(qd)
+        nb = pk.contiguous_workspace_bytes(S, H, D, T, ptok)
+        ws = torch.full((nb // 4,), float("nan"), dtype=torch.float32, device=DEV)
+        pk.pa_decode_contiguous(kd, vd, qd, out, ctxd, partition_tokens=ptok, workspace=ws)
+        torch.cuda.synchronize()
+        assert pk.pa_check_errors() == 0
+        assert_close(out.cpu().numpy(), ref, F16_ATOL, F16_RTOL, f"contiguous D={D} ptok={ptok}")
+
+
 def test_schedule_does_not_change_results():
     # pa_decode_ordered only changes the dispatch order: every (sequence,
     # head) reduces in the same order, so outputs are bit-identical.
