@@ -441,8 +441,11 @@ def main():
         "host_us_first_steps": [round(x * 1e6, 1) for x in host_each[:5]],
         "host_us_max": round(max(host_each) * 1e6, 1),
         "host_us_argmax": int(np.argmax(host_each)),
+        "decode_kernel_us_median": round(float(np.median(dec_ms)) * 1e3, 2),
         "decode_kernel_us_p10_p90": [round(float(np.percentile(dec_ms, 10)) * 1e3, 2),
                                      round(float(np.percentile(dec_ms, 90)) * 1e3, 2)],
+        # Sequences decoded per second by the decode launch(es) alone (one layer).
+        "decode_only_seqs_per_s": round(S / dec_avg_s, 1),
         "kv_bytes_per_decode": int(bytes_avg),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
