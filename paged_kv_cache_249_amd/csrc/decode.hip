@@ -658,58 +658,21 @@ void decode_kernel(Params p, const int32_t* __restrict__ tables, const int32_t* 
     }
   };
 
-  // Two register buffers in turn. Inside the loop the next tile's loads are
-  // always issued before the current tile is used, so every wait leaves one
-  // tile in flight; the last one or two tiles are peeled off so that no load
-  // is issued that nothing consumes.
-  // Double buffering holds 4 * NLD 16-byte registers of tiles per lane; with
-  // 8 loads per unit (fp32 rows of 128) that would spill, and 8 loads per
-  // lane already keep enough bytes in flight, so those run single-buffered.
-  constexpr bool kDouble = PA_DECODE_PREFETCH != 0 && NLD <= 4;
-  if (!kDouble) {
-    convert_new_row();
-    int e = e0;
-    for (int k = 0; k < iters; ++k) {
-      const int e_next = k + 1 < iters ? (k == 0 ? e1 : entry(k + 1)) : 0;   // consumed next iteration
-      uint4 ka[NLD], va[NLD];
-      const TileRef ta = fetch(k, e, ka, va);
-      process(ta, ka, va);
-      e = e_next;
-    }
-  } else if (iters > 0) {
-    uint4 ka[NLD], va[NLD], kb[NLD], vb[NLD];
-    const int last = iters - 1;
-    int e_next = last >= 1 ? e1 : e0;
-    TileRef ta = fetch(0, e0, ka, va);
-    convert_new_row();
-    int k = 0;
-    for (; k + 2 < iters; k += 2) {
-      const int e1 = e_next;
-      const int e2 = entry(k + 2);
-      const TileRef tb = fetch(k + 1, e1, kb, vb);
-      process(ta, ka, va);
-      e_next = entry(min(k + 3, last));
-      ta = fetch(k + 2, e2, ka, va);
-      process(tb, kb, vb);
-    }
-    if (k + 1 < iters) {
-      const TileRef tb = fetch(k + 1, e_next, kb, vb);
-      process(ta, ka, va);
-      process(tb, kb, vb);
-    } else {
-      process(ta, ka, va);
-    }
-  }
-
-  // Mixed pages: the hot unit, by the wave that owns it.
-  if constexpr (kMixed) {
-    const int hu = nunits - 1;
-    if (nunits > 0 && hu >= first && hu < unit_begin + p.partition_units && (hu - first) % ustride == 0) {
-      constexpr int kHW = EPC * 2 / 16;   // 16-byte words of fp16 per lane and row
-      const bool ok = unsigned(hot_blk) < unsigned(p.num_hot);
-      bad_entry |= !ok;
-      const int64_t tile = (int64_t(ok ? hot_blk : 0) * p.num_heads + h) * kTileRows * D * 2;
-      uint4 hk[NLD][kHW], hv[NLD][kHW];
+  // Mixed pages: the hot unit (the sequence's last, fp16, from its hot
+  // block), by the wave that owns it. Its loads go out before the wave's
+  // first tile's, and it is folded in while that tile is in flight, so the
+  // hot block costs no round trip of its own.
+  constexpr int kHW = kMixed ? EPC * 2 / 16 : 1;   // 16-byte words of fp16 per lane and row
+  const int hu = nunits - 1;
+  const bool hot_mine = kMixed && nunits > 0 && hu >= first && hu < unit_begin + p.partition_units &&
+                        (hu - first) % ustride == 0;
+  uint4 hk[NLD][kHW], hv[NLD][kHW];
+  bool hot_ok = false;
+  auto hot_load = [&]() {
+    if constexpr (kMixed) {
+      hot_ok = unsigned(hot_blk) < unsigned(p.num_hot);
+      bad_entry |= !hot_ok;
+      const int64_t tile = (int64_t(hot_ok ? hot_blk : 0) * p.num_heads + h) * kTileRows * D * 2;
 #pragma unroll
       for (int i = 0; i < NLD; ++i) {
         const int64_t off = tile + int64_t(i * TPI + grp) * D * 2 + col * EPC * 2;
@@ -719,6 +682,10 @@ void decode_kernel(Params p, const int32_t* __restrict__ tables, const int32_t* 
           hv[i][j] = *reinterpret_cast<const uint4*>(p.hot_v + off + 16 * j);
         }
       }
+    }
+  };
+  auto hot_process = [&]() {
+    if constexpr (kMixed) {
       const int t0 = hu * kTileRows;
       float sc[NLD];
 #pragma unroll
@@ -734,7 +701,7 @@ void decode_kernel(Params p, const int32_t* __restrict__ tables, const int32_t* 
           }
         }
         sc[i] = group_sum<CPT>(d) * p.scale_log2;
-        if (!ok || t0 + i * TPI + grp >= ctx) {
+        if (!hot_ok || t0 + i * TPI + grp >= ctx) {
           sc[i] = -INFINITY;
 #pragma unroll
           for (int j = 0; j < kHW; ++j) hv[i][j] = make_uint4(0u, 0u, 0u, 0u);
@@ -763,6 +730,63 @@ void decode_kernel(Params p, const int32_t* __restrict__ tables, const int32_t* 
         }
       }
       m = mn;
+    }
+  };
+
+  // Two register buffers in turn. Inside the loop the next tile's loads are
+  // always issued before the current tile is used, so every wait leaves one
+  // tile in flight; the last one or two tiles are peeled off so that no load
+  // is issued that nothing consumes.
+  // Double buffering holds 4 * NLD 16-byte registers of tiles per lane; with
+  // 8 loads per unit (fp32 rows of 128) that would spill, and 8 loads per
+  // lane already keep enough bytes in flight, so those run single-buffered.
+  constexpr bool kDouble = PA_DECODE_PREFETCH != 0 && NLD <= 4;
+  if (!kDouble) {
+    convert_new_row();
+    int e = e0;
+    for (int k = 0; k < iters; ++k) {
+      const int e_next = k + 1 < iters ? (k == 0 ? e1 : entry(k + 1)) : 0;   // consumed next iteration
+      uint4 ka[NLD], va[NLD];
+      const TileRef ta = fetch(k, e, ka, va);
+      process(ta, ka, va);
+      e = e_next;
+    }
+  } else if (iters > 0) {
+    uint4 ka[NLD], va[NLD], kb[NLD], vb[NLD];
+    const int last = iters - 1;
+    int e_next = last >= 1 ? e1 : e0;
+    if constexpr (kMixed) {
+      if (hot_mine) hot_load();
+    }
+    TileRef ta = fetch(0, e0, ka, va);
+    if constexpr (kMixed) {
+      if (hot_mine) hot_process();
+    }
+    convert_new_row();
+    int k = 0;
+    for (; k + 2 < iters; k += 2) {
+      const int e1 = e_next;
+      const int e2 = entry(k + 2);
+      const TileRef tb = fetch(k + 1, e1, kb, vb);
+      process(ta, ka, va);
+      e_next = entry(min(k + 3, last));
+      ta = fetch(k + 2, e2, ka, va);
+      process(tb, kb, vb);
+    }
+    if (k + 1 < iters) {
+      const TileRef tb = fetch(k + 1, e_next, kb, vb);
+      process(ta, ka, va);
+      process(tb, kb, vb);
+    } else {
+      process(ta, ka, va);
+    }
+  }
+
+  // Mixed pages: the hot unit of a wave that had no tile to overlap it with.
+  if constexpr (kMixed) {
+    if (hot_mine && !(kDouble && iters > 0)) {
+      hot_load();
+      hot_process();
     }
   }
 
