@@ -124,10 +124,14 @@ class _Workspace:
     def __init__(self, device):
         self.device, self.buf, self.bytes = device, None, 0
 
-    def get(self, need: int):
+    def get(self, need: int, stream):
         if need > self.bytes:
             self.bytes = max(need, int(self.bytes * 1.5))
             self.buf = torch.empty(self.bytes // 4 + 1, dtype=torch.float32, device=self.device)
+        # Steps may run on different streams: the caching allocator must not
+        # hand this memory out again (once it is replaced) before the last
+        # kernel that uses it, on whichever stream, is done.
+        self.buf.record_stream(stream)
         return self.buf
 
 
@@ -249,8 +253,8 @@ class PagedDecodeEngine:
             raise err
         return pairs
 
-    def _workspace_for(self, n: int, max_ctx: int, ptok: int):
-        return self._ws.get(N.pa_decode_workspace_bytes(self.pool, n, max_ctx, ptok))
+    def _workspace_for(self, n: int, max_ctx: int, ptok: int, stream):
+        return self._ws.get(N.pa_decode_workspace_bytes(self.pool, n, max_ctx, ptok), stream)
 
     # -- the step ---------------------------------------------------------------
     def step(self, seqs, k_new, v_new, q, out, *, decode: bool = True, stream=None,
@@ -292,7 +296,7 @@ class PagedDecodeEngine:
                 N.pa_write_kv(self.pool, k_new, v_new, dv["slots"][:n], stream=cur)
             if decode:
                 ptok = self.partition_tokens
-                ws = self._workspace_for(n, max_ctx, ptok) if ptok else None
+                ws = self._workspace_for(n, max_ctx, ptok, cur) if ptok else None
                 order = dv["order"][:n] if self.longest_first else None
                 if decode_events is not None:
                     decode_events[0].record(cur)
@@ -414,7 +418,7 @@ class MixedDecodeEngine:
             N.pa_write_kv(self.hot, k_new, v_new, dv["slots"][:n], stream=cur)
             if decode:
                 ptok = self.partition_tokens
-                ws = self._ws.get(N.pa_decode_workspace_bytes(self.cold, n, max_ctx, ptok)) if ptok else None
+                ws = self._ws.get(N.pa_decode_workspace_bytes(self.cold, n, max_ctx, ptok), cur) if ptok else None
                 if decode_events is not None:
                     decode_events[0].record(cur)
                 N.pa_decode_mixed(self.cold, self.hot, q, out, dv["tables"][:n], dv["hot"][:n], dv["ctx"][:n],
