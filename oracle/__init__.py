@@ -8,7 +8,7 @@ the product path: the two share no code. The only module both sides use is
 
 Everything here is plain, slow and meant to be checked by eye against the pages
 it cites. Floating-point results are computed in float64 (numpy); integer and
-byte results (slots, tables, block copies, int8 codes) are exact.
+byte results (slots, tables, block copies, int8 and int4 codes) are exact.
 
 Sources, cited by page title and section:
 
@@ -23,7 +23,7 @@ Sources, cited by page title and section:
 * "KV Cache与长上下文管理" (staroceans.org): the section on the second problem
   paging solves (round-robin sliding window in O(1): invalidate the oldest
   page, write the new token into it, update the page-table order), the third
-  (fragmentation), and the quantisation list (FP16 -> INT8).
+  (fragmentation), and the quantisation list (FP16 -> INT8 -> INT4).
 * "PagedAttention的终极用途" (staroceans.org video script), part 三: the same
   sliding-window-by-table-edit statement.
 * "PagedAttention 的技术溯源与演进脉络" (mjmagnets.cn), §4.1 item 2: mixed-
@@ -36,7 +36,8 @@ Modules:
 * :mod:`oracle.attention` — softmax(q K^T / sqrt(d)) V in fp64, partition
   partials (m, l, o) and their log-sum-exp merge.
 * :mod:`oracle.cache_ops` — scatter of new K/V rows into slots, block copy, and
-  the int8 quantise-on-write rule.
+  the int8 and int4 quantise-on-write rule (int4 codes and their nibble
+  layout).
 * :mod:`oracle.block_manager` — free list, reference counts, copy-on-write on
   append, the sliding-window ring, swapping to a host pool and prefix caching,
   as a plain Python model.

@@ -1,4 +1,4 @@
-"""Oracle: writing new K/V rows into slots, copying blocks, int8 quantise-on-write.
+"""Oracle: writing new K/V rows into slots, copying blocks, int8 and int4 quantise-on-write.
 
 Test infrastructure only (see the package docstring).
 
@@ -29,6 +29,14 @@ Pool layout used throughout: ``pool[block][head][offset][dim]``; a slot is
   IEEE fp32 divide). New rows: ``q = clamp(rne(x / s), -127, 127)`` in fp32, or
   0 when ``s == 0``. The stored scale becomes ``s``.
   Parity unpinned beyond this definition: the pages fix no int8 scheme.
+* :func:`write_kv_int4` — the same page's quantisation list goes on from INT8
+  to INT4 (section 二.3 names both; the summary list runs FP16 -> INT8 ->
+  INT4). Same group rule with codes in [-7, 7] and ``s_new = fp16(a / 7)``.
+  The codes are kept here as plain integers ``[block][head][offset][dim]``;
+  :func:`pack_int4` gives the stored bytes: two codes per byte, dim 2j in the
+  low nibble and dim 2j+1 in the high one, each nibble holding ``code + 8``
+  (1..15; a nibble never written is 0). This layout is this project's.
+  Parity unpinned beyond this definition: the pages fix no int4 scheme.
 """
 
 from __future__ import annotations
@@ -81,11 +89,12 @@ def swap_blocks(device_pools, host_pools, pairs, direction: str) -> None:
 
 
 def _quantise_group(codes: np.ndarray, scales: np.ndarray, b: int, h: int,
-                    offsets: list, rows: list, block_size: int) -> None:
-    """Apply the int8 group rule to one (block, head) of one tensor."""
+                    offsets: list, rows: list, block_size: int, qmax: int = 127) -> None:
+    """Apply the group rule to one (block, head) of one tensor; codes lie in
+    [-qmax, qmax] (127: int8, 7: int4)."""
     x = np.stack([np.asarray(r, dtype=F32) for r in rows])          # [G][D] fp32
     a = np.max(np.abs(x)) if x.size else F32(0)
-    s_new = np.float16(F32(a) / F32(127.0))
+    s_new = np.float16(F32(a) / F32(qmax))
     opened = 0 in offsets
     s_old = F32(0.0) if opened else F32(scales[b, h])
     s = max(F32(s_old), F32(s_new))
@@ -94,18 +103,18 @@ def _quantise_group(codes: np.ndarray, scales: np.ndarray, b: int, h: int,
             if r in offsets:
                 continue
             old = codes[b, h, r, :].astype(F32)
-            codes[b, h, r, :] = np.clip(np.rint((old * s_old) / F32(s)), -127, 127).astype(np.int8)
+            codes[b, h, r, :] = np.clip(np.rint((old * s_old) / F32(s)), -qmax, qmax).astype(np.int8)
     for o, row in zip(offsets, x):
         if s == 0:
             codes[b, h, o, :] = 0
         else:
-            codes[b, h, o, :] = np.clip(np.rint(row / F32(s)), -127, 127).astype(np.int8)
+            codes[b, h, o, :] = np.clip(np.rint(row / F32(s)), -qmax, qmax).astype(np.int8)
     scales[b, h] = np.float16(s)
 
 
 def write_kv_int8(k_codes: np.ndarray, k_scale: np.ndarray, v_codes: np.ndarray,
                   v_scale: np.ndarray, k_new: np.ndarray, v_new: np.ndarray,
-                  slot_mapping, block_size: int = 16) -> None:
+                  slot_mapping, block_size: int = 16, qmax: int = 127) -> None:
     """Quantise-on-write into int8 pools with per-(block, head) fp16 scales."""
     groups: "OrderedDict[int, list]" = OrderedDict()
     for i, sl in enumerate(np.asarray(slot_mapping, dtype=np.int64)):
@@ -117,9 +126,37 @@ def write_kv_int8(k_codes: np.ndarray, k_scale: np.ndarray, v_codes: np.ndarray,
         offsets = [o for o, _ in members]
         for h in range(H):
             _quantise_group(k_codes, k_scale, b, h, offsets,
-                            [k_new[i][h] for _, i in members], block_size)
+                            [k_new[i][h] for _, i in members], block_size, qmax)
             _quantise_group(v_codes, v_scale, b, h, offsets,
-                            [v_new[i][h] for _, i in members], block_size)
+                            [v_new[i][h] for _, i in members], block_size, qmax)
+
+
+def write_kv_int4(k_codes: np.ndarray, k_scale: np.ndarray, v_codes: np.ndarray,
+                  v_scale: np.ndarray, k_new: np.ndarray, v_new: np.ndarray,
+                  slot_mapping, block_size: int = 16) -> None:
+    """Quantise-on-write into int4 pools (codes in [-7, 7], kept unpacked as
+    int8 ``[block][head][offset][dim]``) with per-(block, head) fp16 scales."""
+    write_kv_int8(k_codes, k_scale, v_codes, v_scale, k_new, v_new, slot_mapping, block_size, qmax=7)
+
+
+def pack_int4(codes: np.ndarray) -> np.ndarray:
+    """Stored bytes of int4 codes ``[..., D]`` (D even): byte j of a row holds
+    ``code[2j] + 8`` in its low nibble and ``code[2j+1] + 8`` in its high one."""
+    c = np.asarray(codes, dtype=np.int16)
+    if np.any(np.abs(c) > 7):
+        raise ValueError("int4 codes lie in [-7, 7]")
+    n = (c + 8).astype(np.uint8)
+    return (n[..., 0::2] | (n[..., 1::2] << 4)).astype(np.uint8)
+
+
+def unpack_int4(packed: np.ndarray) -> np.ndarray:
+    """Inverse of :func:`pack_int4` for bytes it produced: ``[..., D/2]`` ->
+    int8 codes ``[..., 2 * (D/2)]``. A nibble of 0 (never written) reads -8."""
+    b = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(b.shape[:-1] + (2 * b.shape[-1],), dtype=np.int8)
+    out[..., 0::2] = (b & 0x0F).astype(np.int8) - 8
+    out[..., 1::2] = (b >> 4).astype(np.int8) - 8
+    return out
 
 
 def kv_bytes_per_token(layers: int, hidden: int, bytes_per_value: int) -> int:

@@ -1,4 +1,4 @@
-"""Pins for the oracle's write, copy and int8 quantise-on-write (CPU only)."""
+"""Pins for the oracle's write, copy and int8 / int4 quantise-on-write (CPU only)."""
 
 import math
 
@@ -177,3 +177,85 @@ def test_swap_round_trip_is_a_relabelling():
     assert np.array_equal(before, after)
     with pytest.raises(ValueError):
         C.swap_blocks([kp], [hk], [(0, 0)], "sideways")
+
+
+# ---------------------------------------------------------------------------
+# int4: the int8 group rule with codes in [-7, 7], and the nibble layout.
+
+def test_int4_hand_worked_codes():
+    # max |x| = 7 -> scale = 7/7 = 1 exactly; codes are x rounded to nearest
+    # even and clamped to [-7, 7]. A divisor of 8 (or of 127) would change them.
+    x = np.array([7.0, -3.5, 0.5, 1.5, 2.5, -2.5, 6.4, -7.0], np.float32)
+    kc, ks, vc, vs = _int8_pools(D=8)
+    C.write_kv_int4(kc, ks, vc, vs, x[None, None], x[None, None], [16])
+    assert float(ks[1, 0]) == 1.0
+    assert kc[1, 0, 0].tolist() == [7, -4, 0, 2, 2, -2, 6, -7]
+
+
+def test_int4_requantise_when_the_scale_grows():
+    # Row 0 opens the block with max 0.7 -> s_old = fp16(0.1) = 0.0999755859375.
+    # Row 1 brings max 1.4 -> s_new = fp16(0.2) = 2 * s_old exactly, so old
+    # codes are re-coded as rne(q / 2): 7 -> 4, 1 -> 0, 3 -> 2, -5 -> -2.
+    kc, ks, vc, vs = _int8_pools(D=4)
+    row0 = np.array([0.7, 0.1, 0.3, -0.5], np.float32)
+    C.write_kv_int4(kc, ks, vc, vs, row0[None, None], row0[None, None], [0])
+    assert float(ks[0, 0]) == 0.0999755859375
+    assert kc[0, 0, 0].tolist() == [7, 1, 3, -5]
+    row1 = np.array([1.4, 0.0, 0.0, -0.3], np.float32)
+    C.write_kv_int4(kc, ks, vc, vs, row1[None, None], row1[None, None], [1])
+    assert float(ks[0, 0]) == 0.199951171875
+    assert kc[0, 0, 0].tolist() == [4, 0, 2, -2]
+    assert kc[0, 0, 1].tolist() == [7, 0, 0, -2]
+
+
+def test_int4_round_trip_bound():
+    rng = W.rng(25, 0)
+    D = 128
+    x = rng.standard_normal((16, 1, D)).astype(np.float32)
+    kc, ks, vc, vs = _int8_pools(NB=2, D=D)
+    C.write_kv_int4(kc, ks, vc, vs, x, x, np.arange(16) + 16)
+    s = float(ks[1, 0])
+    assert s == float(np.float16(np.float32(np.abs(x).max()) / np.float32(7)))
+    assert np.abs(kc[1, 0]).max() <= 7
+    err = np.abs(kc[1, 0].astype(np.float64) * s - x[:, 0].astype(np.float64))
+    bound = s / 2 + np.maximum(0.0, np.abs(x[:, 0]) - 7 * s) + 1e-12
+    assert np.all(err <= bound)
+
+
+def test_int4_nibble_layout():
+    # Byte j of a row: code[2j] + 8 in the low nibble, code[2j+1] + 8 in the
+    # high one.
+    codes = np.array([[-7, 7, 0, 1, -1, 3, 5, -6]], np.int8)
+    packed = C.pack_int4(codes)
+    assert packed.dtype == np.uint8 and packed.tolist() == [[0xF1, 0x98, 0xB7, 0x2D]]
+    assert np.array_equal(C.unpack_int4(packed), codes)
+    allc = np.arange(-7, 8, dtype=np.int8)
+    grid = np.stack(np.meshgrid(allc, allc, indexing="ij"), -1).reshape(-1, 2)
+    assert np.array_equal(C.unpack_int4(C.pack_int4(grid)), grid)
+    assert C.unpack_int4(np.zeros((1, 2), np.uint8)).tolist() == [[-8, -8, -8, -8]]
+    with pytest.raises(ValueError):
+        C.pack_int4(np.array([[8, 0]], np.int8))
+
+
+def test_int4_exactly_representable_rows_decode_exactly():
+    # Rows k/7 * 2^-3 with integer k in [-7, 7] and one +-7 per (block, head)
+    # in every written group: the scale is exactly 2^-3 and every code exact,
+    # so attention over the int4 codes equals fp64 attention over the rows.
+    rng = W.rng(26, 0)
+    T, H, D = 70, 2, 8
+    NB = -(-T // 16)
+    K = (rng.integers(-7, 8, size=(T, H, D)) / 8.0).astype(np.float32)
+    V = (rng.integers(-7, 8, size=(T, H, D)) / 8.0).astype(np.float32)
+    K[:, :, 0] = 7 / 8
+    V[:, :, 1] = -7 / 8
+    kc = np.zeros((NB, H, 16, D), np.int8)
+    vc = np.zeros_like(kc)
+    ks = np.zeros((NB, H), np.float16)
+    vs = np.zeros_like(ks)
+    table = W.free_order(26, NB)
+    for t in range(T):
+        C.write_kv_int4(kc, ks, vc, vs, K[t:t + 1], V[t:t + 1], [P.slot(t, table)])
+    assert np.all(ks[table] == np.float16(1 / 8)) and np.all(vs[table] == np.float16(1 / 8))
+    q = rng.standard_normal((1, H, D))
+    got = A.paged_decode(q, kc, vc, [table], [T], k_scale=ks, v_scale=vs)[0]
+    np.testing.assert_array_equal(got, A.attend(q[0], K, V, A.default_scale(D)))
