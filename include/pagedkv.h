@@ -28,7 +28,8 @@
  *   error word is set; pa_check_errors() reads and clears it.
  * - Layouts (all row-major, element type given by the pool dtype):
  *     K, V pools    [num_blocks][num_heads][block_size][head_dim]
- *     int8 scales   [num_blocks][num_heads] fp16 (one per block and head)
+ *                   (PA_I4: [...][head_dim / 2] bytes, two codes per byte)
+ *     int8/int4 scales [num_blocks][num_heads] fp16 (one per block and head)
  *     q, out        [num_seqs][num_heads][head_dim]
  *     new K, V rows [n][num_heads][head_dim]
  *     block tables  int32 [num_seqs][max_blocks], logical order
@@ -67,7 +68,11 @@ enum {
   PA_ERR_HIP = -6            /* a HIP runtime call failed                      */
 };
 
-typedef enum { PA_F32 = 0, PA_F16 = 1, PA_I8 = 2 } pa_dtype;
+/* PA_I4: int4 codes in [-7, 7], two per byte: dim 2j of a row in the low
+ * nibble of byte j and dim 2j+1 in the high nibble, each nibble holding
+ * code + 8 (so a row of head_dim values takes head_dim / 2 bytes). Like
+ * PA_I8, one fp16 scale per (block, head) for K and one for V. */
+typedef enum { PA_F32 = 0, PA_F16 = 1, PA_I8 = 2, PA_I4 = 3 } pa_dtype;
 
 /* Device error word bits, reported by pa_check_errors(). */
 enum {
@@ -75,7 +80,7 @@ enum {
   PA_DEV_BAD_SLOT = 2,         /* a slot outside the pool                      */
   PA_DEV_BAD_PAIR = 4,         /* a copy pair outside the pool                 */
   PA_DEV_BAD_CONTEXT = 8,      /* context_lens[s] < 0 or > the stated maximum  */
-  PA_DEV_BAD_RUN = 16          /* int8 write: one block hit by more than
+  PA_DEV_BAD_RUN = 16          /* int8/int4 write: one block hit by more than
                                   block_size rows of one run (duplicate slots) */
 };
 
@@ -90,22 +95,23 @@ int32_t pa_version(void);
  *
  * The pool is the shared physical block store of the method ("One Deep
  * Concept #01", §4 Core Innovation: logical KV blocks -> block table ->
- * physical GPU blocks). K and V are separate arrays; int8 pools carry one fp16
- * scale per (block, head) for K and one for V.
+ * physical GPU blocks). K and V are separate arrays; int8 and int4 pools carry
+ * one fp16 scale per (block, head) for K and one for V.
  * ------------------------------------------------------------------------- */
 typedef struct pa_pool pa_pool;
 
 /* Bytes the caller must allocate for one of K or V (*kv_bytes) and for one of
- * the int8 scale arrays (*scale_bytes, 0 unless kv_dtype == PA_I8).
+ * the scale arrays (*scale_bytes, 0 unless kv_dtype is PA_I8 or PA_I4).
  * Errors: PA_ERR_INVALID_ARG (null outputs, non-positive sizes),
- * PA_ERR_UNSUPPORTED (block_size not 16/32/64, head_dim not 64/128). */
+ * PA_ERR_UNSUPPORTED (block_size not 16/32/64, head_dim not 64/128, or PA_I4
+ * with head_dim other than 128). */
 pa_status pa_pool_bytes(int32_t num_blocks, int32_t block_size, int32_t num_heads,
                         int32_t head_dim, pa_dtype kv_dtype, int64_t* kv_bytes,
                         int64_t* scale_bytes);
 
 /* Create a descriptor over caller-owned device buffers. k_cache / v_cache must
  * each hold pa_pool_bytes(...)->kv_bytes and be 16-byte aligned; k_scale /
- * v_scale must be given for PA_I8 and NULL otherwise. The buffers stay owned
+ * v_scale must be given for PA_I8 and PA_I4 and NULL otherwise. The buffers stay owned
  * by the caller and must outlive the descriptor. *out receives the handle.
  * Errors: as pa_pool_bytes, plus PA_ERR_INVALID_ARG for null or misaligned
  * buffers and scales given for a float pool. */
@@ -133,7 +139,9 @@ pa_status pa_free_pool(pa_pool* pool);
  * written by the call are re-coded as clamp(rne(q * s_old / s), -127, 127);
  * new rows are clamp(rne(x / s), -127, 127) (0 if s == 0); the stored scale
  * becomes s. All arithmetic is IEEE fp32 with correctly rounded division.
- * Precondition for int8 pools: the entries of slot_mapping that hit one block
+ * int4 pools (INT4, the next step of the same page's list) follow the same
+ * rule with 7 in place of 127, codes stored as in the PA_I4 layout.
+ * Precondition for int8 and int4 pools: the entries of slot_mapping that hit one block
  * are adjacent (true for decode, one row per sequence, and for a sequence's
  * prefill in token order); otherwise the result for that block is unspecified
  * (never out of bounds).
@@ -148,7 +156,7 @@ pa_status pa_write_kv(pa_pool* pool, const void* k_new, const void* v_new, pa_dt
  *
  * For every pair p < n of pairs ([n][2] device int32, {src, dst}) copies
  * K[src] -> K[dst] and V[src] -> V[dst] over all heads and offsets, plus the
- * two scales of an int8 pool. The unit of the copy is one block, as in
+ * two scales of an int8 or int4 pool. The unit of the copy is one block, as in
  * "PagedAttention — 把 KV cache 当虚拟内存页来管理", 实践案例 / 案例 3. Pairs are
  * independent: no dst may appear twice or also be a src in the same call.
  * n == 0 is a no-op. Errors: PA_ERR_INVALID_ARG, PA_ERR_HIP.
@@ -163,10 +171,10 @@ pa_status pa_copy_blocks(pa_pool* pool, const int32_t* pairs, int32_t n, pa_stre
  * caller-owned pinned host memory (hipHostMalloc, or a pinned tensor) with
  * the pool's per-block layout: host_k / host_v [num_host_blocks][num_heads]
  * [block_size][head_dim] of the pool's dtype, 16-byte aligned; host_k_scale /
- * host_v_scale [num_host_blocks][num_heads] fp16 for int8 pools, NULL
+ * host_v_scale [num_host_blocks][num_heads] fp16 for int8 and int4 pools, NULL
  * otherwise. pairs ([n][2] device int32): PA_SWAP_OUT copies device block
  * pairs[i][0] to host block pairs[i][1]; PA_SWAP_IN copies host block
- * pairs[i][0] to device block pairs[i][1] (K, V and int8 scales). One kernel
+ * pairs[i][0] to device block pairs[i][1] (K, V and the scales). One kernel
  * reads or writes the host pool directly over the host link; no destination
  * may appear twice in one call. An id outside its pool flags
  * PA_DEV_BAD_PAIR and the pair is skipped. The host sees swapped-out data
@@ -183,8 +191,8 @@ pa_status pa_swap_blocks(pa_pool* pool, void* host_k, void* host_v, void* host_k
  * Paged decode attention.
  *
  * For each sequence s and head h, with ctx = context_lens[s] and
- * k_t = K[table[s][t / B]][h][t % B] with B = the pool's block_size (int8:
- * code * scale[block][h]):
+ * k_t = K[table[s][t / B]][h][t % B] with B = the pool's block_size (int8 and
+ * int4: code * scale[block][h]):
  *     out[s][h] = sum_{t < ctx} softmax_t(q[s][h] . k_t * sm_scale) v_t
  * ("One Deep Concept #01", §2 Background: softmax(Q K^T / sqrt(d)) V; the
  * table indirection of "PagedAttention — 把 KV cache 当虚拟内存页来管理",
@@ -250,8 +258,8 @@ pa_status pa_decode_ordered(pa_pool* pool, const void* q, pa_dtype q_dtype, void
  * launch. The pool ends up byte-identical to pa_write_kv's result and out
  * identical to the two calls. A negative slot writes nothing; a slot that is
  * not the newest token's flags PA_DEV_BAD_SLOT and is not written.
- * Errors: PA_ERR_UNSUPPORTED for int8 pools (their quantisation works on
- * whole blocks: use pa_write_kv), otherwise as pa_decode. */
+ * Errors: PA_ERR_UNSUPPORTED for int8 and int4 pools (their quantisation works
+ * on whole blocks: use pa_write_kv), otherwise as pa_decode. */
 pa_status pa_write_decode(pa_pool* pool, const void* k_new, const void* v_new, pa_dtype src_dtype,
                           const int64_t* slot_mapping, const void* q, pa_dtype q_dtype, void* out,
                           const int32_t* block_tables, int32_t max_blocks,

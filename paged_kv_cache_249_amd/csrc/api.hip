@@ -84,8 +84,10 @@ pa_status check_geometry(const char* fn, int32_t num_blocks, int32_t block_size,
   if (!pa::geometry_supported(block_size, head_dim))
     return fail(PA_ERR_UNSUPPORTED, "%s: block_size=%d head_dim=%d (supported: 16/32/64 and 64/128)", fn,
                 block_size, head_dim);
-  if (kv_dtype != PA_F32 && kv_dtype != PA_F16 && kv_dtype != PA_I8)
+  if (kv_dtype != PA_F32 && kv_dtype != PA_F16 && kv_dtype != PA_I8 && kv_dtype != PA_I4)
     return fail(PA_ERR_UNSUPPORTED, "%s: kv dtype %d", fn, int(kv_dtype));
+  if (kv_dtype == PA_I4 && head_dim != 128)
+    return fail(PA_ERR_UNSUPPORTED, "%s: int4 pools need head_dim 128 (got %d)", fn, head_dim);
   return PA_OK;
 }
 
@@ -107,8 +109,8 @@ pa_status pa_pool_bytes(int32_t num_blocks, int32_t block_size, int32_t num_head
   if (!kv_bytes || !scale_bytes) return fail(PA_ERR_INVALID_ARG, "pa_pool_bytes: NULL output");
   pa_status st = check_geometry("pa_pool_bytes", num_blocks, block_size, num_heads, head_dim, kv_dtype);
   if (st != PA_OK) return st;
-  *kv_bytes = int64_t(num_blocks) * num_heads * block_size * head_dim * pa::elem_bytes(kv_dtype);
-  *scale_bytes = kv_dtype == PA_I8 ? int64_t(num_blocks) * num_heads * 2 : 0;
+  *kv_bytes = int64_t(num_blocks) * num_heads * block_size * pa::row_bytes(kv_dtype, head_dim);
+  *scale_bytes = pa::is_quantised(kv_dtype) ? int64_t(num_blocks) * num_heads * 2 : 0;
   return PA_OK;
 }
 
@@ -122,8 +124,8 @@ pa_status pa_alloc_pool(int32_t num_blocks, int32_t block_size, int32_t num_head
   if (!k_cache || !v_cache) return fail(PA_ERR_INVALID_ARG, "pa_alloc_pool: NULL cache buffer");
   if (!aligned16(k_cache) || !aligned16(v_cache))
     return fail(PA_ERR_INVALID_ARG, "pa_alloc_pool: cache buffers must be 16-byte aligned");
-  if (kv_dtype == PA_I8) {
-    if (!k_scale || !v_scale) return fail(PA_ERR_INVALID_ARG, "pa_alloc_pool: int8 pool needs scales");
+  if (pa::is_quantised(kv_dtype)) {
+    if (!k_scale || !v_scale) return fail(PA_ERR_INVALID_ARG, "pa_alloc_pool: int8/int4 pool needs scales");
   } else if (k_scale || v_scale) {
     return fail(PA_ERR_INVALID_ARG, "pa_alloc_pool: scales given for a float pool");
   }
@@ -186,9 +188,10 @@ pa_status pa_swap_blocks(pa_pool* pool, void* host_k, void* host_v, void* host_k
   if (n > 65535) return fail(PA_ERR_INVALID_ARG, "pa_swap_blocks: n=%d > 65535 pairs per call", n);
   if (!host_k || !host_v || !aligned16(host_k) || !aligned16(host_v))
     return fail(PA_ERR_INVALID_ARG, "pa_swap_blocks: host K/V must be non-NULL and 16-byte aligned");
-  const bool i8 = pool->kv_dtype == PA_I8;
-  if (i8 != (host_k_scale != nullptr && host_v_scale != nullptr) || (!i8 && (host_k_scale || host_v_scale)))
-    return fail(PA_ERR_INVALID_ARG, "pa_swap_blocks: host scales are required for int8 pools and only for them");
+  const bool quant = pa::is_quantised(pool->kv_dtype);
+  if (quant != (host_k_scale != nullptr && host_v_scale != nullptr) || (!quant && (host_k_scale || host_v_scale)))
+    return fail(PA_ERR_INVALID_ARG,
+                "pa_swap_blocks: host scales are required for int8 and int4 pools and only for them");
   pa::SwapHost h{};
   hipError_t e = hipSuccess;
   h.num_blocks = num_host_blocks;
@@ -321,8 +324,8 @@ pa_status pa_write_decode(pa_pool* pool, const void* k_new, const void* v_new, p
                           int32_t partition_tokens, void* workspace, int64_t workspace_bytes,
                           pa_stream stream) {
   if (!pool) return fail(PA_ERR_INVALID_ARG, "pa_write_decode: pool is NULL");
-  if (pool->kv_dtype == PA_I8)
-    return fail(PA_ERR_UNSUPPORTED, "pa_write_decode: int8 pools quantise per block; use pa_write_kv");
+  if (pa::is_quantised(pool->kv_dtype))
+    return fail(PA_ERR_UNSUPPORTED, "pa_write_decode: int8 and int4 pools quantise per block; use pa_write_kv");
   if (src_dtype != PA_F32 && src_dtype != PA_F16)
     return fail(PA_ERR_UNSUPPORTED, "pa_write_decode: source dtype %d (F32 or F16)", int(src_dtype));
   if (num_seqs > 0 && (!k_new || !v_new || !slot_mapping))

@@ -11,7 +11,8 @@
 // int8 pools quantise on write with one fp16 scale per (block, head), for K
 // and V separately (FP16 -> INT8 compression is listed in "KV Cache与长上下文管理",
 // section 二.3, without a scheme; the group rule below is this library's and
-// is stated in pagedkv.h). One wave handles one run of adjacent slot entries
+// is stated in pagedkv.h). int4 pools (INT4, the next entry of the same list)
+// use the same rule with codes in [-7, 7], two per byte. One wave handles one run of adjacent slot entries
 // that hit the same block (at most B rows), for one head and one tensor.
 //
 // copy_blocks: whole-block copies, the copy-on-write unit of the study note's
@@ -153,6 +154,94 @@ __global__ __launch_bounds__(kThreads) void write_kv_i8_kernel(
       if (s > 0.f) qf = fminf(fmaxf(__builtin_rintf(ld_f(x + e) / s), -127.f), 127.f);
       tile[o * D + lane * kDPL + e] = int8_t(qf);
     }
+  }
+  if (lane == 0) scale[sidx] = _Float16(s);
+}
+
+// ---------------------------------------------------------------------------
+// int4 pools (head_dim 128): the int8 group rule with codes in [-7, 7]; a
+// row is 64 bytes, byte j holding code[2j] + 8 in its low nibble and
+// code[2j+1] + 8 in its high one, so lane l owns byte l of every row (dims
+// 2l and 2l+1). One wave per (run leader i, head h, tensor), as for int8.
+template <typename SRC>
+__global__ __launch_bounds__(kThreads) void write_kv_i4_kernel(
+    const SRC* __restrict__ k_new, const SRC* __restrict__ v_new, uint8_t* __restrict__ k_pool,
+    uint8_t* __restrict__ v_pool, _Float16* __restrict__ k_scale, _Float16* __restrict__ v_scale,
+    const int64_t* __restrict__ slots, int n, int H, int num_blocks, int bshift, int32_t* err) {
+  constexpr int D = 128;
+  constexpr int kRowBytes = D / 2;   // == kWave: one byte per lane
+  const int bs = 1 << bshift;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t wid = int64_t(blockIdx.x) * (kThreads / kWave) + wave_uniform(threadIdx.x / kWave);
+  if (wid >= int64_t(n) * H) return;
+  const int64_t i = wid / H;
+  const int h = int(wid % H);
+  const int64_t slot = slots[i];
+  if (slot < 0) return;
+  const int64_t blk = slot >> bshift;
+  if (blk >= num_blocks) {
+    if (lane == 0) flag_error(err, PA_DEV_BAD_SLOT);
+    return;
+  }
+  if (i > 0) {
+    const int64_t prev = slots[i - 1];
+    if (prev >= 0 && (prev >> bshift) == blk) return;   // not the first row of its run
+  }
+  const bool is_v = blockIdx.y != 0;
+  const SRC* src = is_v ? v_new : k_new;
+  uint8_t* pool = is_v ? v_pool : k_pool;
+  _Float16* scale = is_v ? v_scale : k_scale;
+
+  // The run: rows i .. i+R-1 hitting block blk.
+  uint64_t mask = 0;
+  int R = 0;
+  bool dup = false;
+  while (R < bs && i + R < n) {
+    const int64_t sl = slots[i + R];
+    if (sl < 0 || (sl >> bshift) != blk) break;
+    const uint64_t bit = uint64_t(1) << int(sl & (bs - 1));
+    dup |= (mask & bit) != 0;
+    mask |= bit;
+    ++R;
+  }
+  if (i + R < n && R == bs) {
+    const int64_t sl = slots[i + R];
+    dup |= sl >= 0 && (sl >> bshift) == blk;
+  }
+  if (dup && lane == 0) flag_error(err, PA_DEV_BAD_RUN);
+
+  float a = 0.f;
+  for (int r = 0; r < R; ++r) {
+    const SRC* x = src + ((i + r) * H + h) * D + 2 * lane;
+    a = fmaxf(a, fmaxf(fabsf(ld_f(x)), fabsf(ld_f(x + 1))));
+  }
+  a = wave_max(a);
+  const float s_new = float(_Float16(a / 7.0f));
+  const int64_t sidx = blk * H + h;
+  const float s_old = (mask & 1u) ? 0.f : float(scale[sidx]);
+  const float s = fmaxf(s_old, s_new);
+  uint8_t* tile = pool + (sidx << bshift) * kRowBytes;
+  auto code = [](float qf) { return uint32_t(int(fminf(fmaxf(qf, -7.f), 7.f)) + 8); };
+
+  if (s_old > 0.f && s > s_old) {
+    for (int o = 0; o < bs; ++o) {
+      if (mask & (uint64_t(1) << o)) continue;
+      uint8_t* c = tile + o * kRowBytes + lane;
+      const uint32_t b = *c;
+      const float lo = __builtin_rintf((float(int(b & 15u) - 8) * s_old) / s);
+      const float hi = __builtin_rintf((float(int(b >> 4) - 8) * s_old) / s);
+      *c = uint8_t(code(lo) | (code(hi) << 4));
+    }
+  }
+  for (int r = 0; r < R; ++r) {
+    const int o = int(slots[i + r] & (bs - 1));
+    const SRC* x = src + ((i + r) * H + h) * D + 2 * lane;
+    float lo = 0.f, hi = 0.f;
+    if (s > 0.f) {
+      lo = __builtin_rintf(ld_f(x) / s);
+      hi = __builtin_rintf(ld_f(x + 1) / s);
+    }
+    tile[o * kRowBytes + lane] = uint8_t(code(lo) | (code(hi) << 4));
   }
   if (lane == 0) scale[sidx] = _Float16(s);
 }
@@ -381,6 +470,19 @@ int launch_write_i8(const pa_pool* p, const void* k_new, const void* v_new, cons
   return int(hipGetLastError());
 }
 
+template <typename SRC>
+int launch_write_i4(const pa_pool* p, const void* k_new, const void* v_new, const int64_t* slots,
+                    int32_t n, hipStream_t st) {
+  const int64_t waves = int64_t(n) * p->num_heads;
+  const dim3 grid(unsigned((waves + (kThreads / kWave) - 1) / (kThreads / kWave)), 2);
+  hipLaunchKernelGGL(write_kv_i4_kernel<SRC>, grid, dim3(kThreads), 0, st, static_cast<const SRC*>(k_new),
+                     static_cast<const SRC*>(v_new), static_cast<uint8_t*>(p->k_cache),
+                     static_cast<uint8_t*>(p->v_cache), static_cast<_Float16*>(p->k_scale),
+                     static_cast<_Float16*>(p->v_scale), slots, n, p->num_heads, p->num_blocks,
+                     block_shift(p->block_size), device_error_ptr());
+  return int(hipGetLastError());
+}
+
 }  // namespace
 
 int launch_write_kv(const pa_pool* p, const void* k_new, const void* v_new, pa_dtype src,
@@ -397,6 +499,9 @@ int launch_write_kv(const pa_pool* p, const void* k_new, const void* v_new, pa_d
     case PA_I8:
       return src == PA_F32 ? launch_write_i8<float>(p, k_new, v_new, slots, n, st)
                            : launch_write_i8<_Float16>(p, k_new, v_new, slots, n, st);
+    case PA_I4:
+      return src == PA_F32 ? launch_write_i4<float>(p, k_new, v_new, slots, n, st)
+                           : launch_write_i4<_Float16>(p, k_new, v_new, slots, n, st);
   }
   return int(hipErrorInvalidValue);
 }
@@ -421,7 +526,7 @@ int launch_demote_blocks(const pa_pool* hot, const pa_pool* cold, const int32_t*
 
 int launch_copy_blocks(const pa_pool* p, const int32_t* pairs, int32_t n, void* stream) {
   if (n == 0) return 0;
-  const int64_t block_bytes = int64_t(p->num_heads) * p->block_size * p->head_dim * elem_bytes(p->kv_dtype);
+  const int64_t block_bytes = int64_t(p->num_heads) * p->block_size * row_bytes(p->kv_dtype, p->head_dim);
   const dim3 grid(unsigned((block_bytes / 16 + kThreads - 1) / kThreads), unsigned(n), 2);
   hipLaunchKernelGGL(copy_blocks_kernel, grid, dim3(kThreads), 0, static_cast<hipStream_t>(stream), pairs,
                      n, static_cast<char*>(p->k_cache), static_cast<char*>(p->v_cache), block_bytes,
@@ -433,7 +538,7 @@ int launch_copy_blocks(const pa_pool* p, const int32_t* pairs, int32_t n, void* 
 int launch_swap_blocks(const pa_pool* p, const SwapHost& h, const int32_t* pairs, int32_t n, bool out_dir,
                        void* stream) {
   if (n == 0) return 0;
-  const int64_t block_bytes = int64_t(p->num_heads) * p->block_size * p->head_dim * elem_bytes(p->kv_dtype);
+  const int64_t block_bytes = int64_t(p->num_heads) * p->block_size * row_bytes(p->kv_dtype, p->head_dim);
   const int64_t words = block_bytes / 8;   // whole 1 KiB wave chunks for every supported geometry
   const dim3 grid(unsigned((words + kSwapWordsPerGroup - 1) / kSwapWordsPerGroup), unsigned(n), 2);
   hipLaunchKernelGGL(swap_blocks_kernel, grid, dim3(kThreads), 0, static_cast<hipStream_t>(stream), pairs,

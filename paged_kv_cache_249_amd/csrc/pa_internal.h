@@ -38,9 +38,14 @@ inline int block_shift(int32_t block_size) {
 pa_status fail(pa_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 void clear_error();
 
-inline int64_t elem_bytes(pa_dtype t) {
-  return t == PA_F32 ? 4 : t == PA_F16 ? 2 : 1;
+// Bytes of one row of head_dim values (int4: two values per byte).
+inline int64_t row_bytes(pa_dtype t, int32_t head_dim) {
+  return t == PA_F32 ? 4 * int64_t(head_dim) : t == PA_F16 ? 2 * int64_t(head_dim)
+                                             : t == PA_I8 ? int64_t(head_dim) : int64_t(head_dim) / 2;
 }
+
+// Pools that store codes with one fp16 scale per (block, head).
+inline bool is_quantised(pa_dtype t) { return t == PA_I8 || t == PA_I4; }
 
 inline bool geometry_supported(int32_t block_size, int32_t head_dim) {
   return block_size_supported(block_size) && (head_dim == 64 || head_dim == 128);

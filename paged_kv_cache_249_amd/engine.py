@@ -156,7 +156,7 @@ class PagedDecodeEngine:
         # every context length, so the schedule costs one argsort per step.
         self.longest_first = longest_first
         # Float pools write the new token inside the decode launch (pa_write_decode).
-        self.fuse_write = fuse_write and kv_dtype != N.PA_I8
+        self.fuse_write = fuse_write and not N.is_quantised(kv_dtype)
         # Everything a step uploads lives in one packed buffer.
         self._stage = _Staging([("slots", torch.int64, ()), ("ctx", torch.int32, ()), ("order", torch.int32, ()),
                                 ("pairs", torch.int32, (2,)), ("tables", torch.int32, (self.cap,))],

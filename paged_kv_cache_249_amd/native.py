@@ -26,7 +26,7 @@ PA_ERR_OUT_OF_RANGE = -4
 PA_ERR_STATE = -5
 PA_ERR_HIP = -6
 
-PA_F32, PA_F16, PA_I8 = 0, 1, 2
+PA_F32, PA_F16, PA_I8, PA_I4 = 0, 1, 2, 3
 
 PA_DEV_BAD_TABLE_ENTRY = 1
 PA_DEV_BAD_SLOT = 2
@@ -140,8 +140,19 @@ def dtype_code(dtype) -> int:
 
 
 def torch_dtype(code: int):
+    """Element type of a pool's K/V tensors (int4: bytes of two codes)."""
     torch = _torch()
-    return {PA_F32: torch.float32, PA_F16: torch.float16, PA_I8: torch.int8}[code]
+    return {PA_F32: torch.float32, PA_F16: torch.float16, PA_I8: torch.int8, PA_I4: torch.uint8}[code]
+
+
+def is_quantised(code: int) -> bool:
+    """Pools that store codes with one fp16 scale per (block, head)."""
+    return code in (PA_I8, PA_I4)
+
+
+def pool_shape(num_blocks: int, num_heads: int, block_size: int, head_dim: int, kv_dtype: int):
+    """Shape of one K/V pool tensor: int4 rows hold head_dim / 2 bytes."""
+    return (num_blocks, num_heads, block_size, head_dim // 2 if kv_dtype == PA_I4 else head_dim)
 
 
 def _ptr(t, name: str, dtype=None, device=True):
@@ -223,13 +234,13 @@ def new_pool(num_blocks: int, num_heads: int, head_dim: int, kv_dtype: int, devi
              block_size: int = BLOCK_SIZE, fill=None) -> Pool:
     """Allocate pool tensors with torch on ``device`` and bind them."""
     torch = _torch()
-    shape = (num_blocks, num_heads, block_size, head_dim)
+    shape = pool_shape(num_blocks, num_heads, block_size, head_dim, kv_dtype)
     dt = torch_dtype(kv_dtype)
     alloc = torch.empty if fill is None else (lambda *a, **k: torch.full(*a, fill_value=fill, **k))
     k = alloc(shape, dtype=dt, device=device)
     v = alloc(shape, dtype=dt, device=device)
     ks = vs = None
-    if kv_dtype == PA_I8:
+    if is_quantised(kv_dtype):
         ks = torch.zeros((num_blocks, num_heads), dtype=torch.float16, device=device)
         vs = torch.zeros((num_blocks, num_heads), dtype=torch.float16, device=device)
     return pa_alloc_pool(num_blocks, block_size, num_heads, head_dim, kv_dtype, k, v, ks, vs)
@@ -266,12 +277,12 @@ class HostPool:
     def __init__(self, pool: Pool, num_blocks: int):
         torch = _torch()
         self.num_blocks = num_blocks
-        shape = (num_blocks, pool.num_heads, pool.block_size, pool.head_dim)
+        shape = pool_shape(num_blocks, pool.num_heads, pool.block_size, pool.head_dim, pool.kv_dtype)
         dt = torch_dtype(pool.kv_dtype)
         self.k = torch.zeros(shape, dtype=dt, pin_memory=True)
         self.v = torch.zeros(shape, dtype=dt, pin_memory=True)
         self.k_scale = self.v_scale = None
-        if pool.kv_dtype == PA_I8:
+        if is_quantised(pool.kv_dtype):
             self.k_scale = torch.zeros((num_blocks, pool.num_heads), dtype=torch.float16, pin_memory=True)
             self.v_scale = torch.zeros((num_blocks, pool.num_heads), dtype=torch.float16, pin_memory=True)
 

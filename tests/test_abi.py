@@ -48,6 +48,32 @@ def test_pool_bytes():
         assert kv == 10 * 32 * bs * 128 and sc == 10 * 32 * 2
 
 
+def test_int4_pool_geometry():
+    # Two codes per byte: a row of 128 values takes 64 bytes; one fp16 scale
+    # per (block, head) as for int8. head_dim 64 is not supported for int4.
+    import paged_kv_cache_249_amd as pk
+    for bs in (16, 32, 64):
+        kv, sc = pk.pa_pool_bytes(10, bs, 32, 128, pk.PA_I4)
+        assert kv == 10 * 32 * bs * 64 and sc == 10 * 32 * 2
+    with pytest.raises(pk.PagedKVError) as e:
+        pk.pa_pool_bytes(10, 16, 32, 64, pk.PA_I4)
+    assert e.value.status == pk.PA_ERR_UNSUPPORTED
+    h = C.c_void_p()
+    assert pk.lib.pa_alloc_pool(8, 16, 2, 128, pk.PA_I4, C.c_void_p(0x1000), C.c_void_p(0x2000),
+                                None, None, C.byref(h)) == pk.PA_ERR_INVALID_ARG
+    assert pk.lib.pa_alloc_pool(8, 16, 2, 128, pk.PA_I4, C.c_void_p(0x1000), C.c_void_p(0x2000),
+                                C.c_void_p(0x3000), C.c_void_p(0x4000), C.byref(h)) == 0
+    p = C.c_void_p
+    # Quantised pools take new rows through pa_write_kv only.
+    assert pk.lib.pa_write_decode(h, p(0x1000), p(0x2000), pk.PA_F16, p(0x3000), p(0x4000), pk.PA_F16,
+                                  p(0x5000), p(0x6000), 8, p(0x7000), None, 0, 1, 16, 0.0, 0, None, 0,
+                                  None) == pk.PA_ERR_UNSUPPORTED
+    # Swapping an int4 pool needs the host scales.
+    assert pk.lib.pa_swap_blocks(h, p(0x10000), p(0x20000), None, None, 4, p(0x8000), 1, pk.PA_SWAP_OUT,
+                                 None) == pk.PA_ERR_INVALID_ARG
+    assert pk.lib.pa_free_pool(h) == 0
+
+
 @pytest.mark.parametrize("args,status", [
     ((0, 16, 8, 64, 1), -1),
     ((4, 16, 0, 64, 1), -1),

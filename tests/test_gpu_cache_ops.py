@@ -1,4 +1,4 @@
-"""GPU parity of the cache kernels: pa_write_kv (float and int8) and
+"""GPU parity of the cache kernels: pa_write_kv (float, int8 and int4) and
 pa_copy_blocks, bit for bit against the oracle, through the C ABI."""
 
 import numpy as np
@@ -26,7 +26,8 @@ def _random_pool(pk, NB, H, D, code, seed, bs=16):
     """Pool tensors filled with random bits (stale data) and their host copies."""
     g = torch.Generator(device="cpu").manual_seed(seed)
     dt = pk.torch_dtype(code)
-    nbytes = NB * H * bs * D * torch.empty(0, dtype=dt).element_size()
+    shape = pk.pool_shape(NB, H, bs, D, code)
+    nbytes = int(np.prod(shape)) * torch.empty(0, dtype=dt).element_size()
     raw_k = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, generator=g)
     raw_v = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, generator=g)
     if code == pk.PA_F16:
@@ -36,10 +37,10 @@ def _random_pool(pk, NB, H, D, code, seed, bs=16):
     if code == pk.PA_F32:
         raw_k.view(torch.int32).bitwise_and_(0x3effffff)
         raw_v.view(torch.int32).bitwise_and_(0x3effffff)
-    k = raw_k.view(dt).view(NB, H, bs, D).to(DEV)
-    v = raw_v.view(dt).view(NB, H, bs, D).to(DEV)
+    k = raw_k.view(dt).view(shape).to(DEV)
+    v = raw_v.view(dt).view(shape).to(DEV)
     ks = vs = None
-    if code == pk.PA_I8:
+    if pk.is_quantised(code):
         ks = (torch.rand((NB, H), generator=g) * 0.05).to(torch.float16).to(DEV)
         vs = (torch.rand((NB, H), generator=g) * 0.05).to(torch.float16).to(DEV)
     pool = pk.pa_alloc_pool(NB, bs, H, D, code, k, v, ks, vs)
@@ -116,11 +117,53 @@ def test_write_kv_int8_bit_exact(D, src_dtype, bs):
     assert pk.pa_check_errors() == 0
 
 
+@pytest.mark.parametrize("src_dtype,bs", [(torch.float32, 16), (torch.float16, 16), (torch.float16, 32),
+                                          (torch.float32, 64)])
+def test_write_kv_int4_bit_exact(src_dtype, bs):
+    # The int8 sequence of calls on an int4 pool. The pool starts as random
+    # bytes (stale nibbles read as codes -8..7); codes and scales must match
+    # the oracle's exactly after every kind of call (prefill, partial blocks,
+    # growing scales that re-code rows already in a block).
+    pk = _pk()
+    D, NB, H = 128, 24, 3
+    pool, (hkb, hvb, hks, hvs) = _random_pool(pk, NB, H, D, pk.PA_I4, 9, bs)
+    hk, hv = OC.unpack_int4(hkb), OC.unpack_int4(hvb)
+    rng = W.rng(9, 5)
+    order = rng.permutation(NB)
+    seqs = [(order[0:4], 50 * bs // 16), (order[4:8], bs), (order[8:12], 7)]
+    lens, calls = [], []
+    for table, plen in seqs:
+        calls.append(np.array([table[t // bs] * bs + t % bs for t in range(plen)], np.int64))
+        lens.append(plen)
+    for step in range(12):
+        calls.append(np.array([tb[lens[i] // bs] * bs + lens[i] % bs for i, (tb, _) in enumerate(seqs)],
+                              np.int64))
+        lens = [x + 1 for x in lens]
+    for ci, slots in enumerate(calls):
+        n = slots.size
+        amp = 1.0 + (3.0 if ci % 4 == 3 else 0.0) + 0.1 * ci
+        k_new = torch.from_numpy(W.normal_np((n, H, D), 9, 10 + ci) * amp).to(src_dtype)
+        v_new = torch.from_numpy(W.normal_np((n, H, D), 9, 100 + ci) * amp).to(src_dtype)
+        print(f"int4 write call {ci} n={n} bs={bs}", flush=True)
+        pk.pa_write_kv(pool, k_new.to(DEV), v_new.to(DEV), torch.from_numpy(slots).to(DEV))
+        OC.write_kv_int4(hk, hks, hv, hvs, k_new.float().numpy(), v_new.float().numpy(), slots, block_size=bs)
+    torch.cuda.synchronize()
+    assert np.array_equal(pool.k_scale.cpu().numpy().view(np.uint16), hks.view(np.uint16))
+    assert np.array_equal(pool.v_scale.cpu().numpy().view(np.uint16), hvs.view(np.uint16))
+    assert np.array_equal(OC.unpack_int4(pool.k_cache.cpu().numpy()), hk)
+    assert np.array_equal(OC.unpack_int4(pool.v_cache.cpu().numpy()), hv)
+    # Rows written by the calls hold codes in [-7, 7] only.
+    written = np.unique(np.concatenate(calls))
+    blk, off = written // bs, written % bs
+    assert np.abs(OC.unpack_int4(pool.k_cache.cpu().numpy())[blk, :, off]).max() <= 7
+    assert pk.pa_check_errors() == 0
+
+
 @pytest.mark.parametrize("code,D,bs", [("f16", 128, 16), ("i8", 128, 16), ("f32", 64, 16), ("f16", 128, 64),
-                                       ("i8", 64, 32)])
+                                       ("i8", 64, 32), ("i4", 128, 16), ("i4", 128, 64)])
 def test_copy_blocks_bit_exact(code, D, bs):
     pk = _pk()
-    c = {"f32": pk.PA_F32, "f16": pk.PA_F16, "i8": pk.PA_I8}[code]
+    c = {"f32": pk.PA_F32, "f16": pk.PA_F16, "i8": pk.PA_I8, "i4": pk.PA_I4}[code]
     NB, H = 50, 40 if D == 128 else 8
     pool, host = _random_pool(pk, NB, H, D, c, 3, bs)
     rng = W.rng(33, 0)
@@ -130,7 +173,7 @@ def test_copy_blocks_bit_exact(code, D, bs):
     pk.pa_copy_blocks(pool, torch.from_numpy(pairs).to(DEV))
     torch.cuda.synchronize()
     OC.copy_blocks(host, pairs)
-    got = [pool.k_cache, pool.v_cache] + ([pool.k_scale, pool.v_scale] if c == pk.PA_I8 else [])
+    got = [pool.k_cache, pool.v_cache] + ([pool.k_scale, pool.v_scale] if pk.is_quantised(c) else [])
     for g, h in zip(got, host):
         assert np.array_equal(_bytes(g), h.view(np.uint8).reshape(-1))
     assert pk.pa_check_errors() == 0

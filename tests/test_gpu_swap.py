@@ -40,17 +40,17 @@ def _fill(t, seed):
 
 
 @pytest.mark.parametrize("code,D,bs", [("f16", 128, 16), ("i8", 128, 16), ("f32", 64, 32), ("f16", 64, 64),
-                                       ("i8", 64, 64)])
+                                       ("i8", 64, 64), ("i4", 128, 16), ("i4", 128, 32)])
 def test_swap_blocks_bit_exact(code, D, bs):
     pk = _pk()
-    c = {"f32": pk.PA_F32, "f16": pk.PA_F16, "i8": pk.PA_I8}[code]
+    c = {"f32": pk.PA_F32, "f16": pk.PA_F16, "i8": pk.PA_I8, "i4": pk.PA_I4}[code]
     NB, NH, H = 40, 24, 5
     pool = pk.new_pool(NB, H, D, c, device=DEV, block_size=bs)
-    dev = [pool.k_cache, pool.v_cache] + ([pool.k_scale, pool.v_scale] if c == pk.PA_I8 else [])
+    dev = [pool.k_cache, pool.v_cache] + ([pool.k_scale, pool.v_scale] if pk.is_quantised(c) else [])
     for i, t in enumerate(dev):
         _fill(t, 100 + i)
     host = pk.HostPool(pool, NH)
-    hp = [host.k, host.v] + ([host.k_scale, host.v_scale] if c == pk.PA_I8 else [])
+    hp = [host.k, host.v] + ([host.k_scale, host.v_scale] if pk.is_quantised(c) else [])
     for i, t in enumerate(hp):
         _fill(t, 200 + i)
     d_np = [t.cpu().numpy().copy() for t in dev]
