@@ -650,6 +650,7 @@ def extras(eng, wl, q, ptok, dev):
     res["swap"] = swap_probe(pk, torch, np, eng, q, dev)
     res["prefix_cache"] = prefix_probe(pk, W, np)
     res["mixed_precision"] = mixed_probe(pk, W, torch, np, wl, ctx, q, t_paged, nbytes, dev)
+    res["quantised_pools"] = quantised_probe(pk, W, torch, np, wl, [int(c) for c in ctx], q, dev)
     # Streaming copy probe: achievable HBM bandwidth (read + write bytes).
     n = 1 << 30
     a = torch.empty(n, dtype=torch.uint8, device=dev)
@@ -698,6 +699,47 @@ def mixed_probe(pk, W, torch, np, wl, ctx, q, t_fp16, fp16_bytes, dev):
     return {"decode_us": round(t * 1e6, 2), "bytes": int(nbytes), "gbs": round(nbytes / t / 1e9, 1),
             "fp16_decode_us": round(t_fp16 * 1e6, 2), "fp16_bytes": int(fp16_bytes),
             "speedup_vs_fp16": round(t_fp16 / t, 3), "cold_token_fraction": round(cold_tokens / int(cl.sum()), 4)}
+
+
+def quantised_probe(pk, W, torch, np, wl, ctx, q, dev):
+    """The same contexts stored as int8 and as int4 pools (quantised on write
+    by pa_write_kv from the same fp32 rows an fp16 pool holds rounded): decode
+    time, bytes read (codes and scales) and the largest output difference
+    from the fp16 pool's decode."""
+    from paged_kv_cache_249_amd.engine import PagedDecodeEngine
+    S, H, D = wl.num_seqs, wl.num_heads, wl.head_dim
+    need = sum(-(-int(c) // 16) for c in ctx)
+    nb = -(-5 * need // 4)
+    res, outs = {}, {}
+    order = torch.from_numpy(np.argsort(-np.asarray(ctx), kind="stable").astype(np.int32)).to(dev)
+    for name, code in (("f16", pk.PA_F16), ("i8", pk.PA_I8), ("i4", pk.PA_I4)):
+        eng = PagedDecodeEngine(nb, H, D, code, S, -(-max(ctx) // 16), free_order=W.free_order(wl.seed, nb),
+                                device=dev)
+        for s, c in enumerate(ctx):
+            k = W.normal_torch((int(c), H, D), wl.seed, W.STREAM_K, s, device=dev)
+            v = W.normal_torch((int(c), H, D), wl.seed, W.STREAM_V, s, device=dev)
+            if code == pk.PA_F16:
+                k, v = k.half(), v.half()
+            eng.add_sequence(s, k, v)
+            del k, v
+        tables, cl = eng.bm.export(np.arange(S), eng.cap)
+        tabd, ctxd = torch.from_numpy(tables).to(dev), torch.from_numpy(cl).to(dev)
+        out = torch.empty_like(q)
+        maxc = int(cl.max())
+        t = _time_calls(lambda: pk.pa_decode(eng.pool, q, out, tabd, ctxd, maxc, seq_order=order))
+        torch.cuda.synchronize()
+        outs[name] = out.float()
+        tok = int(cl.astype(np.int64).sum())
+        blocks = int(((cl.astype(np.int64) + 15) // 16).sum())
+        elem = {"f16": 2.0, "i8": 1.0, "i4": 0.5}[name]
+        nbytes = int(tok * H * D * 2 * elem) + (blocks * H * 2 * 2 if name != "f16" else 0)
+        res[name] = {"decode_us": round(t * 1e6, 2), "bytes": nbytes, "gbs": round(nbytes / t / 1e9, 1)}
+        del eng
+        torch.cuda.empty_cache()
+    for name in ("i8", "i4"):
+        res[name]["speedup_vs_f16"] = round(res["f16"]["decode_us"] / res[name]["decode_us"], 3)
+        res[name]["max_abs_diff_vs_f16"] = round(float((outs[name] - outs["f16"]).abs().max()), 5)
+    return res
 
 
 def prefix_probe(pk, W, np):

@@ -133,13 +133,32 @@ constexpr int kMaxGroupParts = 16;
 #define PA_DECODE_MIN_WAVES (PA_DECODE_PREFETCH ? 4 : 8)
 #endif
 
+// int4 pools: a tag type for bytes that hold two codes (each nibble code + 8,
+// even dim in the low nibble).
+struct Int4 {};
+template <typename KV>
+struct KvBits {
+  static constexpr int value = 8 * int(sizeof(KV));
+};
+template <>
+struct KvBits<Int4> {
+  static constexpr int value = 4;
+};
+template <typename KV>
+constexpr bool kQuantKV = std::is_same<KV, int8_t>::value || std::is_same<KV, Int4>::value;
+
+// A lane loads 16-byte chunks (int4: 8-byte chunks, 16 values, so that q and
+// the accumulators of a lane stay at 16 values each, as for int8).
 template <typename KV, int D>
 struct Geo {
-  static constexpr int kRowBytes = D * int(sizeof(KV));
-  static constexpr int kCPT = kRowBytes / 16;      // lanes per row
+  static constexpr int kChunkBytes = std::is_same<KV, Int4>::value ? 8 : 16;
+  using Chunk = typename std::conditional<kChunkBytes == 8, uint2, uint4>::type;
+  static constexpr int kRowBytes = D * KvBits<KV>::value / 8;
+  static constexpr int kCPT = kRowBytes / kChunkBytes;   // lanes per row
   static constexpr int kTPI = kWave / kCPT;        // rows per wave-wide load
   static constexpr int kNLD = kTileRows / kTPI;    // loads per lane per unit
-  static constexpr int kEPC = 16 / int(sizeof(KV));  // elements per lane per row
+  static constexpr int kEPC = kChunkBytes * 8 / KvBits<KV>::value;  // elements per lane per row
+  static constexpr int kLoadBytes = kWave * kChunkBytes;     // one wave-wide load
   static constexpr int kTileBytes = kTileRows * kRowBytes;   // one 16-row unit
   static_assert(kCPT >= 4 && kCPT <= 32, "unsupported row size");
 };
@@ -267,6 +286,51 @@ __device__ __forceinline__ void axpy16(float p, const uint4& r, float (&acc)[EPC
   }
 }
 
+// int4 chunks: 8 bytes, 16 unsigned nibbles n = code + 8 (the callers account
+// for the offset). The low nibbles of word j are dims 8j, 8j+2, 8j+4, 8j+6,
+// the high ones 8j+1, ...; each byte of a masked word converts to float in
+// one instruction (v_cvt_f32_ubyte0..3). The masked words pass through an
+// empty asm statement so that the compiler, which knows they hold nibbles,
+// does not fold each conversion into a bit-field extract plus a conversion.
+__device__ __forceinline__ void nibble_words(uint32_t w, uint32_t& lo, uint32_t& hi) {
+  lo = w & 0x0F0F0F0Fu;
+  hi = (w >> 4) & 0x0F0F0F0Fu;
+  asm("" : "+v"(lo), "+v"(hi));
+}
+template <typename KV, typename QT, int EPC>
+__device__ __forceinline__ float dot16(const uint2& r, const QSlice<KV, QT, EPC>& q) {
+  static_assert(std::is_same<KV, Int4>::value && EPC == 16, "8-byte chunks are int4");
+  const uint32_t w[2] = {r.x, r.y};
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    uint32_t lo, hi;
+    nibble_words(w[j], lo, hi);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      s = fmaf(float((lo >> (8 * b)) & 0xFFu), q.f[8 * j + 2 * b], s);
+      s = fmaf(float((hi >> (8 * b)) & 0xFFu), q.f[8 * j + 2 * b + 1], s);
+    }
+  }
+  return s;
+}
+
+template <typename KV, int EPC>
+__device__ __forceinline__ void axpy16(float p, const uint2& r, float (&acc)[EPC]) {
+  static_assert(std::is_same<KV, Int4>::value && EPC == 16, "8-byte chunks are int4");
+  const uint32_t w[2] = {r.x, r.y};
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    uint32_t lo, hi;
+    nibble_words(w[j], lo, hi);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      acc[8 * j + 2 * b] = fmaf(p, float((lo >> (8 * b)) & 0xFFu), acc[8 * j + 2 * b]);
+      acc[8 * j + 2 * b + 1] = fmaf(p, float((hi >> (8 * b)) & 0xFFu), acc[8 * j + 2 * b + 1]);
+    }
+  }
+}
+
 // W consecutive 32-bit words from a 16-byte aligned address (8-byte aligned
 // when W == 2), with the widest loads that fit.
 template <typename T, int W>
@@ -322,7 +386,10 @@ void decode_kernel(Params p, const int32_t* __restrict__ tables, const int32_t* 
   // output) never alias them and keeps reading them through the scalar cache.
   using G = Geo<KV, D>;
   constexpr int CPT = G::kCPT, TPI = G::kTPI, NLD = G::kNLD, EPC = G::kEPC;
+  using Chunk = typename G::Chunk;
   constexpr bool kInt8 = std::is_same<KV, int8_t>::value;
+  constexpr bool kInt4 = std::is_same<KV, Int4>::value;
+  constexpr bool kQuant = kQuantKV<KV>;
 
   const int parts_per_group = kWavePart ? kWaves : p.parts_per_group;
   const int groups = (p.num_partitions + parts_per_group - 1) / parts_per_group;
@@ -399,7 +466,7 @@ void decode_kernel(Params p, const int32_t* __restrict__ tables, const int32_t* 
   // Fused write (float pools): the new row's slot and this lane's chunk of
   // the row, fetched speculatively with the rest (used only by the wave that
   // owns the sequence's last block).
-  constexpr bool kFusable = kPaged && !kInt8 && !std::is_same<NEW, void>::value;
+  constexpr bool kFusable = kPaged && !kQuant && !std::is_same<NEW, void>::value;
   using NewT = typename std::conditional<std::is_same<NEW, void>::value, float, NEW>::type;
   constexpr int kNewWords = EPC * int(sizeof(NewT)) / 4;        // 32-bit words per lane chunk
   int64_t new_slot = -1;
@@ -452,14 +519,19 @@ void decode_kernel(Params p, const int32_t* __restrict__ tables, const int32_t* 
   // A unit is read through a buffer resource built per unit (uniform base in
   // SGPRs, loop-invariant lane offset): no 64-bit vector address arithmetic in
   // the loop, and the hardware clamps any access outside the unit to zero.
-  auto load_tile = [&](const char* base, int64_t off, uint4 (&r)[NLD]) {
+  auto load_tile = [&](const char* base, int64_t off, Chunk (&r)[NLD]) {
     const __amdgpu_buffer_rsrc_t rs =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base + off), 0, G::kTileBytes, kRsrcWord3);
 #pragma unroll
     for (int i = 0; i < NLD; ++i)
-      r[i] = __builtin_bit_cast(
-          uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, lane * 16 + i * 1024, 0,
-                                                       kCached ? kLoadAuxShared : PA_DECODE_LOAD_AUX));
+      if constexpr (G::kChunkBytes == 16)
+        r[i] = __builtin_bit_cast(
+            uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, lane * 16 + i * G::kLoadBytes, 0,
+                                                         kCached ? kLoadAuxShared : PA_DECODE_LOAD_AUX));
+      else
+        r[i] = __builtin_bit_cast(
+            uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, lane * 8 + i * G::kLoadBytes, 0,
+                                                        kCached ? kLoadAuxShared : PA_DECODE_LOAD_AUX));
   };
   struct TileRef {
     int b;
@@ -468,17 +540,22 @@ void decode_kernel(Params p, const int32_t* __restrict__ tables, const int32_t* 
     float kscale, vscale;
   };
   // Issue the loads of the wave's k-th unit (table entry phys) into (kr, vr).
-  auto fetch = [&](int k, int phys, uint4 (&kr)[NLD], uint4 (&vr)[NLD]) -> TileRef {
+  auto fetch = [&](int k, int phys, Chunk (&kr)[NLD], Chunk (&vr)[NLD]) -> TileRef {
     TileRef t;
     t.b = first + k * ustride;
     t.phys = phys;
     const int64_t off = tile_offset(t.b, phys, &t.ok);
     load_tile(p.k, off, kr);
     load_tile(p.v, off, vr);
-    if constexpr (kInt8) {
+    if constexpr (kQuant) {
+      // A masked unit (entry outside the pool) weighs nothing, whatever
+      // block 0's scale holds. (Loaded unconditionally, then selected: a
+      // conditional load would become a branch around it.)
       const int64_t si = int64_t(t.ok ? phys : 0) * p.num_heads + h;
-      t.kscale = float(p.k_scale[si]);
-      t.vscale = float(p.v_scale[si]);
+      const float ks = float(p.k_scale[si]);
+      const float vs = float(p.v_scale[si]);
+      t.kscale = t.ok ? ks : 0.f;
+      t.vscale = t.ok ? vs : 0.f;
     } else {
       t.kscale = 1.f;
       t.vscale = 1.f;
@@ -490,6 +567,20 @@ void decode_kernel(Params p, const int32_t* __restrict__ tables, const int32_t* 
   float acc[EPC];
 #pragma unroll
   for (int e = 0; e < EPC; ++e) acc[e] = 0.f;
+  // int4: the loop works on unsigned nibbles n = code + 8. A logit is then
+  // sum q n - 8 sum q (q_bias = 8 sum q over the row, set before the first
+  // unit), and every value of the lane's rows carries +8, so the lane also
+  // keeps vbias = sum of the weights it has applied (rescaled with acc) and
+  // takes 8 vbias off acc when it hands over.
+  float q_bias = 0.f, vbias = 0.f;
+  auto prepare_q = [&]() {
+    if constexpr (kInt4) {
+      float qsum = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) qsum += qs.f[e];
+      q_bias = 8.f * group_sum<CPT>(qsum);
+    }
+  };
   // A bad table entry is only recorded here and flagged after the loop: a
   // store inside the loop would stop the compiler from fetching table entries
   // and scales through the scalar cache.
@@ -564,7 +655,7 @@ void decode_kernel(Params p, const int32_t* __restrict__ tables, const int32_t* 
   auto flush = [&](int pidx) {
     float fm = m, fl = l, fa[EPC];
 #pragma unroll
-    for (int e = 0; e < EPC; ++e) fa[e] = acc[e];
+    for (int e = 0; e < EPC; ++e) fa[e] = kInt4 ? acc[e] - 8.f * vbias : acc[e];
 #pragma unroll
     for (int mask = CPT; mask < kWave; mask <<= 1) {
       const float m2 = __shfl_xor(fm, mask);
@@ -593,6 +684,7 @@ void decode_kernel(Params p, const int32_t* __restrict__ tables, const int32_t* 
     }
     m = kNegBig;
     l = 0.f;
+    vbias = 0.f;
 #pragma unroll
     for (int e = 0; e < EPC; ++e) acc[e] = 0.f;
   };
@@ -604,34 +696,41 @@ void decode_kernel(Params p, const int32_t* __restrict__ tables, const int32_t* 
   int next_flush = unit_begin + p.partition_units;
 
   // Online-softmax update with one unit.
-  auto process = [&](const TileRef& t, uint4 (&kr)[NLD], uint4 (&vr)[NLD]) {
+  auto process = [&](const TileRef& t, Chunk (&kr)[NLD], Chunk (&vr)[NLD]) {
     bad_entry |= !t.ok;
     const int t0 = t.b * kTileRows;
-    if (new_row >= 0 && t.b == nunits - 1) {
-      if (t.ok && int64_t(t.phys) == (new_slot >> bshift)) {
-        patched = true;
-        new_dst = int64_t(t.phys) * block_stride + int64_t(h) * head_stride +
-                  (new_slot & in_block) * G::kRowBytes + col * 16;
+    if constexpr (kFusable) {
+      if (new_row >= 0 && t.b == nunits - 1) {
+        if (t.ok && int64_t(t.phys) == (new_slot >> bshift)) {
+          patched = true;
+          new_dst = int64_t(t.phys) * block_stride + int64_t(h) * head_stride +
+                    (new_slot & in_block) * G::kRowBytes + col * 16;
 #pragma unroll
-        for (int i = 0; i < NLD; ++i) {
-          if (i == new_row / TPI && grp == new_row % TPI) {
-            kr[i] = nk;
-            vr[i] = nv;
+          for (int i = 0; i < NLD; ++i) {
+            if (i == new_row / TPI && grp == new_row % TPI) {
+              kr[i] = nk;
+              vr[i] = nv;
+            }
           }
+        } else {
+          bad_slot = true;
         }
-      } else {
-        bad_slot = true;
       }
     }
     float sc[NLD];
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) sc[i] = group_sum<CPT>(dot16(kr[i], qs)) * (t.kscale * p.scale_log2);
+    for (int i = 0; i < NLD; ++i) {
+      if constexpr (kInt4)
+        sc[i] = (group_sum<CPT>(dot16(kr[i], qs)) - q_bias) * (t.kscale * p.scale_log2);
+      else
+        sc[i] = group_sum<CPT>(dot16(kr[i], qs)) * (t.kscale * p.scale_log2);
+    }
     if (t0 + kTileRows > ctx || !t.ok) {
 #pragma unroll
       for (int i = 0; i < NLD; ++i) {
         if (!t.ok || t0 + i * TPI + grp >= ctx) {
           sc[i] = -INFINITY;
-          vr[i] = make_uint4(0u, 0u, 0u, 0u);
+          vr[i] = Chunk{};
         }
       }
     }
@@ -641,6 +740,7 @@ void decode_kernel(Params p, const int32_t* __restrict__ tables, const int32_t* 
     const float mn = fmaxf(m, bmax);
     const float alpha = __builtin_amdgcn_exp2f(m - mn);
     l *= alpha;
+    if constexpr (kInt4) vbias *= alpha;
 #pragma unroll
     for (int e = 0; e < EPC; ++e) acc[e] *= alpha;
 #pragma unroll
@@ -648,6 +748,7 @@ void decode_kernel(Params p, const int32_t* __restrict__ tables, const int32_t* 
       const float pi = __builtin_amdgcn_exp2f(sc[i] - mn);
       l += pi;
       axpy16<KV, EPC>(pi * t.vscale, vr[i], acc);
+      if constexpr (kInt4) vbias += pi * t.vscale;
     }
     m = mn;
     if constexpr (!kWavePart && !kMixed) {
@@ -742,23 +843,25 @@ void decode_kernel(Params p, const int32_t* __restrict__ tables, const int32_t* 
   // lane already keep enough bytes in flight, so those run single-buffered.
   constexpr bool kDouble = PA_DECODE_PREFETCH != 0 && NLD <= 4;
   if (!kDouble) {
+    prepare_q();
     convert_new_row();
     int e = e0;
     for (int k = 0; k < iters; ++k) {
       const int e_next = k + 1 < iters ? (k == 0 ? e1 : entry(k + 1)) : 0;   // consumed next iteration
-      uint4 ka[NLD], va[NLD];
+      Chunk ka[NLD], va[NLD];
       const TileRef ta = fetch(k, e, ka, va);
       process(ta, ka, va);
       e = e_next;
     }
   } else if (iters > 0) {
-    uint4 ka[NLD], va[NLD], kb[NLD], vb[NLD];
+    Chunk ka[NLD], va[NLD], kb[NLD], vb[NLD];
     const int last = iters - 1;
     int e_next = last >= 1 ? e1 : e0;
     if constexpr (kMixed) {
       if (hot_mine) hot_load();
     }
     TileRef ta = fetch(0, e0, ka, va);
+    prepare_q();
     if constexpr (kMixed) {
       if (hot_mine) hot_process();
     }
@@ -963,6 +1066,8 @@ void launch_kernels(const Params& p, int grid, hipStream_t st) {
       launch_one<KV, QT, D, kPaged, void, true, kWP>(p, grid, lds, st);
     else
       launch_one<KV, QT, D, kPaged, void, false, kWP>(p, grid, lds, st);
+  } else if constexpr (kPaged && std::is_same<KV, Int4>::value) {
+    launch_one<KV, QT, D, kPaged, void, false, kWP>(p, grid, lds, st);
   } else if constexpr (kPaged) {
     if (p.slots != nullptr) {
       if (p.new_is_f32)
@@ -1005,8 +1110,12 @@ int launch_typed(const Params& p, int sh_count, hipStream_t st) {
 
 template <typename KV, typename QT, bool kPaged>
 int launch_d(const Params& p, int D, int sh_count, hipStream_t st) {
-  return D == 64 ? launch_typed<KV, QT, 64, kPaged>(p, sh_count, st)
-                 : launch_typed<KV, QT, 128, kPaged>(p, sh_count, st);
+  if constexpr (std::is_same<KV, Int4>::value) {
+    return launch_typed<KV, QT, 128, kPaged>(p, sh_count, st);   // int4 pools: head_dim 128 only
+  } else {
+    return D == 64 ? launch_typed<KV, QT, 64, kPaged>(p, sh_count, st)
+                   : launch_typed<KV, QT, 128, kPaged>(p, sh_count, st);
+  }
 }
 
 template <typename KV, bool kPaged>
@@ -1067,6 +1176,8 @@ int launch_decode(const DecodeArgs& a, void* stream) {
                    : launch_q<_Float16, false>(p, a.q_dtype, a.head_dim, sh_count, st);
     case PA_I8:
       return launch_q<int8_t, true>(p, a.q_dtype, a.head_dim, sh_count, st);
+    case PA_I4:
+      return launch_q<Int4, true>(p, a.q_dtype, a.head_dim, sh_count, st);
   }
   return int(hipErrorInvalidValue);
 }

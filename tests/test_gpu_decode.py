@@ -203,14 +203,86 @@ def test_split_partials_match_the_oracle():
             assert_close(o[s, :, p], oo, 1e-4, 1e-4, f"o s={s} p={p}")
 
 
+def _int4_pool(pk, ctx, H, seed, bs, poison=False):
+    """An int4 pool written by the oracle (prefill of each context in one call,
+    then one token per call for the last few), uploaded as packed bytes."""
+    D = 128
+    need = sum(-(-c // bs) for c in ctx)
+    NB = need + 5
+    order = W.free_order(seed, NB)
+    tables, used = [], 0
+    for c in ctx:
+        tables.append(order[used:used + -(-c // bs)])
+        used += len(tables[-1])
+    kc = np.zeros((NB, H, bs, D), np.int8)
+    vc = np.zeros_like(kc)
+    ks = np.zeros((NB, H), np.float16)
+    vs = np.zeros_like(ks)
+    for s, c in enumerate(ctx):
+        K = W.normal_np((c, H, D), seed, W.STREAM_K, s)
+        V = W.normal_np((c, H, D), seed, W.STREAM_V, s)
+        slots = OP.slots(c, tables[s], bs)
+        pre = max(0, c - 5)
+        OC.write_kv_int4(kc, ks, vc, vs, K[:pre], V[:pre], slots[:pre], block_size=bs)
+        for t in range(pre, c):
+            OC.write_kv_int4(kc, ks, vc, vs, K[t:t + 1] * (1 + (t % 3)), V[t:t + 1], slots[t:t + 1],
+                             block_size=bs)
+    kb, vb = OC.pack_int4(kc), OC.pack_int4(vc)
+    if poison:
+        # Blocks no table uses hold random bytes and NaN scales: never read.
+        unused = np.setdiff1d(np.arange(NB), np.concatenate([t for t in tables if len(t)]))
+        rng = W.rng(seed, 77)
+        kb[unused] = rng.integers(0, 256, size=kb[unused].shape, dtype=np.uint8)
+        ks[unused] = np.nan
+        vs[unused] = np.nan
+    pool = pk.new_pool(NB, H, D, pk.PA_I4, device=DEV, block_size=bs)
+    for dst, src in ((pool.k_cache, kb), (pool.v_cache, vb), (pool.k_scale, ks), (pool.v_scale, vs)):
+        dst.copy_(torch.from_numpy(src))
+    tab = np.full((len(ctx), max(1, max(len(t) for t in tables))), -1, np.int32)
+    for i, t in enumerate(tables):
+        tab[i, :len(t)] = t
+    return pool, (kc, vc, ks, vs), tables, tab
+
+
+@pytest.mark.parametrize("bs,qd", [(16, "f16"), (32, "f32"), (64, "f16")])
+def test_int4_decode_matches_the_oracle(bs, qd):
+    # Ragged contexts over int4 codes (scales that grew during the last
+    # single-token writes included), single pass and split: the oracle
+    # decodes the same codes and scales in fp64.
+    pk = _pk()
+    ctx = [1, 2, 15, 16, 17, 63, 64, 65, 300, 1000, 0, 513]
+    H, D, seed = 5, 128, 80 + bs
+    print(f"int4 decode bs={bs} q={qd}", flush=True)
+    pool, (kc, vc, ks, vs), tables, tab = _int4_pool(pk, ctx, H, seed, bs, poison=True)
+    q = W.normal_np((len(ctx), H, D), seed, W.STREAM_Q, dtype=np.float16 if qd == "f16" else np.float32)
+    ref = OA.paged_decode(q, kc, vc, tables, ctx, block_size=bs, k_scale=ks, v_scale=vs)
+    qd_t = torch.from_numpy(q).to(DEV)
+    ctxd = torch.tensor(ctx, dtype=torch.int32, device=DEV)
+    maxc = max(ctx)
+    for ptok in (0, bs, 4 * bs, 512):
+        out = torch.empty_like(qd_t)
+        ws = None
+        if ptok:
+            nb = pk.pa_decode_workspace_bytes(pool, len(ctx), maxc, ptok)
+            ws = torch.full((max(nb // 4, 1),), float("nan"), device=DEV)
+        pk.pa_decode(pool, qd_t, out, torch.from_numpy(tab).to(DEV), ctxd, maxc, partition_tokens=ptok,
+                     workspace=ws)
+        torch.cuda.synchronize()
+        assert pk.pa_check_errors() == 0
+        got = out.cpu().numpy()
+        atol, rtol = (F16_ATOL, F16_RTOL) if qd == "f16" else (1e-4, 1e-4)
+        assert_close(got, ref, atol, rtol, f"int4 bs={bs} q={qd} ptok={ptok}")
+        assert not got[ctx.index(0)].any()
+
+
 STREAM_CTX = [1, 16, 17, 700, 2047, 2048, 2049, 4001]
 STREAM_H = 16
 
 
-@functools.lru_cache(maxsize=1)
-def _int8_stream_batch(H, D, seed):
-    """Int8 pools written by the oracle's quantise-on-write (whole contexts
-    at once), their tables, q and the oracle's decode over the codes."""
+@functools.lru_cache(maxsize=2)
+def _int8_stream_batch(H, D, seed, int4=False):
+    """Int8 (or int4) pools written by the oracle's quantise-on-write (whole
+    contexts at once), their tables, q and the oracle's decode over the codes."""
     ctx = STREAM_CTX
     NB = sum(-(-c // 16) for c in ctx) + 5
     order = W.free_order(seed, NB)
@@ -225,14 +297,14 @@ def _int8_stream_batch(H, D, seed):
     for s, c in enumerate(ctx):
         K = W.normal_np((c, H, D), seed, W.STREAM_K, s)
         V = W.normal_np((c, H, D), seed, W.STREAM_V, s)
-        OC.write_kv_int8(kc, ks, vc, vs, K, V, OP.slots(c, tables[s]))
+        (OC.write_kv_int4 if int4 else OC.write_kv_int8)(kc, ks, vc, vs, K, V, OP.slots(c, tables[s]))
     q = W.normal_np((len(ctx), H, D), seed, W.STREAM_Q, dtype=np.float16)
     ref = OA.paged_decode(q, kc, vc, tables, ctx, k_scale=ks, v_scale=vs)
     return NB, tables, (kc, vc, ks, vs), q, ref
 
 
 @pytest.mark.parametrize("ptok", [32, 64, 128])
-@pytest.mark.parametrize("kv,D", [("f16", 128), ("f32", 64), ("i8", 128)])
+@pytest.mark.parametrize("kv,D", [("f16", 128), ("f32", 64), ("i8", 128), ("i4", 128)])
 def test_many_partitions_per_sequence(kv, D, ptok):
     # Many partitions per sequence (16 heads x 8 sequences, contexts up to
     # 4001): a workgroup streams several partitions (64 and 128 tokens) or a
@@ -244,11 +316,13 @@ def test_many_partitions_per_sequence(kv, D, ptok):
     pk = _pk()
     print(f"many partitions kv={kv} D={D} ptok={ptok}", flush=True)
     H, seed = STREAM_H, 64
-    if kv == "i8":
-        NB, tables, (kc, vc, ks, vs), q, ref = _int8_stream_batch(H, D, seed)
+    if kv in ("i8", "i4"):
+        NB, tables, (kc, vc, ks, vs), q, ref = _int8_stream_batch(H, D, seed, kv == "i4")
         ctx = STREAM_CTX
-        pool = pk.new_pool(NB, H, D, pk.PA_I8, device=DEV)
-        for dst, src in ((pool.k_cache, kc), (pool.v_cache, vc), (pool.k_scale, ks), (pool.v_scale, vs)):
+        pool = pk.new_pool(NB, H, D, pk.PA_I8 if kv == "i8" else pk.PA_I4, device=DEV)
+        stored = (kc, vc) if kv == "i8" else (OC.pack_int4(kc), OC.pack_int4(vc))
+        for dst, src in ((pool.k_cache, stored[0]), (pool.v_cache, stored[1]), (pool.k_scale, ks),
+                         (pool.v_scale, vs)):
             dst.copy_(torch.from_numpy(src))
         tab = np.full((len(ctx), max(len(t) for t in tables)), -1, np.int32)
         for i, t in enumerate(tables):
