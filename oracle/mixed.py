@@ -22,6 +22,10 @@ shares them; the child gets its own hot block, a copy of the parent's).
 Prefill writes full blocks straight into the cold pool (same rule) and the
 remainder into the hot block. Block size 16.
 
+The cold pool may also hold int4 codes (the same page lists INT4 after INT8
+as the next compression step): the same demotion with codes in [-7, 7] and
+``s = fp16(max|x| / 7)`` (:func:`oracle.cache_ops.write_kv_int4`'s rule).
+
 Layout: a sequence of ``ctx`` tokens has ``max(0, ceil(ctx / 16) - 1)`` cold
 blocks holding tokens ``[0, 16 * n_cold)`` and its hot block holding tokens
 ``[16 * n_cold, ctx)`` (1 to 16 of them when ``ctx > 0``).
@@ -154,16 +158,17 @@ class MixedBlockManager:
         return rows, hot, ctx
 
 
-def demote(hot_k, hot_v, cold_k, cold_ks, cold_v, cold_vs, pairs) -> None:
+def demote(hot_k, hot_v, cold_k, cold_ks, cold_v, cold_vs, pairs, qmax: int = 127) -> None:
     """Quantise whole hot blocks into cold blocks: for every ``(hot, cold)``
-    pair and head, the block's 16 rows form one int8 group written at once."""
+    pair and head, the block's 16 rows form one group written at once (codes
+    in [-qmax, qmax]: 127 for int8 cold blocks, 7 for int4)."""
     H = hot_k.shape[1]
     for src, dst in np.asarray(pairs, dtype=np.int64).reshape(-1, 2):
         for h in range(H):
             cache_ops._quantise_group(cold_k, cold_ks, int(dst), h, list(range(BS)),
-                                      list(hot_k[src, h].astype(np.float32)), BS)
+                                      list(hot_k[src, h].astype(np.float32)), BS, qmax)
             cache_ops._quantise_group(cold_v, cold_vs, int(dst), h, list(range(BS)),
-                                      list(hot_v[src, h].astype(np.float32)), BS)
+                                      list(hot_v[src, h].astype(np.float32)), BS, qmax)
 
 
 def gather(cold, cold_scale, hot, cold_row, hot_block: int, ctx: int) -> np.ndarray:

@@ -195,3 +195,46 @@ def test_random_operations_read_back_their_tokens(seed):
                 refs[b] += 1
         assert refs == bm.ref
         assert sorted(list(bm.hot_free) + [st.hot for st in bm.seqs.values()]) == list(range(12))
+
+
+def test_int4_cold_blocks_decode_exactly_when_representable():
+    # Rows k/8 with integer k in [-7, 7] and one +-7/8 per (block, head): the
+    # int4 scale is exactly 1/8 and every code exact, so mixed decode over
+    # int4 cold blocks equals fp16 attention over the same rows exactly.
+    rng = W.rng(65, 0)
+    H, D, n = 2, 8, 75
+    K = (rng.integers(-7, 8, size=(n, H, D)) / 8.0).astype(np.float16)
+    V = (rng.integers(-7, 8, size=(n, H, D)) / 8.0).astype(np.float16)
+    K[::BS, :, 0] = 7 / 8
+    V[::BS, :, 1] = -7 / 8
+    bm = M.MixedBlockManager(10, 4, cold_order=W.free_order(65, 10))
+    ck, cks, cv, cvs, hk, hv = _pools(10, 4, H, D)
+    cold, hot = bm.add_seq(0, 40)
+    C.write_kv_int4(ck, cks, cv, cvs, K[:40].astype(np.float32), V[:40].astype(np.float32), cold)
+    C.write_kv(hk, hv, K[:40], V[:40], hot)
+    for t in range(40, n):
+        slot, src, dst = bm.append(0)
+        if src >= 0:
+            M.demote(hk, hv, ck, cks, cv, cvs, [(src, dst)], qmax=7)
+        C.write_kv(hk, hv, K[t][None], V[t][None], [slot])
+    rows, hot, ctx = bm.export([0], 8)
+    assert (rows[0] >= 0).sum() == 4 and np.abs(ck[rows[0][:4]]).max() <= 7
+    assert np.all(cks[rows[0][:4]] == np.float16(1 / 8))
+    q = rng.standard_normal((1, H, D))
+    got = M.decode(q, ck, cks, cv, cvs, hk, hv, rows, hot, ctx)
+    np.testing.assert_array_equal(got[0], A.attend(q[0], K, V, A.default_scale(D)))
+
+
+def test_int4_demotion_is_the_whole_block_int4_write():
+    rng = W.rng(66, 0)
+    H, D = 2, 16
+    hk = rng.standard_normal((3, H, BS, D)).astype(np.float16)
+    hv = rng.standard_normal((3, H, BS, D)).astype(np.float16)
+    ck, cks = np.zeros((4, H, BS, D), np.int8), np.zeros((4, H), np.float16)
+    cv, cvs = np.zeros_like(ck), np.zeros_like(cks)
+    M.demote(hk, hv, ck, cks, cv, cvs, [(2, 1)], qmax=7)
+    wk, wks = np.zeros_like(ck), np.zeros_like(cks)
+    C.write_kv_int4(wk, wks, wk.copy(), wks.copy(), hk[2].transpose(1, 0, 2).astype(np.float32),
+                    hv[2].transpose(1, 0, 2).astype(np.float32), np.arange(BS) + 3 * BS)
+    assert np.array_equal(wk[3], ck[1]) and np.array_equal(wks[3], cks[1])
+    assert np.all(cks[1] == np.float16(np.abs(hk[2].astype(np.float32)).max(axis=(1, 2)) / np.float32(7)))
