@@ -650,6 +650,8 @@ def extras(eng, wl, q, ptok, dev):
     res["swap"] = swap_probe(pk, torch, np, eng, q, dev)
     res["prefix_cache"] = prefix_probe(pk, W, np)
     res["mixed_precision"] = mixed_probe(pk, W, torch, np, wl, ctx, q, t_paged, nbytes, dev)
+    res["mixed_precision_int4_cold"] = mixed_probe(pk, W, torch, np, wl, ctx, q, t_paged, nbytes, dev,
+                                                   pk.PA_I4)
     res["quantised_pools"] = quantised_probe(pk, W, torch, np, wl, [int(c) for c in ctx], q, dev)
     # Streaming copy probe: achievable HBM bandwidth (read + write bytes).
     n = 1 << 30
@@ -670,15 +672,17 @@ def extras(eng, wl, q, ptok, dev):
     return res
 
 
-def mixed_probe(pk, W, torch, np, wl, ctx, q, t_fp16, fp16_bytes, dev):
-    """The same contexts stored as mixed-precision pages (int8 cold blocks,
-    one fp16 hot block per sequence): decode time and bytes against the
-    all-fp16 paged decode of the same batch."""
+def mixed_probe(pk, W, torch, np, wl, ctx, q, t_fp16, fp16_bytes, dev, cold_dtype=None):
+    """The same contexts stored as mixed-precision pages (int8, or int4, cold
+    blocks, one fp16 hot block per sequence): decode time and bytes against
+    the all-fp16 paged decode of the same batch."""
     from paged_kv_cache_249_amd.engine import MixedDecodeEngine
     S, H, D = wl.num_seqs, wl.num_heads, wl.head_dim
+    cold_dtype = pk.PA_I8 if cold_dtype is None else cold_dtype
     n_cold = [max(0, -(-int(c) // 16) - 1) for c in ctx]
     nc = -(-5 * sum(n_cold) // 4)
-    eng = MixedDecodeEngine(nc, S, H, D, S, max(n_cold) + 1, cold_order=W.free_order(wl.seed, nc), device=dev)
+    eng = MixedDecodeEngine(nc, S, H, D, S, max(n_cold) + 1, cold_order=W.free_order(wl.seed, nc), device=dev,
+                            cold_dtype=cold_dtype)
     for s, c in enumerate(ctx):
         k = W.normal_torch((int(c), H, D), wl.seed, W.STREAM_K, s, dtype=torch.float16, device=dev)
         v = W.normal_torch((int(c), H, D), wl.seed, W.STREAM_V, s, dtype=torch.float16, device=dev)
@@ -693,7 +697,8 @@ def mixed_probe(pk, W, torch, np, wl, ctx, q, t_fp16, fp16_bytes, dev):
                                                seq_order=order))
     cold_tokens = 16 * sum(n_cold)
     hot_tokens = int(cl.sum()) - cold_tokens
-    nbytes = cold_tokens * H * D * 2 + sum(n_cold) * H * 2 * 2 + hot_tokens * H * D * 2 * 2
+    code_bytes = 2.0 if cold_dtype == pk.PA_I8 else 1.0      # K and V codes per value pair
+    nbytes = int(cold_tokens * H * D * code_bytes) + sum(n_cold) * H * 2 * 2 + hot_tokens * H * D * 2 * 2
     del eng
     torch.cuda.empty_cache()
     return {"decode_us": round(t * 1e6, 2), "bytes": int(nbytes), "gbs": round(nbytes / t / 1e9, 1),

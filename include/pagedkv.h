@@ -458,7 +458,8 @@ pa_status pa_bm_is_swapped(const pa_bm* bm, int64_t seq, int32_t* out);
 pa_status pa_bm_host_free_list(const pa_bm* bm, int32_t* out, int32_t cap, int32_t* n);
 
 /* ----------------------------------------------------------------------------
- * Mixed-precision pages: an fp16 hot block per sequence, int8 cold blocks.
+ * Mixed-precision pages: an fp16 hot block per sequence, int8 (or int4) cold
+ * blocks.
  *
  * Pages used often stay in FP16 and pages used rarely are stored as INT8
  * ("PagedAttention 的技术溯源与演进脉络", §4.1 item 2, mixed-precision page
@@ -466,7 +467,8 @@ pa_status pa_bm_host_free_list(const pa_bm* bm, int32_t* out, int32_t cap, int32
  * section 二.3). Here the hot page of a sequence is its newest block, the one
  * each decode step writes. Two pools with block_size 16 and the same heads and
  * head_dim: a PA_F16 "hot" pool (one block per sequence for its whole life)
- * and a PA_I8 "cold" pool (with its scales). A sequence of ctx tokens holds
+ * and a PA_I8 or PA_I4 "cold" pool (with its scales; INT4 is the next step
+ * of the same page's compression list). A sequence of ctx tokens holds
  * n_cold = max(0, ceil(ctx / 16) - 1) cold blocks (tokens [0, 16 n_cold)) and
  * its hot block (tokens [16 n_cold, ctx)).
  *
@@ -511,7 +513,8 @@ pa_status pa_mbm_free_lists(const pa_mbm* m, int32_t* cold_out, int32_t cold_cap
  * head, the hot block's 16 fp16 rows of K (and of V) are quantised as one
  * group into the cold block: s = fp16(max|x| / 127) (IEEE fp32 divide, RNE),
  * codes clamp(rne(x / s), -127, 127) (0 if s == 0) — the pa_write_kv int8
- * rule for a whole block written at once. Ids outside their pools flag
+ * rule for a whole block written at once; for an int4 cold pool 7 in place of
+ * 127 (codes stored as in the PA_I4 layout). Ids outside their pools flag
  * PA_DEV_BAD_PAIR and are skipped. Errors: PA_ERR_INVALID_ARG (pool kinds or
  * geometry do not match), PA_ERR_HIP. */
 pa_status pa_demote_blocks(pa_pool* hot_pool, pa_pool* cold_pool, const int32_t* pairs, int32_t n,
@@ -524,8 +527,8 @@ pa_status pa_demote_blocks(pa_pool* hot_pool, pa_pool* cold_pool, const int32_t*
  * as pa_decode_ordered. A hot block
  * id outside the hot pool flags PA_DEV_BAD_TABLE_ENTRY and its rows are
  * masked. Errors: as pa_decode, plus PA_ERR_INVALID_ARG when the pools are not
- * an int8 cold pool and an fp16 hot pool of block size 16 with equal heads and
- * head_dim. */
+ * an int8 or int4 cold pool and an fp16 hot pool of block size 16 with equal
+ * heads and head_dim. */
 pa_status pa_decode_mixed(pa_pool* cold_pool, pa_pool* hot_pool, const void* q, pa_dtype q_dtype, void* out,
                           const int32_t* cold_tables, int32_t max_blocks, const int32_t* hot_blocks,
                           const int32_t* context_lens, const int32_t* seq_order, int32_t schedule,

@@ -363,14 +363,14 @@ pa_status pa_write_decode(pa_pool* pool, const void* k_new, const void* v_new, p
   return decode_common("pa_write_decode", a, workspace, workspace_bytes, stream);
 }
 
-// The two pools of mixed-precision pages: int8 cold, fp16 hot, 16-token
-// blocks, equal heads and head_dim.
+// The two pools of mixed-precision pages: int8 or int4 cold, fp16 hot,
+// 16-token blocks, equal heads and head_dim.
 static pa_status check_mixed_pools(const char* fn, const pa_pool* cold, const pa_pool* hot) {
   if (!cold || !hot) return fail(PA_ERR_INVALID_ARG, "%s: pool is NULL", fn);
-  if (cold->kv_dtype != PA_I8 || hot->kv_dtype != PA_F16 || cold->block_size != 16 || hot->block_size != 16 ||
-      cold->num_heads != hot->num_heads || cold->head_dim != hot->head_dim)
-    return fail(PA_ERR_INVALID_ARG, "%s: needs an int8 cold pool and an fp16 hot pool of 16-token blocks with "
-                "equal heads and head_dim", fn);
+  if (!pa::is_quantised(cold->kv_dtype) || hot->kv_dtype != PA_F16 || cold->block_size != 16 ||
+      hot->block_size != 16 || cold->num_heads != hot->num_heads || cold->head_dim != hot->head_dim)
+    return fail(PA_ERR_INVALID_ARG, "%s: needs an int8 or int4 cold pool and an fp16 hot pool of 16-token "
+                "blocks with equal heads and head_dim", fn);
   return PA_OK;
 }
 
@@ -405,7 +405,7 @@ pa_status pa_decode_mixed(pa_pool* cold_pool, pa_pool* hot_pool, const void* q, 
   a.v = cold_pool->v_cache;
   a.k_scale = cold_pool->k_scale;
   a.v_scale = cold_pool->v_scale;
-  a.kv_dtype = PA_I8;
+  a.kv_dtype = cold_pool->kv_dtype;
   a.tables = cold_tables;
   a.max_blocks = max_blocks;
   a.block_size = 16;

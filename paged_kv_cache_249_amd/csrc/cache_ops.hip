@@ -298,6 +298,55 @@ __global__ __launch_bounds__(kThreads) void demote_kernel(const int32_t* __restr
   if (lane == 0) (is_v ? v_scale : k_scale)[int64_t(dst) * H + h] = _Float16(s);
 }
 
+// The same demotion into int4 cold blocks (head_dim 128): lane l quantises the
+// 32 values of the tile starting at l * 32 (a quarter row) into 16 bytes.
+__global__ __launch_bounds__(kThreads) void demote_i4_kernel(const int32_t* __restrict__ pairs, int n,
+                                                             const _Float16* __restrict__ hot_k,
+                                                             const _Float16* __restrict__ hot_v,
+                                                             uint8_t* __restrict__ cold_k,
+                                                             uint8_t* __restrict__ cold_v,
+                                                             _Float16* __restrict__ k_scale,
+                                                             _Float16* __restrict__ v_scale, int H, int num_hot,
+                                                             int num_cold, int32_t* err) {
+  constexpr int kRows = 16, D = 128;
+  constexpr int kPer = kRows * D / kWave;   // 32 values per lane
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t wid = int64_t(blockIdx.x) * (kThreads / kWave) + wave_uniform(threadIdx.x / kWave);
+  if (wid >= int64_t(n) * H) return;
+  const int pair = int(wid / H);
+  const int h = int(wid % H);
+  const bool is_v = blockIdx.y != 0;
+  const int src = pairs[2 * pair];
+  const int dst = pairs[2 * pair + 1];
+  if (unsigned(src) >= unsigned(num_hot) || unsigned(dst) >= unsigned(num_cold)) {
+    if (lane == 0 && h == 0 && !is_v) flag_error(err, PA_DEV_BAD_PAIR);
+    return;
+  }
+  const _Float16* x = (is_v ? hot_v : hot_k) + (int64_t(src) * H + h) * kRows * D + lane * kPer;
+  _Float16 vals[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer / 8; ++j)
+    *reinterpret_cast<uint4*>(vals + 8 * j) = reinterpret_cast<const uint4*>(x)[j];
+  float a = 0.f;
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) a = fmaxf(a, fabsf(float(vals[e])));
+  a = wave_max(a);
+  const float s = float(_Float16(a / 7.0f));
+  uint8_t bytes[kPer / 2];
+#pragma unroll
+  for (int e = 0; e < kPer / 2; ++e) {
+    float lo = 0.f, hi = 0.f;
+    if (s > 0.f) {
+      lo = fminf(fmaxf(__builtin_rintf(float(vals[2 * e]) / s), -7.f), 7.f);
+      hi = fminf(fmaxf(__builtin_rintf(float(vals[2 * e + 1]) / s), -7.f), 7.f);
+    }
+    bytes[e] = uint8_t(uint32_t(int(lo) + 8) | (uint32_t(int(hi) + 8) << 4));
+  }
+  uint8_t* y = (is_v ? cold_v : cold_k) + (int64_t(dst) * H + h) * kRows * (D / 2) + lane * (kPer / 2);
+  *reinterpret_cast<uint4*>(y) = *reinterpret_cast<const uint4*>(bytes);
+  if (lane == 0) (is_v ? v_scale : k_scale)[int64_t(dst) * H + h] = _Float16(s);
+}
+
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void copy_blocks_kernel(const int32_t* __restrict__ pairs, int n,
                                                                char* __restrict__ k, char* __restrict__ v,
@@ -510,6 +559,14 @@ int launch_demote_blocks(const pa_pool* hot, const pa_pool* cold, const int32_t*
   if (n == 0) return 0;
   const int64_t waves = int64_t(n) * hot->num_heads;
   const dim3 grid(unsigned((waves + (kThreads / kWave) - 1) / (kThreads / kWave)), 2);
+  if (cold->kv_dtype == PA_I4) {
+    hipLaunchKernelGGL(demote_i4_kernel, grid, dim3(kThreads), 0, static_cast<hipStream_t>(stream), pairs, n,
+                       static_cast<const _Float16*>(hot->k_cache), static_cast<const _Float16*>(hot->v_cache),
+                       static_cast<uint8_t*>(cold->k_cache), static_cast<uint8_t*>(cold->v_cache),
+                       static_cast<_Float16*>(cold->k_scale), static_cast<_Float16*>(cold->v_scale),
+                       hot->num_heads, hot->num_blocks, cold->num_blocks, device_error_ptr());
+    return int(hipGetLastError());
+  }
   auto go = [&](auto kern) {
     hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, static_cast<hipStream_t>(stream), pairs, n,
                        static_cast<const _Float16*>(hot->k_cache), static_cast<const _Float16*>(hot->v_cache),

@@ -49,11 +49,11 @@
 // reduce kernel merges partitions as out = sum w_p o_p / sum w_p with
 // w_p = exp(m_p - M) l_p. Sequences with one partition are written directly.
 //
-// Mixed-precision pages. With an fp16 hot pool, the table holds the int8
-// cold blocks and the last unit of every sequence comes from its hot block:
-// the wave that owns that unit reads its fp16 rows after the loop, in the
-// int8 lane layout (each lane 16 values of a row), and folds them into the
-// same softmax stream.
+// Mixed-precision pages. With an fp16 hot pool, the table holds the int8 (or
+// int4) cold blocks and the last unit of every sequence comes from its hot
+// block: the wave that owns that unit reads its fp16 rows together with its
+// first tile, in the cold pool's lane layout (each lane 16 values of a row),
+// and folds them into the same softmax stream.
 //
 // XCD-aware order. Workgroup ids are dealt to the 8 XCDs round-robin; groups
 // of 4 consecutive work items are steered onto one XCD, while the deal stays
@@ -479,7 +479,8 @@ void decode_kernel(Params p, const int32_t* __restrict__ tables, const int32_t* 
     load_words(vsrc, rv);
   }
 
-  static_assert(!kMixed || (kInt8 && kPaged && std::is_same<NEW, void>::value), "mixed pages: int8 cold pool");
+  static_assert(!kMixed || (kQuant && kPaged && std::is_same<NEW, void>::value),
+                "mixed pages: int8 or int4 cold pool");
   int hot_blk = 0;
   if constexpr (kMixed) hot_blk = p.hot_blocks[s];
   const bool bad_ctx = ctx < 0 || ctx > p.max_ctx;
@@ -814,6 +815,7 @@ void decode_kernel(Params p, const int32_t* __restrict__ tables, const int32_t* 
       const float mn = fmaxf(m, bmax);
       const float alpha = __builtin_amdgcn_exp2f(m - mn);
       l *= alpha;
+      if constexpr (kInt4) vbias *= alpha;   // hot rows are fp16: they add no offset
 #pragma unroll
       for (int e = 0; e < EPC; ++e) acc[e] *= alpha;
 #pragma unroll
@@ -1067,7 +1069,10 @@ void launch_kernels(const Params& p, int grid, hipStream_t st) {
     else
       launch_one<KV, QT, D, kPaged, void, false, kWP>(p, grid, lds, st);
   } else if constexpr (kPaged && std::is_same<KV, Int4>::value) {
-    launch_one<KV, QT, D, kPaged, void, false, kWP>(p, grid, lds, st);
+    if (p.hot_blocks != nullptr)
+      launch_one<KV, QT, D, kPaged, void, true, kWP>(p, grid, lds, st);
+    else
+      launch_one<KV, QT, D, kPaged, void, false, kWP>(p, grid, lds, st);
   } else if constexpr (kPaged) {
     if (p.slots != nullptr) {
       if (p.new_is_f32)

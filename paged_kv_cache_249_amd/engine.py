@@ -344,7 +344,7 @@ class PagedDecodeEngine:
 
 class MixedDecodeEngine:
     """Decode steps over mixed-precision pages: an fp16 hot block per
-    sequence (its newest tokens), int8 cold blocks for everything older.
+    sequence (its newest tokens), int8 (or int4) cold blocks for everything older.
 
     A step: the manager appends one token per sequence (demoting full hot
     blocks into fresh cold blocks) and exports cold tables, hot blocks and
@@ -355,10 +355,13 @@ class MixedDecodeEngine:
 
     def __init__(self, num_cold: int, num_hot: int, num_heads: int, head_dim: int, max_seqs: int,
                  max_cold_per_seq: int, *, cold_order=None, hot_order=None, device="cuda",
-                 partition_tokens: int = 0, staging_depth: int = 3, longest_first: bool = True, host_tables=None):
+                 partition_tokens: int = 0, staging_depth: int = 3, longest_first: bool = True, host_tables=None,
+                 cold_dtype: int = N.PA_I8):
         self.device = torch.device(device)
         self.num_heads, self.head_dim = num_heads, head_dim
-        self.cold = N.new_pool(num_cold, num_heads, head_dim, N.PA_I8, device=self.device, fill=0)
+        if not N.is_quantised(cold_dtype):
+            raise N.PagedKVError(N.PA_ERR_INVALID_ARG, "cold blocks are int8 or int4")
+        self.cold = N.new_pool(num_cold, num_heads, head_dim, cold_dtype, device=self.device, fill=0)
         self.hot = N.new_pool(num_hot, num_heads, head_dim, N.PA_F16, device=self.device, fill=0.0)
         self.mbm = N.MixedBlockManager(num_cold, num_hot, cold_order, hot_order)
         self.max_seqs = max_seqs

@@ -342,7 +342,7 @@ def pa_decode(pool: Pool, q, out, block_tables, context_lens, max_context_len: i
 
 
 def pa_demote_blocks(hot: Pool, cold: Pool, pairs, stream=None) -> None:
-    """Quantise full fp16 hot blocks into int8 cold blocks for int32 ``[n][2]``
+    """Quantise full fp16 hot blocks into int8 or int4 cold blocks for int32 ``[n][2]``
     device (hot, cold) pairs."""
     torch = _torch()
     n = int(pairs.shape[0]) if pairs.numel() else 0
@@ -353,7 +353,7 @@ def pa_demote_blocks(hot: Pool, cold: Pool, pairs, stream=None) -> None:
 def pa_decode_mixed(cold: Pool, hot: Pool, q, out, cold_tables, hot_blocks, context_lens, max_context_len: int,
                     sm_scale: float = 0.0, partition_tokens: int = 0, workspace=None, stream=None,
                     seq_order=None, schedule: int = PA_SCHED_HEADS) -> None:
-    """Decode over mixed-precision pages (int8 cold pool through ``cold_tables``,
+    """Decode over mixed-precision pages (int8 or int4 cold pool through ``cold_tables``,
     each sequence's fp16 hot block ``hot_blocks[s]`` for its last tokens)."""
     torch = _torch()
     S = int(q.shape[0])

@@ -61,20 +61,58 @@ def test_demote_is_bit_exact(D):
     assert torch.equal(before, cold.k_cache)
 
 
+def test_demote_int4_is_bit_exact():
+    # Demotion into an int4 cold pool whose blocks start as random bytes:
+    # demoted blocks hold the oracle's codes and scales, the others keep
+    # their bytes.
+    from oracle import cache_ops as OC
+    pk = _pk()
+    NH, NC, H, D = 12, 20, 5, 128
+    rng = W.rng(75, D)
+    hk = (rng.standard_normal((NH, H, 16, D)) * rng.uniform(0.1, 4, size=(NH, H, 1, 1))).astype(np.float16)
+    hv = (rng.standard_normal((NH, H, 16, D)) * rng.uniform(0.1, 4, size=(NH, H, 1, 1))).astype(np.float16)
+    hv[3] = 0
+    hot = pk.new_pool(NH, H, D, pk.PA_F16, device=DEV)
+    cold = pk.new_pool(NC, H, D, pk.PA_I4, device=DEV)
+    hot.k_cache.copy_(torch.from_numpy(hk))
+    hot.v_cache.copy_(torch.from_numpy(hv))
+    kb = rng.integers(0, 256, size=(NC, H, 16, D // 2), dtype=np.uint8)
+    vb = rng.integers(0, 256, size=(NC, H, 16, D // 2), dtype=np.uint8)
+    cks = rng.uniform(0.01, 0.1, size=(NC, H)).astype(np.float16)
+    cvs = cks.copy()
+    for t, a in ((cold.k_cache, kb), (cold.v_cache, vb), (cold.k_scale, cks), (cold.v_scale, cvs)):
+        t.copy_(torch.from_numpy(a))
+    ck, cv = OC.unpack_int4(kb), OC.unpack_int4(vb)
+    pairs = np.stack([rng.permutation(NH)[:9], rng.permutation(NC)[:9]], axis=1).astype(np.int32)
+    print(f"demote int4 pairs={pairs.tolist()}", flush=True)
+    pk.pa_demote_blocks(hot, cold, torch.from_numpy(pairs).to(DEV))
+    torch.cuda.synchronize()
+    assert pk.pa_check_errors() == 0
+    OM.demote(hk, hv, ck, cks, cv, cvs, pairs, qmax=7)
+    assert np.array_equal(OC.unpack_int4(cold.k_cache.cpu().numpy()), ck)
+    assert np.array_equal(OC.unpack_int4(cold.v_cache.cpu().numpy()), cv)
+    assert np.array_equal(cold.k_scale.cpu().numpy().view(np.uint16), cks.view(np.uint16))
+    assert np.array_equal(cold.v_scale.cpu().numpy().view(np.uint16), cvs.view(np.uint16))
+    untouched = np.setdiff1d(np.arange(NC), pairs[:, 1])
+    assert np.array_equal(cold.k_cache.cpu().numpy()[untouched], kb[untouched])
+
+
 class MixedBatch:
     """Cold codes/scales and hot rows drawn at random (stored values, not
     demoted ones: decode must read whatever the pools hold), random tables."""
 
-    def __init__(self, ctx, H, D, seed, q="f16", poison=False):
+    def __init__(self, ctx, H, D, seed, q="f16", poison=False, cold="i8"):
+        from oracle import cache_ops as OC
         pk = _pk()
         rng = W.rng(seed, 1)
+        qmax = 127 if cold == "i8" else 7
         self.ctx = list(ctx)
         S = len(ctx)
         n_cold = [max(0, -(-c // 16) - 1) for c in ctx]
         self.NC = sum(n_cold) + 5
         self.NH = S + 3
-        self.ck = rng.integers(-127, 128, size=(self.NC, H, 16, D)).astype(np.int8)
-        self.cv = rng.integers(-127, 128, size=(self.NC, H, 16, D)).astype(np.int8)
+        self.ck = rng.integers(-qmax, qmax + 1, size=(self.NC, H, 16, D)).astype(np.int8)
+        self.cv = rng.integers(-qmax, qmax + 1, size=(self.NC, H, 16, D)).astype(np.int8)
         self.cks = rng.uniform(0.002, 0.02, size=(self.NC, H)).astype(np.float16)
         self.cvs = rng.uniform(0.002, 0.02, size=(self.NC, H)).astype(np.float16)
         self.hk = rng.standard_normal((self.NH, H, 16, D)).astype(np.float16)
@@ -92,9 +130,10 @@ class MixedBatch:
                 self.hk[self.hot[s], :, live:, :] = np.nan
                 self.hv[self.hot[s], :, live:, :] = np.nan
         self.q = W.normal_np((S, H, D), seed, W.STREAM_Q, dtype=np.float16 if q == "f16" else np.float32)
-        self.cold = pk.new_pool(self.NC, H, D, pk.PA_I8, device=DEV)
+        self.cold = pk.new_pool(self.NC, H, D, pk.PA_I8 if cold == "i8" else pk.PA_I4, device=DEV)
         self.hotp = pk.new_pool(self.NH, H, D, pk.PA_F16, device=DEV)
-        for t, a in ((self.cold.k_cache, self.ck), (self.cold.v_cache, self.cv), (self.cold.k_scale, self.cks),
+        stored = (self.ck, self.cv) if cold == "i8" else (OC.pack_int4(self.ck), OC.pack_int4(self.cv))
+        for t, a in ((self.cold.k_cache, stored[0]), (self.cold.v_cache, stored[1]), (self.cold.k_scale, self.cks),
                      (self.cold.v_scale, self.cvs), (self.hotp.k_cache, self.hk), (self.hotp.v_cache, self.hv)):
             t.copy_(torch.from_numpy(a))
         self.qd = torch.from_numpy(self.q).to(DEV)
@@ -125,14 +164,14 @@ class MixedBatch:
 EDGE = [1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 511, 512, 513, 1000]
 
 
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D,cold", [(64, "i8"), (128, "i8"), (128, "i4")])
 @pytest.mark.parametrize("q", ["f16", "f32"])
-def test_decode_mixed_matches_the_oracle(D, q):
-    print(f"mixed decode D={D} q={q}", flush=True)
-    b = MixedBatch(EDGE, 4, D, seed=71 + D, q=q)
+def test_decode_mixed_matches_the_oracle(D, q, cold):
+    print(f"mixed decode D={D} q={q} cold={cold}", flush=True)
+    b = MixedBatch(EDGE, 4, D, seed=71 + D, q=q, cold=cold)
     ref = b.oracle()
     for ptok in (0, 16, 64, 512):
-        assert_close(b.gpu(ptok), ref, F16_ATOL, F16_RTOL, f"mixed D={D} q={q} ptok={ptok}")
+        assert_close(b.gpu(ptok), ref, F16_ATOL, F16_RTOL, f"mixed D={D} q={q} cold={cold} ptok={ptok}")
     order = torch.from_numpy(np.argsort(-np.array(EDGE), kind="stable").astype(np.int32)).to(DEV)
     assert np.array_equal(b.gpu(0, order).view(np.uint16 if q == "f16" else np.uint32),
                           b.gpu(0).view(np.uint16 if q == "f16" else np.uint32))
@@ -163,8 +202,8 @@ def test_decode_mixed_flags_a_bad_hot_block_and_rejects_bad_pools():
         pk.pa_demote_blocks(other, b.cold, torch.zeros((1, 2), dtype=torch.int32, device=DEV))
 
 
-@pytest.mark.parametrize("ptok", [0, 64])
-def test_engine_steps_match_the_oracle_bit_for_bit(ptok):
+@pytest.mark.parametrize("ptok,cold", [(0, "i8"), (64, "i8"), (0, "i4"), (64, "i4")])
+def test_engine_steps_match_the_oracle_bit_for_bit(ptok, cold):
     # Prefill, a fork, then 40 steps (every sequence crosses block boundaries,
     # so blocks get demoted): cold codes and scales, hot rows and tables must
     # equal the oracle's bit for bit, and outputs the oracle's attention.
@@ -174,7 +213,10 @@ def test_engine_steps_match_the_oracle_bit_for_bit(ptok):
     seed, H, D, NC, NH, steps = 74, 4, 128, 120, 10, 40
     ctx0 = [int(c) for c in W.rng(seed, W.STREAM_CTX).integers(1, 200, size=5)]
     co, ho = W.free_order(seed, NC), W.free_order(seed + 1, NH)
-    eng = MixedDecodeEngine(NC, NH, H, D, 6, 32, cold_order=co, hot_order=ho, device=DEV, partition_tokens=ptok)
+    eng = MixedDecodeEngine(NC, NH, H, D, 6, 32, cold_order=co, hot_order=ho, device=DEV, partition_tokens=ptok,
+                            cold_dtype=pk.PA_I8 if cold == "i8" else pk.PA_I4)
+    qmax = 127 if cold == "i8" else 7
+    codes = (lambda t: t) if cold == "i8" else OC.unpack_int4
     obm = OM.MixedBlockManager(NC, NH, co, ho)
     ck, cv = np.zeros((NC, H, 16, D), np.int8), np.zeros((NC, H, 16, D), np.int8)
     cks, cvs = np.zeros((NC, H), np.float16), np.zeros((NC, H), np.float16)
@@ -185,13 +227,13 @@ def test_engine_steps_match_the_oracle_bit_for_bit(ptok):
         eng.add_sequence(s, K, V)
         cs, hs = obm.add_seq(s, c)
         Kh, Vh = K.cpu().numpy(), V.cpu().numpy()
-        OC.write_kv_int8(ck, cks, cv, cvs, Kh.astype(np.float32), Vh.astype(np.float32), cs)
+        OC.write_kv_int8(ck, cks, cv, cvs, Kh.astype(np.float32), Vh.astype(np.float32), cs, qmax=qmax)
         OC.write_kv(hk, hv, Kh, Vh, hs)
     eng.fork(2, 5)
     src, dst = obm.fork(2, 5)
     OC.copy_blocks([hk, hv], [(src, dst)])
     seqs = np.arange(6)
-    print(f"mixed engine ptok={ptok} ctx0={ctx0}", flush=True)
+    print(f"mixed engine ptok={ptok} cold={cold} ctx0={ctx0}", flush=True)
     for t in range(steps):
         kn = W.normal_torch((6, H, D), seed, W.STREAM_KNEW, t, dtype=torch.float16, device=DEV)
         vn = W.normal_torch((6, H, D), seed, W.STREAM_VNEW, t, dtype=torch.float16, device=DEV)
@@ -200,7 +242,7 @@ def test_engine_steps_match_the_oracle_bit_for_bit(ptok):
         eng.step(seqs, kn, vn, q, out)
         res = [obm.append(int(s)) for s in seqs]
         M_pairs = [(a, b) for _, a, b in res if a >= 0]
-        OM.demote(hk, hv, ck, cks, cv, cvs, M_pairs)
+        OM.demote(hk, hv, ck, cks, cv, cvs, M_pairs, qmax=qmax)
         OC.write_kv(hk, hv, kn.cpu().numpy(), vn.cpu().numpy(), [r[0] for r in res])
         if t % 13 == 12 or t == steps - 1:
             torch.cuda.synchronize()
@@ -208,8 +250,9 @@ def test_engine_steps_match_the_oracle_bit_for_bit(ptok):
             tabs, hot, ctx = obm.export(list(seqs), 32)
             ref = OM.decode(q.cpu().numpy(), ck, cks, cv, cvs, hk, hv, tabs, hot, ctx)
             assert_close(out.cpu().numpy(), ref, F16_ATOL, F16_RTOL, f"step {t}")
-            assert np.array_equal(eng.cold.k_cache.cpu().numpy(), ck)
-            assert np.array_equal(eng.cold.v_cache.cpu().numpy(), cv)
+            live = np.unique(tabs[tabs >= 0])            # blocks never written read -8 as int4
+            assert np.array_equal(codes(eng.cold.k_cache.cpu().numpy())[live], ck[live])
+            assert np.array_equal(codes(eng.cold.v_cache.cpu().numpy())[live], cv[live])
             assert np.array_equal(eng.cold.k_scale.cpu().numpy().view(np.uint16), cks.view(np.uint16))
             assert np.array_equal(eng.hot.k_cache.cpu().numpy().view(np.uint16), hk.view(np.uint16))
             nt, nh, nc = eng.mbm.export(seqs, 32)
