@@ -103,8 +103,7 @@ typedef struct pa_pool pa_pool;
 /* Bytes the caller must allocate for one of K or V (*kv_bytes) and for one of
  * the scale arrays (*scale_bytes, 0 unless kv_dtype is PA_I8 or PA_I4).
  * Errors: PA_ERR_INVALID_ARG (null outputs, non-positive sizes),
- * PA_ERR_UNSUPPORTED (block_size not 16/32/64, head_dim not 64/128, or PA_I4
- * with head_dim other than 128). */
+ * PA_ERR_UNSUPPORTED (block_size not 16/32/64, head_dim not 64/128). */
 pa_status pa_pool_bytes(int32_t num_blocks, int32_t block_size, int32_t num_heads,
                         int32_t head_dim, pa_dtype kv_dtype, int64_t* kv_bytes,
                         int64_t* scale_bytes);

@@ -86,8 +86,6 @@ pa_status check_geometry(const char* fn, int32_t num_blocks, int32_t block_size,
                 block_size, head_dim);
   if (kv_dtype != PA_F32 && kv_dtype != PA_F16 && kv_dtype != PA_I8 && kv_dtype != PA_I4)
     return fail(PA_ERR_UNSUPPORTED, "%s: kv dtype %d", fn, int(kv_dtype));
-  if (kv_dtype == PA_I4 && head_dim != 128)
-    return fail(PA_ERR_UNSUPPORTED, "%s: int4 pools need head_dim 128 (got %d)", fn, head_dim);
   return PA_OK;
 }
 

@@ -159,17 +159,18 @@ __global__ __launch_bounds__(kThreads) void write_kv_i8_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// int4 pools (head_dim 128): the int8 group rule with codes in [-7, 7]; a
-// row is 64 bytes, byte j holding code[2j] + 8 in its low nibble and
-// code[2j+1] + 8 in its high one, so lane l owns byte l of every row (dims
-// 2l and 2l+1). One wave per (run leader i, head h, tensor), as for int8.
-template <typename SRC>
+// int4 pools: the int8 group rule with codes in [-7, 7]; a row is D / 2
+// bytes, byte j holding code[2j] + 8 in its low nibble and code[2j+1] + 8 in
+// its high one, so lane l owns byte l of every row (dims 2l and 2l+1; at
+// D = 64 the upper half of the wave holds no byte). One wave per (run leader
+// i, head h, tensor), as for int8.
+template <typename SRC, int D>
 __global__ __launch_bounds__(kThreads) void write_kv_i4_kernel(
     const SRC* __restrict__ k_new, const SRC* __restrict__ v_new, uint8_t* __restrict__ k_pool,
     uint8_t* __restrict__ v_pool, _Float16* __restrict__ k_scale, _Float16* __restrict__ v_scale,
     const int64_t* __restrict__ slots, int n, int H, int num_blocks, int bshift, int32_t* err) {
-  constexpr int D = 128;
-  constexpr int kRowBytes = D / 2;   // == kWave: one byte per lane
+  constexpr int kRowBytes = D / 2;
+  static_assert(kRowBytes <= kWave, "one byte per lane");
   const int bs = 1 << bshift;
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t wid = int64_t(blockIdx.x) * (kThreads / kWave) + wave_uniform(threadIdx.x / kWave);
@@ -210,10 +211,13 @@ __global__ __launch_bounds__(kThreads) void write_kv_i4_kernel(
   }
   if (dup && lane == 0) flag_error(err, PA_DEV_BAD_RUN);
 
+  const bool mine = lane < kRowBytes;   // this lane owns a byte of each row
   float a = 0.f;
-  for (int r = 0; r < R; ++r) {
-    const SRC* x = src + ((i + r) * H + h) * D + 2 * lane;
-    a = fmaxf(a, fmaxf(fabsf(ld_f(x)), fabsf(ld_f(x + 1))));
+  if (mine) {
+    for (int r = 0; r < R; ++r) {
+      const SRC* x = src + ((i + r) * H + h) * D + 2 * lane;
+      a = fmaxf(a, fmaxf(fabsf(ld_f(x)), fabsf(ld_f(x + 1))));
+    }
   }
   a = wave_max(a);
   const float s_new = float(_Float16(a / 7.0f));
@@ -223,7 +227,7 @@ __global__ __launch_bounds__(kThreads) void write_kv_i4_kernel(
   uint8_t* tile = pool + (sidx << bshift) * kRowBytes;
   auto code = [](float qf) { return uint32_t(int(fminf(fmaxf(qf, -7.f), 7.f)) + 8); };
 
-  if (s_old > 0.f && s > s_old) {
+  if (s_old > 0.f && s > s_old && mine) {
     for (int o = 0; o < bs; ++o) {
       if (mask & (uint64_t(1) << o)) continue;
       uint8_t* c = tile + o * kRowBytes + lane;
@@ -233,7 +237,7 @@ __global__ __launch_bounds__(kThreads) void write_kv_i4_kernel(
       *c = uint8_t(code(lo) | (code(hi) << 4));
     }
   }
-  for (int r = 0; r < R; ++r) {
+  for (int r = 0; r < R && mine; ++r) {
     const int o = int(slots[i + r] & (bs - 1));
     const SRC* x = src + ((i + r) * H + h) * D + 2 * lane;
     float lo = 0.f, hi = 0.f;
@@ -298,8 +302,10 @@ __global__ __launch_bounds__(kThreads) void demote_kernel(const int32_t* __restr
   if (lane == 0) (is_v ? v_scale : k_scale)[int64_t(dst) * H + h] = _Float16(s);
 }
 
-// The same demotion into int4 cold blocks (head_dim 128): lane l quantises the
-// 32 values of the tile starting at l * 32 (a quarter row) into 16 bytes.
+// The same demotion into int4 cold blocks: lane l quantises the kPer values
+// of the tile starting at l * kPer into kPer / 2 bytes (32 values into 16
+// bytes at D = 128, 16 into 8 at D = 64).
+template <int D>
 __global__ __launch_bounds__(kThreads) void demote_i4_kernel(const int32_t* __restrict__ pairs, int n,
                                                              const _Float16* __restrict__ hot_k,
                                                              const _Float16* __restrict__ hot_v,
@@ -308,8 +314,8 @@ __global__ __launch_bounds__(kThreads) void demote_i4_kernel(const int32_t* __re
                                                              _Float16* __restrict__ k_scale,
                                                              _Float16* __restrict__ v_scale, int H, int num_hot,
                                                              int num_cold, int32_t* err) {
-  constexpr int kRows = 16, D = 128;
-  constexpr int kPer = kRows * D / kWave;   // 32 values per lane
+  constexpr int kRows = 16;
+  constexpr int kPer = kRows * D / kWave;   // values per lane
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t wid = int64_t(blockIdx.x) * (kThreads / kWave) + wave_uniform(threadIdx.x / kWave);
   if (wid >= int64_t(n) * H) return;
@@ -343,7 +349,10 @@ __global__ __launch_bounds__(kThreads) void demote_i4_kernel(const int32_t* __re
     bytes[e] = uint8_t(uint32_t(int(lo) + 8) | (uint32_t(int(hi) + 8) << 4));
   }
   uint8_t* y = (is_v ? cold_v : cold_k) + (int64_t(dst) * H + h) * kRows * (D / 2) + lane * (kPer / 2);
-  *reinterpret_cast<uint4*>(y) = *reinterpret_cast<const uint4*>(bytes);
+  if constexpr (kPer / 2 == 16)
+    *reinterpret_cast<uint4*>(y) = *reinterpret_cast<const uint4*>(bytes);
+  else
+    *reinterpret_cast<uint2*>(y) = *reinterpret_cast<const uint2*>(bytes);
   if (lane == 0) (is_v ? v_scale : k_scale)[int64_t(dst) * H + h] = _Float16(s);
 }
 
@@ -397,18 +406,22 @@ __global__ __launch_bounds__(kThreads) void swap_blocks_kernel(
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t w0 = int64_t(blockIdx.x) * kSwapWordsPerGroup + (threadIdx.x / kWave) * (2 * kWave) + lane;
   const int64_t w1 = w0 + kWave;
-  if (w1 < block_words) {
-    if (out_dir) {
-      const uint64_t x0 = dev[w0];
-      const uint64_t x1 = dev[w1];
-      __hip_atomic_store(host + w0, x0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-      __hip_atomic_store(host + w1, x1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-    } else {
-      const uint64_t x0 = __hip_atomic_load(host + w0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-      const uint64_t x1 = __hip_atomic_load(host + w1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-      dev[w0] = x0;
-      dev[w1] = x1;
-    }
+  // Blocks are whole 512-byte wave spans (the smallest row is 32 bytes and a
+  // block holds a multiple of 16 rows), so a wave's first word can be in range
+  // while its second is not: each word has its own guard.
+  const bool in0 = w0 < block_words, in1 = w1 < block_words;
+  if (out_dir) {
+    uint64_t x0 = 0, x1 = 0;
+    if (in0) x0 = dev[w0];
+    if (in1) x1 = dev[w1];
+    if (in0) __hip_atomic_store(host + w0, x0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    if (in1) __hip_atomic_store(host + w1, x1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  } else {
+    uint64_t x0 = 0, x1 = 0;
+    if (in0) x0 = __hip_atomic_load(host + w0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    if (in1) x1 = __hip_atomic_load(host + w1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    if (in0) dev[w0] = x0;
+    if (in1) dev[w1] = x1;
   }
   if (dev_ks && blockIdx.x == 0) {
     uint16_t* ds = (blockIdx.z == 0 ? dev_ks : dev_vs) + int64_t(dblk) * H;
@@ -524,11 +537,17 @@ int launch_write_i4(const pa_pool* p, const void* k_new, const void* v_new, cons
                     int32_t n, hipStream_t st) {
   const int64_t waves = int64_t(n) * p->num_heads;
   const dim3 grid(unsigned((waves + (kThreads / kWave) - 1) / (kThreads / kWave)), 2);
-  hipLaunchKernelGGL(write_kv_i4_kernel<SRC>, grid, dim3(kThreads), 0, st, static_cast<const SRC*>(k_new),
-                     static_cast<const SRC*>(v_new), static_cast<uint8_t*>(p->k_cache),
-                     static_cast<uint8_t*>(p->v_cache), static_cast<_Float16*>(p->k_scale),
-                     static_cast<_Float16*>(p->v_scale), slots, n, p->num_heads, p->num_blocks,
-                     block_shift(p->block_size), device_error_ptr());
+  auto args = [&](auto kern) {
+    hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, st, static_cast<const SRC*>(k_new),
+                       static_cast<const SRC*>(v_new), static_cast<uint8_t*>(p->k_cache),
+                       static_cast<uint8_t*>(p->v_cache), static_cast<_Float16*>(p->k_scale),
+                       static_cast<_Float16*>(p->v_scale), slots, n, p->num_heads, p->num_blocks,
+                       block_shift(p->block_size), device_error_ptr());
+  };
+  if (p->head_dim == 64)
+    args(write_kv_i4_kernel<SRC, 64>);
+  else
+    args(write_kv_i4_kernel<SRC, 128>);
   return int(hipGetLastError());
 }
 
@@ -560,11 +579,17 @@ int launch_demote_blocks(const pa_pool* hot, const pa_pool* cold, const int32_t*
   const int64_t waves = int64_t(n) * hot->num_heads;
   const dim3 grid(unsigned((waves + (kThreads / kWave) - 1) / (kThreads / kWave)), 2);
   if (cold->kv_dtype == PA_I4) {
-    hipLaunchKernelGGL(demote_i4_kernel, grid, dim3(kThreads), 0, static_cast<hipStream_t>(stream), pairs, n,
-                       static_cast<const _Float16*>(hot->k_cache), static_cast<const _Float16*>(hot->v_cache),
-                       static_cast<uint8_t*>(cold->k_cache), static_cast<uint8_t*>(cold->v_cache),
-                       static_cast<_Float16*>(cold->k_scale), static_cast<_Float16*>(cold->v_scale),
-                       hot->num_heads, hot->num_blocks, cold->num_blocks, device_error_ptr());
+    auto go4 = [&](auto kern) {
+      hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, static_cast<hipStream_t>(stream), pairs, n,
+                         static_cast<const _Float16*>(hot->k_cache), static_cast<const _Float16*>(hot->v_cache),
+                         static_cast<uint8_t*>(cold->k_cache), static_cast<uint8_t*>(cold->v_cache),
+                         static_cast<_Float16*>(cold->k_scale), static_cast<_Float16*>(cold->v_scale),
+                         hot->num_heads, hot->num_blocks, cold->num_blocks, device_error_ptr());
+    };
+    if (hot->head_dim == 64)
+      go4(demote_i4_kernel<64>);
+    else
+      go4(demote_i4_kernel<128>);
     return int(hipGetLastError());
   }
   auto go = [&](auto kern) {
@@ -596,7 +621,7 @@ int launch_swap_blocks(const pa_pool* p, const SwapHost& h, const int32_t* pairs
                        void* stream) {
   if (n == 0) return 0;
   const int64_t block_bytes = int64_t(p->num_heads) * p->block_size * row_bytes(p->kv_dtype, p->head_dim);
-  const int64_t words = block_bytes / 8;   // whole 1 KiB wave chunks for every supported geometry
+  const int64_t words = block_bytes / 8;   // a multiple of 64: whole 512-byte wave spans
   const dim3 grid(unsigned((words + kSwapWordsPerGroup - 1) / kSwapWordsPerGroup), unsigned(n), 2);
   hipLaunchKernelGGL(swap_blocks_kernel, grid, dim3(kThreads), 0, static_cast<hipStream_t>(stream), pairs,
                      static_cast<uint64_t*>(p->k_cache), static_cast<uint64_t*>(p->v_cache),

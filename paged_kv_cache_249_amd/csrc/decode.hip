@@ -148,7 +148,8 @@ template <typename KV>
 constexpr bool kQuantKV = std::is_same<KV, int8_t>::value || std::is_same<KV, Int4>::value;
 
 // A lane loads 16-byte chunks (int4: 8-byte chunks, 16 values, so that q and
-// the accumulators of a lane stay at 16 values each, as for int8).
+// the accumulators of a lane stay at 16 values each and the lane layout is
+// int8's at the same head_dim).
 template <typename KV, int D>
 struct Geo {
   static constexpr int kChunkBytes = std::is_same<KV, Int4>::value ? 8 : 16;
@@ -1115,12 +1116,8 @@ int launch_typed(const Params& p, int sh_count, hipStream_t st) {
 
 template <typename KV, typename QT, bool kPaged>
 int launch_d(const Params& p, int D, int sh_count, hipStream_t st) {
-  if constexpr (std::is_same<KV, Int4>::value) {
-    return launch_typed<KV, QT, 128, kPaged>(p, sh_count, st);   // int4 pools: head_dim 128 only
-  } else {
-    return D == 64 ? launch_typed<KV, QT, 64, kPaged>(p, sh_count, st)
-                   : launch_typed<KV, QT, 128, kPaged>(p, sh_count, st);
-  }
+  return D == 64 ? launch_typed<KV, QT, 64, kPaged>(p, sh_count, st)
+                 : launch_typed<KV, QT, 128, kPaged>(p, sh_count, st);
 }
 
 template <typename KV, bool kPaged>

@@ -117,15 +117,16 @@ def test_write_kv_int8_bit_exact(D, src_dtype, bs):
     assert pk.pa_check_errors() == 0
 
 
-@pytest.mark.parametrize("src_dtype,bs", [(torch.float32, 16), (torch.float16, 16), (torch.float16, 32),
-                                          (torch.float32, 64)])
-def test_write_kv_int4_bit_exact(src_dtype, bs):
+@pytest.mark.parametrize("src_dtype,bs,D", [(torch.float32, 16, 128), (torch.float16, 16, 128),
+                                            (torch.float16, 32, 128), (torch.float32, 64, 128),
+                                            (torch.float32, 16, 64), (torch.float16, 64, 64)])
+def test_write_kv_int4_bit_exact(src_dtype, bs, D):
     # The int8 sequence of calls on an int4 pool. The pool starts as random
     # bytes (stale nibbles read as codes -8..7); codes and scales must match
     # the oracle's exactly after every kind of call (prefill, partial blocks,
     # growing scales that re-code rows already in a block).
     pk = _pk()
-    D, NB, H = 128, 24, 3
+    NB, H = 24, 3
     pool, (hkb, hvb, hks, hvs) = _random_pool(pk, NB, H, D, pk.PA_I4, 9, bs)
     hk, hv = OC.unpack_int4(hkb), OC.unpack_int4(hvb)
     rng = W.rng(9, 5)
@@ -144,7 +145,7 @@ def test_write_kv_int4_bit_exact(src_dtype, bs):
         amp = 1.0 + (3.0 if ci % 4 == 3 else 0.0) + 0.1 * ci
         k_new = torch.from_numpy(W.normal_np((n, H, D), 9, 10 + ci) * amp).to(src_dtype)
         v_new = torch.from_numpy(W.normal_np((n, H, D), 9, 100 + ci) * amp).to(src_dtype)
-        print(f"int4 write call {ci} n={n} bs={bs}", flush=True)
+        print(f"int4 write call {ci} n={n} bs={bs} D={D}", flush=True)
         pk.pa_write_kv(pool, k_new.to(DEV), v_new.to(DEV), torch.from_numpy(slots).to(DEV))
         OC.write_kv_int4(hk, hks, hv, hvs, k_new.float().numpy(), v_new.float().numpy(), slots, block_size=bs)
     torch.cuda.synchronize()
@@ -160,7 +161,7 @@ def test_write_kv_int4_bit_exact(src_dtype, bs):
 
 
 @pytest.mark.parametrize("code,D,bs", [("f16", 128, 16), ("i8", 128, 16), ("f32", 64, 16), ("f16", 128, 64),
-                                       ("i8", 64, 32), ("i4", 128, 16), ("i4", 128, 64)])
+                                       ("i8", 64, 32), ("i4", 128, 16), ("i4", 128, 64), ("i4", 64, 32)])
 def test_copy_blocks_bit_exact(code, D, bs):
     pk = _pk()
     c = {"f32": pk.PA_F32, "f16": pk.PA_F16, "i8": pk.PA_I8, "i4": pk.PA_I4}[code]

@@ -203,10 +203,9 @@ def test_split_partials_match_the_oracle():
             assert_close(o[s, :, p], oo, 1e-4, 1e-4, f"o s={s} p={p}")
 
 
-def _int4_pool(pk, ctx, H, seed, bs, poison=False):
+def _int4_pool(pk, ctx, H, seed, bs, poison=False, D=128):
     """An int4 pool written by the oracle (prefill of each context in one call,
     then one token per call for the last few), uploaded as packed bytes."""
-    D = 128
     need = sum(-(-c // bs) for c in ctx)
     NB = need + 5
     order = W.free_order(seed, NB)
@@ -244,16 +243,17 @@ def _int4_pool(pk, ctx, H, seed, bs, poison=False):
     return pool, (kc, vc, ks, vs), tables, tab
 
 
-@pytest.mark.parametrize("bs,qd", [(16, "f16"), (32, "f32"), (64, "f16")])
-def test_int4_decode_matches_the_oracle(bs, qd):
+@pytest.mark.parametrize("bs,qd,D", [(16, "f16", 128), (32, "f32", 128), (64, "f16", 128), (16, "f16", 64),
+                                     (32, "f32", 64)])
+def test_int4_decode_matches_the_oracle(bs, qd, D):
     # Ragged contexts over int4 codes (scales that grew during the last
     # single-token writes included), single pass and split: the oracle
     # decodes the same codes and scales in fp64.
     pk = _pk()
     ctx = [1, 2, 15, 16, 17, 63, 64, 65, 300, 1000, 0, 513]
-    H, D, seed = 5, 128, 80 + bs
-    print(f"int4 decode bs={bs} q={qd}", flush=True)
-    pool, (kc, vc, ks, vs), tables, tab = _int4_pool(pk, ctx, H, seed, bs, poison=True)
+    H, seed = 5, 80 + bs + D
+    print(f"int4 decode bs={bs} q={qd} D={D}", flush=True)
+    pool, (kc, vc, ks, vs), tables, tab = _int4_pool(pk, ctx, H, seed, bs, poison=True, D=D)
     q = W.normal_np((len(ctx), H, D), seed, W.STREAM_Q, dtype=np.float16 if qd == "f16" else np.float32)
     ref = OA.paged_decode(q, kc, vc, tables, ctx, block_size=bs, k_scale=ks, v_scale=vs)
     qd_t = torch.from_numpy(q).to(DEV)
@@ -271,7 +271,7 @@ def test_int4_decode_matches_the_oracle(bs, qd):
         assert pk.pa_check_errors() == 0
         got = out.cpu().numpy()
         atol, rtol = (F16_ATOL, F16_RTOL) if qd == "f16" else (1e-4, 1e-4)
-        assert_close(got, ref, atol, rtol, f"int4 bs={bs} q={qd} ptok={ptok}")
+        assert_close(got, ref, atol, rtol, f"int4 bs={bs} q={qd} D={D} ptok={ptok}")
         assert not got[ctx.index(0)].any()
 
 
@@ -304,7 +304,7 @@ def _int8_stream_batch(H, D, seed, int4=False):
 
 
 @pytest.mark.parametrize("ptok", [32, 64, 128])
-@pytest.mark.parametrize("kv,D", [("f16", 128), ("f32", 64), ("i8", 128), ("i4", 128)])
+@pytest.mark.parametrize("kv,D", [("f16", 128), ("f32", 64), ("i8", 128), ("i4", 128), ("i4", 64)])
 def test_many_partitions_per_sequence(kv, D, ptok):
     # Many partitions per sequence (16 heads x 8 sequences, contexts up to
     # 4001): a workgroup streams several partitions (64 and 128 tokens) or a

@@ -61,13 +61,14 @@ def test_demote_is_bit_exact(D):
     assert torch.equal(before, cold.k_cache)
 
 
-def test_demote_int4_is_bit_exact():
+@pytest.mark.parametrize("D", [64, 128])
+def test_demote_int4_is_bit_exact(D):
     # Demotion into an int4 cold pool whose blocks start as random bytes:
     # demoted blocks hold the oracle's codes and scales, the others keep
     # their bytes.
     from oracle import cache_ops as OC
     pk = _pk()
-    NH, NC, H, D = 12, 20, 5, 128
+    NH, NC, H = 12, 20, 5
     rng = W.rng(75, D)
     hk = (rng.standard_normal((NH, H, 16, D)) * rng.uniform(0.1, 4, size=(NH, H, 1, 1))).astype(np.float16)
     hv = (rng.standard_normal((NH, H, 16, D)) * rng.uniform(0.1, 4, size=(NH, H, 1, 1))).astype(np.float16)
@@ -164,7 +165,7 @@ class MixedBatch:
 EDGE = [1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 511, 512, 513, 1000]
 
 
-@pytest.mark.parametrize("D,cold", [(64, "i8"), (128, "i8"), (128, "i4")])
+@pytest.mark.parametrize("D,cold", [(64, "i8"), (128, "i8"), (128, "i4"), (64, "i4")])
 @pytest.mark.parametrize("q", ["f16", "f32"])
 def test_decode_mixed_matches_the_oracle(D, q, cold):
     print(f"mixed decode D={D} q={q} cold={cold}", flush=True)

@@ -40,7 +40,7 @@ def _fill(t, seed):
 
 
 @pytest.mark.parametrize("code,D,bs", [("f16", 128, 16), ("i8", 128, 16), ("f32", 64, 32), ("f16", 64, 64),
-                                       ("i8", 64, 64), ("i4", 128, 16), ("i4", 128, 32)])
+                                       ("i8", 64, 64), ("i4", 128, 16), ("i4", 128, 32), ("i4", 64, 16)])
 def test_swap_blocks_bit_exact(code, D, bs):
     pk = _pk()
     c = {"f32": pk.PA_F32, "f16": pk.PA_F16, "i8": pk.PA_I8, "i4": pk.PA_I4}[code]
