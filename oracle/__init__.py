@@ -34,7 +34,8 @@ Modules:
 
 * :mod:`oracle.paging` — ``locate``, slot numbers, gather through a table.
 * :mod:`oracle.attention` — softmax(q K^T / sqrt(d)) V in fp64, partition
-  partials (m, l, o) and their log-sum-exp merge.
+  partials (m, l, o) and their log-sum-exp merge, and several new tokens of a
+  sequence attending at once (each over the context up to itself).
 * :mod:`oracle.cache_ops` — scatter of new K/V rows into slots, block copy, and
   the int8 and int4 quantise-on-write rule (int4 codes and their nibble
   layout).

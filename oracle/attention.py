@@ -136,3 +136,45 @@ def split_decode(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float,
     l = np.stack([p[1] for p in parts])
     o = np.stack([p[2] for p in parts])
     return merge_partials(m, l, o)
+
+
+def paged_prefill(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray, block_tables,
+                  context_lens, query_start, scale: float | None = None,
+                  block_size: int = 16) -> np.ndarray:
+    """Several new tokens of each sequence attend at once (float64).
+
+    The attention formula of "One Deep Concept #01", §2 Background, takes a
+    matrix of queries; during generation each token attends to the tokens
+    before it and to itself ("PagedAttention的终极用途", part 一). So when the
+    last ``n_s`` tokens of sequence ``s`` are processed together, the one at
+    position ``p = ctx_s - n_s + i`` gets exactly what decoding it alone over
+    the first ``p + 1`` tokens gives: logits of tokens after ``p`` are
+    excluded (a causal mask aligned to the end of the context).
+
+    ``q``: [N][H][D], rows ``query_start[s] .. query_start[s+1]`` belonging to
+    sequence ``s`` in position order; their K and V are already in the pools.
+    Returns [N][H][D] float64.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    N, H, D = q.shape
+    if scale is None:
+        scale = default_scale(D)
+    out = np.zeros((N, H, D), dtype=np.float64)
+    for s in range(len(context_lens)):
+        a, b = int(query_start[s]), int(query_start[s + 1])
+        n, ctx = b - a, int(context_lens[s])
+        if n == 0:
+            continue
+        if n > ctx:
+            raise ValueError("more new tokens than the context holds")
+        K = paging.gather(k_pool, block_tables[s], ctx, block_size)
+        V = paging.gather(v_pool, block_tables[s], ctx, block_size)
+        pos = ctx - n + np.arange(n)                               # [n]
+        allowed = np.arange(ctx)[None, :] <= pos[:, None]          # [n][ctx]
+        for h in range(H):
+            z = (q[a:b, h, :] @ K[:, h, :].T) * scale              # [n][ctx]
+            z = np.where(allowed, z, -np.inf)
+            e = np.exp(z - z.max(axis=1, keepdims=True))
+            w = e / e.sum(axis=1, keepdims=True)
+            out[a:b, h, :] = w @ V[:, h, :]
+    return out
