@@ -248,6 +248,38 @@ pa_status pa_decode_ordered(pa_pool* pool, const void* q, pa_dtype q_dtype, void
                             int32_t max_context_len, float sm_scale, int32_t partition_tokens,
                             void* workspace, int64_t workspace_bytes, pa_stream stream);
 
+/* Several new tokens per sequence attending at once (a prompt, or a chunk of
+ * one). The attention formula of "One Deep Concept #01" (§2 Background) takes
+ * a matrix of queries, and each generated token attends to every earlier
+ * token and itself ("PagedAttention的终极用途", part 一). So when the last
+ * n_s = query_start[s+1] - query_start[s] tokens of sequence s are processed
+ * together, row query_start[s] + i (position p = context_lens[s] - n_s + i)
+ * gets exactly its own decode over tokens 0..p:
+ *     out[r][h] = sum_{t <= p} softmax_t(q[r][h] . k_t * sm_scale) v_t
+ * Their K and V must already be in the pool (pa_write_kv with the slots of
+ * positions ctx - n_s .. ctx - 1); K and V are read through block_tables as
+ * in pa_decode.
+ *
+ * q, out: device fp16 [num_rows][num_heads][head_dim], 16-byte aligned; rows
+ * of a sequence are contiguous and in position order. query_start: device
+ * int32 [num_seqs + 1], non-decreasing, query_start[num_seqs] <= num_rows.
+ * block_tables, context_lens, max_blocks, max_context_len: as pa_decode.
+ * max_query_len bounds every n_s. q_dtype and the pool must be PA_F16 (the
+ * products run on the matrix cores in fp16 with fp32 accumulation; the
+ * softmax weights are rounded to fp16 before they meet V). sm_scale <= 0
+ * selects 1/sqrt(head_dim). n_s == 0 writes nothing. On the device, n_s < 0,
+ * n_s > context_lens[s], n_s > max_query_len, context_lens[s] >
+ * max_context_len or rows outside [0, num_rows) flag PA_DEV_BAD_CONTEXT and
+ * leave that sequence's rows unwritten; a table entry outside the pool flags
+ * PA_DEV_BAD_TABLE_ENTRY and block 0 is read in its place.
+ * Errors: PA_ERR_INVALID_ARG (null pointers, misalignment, bad sizes),
+ * PA_ERR_UNSUPPORTED (non-fp16 pool or q), PA_ERR_HIP. */
+pa_status pa_prefill(pa_pool* pool, const void* q, pa_dtype q_dtype, void* out,
+                     const int32_t* query_start, int32_t num_rows, const int32_t* block_tables,
+                     int32_t max_blocks, const int32_t* context_lens, int32_t num_seqs,
+                     int32_t max_query_len, int32_t max_context_len, float sm_scale,
+                     pa_stream stream);
+
 /* pa_write_kv followed by pa_decode_ordered, in one launch, for float pools:
  * row s of k_new / v_new ([num_seqs][num_heads][head_dim], src_dtype PA_F32
  * or PA_F16) is sequence s's newest token and slot_mapping[s] (device int64)

@@ -22,7 +22,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpagedkv.so")
 
-HIP_SOURCES = ["api.hip", "decode.hip", "cache_ops.hip"]
+HIP_SOURCES = ["api.hip", "decode.hip", "cache_ops.hip", "prefill.hip"]
 CXX_SOURCES = ["block_manager.cpp", "mixed_manager.cpp"]
 
 ARCH = "gfx950"

@@ -314,6 +314,41 @@ pa_status pa_decode_ordered(pa_pool* pool, const void* q, pa_dtype q_dtype, void
   return decode_common("pa_decode", a, workspace, workspace_bytes, stream);
 }
 
+pa_status pa_prefill(pa_pool* pool, const void* q, pa_dtype q_dtype, void* out, const int32_t* query_start,
+                     int32_t num_rows, const int32_t* block_tables, int32_t max_blocks,
+                     const int32_t* context_lens, int32_t num_seqs, int32_t max_query_len,
+                     int32_t max_context_len, float sm_scale, pa_stream stream) {
+  const char* fn = "pa_prefill";
+  if (!pool) return fail(PA_ERR_INVALID_ARG, "%s: pool is NULL", fn);
+  if (pool->kv_dtype != PA_F16) return fail(PA_ERR_UNSUPPORTED, "%s: pool dtype %d (F16 only)", fn, int(pool->kv_dtype));
+  if (q_dtype != PA_F16) return fail(PA_ERR_UNSUPPORTED, "%s: q dtype %d (F16 only)", fn, int(q_dtype));
+  if (num_seqs < 0 || num_rows < 0 || max_query_len < 0 || max_context_len < 0 || max_blocks < 0)
+    return fail(PA_ERR_INVALID_ARG, "%s: negative size", fn);
+  if (int64_t(max_blocks) * pool->block_size < int64_t(max_context_len))
+    return fail(PA_ERR_INVALID_ARG, "%s: max_blocks=%d cannot hold max_context_len=%d", fn, max_blocks,
+                max_context_len);
+  if (num_seqs == 0 || max_query_len == 0) return PA_OK;
+  if (!q || !out || !query_start || !block_tables || !context_lens)
+    return fail(PA_ERR_INVALID_ARG, "%s: NULL buffer", fn);
+  if (!aligned16(q) || !aligned16(out)) return fail(PA_ERR_INVALID_ARG, "%s: q and out must be 16-byte aligned", fn);
+  if (pa::prefill_groups(num_seqs, pool->num_heads, max_query_len) > int64_t(0x7fffffff))
+    return fail(PA_ERR_INVALID_ARG, "%s: grid too large", fn);
+  pa::PrefillArgs a{};
+  a.pool = pool;
+  a.q = q;
+  a.out = out;
+  a.query_start = query_start;
+  a.num_rows = num_rows;
+  a.tables = block_tables;
+  a.max_blocks = max_blocks;
+  a.ctx = context_lens;
+  a.num_seqs = num_seqs;
+  a.max_query_len = max_query_len;
+  a.max_ctx = max_context_len;
+  a.sm_scale = (sm_scale > 0.f && !std::isinf(sm_scale)) ? sm_scale : 1.0f / std::sqrt(float(pool->head_dim));
+  return hip_status(fn, pa::launch_prefill(a, stream));
+}
+
 pa_status pa_write_decode(pa_pool* pool, const void* k_new, const void* v_new, pa_dtype src_dtype,
                           const int64_t* slot_mapping, const void* q, pa_dtype q_dtype, void* out,
                           const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens,

@@ -95,6 +95,24 @@ struct DecodeArgs {
 };
 
 int launch_decode(const DecodeArgs& a, void* stream);
+// Several new tokens per sequence (pa_prefill): fp16 pool, q and out.
+struct PrefillArgs {
+  const pa_pool* pool;
+  const void* q;
+  void* out;
+  const int32_t* query_start;  // [num_seqs + 1]
+  int32_t num_rows;            // rows of q and out
+  const int32_t* tables;
+  int32_t max_blocks;
+  const int32_t* ctx;
+  int32_t num_seqs;
+  int32_t max_query_len;
+  int32_t max_ctx;
+  float sm_scale;
+};
+// Workgroups of one pa_prefill launch.
+int64_t prefill_groups(int32_t num_seqs, int32_t num_heads, int32_t max_query_len);
+int launch_prefill(const PrefillArgs& a, void* stream);
 int launch_write_kv(const pa_pool* p, const void* k_new, const void* v_new, pa_dtype src,
                     const int64_t* slots, int32_t n, void* stream);
 int launch_copy_blocks(const pa_pool* p, const int32_t* pairs, int32_t n, void* stream);

@@ -1,0 +1,292 @@
+// Several new tokens of each sequence attending at once over paged fp16 KV.
+//
+// The attention formula of "One Deep Concept #01" (§2 Background) takes a
+// matrix of queries. When the last n tokens of a sequence are processed
+// together (their K and V already written into the pool), the token at
+// position p attends to tokens 0..p: each gets exactly its own decode over the
+// context up to itself ("PagedAttention的终极用途", part 一: a generated token
+// attends to every earlier token and itself). K and V are read through the
+// block table as in decode ("PagedAttention — 把 KV cache 当虚拟内存页来管理",
+// 实践案例 / 案例 2).
+//
+// Unlike decode, every K and V row here meets up to 16 queries, so the two
+// products are dense and run on the matrix cores (v_mfma_f32_16x16x32_f16).
+// One wave owns 16 query rows of one (sequence, head) and walks the context
+// 32 tokens at a time:
+//   S^T[t][q] = K[t] . Q[q]          two 16x16 tiles, k = head_dim in steps of 32
+//   online softmax per query column  (exp2 domain, fp32)
+//   O[q][d] += P[q][t] V[t][d]       one 16x16x32 product per 16 output columns
+// S^T's accumulator layout (lane = query column, 4 tokens per lane and lane
+// group) is exactly the A-operand layout P needs for the second product, so P
+// never leaves the registers. V is loaded so that a lane's 16-byte row chunk
+// feeds eight output tiles: output column j of tile c is dimension
+// (head_dim/16)*j + c. No LDS, no barriers: the four waves of a workgroup are
+// independent and share K and V through the caches.
+#include <hip/hip_runtime.h>
+
+#include "device_common.h"
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kPfWaves = 4;          // waves per workgroup
+constexpr int kPfRows = 16;          // query rows per wave (one MFMA tile)
+constexpr int kPfWgRows = kPfWaves * kPfRows;
+constexpr int kPfStep = 32;          // tokens per step: the k extent of one 16x16x32 product
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct PrefillParams {
+  const _Float16* q;             // [num_rows][H][D]
+  _Float16* out;                 // [num_rows][H][D]
+  const _Float16* k;             // pool [num_blocks][H][B][D]
+  const _Float16* v;
+  const int32_t* query_start;    // [S + 1]
+  const int32_t* tables;         // [S][max_blocks]
+  const int32_t* ctx;            // [S]
+  int32_t num_rows;
+  int32_t max_blocks;
+  int32_t num_heads;
+  int32_t num_blocks;
+  int32_t max_ctx;
+  int32_t max_query;
+  int32_t row_tiles;             // workgroups per (sequence, head): ceil(max_query / 64)
+  float scale_log2;              // sm_scale * log2(e)
+  int32_t* err;
+};
+
+// Element c of a row chunk of kNT halves (kNT = 8: uint4, kNT = 4: uint2).
+template <int kNT>
+using RowChunk = typename std::conditional<kNT == 8, uint4, uint2>::type;
+
+template <int kNT>
+__device__ __forceinline__ _Float16 half_at(const RowChunk<kNT>& v, int c) {
+  uint32_t w;
+  if constexpr (kNT == 8) {
+    w = c < 2 ? v.x : c < 4 ? v.y : c < 6 ? v.z : v.w;
+  } else {
+    w = c < 2 ? v.x : v.y;
+  }
+  return __builtin_bit_cast(_Float16, uint16_t((c & 1) ? (w >> 16) : (w & 0xffffu)));
+}
+
+template <int D, int BS>
+__global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(PrefillParams p) {
+  constexpr int kNT = D / 16;      // output tiles; lane column j holds dims kNT*j .. kNT*j + kNT - 1
+  constexpr int kKS = D / 32;      // k steps of the QK product
+  constexpr int kGD = D / 4;       // dims a lane group covers in the QK product
+  using Chunk = RowChunk<kNT>;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int col = lane & 15;       // MFMA row/column index of this lane
+  const int grp = lane >> 4;       // MFMA lane group (k slice / output row quad)
+
+  // Workgroup -> (sequence, head, row tile). Workgroups are dealt to the 8
+  // XCDs round robin; remapping puts consecutive (row tile, head) items on
+  // one XCD so the row tiles of one (sequence, head) share its L2. The
+  // heaviest row tile (the last rows attend to the most tokens) goes first.
+  const int total = int(gridDim.x);
+  int id = int(blockIdx.x);
+  if ((total & 7) == 0) id = (id & 7) * (total >> 3) + (id >> 3);
+  const int tile = p.row_tiles - 1 - id % p.row_tiles;
+  const int h = (id / p.row_tiles) % p.num_heads;
+  const int s = id / (p.row_tiles * p.num_heads);
+
+  const int qa = p.query_start[s];
+  const int n = p.query_start[s + 1] - qa;
+  const int r0 = tile * kPfWgRows + wave * kPfRows;   // first chunk row of this wave
+  if (r0 >= n) {
+    if (n < 0 && tile == 0 && threadIdx.x == 0 && h == 0) flag_error(p.err, PA_DEV_BAD_CONTEXT);
+    return;
+  }
+  const int ctx = p.ctx[s];
+  if (qa < 0 || qa + n > p.num_rows || n > ctx || ctx > p.max_ctx || n > p.max_query) {
+    if (lane == 0) flag_error(p.err, PA_DEV_BAD_CONTEXT);
+    return;
+  }
+  const int last = min(r0 + kPfRows, n) - 1;           // last valid row of this wave
+  const int base_pos = ctx - n;                         // position of chunk row 0
+  const int t_end = base_pos + last + 1;                // tokens read: [0, t_end), t_end <= ctx
+  const int my_row = min(r0 + col, last);               // query row of this lane's column
+  const int my_pos = base_pos + my_row;                 // its position: tokens t <= my_pos count
+
+  // Q as the B operand of S^T = K Q^T: column my_row, dims grp*kGD + 8*kk .. +7.
+  f16x8 qv[kKS];
+  {
+    const _Float16* qrow = p.q + (int64_t(qa + my_row) * p.num_heads + h) * D + grp * kGD;
+#pragma unroll
+    for (int kk = 0; kk < kKS; ++kk) qv[kk] = *reinterpret_cast<const f16x8*>(qrow + 8 * kk);
+  }
+
+  const int32_t* trow = p.tables + int64_t(s) * p.max_blocks;
+  const int64_t head_off = int64_t(h) * BS * D;
+  const int64_t block_elems = int64_t(p.num_heads) * BS * D;
+
+  f32x4 o[kNT];
+#pragma unroll
+  for (int c = 0; c < kNT; ++c) o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY;   // running max (log2 units) of this lane's query column
+  float lsum = 0.f;      // this lane group's share of the column's weight sum
+
+  for (int t0 = 0; t0 < t_end; t0 += kPfStep) {
+    f16x8 kv[2][kKS];
+    Chunk vv[8];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      // A 16-token tile lies inside one block (B is 16, 32 or 64). A tile
+      // wholly past t_end re-reads the step's first tile; all its tokens are
+      // masked below.
+      const int tt = t0 + 16 * j < t_end ? t0 + 16 * j : t0;
+      int blk = trow[tt / BS];
+      if (unsigned(blk) >= unsigned(p.num_blocks)) {
+        if (lane == 0) flag_error(p.err, PA_DEV_BAD_TABLE_ENTRY);
+        blk = 0;
+      }
+      const int64_t tile_off = int64_t(blk) * block_elems + head_off + int64_t(tt % BS) * D;
+      const _Float16* krow = p.k + tile_off + col * D + grp * kGD;
+#pragma unroll
+      for (int kk = 0; kk < kKS; ++kk) kv[j][kk] = *reinterpret_cast<const f16x8*>(krow + 8 * kk);
+      const _Float16* vrow = p.v + tile_off + (grp * 4) * D + kNT * col;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vv[4 * j + i] = *reinterpret_cast<const Chunk*>(vrow + i * D);
+    }
+    // Rows past t_end may hold anything (unused slots of the last block):
+    // their weights are 0 and their values are zeroed so that 0 * NaN
+    // cannot reach the output.
+    if (t0 + kPfStep > t_end) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int t = t0 + 16 * (e >> 2) + grp * 4 + (e & 3);
+        if (t >= t_end) vv[e] = Chunk{};
+      }
+    }
+
+    // S^T tiles: lane holds S^T[t = 16j + 4*grp + r][q = col], r = 0..3.
+    f32x4 sc[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      sc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < kKS; ++kk)
+        sc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kv[j][kk], qv[kk], sc[j], 0, 0, 0);
+    }
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int t = t0 + 16 * (e >> 2) + grp * 4 + (e & 3);
+      x[e] = t <= my_pos ? sc[e >> 2][e & 3] * p.scale_log2 : -INFINITY;
+    }
+    float mx = x[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) mx = fmaxf(mx, x[e]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    // Token 0 counts for every query, so m_new is finite from the first step.
+    const float m_new = fmaxf(m, mx);
+    const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+    m = m_new;
+    f16x8 pa;
+    float ps = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      pa[e] = _Float16(__builtin_amdgcn_exp2f(x[e] - m_new));
+      ps += float(pa[e]);   // the weights the product below applies
+    }
+    lsum = lsum * alpha + ps;
+
+    // O rows are 4*grp + r: fetch their rescale factors from the lanes whose
+    // column is that row.
+    float ar[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) ar[r] = __shfl(alpha, grp * 4 + r, 64);
+#pragma unroll
+    for (int c = 0; c < kNT; ++c) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[c][r] *= ar[r];
+    }
+    // P (A operand: row = this lane's query column, k = the lane's 8 tokens)
+    // times V (B operand: column j of tile c = dim kNT*j + c, the same 8 tokens).
+#pragma unroll
+    for (int c = 0; c < kNT; ++c) {
+      f16x8 vb;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) vb[e] = half_at<kNT>(vv[e], c);
+      o[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, vb, o[c], 0, 0, 0);
+    }
+  }
+
+  lsum += __shfl_xor(lsum, 16, 64);
+  lsum += __shfl_xor(lsum, 32, 64);
+  const float inv = 1.f / lsum;   // >= 1 before the inverse: the max token weighs 1
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float ir = __shfl(inv, grp * 4 + r, 64);
+    const int row = r0 + grp * 4 + r;
+    if (row < n) {
+      uint32_t w[kNT / 2];
+#pragma unroll
+      for (int c = 0; c < kNT; c += 2) {
+        const uint32_t lo = __builtin_bit_cast(uint16_t, _Float16(o[c][r] * ir));
+        const uint32_t hi = __builtin_bit_cast(uint16_t, _Float16(o[c + 1][r] * ir));
+        w[c / 2] = lo | (hi << 16);
+      }
+      Chunk out;
+      if constexpr (kNT == 8) out = Chunk{w[0], w[1], w[2], w[3]};
+      else out = Chunk{w[0], w[1]};
+      *reinterpret_cast<Chunk*>(p.out + (int64_t(qa + row) * p.num_heads + h) * D + kNT * col) = out;
+    }
+  }
+}
+
+template <int D, int BS>
+int launch_prefill_d(const PrefillParams& p, int64_t groups, hipStream_t st) {
+  hipLaunchKernelGGL((prefill_kernel<D, BS>), dim3(unsigned(groups)), dim3(kPfWaves * 64), 0, st, p);
+  return int(hipGetLastError());
+}
+
+template <int D>
+int launch_prefill_bs(const PrefillParams& p, int block_size, int64_t groups, hipStream_t st) {
+  switch (block_size) {
+    case 16: return launch_prefill_d<D, 16>(p, groups, st);
+    case 32: return launch_prefill_d<D, 32>(p, groups, st);
+    default: return launch_prefill_d<D, 64>(p, groups, st);
+  }
+}
+
+}  // namespace
+
+int64_t prefill_groups(int32_t num_seqs, int32_t num_heads, int32_t max_query_len) {
+  const int64_t tiles = (int64_t(max_query_len) + kPfWgRows - 1) / kPfWgRows;
+  return int64_t(num_seqs) * num_heads * tiles;
+}
+
+int launch_prefill(const PrefillArgs& a, void* stream) {
+  const int64_t groups = prefill_groups(a.num_seqs, a.pool->num_heads, a.max_query_len);
+  if (groups == 0) return 0;
+  PrefillParams p{};
+  p.q = static_cast<const _Float16*>(a.q);
+  p.out = static_cast<_Float16*>(a.out);
+  p.k = static_cast<const _Float16*>(a.pool->k_cache);
+  p.v = static_cast<const _Float16*>(a.pool->v_cache);
+  p.query_start = a.query_start;
+  p.tables = a.tables;
+  p.ctx = a.ctx;
+  p.num_rows = a.num_rows;
+  p.max_blocks = a.max_blocks;
+  p.num_heads = a.pool->num_heads;
+  p.num_blocks = a.pool->num_blocks;
+  p.max_ctx = a.max_ctx;
+  p.max_query = a.max_query_len;
+  p.row_tiles = int32_t((int64_t(a.max_query_len) + kPfWgRows - 1) / kPfWgRows);
+  p.scale_log2 = a.sm_scale * kLog2e;
+  p.err = device_error_ptr();
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (a.pool->head_dim == 64) return launch_prefill_bs<64>(p, a.pool->block_size, groups, st);
+  return launch_prefill_bs<128>(p, a.pool->block_size, groups, st);
+}
+
+}  // namespace pa
