@@ -31,6 +31,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, 8 TB/s
+MFMA_PEAK_F16_TFLOPS = 2500.0   # MI355X dense fp16 matrix-core peak, 2.5 PFLOP/s
 METRIC = "paged decode attention: KV GB/s read (% of HBM peak); decode steps·seqs/s"
 
 
@@ -653,6 +654,7 @@ def extras(eng, wl, q, ptok, dev):
     res["mixed_precision_int4_cold"] = mixed_probe(pk, W, torch, np, wl, ctx, q, t_paged, nbytes, dev,
                                                    pk.PA_I4)
     res["quantised_pools"] = quantised_probe(pk, W, torch, np, wl, [int(c) for c in ctx], q, dev)
+    res["prefill"] = prefill_probe(pk, W, torch, np, dev, H=H, D=D)
     # Streaming copy probe: achievable HBM bandwidth (read + write bytes).
     n = 1 << 30
     a = torch.empty(n, dtype=torch.uint8, device=dev)
@@ -744,6 +746,52 @@ def quantised_probe(pk, W, torch, np, wl, ctx, q, dev):
     for name in ("i8", "i4"):
         res[name]["speedup_vs_f16"] = round(res["f16"]["decode_us"] / res[name]["decode_us"], 3)
         res[name]["max_abs_diff_vs_f16"] = round(float((outs[name] - outs["f16"]).abs().max()), 5)
+    return res
+
+
+def causal_prefill_flops(ctx, nq, H, D):
+    """Flops of the attention itself for chunks of nq[s] new tokens at the end
+    of contexts ctx[s]: the token at position p scores and weights p + 1
+    tokens, 2·D flops each for q·k and for the weighted sum of v."""
+    total = 0
+    for c, n in zip(ctx, nq):
+        first = c - n + 1                      # tokens attended by the chunk's first row
+        total += (first + c) * n // 2          # sum of an arithmetic series first..c
+    return 4 * D * H * total
+
+
+def prefill_probe(pk, W, torch, np, dev, H=40, D=128, S=16, n=2048, seed=7):
+    """Paged prefill at the OPT-13B head shape: S whole prompts of n tokens
+    over scattered 16-token blocks, all rows attending causally in one launch;
+    its rate in TFLOP/s of the causal attention's flops against the fp16
+    matrix-core peak, and a chunked variant (the last 512 tokens of each)."""
+    nb = -(-n // 16)
+    NB = S * nb + 8
+    pool = pk.new_pool(NB, H, D, pk.PA_F16, device=dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    pool.k_cache.normal_(generator=g)
+    pool.v_cache.normal_(generator=g)
+    perm = W.free_order(seed, NB)
+    tab = torch.from_numpy(perm[:S * nb].reshape(S, nb).astype(np.int32)).to(dev)
+    ctx = torch.full((S,), n, dtype=torch.int32, device=dev)
+    res = {"seqs": S, "prompt_tokens": n, "heads": H, "head_dim": D,
+           "peak_tflops_fp16": MFMA_PEAK_F16_TFLOPS}
+    for name, chunk in (("whole_prompt", n), ("last_512", 512)):
+        nq = [chunk] * S
+        qs = torch.tensor([0] + list(np.cumsum(nq)), dtype=torch.int32, device=dev)
+        q = torch.randn((sum(nq), H, D), generator=g, device=dev, dtype=torch.float16)
+        out = torch.empty_like(q)
+        t = _time_calls(lambda: pk.pa_prefill(pool, q, out, qs, tab, ctx, chunk, n))
+        fl = causal_prefill_flops([n] * S, nq, H, D)
+        kv = S * n * H * D * 2 * 2
+        res[name] = {"us": round(t * 1e6, 2), "tflops": round(fl / t / 1e12, 1),
+                     "frac_of_mfma_peak": round(fl / t / 1e12 / MFMA_PEAK_F16_TFLOPS, 4),
+                     "kv_gbs_once": round(kv / t / 1e9, 1)}
+        del q, out
+    assert pk.pa_check_errors() == 0
+    del pool
+    torch.cuda.empty_cache()
     return res
 
 
