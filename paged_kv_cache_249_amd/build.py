@@ -40,6 +40,11 @@ HIP_FLAGS = [
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", f"-I{INCLUDE}", f"-I{CSRC}"]
 
 
+# Per-source extra flags. prefill.hip: matrix-core accumulators in ordinary
+# VGPRs, so the softmax rescale of the output tiles needs no AGPR moves.
+EXTRA_FLAGS = {"prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"]}
+
+
 def _run(cmd):
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -55,7 +60,7 @@ def build(verbose: bool = False, save_temps: str | None = None) -> str:
     jobs = []
     for src in HIP_SOURCES:
         obj = os.path.join(BUILD, src + ".o")
-        cmd = [HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [HIPCC, *HIP_FLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
         if save_temps:
             os.makedirs(save_temps, exist_ok=True)
             cmd += ["--save-temps"]

@@ -38,6 +38,7 @@ constexpr int kPfRows = 16;          // query rows per wave (one MFMA tile)
 constexpr int kPfWgRows = kPfWaves * kPfRows;
 constexpr int kPfStep = 32;          // tokens per step: the k extent of one 16x16x32 product
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLazy = 8.f;        // log2 headroom before the reference max moves
 
 struct PrefillParams {
   const _Float16* q;             // [num_rows][H][D]
@@ -78,10 +79,19 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(PrefillParams p)
   constexpr int kNT = D / 16;      // output tiles; lane column j holds dims kNT*j .. kNT*j + kNT - 1
   constexpr int kKS = D / 32;      // k steps of the QK product
   constexpr int kGD = D / 4;       // dims a lane group covers in the QK product
+  constexpr int kRS = D + 8;       // LDS row stride (halves): 16 bytes of padding per row
+  constexpr int kRowChunks = D / 8;                    // 16-byte chunks per K or V row
+  constexpr int kPerThr = kPfStep * kRowChunks / (kPfWaves * 64);
+  static_assert(kPerThr * kPfWaves * 64 == kPfStep * kRowChunks, "step tile must split evenly");
   using Chunk = RowChunk<kNT>;
 
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // One step's K and V rows (32 tokens), shared by the workgroup's waves.
+  __shared__ __align__(16) _Float16 lk[kPfStep * kRS];
+  __shared__ __align__(16) _Float16 lv[kPfStep * kRS];
+
+  const int tid = int(threadIdx.x);
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   const int col = lane & 15;       // MFMA row/column index of this lane
   const int grp = lane >> 4;       // MFMA lane group (k slice / output row quad)
 
@@ -96,27 +106,34 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(PrefillParams p)
   const int h = (id / p.row_tiles) % p.num_heads;
   const int s = id / (p.row_tiles * p.num_heads);
 
+  // Everything up to the loop depends on (s, tile) only, so a workgroup
+  // leaves as a whole or not at all (the loop has barriers).
   const int qa = p.query_start[s];
   const int n = p.query_start[s + 1] - qa;
-  const int r0 = tile * kPfWgRows + wave * kPfRows;   // first chunk row of this wave
-  if (r0 >= n) {
-    if (n < 0 && tile == 0 && threadIdx.x == 0 && h == 0) flag_error(p.err, PA_DEV_BAD_CONTEXT);
+  const int wg_r0 = tile * kPfWgRows;                   // first chunk row of the workgroup
+  if (wg_r0 >= n) {
+    if (n < 0 && tile == 0 && tid == 0 && h == 0) flag_error(p.err, PA_DEV_BAD_CONTEXT);
     return;
   }
   const int ctx = p.ctx[s];
   if (qa < 0 || qa + n > p.num_rows || n > ctx || ctx > p.max_ctx || n > p.max_query) {
-    if (lane == 0) flag_error(p.err, PA_DEV_BAD_CONTEXT);
+    if (tid == 0) flag_error(p.err, PA_DEV_BAD_CONTEXT);
     return;
   }
-  const int last = min(r0 + kPfRows, n) - 1;           // last valid row of this wave
   const int base_pos = ctx - n;                         // position of chunk row 0
-  const int t_end = base_pos + last + 1;                // tokens read: [0, t_end), t_end <= ctx
+  const int wg_t_end = base_pos + min(wg_r0 + kPfWgRows, n);   // tokens the workgroup reads
+  const int r0 = wg_r0 + wave * kPfRows;                // first chunk row of this wave
+  const bool active = r0 < n;
+  const int last = active ? min(r0 + kPfRows, n) - 1 : r0;      // last valid row of this wave
+  const int t_end = active ? base_pos + last + 1 : 0;   // tokens this wave attends: [0, t_end)
   const int my_row = min(r0 + col, last);               // query row of this lane's column
   const int my_pos = base_pos + my_row;                 // its position: tokens t <= my_pos count
 
   // Q as the B operand of S^T = K Q^T: column my_row, dims grp*kGD + 8*kk .. +7.
   f16x8 qv[kKS];
-  {
+#pragma unroll
+  for (int kk = 0; kk < kKS; ++kk) qv[kk] = f16x8{};
+  if (active) {
     const _Float16* qrow = p.q + (int64_t(qa + my_row) * p.num_heads + h) * D + grp * kGD;
 #pragma unroll
     for (int kk = 0; kk < kKS; ++kk) qv[kk] = *reinterpret_cast<const f16x8*>(qrow + 8 * kk);
@@ -126,88 +143,134 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(PrefillParams p)
   const int64_t head_off = int64_t(h) * BS * D;
   const int64_t block_elems = int64_t(p.num_heads) * BS * D;
 
+  // Staging: thread tid moves 16-byte chunks tid + 256 j of the step's K and
+  // V rows (row c / kRowChunks, chunk c % kRowChunks). Rows at or past the
+  // workgroup's last token are zero: no table entry past it is read, and no
+  // unused slot of a last block reaches the products.
+  uint4 sk[kPerThr], sv[kPerThr];
+  auto load_chunk = [&](int j, int tt) {
+    const int c = tid + j * kPfWaves * 64;
+    const int blk = trow[tt / BS];
+    if (unsigned(blk) < unsigned(p.num_blocks)) {
+      const int64_t off = int64_t(blk) * block_elems + head_off + int64_t(tt % BS) * D + (c % kRowChunks) * 8;
+      sk[j] = *reinterpret_cast<const uint4*>(p.k + off);
+      sv[j] = *reinterpret_cast<const uint4*>(p.v + off);
+    } else {
+      flag_error(p.err, PA_DEV_BAD_TABLE_ENTRY);
+      sk[j] = uint4{0u, 0u, 0u, 0u};
+      sv[j] = uint4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto load_step = [&](int t0) {
+    if (t0 + kPfStep <= wg_t_end) {  // workgroup-uniform: every row of the step is a token
+#pragma unroll
+      for (int j = 0; j < kPerThr; ++j) load_chunk(j, t0 + (tid + j * kPfWaves * 64) / kRowChunks);
+    } else {
+#pragma unroll
+      for (int j = 0; j < kPerThr; ++j) {
+        const int tt = t0 + (tid + j * kPfWaves * 64) / kRowChunks;
+        if (tt < wg_t_end) {
+          load_chunk(j, tt);
+        } else {
+          sk[j] = uint4{0u, 0u, 0u, 0u};
+          sv[j] = uint4{0u, 0u, 0u, 0u};
+        }
+      }
+    }
+  };
+  auto store_step = [&]() {
+#pragma unroll
+    for (int j = 0; j < kPerThr; ++j) {
+      const int c = tid + j * kPfWaves * 64;
+      const int at = (c / kRowChunks) * kRS + (c % kRowChunks) * 8;
+      *reinterpret_cast<uint4*>(lk + at) = sk[j];
+      *reinterpret_cast<uint4*>(lv + at) = sv[j];
+    }
+  };
+
   f32x4 o[kNT];
 #pragma unroll
   for (int c = 0; c < kNT; ++c) o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY;   // running max (log2 units) of this lane's query column
-  float lsum = 0.f;      // this lane group's share of the column's weight sum
+  // Weight sums of rows 4*grp + r (P times a ones operand: every column of
+  // this tile holds its row's sum), rescaled together with o.
+  f32x4 osum = f32x4{0.f, 0.f, 0.f, 0.f};
+  f16x8 ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = _Float16(1.f);
+  // Reference max (log2 units) of this lane's query column. Weights are
+  // exp2(logit - m); m moves (and o, osum are rescaled) only when a logit
+  // exceeds it by more than kLazy, so weights stay below 2^kLazy and most
+  // steps skip the rescale. Any reference gives the same quotient o / osum.
+  float m = -INFINITY;
+  const float c2 = p.scale_log2;
+  const int first_pos = base_pos + r0;                  // smallest position among the wave's rows
+  const int xor16 = (lane ^ 16) << 2;                   // ds_bpermute byte addresses of the lanes
+  const int xor32 = (lane ^ 32) << 2;                   // with the same column in other lane groups
 
-  for (int t0 = 0; t0 < t_end; t0 += kPfStep) {
-    f16x8 kv[2][kKS];
-    Chunk vv[8];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      // A 16-token tile lies inside one block (B is 16, 32 or 64). A tile
-      // wholly past t_end re-reads the step's first tile; all its tokens are
-      // masked below.
-      const int tt = t0 + 16 * j < t_end ? t0 + 16 * j : t0;
-      int blk = trow[tt / BS];
-      if (unsigned(blk) >= unsigned(p.num_blocks)) {
-        if (lane == 0) flag_error(p.err, PA_DEV_BAD_TABLE_ENTRY);
-        blk = 0;
-      }
-      const int64_t tile_off = int64_t(blk) * block_elems + head_off + int64_t(tt % BS) * D;
-      const _Float16* krow = p.k + tile_off + col * D + grp * kGD;
-#pragma unroll
-      for (int kk = 0; kk < kKS; ++kk) kv[j][kk] = *reinterpret_cast<const f16x8*>(krow + 8 * kk);
-      const _Float16* vrow = p.v + tile_off + (grp * 4) * D + kNT * col;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) vv[4 * j + i] = *reinterpret_cast<const Chunk*>(vrow + i * D);
-    }
-    // Rows past t_end may hold anything (unused slots of the last block):
-    // their weights are 0 and their values are zeroed so that 0 * NaN
-    // cannot reach the output.
-    if (t0 + kPfStep > t_end) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int t = t0 + 16 * (e >> 2) + grp * 4 + (e & 3);
-        if (t >= t_end) vv[e] = Chunk{};
-      }
-    }
+  load_step(0);
+  for (int t0 = 0; t0 < wg_t_end; t0 += kPfStep) {
+    __syncthreads();                 // every wave is done with the previous step's rows
+    store_step();
+    __syncthreads();                 // this step's rows are in LDS
+    if (t0 + kPfStep < wg_t_end) load_step(t0 + kPfStep);   // in flight during the products
+    if (t0 >= t_end) continue;       // wave-uniform: this wave's rows are done
 
-    // S^T tiles: lane holds S^T[t = 16j + 4*grp + r][q = col], r = 0..3.
+    // S^T tiles: lane holds S^T[t = 16j + 4*grp + r][q = col], r = 0..3 (raw q.k).
     f32x4 sc[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       sc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < kKS; ++kk)
-        sc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kv[j][kk], qv[kk], sc[j], 0, 0, 0);
+      for (int kk = 0; kk < kKS; ++kk) {
+        const f16x8 kv = *reinterpret_cast<const f16x8*>(lk + (16 * j + col) * kRS + grp * kGD + 8 * kk);
+        sc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kv, qv[kk], sc[j], 0, 0, 0);
+      }
     }
+    // V rows t = 16*(e/4) + 4*grp + e%4, this lane's kNT dims.
+    Chunk vv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      vv[e] = *reinterpret_cast<const Chunk*>(lv + (16 * (e >> 2) + grp * 4 + (e & 3)) * kRS + kNT * col);
+
     float x[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int t = t0 + 16 * (e >> 2) + grp * 4 + (e & 3);
-      x[e] = t <= my_pos ? sc[e >> 2][e & 3] * p.scale_log2 : -INFINITY;
+    for (int e = 0; e < 8; ++e) x[e] = sc[e >> 2][e & 3];
+    // Only steps reaching past the wave's first position need the causal
+    // mask (it also hides the zero rows past the workgroup's last token).
+    if (t0 + kPfStep - 1 > first_pos) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int t = t0 + 16 * (e >> 2) + grp * 4 + (e & 3);
+        if (t > my_pos) x[e] = -INFINITY;
+      }
     }
     float mx = x[0];
 #pragma unroll
     for (int e = 1; e < 8; ++e) mx = fmaxf(mx, x[e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    // Token 0 counts for every query, so m_new is finite from the first step.
-    const float m_new = fmaxf(m, mx);
-    const float alpha = __builtin_amdgcn_exp2f(m - m_new);
-    m = m_new;
+    mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_ds_bpermute(xor16, __float_as_int(mx))));
+    mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_ds_bpermute(xor32, __float_as_int(mx))));
+    const float ms = mx * c2;        // the column's step max in log2 units (-inf if all masked)
+    // Token 0 is visible to every query in the first step, so every m is
+    // finite after it and the first step always rescales (from m = -inf).
+    if (__any(ms > m + kLazy)) {
+      const float m_new = fmaxf(m, ms);
+      const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+      m = m_new;
+      // O rows are 4*grp + r: their factors live in the lanes whose column is that row.
+      float ar[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ar[r] = __shfl(alpha, grp * 4 + r, 64);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        osum[r] *= ar[r];
+#pragma unroll
+        for (int c = 0; c < kNT; ++c) o[c][r] *= ar[r];
+      }
+    }
     f16x8 pa;
-    float ps = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      pa[e] = _Float16(__builtin_amdgcn_exp2f(x[e] - m_new));
-      ps += float(pa[e]);   // the weights the product below applies
-    }
-    lsum = lsum * alpha + ps;
-
-    // O rows are 4*grp + r: fetch their rescale factors from the lanes whose
-    // column is that row.
-    float ar[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) ar[r] = __shfl(alpha, grp * 4 + r, 64);
-#pragma unroll
-    for (int c = 0; c < kNT; ++c) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) o[c][r] *= ar[r];
-    }
+    for (int e = 0; e < 8; ++e) pa[e] = _Float16(__builtin_amdgcn_exp2f(__builtin_fmaf(x[e], c2, -m)));
+    osum = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, ones, osum, 0, 0, 0);
     // P (A operand: row = this lane's query column, k = the lane's 8 tokens)
     // times V (B operand: column j of tile c = dim kNT*j + c, the same 8 tokens).
 #pragma unroll
@@ -218,13 +281,12 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(PrefillParams p)
       o[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, vb, o[c], 0, 0, 0);
     }
   }
+  if (!active) return;
 
-  lsum += __shfl_xor(lsum, 16, 64);
-  lsum += __shfl_xor(lsum, 32, 64);
-  const float inv = 1.f / lsum;   // >= 1 before the inverse: the max token weighs 1
+  // osum[r] >= 1: the largest weight applied is at least exp2(0).
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const float ir = __shfl(inv, grp * 4 + r, 64);
+    const float ir = 1.f / osum[r];
     const int row = r0 + grp * 4 + r;
     if (row < n) {
       uint32_t w[kNT / 2];

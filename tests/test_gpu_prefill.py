@@ -35,7 +35,7 @@ class Chunks:
     """Sequences whose whole contexts sit in a NaN-poisoned fp16 pool (seeded
     placement), with queries for the last ``nq[s]`` tokens of each."""
 
-    def __init__(self, ctx, nq, H, D, bs=16, seed=0, write_chunk_on_gpu=False):
+    def __init__(self, ctx, nq, H, D, bs=16, seed=0, write_chunk_on_gpu=False, key_gain=None):
         pk = _pk()
         self.ctx, self.nq, self.H, self.D, self.bs = list(ctx), list(nq), H, D, bs
         nbs = [-(-c // bs) for c in ctx]
@@ -58,6 +58,10 @@ class Chunks:
         for s, c in enumerate(ctx):
             K = W.normal_np((c, H, D), seed, W.STREAM_K, s, dtype=np.float16)
             V = W.normal_np((c, H, D), seed, W.STREAM_V, s, dtype=np.float16)
+            if key_gain is not None:
+                # Keys scaled by a gain per position (then rounded to fp16 like the pool).
+                K = (K.astype(np.float32) * key_gain(np.arange(c))[:, None, None].astype(np.float32)
+                     ).astype(np.float16)
             slots = OP.slots(c, self.tables[s], bs)
             OC.write_kv(self.k_pool, self.v_pool, K, V, slots, block_size=bs)
             old = c - nq[s] if write_chunk_on_gpu else c
@@ -129,6 +133,24 @@ def test_single_rows_equal_decode():
     got = b.gpu()
     ref = OA.paged_decode(b.q, b.k_pool, b.v_pool, b.tables, b.ctx)
     assert_close(got, ref, "single rows")
+
+
+@pytest.mark.parametrize("direction", ["rising", "falling"])
+def test_logits_whose_max_moves_many_times(direction):
+    # Keys whose scale grows (or shrinks) with position: each row's running
+    # max of q.k climbs by far more than 2^8 in log2 units over its context,
+    # so the kernel's reference max moves and the tiles are rescaled many
+    # times (rising), or the first step already holds the max (falling).
+    c = 700
+    gain = (lambda t: 1.0 + t / 16.0) if direction == "rising" else (lambda t: 1.0 + (c - t) / 16.0)
+    b = Chunks([c, 333, 96], [c, 200, 96], H=3, D=128, seed=17, key_gain=gain)
+    got = b.gpu()
+    ref = b.oracle()
+    # Logits reach far beyond 8 (log2 units beyond 11): confirm the inputs do
+    # what the test needs (block 10 holds tokens 160..175, gain 11 or 34).
+    z = b.q[:c, 0].astype(np.float64) @ b.k_pool[b.tables[0][10], 0].astype(np.float64).T / np.sqrt(128)
+    assert np.abs(z).max() > 8
+    assert_close(got, ref, direction)
 
 
 def test_bad_lengths_flag_and_leave_rows_unwritten():
