@@ -34,7 +34,8 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kPfWaves = 4;          // waves per workgroup
-constexpr int kPfRows = 16;          // query rows per wave (one MFMA tile)
+constexpr int kPfTiles = 2;          // 16-row query tiles per wave
+constexpr int kPfRows = 16 * kPfTiles;   // query rows per wave
 constexpr int kPfWgRows = kPfWaves * kPfRows;
 constexpr int kPfStep = 32;          // tokens per step: the k extent of one 16x16x32 product
 constexpr float kLog2e = 1.4426950408889634f;
@@ -72,6 +73,17 @@ __device__ __forceinline__ _Float16 half_at(const RowChunk<kNT>& v, int c) {
     w = c < 2 ? v.x : v.y;
   }
   return __builtin_bit_cast(_Float16, uint16_t((c & 1) ? (w >> 16) : (w & 0xffffu)));
+}
+
+// Max over the four lanes of a column (lanes l, l^16, l^32, l^48). With both
+// operands the same value, permlane16_swap returns rows (0,0,2,2) and
+// (1,1,3,3) of it, and permlane32_swap the lower and the upper 32 lanes each
+// twice, so two swaps and two maxima reduce across the rows without LDS.
+__device__ __forceinline__ float col_max(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 template <int D, int BS>
@@ -126,17 +138,25 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(PrefillParams p)
   const bool active = r0 < n;
   const int last = active ? min(r0 + kPfRows, n) - 1 : r0;      // last valid row of this wave
   const int t_end = active ? base_pos + last + 1 : 0;   // tokens this wave attends: [0, t_end)
-  const int my_row = min(r0 + col, last);               // query row of this lane's column
-  const int my_pos = base_pos + my_row;                 // its position: tokens t <= my_pos count
+  // Query tile qt of the wave holds rows r0 + 16 qt .. + 15; lane column col
+  // is row min(r0 + 16 qt + col, last) (rows past the chunk repeat its last
+  // row and are never stored); my_pos is that row's position.
+  int my_pos[kPfTiles];
+#pragma unroll
+  for (int qt = 0; qt < kPfTiles; ++qt) my_pos[qt] = base_pos + min(r0 + 16 * qt + col, last);
 
-  // Q as the B operand of S^T = K Q^T: column my_row, dims grp*kGD + 8*kk .. +7.
-  f16x8 qv[kKS];
+  // Q as the B operand of S^T = K Q^T: this lane's row, dims grp*kGD + 8*kk .. +7.
+  f16x8 qv[kPfTiles][kKS];
 #pragma unroll
-  for (int kk = 0; kk < kKS; ++kk) qv[kk] = f16x8{};
-  if (active) {
-    const _Float16* qrow = p.q + (int64_t(qa + my_row) * p.num_heads + h) * D + grp * kGD;
+  for (int qt = 0; qt < kPfTiles; ++qt) {
 #pragma unroll
-    for (int kk = 0; kk < kKS; ++kk) qv[kk] = *reinterpret_cast<const f16x8*>(qrow + 8 * kk);
+    for (int kk = 0; kk < kKS; ++kk) qv[qt][kk] = f16x8{};
+    if (active) {
+      const int row = my_pos[qt] - base_pos;
+      const _Float16* qrow = p.q + (int64_t(qa + row) * p.num_heads + h) * D + grp * kGD;
+#pragma unroll
+      for (int kk = 0; kk < kKS; ++kk) qv[qt][kk] = *reinterpret_cast<const f16x8*>(qrow + 8 * kk);
+    }
   }
 
   const int32_t* trow = p.tables + int64_t(s) * p.max_blocks;
@@ -188,24 +208,26 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(PrefillParams p)
     }
   };
 
-  f32x4 o[kNT];
-#pragma unroll
-  for (int c = 0; c < kNT; ++c) o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 o[kPfTiles][kNT];
   // Weight sums of rows 4*grp + r (P times a ones operand: every column of
   // this tile holds its row's sum), rescaled together with o.
-  f32x4 osum = f32x4{0.f, 0.f, 0.f, 0.f};
-  f16x8 ones;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) ones[e] = _Float16(1.f);
+  f32x4 osum[kPfTiles];
   // Reference max (log2 units) of this lane's query column. Weights are
   // exp2(logit - m); m moves (and o, osum are rescaled) only when a logit
   // exceeds it by more than kLazy, so weights stay below 2^kLazy and most
   // steps skip the rescale. Any reference gives the same quotient o / osum.
-  float m = -INFINITY;
+  float m[kPfTiles];
+#pragma unroll
+  for (int qt = 0; qt < kPfTiles; ++qt) {
+#pragma unroll
+    for (int c = 0; c < kNT; ++c) o[qt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    osum[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m[qt] = -INFINITY;
+  }
+  f16x8 ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = _Float16(1.f);
   const float c2 = p.scale_log2;
-  const int first_pos = base_pos + r0;                  // smallest position among the wave's rows
-  const int xor16 = (lane ^ 16) << 2;                   // ds_bpermute byte addresses of the lanes
-  const int xor32 = (lane ^ 32) << 2;                   // with the same column in other lane groups
 
   load_step(0);
   for (int t0 = 0; t0 < wg_t_end; t0 += kPfStep) {
@@ -215,15 +237,19 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(PrefillParams p)
     if (t0 + kPfStep < wg_t_end) load_step(t0 + kPfStep);   // in flight during the products
     if (t0 >= t_end) continue;       // wave-uniform: this wave's rows are done
 
-    // S^T tiles: lane holds S^T[t = 16j + 4*grp + r][q = col], r = 0..3 (raw q.k).
-    f32x4 sc[2];
+    // S^T tiles: lane holds S^T[t = 16j + 4*grp + r][q = col] of query tile
+    // qt, r = 0..3 (raw q.k). Each K operand serves both query tiles.
+    f32x4 sc[kPfTiles][2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      sc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int qt = 0; qt < kPfTiles; ++qt) sc[qt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < kKS; ++kk) {
         const f16x8 kv = *reinterpret_cast<const f16x8*>(lk + (16 * j + col) * kRS + grp * kGD + 8 * kk);
-        sc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kv, qv[kk], sc[j], 0, 0, 0);
+#pragma unroll
+        for (int qt = 0; qt < kPfTiles; ++qt)
+          sc[qt][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kv, qv[qt][kk], sc[qt][j], 0, 0, 0);
       }
     }
     // V rows t = 16*(e/4) + 4*grp + e%4, this lane's kNT dims.
@@ -232,45 +258,48 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(PrefillParams p)
     for (int e = 0; e < 8; ++e)
       vv[e] = *reinterpret_cast<const Chunk*>(lv + (16 * (e >> 2) + grp * 4 + (e & 3)) * kRS + kNT * col);
 
-    float x[8];
+    f16x8 pa[kPfTiles];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = sc[e >> 2][e & 3];
-    // Only steps reaching past the wave's first position need the causal
-    // mask (it also hides the zero rows past the workgroup's last token).
-    if (t0 + kPfStep - 1 > first_pos) {
+    for (int qt = 0; qt < kPfTiles; ++qt) {
+      float x[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int t = t0 + 16 * (e >> 2) + grp * 4 + (e & 3);
-        if (t > my_pos) x[e] = -INFINITY;
+      for (int e = 0; e < 8; ++e) x[e] = sc[qt][e >> 2][e & 3];
+      // Only steps reaching past the tile's first position need the causal
+      // mask (it also hides the zero rows past the workgroup's last token).
+      if (t0 + kPfStep - 1 > base_pos + r0 + 16 * qt) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int t = t0 + 16 * (e >> 2) + grp * 4 + (e & 3);
+          if (t > my_pos[qt]) x[e] = -INFINITY;
+        }
       }
-    }
-    float mx = x[0];
+      float mx = x[0];
 #pragma unroll
-    for (int e = 1; e < 8; ++e) mx = fmaxf(mx, x[e]);
-    mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_ds_bpermute(xor16, __float_as_int(mx))));
-    mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_ds_bpermute(xor32, __float_as_int(mx))));
-    const float ms = mx * c2;        // the column's step max in log2 units (-inf if all masked)
-    // Token 0 is visible to every query in the first step, so every m is
-    // finite after it and the first step always rescales (from m = -inf).
-    if (__any(ms > m + kLazy)) {
-      const float m_new = fmaxf(m, ms);
-      const float alpha = __builtin_amdgcn_exp2f(m - m_new);
-      m = m_new;
-      // O rows are 4*grp + r: their factors live in the lanes whose column is that row.
-      float ar[4];
+      for (int e = 1; e < 8; ++e) mx = fmaxf(mx, x[e]);
+      mx = col_max(mx);
+      const float ms = mx * c2;      // the column's step max in log2 units (-inf if all masked)
+      // Token 0 is visible to every query in the first step, so every m is
+      // finite after it and the first step always rescales (from m = -inf).
+      if (__any(ms > m[qt] + kLazy)) {
+        const float m_new = fmaxf(m[qt], ms);
+        const float alpha = __builtin_amdgcn_exp2f(m[qt] - m_new);
+        m[qt] = m_new;
+        // O rows are 4*grp + r: their factors live in the lanes whose column is that row.
+        float ar[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) ar[r] = __shfl(alpha, grp * 4 + r, 64);
+        for (int r = 0; r < 4; ++r) ar[r] = __shfl(alpha, grp * 4 + r, 64);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        osum[r] *= ar[r];
+        for (int r = 0; r < 4; ++r) {
+          osum[qt][r] *= ar[r];
 #pragma unroll
-        for (int c = 0; c < kNT; ++c) o[c][r] *= ar[r];
+          for (int c = 0; c < kNT; ++c) o[qt][c][r] *= ar[r];
+        }
       }
-    }
-    f16x8 pa;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) pa[e] = _Float16(__builtin_amdgcn_exp2f(__builtin_fmaf(x[e], c2, -m)));
-    osum = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, ones, osum, 0, 0, 0);
+      for (int e = 0; e < 8; ++e)
+        pa[qt][e] = _Float16(__builtin_amdgcn_exp2f(__builtin_fmaf(x[e], c2, -m[qt])));
+      osum[qt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[qt], ones, osum[qt], 0, 0, 0);
+    }
     // P (A operand: row = this lane's query column, k = the lane's 8 tokens)
     // times V (B operand: column j of tile c = dim kNT*j + c, the same 8 tokens).
 #pragma unroll
@@ -278,28 +307,33 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(PrefillParams p)
       f16x8 vb;
 #pragma unroll
       for (int e = 0; e < 8; ++e) vb[e] = half_at<kNT>(vv[e], c);
-      o[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, vb, o[c], 0, 0, 0);
+#pragma unroll
+      for (int qt = 0; qt < kPfTiles; ++qt)
+        o[qt][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[qt], vb, o[qt][c], 0, 0, 0);
     }
   }
   if (!active) return;
 
   // osum[r] >= 1: the largest weight applied is at least exp2(0).
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const float ir = 1.f / osum[r];
-    const int row = r0 + grp * 4 + r;
-    if (row < n) {
-      uint32_t w[kNT / 2];
+  for (int qt = 0; qt < kPfTiles; ++qt) {
 #pragma unroll
-      for (int c = 0; c < kNT; c += 2) {
-        const uint32_t lo = __builtin_bit_cast(uint16_t, _Float16(o[c][r] * ir));
-        const uint32_t hi = __builtin_bit_cast(uint16_t, _Float16(o[c + 1][r] * ir));
-        w[c / 2] = lo | (hi << 16);
+    for (int r = 0; r < 4; ++r) {
+      const float ir = 1.f / osum[qt][r];
+      const int row = r0 + 16 * qt + grp * 4 + r;
+      if (row < n) {
+        uint32_t w[kNT / 2];
+#pragma unroll
+        for (int c = 0; c < kNT; c += 2) {
+          const uint32_t lo = __builtin_bit_cast(uint16_t, _Float16(o[qt][c][r] * ir));
+          const uint32_t hi = __builtin_bit_cast(uint16_t, _Float16(o[qt][c + 1][r] * ir));
+          w[c / 2] = lo | (hi << 16);
+        }
+        Chunk out;
+        if constexpr (kNT == 8) out = Chunk{w[0], w[1], w[2], w[3]};
+        else out = Chunk{w[0], w[1]};
+        *reinterpret_cast<Chunk*>(p.out + (int64_t(qa + row) * p.num_heads + h) * D + kNT * col) = out;
       }
-      Chunk out;
-      if constexpr (kNT == 8) out = Chunk{w[0], w[1], w[2], w[3]};
-      else out = Chunk{w[0], w[1]};
-      *reinterpret_cast<Chunk*>(p.out + (int64_t(qa + row) * p.num_heads + h) * D + kNT * col) = out;
     }
   }
 }
