@@ -97,9 +97,11 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(PrefillParams p)
   static_assert(kPerThr * kPfWaves * 64 == kPfStep * kRowChunks, "step tile must split evenly");
   using Chunk = RowChunk<kNT>;
 
-  // One step's K and V rows (32 tokens), shared by the workgroup's waves.
-  __shared__ __align__(16) _Float16 lk[kPfStep * kRS];
-  __shared__ __align__(16) _Float16 lv[kPfStep * kRS];
+  // Two steps' K and V rows (32 tokens each), shared by the workgroup's
+  // waves: the products read one buffer while the next step is stored into
+  // the other.
+  __shared__ __align__(16) _Float16 lk[2][kPfStep * kRS];
+  __shared__ __align__(16) _Float16 lv[2][kPfStep * kRS];
 
   const int tid = int(threadIdx.x);
   const int lane = tid & 63;
@@ -164,47 +166,48 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(PrefillParams p)
   const int64_t block_elems = int64_t(p.num_heads) * BS * D;
 
   // Staging: thread tid moves 16-byte chunks tid + 256 j of the step's K and
-  // V rows (row c / kRowChunks, chunk c % kRowChunks). Rows at or past the
-  // workgroup's last token are zero: no table entry past it is read, and no
-  // unused slot of a last block reaches the products.
+  // V rows (row c / kRowChunks, chunk c % kRowChunks). A 16-row half of a
+  // step lies in one block (B is 16, 32 or 64 and steps start at multiples
+  // of 32), so its table entry is one value for the workgroup; the entries
+  // of the step after next are read (scalar loads) while this one streams.
+  // Rows at or past the workgroup's last token are zero: no table entry
+  // past it is read, and no unused slot of a last block reaches the products.
   uint4 sk[kPerThr], sv[kPerThr];
-  auto load_chunk = [&](int j, int tt) {
-    const int c = tid + j * kPfWaves * 64;
-    const int blk = trow[tt / BS];
-    if (unsigned(blk) < unsigned(p.num_blocks)) {
-      const int64_t off = int64_t(blk) * block_elems + head_off + int64_t(tt % BS) * D + (c % kRowChunks) * 8;
-      sk[j] = *reinterpret_cast<const uint4*>(p.k + off);
-      sv[j] = *reinterpret_cast<const uint4*>(p.v + off);
-    } else {
-      flag_error(p.err, PA_DEV_BAD_TABLE_ENTRY);
-      sk[j] = uint4{0u, 0u, 0u, 0u};
-      sv[j] = uint4{0u, 0u, 0u, 0u};
+  int tab[2] = {0, 0};               // table entries of the two halves of the next step to load
+  auto fetch_table = [&](int t0, int (&dst)[2]) {
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int t = t0 + 16 * half;
+      dst[half] = t < wg_t_end ? trow[t / BS] : 0;
     }
   };
-  auto load_step = [&](int t0) {
-    if (t0 + kPfStep <= wg_t_end) {  // workgroup-uniform: every row of the step is a token
+  auto load_step = [&](int t0, const int (&blk)[2]) {
 #pragma unroll
-      for (int j = 0; j < kPerThr; ++j) load_chunk(j, t0 + (tid + j * kPfWaves * 64) / kRowChunks);
-    } else {
-#pragma unroll
-      for (int j = 0; j < kPerThr; ++j) {
-        const int tt = t0 + (tid + j * kPfWaves * 64) / kRowChunks;
-        if (tt < wg_t_end) {
-          load_chunk(j, tt);
+    for (int j = 0; j < kPerThr; ++j) {
+      const int c = tid + j * kPfWaves * 64;
+      const int row = c / kRowChunks;
+      const int tt = t0 + row;
+      const int b = blk[row >> 4];
+      sk[j] = uint4{0u, 0u, 0u, 0u};
+      sv[j] = uint4{0u, 0u, 0u, 0u};
+      if (tt < wg_t_end) {
+        if (unsigned(b) < unsigned(p.num_blocks)) {
+          const int64_t off = int64_t(b) * block_elems + head_off + int64_t(tt % BS) * D + (c % kRowChunks) * 8;
+          sk[j] = *reinterpret_cast<const uint4*>(p.k + off);
+          sv[j] = *reinterpret_cast<const uint4*>(p.v + off);
         } else {
-          sk[j] = uint4{0u, 0u, 0u, 0u};
-          sv[j] = uint4{0u, 0u, 0u, 0u};
+          flag_error(p.err, PA_DEV_BAD_TABLE_ENTRY);
         }
       }
     }
   };
-  auto store_step = [&]() {
+  auto store_step = [&](int buf) {
 #pragma unroll
     for (int j = 0; j < kPerThr; ++j) {
       const int c = tid + j * kPfWaves * 64;
       const int at = (c / kRowChunks) * kRS + (c % kRowChunks) * 8;
-      *reinterpret_cast<uint4*>(lk + at) = sk[j];
-      *reinterpret_cast<uint4*>(lv + at) = sv[j];
+      *reinterpret_cast<uint4*>(&lk[buf][at]) = sk[j];
+      *reinterpret_cast<uint4*>(&lv[buf][at]) = sv[j];
     }
   };
 
@@ -229,88 +232,101 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(PrefillParams p)
   for (int e = 0; e < 8; ++e) ones[e] = _Float16(1.f);
   const float c2 = p.scale_log2;
 
-  load_step(0);
-  for (int t0 = 0; t0 < wg_t_end; t0 += kPfStep) {
-    __syncthreads();                 // every wave is done with the previous step's rows
-    store_step();
-    __syncthreads();                 // this step's rows are in LDS
-    if (t0 + kPfStep < wg_t_end) load_step(t0 + kPfStep);   // in flight during the products
-    if (t0 >= t_end) continue;       // wave-uniform: this wave's rows are done
-
-    // S^T tiles: lane holds S^T[t = 16j + 4*grp + r][q = col] of query tile
-    // qt, r = 0..3 (raw q.k). Each K operand serves both query tiles.
-    f32x4 sc[kPfTiles][2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-#pragma unroll
-      for (int qt = 0; qt < kPfTiles; ++qt) sc[qt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < kKS; ++kk) {
-        const f16x8 kv = *reinterpret_cast<const f16x8*>(lk + (16 * j + col) * kRS + grp * kGD + 8 * kk);
-#pragma unroll
-        for (int qt = 0; qt < kPfTiles; ++qt)
-          sc[qt][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kv, qv[qt][kk], sc[qt][j], 0, 0, 0);
-      }
+  {
+    int first[2];
+    fetch_table(0, first);
+    load_step(0, first);
+    fetch_table(kPfStep, tab);
+    store_step(0);
+  }
+  __syncthreads();
+  int buf = 0;
+  for (int t0 = 0; t0 < wg_t_end; t0 += kPfStep, buf ^= 1) {
+    const _Float16* ck = lk[buf];
+    const _Float16* cv = lv[buf];
+    const bool more = t0 + kPfStep < wg_t_end;   // workgroup-uniform
+    if (more) {
+      load_step(t0 + kPfStep, tab);            // in flight during the products
+      fetch_table(t0 + 2 * kPfStep, tab);
     }
-    // V rows t = 16*(e/4) + 4*grp + e%4, this lane's kNT dims.
-    Chunk vv[8];
+    if (t0 < t_end) {                // wave-uniform: this wave still has rows to serve
+      // S^T tiles: lane holds S^T[t = 16j + 4*grp + r][q = col] of query tile
+      // qt, r = 0..3 (raw q.k). Each K operand serves both query tiles.
+      f32x4 sc[kPfTiles][2];
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      vv[e] = *reinterpret_cast<const Chunk*>(lv + (16 * (e >> 2) + grp * 4 + (e & 3)) * kRS + kNT * col);
-
-    f16x8 pa[kPfTiles];
+      for (int j = 0; j < 2; ++j) {
 #pragma unroll
-    for (int qt = 0; qt < kPfTiles; ++qt) {
-      float x[8];
+        for (int qt = 0; qt < kPfTiles; ++qt) sc[qt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = sc[qt][e >> 2][e & 3];
-      // Only steps reaching past the tile's first position need the causal
-      // mask (it also hides the zero rows past the workgroup's last token).
-      if (t0 + kPfStep - 1 > base_pos + r0 + 16 * qt) {
+        for (int kk = 0; kk < kKS; ++kk) {
+          const f16x8 kv = *reinterpret_cast<const f16x8*>(ck + (16 * j + col) * kRS + grp * kGD + 8 * kk);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int t = t0 + 16 * (e >> 2) + grp * 4 + (e & 3);
-          if (t > my_pos[qt]) x[e] = -INFINITY;
+          for (int qt = 0; qt < kPfTiles; ++qt)
+            sc[qt][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kv, qv[qt][kk], sc[qt][j], 0, 0, 0);
         }
       }
-      float mx = x[0];
-#pragma unroll
-      for (int e = 1; e < 8; ++e) mx = fmaxf(mx, x[e]);
-      mx = col_max(mx);
-      const float ms = mx * c2;      // the column's step max in log2 units (-inf if all masked)
-      // Token 0 is visible to every query in the first step, so every m is
-      // finite after it and the first step always rescales (from m = -inf).
-      if (__any(ms > m[qt] + kLazy)) {
-        const float m_new = fmaxf(m[qt], ms);
-        const float alpha = __builtin_amdgcn_exp2f(m[qt] - m_new);
-        m[qt] = m_new;
-        // O rows are 4*grp + r: their factors live in the lanes whose column is that row.
-        float ar[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) ar[r] = __shfl(alpha, grp * 4 + r, 64);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          osum[qt][r] *= ar[r];
-#pragma unroll
-          for (int c = 0; c < kNT; ++c) o[qt][c][r] *= ar[r];
-        }
-      }
+      // V rows t = 16*(e/4) + 4*grp + e%4, this lane's kNT dims.
+      Chunk vv[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        pa[qt][e] = _Float16(__builtin_amdgcn_exp2f(__builtin_fmaf(x[e], c2, -m[qt])));
-      osum[qt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[qt], ones, osum[qt], 0, 0, 0);
+        vv[e] = *reinterpret_cast<const Chunk*>(cv + (16 * (e >> 2) + grp * 4 + (e & 3)) * kRS + kNT * col);
+
+      f16x8 pa[kPfTiles];
+#pragma unroll
+      for (int qt = 0; qt < kPfTiles; ++qt) {
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = sc[qt][e >> 2][e & 3];
+        // Only steps reaching past the tile's first position need the causal
+        // mask (it also hides the zero rows past the workgroup's last token).
+        if (t0 + kPfStep - 1 > base_pos + r0 + 16 * qt) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int t = t0 + 16 * (e >> 2) + grp * 4 + (e & 3);
+            if (t > my_pos[qt]) x[e] = -INFINITY;
+          }
+        }
+        float mx = x[0];
+#pragma unroll
+        for (int e = 1; e < 8; ++e) mx = fmaxf(mx, x[e]);
+        mx = col_max(mx);
+        const float ms = mx * c2;      // the column's step max in log2 units (-inf if all masked)
+        // Token 0 is visible to every query in the first step, so every m is
+        // finite after it and the first step always rescales (from m = -inf).
+        if (__any(ms > m[qt] + kLazy)) {
+          const float m_new = fmaxf(m[qt], ms);
+          const float alpha = __builtin_amdgcn_exp2f(m[qt] - m_new);
+          m[qt] = m_new;
+          // O rows are 4*grp + r: their factors live in the lanes whose column is that row.
+          float ar[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) ar[r] = __shfl(alpha, grp * 4 + r, 64);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            osum[qt][r] *= ar[r];
+#pragma unroll
+            for (int c = 0; c < kNT; ++c) o[qt][c][r] *= ar[r];
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          pa[qt][e] = _Float16(__builtin_amdgcn_exp2f(__builtin_fmaf(x[e], c2, -m[qt])));
+        osum[qt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[qt], ones, osum[qt], 0, 0, 0);
+      }
+      // P (A operand: row = this lane's query column, k = the lane's 8 tokens)
+      // times V (B operand: column j of tile c = dim kNT*j + c, the same 8 tokens).
+#pragma unroll
+      for (int c = 0; c < kNT; ++c) {
+        f16x8 vb;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vb[e] = half_at<kNT>(vv[e], c);
+#pragma unroll
+        for (int qt = 0; qt < kPfTiles; ++qt)
+          o[qt][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[qt], vb, o[qt][c], 0, 0, 0);
+      }
     }
-    // P (A operand: row = this lane's query column, k = the lane's 8 tokens)
-    // times V (B operand: column j of tile c = dim kNT*j + c, the same 8 tokens).
-#pragma unroll
-    for (int c = 0; c < kNT; ++c) {
-      f16x8 vb;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) vb[e] = half_at<kNT>(vv[e], c);
-#pragma unroll
-      for (int qt = 0; qt < kPfTiles; ++qt)
-        o[qt][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[qt], vb, o[qt][c], 0, 0, 0);
-    }
+    if (more) store_step(buf ^ 1);   // the other buffer: every wave left it before the last barrier
+    __syncthreads();                 // next step's rows stored; this step's reads done
   }
   if (!active) return;
 
