@@ -9,19 +9,20 @@
 // block table as in decode ("PagedAttention — 把 KV cache 当虚拟内存页来管理",
 // 实践案例 / 案例 2).
 //
-// Unlike decode, every K and V row here meets up to 16 queries, so the two
-// products are dense and run on the matrix cores (v_mfma_f32_16x16x32_f16).
-// One wave owns 16 query rows of one (sequence, head) and walks the context
-// 32 tokens at a time:
+// Unlike decode, every K and V row here meets up to 128 queries, so the two
+// products are dense and run on the matrix cores (v_mfma_f32_16x16x32_f16,
+// fp32 accumulation). A workgroup of 4 waves owns 128 query rows of one
+// (sequence, head); a wave holds two 16-row query tiles. The context is
+// walked 32 tokens per step; the workgroup stages each step's K and V rows in
+// LDS (double-buffered: the next step's global loads are in flight during
+// the products, one barrier per step). Per step and query tile:
 //   S^T[t][q] = K[t] . Q[q]          two 16x16 tiles, k = head_dim in steps of 32
-//   online softmax per query column  (exp2 domain, fp32)
+//   online softmax per query column  (exp2 domain, fp32, lazy reference max)
 //   O[q][d] += P[q][t] V[t][d]       one 16x16x32 product per 16 output columns
 // S^T's accumulator layout (lane = query column, 4 tokens per lane and lane
 // group) is exactly the A-operand layout P needs for the second product, so P
-// never leaves the registers. V is loaded so that a lane's 16-byte row chunk
-// feeds eight output tiles: output column j of tile c is dimension
-// (head_dim/16)*j + c. No LDS, no barriers: the four waves of a workgroup are
-// independent and share K and V through the caches.
+// never leaves the registers. A lane's 16-byte V row chunk feeds eight output
+// tiles: output column j of tile c is dimension (head_dim/16)*j + c.
 #include <hip/hip_runtime.h>
 
 #include "device_common.h"
