@@ -407,6 +407,50 @@ def cpu_baseline_child(seconds: float, workers: int = 1) -> None:
                       "workers": workers}))
 
 
+def prefill_cpu_child(seconds: float) -> None:
+    """The prefill oracle on whole 2048-token prompts (40 heads x 128, one
+    sequence at a time, its blocks scattered over a seeded placement) until
+    ``seconds`` of oracle time are spent; generation is not timed."""
+    import numpy as np
+    import workloads as W
+    from oracle import attention as OA
+    from oracle import cache_ops as OC
+    from oracle import paging as OP
+
+    n, H, D, seed = (PREFILL_SHAPE[k] for k in ("n", "H", "D", "seed"))
+    nb = -(-n // 16)
+    table = [int(b) for b in W.free_order(seed, nb)]
+    K = W.normal_np((n, H, D), seed, W.STREAM_K, 0, dtype=np.float16)
+    V = W.normal_np((n, H, D), seed, W.STREAM_V, 0, dtype=np.float16)
+    q = W.normal_np((n, H, D), seed, W.STREAM_Q, dtype=np.float16)
+    kp = np.zeros((nb, H, 16, D), np.float16)
+    vp = np.zeros((nb, H, 16, D), np.float16)
+    OC.write_kv(kp, vp, K, V, OP.slots(n, table, 16))
+    qs = [0, n]
+    spent, seqs = 0.0, 0
+    while spent < seconds:
+        t0 = time.perf_counter()
+        OA.paged_prefill(q, kp, vp, [table], [n], qs)
+        spent += time.perf_counter() - t0
+        seqs += 1
+    print(json.dumps({"seconds": spent, "flops": causal_prefill_flops([n] * seqs, [n] * seqs, H, D),
+                      "seqs": seqs}))
+
+
+def prefill_cpu_baseline(seconds: float) -> dict:
+    env = dict(os.environ, OMP_NUM_THREADS="1", OPENBLAS_NUM_THREADS="1", MKL_NUM_THREADS="1",
+               HIP_VISIBLE_DEVICES="", CUDA_VISIBLE_DEVICES="")
+    r = subprocess.run([sys.executable, os.path.abspath(__file__), "--cpu-baseline-only", "--workload", "prefill",
+                        "--cpu-seconds", str(seconds)], capture_output=True, text=True, env=env, cwd=ROOT,
+                       timeout=600)
+    if r.returncode != 0:
+        return {"error": r.stderr[-500:]}
+    d = json.loads(r.stdout.strip().splitlines()[-1])
+    return {"value": round(d["flops"] / d["seconds"] / 1e12, 6), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": f"fp64 numpy prefill oracle (gather through the block table + causal attention), "
+                      f"{d['seqs']} whole 2048-token prompts x 40 heads in {d['seconds']:.2f} s on one thread"}
+
+
 def _cpu_run(seconds: float, workers: int) -> dict:
     env = dict(os.environ, OMP_NUM_THREADS="1", OPENBLAS_NUM_THREADS="1", MKL_NUM_THREADS="1",
                HIP_VISIBLE_DEVICES="", CUDA_VISIBLE_DEVICES="")
@@ -445,7 +489,10 @@ def cpu_baseline(seconds: float) -> dict:
 def main():
     args = parse()
     if args.cpu_baseline_only:
-        cpu_baseline_child(args.cpu_seconds, args.cpu_workers)
+        if args.workload == "prefill":
+            prefill_cpu_child(args.cpu_seconds)
+        else:
+            cpu_baseline_child(args.cpu_seconds, args.cpu_workers)
         return 0
     if args.summarize_profiles:
         if args.workload == "prefill":
@@ -1003,6 +1050,8 @@ def prefill_main(args) -> int:
                      "traffic": recorded_prefill_traffic()},
         "device_error_bits": pk.pa_check_errors(),
     }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = prefill_cpu_baseline(args.cpu_seconds)
     print(json.dumps(result), flush=True)
     return 0
 
