@@ -41,6 +41,7 @@ constexpr int kPfWgRows = kPfWaves * kPfRows;
 constexpr int kPfStep = 32;          // tokens per step: the k extent of one 16x16x32 product
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazy = 8.f;        // log2 headroom before the reference max moves
+constexpr int kTabCap = 2048;       // table entries a workgroup can keep in LDS
 
 struct PrefillParams {
   const _Float16* q;             // [num_rows][H][D]
@@ -87,7 +88,7 @@ __device__ __forceinline__ float col_max(float x) {
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
-template <int D, int BS>
+template <int D, int BS, bool kTabLds>
 __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(PrefillParams p) {
   constexpr int kNT = D / 16;      // output tiles; lane column j holds dims kNT*j .. kNT*j + kNT - 1
   constexpr int kKS = D / 32;      // k steps of the QK product
@@ -103,6 +104,10 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(PrefillParams p)
   // the other.
   __shared__ __align__(16) _Float16 lk[2][kPfStep * kRS];
   __shared__ __align__(16) _Float16 lv[2][kPfStep * kRS];
+  // The workgroup's table row (when the launch's contexts fit): entries are
+  // then LDS broadcasts, so the only vector loads in flight are K and V rows
+  // and waiting for a table entry never drains them.
+  __shared__ int32_t ltab[kTabLds ? kTabCap : 1];
 
   const int tid = int(threadIdx.x);
   const int lane = tid & 63;
@@ -173,42 +178,71 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(PrefillParams p)
   // of the step after next are read (scalar loads) while this one streams.
   // Rows at or past the workgroup's last token are zero: no table entry
   // past it is read, and no unused slot of a last block reaches the products.
-  uint4 sk[kPerThr], sv[kPerThr];
   int tab[2] = {0, 0};               // table entries of the two halves of the next step to load
+  if constexpr (kTabLds) {
+    // Entries are checked here, once: a bad one is flagged and read as block
+    // 0 (the rows it should have named are then unspecified, never out of
+    // bounds), so the loop below needs no checks.
+    const int nblk = (wg_t_end + BS - 1) / BS;   // <= kTabCap: the host checked the launch's max_ctx
+    for (int i = tid; i < nblk; i += kPfWaves * 64) {
+      int b = trow[i];
+      if (unsigned(b) >= unsigned(p.num_blocks)) {
+        flag_error(p.err, PA_DEV_BAD_TABLE_ENTRY);
+        b = 0;
+      }
+      ltab[i] = b;
+    }
+    __syncthreads();
+  }
   auto fetch_table = [&](int t0, int (&dst)[2]) {
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       const int t = t0 + 16 * half;
-      dst[half] = t < wg_t_end ? trow[t / BS] : 0;
+      if constexpr (kTabLds) dst[half] = t < wg_t_end ? ltab[t / BS] : 0;
+      else dst[half] = t < wg_t_end ? trow[t / BS] : 0;
     }
   };
-  auto load_step = [&](int t0, const int (&blk)[2]) {
+  // Every call issues the same loads whatever the step (rows past the
+  // workgroup's last token, or a whole step past it, read the pool's first
+  // row instead), so the loads in flight are counted the same on every path
+  // and waiting for one stage never drains the next.
+  auto load_step = [&](int t0, const int (&blk)[2], uint4 (&sk)[kPerThr], uint4 (&sv)[kPerThr]) {
 #pragma unroll
     for (int j = 0; j < kPerThr; ++j) {
       const int c = tid + j * kPfWaves * 64;
       const int row = c / kRowChunks;
       const int tt = t0 + row;
       const int b = blk[row >> 4];
-      sk[j] = uint4{0u, 0u, 0u, 0u};
-      sv[j] = uint4{0u, 0u, 0u, 0u};
-      if (tt < wg_t_end) {
-        if (unsigned(b) < unsigned(p.num_blocks)) {
-          const int64_t off = int64_t(b) * block_elems + head_off + int64_t(tt % BS) * D + (c % kRowChunks) * 8;
-          sk[j] = *reinterpret_cast<const uint4*>(p.k + off);
-          sv[j] = *reinterpret_cast<const uint4*>(p.v + off);
-        } else {
+      bool ok = tt < wg_t_end;
+      if constexpr (!kTabLds) {
+        if (ok && unsigned(b) >= unsigned(p.num_blocks)) {
           flag_error(p.err, PA_DEV_BAD_TABLE_ENTRY);
+          ok = false;
         }
       }
+      const int64_t off =
+          ok ? int64_t(b) * block_elems + head_off + int64_t(tt % BS) * D + (c % kRowChunks) * 8 : int64_t(0);
+      sk[j] = *reinterpret_cast<const uint4*>(p.k + off);
+      sv[j] = *reinterpret_cast<const uint4*>(p.v + off);
     }
   };
-  auto store_step = [&](int buf) {
+  // Rows at or past the workgroup's last token are stored as zeros: no
+  // unused slot of a last block (or other row read in its place) reaches the
+  // products.
+  auto store_step = [&](int buf, int t0, const uint4 (&sk)[kPerThr], const uint4 (&sv)[kPerThr]) {
 #pragma unroll
     for (int j = 0; j < kPerThr; ++j) {
       const int c = tid + j * kPfWaves * 64;
       const int at = (c / kRowChunks) * kRS + (c % kRowChunks) * 8;
-      *reinterpret_cast<uint4*>(&lk[buf][at]) = sk[j];
-      *reinterpret_cast<uint4*>(&lv[buf][at]) = sv[j];
+      uint4 kx = sk[j], vx = sv[j];
+      if (t0 + kPfStep > wg_t_end) {          // workgroup-uniform: only the last step has such rows
+        if (t0 + c / kRowChunks >= wg_t_end) {
+          kx = uint4{0u, 0u, 0u, 0u};
+          vx = uint4{0u, 0u, 0u, 0u};
+        }
+      }
+      *reinterpret_cast<uint4*>(&lk[buf][at]) = kx;
+      *reinterpret_cast<uint4*>(&lv[buf][at]) = vx;
     }
   };
 
@@ -233,23 +267,8 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(PrefillParams p)
   for (int e = 0; e < 8; ++e) ones[e] = _Float16(1.f);
   const float c2 = p.scale_log2;
 
-  {
-    int first[2];
-    fetch_table(0, first);
-    load_step(0, first);
-    fetch_table(kPfStep, tab);
-    store_step(0);
-  }
-  __syncthreads();
-  int buf = 0;
-  for (int t0 = 0; t0 < wg_t_end; t0 += kPfStep, buf ^= 1) {
-    const _Float16* ck = lk[buf];
-    const _Float16* cv = lv[buf];
-    const bool more = t0 + kPfStep < wg_t_end;   // workgroup-uniform
-    if (more) {
-      load_step(t0 + kPfStep, tab);            // in flight during the products
-      fetch_table(t0 + 2 * kPfStep, tab);
-    }
+  // Products of one step over the rows in LDS buffer ck / cv.
+  auto compute = [&](int t0, const _Float16* ck, const _Float16* cv) {
     if (t0 < t_end) {                // wave-uniform: this wave still has rows to serve
       // S^T tiles: lane holds S^T[t = 16j + 4*grp + r][q = col] of query tile
       // qt, r = 0..3 (raw q.k). Each K operand serves both query tiles.
@@ -326,8 +345,43 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(PrefillParams p)
           o[qt][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[qt], vb, o[qt][c], 0, 0, 0);
       }
     }
-    if (more) store_step(buf ^ 1);   // the other buffer: every wave left it before the last barrier
+  };
+
+  // Two register stages: while a step is computed, the next one's rows wait
+  // in registers for the other LDS buffer and the one after is in flight
+  // from memory (a first touch from HBM can outlast one step's products).
+  // Table entries are read one step further ahead still.
+  uint4 skA[kPerThr], svA[kPerThr], skB[kPerThr], svB[kPerThr];
+  {
+    int blk[2];
+    fetch_table(0, blk);
+    load_step(0, blk, skA, svA);
+    fetch_table(kPfStep, blk);
+    load_step(kPfStep, blk, skB, svB);
+    fetch_table(2 * kPfStep, tab);
+    store_step(0, 0, skA, svA);
+  }
+  __syncthreads();
+  // nk/nv: the next step's rows (stored after the products); fk/fv: free,
+  // they receive the step after it.
+  auto step = [&](int t0, int buf, uint4 (&nk)[kPerThr], uint4 (&nv)[kPerThr], uint4 (&fk)[kPerThr],
+                  uint4 (&fv)[kPerThr]) {
+    int nt[2];
+    fetch_table(t0 + 3 * kPfStep, nt);
+    load_step(t0 + 2 * kPfStep, tab, fk, fv);
+    tab[0] = nt[0];
+    tab[1] = nt[1];
+    compute(t0, lk[buf], lv[buf]);
+    // The other buffer: every wave left it before the last barrier.
+    if (t0 + kPfStep < wg_t_end) store_step(buf ^ 1, t0 + kPfStep, nk, nv);
     __syncthreads();                 // next step's rows stored; this step's reads done
+  };
+  for (int t0 = 0; t0 < wg_t_end;) {
+    step(t0, 0, skB, svB, skA, svA);
+    t0 += kPfStep;
+    if (t0 >= wg_t_end) break;
+    step(t0, 1, skA, svA, skB, svB);
+    t0 += kPfStep;
   }
   if (!active) return;
 
@@ -357,7 +411,11 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(PrefillParams p)
 
 template <int D, int BS>
 int launch_prefill_d(const PrefillParams& p, int64_t groups, hipStream_t st) {
-  hipLaunchKernelGGL((prefill_kernel<D, BS>), dim3(unsigned(groups)), dim3(kPfWaves * 64), 0, st, p);
+  // Every workgroup's table row fits in LDS when the launch's longest context does.
+  if ((int64_t(p.max_ctx) + BS - 1) / BS <= kTabCap)
+    hipLaunchKernelGGL((prefill_kernel<D, BS, true>), dim3(unsigned(groups)), dim3(kPfWaves * 64), 0, st, p);
+  else
+    hipLaunchKernelGGL((prefill_kernel<D, BS, false>), dim3(unsigned(groups)), dim3(kPfWaves * 64), 0, st, p);
   return int(hipGetLastError());
 }
 

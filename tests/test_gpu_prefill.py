@@ -153,6 +153,34 @@ def test_logits_whose_max_moves_many_times(direction):
     assert_close(got, ref, direction)
 
 
+def test_table_rows_longer_than_the_kernel_keeps_in_lds():
+    # A context of 33000 tokens needs 2063 table entries of 16-token blocks:
+    # more than a workgroup keeps in LDS (2048), so the kernel reads the
+    # table from memory as it walks; 64-token blocks (516 entries) keep it in
+    # LDS. Both against the oracle, with a ragged chunk and a short sequence.
+    for bs in (16, 64):
+        b = Chunks([33000, 100], [70, 100], H=2, D=64, bs=bs, seed=23)
+        got = b.gpu()
+        assert _pk().pa_check_errors() == 0
+        assert_close(got, b.oracle(), f"bs={bs}")
+
+
+@pytest.mark.parametrize("ctx", [300, 33000])
+def test_bad_table_entry_is_flagged(ctx):
+    # An entry past the pool in sequence 0's row (table kept in LDS at 300
+    # tokens, read from memory at 33000): the kernel flags it and reads an
+    # in-bounds row instead; the other sequence is unaffected.
+    pk = _pk()
+    assert pk.pa_check_errors() == 0
+    b = Chunks([ctx, 90], [40, 90], H=2, D=64, seed=29)
+    tab = b.tabd.clone()
+    tab[0, 3] = b.NB + 7
+    b.tabd = tab
+    got = b.gpu()
+    assert pk.pa_check_errors() & pk.PA_DEV_BAD_TABLE_ENTRY
+    assert_close(got[40:], b.oracle()[40:], "good sequence beside a bad table row")
+
+
 def test_bad_lengths_flag_and_leave_rows_unwritten():
     pk = _pk()
     assert pk.pa_check_errors() == 0
