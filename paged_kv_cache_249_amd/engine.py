@@ -201,6 +201,50 @@ class PagedDecodeEngine:
             N.pa_write_kv(self.pool, k_rows, v_rows, torch.from_numpy(slots).to(self.device))
         return slots
 
+    def prefill(self, seqs, counts, k_rows, v_rows, q_rows, out, *, stream=None) -> None:
+        """A chunked-prefill step: the next ``counts[i]`` tokens of each of
+        ``seqs`` arrive together (rows of ``k_rows``/``v_rows``/``q_rows``
+        ``[sum(counts)][heads][head_dim]`` in sequence order). Unknown
+        sequences are registered; each token goes through the block manager
+        (copy-on-write pairs included), the chunk's K/V is written into its
+        slots, and the chunk's rows attend causally over their sequences'
+        tables at once (``pa_prefill``), results in ``out``. fp16 pools."""
+        seqs = np.asarray(seqs, dtype=np.int64).reshape(-1)
+        counts = np.asarray(counts, dtype=np.int64).reshape(-1)
+        if seqs.size != counts.size or (counts < 0).any():
+            raise N.PagedKVError(N.PA_ERR_INVALID_ARG, "seqs and counts must pair up, counts >= 0")
+        if self.kv_dtype != N.PA_F16:
+            raise N.PagedKVError(N.PA_ERR_UNSUPPORTED, "chunked prefill attends over fp16 pools only")
+        if self.bm.window_blocks:
+            raise N.PagedKVError(N.PA_ERR_UNSUPPORTED, "chunked prefill over a sliding-window ring")
+        R = int(counts.sum())
+        if tuple(k_rows.shape[:1]) != (R,) or q_rows.shape != k_rows.shape or v_rows.shape != k_rows.shape:
+            raise N.PagedKVError(N.PA_ERR_INVALID_ARG, "row counts do not match the chunk sizes")
+        slots, pairs = [], []
+        for s, c in zip(seqs.tolist(), counts.tolist()):
+            if not self.bm.has_seq(s):
+                slots.append(self.bm.add_seq(s, c))
+                continue
+            for _ in range(c):
+                slot, src, dst = self.bm.append(s)
+                slots.append(np.array([slot], dtype=np.int64))
+                if src >= 0:
+                    pairs.append((src, dst))
+        tables, ctx = self.bm.export(seqs, self.cap)
+        qs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+        cur = torch.cuda.current_stream(self.device) if stream is None else stream
+        with torch.cuda.stream(cur):
+            if pairs:
+                N.pa_copy_blocks(self.pool, torch.tensor(pairs, dtype=torch.int32, device=self.device), stream=cur)
+            if R:
+                sl = torch.from_numpy(np.concatenate(slots)).to(self.device, non_blocking=False)
+                N.pa_write_kv(self.pool, k_rows, v_rows, sl, stream=cur)
+                N.pa_prefill(self.pool, q_rows, out, torch.from_numpy(qs).to(self.device),
+                             torch.from_numpy(tables).to(self.device), torch.from_numpy(ctx).to(self.device),
+                             int(counts.max()), int(ctx.max()), stream=cur)
+        self.last_ctx = ctx.copy()
+        self.last_pairs = len(pairs)
+
     def add_sequence_prefix(self, seq: int, tokens, k_rows, v_rows):
         """Register ``seq`` from its token ids, sharing cached full blocks
         (prefix caching), and write the rows of the tokens not shared.

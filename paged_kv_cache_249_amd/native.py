@@ -508,11 +508,21 @@ class BlockManager:
         self.handle = h.value
         self.num_blocks = num_blocks
         self.block_size = block_size
+        self.window_blocks = window_blocks
 
     def __del__(self):
         if getattr(self, "handle", None) and getattr(self, "_lib", None) is not None:
             self._lib.pa_bm_destroy(self.handle)
             self.handle = None
+
+    def has_seq(self, seq: int) -> bool:
+        """Whether ``seq`` is registered (pa_bm_table answers PA_ERR_STATE if not)."""
+        nb, ctx = C.c_int32(), C.c_int32()
+        st = lib.pa_bm_table(self.handle, seq, None, 0, C.byref(nb), C.byref(ctx))
+        if st == PA_ERR_STATE:
+            return False
+        _check(st, "pa_bm_table")
+        return True
 
     def add_seq(self, seq: int, prefill_tokens: int) -> np.ndarray:
         slots = np.empty(max(prefill_tokens, 0), dtype=np.int64)
