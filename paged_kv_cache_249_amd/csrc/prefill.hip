@@ -33,6 +33,7 @@ namespace {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kPfWaves = 4;          // waves per workgroup
 constexpr int kPfTiles = 2;          // 16-row query tiles per wave
@@ -46,8 +47,10 @@ constexpr int kTabCap = 2048;       // table entries a workgroup can keep in LDS
 struct PrefillParams {
   const _Float16* q;             // [num_rows][H][D]
   _Float16* out;                 // [num_rows][H][D]
-  const _Float16* k;             // pool [num_blocks][H][B][D]
-  const _Float16* v;
+  const void* k;                 // pool [num_blocks][H][B][D]: fp16, or int8 codes
+  const void* v;
+  const _Float16* k_scale;       // int8 pools: fp16 [num_blocks][H]
+  const _Float16* v_scale;
   const int32_t* query_start;    // [S + 1]
   const int32_t* tables;         // [S][max_blocks]
   const int32_t* ctx;            // [S]
@@ -57,7 +60,7 @@ struct PrefillParams {
   int32_t num_blocks;
   int32_t max_ctx;
   int32_t max_query;
-  int32_t row_tiles;             // workgroups per (sequence, head): ceil(max_query / 64)
+  int32_t row_tiles;             // workgroups per (sequence, head): ceil(max_query / 128)
   float scale_log2;              // sm_scale * log2(e)
   int32_t* err;
 };
@@ -77,6 +80,20 @@ __device__ __forceinline__ _Float16 half_at(const RowChunk<kNT>& v, int c) {
   return __builtin_bit_cast(_Float16, uint16_t((c & 1) ? (w >> 16) : (w & 0xffffu)));
 }
 
+// Four int8 codes (one 32-bit word) times an fp16 scale, as four fp16
+// values (two words). Each code c becomes the half 1024 + (c + 128) by
+// placing the byte c ^ 0x80 under the exponent byte 0x64 (exact: halves in
+// [1024, 2048) step by 1); subtracting 1152 gives c exactly, and one
+// multiply rounds c * s to nearest even, as fp32 c * s rounded to fp16 would.
+__device__ __forceinline__ void dequant4(uint32_t w, f16x2 s2, uint32_t& lo, uint32_t& hi) {
+  const uint32_t u = w ^ 0x80808080u;
+  const f16x2 off = f16x2{_Float16(1152.f), _Float16(1152.f)};
+  const f16x2 a = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(u, 0x64646464u, 0x00050004u));
+  const f16x2 b = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(u, 0x64646464u, 0x00070006u));
+  lo = __builtin_bit_cast(uint32_t, f16x2((a - off) * s2));
+  hi = __builtin_bit_cast(uint32_t, f16x2((b - off) * s2));
+}
+
 // Max over the four lanes of a column (lanes l, l^16, l^32, l^48). With both
 // operands the same value, permlane16_swap returns rows (0,0,2,2) and
 // (1,1,3,3) of it, and permlane32_swap the lower and the upper 32 lanes each
@@ -88,15 +105,21 @@ __device__ __forceinline__ float col_max(float x) {
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
-template <int D, int BS, bool kTabLds>
+template <int D, int BS, bool kTabLds, bool kI8>
 __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(PrefillParams p) {
   constexpr int kNT = D / 16;      // output tiles; lane column j holds dims kNT*j .. kNT*j + kNT - 1
   constexpr int kKS = D / 32;      // k steps of the QK product
   constexpr int kGD = D / 4;       // dims a lane group covers in the QK product
   constexpr int kRS = D + 8;       // LDS row stride (halves): 16 bytes of padding per row
-  constexpr int kRowChunks = D / 8;                    // 16-byte chunks per K or V row
+  // Staging: a thread moves kPerThr chunks of kChunkVals values of the step's
+  // K and V rows (fp16: 16-byte chunks; int8: one chunk of D/8 codes).
+  constexpr int kChunkVals = kI8 ? D / 8 : 8;
+  constexpr int kRowChunks = D / kChunkVals;           // chunks per K or V row
   constexpr int kPerThr = kPfStep * kRowChunks / (kPfWaves * 64);
   static_assert(kPerThr * kPfWaves * 64 == kPfStep * kRowChunks, "step tile must split evenly");
+  static_assert(!kI8 || kPerThr == 1, "int8 staging moves one chunk per thread");
+  // Raw staging registers per chunk: fp16 16 bytes; int8 16 (D 128) or 8 bytes.
+  using Raw = typename std::conditional<kI8 && D == 64, uint2, uint4>::type;
   using Chunk = RowChunk<kNT>;
 
   // Two steps' K and V rows (32 tokens each), shared by the workgroup's
@@ -174,10 +197,8 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(PrefillParams p)
   // Staging: thread tid moves 16-byte chunks tid + 256 j of the step's K and
   // V rows (row c / kRowChunks, chunk c % kRowChunks). A 16-row half of a
   // step lies in one block (B is 16, 32 or 64 and steps start at multiples
-  // of 32), so its table entry is one value for the workgroup; the entries
-  // of the step after next are read (scalar loads) while this one streams.
-  // Rows at or past the workgroup's last token are zero: no table entry
-  // past it is read, and no unused slot of a last block reaches the products.
+  // of 32), so its table entry is one value for the workgroup. No table
+  // entry at or past the workgroup's last token is read.
   int tab[2] = {0, 0};               // table entries of the two halves of the next step to load
   if constexpr (kTabLds) {
     // Entries are checked here, once: a bad one is flagged and read as block
@@ -202,11 +223,17 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(PrefillParams p)
       else dst[half] = t < wg_t_end ? trow[t / BS] : 0;
     }
   };
+  // Raw rows of one step as one thread holds them (and, for int8, the
+  // scales of the blocks its chunk came from).
+  struct Stage {
+    Raw k[kPerThr], v[kPerThr];
+    f16x2 ks, vs;
+  };
   // Every call issues the same loads whatever the step (rows past the
   // workgroup's last token, or a whole step past it, read the pool's first
   // row instead), so the loads in flight are counted the same on every path
   // and waiting for one stage never drains the next.
-  auto load_step = [&](int t0, const int (&blk)[2], uint4 (&sk)[kPerThr], uint4 (&sv)[kPerThr]) {
+  auto load_step = [&](int t0, const int (&blk)[2], Stage& st) {
 #pragma unroll
     for (int j = 0; j < kPerThr; ++j) {
       const int c = tid + j * kPfWaves * 64;
@@ -220,29 +247,62 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(PrefillParams p)
           ok = false;
         }
       }
-      const int64_t off =
-          ok ? int64_t(b) * block_elems + head_off + int64_t(tt % BS) * D + (c % kRowChunks) * 8 : int64_t(0);
-      sk[j] = *reinterpret_cast<const uint4*>(p.k + off);
-      sv[j] = *reinterpret_cast<const uint4*>(p.v + off);
+      const int64_t off =   // in elements (halves or codes)
+          ok ? int64_t(b) * block_elems + head_off + int64_t(tt % BS) * D + (c % kRowChunks) * kChunkVals
+             : int64_t(0);
+      if constexpr (kI8) {
+        st.k[j] = *reinterpret_cast<const Raw*>(static_cast<const int8_t*>(p.k) + off);
+        st.v[j] = *reinterpret_cast<const Raw*>(static_cast<const int8_t*>(p.v) + off);
+        const int64_t si = ok ? int64_t(b) * p.num_heads + h : int64_t(0);
+        const _Float16 ks = p.k_scale[si], vs = p.v_scale[si];
+        st.ks = f16x2{ks, ks};
+        st.vs = f16x2{vs, vs};
+      } else {
+        st.k[j] = *reinterpret_cast<const Raw*>(static_cast<const _Float16*>(p.k) + off);
+        st.v[j] = *reinterpret_cast<const Raw*>(static_cast<const _Float16*>(p.v) + off);
+      }
     }
   };
   // Rows at or past the workgroup's last token are stored as zeros: no
   // unused slot of a last block (or other row read in its place) reaches the
-  // products.
-  auto store_step = [&](int buf, int t0, const uint4 (&sk)[kPerThr], const uint4 (&sv)[kPerThr]) {
+  // products. int8 codes are scaled into fp16 on the way.
+  auto store_step = [&](int buf, int t0, const Stage& st) {
 #pragma unroll
     for (int j = 0; j < kPerThr; ++j) {
       const int c = tid + j * kPfWaves * 64;
-      const int at = (c / kRowChunks) * kRS + (c % kRowChunks) * 8;
-      uint4 kx = sk[j], vx = sv[j];
-      if (t0 + kPfStep > wg_t_end) {          // workgroup-uniform: only the last step has such rows
-        if (t0 + c / kRowChunks >= wg_t_end) {
+      const int at = (c / kRowChunks) * kRS + (c % kRowChunks) * kChunkVals;
+      // Workgroup-uniform outer test: only the last step has such rows.
+      const bool zero = t0 + kPfStep > wg_t_end && t0 + c / kRowChunks >= wg_t_end;
+      if constexpr (kI8) {
+        constexpr int kW = int(sizeof(Raw)) / 4;      // code words: 4 (D 128) or 2 (D 64)
+        uint32_t kw[2 * kW], vw[2 * kW];
+        const uint32_t* kr = reinterpret_cast<const uint32_t*>(&st.k[j]);
+        const uint32_t* vr = reinterpret_cast<const uint32_t*>(&st.v[j]);
+#pragma unroll
+        for (int i = 0; i < kW; ++i) {
+          dequant4(kr[i], st.ks, kw[2 * i], kw[2 * i + 1]);
+          dequant4(vr[i], st.vs, vw[2 * i], vw[2 * i + 1]);
+        }
+#pragma unroll
+        for (int i = 0; i < kW / 2; ++i) {
+          uint4 kx = uint4{kw[4 * i], kw[4 * i + 1], kw[4 * i + 2], kw[4 * i + 3]};
+          uint4 vx = uint4{vw[4 * i], vw[4 * i + 1], vw[4 * i + 2], vw[4 * i + 3]};
+          if (zero) {
+            kx = uint4{0u, 0u, 0u, 0u};
+            vx = uint4{0u, 0u, 0u, 0u};
+          }
+          *reinterpret_cast<uint4*>(&lk[buf][at + 8 * i]) = kx;
+          *reinterpret_cast<uint4*>(&lv[buf][at + 8 * i]) = vx;
+        }
+      } else {
+        uint4 kx = st.k[j], vx = st.v[j];
+        if (zero) {
           kx = uint4{0u, 0u, 0u, 0u};
           vx = uint4{0u, 0u, 0u, 0u};
         }
+        *reinterpret_cast<uint4*>(&lk[buf][at]) = kx;
+        *reinterpret_cast<uint4*>(&lv[buf][at]) = vx;
       }
-      *reinterpret_cast<uint4*>(&lk[buf][at]) = kx;
-      *reinterpret_cast<uint4*>(&lv[buf][at]) = vx;
     }
   };
 
@@ -351,36 +411,35 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(PrefillParams p)
   // in registers for the other LDS buffer and the one after is in flight
   // from memory (a first touch from HBM can outlast one step's products).
   // Table entries are read one step further ahead still.
-  uint4 skA[kPerThr], svA[kPerThr], skB[kPerThr], svB[kPerThr];
+  Stage sA, sB;
   {
     int blk[2];
     fetch_table(0, blk);
-    load_step(0, blk, skA, svA);
+    load_step(0, blk, sA);
     fetch_table(kPfStep, blk);
-    load_step(kPfStep, blk, skB, svB);
+    load_step(kPfStep, blk, sB);
     fetch_table(2 * kPfStep, tab);
-    store_step(0, 0, skA, svA);
+    store_step(0, 0, sA);
   }
   __syncthreads();
-  // nk/nv: the next step's rows (stored after the products); fk/fv: free,
-  // they receive the step after it.
-  auto step = [&](int t0, int buf, uint4 (&nk)[kPerThr], uint4 (&nv)[kPerThr], uint4 (&fk)[kPerThr],
-                  uint4 (&fv)[kPerThr]) {
+  // nx: the next step's rows (stored after the products); fr: free, it
+  // receives the step after it.
+  auto step = [&](int t0, int buf, Stage& nx, Stage& fr) {
     int nt[2];
     fetch_table(t0 + 3 * kPfStep, nt);
-    load_step(t0 + 2 * kPfStep, tab, fk, fv);
+    load_step(t0 + 2 * kPfStep, tab, fr);
     tab[0] = nt[0];
     tab[1] = nt[1];
     compute(t0, lk[buf], lv[buf]);
     // The other buffer: every wave left it before the last barrier.
-    if (t0 + kPfStep < wg_t_end) store_step(buf ^ 1, t0 + kPfStep, nk, nv);
+    if (t0 + kPfStep < wg_t_end) store_step(buf ^ 1, t0 + kPfStep, nx);
     __syncthreads();                 // next step's rows stored; this step's reads done
   };
   for (int t0 = 0; t0 < wg_t_end;) {
-    step(t0, 0, skB, svB, skA, svA);
+    step(t0, 0, sB, sA);
     t0 += kPfStep;
     if (t0 >= wg_t_end) break;
-    step(t0, 1, skA, svA, skB, svB);
+    step(t0, 1, sA, sB);
     t0 += kPfStep;
   }
   if (!active) return;
@@ -409,22 +468,22 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(PrefillParams p)
   }
 }
 
-template <int D, int BS>
+template <int D, int BS, bool kI8>
 int launch_prefill_d(const PrefillParams& p, int64_t groups, hipStream_t st) {
   // Every workgroup's table row fits in LDS when the launch's longest context does.
   if ((int64_t(p.max_ctx) + BS - 1) / BS <= kTabCap)
-    hipLaunchKernelGGL((prefill_kernel<D, BS, true>), dim3(unsigned(groups)), dim3(kPfWaves * 64), 0, st, p);
+    hipLaunchKernelGGL((prefill_kernel<D, BS, true, kI8>), dim3(unsigned(groups)), dim3(kPfWaves * 64), 0, st, p);
   else
-    hipLaunchKernelGGL((prefill_kernel<D, BS, false>), dim3(unsigned(groups)), dim3(kPfWaves * 64), 0, st, p);
+    hipLaunchKernelGGL((prefill_kernel<D, BS, false, kI8>), dim3(unsigned(groups)), dim3(kPfWaves * 64), 0, st, p);
   return int(hipGetLastError());
 }
 
-template <int D>
+template <int D, bool kI8>
 int launch_prefill_bs(const PrefillParams& p, int block_size, int64_t groups, hipStream_t st) {
   switch (block_size) {
-    case 16: return launch_prefill_d<D, 16>(p, groups, st);
-    case 32: return launch_prefill_d<D, 32>(p, groups, st);
-    default: return launch_prefill_d<D, 64>(p, groups, st);
+    case 16: return launch_prefill_d<D, 16, kI8>(p, groups, st);
+    case 32: return launch_prefill_d<D, 32, kI8>(p, groups, st);
+    default: return launch_prefill_d<D, 64, kI8>(p, groups, st);
   }
 }
 
@@ -441,8 +500,10 @@ int launch_prefill(const PrefillArgs& a, void* stream) {
   PrefillParams p{};
   p.q = static_cast<const _Float16*>(a.q);
   p.out = static_cast<_Float16*>(a.out);
-  p.k = static_cast<const _Float16*>(a.pool->k_cache);
-  p.v = static_cast<const _Float16*>(a.pool->v_cache);
+  p.k = a.pool->k_cache;
+  p.v = a.pool->v_cache;
+  p.k_scale = static_cast<const _Float16*>(a.pool->k_scale);
+  p.v_scale = static_cast<const _Float16*>(a.pool->v_scale);
   p.query_start = a.query_start;
   p.tables = a.tables;
   p.ctx = a.ctx;
@@ -456,8 +517,12 @@ int launch_prefill(const PrefillArgs& a, void* stream) {
   p.scale_log2 = a.sm_scale * kLog2e;
   p.err = device_error_ptr();
   const hipStream_t st = static_cast<hipStream_t>(stream);
-  if (a.pool->head_dim == 64) return launch_prefill_bs<64>(p, a.pool->block_size, groups, st);
-  return launch_prefill_bs<128>(p, a.pool->block_size, groups, st);
+  const bool i8 = a.pool->kv_dtype == PA_I8;
+  if (a.pool->head_dim == 64)
+    return i8 ? launch_prefill_bs<64, true>(p, a.pool->block_size, groups, st)
+              : launch_prefill_bs<64, false>(p, a.pool->block_size, groups, st);
+  return i8 ? launch_prefill_bs<128, true>(p, a.pool->block_size, groups, st)
+            : launch_prefill_bs<128, false>(p, a.pool->block_size, groups, st);
 }
 
 }  // namespace pa

@@ -175,12 +175,19 @@ def test_quantised_engine_steps_match_the_oracle(kv, ptok):
     assert not (err > 5e-3 + 1e-2 * np.abs(ref)).any(), f"max abs {err.max():.3e}"
 
 
-def test_chunked_prefill_then_decode():
+@pytest.mark.parametrize("kv", ["f16", "i8"])
+def test_chunked_prefill_then_decode(kv):
     # Prompts arrive in chunks through the engine (block manager, K/V write,
     # pa_prefill over the tables), with a fork between chunks so the next
     # chunk's first append copies the shared partial block; then decode steps.
     # Every output row is checked against fp64 attention over the sequence's
-    # own rows up to its position, in a NaN-poisoned pool.
+    # own rows up to its position, in a NaN-poisoned pool (fp16: the fp16
+    # bar). An int8 pool quantises each chunk as it is written: rows
+    # attending at least 256 tokens would be held to the int8 bar (2e-2),
+    # shorter ones, where one block's quantisation error shows through, to
+    # 6e-2 — every row here is shorter, so this is a sanity bound on the
+    # engine's int8 path; the kernel's strict int8 check (against the oracle
+    # over the same codes) is in the prefill tests.
     import paged_kv_cache_249_amd as pk
     from paged_kv_cache_249_amd.engine import PagedDecodeEngine
 
@@ -197,8 +204,9 @@ def test_chunked_prefill_then_decode():
     # Sequence 3 is forked from 0 after 50 tokens: it shares those rows.
     K[3][:50], V[3][:50] = K[0][:50], V[0][:50]
 
-    eng = PagedDecodeEngine(256, Hh, Dd, pk.PA_F16, 4, 64, free_order=W.free_order(seed, 256), device=DEV,
-                            pool_fill=float("nan"))
+    i8 = kv == "i8"
+    eng = PagedDecodeEngine(256, Hh, Dd, pk.PA_I8 if i8 else pk.PA_F16, 4, 64, free_order=W.free_order(seed, 256),
+                            device=DEV, pool_fill=None if i8 else float("nan"))
     pos = {s: 0 for s in total}
 
     def check(seqs, counts, got):
@@ -210,7 +218,10 @@ def test_chunked_prefill_then_decode():
                 g = got[r].astype(np.float64)
                 assert not np.isnan(g).any(), f"seq {s} pos {p}: NaN"
                 err = np.abs(g - ref)
-                assert (err <= 5e-3 + 1e-2 * np.abs(ref)).all(), f"seq {s} pos {p}: max err {err.max():.3e}"
+                if i8:
+                    assert err.max() <= (2e-2 if p + 1 >= 256 else 6e-2), f"seq {s} pos {p}: max err {err.max():.3e}"
+                else:
+                    assert (err <= 5e-3 + 1e-2 * np.abs(ref)).all(), f"seq {s} pos {p}: max err {err.max():.3e}"
                 r += 1
             pos[s] += c
 
