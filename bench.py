@@ -974,19 +974,21 @@ def prefill_probe(pk, W, torch, np, dev, H=40, D=128):
                      "frac_of_mfma_peak": round(fl / t / 1e12 / MFMA_PEAK_F16_TFLOPS, 4),
                      "kv_gbs_once": round(kv / t / 1e9, 1)}
         del q, out
-    # The same prompts in an int8 pool (random codes, one fp16 scale per
-    # (block, head)): codes are dequantised to fp16 as they are staged.
-    i8 = pk.new_pool(pool.num_blocks, H, D, pk.PA_I8, device=dev)
-    i8.k_cache.copy_(torch.randint(-127, 128, i8.k_cache.shape, generator=g, device=dev, dtype=torch.int8))
-    i8.v_cache.copy_(torch.randint(-127, 128, i8.v_cache.shape, generator=g, device=dev, dtype=torch.int8))
-    i8.k_scale.fill_(4.0 / 127)
-    i8.v_scale.fill_(4.0 / 127)
-    q, out, qs = prefill_chunk(torch, np, dev, g, S, n, H, D)
-    t = _time_calls(lambda: pk.pa_prefill(i8, q, out, qs, tab, ctx, n, n))
+    # The same prompts in int8 and int4 pools (random codes, one fp16 scale
+    # per (block, head)): codes are dequantised to fp16 as they are staged.
     fl = causal_prefill_flops([n] * S, [n] * S, H, D)
-    res["whole_prompt_int8_pool"] = {"us": round(t * 1e6, 2), "tflops": round(fl / t / 1e12, 1),
-                                     "frac_of_mfma_peak": round(fl / t / 1e12 / MFMA_PEAK_F16_TFLOPS, 4)}
-    del q, out, i8
+    for name, code, qmax in (("int8", pk.PA_I8, 127), ("int4", pk.PA_I4, 7)):
+        qp = pk.new_pool(pool.num_blocks, H, D, code, device=dev)
+        for c in (qp.k_cache, qp.v_cache):
+            lo, hi = (-128, 128) if code == pk.PA_I8 else (0, 256)     # int4: any byte is two codes
+            c.copy_(torch.randint(lo, hi, c.shape, generator=g, device=dev, dtype=torch.int16).to(c.dtype))
+        qp.k_scale.fill_(4.0 / qmax)
+        qp.v_scale.fill_(4.0 / qmax)
+        q, out, qs = prefill_chunk(torch, np, dev, g, S, n, H, D)
+        t = _time_calls(lambda: pk.pa_prefill(qp, q, out, qs, tab, ctx, n, n))
+        res[f"whole_prompt_{name}_pool"] = {"us": round(t * 1e6, 2), "tflops": round(fl / t / 1e12, 1),
+                                           "frac_of_mfma_peak": round(fl / t / 1e12 / MFMA_PEAK_F16_TFLOPS, 4)}
+        del q, out, qp
     assert pk.pa_check_errors() == 0
     del pool
     torch.cuda.empty_cache()

@@ -264,17 +264,17 @@ pa_status pa_decode_ordered(pa_pool* pool, const void* q, pa_dtype q_dtype, void
  * of a sequence are contiguous and in position order. query_start: device
  * int32 [num_seqs + 1], non-decreasing, query_start[num_seqs] <= num_rows.
  * block_tables, context_lens, max_blocks, max_context_len: as pa_decode.
- * max_query_len bounds every n_s. q_dtype must be PA_F16 and the pool PA_F16
- * or PA_I8 (the products run on the matrix cores in fp16 with fp32
- * accumulation; int8 codes are dequantised to fp16 as code * scale, rounded
- * once; the softmax weights are rounded to fp16 before they meet V). sm_scale <= 0
+ * max_query_len bounds every n_s. q_dtype must be PA_F16 and the pool PA_F16,
+ * PA_I8 or PA_I4 (the products run on the matrix cores in fp16 with fp32
+ * accumulation; int8 and int4 codes are dequantised to fp16 as code * scale,
+ * rounded once; the softmax weights are rounded to fp16 before they meet V). sm_scale <= 0
  * selects 1/sqrt(head_dim). n_s == 0 writes nothing. On the device, n_s < 0,
  * n_s > context_lens[s], n_s > max_query_len, context_lens[s] >
  * max_context_len or rows outside [0, num_rows) flag PA_DEV_BAD_CONTEXT and
  * leave that sequence's rows unwritten; a table entry outside the pool flags
  * PA_DEV_BAD_TABLE_ENTRY and block 0 is read in its place.
  * Errors: PA_ERR_INVALID_ARG (null pointers, misalignment, bad sizes),
- * PA_ERR_UNSUPPORTED (int4 or fp32 pool, non-fp16 q), PA_ERR_HIP. */
+ * PA_ERR_UNSUPPORTED (fp32 pool, non-fp16 q), PA_ERR_HIP. */
 pa_status pa_prefill(pa_pool* pool, const void* q, pa_dtype q_dtype, void* out,
                      const int32_t* query_start, int32_t num_rows, const int32_t* block_tables,
                      int32_t max_blocks, const int32_t* context_lens, int32_t num_seqs,

@@ -320,8 +320,8 @@ pa_status pa_prefill(pa_pool* pool, const void* q, pa_dtype q_dtype, void* out, 
                      int32_t max_context_len, float sm_scale, pa_stream stream) {
   const char* fn = "pa_prefill";
   if (!pool) return fail(PA_ERR_INVALID_ARG, "%s: pool is NULL", fn);
-  if (pool->kv_dtype != PA_F16 && pool->kv_dtype != PA_I8)
-    return fail(PA_ERR_UNSUPPORTED, "%s: pool dtype %d (F16 or I8 only)", fn, int(pool->kv_dtype));
+  if (pool->kv_dtype != PA_F16 && pool->kv_dtype != PA_I8 && pool->kv_dtype != PA_I4)
+    return fail(PA_ERR_UNSUPPORTED, "%s: pool dtype %d (F16, I8 or I4 only)", fn, int(pool->kv_dtype));
   if (q_dtype != PA_F16) return fail(PA_ERR_UNSUPPORTED, "%s: q dtype %d (F16 only)", fn, int(q_dtype));
   if (num_seqs < 0 || num_rows < 0 || max_query_len < 0 || max_context_len < 0 || max_blocks < 0)
     return fail(PA_ERR_INVALID_ARG, "%s: negative size", fn);

@@ -94,6 +94,22 @@ __device__ __forceinline__ void dequant4(uint32_t w, f16x2 s2, uint32_t& lo, uin
   hi = __builtin_bit_cast(uint32_t, f16x2((b - off) * s2));
 }
 
+// Eight int4 codes (one 32-bit word: byte j holds dim 2j in its low nibble
+// and dim 2j+1 in its high one, each as code + 8) times an fp16 scale, as
+// eight fp16 values in dim order (four words). Each nibble n goes under the
+// exponent byte 0x64 (the half 1024 + n, exact); subtracting 1032 gives the
+// code exactly and one multiply rounds code * s to nearest even.
+__device__ __forceinline__ void dequant8_i4(uint32_t w, f16x2 s2, uint32_t (&out)[4]) {
+  const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+  const f16x2 off = f16x2{_Float16(1032.f), _Float16(1032.f)};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    // Bytes: lo[j], 0, hi[j], 0 (selector 0x0C yields zero), then the exponent bytes.
+    const uint32_t t = __builtin_amdgcn_perm(hi, lo, 0x0C040C00u + 0x00010001u * uint32_t(j)) | 0x64006400u;
+    out[j] = __builtin_bit_cast(uint32_t, f16x2((__builtin_bit_cast(f16x2, t) - off) * s2));
+  }
+}
+
 // Max over the four lanes of a column (lanes l, l^16, l^32, l^48). With both
 // operands the same value, permlane16_swap returns rows (0,0,2,2) and
 // (1,1,3,3) of it, and permlane32_swap the lower and the upper 32 lanes each
@@ -105,21 +121,30 @@ __device__ __forceinline__ float col_max(float x) {
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
-template <int D, int BS, bool kTabLds, bool kI8>
+// Pool element types the kernel reads.
+enum : int { kKvF16 = 0, kKvI8 = 1, kKvI4 = 2 };
+
+template <int D, int BS, bool kTabLds, int kKV>
 __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(PrefillParams p) {
+  constexpr bool kI8 = kKV == kKvI8;
+  constexpr bool kI4 = kKV == kKvI4;
+  constexpr bool kQuant = kI8 || kI4;
   constexpr int kNT = D / 16;      // output tiles; lane column j holds dims kNT*j .. kNT*j + kNT - 1
   constexpr int kKS = D / 32;      // k steps of the QK product
   constexpr int kGD = D / 4;       // dims a lane group covers in the QK product
   constexpr int kRS = D + 8;       // LDS row stride (halves): 16 bytes of padding per row
   // Staging: a thread moves kPerThr chunks of kChunkVals values of the step's
-  // K and V rows (fp16: 16-byte chunks; int8: one chunk of D/8 codes).
-  constexpr int kChunkVals = kI8 ? D / 8 : 8;
+  // K and V rows (fp16: 16-byte chunks; int8, int4: one chunk of D/8 codes).
+  constexpr int kChunkVals = kQuant ? D / 8 : 8;
   constexpr int kRowChunks = D / kChunkVals;           // chunks per K or V row
   constexpr int kPerThr = kPfStep * kRowChunks / (kPfWaves * 64);
   static_assert(kPerThr * kPfWaves * 64 == kPfStep * kRowChunks, "step tile must split evenly");
-  static_assert(!kI8 || kPerThr == 1, "int8 staging moves one chunk per thread");
-  // Raw staging registers per chunk: fp16 16 bytes; int8 16 (D 128) or 8 bytes.
-  using Raw = typename std::conditional<kI8 && D == 64, uint2, uint4>::type;
+  static_assert(!kQuant || kPerThr == 1, "int8 and int4 staging move one chunk per thread");
+  // Raw staging registers per chunk: fp16 16 bytes; int8 16 (D 128) or 8
+  // bytes; int4 8 (D 128) or 4 bytes.
+  using Raw = typename std::conditional<
+      kI4, typename std::conditional<D == 64, uint32_t, uint2>::type,
+      typename std::conditional<kI8 && D == 64, uint2, uint4>::type>::type;
   using Chunk = RowChunk<kNT>;
 
   // Two steps' K and V rows (32 tokens each), shared by the workgroup's
@@ -250,9 +275,10 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(PrefillParams p)
       const int64_t off =   // in elements (halves or codes)
           ok ? int64_t(b) * block_elems + head_off + int64_t(tt % BS) * D + (c % kRowChunks) * kChunkVals
              : int64_t(0);
-      if constexpr (kI8) {
-        st.k[j] = *reinterpret_cast<const Raw*>(static_cast<const int8_t*>(p.k) + off);
-        st.v[j] = *reinterpret_cast<const Raw*>(static_cast<const int8_t*>(p.v) + off);
+      if constexpr (kQuant) {
+        const int64_t byte = kI4 ? off / 2 : off;      // int4: two codes per byte
+        st.k[j] = *reinterpret_cast<const Raw*>(static_cast<const uint8_t*>(p.k) + byte);
+        st.v[j] = *reinterpret_cast<const Raw*>(static_cast<const uint8_t*>(p.v) + byte);
         const int64_t si = ok ? int64_t(b) * p.num_heads + h : int64_t(0);
         const _Float16 ks = p.k_scale[si], vs = p.v_scale[si];
         st.ks = f16x2{ks, ks};
@@ -273,18 +299,30 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(PrefillParams p)
       const int at = (c / kRowChunks) * kRS + (c % kRowChunks) * kChunkVals;
       // Workgroup-uniform outer test: only the last step has such rows.
       const bool zero = t0 + kPfStep > wg_t_end && t0 + c / kRowChunks >= wg_t_end;
-      if constexpr (kI8) {
-        constexpr int kW = int(sizeof(Raw)) / 4;      // code words: 4 (D 128) or 2 (D 64)
-        uint32_t kw[2 * kW], vw[2 * kW];
+      if constexpr (kQuant) {
+        constexpr int kW = int(sizeof(Raw)) / 4;      // code words per chunk
+        constexpr int kOut = kI4 ? 4 * kW : 2 * kW;    // fp16 pair words they become
+        uint32_t kw[kOut], vw[kOut];
         const uint32_t* kr = reinterpret_cast<const uint32_t*>(&st.k[j]);
         const uint32_t* vr = reinterpret_cast<const uint32_t*>(&st.v[j]);
 #pragma unroll
         for (int i = 0; i < kW; ++i) {
-          dequant4(kr[i], st.ks, kw[2 * i], kw[2 * i + 1]);
-          dequant4(vr[i], st.vs, vw[2 * i], vw[2 * i + 1]);
+          if constexpr (kI4) {
+            uint32_t a[4], b[4];
+            dequant8_i4(kr[i], st.ks, a);
+            dequant8_i4(vr[i], st.vs, b);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              kw[4 * i + e] = a[e];
+              vw[4 * i + e] = b[e];
+            }
+          } else {
+            dequant4(kr[i], st.ks, kw[2 * i], kw[2 * i + 1]);
+            dequant4(vr[i], st.vs, vw[2 * i], vw[2 * i + 1]);
+          }
         }
 #pragma unroll
-        for (int i = 0; i < kW / 2; ++i) {
+        for (int i = 0; i < kOut / 4; ++i) {
           uint4 kx = uint4{kw[4 * i], kw[4 * i + 1], kw[4 * i + 2], kw[4 * i + 3]};
           uint4 vx = uint4{vw[4 * i], vw[4 * i + 1], vw[4 * i + 2], vw[4 * i + 3]};
           if (zero) {
@@ -468,22 +506,31 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(PrefillParams p)
   }
 }
 
-template <int D, int BS, bool kI8>
+template <int D, int BS, int kKV>
 int launch_prefill_d(const PrefillParams& p, int64_t groups, hipStream_t st) {
   // Every workgroup's table row fits in LDS when the launch's longest context does.
   if ((int64_t(p.max_ctx) + BS - 1) / BS <= kTabCap)
-    hipLaunchKernelGGL((prefill_kernel<D, BS, true, kI8>), dim3(unsigned(groups)), dim3(kPfWaves * 64), 0, st, p);
+    hipLaunchKernelGGL((prefill_kernel<D, BS, true, kKV>), dim3(unsigned(groups)), dim3(kPfWaves * 64), 0, st, p);
   else
-    hipLaunchKernelGGL((prefill_kernel<D, BS, false, kI8>), dim3(unsigned(groups)), dim3(kPfWaves * 64), 0, st, p);
+    hipLaunchKernelGGL((prefill_kernel<D, BS, false, kKV>), dim3(unsigned(groups)), dim3(kPfWaves * 64), 0, st, p);
   return int(hipGetLastError());
 }
 
-template <int D, bool kI8>
+template <int D, int kKV>
 int launch_prefill_bs(const PrefillParams& p, int block_size, int64_t groups, hipStream_t st) {
   switch (block_size) {
-    case 16: return launch_prefill_d<D, 16, kI8>(p, groups, st);
-    case 32: return launch_prefill_d<D, 32, kI8>(p, groups, st);
-    default: return launch_prefill_d<D, 64, kI8>(p, groups, st);
+    case 16: return launch_prefill_d<D, 16, kKV>(p, groups, st);
+    case 32: return launch_prefill_d<D, 32, kKV>(p, groups, st);
+    default: return launch_prefill_d<D, 64, kKV>(p, groups, st);
+  }
+}
+
+template <int D>
+int launch_prefill_kv(const PrefillParams& p, pa_dtype kv, int block_size, int64_t groups, hipStream_t st) {
+  switch (kv) {
+    case PA_I8: return launch_prefill_bs<D, kKvI8>(p, block_size, groups, st);
+    case PA_I4: return launch_prefill_bs<D, kKvI4>(p, block_size, groups, st);
+    default: return launch_prefill_bs<D, kKvF16>(p, block_size, groups, st);
   }
 }
 
@@ -517,12 +564,8 @@ int launch_prefill(const PrefillArgs& a, void* stream) {
   p.scale_log2 = a.sm_scale * kLog2e;
   p.err = device_error_ptr();
   const hipStream_t st = static_cast<hipStream_t>(stream);
-  const bool i8 = a.pool->kv_dtype == PA_I8;
-  if (a.pool->head_dim == 64)
-    return i8 ? launch_prefill_bs<64, true>(p, a.pool->block_size, groups, st)
-              : launch_prefill_bs<64, false>(p, a.pool->block_size, groups, st);
-  return i8 ? launch_prefill_bs<128, true>(p, a.pool->block_size, groups, st)
-            : launch_prefill_bs<128, false>(p, a.pool->block_size, groups, st);
+  if (a.pool->head_dim == 64) return launch_prefill_kv<64>(p, a.pool->kv_dtype, a.pool->block_size, groups, st);
+  return launch_prefill_kv<128>(p, a.pool->kv_dtype, a.pool->block_size, groups, st);
 }
 
 }  // namespace pa

@@ -208,15 +208,15 @@ class PagedDecodeEngine:
         sequences are registered; each token goes through the block manager
         (copy-on-write pairs included), the chunk's K/V is written into its
         slots, and the chunk's rows attend causally over their sequences'
-        tables at once (``pa_prefill``), results in ``out``. fp16 or int8
-        pools (an int8 pool quantises each chunk's rows per (block, head) as
-        it writes them), fp16 queries."""
+        tables at once (``pa_prefill``), results in ``out``. fp16, int8 or
+        int4 pools (a quantised pool codes each chunk's rows per (block, head)
+        as it writes them), fp16 queries."""
         seqs = np.asarray(seqs, dtype=np.int64).reshape(-1)
         counts = np.asarray(counts, dtype=np.int64).reshape(-1)
         if seqs.size != counts.size or (counts < 0).any():
             raise N.PagedKVError(N.PA_ERR_INVALID_ARG, "seqs and counts must pair up, counts >= 0")
-        if self.kv_dtype not in (N.PA_F16, N.PA_I8):
-            raise N.PagedKVError(N.PA_ERR_UNSUPPORTED, "chunked prefill attends over fp16 or int8 pools")
+        if self.kv_dtype not in (N.PA_F16, N.PA_I8, N.PA_I4):
+            raise N.PagedKVError(N.PA_ERR_UNSUPPORTED, "chunked prefill attends over fp16, int8 or int4 pools")
         if self.bm.window_blocks:
             raise N.PagedKVError(N.PA_ERR_UNSUPPORTED, "chunked prefill over a sliding-window ring")
         R = int(counts.sum())

@@ -175,7 +175,7 @@ def test_quantised_engine_steps_match_the_oracle(kv, ptok):
     assert not (err > 5e-3 + 1e-2 * np.abs(ref)).any(), f"max abs {err.max():.3e}"
 
 
-@pytest.mark.parametrize("kv", ["f16", "i8"])
+@pytest.mark.parametrize("kv", ["f16", "i8", "i4"])
 def test_chunked_prefill_then_decode(kv):
     # Prompts arrive in chunks through the engine (block manager, K/V write,
     # pa_prefill over the tables), with a fork between chunks so the next
@@ -186,8 +186,10 @@ def test_chunked_prefill_then_decode(kv):
     # attending at least 256 tokens would be held to the int8 bar (2e-2),
     # shorter ones, where one block's quantisation error shows through, to
     # 6e-2 — every row here is shorter, so this is a sanity bound on the
-    # engine's int8 path; the kernel's strict int8 check (against the oracle
-    # over the same codes) is in the prefill tests.
+    # engine's int8 path (int4, 18 times coarser steps, where a row of two
+    # tokens is off by up to a code step of about 0.5: 0.6); the kernels'
+    # strict checks (against the oracle over the same codes) are in the
+    # prefill tests.
     import paged_kv_cache_249_amd as pk
     from paged_kv_cache_249_amd.engine import PagedDecodeEngine
 
@@ -204,8 +206,10 @@ def test_chunked_prefill_then_decode(kv):
     # Sequence 3 is forked from 0 after 50 tokens: it shares those rows.
     K[3][:50], V[3][:50] = K[0][:50], V[0][:50]
 
-    i8 = kv == "i8"
-    eng = PagedDecodeEngine(256, Hh, Dd, pk.PA_I8 if i8 else pk.PA_F16, 4, 64, free_order=W.free_order(seed, 256),
+    i8 = kv != "f16"
+    code = {"f16": pk.PA_F16, "i8": pk.PA_I8, "i4": pk.PA_I4}[kv]
+    bound = 6e-2 if kv == "i8" else 0.6
+    eng = PagedDecodeEngine(256, Hh, Dd, code, 4, 64, free_order=W.free_order(seed, 256),
                             device=DEV, pool_fill=None if i8 else float("nan"))
     pos = {s: 0 for s in total}
 
@@ -219,7 +223,8 @@ def test_chunked_prefill_then_decode(kv):
                 assert not np.isnan(g).any(), f"seq {s} pos {p}: NaN"
                 err = np.abs(g - ref)
                 if i8:
-                    assert err.max() <= (2e-2 if p + 1 >= 256 else 6e-2), f"seq {s} pos {p}: max err {err.max():.3e}"
+                    lim = 2e-2 if kv == "i8" and p + 1 >= 256 else bound
+                    assert err.max() <= lim, f"seq {s} pos {p}: max err {err.max():.3e}"
                 else:
                     assert (err <= 5e-3 + 1e-2 * np.abs(ref)).all(), f"seq {s} pos {p}: max err {err.max():.3e}"
                 r += 1

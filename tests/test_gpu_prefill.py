@@ -196,10 +196,10 @@ def test_bad_lengths_flag_and_leave_rows_unwritten():
 def test_host_validation():
     pk = _pk()
     b = Chunks([20], [4], H=2, D=64, seed=1)
-    # int4 pools are not attended by pa_prefill.
-    i4 = pk.new_pool(4, 2, 64, pk.PA_I4, device=DEV)
+    # fp32 pools are not attended by pa_prefill.
+    f32 = pk.new_pool(4, 2, 64, pk.PA_F32, device=DEV)
     with pytest.raises(pk.PagedKVError) as e:
-        pk.pa_prefill(i4, b.qd, torch.empty_like(b.qd), b.qsd, b.tabd, b.ctxd, 4, 20)
+        pk.pa_prefill(f32, b.qd, torch.empty_like(b.qd), b.qsd, b.tabd, b.ctxd, 4, 20)
     assert e.value.status == pk.PA_ERR_UNSUPPORTED
     out = torch.empty_like(b.qd)
     with pytest.raises(pk.PagedKVError) as e:
@@ -227,12 +227,13 @@ def test_chunked_prefill_at_full_size_sampled_rows():
             assert_close(got[r:r + 1], ref, f"seq {s} row {i}")
 
 
-class Int8Chunks:
-    """Sequences quantised into an int8 pool (one fp16 scale per (block,
-    head), the oracle's quantiser) whose other bytes are random and whose
-    unused blocks have NaN scales; queries for the last ``nq[s]`` tokens."""
+class QuantChunks:
+    """Sequences quantised into an int8 or int4 pool (one fp16 scale per
+    (block, head), the oracle's quantiser; int4 packed two codes per byte)
+    whose other bytes are random and whose unused blocks have NaN scales;
+    queries for the last ``nq[s]`` tokens."""
 
-    def __init__(self, ctx, nq, H, D, bs=16, seed=0):
+    def __init__(self, ctx, nq, H, D, bs=16, seed=0, kv="i8"):
         pk = _pk()
         self.ctx, self.nq, self.bs = list(ctx), list(nq), bs
         nbs = [-(-c // bs) for c in ctx]
@@ -247,25 +248,33 @@ class Int8Chunks:
         for i, t in enumerate(self.tables):
             tab[i, :len(t)] = t
         rng = np.random.default_rng(seed)
-        kc = rng.integers(-128, 128, size=(NB, H, bs, D), dtype=np.int8)
-        vc = rng.integers(-128, 128, size=(NB, H, bs, D), dtype=np.int8)
+        if kv == "i8":
+            kc = rng.integers(-128, 128, size=(NB, H, bs, D), dtype=np.int8)
+            vc = rng.integers(-128, 128, size=(NB, H, bs, D), dtype=np.int8)
+        else:   # random codes in [-7, 7] (every nibble 1..15), kept unpacked until the writes are done
+            kc = rng.integers(-7, 8, size=(NB, H, bs, D), dtype=np.int8)
+            vc = rng.integers(-7, 8, size=(NB, H, bs, D), dtype=np.int8)
         ks = np.full((NB, H), np.nan, np.float16)
         vs = np.full((NB, H), np.nan, np.float16)
+        write = OC.write_kv_int8 if kv == "i8" else OC.write_kv_int4
         self.K, self.V = [], []
         for s, c in enumerate(ctx):
             K = W.normal_np((c, H, D), seed, W.STREAM_K, s, dtype=np.float32)
             V = W.normal_np((c, H, D), seed, W.STREAM_V, s, dtype=np.float32)
-            OC.write_kv_int8(kc, ks, vc, vs, K, V, OP.slots(c, self.tables[s], bs), block_size=bs)
+            write(kc, ks, vc, vs, K, V, OP.slots(c, self.tables[s], bs), block_size=bs)
             self.K.append(K)
             self.V.append(V)
         # The pools the kernel reads, dequantised in float64 (blocks nobody uses stay NaN).
         self.k_pool = kc.astype(np.float64) * ks.astype(np.float64)[:, :, None, None]
         self.v_pool = vc.astype(np.float64) * vs.astype(np.float64)[:, :, None, None]
+        if kv == "i4":
+            kc, vc = OC.pack_int4(kc), OC.pack_int4(vc)
         self.qs = np.concatenate([[0], np.cumsum(nq)]).astype(np.int32)
         self.q = W.normal_np((int(self.qs[-1]), H, D), seed, W.STREAM_Q, dtype=np.float16)
         t = {n: torch.from_numpy(a).to(DEV) for n, a in (("kc", kc), ("vc", vc), ("ks", ks), ("vs", vs))}
         self.t = t
-        self.pool = pk.pa_alloc_pool(NB, bs, H, D, pk.PA_I8, t["kc"], t["vc"], t["ks"], t["vs"])
+        self.pool = pk.pa_alloc_pool(NB, bs, H, D, pk.PA_I8 if kv == "i8" else pk.PA_I4, t["kc"], t["vc"],
+                                     t["ks"], t["vs"])
         self.qd = torch.from_numpy(self.q).to(DEV)
         self.qsd = torch.from_numpy(self.qs).to(DEV)
         self.tabd = torch.from_numpy(tab).to(DEV)
@@ -282,6 +291,10 @@ class Int8Chunks:
     def oracle(self):
         return OA.paged_prefill(self.q, self.k_pool, self.v_pool, self.tables, self.ctx, self.qs,
                                 block_size=self.bs)
+
+
+def Int8Chunks(*args, **kw):
+    return QuantChunks(*args, kv="i8", **kw)
 
 
 @pytest.mark.parametrize("D", [64, 128])
@@ -322,3 +335,16 @@ def test_int8_prefill_table_read_from_memory():
     # 33000 tokens in 16-token blocks: the table row is walked from memory.
     b = Int8Chunks([33000, 50], [40, 50], H=2, D=64, seed=43)
     assert_close(b.gpu(), b.oracle(), "int8 long table")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("bs", [16, 64])
+def test_int4_prefill_matches_the_oracle(D, bs):
+    # Packed int4 codes against fp64 prefill over the same dequantised codes: the fp16 bar.
+    b = QuantChunks(CTX, NQ, H=3, D=D, bs=bs, seed=5 * bs + D, kv="i4")
+    assert_close(b.gpu(), b.oracle(), f"int4 D={D} bs={bs}")
+
+
+def test_int4_prefill_table_read_from_memory():
+    b = QuantChunks([33000, 50], [40, 50], H=2, D=128, seed=47, kv="i4")
+    assert_close(b.gpu(), b.oracle(), "int4 long table")
