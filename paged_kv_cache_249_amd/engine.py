@@ -215,6 +215,8 @@ class PagedDecodeEngine:
         counts = np.asarray(counts, dtype=np.int64).reshape(-1)
         if seqs.size != counts.size or (counts < 0).any():
             raise N.PagedKVError(N.PA_ERR_INVALID_ARG, "seqs and counts must pair up, counts >= 0")
+        if np.unique(seqs).size != seqs.size:
+            raise N.PagedKVError(N.PA_ERR_INVALID_ARG, "a sequence appears twice in one chunk")
         if self.kv_dtype not in (N.PA_F16, N.PA_I8, N.PA_I4):
             raise N.PagedKVError(N.PA_ERR_UNSUPPORTED, "chunked prefill attends over fp16, int8 or int4 pools")
         if self.bm.window_blocks:

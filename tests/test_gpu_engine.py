@@ -260,3 +260,5 @@ def test_chunked_prefill_then_decode(kv):
         check(seqs, [1] * 4, out.cpu().numpy())
     with pytest.raises(pk.PagedKVError):
         eng.prefill([0], [2], k[:1], v[:1], q[:1], out[:1])     # 1 row for a chunk of 2
+    with pytest.raises(pk.PagedKVError):
+        eng.prefill([0, 0], [1, 1], k[:2], v[:2], q[:2], out[:2])   # one sequence twice
