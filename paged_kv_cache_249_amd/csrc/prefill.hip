@@ -353,8 +353,10 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(PrefillParams p)
   // exceeds it by more than kLazy, so weights stay below 2^kLazy and most
   // steps skip the rescale. Any reference gives the same quotient o / osum.
   float m[kPfTiles];
+  float thr[kPfTiles];   // raw q.k above which a logit exceeds m + kLazy
 #pragma unroll
   for (int qt = 0; qt < kPfTiles; ++qt) {
+    thr[qt] = -INFINITY;
 #pragma unroll
     for (int c = 0; c < kNT; ++c) o[qt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
     osum[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -407,14 +409,16 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(PrefillParams p)
         float mx = x[0];
 #pragma unroll
         for (int e = 1; e < 8; ++e) mx = fmaxf(mx, x[e]);
-        mx = col_max(mx);
-        const float ms = mx * c2;      // the column's step max in log2 units (-inf if all masked)
-        // Token 0 is visible to every query in the first step, so every m is
-        // finite after it and the first step always rescales (from m = -inf).
-        if (__any(ms > m[qt] + kLazy)) {
-          const float m_new = fmaxf(m[qt], ms);
+        // A logit of the column past m + kLazy shows in this lane's own
+        // maximum already (thr = (m + kLazy) / c2, c2 > 0): the column-wide
+        // maximum is needed only to move m. Token 0 is visible to every query
+        // in the first step, so every m is finite after it and the first step
+        // always rescales (from m = -inf, thr = -inf).
+        if (__any(mx > thr[qt])) {
+          const float m_new = fmaxf(m[qt], col_max(mx) * c2);
           const float alpha = __builtin_amdgcn_exp2f(m[qt] - m_new);
           m[qt] = m_new;
+          thr[qt] = (m_new + kLazy) / c2;
           // O rows are 4*grp + r: their factors live in the lanes whose column is that row.
           float ar[4];
 #pragma unroll
