@@ -39,7 +39,9 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed warm-up steps (default 10; prefill: 30 launches, which is where its "
+                         "launch time settles)")
     ap.add_argument("--partition-tokens", type=int, default=-1,
                     help="split-K partition size (0 = single pass, -1 = the tuned default)")
     ap.add_argument("--workload", default="opt13b",
@@ -219,7 +221,7 @@ def prefill_profile_cmds() -> dict:
     run = "-- python bench.py --workload prefill --profile-run --steps 5 --warmup 3"
     return {
         "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_prefill_trace -o trace "
-                 "-- python bench.py --workload prefill --steps 20 --warmup 5",
+                 "-- python bench.py --workload prefill --steps 100 --warmup 30 --no-cpu-baseline",
         "fetch": f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/prof_prefill_fetch -o fetch "
                  f"{run} > gpurun_out/prof_prefill_fetch.log",
         "write": f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/prof_prefill_write -o write "
@@ -488,6 +490,8 @@ def cpu_baseline(seconds: float) -> dict:
 # ---------------------------------------------------------------------------
 def main():
     args = parse()
+    if args.warmup is None:
+        args.warmup = 30 if args.workload == "prefill" else 10
     if args.cpu_baseline_only:
         if args.workload == "prefill":
             prefill_cpu_child(args.cpu_seconds)
