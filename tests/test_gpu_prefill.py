@@ -298,7 +298,7 @@ def Int8Chunks(*args, **kw):
 
 
 @pytest.mark.parametrize("D", [64, 128])
-@pytest.mark.parametrize("bs", [16, 64])
+@pytest.mark.parametrize("bs", [16, 32, 64])
 def test_int8_prefill_matches_the_oracle(D, bs):
     # Against fp64 prefill over the same dequantised codes: the fp16 bar.
     b = Int8Chunks(CTX, NQ, H=3, D=D, bs=bs, seed=3 * bs + D)
@@ -338,7 +338,7 @@ def test_int8_prefill_table_read_from_memory():
 
 
 @pytest.mark.parametrize("D", [64, 128])
-@pytest.mark.parametrize("bs", [16, 64])
+@pytest.mark.parametrize("bs", [16, 32, 64])
 def test_int4_prefill_matches_the_oracle(D, bs):
     # Packed int4 codes against fp64 prefill over the same dequantised codes: the fp16 bar.
     b = QuantChunks(CTX, NQ, H=3, D=D, bs=bs, seed=5 * bs + D, kv="i4")
@@ -348,3 +348,13 @@ def test_int4_prefill_matches_the_oracle(D, bs):
 def test_int4_prefill_table_read_from_memory():
     b = QuantChunks([33000, 50], [40, 50], H=2, D=128, seed=47, kv="i4")
     assert_close(b.gpu(), b.oracle(), "int4 long table")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_whole_prompt_of_4096_tokens(D):
+    # One 4096-token prompt attending causally at once (32 row tiles per
+    # (sequence, head), the longest walks) beside a short one.
+    b = Chunks([4096, 70], [4096, 70], H=2, D=D, seed=53)
+    got = b.gpu()
+    assert _pk().pa_check_errors() == 0
+    assert_close(got, b.oracle(), f"4096-token prompt D={D}")
