@@ -210,7 +210,10 @@ class PagedDecodeEngine:
         slots, and the chunk's rows attend causally over their sequences'
         tables at once (``pa_prefill``), results in ``out``. fp16, int8 or
         int4 pools (a quantised pool codes each chunk's rows per (block, head)
-        as it writes them), fp16 queries."""
+        as it writes them), fp16 queries. Arguments are checked before any
+        state changes; if the pool runs out of blocks part-way, the sequences
+        before the failing one keep the tokens already appended (each append
+        is atomic in the block manager) and nothing is launched."""
         seqs = np.asarray(seqs, dtype=np.int64).reshape(-1)
         counts = np.asarray(counts, dtype=np.int64).reshape(-1)
         if seqs.size != counts.size or (counts < 0).any():
@@ -224,6 +227,9 @@ class PagedDecodeEngine:
         R = int(counts.sum())
         if tuple(k_rows.shape[:1]) != (R,) or q_rows.shape != k_rows.shape or v_rows.shape != k_rows.shape:
             raise N.PagedKVError(N.PA_ERR_INVALID_ARG, "row counts do not match the chunk sizes")
+        for s in seqs.tolist():
+            if self.bm.has_seq(s) and self.bm.is_swapped(s):
+                raise N.PagedKVError(N.PA_ERR_STATE, f"sequence {s} is swapped out")
         slots, pairs = [], []
         for s, c in zip(seqs.tolist(), counts.tolist()):
             if not self.bm.has_seq(s):
