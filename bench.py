@@ -993,8 +993,33 @@ def prefill_probe(pk, W, torch, np, dev, H=40, D=128):
         res[f"whole_prompt_{name}_pool"] = {"us": round(t * 1e6, 2), "tflops": round(fl / t / 1e12, 1),
                                            "frac_of_mfma_peak": round(fl / t / 1e12 / MFMA_PEAK_F16_TFLOPS, 4)}
         del q, out, qp
-    assert pk.pa_check_errors() == 0
     del pool
+    torch.cuda.empty_cache()
+    # A few new tokens per sequence (multi-token decoding) over the
+    # OPT-13B-shaped decode batch's contexts: a memory-bound launch, rated in
+    # KV bytes read per second, dispatched longest first.
+    wl = W.opt13b()
+    ctxs = np.asarray(wl.context_lens, dtype=np.int64)
+    nbs = -(-ctxs // 16)
+    bpool = pk.new_pool(int(nbs.sum()) + 8, H, D, pk.PA_F16, device=dev)
+    bpool.k_cache.normal_(generator=g)
+    bpool.v_cache.normal_(generator=g)
+    perm = W.free_order(seed, bpool.num_blocks)
+    btab = np.full((len(ctxs), int(nbs.max())), -1, np.int32)
+    used = 0
+    for s, nb in enumerate(nbs):
+        btab[s, :nb] = perm[used:used + nb]
+        used += nb
+    btabd, bctx = torch.from_numpy(btab).to(dev), torch.from_numpy(ctxs.astype(np.int32)).to(dev)
+    order = torch.from_numpy(np.argsort(-ctxs, kind="stable").astype(np.int32)).to(dev)
+    kv = int(ctxs.sum()) * H * D * 2 * 2
+    for nt in (1, 4, 16):
+        q, out, qs = prefill_chunk(torch, np, dev, g, len(ctxs), nt, H, D)
+        t = _time_calls(lambda: pk.pa_prefill(bpool, q, out, qs, btabd, bctx, nt, int(ctxs.max()), seq_order=order))
+        res[f"decode_batch_{nt}_new_tokens"] = {"us": round(t * 1e6, 2), "kv_gbs": round(kv / t / 1e9, 1)}
+        del q, out
+    assert pk.pa_check_errors() == 0
+    del bpool
     torch.cuda.empty_cache()
     return res
 

@@ -281,6 +281,18 @@ pa_status pa_prefill(pa_pool* pool, const void* q, pa_dtype q_dtype, void* out,
                      int32_t max_query_len, int32_t max_context_len, float sm_scale,
                      pa_stream stream);
 
+/* pa_prefill with a dispatch order: seq_order (device int32 [num_seqs]) is
+ * a permutation of the batch and sequences are dispatched in that order
+ * (callers pass them longest first, so a long sequence does not stretch the
+ * launch's tail); NULL is batch order. Results are identical to pa_prefill's
+ * whatever the order. An entry outside [0, num_seqs) flags
+ * PA_DEV_BAD_CONTEXT and that work is skipped. Otherwise as pa_prefill. */
+pa_status pa_prefill_ordered(pa_pool* pool, const void* q, pa_dtype q_dtype, void* out,
+                             const int32_t* query_start, int32_t num_rows, const int32_t* block_tables,
+                             int32_t max_blocks, const int32_t* context_lens, const int32_t* seq_order,
+                             int32_t num_seqs, int32_t max_query_len, int32_t max_context_len, float sm_scale,
+                             pa_stream stream);
+
 /* pa_write_kv followed by pa_decode_ordered, in one launch, for float pools:
  * row s of k_new / v_new ([num_seqs][num_heads][head_dim], src_dtype PA_F32
  * or PA_F16) is sequence s's newest token and slot_mapping[s] (device int64)

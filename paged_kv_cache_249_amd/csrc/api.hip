@@ -318,6 +318,15 @@ pa_status pa_prefill(pa_pool* pool, const void* q, pa_dtype q_dtype, void* out, 
                      int32_t num_rows, const int32_t* block_tables, int32_t max_blocks,
                      const int32_t* context_lens, int32_t num_seqs, int32_t max_query_len,
                      int32_t max_context_len, float sm_scale, pa_stream stream) {
+  return pa_prefill_ordered(pool, q, q_dtype, out, query_start, num_rows, block_tables, max_blocks, context_lens,
+                            nullptr, num_seqs, max_query_len, max_context_len, sm_scale, stream);
+}
+
+pa_status pa_prefill_ordered(pa_pool* pool, const void* q, pa_dtype q_dtype, void* out,
+                             const int32_t* query_start, int32_t num_rows, const int32_t* block_tables,
+                             int32_t max_blocks, const int32_t* context_lens, const int32_t* seq_order,
+                             int32_t num_seqs, int32_t max_query_len, int32_t max_context_len, float sm_scale,
+                             pa_stream stream) {
   const char* fn = "pa_prefill";
   if (!pool) return fail(PA_ERR_INVALID_ARG, "%s: pool is NULL", fn);
   if (pool->kv_dtype != PA_F16 && pool->kv_dtype != PA_I8 && pool->kv_dtype != PA_I4)
@@ -343,6 +352,7 @@ pa_status pa_prefill(pa_pool* pool, const void* q, pa_dtype q_dtype, void* out, 
   a.tables = block_tables;
   a.max_blocks = max_blocks;
   a.ctx = context_lens;
+  a.order = seq_order;
   a.num_seqs = num_seqs;
   a.max_query_len = max_query_len;
   a.max_ctx = max_context_len;

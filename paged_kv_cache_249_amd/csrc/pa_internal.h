@@ -105,6 +105,7 @@ struct PrefillArgs {
   const int32_t* tables;
   int32_t max_blocks;
   const int32_t* ctx;
+  const int32_t* order;        // [num_seqs] dispatch order, or nullptr
   int32_t num_seqs;
   int32_t max_query_len;
   int32_t max_ctx;

@@ -54,6 +54,8 @@ struct PrefillParams {
   const int32_t* query_start;    // [S + 1]
   const int32_t* tables;         // [S][max_blocks]
   const int32_t* ctx;            // [S]
+  const int32_t* order;          // [S] dispatch order (a permutation), or nullptr
+  int32_t num_seqs;
   int32_t num_rows;
   int32_t max_blocks;
   int32_t num_heads;
@@ -164,15 +166,31 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(PrefillParams p)
   const int grp = lane >> 4;       // MFMA lane group (k slice / output row quad)
 
   // Workgroup -> (sequence, head, row tile). Workgroups are dealt to the 8
-  // XCDs round robin; remapping puts consecutive (row tile, head) items on
-  // one XCD so the row tiles of one (sequence, head) share its L2. The
-  // heaviest row tile (the last rows attend to the most tokens) goes first.
-  const int total = int(gridDim.x);
-  int id = int(blockIdx.x);
-  if ((total & 7) == 0) id = (id & 7) * (total >> 3) + (id >> 3);
-  const int tile = p.row_tiles - 1 - id % p.row_tiles;
-  const int h = (id / p.row_tiles) % p.num_heads;
-  const int s = id / (p.row_tiles * p.num_heads);
+  // XCDs round robin (block b runs on XCD b % 8, as its (b / 8)-th). Groups
+  // (the row tiles of one (sequence, head)) are dealt round robin over the
+  // XCDs in dispatch order, each group's tiles consecutive on one XCD so they
+  // share its L2: XCD x takes groups x, x + 8, ... — every XCD gets its share
+  // of long and short sequences whatever the order. The heaviest row tile
+  // (the last rows attend to the most tokens) goes first.
+  const int T = p.row_tiles;
+  const int groups = int(gridDim.x) / T;
+  int g, k;
+  if ((groups & 7) == 0) {
+    const int x = int(blockIdx.x) & 7, j = int(blockIdx.x) >> 3;
+    g = x + 8 * (j / T);
+    k = j % T;
+  } else {
+    g = int(blockIdx.x) / T;
+    k = int(blockIdx.x) % T;
+  }
+  const int tile = T - 1 - k;
+  const int h = g % p.num_heads;
+  const int rank = g / p.num_heads;
+  const int s = p.order ? p.order[rank] : rank;      // sequences in the caller's dispatch order
+  if (unsigned(s) >= unsigned(p.num_seqs)) {
+    if (tile == 0 && h == 0 && threadIdx.x == 0) flag_error(p.err, PA_DEV_BAD_CONTEXT);
+    return;
+  }
 
   // Everything up to the loop depends on (s, tile) only, so a workgroup
   // leaves as a whole or not at all (the loop has barriers).
@@ -558,6 +576,8 @@ int launch_prefill(const PrefillArgs& a, void* stream) {
   p.query_start = a.query_start;
   p.tables = a.tables;
   p.ctx = a.ctx;
+  p.order = a.order;
+  p.num_seqs = a.num_seqs;
   p.num_rows = a.num_rows;
   p.max_blocks = a.max_blocks;
   p.num_heads = a.pool->num_heads;

@@ -249,9 +249,13 @@ class PagedDecodeEngine:
             if R:
                 sl = torch.from_numpy(np.concatenate(slots)).to(self.device, non_blocking=False)
                 N.pa_write_kv(self.pool, k_rows, v_rows, sl, stream=cur)
+                # Heaviest sequences first (pairs attended: n (2 ctx - n + 1) / 2),
+                # so a long one does not stretch the launch's tail.
+                work = counts * (2 * ctx.astype(np.int64) - counts + 1)
+                order = torch.from_numpy(np.argsort(-work, kind="stable").astype(np.int32)).to(self.device)
                 N.pa_prefill(self.pool, q_rows, out, torch.from_numpy(qs).to(self.device),
                              torch.from_numpy(tables).to(self.device), torch.from_numpy(ctx).to(self.device),
-                             int(counts.max()), int(ctx.max()), stream=cur)
+                             int(counts.max()), int(ctx.max()), stream=cur, seq_order=order)
         self.last_ctx = ctx.copy()
         self.last_pairs = len(pairs)
 

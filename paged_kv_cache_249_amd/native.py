@@ -72,6 +72,7 @@ _SIGS = {
     "pa_write_decode": ([_vp, _vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _f32,
                          _i32, _vp, _i64, _vp], _i32),
     "pa_prefill": ([_vp, _vp, _i32, _vp, _vp, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _f32, _vp], _i32),
+    "pa_prefill_ordered": ([_vp, _vp, _i32, _vp, _vp, _i32, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _f32, _vp], _i32),
     "pa_check_errors": ([_vp, _pi32], _i32),
     "pa_decode_contiguous": ([_vp, _vp, _i32, _i32, _i32, _i32, _vp, _i32, _vp, _vp, _vp, _i32, _f32, _i32,
                               _vp, _i64, _vp], _i32),
@@ -343,10 +344,12 @@ def pa_decode(pool: Pool, q, out, block_tables, context_lens, max_context_len: i
 
 
 def pa_prefill(pool: Pool, q, out, query_start, block_tables, context_lens, max_query_len: int,
-               max_context_len: int, sm_scale: float = 0.0, stream=None) -> None:
+               max_context_len: int, sm_scale: float = 0.0, stream=None, seq_order=None) -> None:
     """Several new tokens per sequence at once: ``q``/``out`` fp16
     ``[rows][heads][head_dim]``, rows ``query_start[s] .. query_start[s+1]``
-    being the last tokens of sequence ``s`` (int32 ``[S+1]`` on the device)."""
+    being the last tokens of sequence ``s`` (int32 ``[S+1]`` on the device).
+    ``seq_order`` (device int32 ``[S]``, a permutation) sets the dispatch
+    order (pa_prefill_ordered)."""
     torch = _torch()
     S = int(query_start.numel()) - 1
     R = int(q.shape[0])
@@ -355,11 +358,21 @@ def pa_prefill(pool: Pool, q, out, query_start, block_tables, context_lens, max_
         raise PagedKVError(PA_ERR_INVALID_ARG, "q/out/query_start shape or dtype mismatch")
     if block_tables.dim() != 2 or block_tables.shape[0] < S or context_lens.numel() < S:
         raise PagedKVError(PA_ERR_INVALID_ARG, "block_tables/context_lens do not cover the batch")
-    _check(lib.pa_prefill(pool.handle, _ptr(q, "q"), dtype_code(q.dtype), _ptr(out, "out"),
-                          _ptr(query_start, "query_start", torch.int32), R,
-                          _ptr(block_tables, "block_tables", torch.int32), int(block_tables.shape[1]),
-                          _ptr(context_lens, "context_lens", torch.int32), S, int(max_query_len),
-                          int(max_context_len), float(sm_scale), _stream(stream, q)), "pa_prefill")
+    if seq_order is None:
+        _check(lib.pa_prefill(pool.handle, _ptr(q, "q"), dtype_code(q.dtype), _ptr(out, "out"),
+                              _ptr(query_start, "query_start", torch.int32), R,
+                              _ptr(block_tables, "block_tables", torch.int32), int(block_tables.shape[1]),
+                              _ptr(context_lens, "context_lens", torch.int32), S, int(max_query_len),
+                              int(max_context_len), float(sm_scale), _stream(stream, q)), "pa_prefill")
+        return
+    if seq_order.numel() < S:
+        raise PagedKVError(PA_ERR_INVALID_ARG, "seq_order does not cover the batch")
+    _check(lib.pa_prefill_ordered(pool.handle, _ptr(q, "q"), dtype_code(q.dtype), _ptr(out, "out"),
+                                  _ptr(query_start, "query_start", torch.int32), R,
+                                  _ptr(block_tables, "block_tables", torch.int32), int(block_tables.shape[1]),
+                                  _ptr(context_lens, "context_lens", torch.int32),
+                                  _ptr(seq_order, "seq_order", torch.int32), S, int(max_query_len),
+                                  int(max_context_len), float(sm_scale), _stream(stream, q)), "pa_prefill_ordered")
 
 
 def pa_demote_blocks(hot: Pool, cold: Pool, pairs, stream=None) -> None:

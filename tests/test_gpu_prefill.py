@@ -83,12 +83,13 @@ class Chunks:
         self.tabd = torch.from_numpy(tab).to(DEV)
         self.ctxd = torch.tensor(ctx, dtype=torch.int32, device=DEV)
 
-    def gpu(self, max_query_len=None, max_ctx=None, sm_scale=0.0):
+    def gpu(self, max_query_len=None, max_ctx=None, sm_scale=0.0, seq_order=None):
         pk = _pk()
         out = torch.full_like(self.qd, float("nan"))
+        order = None if seq_order is None else torch.tensor(seq_order, dtype=torch.int32, device=DEV)
         pk.pa_prefill(self.pool, self.qd, out, self.qsd, self.tabd, self.ctxd,
                       max(self.nq) if max_query_len is None else max_query_len,
-                      max(self.ctx) if max_ctx is None else max_ctx, sm_scale)
+                      max(self.ctx) if max_ctx is None else max_ctx, sm_scale, seq_order=order)
         torch.cuda.synchronize()
         return out.cpu().numpy()
 
@@ -179,6 +180,30 @@ def test_bad_table_entry_is_flagged(ctx):
     got = b.gpu()
     assert pk.pa_check_errors() & pk.PA_DEV_BAD_TABLE_ENTRY
     assert_close(got[40:], b.oracle()[40:], "good sequence beside a bad table row")
+
+
+def test_dispatch_order_changes_nothing():
+    # pa_prefill_ordered: any permutation of the batch gives the same bits.
+    pk = _pk()
+    b = Chunks(CTX, NQ, H=3, D=128, seed=61)
+    ref = b.gpu()
+    S = len(CTX)
+    work = [n * (2 * c - n + 1) // 2 for c, n in zip(CTX, NQ)]
+    rng = np.random.default_rng(61)
+    for order in (sorted(range(S), key=lambda s: -work[s]), list(rng.permutation(S)), list(range(S))[::-1]):
+        got = b.gpu(seq_order=order)
+        assert pk.pa_check_errors() == 0
+        assert np.array_equal(got.view(np.uint16), ref.view(np.uint16)), order
+    # An entry outside the batch is flagged and its work skipped; the rest is computed.
+    bad = list(range(S))
+    bad[2] = S + 3
+    got = b.gpu(seq_order=bad)
+    assert pk.pa_check_errors() & pk.PA_DEV_BAD_CONTEXT
+    r2 = slice(int(b.qs[2]), int(b.qs[3]))
+    assert np.isnan(got[r2]).all()
+    keep = np.ones(got.shape[0], bool)
+    keep[r2] = False
+    assert np.array_equal(got[keep].view(np.uint16), ref[keep].view(np.uint16))
 
 
 def test_bad_lengths_flag_and_leave_rows_unwritten():
