@@ -383,3 +383,28 @@ def test_whole_prompt_of_4096_tokens(D):
     got = b.gpu()
     assert _pk().pa_check_errors() == 0
     assert_close(got, b.oracle(), f"4096-token prompt D={D}")
+
+
+@pytest.mark.parametrize("kv", ["f16", "i8", "i4"])
+@pytest.mark.parametrize("seed", [71, 72, 73])
+def test_random_batches_against_the_oracle(kv, seed):
+    # Seeded random batches: 12 sequences with contexts of 1..1500 tokens,
+    # chunks of 0..ctx rows (whole prompts, single rows and empty chunks
+    # included), a random head_dim and block size, dispatched in a random
+    # order; every row against the oracle.
+    rng = np.random.default_rng(seed)
+    D = int(rng.choice([64, 128]))
+    bs = int(rng.choice([16, 32, 64]))
+    ctx = [int(c) for c in rng.integers(1, 1500, 12)]
+    ctx[0] = 1
+    nq = [int(rng.integers(0, c + 1)) for c in ctx]
+    nq[1] = ctx[1]
+    nq[2] = 0
+    if kv == "f16":
+        b = Chunks(ctx, nq, H=2, D=D, bs=bs, seed=seed)
+        got = b.gpu(seq_order=list(rng.permutation(len(ctx))))
+    else:
+        b = QuantChunks(ctx, nq, H=2, D=D, bs=bs, seed=seed, kv=kv)
+        got = b.gpu()
+    assert _pk().pa_check_errors() == 0
+    assert_close(got, b.oracle(), f"{kv} seed={seed} D={D} bs={bs}")
