@@ -625,3 +625,21 @@ def test_block_size_rejects_partitions_that_split_a_block():
     with pytest.raises(pk.PagedKVError) as e:
         b.gpu(32)
     assert e.value.status == pk.PA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("seed", [81, 82, 83, 84])
+def test_random_batches_against_the_oracle(seed):
+    # Seeded random batches: 24 sequences with contexts of 1..3000 tokens in a
+    # NaN-poisoned pool, a random KV/query dtype pair, head_dim, block size and
+    # partition size (single pass or split-K in whole blocks); every output
+    # against the oracle.
+    rng = np.random.default_rng(seed)
+    kv, q = [("f16", "f16"), ("f16", "f32"), ("f32", "f32")][int(rng.integers(0, 3))]
+    D = int(rng.choice([64, 128]))
+    bs = int(rng.choice([16, 32, 64]))
+    ptok = int(rng.choice([0, bs, 4 * bs, 512]))
+    ctx = [int(c) for c in rng.integers(1, 3000, 24)]
+    b = Batch(ctx, 3, D, kv, q, seed=seed, poison=True, bs=bs)
+    got, _ = b.gpu(ptok)
+    atol, rtol = (F32_ATOL, F32_RTOL) if kv == "f32" and q == "f32" else (F16_ATOL, F16_RTOL)
+    assert_close(got, b.oracle(), atol, rtol, f"seed={seed} {kv}/{q} D={D} bs={bs} ptok={ptok}")
