@@ -526,7 +526,7 @@ def main():
     num_blocks = eng.pool.num_blocks
     seqs = np.arange(S)
     torch.cuda.synchronize()
-    assert pk.pa_check_errors() == 0
+    assert pk.pa_check_errors(eng.pool) == 0
 
     # Warm-up steps carry timing events like the timed steps do: the first
     # timed event pair of a process can stall the host for tens of ms.
@@ -580,7 +580,7 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     gc.enable()
-    dev_err = pk.pa_check_errors()
+    dev_err = pk.pa_check_errors(eng.pool)
     wall = t1 - t0
     dec_ms = [events[i][0].elapsed_time(events[i][1]) for i in timed]
     dec_avg_s = sum(dec_ms) / len(dec_ms) / 1e3
@@ -1018,7 +1018,7 @@ def prefill_probe(pk, W, torch, np, dev, H=40, D=128):
         t = _time_calls(lambda: pk.pa_prefill(bpool, q, out, qs, btabd, bctx, nt, int(ctxs.max()), seq_order=order))
         res[f"decode_batch_{nt}_new_tokens"] = {"us": round(t * 1e6, 2), "kv_gbs": round(kv / t / 1e9, 1)}
         del q, out
-    assert pk.pa_check_errors() == 0
+    assert pk.pa_check_errors(bpool) == 0
     del bpool
     torch.cuda.empty_cache()
     return res
@@ -1045,7 +1045,7 @@ def prefill_main(args) -> int:
     for _ in range(args.warmup):
         launch()
     torch.cuda.synchronize()
-    assert pk.pa_check_errors() == 0
+    assert pk.pa_check_errors(pool) == 0
     if args.profile_run:
         a = torch.empty(CALIBRATION_BYTES, dtype=torch.uint8, device=dev)
         b = torch.empty(CALIBRATION_BYTES, dtype=torch.uint8, device=dev)
@@ -1092,7 +1092,7 @@ def prefill_main(args) -> int:
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_PEAK_F16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_PEAK_F16_TFLOPS, 4),
                      "traffic": recorded_prefill_traffic()},
-        "device_error_bits": pk.pa_check_errors(),
+        "device_error_bits": pk.pa_check_errors(pool),
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = prefill_cpu_baseline(args.cpu_seconds)

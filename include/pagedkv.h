@@ -24,8 +24,10 @@
  *   is enqueued. A launch failure returns PA_ERR_HIP.
  * - Device-side indices (table entries, slots, copy pairs) are range-checked
  *   in the kernels: an out-of-range entry is skipped (a table entry is
- *   treated as masked, a slot or pair is not written) and a sticky device
- *   error word is set; pa_check_errors() reads and clears it.
+ *   treated as masked, a slot or pair is not written) and a bit is set in the
+ *   pool's own sticky device error word; pa_check_errors(pool, ...) reads and
+ *   clears that word alone, atomically. Calls tied to no pool
+ *   (pa_decode_contiguous) flag a word of their own, read with pool = NULL.
  * - Layouts (all row-major, element type given by the pool dtype):
  *     K, V pools    [num_blocks][num_heads][block_size][head_dim]
  *                   (PA_I4: [...][head_dim / 2] bytes, two codes per byte)
@@ -80,8 +82,9 @@ enum {
   PA_DEV_BAD_SLOT = 2,         /* a slot outside the pool                      */
   PA_DEV_BAD_PAIR = 4,         /* a copy pair outside the pool                 */
   PA_DEV_BAD_CONTEXT = 8,      /* context_lens[s] < 0 or > the stated maximum  */
-  PA_DEV_BAD_RUN = 16          /* int8/int4 write: one block hit by more than
-                                  block_size rows of one run (duplicate slots) */
+  PA_DEV_BAD_RUN = 16          /* int8/int4 write: one block hit by duplicate
+                                  slots, by more than block_size rows, or by
+                                  two runs of rows that are not adjacent     */
 };
 
 /* Text of the last failing call on this thread ("" if none). Never NULL. */
@@ -112,13 +115,22 @@ pa_status pa_pool_bytes(int32_t num_blocks, int32_t block_size, int32_t num_head
  * each hold pa_pool_bytes(...)->kv_bytes and be 16-byte aligned; k_scale /
  * v_scale must be given for PA_I8 and PA_I4 and NULL otherwise. The buffers stay owned
  * by the caller and must outlive the descriptor. *out receives the handle.
+ * The pool belongs to the device current at this call, and takes one of the
+ * library's 4095 device error words (cleared here, with a synchronous copy)
+ * until pa_free_pool; every later call on the pool must run with that device
+ * current.
+ * In a process that sees no GPU the descriptor is still made, without an
+ * error word, so that host-side validation can be exercised; any of its
+ * calls that reaches a kernel launch then fails with PA_ERR_HIP.
  * Errors: as pa_pool_bytes, plus PA_ERR_INVALID_ARG for null or misaligned
- * buffers and scales given for a float pool. */
+ * buffers and scales given for a float pool, PA_ERR_OUT_OF_RANGE if 4095
+ * pools are alive, PA_ERR_HIP. */
 pa_status pa_alloc_pool(int32_t num_blocks, int32_t block_size, int32_t num_heads,
                         int32_t head_dim, pa_dtype kv_dtype, void* k_cache, void* v_cache,
                         void* k_scale, void* v_scale, pa_pool** out);
 
-/* Destroy the descriptor (never the buffers). NULL is accepted. */
+/* Destroy the descriptor (never the buffers) and return its error word.
+ * Kernels enqueued on the pool must have completed. NULL is accepted. */
 pa_status pa_free_pool(pa_pool* pool);
 
 /* ----------------------------------------------------------------------------
@@ -140,11 +152,14 @@ pa_status pa_free_pool(pa_pool* pool);
  * becomes s. All arithmetic is IEEE fp32 with correctly rounded division.
  * int4 pools (INT4, the next step of the same page's list) follow the same
  * rule with 7 in place of 127, codes stored as in the PA_I4 layout.
- * Precondition for int8 and int4 pools: the entries of slot_mapping that hit one block
- * are adjacent (true for decode, one row per sequence, and for a sequence's
- * prefill in token order); otherwise the result for that block is unspecified
- * (never out of bounds).
- * Duplicate slots in one call leave one of the rows (which one is unspecified).
+ * Precondition for int8 and int4 pools: the entries of slot_mapping that hit
+ * one block are adjacent and distinct, at most block_size of them (true for
+ * decode, one row per sequence, and for a sequence's prefill in token order).
+ * A call that breaks it flags PA_DEV_BAD_RUN; the content of that block is
+ * then unspecified (never out of bounds). Checking two runs costs the wave of
+ * each run leader (head 0, K) a read of the slots before it.
+ * Float pools: duplicate slots in one call leave one of the rows (which one
+ * is unspecified).
  * n == 0 is a no-op. Errors: PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_HIP.
  */
 pa_status pa_write_kv(pa_pool* pool, const void* k_new, const void* v_new, pa_dtype src_dtype,
@@ -332,9 +347,18 @@ pa_status pa_write_decode(pa_pool* pool, const void* k_new, const void* v_new, p
  * source that is not pinned host memory), PA_ERR_HIP. */
 pa_status pa_stage_copy(void* dst, const void* host_src, int64_t bytes, pa_stream stream);
 
-/* Read and clear the sticky device error word (PA_DEV_* bits). Synchronises
- * the stream first. *device_error may be NULL to only clear. */
-pa_status pa_check_errors(pa_stream stream, int32_t* device_error);
+/* Read and clear the device error word of `pool` (PA_DEV_* bits set by the
+ * kernels of calls on that pool since it was last read; NULL: the word of calls
+ * tied to no pool). A one-thread kernel on `stream` swaps the word with 0
+ * after the stream's earlier work, so a flag set at any moment is reported
+ * exactly once; the call then synchronises the stream. Flags set by kernels
+ * still running on other streams are reported by a later call. Pools do not
+ * share words: checking one leaves the others' flags in place. Mixed pages
+ * (pa_demote_blocks, pa_decode_mixed) flag the cold pool's word.
+ * *device_error may be NULL to only clear. Concurrent calls are serialised.
+ * Errors: PA_ERR_INVALID_ARG (pool on another device than the current one),
+ * PA_ERR_HIP. */
+pa_status pa_check_errors(const pa_pool* pool, pa_stream stream, int32_t* device_error);
 
 /* ----------------------------------------------------------------------------
  * Measurement helpers (not part of the method).

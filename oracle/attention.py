@@ -140,7 +140,8 @@ def split_decode(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float,
 
 def paged_prefill(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray, block_tables,
                   context_lens, query_start, scale: float | None = None,
-                  block_size: int = 16) -> np.ndarray:
+                  block_size: int = 16, k_scale: np.ndarray | None = None,
+                  v_scale: np.ndarray | None = None) -> np.ndarray:
     """Several new tokens of each sequence attend at once (float64).
 
     The attention formula of "One Deep Concept #01", §2 Background, takes a
@@ -153,7 +154,9 @@ def paged_prefill(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray, block_t
 
     ``q``: [N][H][D], rows ``query_start[s] .. query_start[s+1]`` belonging to
     sequence ``s`` in position order; their K and V are already in the pools.
-    Returns [N][H][D] float64.
+    For int8 or int4 pools pass the codes (int4 unpacked) and the per-(block,
+    head) scales, as for :func:`paged_decode`; codes are dequantised exactly in
+    float64. Returns [N][H][D] float64.
     """
     q = np.asarray(q, dtype=np.float64)
     N, H, D = q.shape
@@ -167,8 +170,8 @@ def paged_prefill(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray, block_t
             continue
         if n > ctx:
             raise ValueError("more new tokens than the context holds")
-        K = paging.gather(k_pool, block_tables[s], ctx, block_size)
-        V = paging.gather(v_pool, block_tables[s], ctx, block_size)
+        K = paging.gather(k_pool, block_tables[s], ctx, block_size, k_scale)
+        V = paging.gather(v_pool, block_tables[s], ctx, block_size, v_scale)
         pos = ctx - n + np.arange(n)                               # [n]
         allowed = np.arange(ctx)[None, :] <= pos[:, None]          # [n][ctx]
         for h in range(H):

@@ -23,7 +23,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpagedkv.so")
 
 HIP_SOURCES = ["api.hip", "decode.hip", "cache_ops.hip", "prefill.hip"]
-CXX_SOURCES = ["block_manager.cpp", "mixed_manager.cpp"]
+CXX_SOURCES = ["block_manager.cpp", "mixed_manager.cpp", "errors.cpp"]
 
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

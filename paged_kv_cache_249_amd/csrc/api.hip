@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <deque>
 #include <mutex>
 #include <new>
 #include <string>
@@ -15,53 +16,108 @@
 
 namespace pa {
 
+// Device error words. Word 0 takes the flags of calls tied to no pool
+// (pa_decode_contiguous); every live pool owns one of the others, handed out
+// by pa_alloc_pool and returned by pa_free_pool, so the flags of two pools
+// never mix and reading one pool's word leaves the others alone. Each GPU
+// holds its own copy of both arrays; host code reaches them through the
+// addresses that hipGetSymbolAddress gives on each device.
+__device__ int32_t g_error_words[kErrorWords];
+// Where pa_check_errors' read-and-clear kernel leaves the old value of a word.
+__device__ int32_t g_error_readout[kErrorWords];
+
 namespace {
-thread_local std::string g_last_error;
 
 constexpr int kMaxDevices = 64;
-std::mutex g_err_mutex;
-int32_t* g_err_ptr[kMaxDevices] = {};
+
+struct DeviceWords {
+  int32_t* words = nullptr;
+  int32_t* readout = nullptr;
+};
+
+std::mutex g_err_mutex;               // guards the tables below and readouts
+DeviceWords g_dev_words[kMaxDevices];
+std::deque<int32_t> g_free_words;     // FIFO: a freed word is reused last
+bool g_words_init = false;
+
+// Device addresses of the error arrays on device dev (looked up once per
+// device, with that device current). Caller holds g_err_mutex.
+hipError_t words_of(int dev, DeviceWords* out) {
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  DeviceWords& w = g_dev_words[dev];
+  if (!w.words) {
+    void* a = nullptr;
+    void* b = nullptr;
+    hipError_t e = hipGetSymbolAddress(&a, HIP_SYMBOL(g_error_words));
+    if (e != hipSuccess) return e;
+    e = hipGetSymbolAddress(&b, HIP_SYMBOL(g_error_readout));
+    if (e != hipSuccess) return e;
+    w.words = static_cast<int32_t*>(a);
+    w.readout = static_cast<int32_t*>(b);
+  }
+  *out = w;
+  return hipSuccess;
+}
+
+// One thread swaps the word with 0 and keeps the old value: no flag set by a
+// kernel between the read and the clear can be lost.
+__global__ void read_clear_kernel(int32_t* word, int32_t* readout) { *readout = atomicExch(word, 0); }
+
 }  // namespace
 
-// The sticky device error word (one per device; each GPU holds its own copy).
-__device__ int32_t g_device_error;
-
-pa_status fail(pa_status st, const char* fmt, ...) {
-  char buf[512];
-  va_list ap;
-  va_start(ap, fmt);
-  vsnprintf(buf, sizeof(buf), fmt, ap);
-  va_end(ap);
-  g_last_error = buf;
-  return st;
-}
-
-void clear_error() { g_last_error.clear(); }
-
-// Device address of g_device_error on the current device (looked up once per
-// device). Returns nullptr if the lookup fails; kernels then skip flagging.
-int32_t* device_error_ptr() {
+int acquire_error_word(int32_t* slot, int32_t** word, int32_t* device) {
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return int(e);
   std::lock_guard<std::mutex> lock(g_err_mutex);
-  if (!g_err_ptr[dev]) {
-    void* ptr = nullptr;
-    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(g_device_error)) != hipSuccess) return nullptr;
-    g_err_ptr[dev] = static_cast<int32_t*>(ptr);
+  DeviceWords w;
+  e = words_of(dev, &w);
+  if (e != hipSuccess) return int(e);
+  if (!g_words_init) {
+    for (int32_t i = 1; i < kErrorWords; ++i) g_free_words.push_back(i);
+    g_words_init = true;
   }
-  return g_err_ptr[dev];
+  if (g_free_words.empty()) return int(hipErrorOutOfMemory);
+  const int32_t i = g_free_words.front();
+  // A word starts clear whatever an earlier pool left in it (synchronous copy).
+  const int32_t zero = 0;
+  e = hipMemcpy(w.words + i, &zero, sizeof(zero), hipMemcpyHostToDevice);
+  if (e != hipSuccess) return int(e);
+  g_free_words.pop_front();
+  *slot = i;
+  *word = w.words + i;
+  *device = dev;
+  return 0;
 }
 
-int read_and_clear_device_error(void* stream, int32_t* value) {
-  int32_t* ptr = device_error_ptr();
-  if (!ptr) return int(hipErrorInvalidSymbol);
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  int32_t host = 0;
-  hipError_t e = hipMemcpyAsync(&host, ptr, sizeof(host), hipMemcpyDeviceToHost, st);
-  if (e == hipSuccess) e = hipStreamSynchronize(st);
+void release_error_word(int32_t slot) {
+  if (slot <= 0 || slot >= kErrorWords) return;
+  std::lock_guard<std::mutex> lock(g_err_mutex);
+  g_free_words.push_back(slot);
+}
+
+int32_t* shared_error_word() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+  std::lock_guard<std::mutex> lock(g_err_mutex);
+  DeviceWords w;
+  if (words_of(dev, &w) != hipSuccess) return nullptr;
+  return w.words;
+}
+
+int read_and_clear_error_word(int32_t slot, void* stream, int32_t* value) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return int(e);
-  const int32_t zero = 0;
-  e = hipMemcpyAsync(ptr, &zero, sizeof(zero), hipMemcpyHostToDevice, st);
+  std::lock_guard<std::mutex> lock(g_err_mutex);
+  DeviceWords w;
+  e = words_of(dev, &w);
+  if (e != hipSuccess) return int(e);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(read_clear_kernel, dim3(1), dim3(1), 0, st, w.words + slot, w.readout + slot);
+  e = hipGetLastError();
+  int32_t host = 0;
+  if (e == hipSuccess) e = hipMemcpyAsync(&host, w.readout + slot, sizeof(host), hipMemcpyDeviceToHost, st);
   if (e == hipSuccess) e = hipStreamSynchronize(st);
   if (e != hipSuccess) return int(e);
   if (value) *value = host;
@@ -98,10 +154,6 @@ pa_status hip_status(const char* fn, int e) {
 
 extern "C" {
 
-const char* pa_last_error(void) { return pa::g_last_error.c_str(); }
-
-int32_t pa_version(void) { return 100; }
-
 pa_status pa_pool_bytes(int32_t num_blocks, int32_t block_size, int32_t num_heads, int32_t head_dim,
                         pa_dtype kv_dtype, int64_t* kv_bytes, int64_t* scale_bytes) {
   if (!kv_bytes || !scale_bytes) return fail(PA_ERR_INVALID_ARG, "pa_pool_bytes: NULL output");
@@ -129,12 +181,27 @@ pa_status pa_alloc_pool(int32_t num_blocks, int32_t block_size, int32_t num_head
   }
   pa_pool* p = new (std::nothrow) pa_pool();
   if (!p) return fail(PA_ERR_INVALID_ARG, "pa_alloc_pool: out of host memory");
-  *p = pa_pool{num_blocks, block_size, num_heads, head_dim, kv_dtype, k_cache, v_cache, k_scale, v_scale};
+  *p = pa_pool{num_blocks, block_size, num_heads, head_dim, kv_dtype, k_cache, v_cache, k_scale, v_scale,
+               0, nullptr, 0};
+  const hipError_t e = hipError_t(pa::acquire_error_word(&p->err_slot, &p->err, &p->device));
+  if (e == hipErrorNoDevice) {
+    // No GPU in this process: the descriptor still serves host-side
+    // validation; any call that reaches a launch fails with PA_ERR_HIP.
+    p->err_slot = 0;
+    p->err = nullptr;
+    p->device = -1;
+  } else if (e != hipSuccess) {
+    delete p;
+    if (e == hipErrorOutOfMemory)
+      return fail(PA_ERR_OUT_OF_RANGE, "pa_alloc_pool: more than %d pools alive", pa::kErrorWords - 1);
+    return fail(PA_ERR_HIP, "pa_alloc_pool: error word: HIP error %d (%s)", int(e), hipGetErrorString(e));
+  }
   *out = p;
   return PA_OK;
 }
 
 pa_status pa_free_pool(pa_pool* pool) {
+  if (pool) pa::release_error_word(pool->err_slot);
   delete pool;
   return PA_OK;
 }
@@ -301,6 +368,7 @@ pa_status pa_decode_ordered(pa_pool* pool, const void* q, pa_dtype q_dtype, void
   a.max_blocks = max_blocks;
   a.block_size = pool->block_size;
   a.max_tokens = 0;
+  a.err = pool->err;
   a.ctx = context_lens;
   a.order = seq_order;
   a.schedule = schedule;
@@ -404,6 +472,7 @@ pa_status pa_write_decode(pa_pool* pool, const void* k_new, const void* v_new, p
   a.v_new = v_new;
   a.new_dtype = src_dtype;
   a.slots = slot_mapping;
+  a.err = pool->err;
   return decode_common("pa_write_decode", a, workspace, workspace_bytes, stream);
 }
 
@@ -467,6 +536,7 @@ pa_status pa_decode_mixed(pa_pool* cold_pool, pa_pool* hot_pool, const void* q, 
   a.hot_v = hot_pool->v_cache;
   a.hot_blocks = hot_blocks;
   a.num_hot = hot_pool->num_blocks;
+  a.err = cold_pool->err;
   return decode_common("pa_decode_mixed", a, workspace, workspace_bytes, stream);
 }
 
@@ -501,13 +571,21 @@ pa_status pa_decode_contiguous(const void* k, const void* v, pa_dtype kv_dtype, 
   a.head_dim = head_dim;
   a.num_blocks = 0;
   a.max_ctx = max_tokens;
+  a.err = pa::shared_error_word();
   a.sm_scale = sm_scale;
   a.partition_tokens = partition_tokens;
   return decode_common("pa_decode_contiguous", a, workspace, workspace_bytes, stream);
 }
 
-pa_status pa_check_errors(pa_stream stream, int32_t* device_error) {
-  return hip_status("pa_check_errors", pa::read_and_clear_device_error(stream, device_error));
+pa_status pa_check_errors(const pa_pool* pool, pa_stream stream, int32_t* device_error) {
+  if (pool) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev != pool->device)
+      return fail(PA_ERR_INVALID_ARG, "pa_check_errors: the pool lives on device %d, device %d is current",
+                  pool->device, dev);
+  }
+  return hip_status("pa_check_errors", pa::read_and_clear_error_word(pool ? pool->err_slot : 0, stream,
+                                                                      device_error));
 }
 
 pa_status pa_stream_copy(void* dst, const void* src, int64_t bytes, pa_stream stream) {

@@ -74,6 +74,32 @@ __global__ __launch_bounds__(kThreads) void write_kv_kernel(const SRC* __restric
 }
 
 // ---------------------------------------------------------------------------
+// Quantised pools write a block's rows of one call as one group, by one wave
+// per run of adjacent rows hitting that block. A second, non-adjacent run into
+// the same block would be written by another wave at the same time, so it is
+// flagged (PA_DEV_BAD_RUN) instead: the wave of the later run leader i (head
+// 0, K tensor only) looks for the block among the rows before i. Reads are 8
+// wave-wide loads of 512 bytes in flight per step.
+__device__ bool earlier_run_hits(const int64_t* __restrict__ slots, int64_t i, int64_t blk, int bshift) {
+  constexpr int kUnroll = 8;
+  const int lane = threadIdx.x & (kWave - 1);
+  bool hit = false;
+  int64_t j = lane;
+  for (; j + (kUnroll - 1) * kWave < i; j += kUnroll * kWave) {
+    int64_t v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) v[u] = slots[j + u * kWave];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) hit |= v[u] >= 0 && (v[u] >> bshift) == blk;
+  }
+  for (; j < i; j += kWave) {
+    const int64_t v = slots[j];
+    hit |= v >= 0 && (v >> bshift) == blk;
+  }
+  return __ballot(hit) != 0;
+}
+
+// ---------------------------------------------------------------------------
 // int8 pools: one wave per (run leader i, head h, tensor).
 template <typename SRC, int D>
 __global__ __launch_bounds__(kThreads) void write_kv_i8_kernel(
@@ -119,6 +145,7 @@ __global__ __launch_bounds__(kThreads) void write_kv_i8_kernel(
     const int64_t sl = slots[i + R];
     dup |= sl >= 0 && (sl >> bshift) == blk;
   }
+  if (h == 0 && !is_v && i > 1) dup |= earlier_run_hits(slots, i - 1, blk, bshift);
   if (dup && lane == 0) flag_error(err, PA_DEV_BAD_RUN);
 
   float a = 0.f;
@@ -209,6 +236,7 @@ __global__ __launch_bounds__(kThreads) void write_kv_i4_kernel(
     const int64_t sl = slots[i + R];
     dup |= sl >= 0 && (sl >> bshift) == blk;
   }
+  if (h == 0 && !is_v && i > 1) dup |= earlier_run_hits(slots, i - 1, blk, bshift);
   if (dup && lane == 0) flag_error(err, PA_DEV_BAD_RUN);
 
   const bool mine = lane < kRowBytes;   // this lane owns a byte of each row
@@ -504,12 +532,12 @@ int launch_write_float(const pa_pool* p, const void* k_new, const void* v_new, c
     hipLaunchKernelGGL((write_kv_kernel<DST, SRC, 64>), grid, dim3(kThreads), 0, st,
                        static_cast<const SRC*>(k_new), static_cast<const SRC*>(v_new),
                        static_cast<DST*>(p->k_cache), static_cast<DST*>(p->v_cache), slots, n,
-                       p->num_heads, p->num_blocks, block_shift(p->block_size), device_error_ptr());
+                       p->num_heads, p->num_blocks, block_shift(p->block_size), p->err);
   else
     hipLaunchKernelGGL((write_kv_kernel<DST, SRC, 128>), grid, dim3(kThreads), 0, st,
                        static_cast<const SRC*>(k_new), static_cast<const SRC*>(v_new),
                        static_cast<DST*>(p->k_cache), static_cast<DST*>(p->v_cache), slots, n,
-                       p->num_heads, p->num_blocks, block_shift(p->block_size), device_error_ptr());
+                       p->num_heads, p->num_blocks, block_shift(p->block_size), p->err);
   return int(hipGetLastError());
 }
 
@@ -523,7 +551,7 @@ int launch_write_i8(const pa_pool* p, const void* k_new, const void* v_new, cons
                        static_cast<const SRC*>(v_new), static_cast<int8_t*>(p->k_cache),
                        static_cast<int8_t*>(p->v_cache), static_cast<_Float16*>(p->k_scale),
                        static_cast<_Float16*>(p->v_scale), slots, n, p->num_heads, p->num_blocks,
-                       block_shift(p->block_size), device_error_ptr());
+                       block_shift(p->block_size), p->err);
   };
   if (p->head_dim == 64)
     args(write_kv_i8_kernel<SRC, 64>);
@@ -542,7 +570,7 @@ int launch_write_i4(const pa_pool* p, const void* k_new, const void* v_new, cons
                        static_cast<const SRC*>(v_new), static_cast<uint8_t*>(p->k_cache),
                        static_cast<uint8_t*>(p->v_cache), static_cast<_Float16*>(p->k_scale),
                        static_cast<_Float16*>(p->v_scale), slots, n, p->num_heads, p->num_blocks,
-                       block_shift(p->block_size), device_error_ptr());
+                       block_shift(p->block_size), p->err);
   };
   if (p->head_dim == 64)
     args(write_kv_i4_kernel<SRC, 64>);
@@ -584,7 +612,7 @@ int launch_demote_blocks(const pa_pool* hot, const pa_pool* cold, const int32_t*
                          static_cast<const _Float16*>(hot->k_cache), static_cast<const _Float16*>(hot->v_cache),
                          static_cast<uint8_t*>(cold->k_cache), static_cast<uint8_t*>(cold->v_cache),
                          static_cast<_Float16*>(cold->k_scale), static_cast<_Float16*>(cold->v_scale),
-                         hot->num_heads, hot->num_blocks, cold->num_blocks, device_error_ptr());
+                         hot->num_heads, hot->num_blocks, cold->num_blocks, cold->err);
     };
     if (hot->head_dim == 64)
       go4(demote_i4_kernel<64>);
@@ -597,7 +625,7 @@ int launch_demote_blocks(const pa_pool* hot, const pa_pool* cold, const int32_t*
                        static_cast<const _Float16*>(hot->k_cache), static_cast<const _Float16*>(hot->v_cache),
                        static_cast<int8_t*>(cold->k_cache), static_cast<int8_t*>(cold->v_cache),
                        static_cast<_Float16*>(cold->k_scale), static_cast<_Float16*>(cold->v_scale),
-                       hot->num_heads, hot->num_blocks, cold->num_blocks, device_error_ptr());
+                       hot->num_heads, hot->num_blocks, cold->num_blocks, cold->err);
   };
   if (hot->head_dim == 64)
     go(demote_kernel<64>);
@@ -613,7 +641,7 @@ int launch_copy_blocks(const pa_pool* p, const int32_t* pairs, int32_t n, void* 
   hipLaunchKernelGGL(copy_blocks_kernel, grid, dim3(kThreads), 0, static_cast<hipStream_t>(stream), pairs,
                      n, static_cast<char*>(p->k_cache), static_cast<char*>(p->v_cache), block_bytes,
                      static_cast<_Float16*>(p->k_scale), static_cast<_Float16*>(p->v_scale),
-                     p->num_heads, p->num_blocks, device_error_ptr());
+                     p->num_heads, p->num_blocks, p->err);
   return int(hipGetLastError());
 }
 
@@ -628,7 +656,7 @@ int launch_swap_blocks(const pa_pool* p, const SwapHost& h, const int32_t* pairs
                      static_cast<uint64_t*>(h.k), static_cast<uint64_t*>(h.v), words,
                      static_cast<uint16_t*>(p->k_scale), static_cast<uint16_t*>(p->v_scale),
                      static_cast<uint16_t*>(h.k_scale), static_cast<uint16_t*>(h.v_scale), p->num_heads,
-                     p->num_blocks, h.num_blocks, out_dir ? 1 : 0, device_error_ptr());
+                     p->num_blocks, h.num_blocks, out_dir ? 1 : 0, p->err);
   return int(hipGetLastError());
 }
 

@@ -1043,7 +1043,9 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(Params p) {
       const float4 v = s_o[j][d / 4];
       Ot += (d % 4 == 0) ? v.x : (d % 4 == 1) ? v.y : (d % 4 == 2) ? v.z : v.w;
     }
-    reinterpret_cast<QT*>(p.out)[int64_t(sh) * D + d] = to_out<QT>(Ot / Lt);
+    // Every partition masked (flagged bad table entries): zeros, as the
+    // single pass writes.
+    reinterpret_cast<QT*>(p.out)[int64_t(sh) * D + d] = to_out<QT>(Lt > 0.f ? Ot / Lt : 0.f);
   }
 }
 
@@ -1156,7 +1158,7 @@ int launch_decode(const DecodeArgs& a, void* stream) {
   p.ws_m = a.ws_m;
   p.ws_l = a.ws_l;
   p.ws_o = a.ws_o;
-  p.err = device_error_ptr();
+  p.err = a.err;
   p.k_new = a.k_new;
   p.v_new = a.v_new;
   p.slots = a.slots;

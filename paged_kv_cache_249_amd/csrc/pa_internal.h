@@ -15,8 +15,11 @@ struct pa_pool {
   pa_dtype kv_dtype;
   void* k_cache;
   void* v_cache;
-  void* k_scale;   // fp16 [num_blocks][num_heads], int8 pools only
+  void* k_scale;   // fp16 [num_blocks][num_heads], int8 and int4 pools only
   void* v_scale;
+  int32_t err_slot;  // index of the pool's device error word
+  int32_t* err;      // device address of that word (on `device`)
+  int32_t device;    // device current at pa_alloc_pool
 };
 
 namespace pa {
@@ -92,6 +95,7 @@ struct DecodeArgs {
   const void* hot_v;
   const int32_t* hot_blocks;
   int32_t num_hot;
+  int32_t* err;           // device error word the kernels flag
 };
 
 int launch_decode(const DecodeArgs& a, void* stream);
@@ -131,10 +135,18 @@ int launch_swap_blocks(const pa_pool* p, const SwapHost& h, const int32_t* pairs
 int launch_stream_copy(void* dst, const void* src, int64_t bytes, void* stream);
 int launch_stream_read(const void* src, int64_t bytes, void* sink, void* stream);
 int launch_stage_copy(void* dst, const void* src_device_view, int64_t bytes, void* stream);
-int read_and_clear_device_error(void* stream, int32_t* value);
-
-// Device address of the sticky error word on the current device (nullptr if
-// the lookup fails; kernels then skip flagging).
-int32_t* device_error_ptr();
+// Device error words (api.hip): one per live pool plus word 0 for calls tied
+// to no pool. kErrorWords bounds the pools alive at once.
+constexpr int kErrorWords = 4096;
+// Takes a free word on the current device and clears it. Returns a hipError_t
+// as int: hipErrorOutOfMemory if every word is taken.
+int acquire_error_word(int32_t* slot, int32_t** word, int32_t* device);
+void release_error_word(int32_t slot);
+// Device address of word 0 on the current device (nullptr if the lookup
+// fails; kernels then skip flagging).
+int32_t* shared_error_word();
+// Atomically reads and clears word `slot` on the current device (after the
+// stream's earlier work), returning a hipError_t as int.
+int read_and_clear_error_word(int32_t slot, void* stream, int32_t* value);
 
 }  // namespace pa

@@ -586,7 +586,7 @@ int launch_prefill(const PrefillArgs& a, void* stream) {
   p.max_query = a.max_query_len;
   p.row_tiles = int32_t((int64_t(a.max_query_len) + kPfWgRows - 1) / kPfWgRows);
   p.scale_log2 = a.sm_scale * kLog2e;
-  p.err = device_error_ptr();
+  p.err = a.pool->err;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   if (a.pool->head_dim == 64) return launch_prefill_kv<64>(p, a.pool->kv_dtype, a.pool->block_size, groups, st);
   return launch_prefill_kv<128>(p, a.pool->kv_dtype, a.pool->block_size, groups, st);

@@ -118,6 +118,46 @@ class _Staging:
         st["event"] = done
 
 
+def prefill_appends(bm, seqs, counts, cap: int):
+    """The block-manager side of a chunked-prefill step, all or nothing.
+
+    ``counts[i]`` tokens are appended to sequence ``seqs[i]`` (distinct ids,
+    sequence order), registering unknown sequences. Returns the chunk's slots
+    (int64, in row order) and copy-on-write pairs (int32 [k][2]). Before any
+    state changes, every sequence's new context must fit ``cap`` table
+    entries (else ``PA_ERR_OUT_OF_RANGE``) and none may be swapped out (else
+    ``PA_ERR_STATE``). New sequences are registered empty and then appended
+    token by token in the same undo-logged batch as the others, which places
+    their blocks as registering them with their tokens would; if the batch
+    fails (``PA_ERR_OUT_OF_BLOCKS``) it is undone, the new sequences are
+    removed again, and the manager is exactly as before the call.
+    """
+    seqs = np.asarray(seqs, dtype=np.int64).reshape(-1)
+    counts = np.asarray(counts, dtype=np.int64).reshape(-1)
+    bs = bm.block_size
+    new = []
+    for s, c in zip(seqs.tolist(), counts.tolist()):
+        if bm.has_seq(s):
+            if bm.is_swapped(s):
+                raise N.PagedKVError(N.PA_ERR_STATE, f"sequence {s} is swapped out")
+            ctx = bm.table(s)[1] + c
+        else:
+            new.append(s)
+            ctx = c
+        if -(-ctx // bs) > cap:
+            raise N.PagedKVError(N.PA_ERR_OUT_OF_RANGE,
+                                 f"sequence {s}: {ctx} tokens need more than {cap} table entries")
+    for s in new:
+        bm.add_seq(s, 0)
+    try:
+        slots, pairs = bm.append_batch(np.repeat(seqs, counts))
+    except N.PagedKVError:
+        for s in new:
+            bm.free_seq(s)
+        raise
+    return slots.copy(), pairs.copy()
+
+
 class _Workspace:
     """Split-K workspace on the device, grown geometrically."""
 
@@ -210,10 +250,17 @@ class PagedDecodeEngine:
         slots, and the chunk's rows attend causally over their sequences'
         tables at once (``pa_prefill``), results in ``out``. fp16, int8 or
         int4 pools (a quantised pool codes each chunk's rows per (block, head)
-        as it writes them), fp16 queries. Arguments are checked before any
-        state changes; if the pool runs out of blocks part-way, the sequences
-        before the failing one keep the tokens already appended (each append
-        is atomic in the block manager) and nothing is launched."""
+        as it writes them), fp16 queries.
+
+        The chunk is all or nothing: arguments and every sequence's table
+        capacity are checked before any state changes, and the tokens go
+        through one undo-logged batch append (new sequences are registered
+        empty first and appended like the others, which places their blocks
+        exactly as registering them with their tokens would). If the pool runs
+        out of blocks, the appends are undone, the sequences registered by
+        this call are removed, and the block manager is left exactly as it
+        was (tables, contexts, reference counts and free list); nothing is
+        launched."""
         seqs = np.asarray(seqs, dtype=np.int64).reshape(-1)
         counts = np.asarray(counts, dtype=np.int64).reshape(-1)
         if seqs.size != counts.size or (counts < 0).any():
@@ -227,27 +274,15 @@ class PagedDecodeEngine:
         R = int(counts.sum())
         if tuple(k_rows.shape[:1]) != (R,) or q_rows.shape != k_rows.shape or v_rows.shape != k_rows.shape:
             raise N.PagedKVError(N.PA_ERR_INVALID_ARG, "row counts do not match the chunk sizes")
-        for s in seqs.tolist():
-            if self.bm.has_seq(s) and self.bm.is_swapped(s):
-                raise N.PagedKVError(N.PA_ERR_STATE, f"sequence {s} is swapped out")
-        slots, pairs = [], []
-        for s, c in zip(seqs.tolist(), counts.tolist()):
-            if not self.bm.has_seq(s):
-                slots.append(self.bm.add_seq(s, c))
-                continue
-            for _ in range(c):
-                slot, src, dst = self.bm.append(s)
-                slots.append(np.array([slot], dtype=np.int64))
-                if src >= 0:
-                    pairs.append((src, dst))
+        slots, pairs = prefill_appends(self.bm, seqs, counts, self.cap)
         tables, ctx = self.bm.export(seqs, self.cap)
         qs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
         cur = torch.cuda.current_stream(self.device) if stream is None else stream
         with torch.cuda.stream(cur):
-            if pairs:
-                N.pa_copy_blocks(self.pool, torch.tensor(pairs, dtype=torch.int32, device=self.device), stream=cur)
+            if pairs.shape[0]:
+                N.pa_copy_blocks(self.pool, torch.from_numpy(pairs).to(self.device), stream=cur)
             if R:
-                sl = torch.from_numpy(np.concatenate(slots)).to(self.device, non_blocking=False)
+                sl = torch.from_numpy(slots.copy()).to(self.device, non_blocking=False)
                 N.pa_write_kv(self.pool, k_rows, v_rows, sl, stream=cur)
                 # Heaviest sequences first (pairs attended: n (2 ctx - n + 1) / 2),
                 # so a long one does not stretch the launch's tail.
@@ -257,7 +292,7 @@ class PagedDecodeEngine:
                              torch.from_numpy(tables).to(self.device), torch.from_numpy(ctx).to(self.device),
                              int(counts.max()), int(ctx.max()), stream=cur, seq_order=order)
         self.last_ctx = ctx.copy()
-        self.last_pairs = len(pairs)
+        self.last_pairs = int(pairs.shape[0])
 
     def add_sequence_prefix(self, seq: int, tokens, k_rows, v_rows):
         """Register ``seq`` from its token ids, sharing cached full blocks

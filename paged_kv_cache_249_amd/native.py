@@ -73,7 +73,7 @@ _SIGS = {
                          _i32, _vp, _i64, _vp], _i32),
     "pa_prefill": ([_vp, _vp, _i32, _vp, _vp, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _f32, _vp], _i32),
     "pa_prefill_ordered": ([_vp, _vp, _i32, _vp, _vp, _i32, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _f32, _vp], _i32),
-    "pa_check_errors": ([_vp, _pi32], _i32),
+    "pa_check_errors": ([_vp, _vp, _pi32], _i32),
     "pa_decode_contiguous": ([_vp, _vp, _i32, _i32, _i32, _i32, _vp, _i32, _vp, _vp, _vp, _i32, _f32, _i32,
                               _vp, _i64, _vp], _i32),
     "pa_stream_copy": ([_vp, _vp, _i64, _vp], _i32),
@@ -457,10 +457,14 @@ def contiguous_workspace_bytes(num_seqs: int, num_heads: int, head_dim: int, max
     return 0 if P <= 1 else (2 * (-(-n // 4) * 4) + n * head_dim) * 4
 
 
-def pa_check_errors(stream=None) -> int:
-    """Synchronise and return (then clear) the sticky device error bits."""
+def pa_check_errors(pool=None, stream=None) -> int:
+    """Return (and clear, atomically) the device error bits of ``pool`` (a
+    :class:`Pool`, or None for calls tied to no pool) after the stream's work."""
+    if pool is not None and not isinstance(pool, Pool):
+        raise PagedKVError(PA_ERR_INVALID_ARG, "pa_check_errors takes a Pool or None")
     v = C.c_int32()
-    _check(lib.pa_check_errors(_stream(stream), C.byref(v)), "pa_check_errors")
+    _check(lib.pa_check_errors(pool.handle if pool is not None else None, _stream(stream), C.byref(v)),
+           "pa_check_errors")
     return v.value
 
 

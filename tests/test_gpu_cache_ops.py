@@ -70,7 +70,7 @@ def test_write_kv_float_bit_exact(pool_code, src_dtype, D, bs):
     OC.write_kv(hk, hv, k_new.numpy(), v_new.numpy(), slots, block_size=bs)
     assert np.array_equal(_bytes(pool.k_cache), hk.view(np.uint8).reshape(-1))
     assert np.array_equal(_bytes(pool.v_cache), hv.view(np.uint8).reshape(-1))
-    assert pk.pa_check_errors() == 0
+    assert pk.pa_check_errors(pool) == 0
 
 
 def _int8_case(pk, D, src_dtype, seed, bs=16):
@@ -114,7 +114,7 @@ def test_write_kv_int8_bit_exact(D, src_dtype, bs):
     assert np.array_equal(pool.v_scale.cpu().numpy().view(np.uint16), hvs.view(np.uint16))
     assert np.array_equal(pool.k_cache.cpu().numpy(), hk)
     assert np.array_equal(pool.v_cache.cpu().numpy(), hv)
-    assert pk.pa_check_errors() == 0
+    assert pk.pa_check_errors(pool) == 0
 
 
 @pytest.mark.parametrize("src_dtype,bs,D", [(torch.float32, 16, 128), (torch.float16, 16, 128),
@@ -157,7 +157,7 @@ def test_write_kv_int4_bit_exact(src_dtype, bs, D):
     written = np.unique(np.concatenate(calls))
     blk, off = written // bs, written % bs
     assert np.abs(OC.unpack_int4(pool.k_cache.cpu().numpy())[blk, :, off]).max() <= 7
-    assert pk.pa_check_errors() == 0
+    assert pk.pa_check_errors(pool) == 0
 
 
 @pytest.mark.parametrize("code,D,bs", [("f16", 128, 16), ("i8", 128, 16), ("f32", 64, 16), ("f16", 128, 64),
@@ -177,4 +177,4 @@ def test_copy_blocks_bit_exact(code, D, bs):
     got = [pool.k_cache, pool.v_cache] + ([pool.k_scale, pool.v_scale] if pk.is_quantised(c) else [])
     for g, h in zip(got, host):
         assert np.array_equal(_bytes(g), h.view(np.uint8).reshape(-1))
-    assert pk.pa_check_errors() == 0
+    assert pk.pa_check_errors(pool) == 0

@@ -86,7 +86,7 @@ class Batch:
         pk.pa_decode(self.pool, self.qd, out, self.tabd if tables is None else tables, self.ctxd, maxc,
                      partition_tokens=ptok, workspace=ws)
         torch.cuda.synchronize()
-        assert pk.pa_check_errors() == 0
+        assert pk.pa_check_errors(self.pool) == 0
         return out.cpu().numpy(), ws
 
     def oracle(self):
@@ -268,7 +268,7 @@ def test_int4_decode_matches_the_oracle(bs, qd, D):
         pk.pa_decode(pool, qd_t, out, torch.from_numpy(tab).to(DEV), ctxd, maxc, partition_tokens=ptok,
                      workspace=ws)
         torch.cuda.synchronize()
-        assert pk.pa_check_errors() == 0
+        assert pk.pa_check_errors(pool) == 0
         got = out.cpu().numpy()
         atol, rtol = (F16_ATOL, F16_RTOL) if qd == "f16" else (1e-4, 1e-4)
         assert_close(got, ref, atol, rtol, f"int4 bs={bs} q={qd} D={D} ptok={ptok}")
@@ -340,7 +340,7 @@ def test_many_partitions_per_sequence(kv, D, ptok):
     pk.pa_decode(pool, qd, out, torch.from_numpy(tab).to(DEV), torch.tensor(ctx, dtype=torch.int32, device=DEV),
                  maxc, partition_tokens=ptok, workspace=ws)
     torch.cuda.synchronize()
-    assert pk.pa_check_errors() == 0
+    assert pk.pa_check_errors(pool) == 0
     assert_close(out.cpu().numpy(), ref, F16_ATOL, F16_RTOL, f"{kv} ptok={ptok}")
     P = -(-maxc // ptok)
     flat = ws.cpu().numpy()
@@ -416,7 +416,7 @@ def test_contiguous_twin_many_partitions(D):
         ws = torch.full((nb // 4,), float("nan"), dtype=torch.float32, device=DEV)
         pk.pa_decode_contiguous(kd, vd, qd, out, ctxd, partition_tokens=ptok, workspace=ws)
         torch.cuda.synchronize()
-        assert pk.pa_check_errors() == 0
+        assert pk.pa_check_errors(None) == 0
         assert_close(out.cpu().numpy(), ref, F16_ATOL, F16_RTOL, f"contiguous D={D} ptok={ptok}")
 
 
@@ -439,7 +439,7 @@ def test_schedule_does_not_change_results():
                 pk.pa_decode(b.pool, b.qd, out, b.tabd, b.ctxd, maxc, partition_tokens=ptok, workspace=ws,
                              seq_order=torch.from_numpy(order.astype(np.int32)).to(DEV), schedule=sched)
                 torch.cuda.synchronize()
-                assert pk.pa_check_errors() == 0
+                assert pk.pa_check_errors(b.pool) == 0
                 assert np.array_equal(out.cpu().numpy().view(np.uint16), base.view(np.uint16))
     with pytest.raises(pk.PagedKVError) as e:
         pk.pa_decode(b.pool, b.qd, out, b.tabd, b.ctxd, maxc, seq_order=b.ctxd, schedule=7)
@@ -457,21 +457,37 @@ def test_out_of_range_indices_are_flagged_not_followed():
     tab[0, 1] = b.NB + 5
     out = torch.empty_like(b.qd)
     pk.pa_decode(b.pool, b.qd, out, torch.from_numpy(tab).to(DEV), b.ctxd, 40)
-    assert pk.pa_check_errors() & pk.PA_DEV_BAD_TABLE_ENTRY
+    assert pk.pa_check_errors(b.pool) & pk.PA_DEV_BAD_TABLE_ENTRY
     assert not np.isnan(out.cpu().numpy()).any()
     pk.pa_decode(b.pool, b.qd, out, b.tabd, torch.tensor([40, 20], dtype=torch.int32, device=DEV), 32)
-    assert pk.pa_check_errors() & pk.PA_DEV_BAD_CONTEXT
+    assert pk.pa_check_errors(b.pool) & pk.PA_DEV_BAD_CONTEXT
     pk.pa_decode(b.pool, b.qd, out, b.tabd, b.ctxd, 40,
                  seq_order=torch.tensor([0, 7], dtype=torch.int32, device=DEV))
-    assert pk.pa_check_errors() & pk.PA_DEV_BAD_CONTEXT
+    assert pk.pa_check_errors(b.pool) & pk.PA_DEV_BAD_CONTEXT
     rows = torch.zeros((1, 2, 64), dtype=torch.float16, device=DEV)
     before = b.kd.clone()
     pk.pa_write_kv(b.pool, rows, rows, torch.tensor([b.NB * 16 + 3], dtype=torch.int64, device=DEV))
-    assert pk.pa_check_errors() & pk.PA_DEV_BAD_SLOT
+    assert pk.pa_check_errors(b.pool) & pk.PA_DEV_BAD_SLOT
     pk.pa_copy_blocks(b.pool, torch.tensor([[0, b.NB]], dtype=torch.int32, device=DEV))
-    assert pk.pa_check_errors() & pk.PA_DEV_BAD_PAIR
+    assert pk.pa_check_errors(b.pool) & pk.PA_DEV_BAD_PAIR
     assert torch.equal(before, b.kd)
-    assert pk.pa_check_errors() == 0
+    assert pk.pa_check_errors(b.pool) == 0
+    # Every table entry of sequence 0 bad: each of its split-K partitions is
+    # masked, and the reduce writes zeros, as the single pass does.
+    tab = b.tab.copy()
+    tab[0, :3] = b.NB + 1
+    tabd = torch.from_numpy(tab).to(DEV)
+    for ptok in (0, 16):
+        ws = None
+        if ptok:
+            nb = pk.pa_decode_workspace_bytes(b.pool, 2, 40, ptok)
+            ws = torch.full((nb // 4,), float("nan"), dtype=torch.float32, device=DEV)
+        out = torch.full_like(b.qd, float("nan"))
+        pk.pa_decode(b.pool, b.qd, out, tabd, b.ctxd, 40, partition_tokens=ptok, workspace=ws)
+        assert pk.pa_check_errors(b.pool) & pk.PA_DEV_BAD_TABLE_ENTRY
+        got = out.cpu().numpy()
+        assert not np.isnan(got).any() and not got[0].any(), f"ptok={ptok}"
+        assert_close(got[1], b.oracle()[1], F16_ATOL, F16_RTOL, f"good sequence, ptok={ptok}")
 
 
 @pytest.mark.parametrize("kv,src,D,ptok", [("f16", torch.float16, 128, 0), ("f16", torch.float32, 128, 64),
@@ -503,7 +519,7 @@ def test_fused_write_decode_matches_write_then_decode(kv, src, D, ptok):
     pk.pa_write_decode(b.pool, k_new, v_new, slots_d, b.qd, out_b, b.tabd, b.ctxd, maxc, partition_tokens=ptok,
                        workspace=ws, seq_order=order)
     torch.cuda.synchronize()
-    assert pk.pa_check_errors() == 0
+    assert pk.pa_check_errors(a.pool) == 0 and pk.pa_check_errors(b.pool) == 0
     assert torch.equal(a.kd.view(torch.uint8), b.kd.view(torch.uint8))
     assert torch.equal(a.vd.view(torch.uint8), b.vd.view(torch.uint8))
     assert torch.equal(out_a.view(torch.int16), out_b.view(torch.int16))
@@ -524,7 +540,7 @@ def test_fused_write_rejects_a_slot_that_is_not_the_newest_token():
     out = torch.empty_like(b.qd)
     pk.pa_write_decode(b.pool, rows, rows, slots, b.qd, out, b.tabd, b.ctxd, 40)
     torch.cuda.synchronize()
-    assert pk.pa_check_errors() & pk.PA_DEV_BAD_SLOT
+    assert pk.pa_check_errors(b.pool) & pk.PA_DEV_BAD_SLOT
     assert torch.equal(before_k, b.kd)                       # nothing written
     assert_close(out.cpu().numpy(), b.oracle(), F16_ATOL, F16_RTOL, "decode unaffected")
     c = Batch([5], 2, 64, "f16", "f16", seed=68)
@@ -608,7 +624,7 @@ def test_block_size_fused_write_decode(bs, kv, src, ptok):
     pk.pa_write_decode(b.pool, k_new, v_new, slots_d, b.qd, out_b, b.tabd, b.ctxd, maxc, partition_tokens=ptok,
                        workspace=ws)
     torch.cuda.synchronize()
-    assert pk.pa_check_errors() == 0
+    assert pk.pa_check_errors(a.pool) == 0 and pk.pa_check_errors(b.pool) == 0
     assert torch.equal(a.kd.view(torch.uint8), b.kd.view(torch.uint8))
     assert torch.equal(a.vd.view(torch.uint8), b.vd.view(torch.uint8))
     assert torch.equal(out_a.view(torch.int16), out_b.view(torch.int16))

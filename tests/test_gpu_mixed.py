@@ -49,7 +49,7 @@ def test_demote_is_bit_exact(D):
     print(f"demote D={D} pairs={pairs.tolist()}", flush=True)
     pk.pa_demote_blocks(hot, cold, torch.from_numpy(pairs).to(DEV))
     torch.cuda.synchronize()
-    assert pk.pa_check_errors() == 0
+    assert pk.pa_check_errors(cold) == 0
     OM.demote(hk, hv, ck, cks, cv, cvs, pairs)
     assert np.array_equal(cold.k_cache.cpu().numpy(), ck) and np.array_equal(cold.v_cache.cpu().numpy(), cv)
     assert np.array_equal(cold.k_scale.cpu().numpy().view(np.uint16), cks.view(np.uint16))
@@ -57,7 +57,7 @@ def test_demote_is_bit_exact(D):
     bad = torch.tensor([[NH, 0], [0, NC]], dtype=torch.int32, device=DEV)
     before = cold.k_cache.clone()
     pk.pa_demote_blocks(hot, cold, bad)
-    assert pk.pa_check_errors() & pk.PA_DEV_BAD_PAIR
+    assert pk.pa_check_errors(cold) & pk.PA_DEV_BAD_PAIR
     assert torch.equal(before, cold.k_cache)
 
 
@@ -88,7 +88,7 @@ def test_demote_int4_is_bit_exact(D):
     print(f"demote int4 pairs={pairs.tolist()}", flush=True)
     pk.pa_demote_blocks(hot, cold, torch.from_numpy(pairs).to(DEV))
     torch.cuda.synchronize()
-    assert pk.pa_check_errors() == 0
+    assert pk.pa_check_errors(cold) == 0
     OM.demote(hk, hv, ck, cks, cv, cvs, pairs, qmax=7)
     assert np.array_equal(OC.unpack_int4(cold.k_cache.cpu().numpy()), ck)
     assert np.array_equal(OC.unpack_int4(cold.v_cache.cpu().numpy()), cv)
@@ -153,7 +153,7 @@ class MixedBatch:
         pk.pa_decode_mixed(self.cold, self.hotp, self.qd, out, self.tabd, self.hotd, self.ctxd, maxc,
                            partition_tokens=ptok, workspace=ws, seq_order=order)
         torch.cuda.synchronize()
-        assert pk.pa_check_errors() == 0
+        assert pk.pa_check_errors(self.cold) == 0
         return out.cpu().numpy()
 
     def oracle(self):
@@ -193,7 +193,7 @@ def test_decode_mixed_flags_a_bad_hot_block_and_rejects_bad_pools():
     bad = torch.tensor([b.NH + 3, b.hot[1]], dtype=torch.int32, device=DEV)
     out = torch.empty_like(b.qd)
     pk.pa_decode_mixed(b.cold, b.hotp, b.qd, out, b.tabd, bad, b.ctxd, 40)
-    assert pk.pa_check_errors() & pk.PA_DEV_BAD_TABLE_ENTRY
+    assert pk.pa_check_errors(b.cold) & pk.PA_DEV_BAD_TABLE_ENTRY
     assert not np.isnan(out.cpu().numpy()).any()
     with pytest.raises(pk.PagedKVError) as e:
         pk.pa_decode_mixed(b.hotp, b.cold, b.qd, out, b.tabd, b.hotd, b.ctxd, 40)
@@ -247,7 +247,7 @@ def test_engine_steps_match_the_oracle_bit_for_bit(ptok, cold):
         OC.write_kv(hk, hv, kn.cpu().numpy(), vn.cpu().numpy(), [r[0] for r in res])
         if t % 13 == 12 or t == steps - 1:
             torch.cuda.synchronize()
-            assert pk.pa_check_errors() == 0
+            assert pk.pa_check_errors(eng.cold) == 0
             tabs, hot, ctx = obm.export(list(seqs), 32)
             ref = OM.decode(q.cpu().numpy(), ck, cks, cv, cvs, hk, hv, tabs, hot, ctx)
             assert_close(out.cpu().numpy(), ref, F16_ATOL, F16_RTOL, f"step {t}")

@@ -111,7 +111,7 @@ def test_prefill_matches_the_oracle(D, bs):
     b = Chunks(CTX, NQ, H=3, D=D, bs=bs, seed=bs + D)
     print(f"prefill D={D} bs={bs}", flush=True)
     got = b.gpu()
-    assert pk.pa_check_errors() == 0
+    assert pk.pa_check_errors(b.pool) == 0
     assert_close(got, b.oracle(), f"D={D} bs={bs}")
 
 
@@ -162,7 +162,7 @@ def test_table_rows_longer_than_the_kernel_keeps_in_lds():
     for bs in (16, 64):
         b = Chunks([33000, 100], [70, 100], H=2, D=64, bs=bs, seed=23)
         got = b.gpu()
-        assert _pk().pa_check_errors() == 0
+        assert _pk().pa_check_errors(b.pool) == 0
         assert_close(got, b.oracle(), f"bs={bs}")
 
 
@@ -172,13 +172,13 @@ def test_bad_table_entry_is_flagged(ctx):
     # tokens, read from memory at 33000): the kernel flags it and reads an
     # in-bounds row instead; the other sequence is unaffected.
     pk = _pk()
-    assert pk.pa_check_errors() == 0
+    assert pk.pa_check_errors(None) == 0
     b = Chunks([ctx, 90], [40, 90], H=2, D=64, seed=29)
     tab = b.tabd.clone()
     tab[0, 3] = b.NB + 7
     b.tabd = tab
     got = b.gpu()
-    assert pk.pa_check_errors() & pk.PA_DEV_BAD_TABLE_ENTRY
+    assert pk.pa_check_errors(b.pool) & pk.PA_DEV_BAD_TABLE_ENTRY
     assert_close(got[40:], b.oracle()[40:], "good sequence beside a bad table row")
 
 
@@ -192,13 +192,13 @@ def test_dispatch_order_changes_nothing():
     rng = np.random.default_rng(61)
     for order in (sorted(range(S), key=lambda s: -work[s]), list(rng.permutation(S)), list(range(S))[::-1]):
         got = b.gpu(seq_order=order)
-        assert pk.pa_check_errors() == 0
+        assert pk.pa_check_errors(b.pool) == 0
         assert np.array_equal(got.view(np.uint16), ref.view(np.uint16)), order
     # An entry outside the batch is flagged and its work skipped; the rest is computed.
     bad = list(range(S))
     bad[2] = S + 3
     got = b.gpu(seq_order=bad)
-    assert pk.pa_check_errors() & pk.PA_DEV_BAD_CONTEXT
+    assert pk.pa_check_errors(b.pool) & pk.PA_DEV_BAD_CONTEXT
     r2 = slice(int(b.qs[2]), int(b.qs[3]))
     assert np.isnan(got[r2]).all()
     keep = np.ones(got.shape[0], bool)
@@ -208,12 +208,12 @@ def test_dispatch_order_changes_nothing():
 
 def test_bad_lengths_flag_and_leave_rows_unwritten():
     pk = _pk()
-    assert pk.pa_check_errors() == 0
+    assert pk.pa_check_errors(None) == 0
     b = Chunks([40, 30], [10, 5], H=2, D=64, seed=13)
     # Sequence 1 claims a context shorter than its chunk.
     b.ctxd = torch.tensor([40, 3], dtype=torch.int32, device=DEV)
     got = b.gpu(max_ctx=40)
-    assert pk.pa_check_errors() & pk.PA_DEV_BAD_CONTEXT
+    assert pk.pa_check_errors(b.pool) & pk.PA_DEV_BAD_CONTEXT
     assert np.isnan(got[10:]).all()
     assert_close(got[:10], b.oracle()[:10], "good sequence beside a bad one")
 
@@ -289,9 +289,9 @@ class QuantChunks:
             write(kc, ks, vc, vs, K, V, OP.slots(c, self.tables[s], bs), block_size=bs)
             self.K.append(K)
             self.V.append(V)
-        # The pools the kernel reads, dequantised in float64 (blocks nobody uses stay NaN).
-        self.k_pool = kc.astype(np.float64) * ks.astype(np.float64)[:, :, None, None]
-        self.v_pool = vc.astype(np.float64) * vs.astype(np.float64)[:, :, None, None]
+        # The codes and scales the kernel reads (int4 codes unpacked here;
+        # blocks nobody uses keep NaN scales).
+        self.kc, self.vc, self.ks, self.vs = kc.copy(), vc.copy(), ks.copy(), vs.copy()
         if kv == "i4":
             kc, vc = OC.pack_int4(kc), OC.pack_int4(vc)
         self.qs = np.concatenate([[0], np.cumsum(nq)]).astype(np.int32)
@@ -310,12 +310,12 @@ class QuantChunks:
         out = torch.full_like(self.qd, float("nan"))
         pk.pa_prefill(self.pool, self.qd, out, self.qsd, self.tabd, self.ctxd, max(self.nq), max(self.ctx))
         torch.cuda.synchronize()
-        assert pk.pa_check_errors() == 0
+        assert pk.pa_check_errors(self.pool) == 0
         return out.cpu().numpy()
 
     def oracle(self):
-        return OA.paged_prefill(self.q, self.k_pool, self.v_pool, self.tables, self.ctx, self.qs,
-                                block_size=self.bs)
+        return OA.paged_prefill(self.q, self.kc, self.vc, self.tables, self.ctx, self.qs,
+                                block_size=self.bs, k_scale=self.ks, v_scale=self.vs)
 
 
 def Int8Chunks(*args, **kw):
@@ -381,7 +381,7 @@ def test_whole_prompt_of_4096_tokens(D):
     # (sequence, head), the longest walks) beside a short one.
     b = Chunks([4096, 70], [4096, 70], H=2, D=D, seed=53)
     got = b.gpu()
-    assert _pk().pa_check_errors() == 0
+    assert _pk().pa_check_errors(b.pool) == 0
     assert_close(got, b.oracle(), f"4096-token prompt D={D}")
 
 
@@ -406,5 +406,5 @@ def test_random_batches_against_the_oracle(kv, seed):
     else:
         b = QuantChunks(ctx, nq, H=2, D=D, bs=bs, seed=seed, kv=kv)
         got = b.gpu()
-    assert _pk().pa_check_errors() == 0
+    assert _pk().pa_check_errors(b.pool) == 0
     assert_close(got, b.oracle(), f"{kv} seed={seed} D={D} bs={bs}")

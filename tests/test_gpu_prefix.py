@@ -57,7 +57,7 @@ def test_prefix_cached_batch_equals_forked_batch(prompt_tokens, bs):
             rows[s][0].append(kn[s:s + 1])
             rows[s][1].append(vn[s:s + 1])
         torch.cuda.synchronize()
-        assert pk.pa_check_errors() == 0
+        assert pk.pa_check_errors(cached.pool) == 0 and pk.pa_check_errors(forked.pool) == 0
         assert torch.equal(out_c.view(torch.int16), out_f.view(torch.int16)), f"step {t}"
     ct, cc = cached.bm.export(seqs, 64)
     ot, oc = obm.export(list(seqs), 64)

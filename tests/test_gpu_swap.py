@@ -60,7 +60,7 @@ def test_swap_blocks_bit_exact(code, D, bs):
     print(f"swap out {code} D={D} bs={bs} pairs={len(out_pairs)}", flush=True)
     pk.pa_swap_blocks(pool, host, torch.from_numpy(out_pairs).to(DEV), pk.PA_SWAP_OUT)
     torch.cuda.synchronize()
-    assert pk.pa_check_errors() == 0
+    assert pk.pa_check_errors(pool) == 0
     OC.swap_blocks(d_np, h_np, out_pairs, "out")
     for got, ref in zip(hp, h_np):
         assert np.array_equal(got.numpy().view(np.uint8), ref.view(np.uint8))
@@ -68,7 +68,7 @@ def test_swap_blocks_bit_exact(code, D, bs):
     print(f"swap in {code} D={D} bs={bs} pairs={len(in_pairs)}", flush=True)
     pk.pa_swap_blocks(pool, host, torch.from_numpy(in_pairs).to(DEV), pk.PA_SWAP_IN)
     torch.cuda.synchronize()
-    assert pk.pa_check_errors() == 0
+    assert pk.pa_check_errors(pool) == 0
     OC.swap_blocks(d_np, h_np, in_pairs, "in")
     for got, ref in zip(dev, d_np):
         assert np.array_equal(got.cpu().numpy().view(np.uint8), ref.view(np.uint8))
@@ -81,7 +81,7 @@ def test_swap_rejects_bad_arguments_and_flags_bad_pairs():
     before_k = host.k.clone()
     bad = torch.tensor([[0, 4], [9, 1]], dtype=torch.int32, device=DEV)   # host id 4, device id 9 out of range
     pk.pa_swap_blocks(pool, host, bad, pk.PA_SWAP_OUT)
-    assert pk.pa_check_errors() & pk.PA_DEV_BAD_PAIR
+    assert pk.pa_check_errors(pool) & pk.PA_DEV_BAD_PAIR
     assert torch.equal(before_k, host.k)
     with pytest.raises(pk.PagedKVError) as e:
         pk.pa_swap_blocks(pool, host, bad, 7)
@@ -93,7 +93,7 @@ def test_swap_rejects_bad_arguments_and_flags_bad_pairs():
     st = pk.lib.pa_swap_blocks(pool.handle, C.c_void_p(p), C.c_void_p(p), None, None, 4,
                                C.c_void_p(bad.data_ptr()), 1, pk.PA_SWAP_OUT, None)
     assert st == pk.PA_ERR_INVALID_ARG
-    assert pk.pa_check_errors() == 0
+    assert pk.pa_check_errors(pool) == 0
 
 
 @pytest.mark.parametrize("kv,bs", [("f16", 16), ("f16", 64), ("i8", 32)])
@@ -151,7 +151,7 @@ def test_engine_swap_round_trip_is_bit_exact(kv, bs):
     after = torch.empty_like(q)
     eng.decode(seqs, q, after)
     torch.cuda.synchronize()
-    assert pk.pa_check_errors() == 0
+    assert pk.pa_check_errors(eng.pool) == 0
     assert torch.equal(before.view(torch.int16), after.view(torch.int16))
     # And for float pools the result is still attention over the sequence's
     # own rows (int8 pools: bit-identity with the result before the swap).

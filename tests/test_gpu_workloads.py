@@ -1,11 +1,18 @@
 """GPU parity at the full sizes of the five paged-decode workloads.
 
-Each test runs the real step path (native block manager, uploads, copy,
-write, decode) in the launch configuration the benchmark uses and checks:
-tables / slots / copy pairs bit for bit against the oracle's block-manager
-model; stored K/V bytes bit for bit (whole pool where it fits the host,
-sampled blocks otherwise); attention outputs of sampled sequences and heads
-against the fp64 oracle within the stated bars.
+The OPT-13B-shaped batch is checked in exactly the configuration bench.py
+times: the pool, tables and inputs come from bench.py's own workload setup,
+the steps run through bench.py's step call with its engine options (fused
+write + decode, longest-first dispatch, the HEADS schedule, table rows read
+in place from pinned memory, single pass = bench.py's default partition
+size) and warm-up / timed step counts, and every one of the 64 sequences x
+40 heads of the first and the last timed step is compared with the fp64
+oracle; split-K partitions of 512 tokens are a second case. The other
+workloads run the real step path (native block manager, copy, write,
+decode) and check: tables / slots / copy pairs bit for bit against the
+oracle's block-manager model; stored K/V bytes bit for bit (whole pool where
+it fits the host, sampled blocks otherwise); attention outputs against the
+fp64 oracle within the stated bars.
 """
 
 import math
@@ -14,6 +21,7 @@ import numpy as np
 import pytest
 import torch
 
+import bench
 import workloads as W
 from oracle import attention as OA
 from oracle import block_manager as OBM
@@ -46,8 +54,62 @@ def _decode_out(eng, pk, seqs, q, ptok):
     out = torch.empty_like(q)
     eng.decode(seqs, q, out, partition_tokens=ptok)
     torch.cuda.synchronize()
-    assert pk.pa_check_errors() == 0
+    assert pk.pa_check_errors(eng.pool) == 0
     return out.cpu().numpy()
+
+
+@pytest.mark.parametrize("ptok", [bench.DEFAULT_PARTITION_TOKENS, BENCH_PTOK])
+def test_opt13b_bench_launch_full_size(ptok):
+    import types
+    pk, _ = _pk()
+    dev = torch.device(DEV)
+    K_STEPS, WARMUP = 20, 5                        # the benchmark's default invocation
+    args = types.SimpleNamespace(partition_tokens=ptok)
+    ws = bench.setup_workload("opt13b", args, dev, K_STEPS, WARMUP)
+    eng, wl, S, H, D = ws["eng"], ws["wl"], ws["S"], ws["H"], ws["D"]
+    knew, vnew, q, out = ws["knew"], ws["vnew"], ws["q"], ws["out"]
+    assert ws["ptok"] == ptok and eng.fuse_write and eng.longest_first and eng.host_tables
+    print(f"opt13b bench launch: ptok={ptok} S={S} blocks={eng.pool.num_blocks}", flush=True)
+    ring = len(knew)
+    seqs = np.arange(S)
+    first_timed = None
+    for i in range(WARMUP + K_STEPS):
+        ev = None
+        if i % bench.EVENT_EVERY == bench.EVENT_EVERY - 1:
+            ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        eng.step(seqs, knew[i % ring], vnew[i % ring], q, out, decode_events=ev)
+        if i == WARMUP:
+            first_timed = (out.clone(), eng.last_ctx.copy())
+    torch.cuda.synchronize()
+    assert pk.pa_check_errors(eng.pool) == 0
+    assert not eng.bm.batch_shares(seqs)          # so the step ran the HEADS schedule
+    tables, ctx = eng.bm.export(seqs, eng.cap)
+    prefill = [c - 1 - WARMUP for c in wl.context_lens]
+    assert list(ctx) == [c - 1 + K_STEPS for c in wl.context_lens]
+    qh = q.cpu().numpy()
+    news_k = [k.cpu().numpy() for k in knew]
+    news_v = [v.cpu().numpy() for v in vnew]
+    out_last = out.cpu().numpy()
+    out_first, ctx_first = first_timed[0].cpu().numpy(), first_timed[1]
+    scale = 1.0 / math.sqrt(D)
+    for s in range(S):
+        # The sequence's logical rows: its prefill, then one new row per step.
+        Kp = W.normal_torch((prefill[s], H, D), wl.seed, W.STREAM_K, s, dtype=torch.float16, device=DEV)
+        Vp = W.normal_torch((prefill[s], H, D), wl.seed, W.STREAM_V, s, dtype=torch.float16, device=DEV)
+        steps = WARMUP + K_STEPS
+        Ks = np.concatenate([Kp.cpu().numpy(), np.stack([news_k[i % ring][s] for i in range(steps)])])
+        Vs = np.concatenate([Vp.cpu().numpy(), np.stack([news_v[i % ring][s] for i in range(steps)])])
+        # Stored rows, gathered back through the table: bit for bit.
+        row = torch.from_numpy(tables[s][tables[s] >= 0].astype(np.int64)).to(DEV)
+        got_k = OP.gather(eng.pool.k_cache.index_select(0, row).cpu().numpy(), np.arange(row.numel()), ctx[s])
+        got_v = OP.gather(eng.pool.v_cache.index_select(0, row).cpu().numpy(), np.arange(row.numel()), ctx[s])
+        assert np.array_equal(got_k, Ks.astype(np.float64)), f"stored K of seq {s}"
+        assert np.array_equal(got_v, Vs.astype(np.float64)), f"stored V of seq {s}"
+        assert_close(out_last[s], OA.attend(qh[s], Ks, Vs, scale), F16_ATOL, F16_RTOL,
+                     f"last timed step, seq {s} ctx {ctx[s]} ptok {ptok}")
+        c0 = int(ctx_first[s])
+        assert_close(out_first[s], OA.attend(qh[s], Ks[:c0], Vs[:c0], scale), F16_ATOL, F16_RTOL,
+                     f"first timed step, seq {s} ctx {c0} ptok {ptok}")
 
 
 def test_opt13b_full_size():
@@ -67,7 +129,7 @@ def test_opt13b_full_size():
     out = torch.empty_like(q)
     eng.step(np.arange(S), torch.stack([k[-1] for k, _ in src]), torch.stack([v[-1] for _, v in src]), q, out)
     torch.cuda.synchronize()
-    assert pk.pa_check_errors() == 0
+    assert pk.pa_check_errors(eng.pool) == 0
     # Tables and contexts: bit-exact against the oracle's model of the policy.
     obm = OBM.BlockManager(NB, 16, free_order=order)
     for s, c in enumerate(wl.context_lens):
@@ -138,7 +200,7 @@ def test_shared_prefix_full_size(prompt_tokens):
         OC.write_kv(kp, vp, Kph[t], Vph[t], [r[0] for r in res])
         total_pairs += len(pairs)
     torch.cuda.synchronize()
-    assert pk.pa_check_errors() == 0
+    assert pk.pa_check_errors(eng.pool) == 0
     # 1024 = 64 full blocks: no copy; 1020: the first three samples of every
     # prompt copy the partial block, the fourth writes in place.
     assert total_pairs == (0 if prompt_tokens % 16 == 0 else P * (Sm - 1))
@@ -170,7 +232,7 @@ def test_long_context_split_k_full_size():
     out = torch.empty_like(q)
     eng.step(np.arange(S), torch.stack([k[-1] for k, _ in src]), torch.stack([v[-1] for _, v in src]), q, out)
     torch.cuda.synchronize()
-    assert pk.pa_check_errors() == 0
+    assert pk.pa_check_errors(eng.pool) == 0
     obm = OBM.BlockManager(NB, 16, free_order=order)
     for s in range(S):
         obm.add_seq(s, T - 1)
@@ -240,7 +302,7 @@ def test_int8_ring_full_size():
         if t % 1024 == 0:
             print(f"  ring token {t}", flush=True)
     torch.cuda.synchronize()
-    assert pk.pa_check_errors() == 0
+    assert pk.pa_check_errors(eng.pool) == 0
     ot, oc = obm.export(list(range(S)), Wb)
     nt, nc = eng.bm.export(seqs, Wb)
     assert np.array_equal(ot, nt) and np.array_equal(oc, nc)
@@ -282,7 +344,7 @@ def test_int8_ring_full_size():
     extra_v = W.normal_torch((S, H, D), wl.seed, W.STREAM_VNEW, 99, device=DEV)
     eng.step(seqs, extra_k, extra_v, q, out)
     torch.cuda.synchronize()
-    assert pk.pa_check_errors() == 0
+    assert pk.pa_check_errors(eng.pool) == 0
     new_blocks = torch.from_numpy((eng.last_slots // 16).astype(np.int64)).to(DEV)
     assert (eng.last_slots % 16 == 0).all()
     assert np.array_equal(eng.last_slots // 16, ot[:, 0])        # the oldest block is reused

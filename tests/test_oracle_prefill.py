@@ -142,3 +142,58 @@ def test_empty_chunks_and_bad_lengths():
     assert out.shape == (3,) + q.shape[1:]
     with pytest.raises(ValueError):
         A.paged_prefill(q, kp, vp, tables, [10, 2], qs)
+
+
+@pytest.mark.parametrize("qmax", [127, 7])
+def test_quantised_pools_reduce_to_library_causal_sdpa(qmax):
+    # Rows k * 2^-e with integer |k| <= qmax, e depending on the logical block
+    # (5, 6, 7, ...), and one entry of +-qmax in every (block, head): the
+    # int8 (int4) write gives the scale 2^-e and the codes k exactly, so
+    # prefill over the codes and scales must equal torch's causal attention
+    # over the rows themselves. Blocks of one sequence carry different scales
+    # and sit at scattered physical blocks, so a scale taken from the wrong
+    # block, or by logical instead of physical index, fails.
+    H, D, bs = 2, 8, 16
+    ctxs = [40, 21]
+    nbs = [-(-c // bs) for c in ctxs]
+    NB = sum(nbs) + 5
+    order = W.free_order(11, NB)
+    kc = np.zeros((NB, H, bs, D), np.int8)
+    vc = np.zeros((NB, H, bs, D), np.int8)
+    ks = np.zeros((NB, H), np.float16)
+    vs = np.zeros((NB, H), np.float16)
+    rng = np.random.default_rng(11)
+    tables, rows, used = [], [], 0
+    for s, ctx in enumerate(ctxs):
+        table = order[used:used + nbs[s]]
+        used += nbs[s]
+        e = np.array([5 + (t // bs + s) % 3 for t in range(ctx)], np.float64)
+        K = rng.integers(-qmax, qmax + 1, size=(ctx, H, D)).astype(np.float64)
+        V = rng.integers(-qmax, qmax + 1, size=(ctx, H, D)).astype(np.float64)
+        for b in range(nbs[s]):
+            K[b * bs, :, 0] = qmax
+            V[b * bs, :, 1] = -qmax
+        K *= 2.0 ** -e[:, None, None]
+        V *= 2.0 ** -e[:, None, None]
+        C.write_kv_int8(kc, ks, vc, vs, K.astype(np.float32), V.astype(np.float32),
+                        P.slots(ctx, table, bs), bs, qmax=qmax)
+        tables.append(table)
+        rows.append((K, V))
+    nqs = [ctxs[0], 9]
+    qs = np.concatenate([[0], np.cumsum(nqs)]).astype(np.int64)
+    q = W.normal_np((int(qs[-1]), H, D), 11, W.STREAM_Q)
+    out = A.paged_prefill(q, kc, vc, tables, ctxs, qs, block_size=bs, k_scale=ks, v_scale=vs)
+    for s, ctx in enumerate(ctxs):
+        n = nqs[s]
+        K, V = rows[s]
+        Q = torch.from_numpy(q[qs[s]:qs[s + 1]].astype(np.float64)).permute(1, 0, 2)
+        Kt = torch.from_numpy(K).permute(1, 0, 2)
+        Vt = torch.from_numpy(V).permute(1, 0, 2)
+        # The chunk's rows are the context's last n: their causal mask is
+        # aligned to the end of the context.
+        mask = torch.ones(n, ctx, dtype=torch.bool).tril(diagonal=ctx - n)
+        ref = torch.nn.functional.scaled_dot_product_attention(Q, Kt, Vt, attn_mask=mask)
+        np.testing.assert_allclose(out[qs[s]:qs[s + 1]], ref.permute(1, 0, 2).numpy(), rtol=1e-12, atol=1e-13)
+    # Without the scales the codes alone give a different answer.
+    raw = A.paged_prefill(q, kc, vc, tables, ctxs, qs, block_size=bs)
+    assert np.abs(raw - out).max() > 1e-3
