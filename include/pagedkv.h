@@ -238,6 +238,26 @@ pa_status pa_decode(pa_pool* pool, const void* q, pa_dtype q_dtype, void* out,
                     float sm_scale, int32_t partition_tokens, void* workspace,
                     int64_t workspace_bytes, pa_stream stream);
 
+/* pa_decode for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same kernels, but the split-K workspace is the library's own static
+ * device scratch of 32 MiB (one per GPU, held until the process ends) instead
+ * of a caller buffer, and nothing is allocated or freed. Arguments are
+ * pa_decode's without workspace / workspace_bytes; batch order, PA_SCHED_HEADS.
+ * The scratch keeps the last call's partials; every (sequence, head,
+ * partition) a call reads is written by that same call first, so nothing is
+ * cleared. Calls that overlap on one GPU (other streams, other threads) share
+ * the scratch and race: serialise them. Single pass (partition_tokens == 0)
+ * uses no scratch.
+ * Errors: PA_ERR_OUT_OF_RANGE when the split-K partials, pa_decode_workspace_bytes
+ * of the call, exceed 32 MiB (checked before anything is launched); otherwise
+ * as pa_decode. */
+pa_status pa_decode_noalloc(pa_pool* pool, const void* q, pa_dtype q_dtype, void* out,
+                            const int32_t* block_tables, int32_t max_blocks,
+                            const int32_t* context_lens, int32_t num_seqs,
+                            int32_t max_context_len, float sm_scale, int32_t partition_tokens,
+                            pa_stream stream);
+
 /* Dispatch schedules for an ordered decode (seq_order not NULL):
  * PA_SCHED_HEADS  — ranks one after the other, all heads of a rank together
  *                   (each XCD takes 4 adjacent heads: 4 adjacent tiles of each

@@ -124,6 +124,36 @@ int read_and_clear_error_word(int32_t slot, void* stream, int32_t* value) {
   return 0;
 }
 
+// Split-K workspace of pa_decode_noalloc: a file-scope device array, so that
+// callers that cannot allocate (graph capture, tight serving loops) still get
+// split-K decode. Each GPU holds its own copy for the life of the process.
+constexpr int64_t kScratchBytes = int64_t(32) << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+namespace {
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+// Device address of `scratch` on the current device, looked up once per
+// device with that device current (the host-side name of the array is not a
+// device address).
+int scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return int(e);
+  if (dev < 0 || dev >= kMaxDevices) return int(hipErrorInvalidDevice);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return int(e);
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return 0;
+}
+
 }  // namespace pa
 
 using pa::fail;
@@ -341,6 +371,57 @@ pa_status pa_decode(pa_pool* pool, const void* q, pa_dtype q_dtype, void* out, c
                     pa_stream stream) {
   return pa_decode_ordered(pool, q, q_dtype, out, block_tables, max_blocks, context_lens, nullptr, PA_SCHED_HEADS,
                            num_seqs, max_context_len, sm_scale, partition_tokens, workspace, workspace_bytes, stream);
+}
+
+pa_status pa_decode_noalloc(pa_pool* pool, const void* q, pa_dtype q_dtype, void* out,
+                            const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens,
+                            int32_t num_seqs, int32_t max_context_len, float sm_scale,
+                            int32_t partition_tokens, pa_stream stream) {
+  const char* fn = "pa_decode_noalloc";
+  if (!pool) return fail(PA_ERR_INVALID_ARG, "%s: pool is NULL", fn);
+  if (num_seqs < 0 || max_context_len < 0 || partition_tokens < 0 || partition_tokens % pool->block_size)
+    return fail(PA_ERR_INVALID_ARG, "%s: bad sizes (partition_tokens=%d, block_size=%d)", fn, partition_tokens,
+                pool->block_size);
+  const int64_t need = workspace_bytes_for(num_seqs, pool->num_heads, pool->head_dim,
+                                           num_partitions(max_context_len, partition_tokens));
+  if (need > pa::kScratchBytes)
+    return fail(PA_ERR_OUT_OF_RANGE, "%s: split-K needs %lld bytes of workspace, more than the %lld of the "
+                "library's static scratch (fewer sequences, shorter contexts or longer partitions)", fn,
+                (long long)need, (long long)pa::kScratchBytes);
+  void* ws = nullptr;
+  if (need > 0) {
+    const int e = pa::scratch_address(&ws);
+    if (e != 0) return hip_status(fn, e);
+  }
+  if (!block_tables) return fail(PA_ERR_INVALID_ARG, "%s: block_tables is NULL", fn);
+  if (max_blocks < 0 || int64_t(max_blocks) * pool->block_size < int64_t(max_context_len))
+    return fail(PA_ERR_INVALID_ARG, "%s: max_blocks=%d cannot hold max_context_len=%d", fn, max_blocks,
+                max_context_len);
+  pa::DecodeArgs a{};
+  a.q = q;
+  a.q_dtype = q_dtype;
+  a.out = out;
+  a.k = pool->k_cache;
+  a.v = pool->v_cache;
+  a.k_scale = pool->k_scale;
+  a.v_scale = pool->v_scale;
+  a.kv_dtype = pool->kv_dtype;
+  a.tables = block_tables;
+  a.max_blocks = max_blocks;
+  a.block_size = pool->block_size;
+  a.max_tokens = 0;
+  a.err = pool->err;
+  a.ctx = context_lens;
+  a.order = nullptr;
+  a.schedule = PA_SCHED_HEADS;
+  a.num_seqs = num_seqs;
+  a.num_heads = pool->num_heads;
+  a.head_dim = pool->head_dim;
+  a.num_blocks = pool->num_blocks;
+  a.max_ctx = max_context_len;
+  a.sm_scale = sm_scale;
+  a.partition_tokens = partition_tokens;
+  return decode_common(fn, a, ws, need, stream);
 }
 
 pa_status pa_decode_ordered(pa_pool* pool, const void* q, pa_dtype q_dtype, void* out,

@@ -67,6 +67,7 @@ _SIGS = {
     "pa_swap_blocks": ([_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _vp], _i32),
     "pa_decode_workspace_bytes": ([_vp, _i32, _i32, _i32, _pi64], _i32),
     "pa_decode": ([_vp, _vp, _i32, _vp, _vp, _i32, _vp, _i32, _i32, _f32, _i32, _vp, _i64, _vp], _i32),
+    "pa_decode_noalloc": ([_vp, _vp, _i32, _vp, _vp, _i32, _vp, _i32, _i32, _f32, _i32, _vp], _i32),
     "pa_decode_ordered": ([_vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _f32, _i32, _vp, _i64,
                            _vp], _i32),
     "pa_write_decode": ([_vp, _vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _f32,
@@ -341,6 +342,26 @@ def pa_decode(pool: Pool, q, out, block_tables, context_lens, max_context_len: i
                                  _ptr(seq_order, "seq_order", torch.int32), int(schedule), S,
                                  int(max_context_len), float(sm_scale), int(partition_tokens),
                                  _ptr(workspace, "workspace"), ws_bytes, _stream(stream, q)), "pa_decode_ordered")
+
+
+SCRATCH_BYTES = 32 << 20      # the static split-K scratch of pa_decode_noalloc
+
+
+def pa_decode_noalloc(pool: Pool, q, out, block_tables, context_lens, max_context_len: int,
+                      sm_scale: float = 0.0, partition_tokens: int = 0, stream=None) -> None:
+    """pa_decode with the library's static split-K scratch: allocates nothing.
+    Calls that overlap on one GPU share the scratch (serialise them)."""
+    torch = _torch()
+    S = int(q.shape[0])
+    if tuple(q.shape) != (S, pool.num_heads, pool.head_dim) or out.shape != q.shape or out.dtype != q.dtype:
+        raise PagedKVError(PA_ERR_INVALID_ARG, "q/out shape or dtype mismatch")
+    if block_tables.dim() != 2 or block_tables.shape[0] < S or context_lens.numel() < S:
+        raise PagedKVError(PA_ERR_INVALID_ARG, "block_tables/context_lens do not cover the batch")
+    _check(lib.pa_decode_noalloc(pool.handle, _ptr(q, "q"), dtype_code(q.dtype), _ptr(out, "out"),
+                                 _ptr(block_tables, "block_tables", torch.int32), int(block_tables.shape[1]),
+                                 _ptr(context_lens, "context_lens", torch.int32), S, int(max_context_len),
+                                 float(sm_scale), int(partition_tokens), _stream(stream, q)),
+           "pa_decode_noalloc")
 
 
 def pa_prefill(pool: Pool, q, out, query_start, block_tables, context_lens, max_query_len: int,
