@@ -62,6 +62,7 @@ def parse():
 
 DEFAULT_PARTITION_TOKENS = 0        # single pass: one decode kernel per step
 CALIBRATION_BYTES = 1 << 30
+CPU_SHARE_CORES = 16                # host cores a one-GPU job may use on the GPU machine
 EVENT_EVERY = 4
 
 # The profiler commands whose summaries live under profiles/ (run from the
@@ -466,7 +467,9 @@ def _cpu_run(seconds: float, workers: int) -> dict:
 
 def cpu_baseline(seconds: float) -> dict:
     """The oracle on one thread (the reported baseline) and on a pool of
-    processes over sequences (one thread each), up to 16 host cores."""
+    processes over sequences (one thread each) on the host cores this process
+    may run on, at most 16: the box gives one GPU's jobs a share of 16 cores,
+    whatever the affinity mask shows (both counts are reported)."""
     d = _cpu_run(seconds, 1)
     if "error" in d:
         return d
@@ -476,13 +479,17 @@ def cpu_baseline(seconds: float) -> dict:
                      f"whole passes over the 64-sequence batch, all 40 heads: {d['bytes'] / 1e6:.1f} MB "
                      f"of KV in {d['seconds']:.2f} s on one thread",
            "seqs_per_s": round(d["seqs"] / d["seconds"], 4)}
-    n = min(16, len(os.sched_getaffinity(0)))
+    affinity = len(os.sched_getaffinity(0))
+    n = min(CPU_SHARE_CORES, affinity)
+    res["affinity_cores"] = affinity
     if n > 1:
         m = _cpu_run(seconds, n)
         if "error" not in m:
             res["multi_core"] = {"value": round(m["bytes"] / m["seconds"] / 1e9, 4), "unit": "GB/s", "cores": n,
+                                 "affinity_cores": affinity,
                                  "sample": f"{m['passes']} whole passes, sequences over {n} processes of one "
-                                           f"thread, {m['seconds']:.2f} s wall",
+                                           f"thread ({affinity} cores in the affinity mask, {CPU_SHARE_CORES} "
+                                           f"the host share of one GPU), {m['seconds']:.2f} s wall",
                                  "seqs_per_s": round(m["seqs"] / m["seconds"], 4)}
     return res
 
@@ -511,15 +518,42 @@ def main():
 
     import numpy as np
     import torch
-    import workloads as W
     import paged_kv_cache_249_amd as pk
-    from paged_kv_cache_249_amd.engine import PagedDecodeEngine
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    K, Wm = args.steps, args.warmup
-    ws = setup_workload(args.workload, args, dev, K, Wm)
-    eng, wl, S, H, D = ws["eng"], ws["wl"], ws["S"], ws["H"], ws["D"]
+    result, ws = run_workload(args.workload, args, dev, args.steps, args.warmup, args.profile_run)
+    if args.profile_run:
+        print(json.dumps(result))
+        return 0
+    eng, q = ws["eng"], ws["q"]
+    if "unique_bytes_of" in ws and not args.no_extras:
+        result["extras"] = shared_prefix_cache_probe(pk, torch, np, eng, q, dev,
+                                                     result["unique_kv_bytes_per_decode"])
+    if args.workload == "opt13b":
+        if not args.no_extras:
+            result["extras"] = extras(eng, ws["wl"], q, ws["ptok"], dev)
+        del eng, ws, q
+        torch.cuda.empty_cache()
+        if not args.no_extras:
+            # The four other workloads, each through the same timed step loop
+            # (same step and warm-up counts), and the copy-on-write step.
+            result["extras"]["configs"] = other_configs(args, dev)
+        if not args.no_cpu_baseline:
+            result["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def run_workload(name, args, dev, K, Wm, profile_run=False):
+    """Set up one workload, run Wm untimed warm-up steps and K timed steps of
+    the whole path, and return (the bench line's fields, the workload)."""
+    import numpy as np
+    import torch
+    import paged_kv_cache_249_amd as pk
+
+    ws = setup_workload(name, args, dev, K, Wm)
+    eng, wl, S = ws["eng"], ws["wl"], ws["S"]
     knew, vnew, q, out, ptok = ws["knew"], ws["vnew"], ws["q"], ws["out"], ws["ptok"]
     ring = len(knew)
     kv_bytes_of = ws["kv_bytes_of"]
@@ -528,6 +562,15 @@ def main():
     torch.cuda.synchronize()
     assert pk.pa_check_errors(eng.pool) == 0
 
+    # A full Python garbage collection inside the loop stalls the host for
+    # tens of ms (the objects of torch's import): collect and freeze them
+    # first, and keep the collector off until the timed steps are done. The
+    # first full collection of a process also leaves the host's caches cold
+    # (the next step's host work took 309 instead of 60 us), so it runs
+    # before the warm-up steps, which warm them again.
+    gc.collect()
+    gc.freeze()
+    gc.disable()
     # Warm-up steps carry timing events like the timed steps do: the first
     # timed event pair of a process can stall the host for tens of ms.
     for i in range(Wm):
@@ -540,9 +583,10 @@ def main():
             ev[0].elapsed_time(ev[1])
     torch.cuda.synchronize()
 
-    if args.profile_run:
+    if profile_run:
         # Calibration for the HBM byte counters: a plain copy of known size
         # (CALIBRATION_BYTES read, CALIBRATION_BYTES written), then the steps.
+        gc.enable()
         a = torch.empty(CALIBRATION_BYTES, dtype=torch.uint8, device=dev)
         b = torch.empty(CALIBRATION_BYTES, dtype=torch.uint8, device=dev)
         pk.pa_stream_copy(b, a)
@@ -550,10 +594,9 @@ def main():
         for i in range(K):
             eng.step(seqs, knew[i % ring], vnew[i % ring], q, out)
         torch.cuda.synchronize()
-        print(json.dumps({"profile_run": True, "steps": K, "calibration_bytes": CALIBRATION_BYTES,
-                          "kv_bytes_per_decode": kv_bytes_of(eng.last_ctx),
-                          "decode_source_sha256": _sha256(DECODE_SOURCE)}))
-        return 0
+        return ({"profile_run": True, "steps": K, "calibration_bytes": CALIBRATION_BYTES,
+                 "kv_bytes_per_decode": kv_bytes_of(eng.last_ctx),
+                 "decode_source_sha256": _sha256(DECODE_SOURCE)}, ws)
 
     # The decode launch is bracketed by a pair of timing events on every
     # EVENT_EVERY-th step of the timed loop (a timed event pair costs the step
@@ -562,14 +605,7 @@ def main():
     events = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for i in timed}
     kv_bytes = []
     torch.cuda.synchronize()
-    host_s = 0.0
     host_each = []
-    # A full Python garbage collection inside the loop stalls the host for
-    # tens of ms (the objects of torch's import): collect and freeze them
-    # first, and keep the collector off during the timed steps.
-    gc.collect()
-    gc.freeze()
-    gc.disable()
     t0 = time.perf_counter()
     for i in range(K):
         h0 = time.perf_counter()
@@ -623,23 +659,107 @@ def main():
         "kv_bytes_per_decode": int(bytes_avg),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": recorded_traffic(args.workload)},
+                     "traffic": recorded_traffic(name)},
         "device_error_bits": dev_err,
     }
-
     if "unique_bytes_of" in ws:
         ub = ws["unique_bytes_of"](eng.last_ctx)
         result["unique_kv_bytes_per_decode"] = ub
         result["unique_gbs"] = round(ub / dec_avg_s / 1e9, 2)
-        if not args.no_extras:
-            result["extras"] = shared_prefix_cache_probe(pk, torch, np, eng, q, dev, ub)
-    if args.workload == "opt13b":
-        if not args.no_extras:
-            result["extras"] = extras(eng, wl, q, ptok, dev)
-        if not args.no_cpu_baseline:
-            result["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
-    print(json.dumps(result), flush=True)
-    return 0
+    return result, ws
+
+
+def other_configs(args, dev):
+    """The long-context, int8-ring, shared-prefix and tiny workloads, each
+    measured like the headline (its own K timed steps after Wm warm-up
+    steps; decode time from HIP events on the step's stream), plus the
+    shared-prefix cache probe and the copy-on-write step of the 1020-token
+    prompts."""
+    import numpy as np
+    import torch
+    import paged_kv_cache_249_amd as pk
+
+    res = {}
+    for name in ("long_context", "int8_ring", "shared_prefix", "tiny"):
+        t0 = time.perf_counter()
+        r, ws = run_workload(name, args, dev, args.steps, args.warmup)
+        entry = {k: r[k] for k in ("value", "ms_per_step", "decode_kernel_us", "decode_kernel_us_median",
+                                   "kv_bytes_per_decode", "decode_steps_seqs_per_s", "decode_only_seqs_per_s",
+                                   "device_error_bits")}
+        entry["workload"] = r["config"]["workload"]
+        entry["partition_tokens"] = r["config"]["partition_tokens"]
+        entry["dtype"] = r["dtype"]
+        entry["roofline"] = r["roofline"]
+        if "unique_kv_bytes_per_decode" in r:
+            entry["unique_kv_bytes_per_decode"] = r["unique_kv_bytes_per_decode"]
+            entry["unique_gbs"] = r["unique_gbs"]
+            entry["cache"] = shared_prefix_cache_probe(pk, torch, np, ws["eng"], ws["q"], dev,
+                                                       r["unique_kv_bytes_per_decode"])
+        del ws
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        entry["setup_and_run_s"] = round(time.perf_counter() - t0, 1)
+        res[name] = entry
+    res["shared_prefix_cow_step"] = cow_step_probe(pk, torch, np, dev)
+    return res
+
+
+def cow_step_probe(pk, torch, np, dev, reps=5):
+    """The step that copies: 8 prompts of 1020 tokens (63 full blocks and
+    12 tokens) forked into 4 samples each, then the first private token of
+    every sample. The first three samples of a prompt append into the
+    shared partial block and copy it (24 pairs), the fourth writes in place.
+    Two 1 GiB streaming reads (about 0.3 ms) are queued first, so that the
+    step's host work (append, export) overlaps them and its kernels run back
+    to back as in a stream of steps; the step (copy, write + decode) is timed
+    on the device from the end of those reads to its own end, and the copy
+    and the decode launches each with their own events. The workload is set
+    up afresh for each of ``reps`` repetitions."""
+    import workloads as W
+    from paged_kv_cache_249_amd.engine import PagedDecodeEngine
+
+    wl = W.shared_prefix(prompt_tokens=1020)
+    P, Sm, pt, H, D = wl.prompts, wl.samples, wl.prompt_tokens, wl.num_heads, wl.head_dim
+    S = P * Sm
+    cap = -(-(pt + wl.private_tokens) // 16)
+    seqs = np.arange(S)
+    step_us, copy_us, dec_us, pairs = [], [], [], None
+    busy = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1024, dtype=torch.int32, device=dev)
+    for r in range(reps):
+        eng = PagedDecodeEngine(wl.num_blocks, H, D, pk.PA_F16, S, cap,
+                                free_order=W.free_order(wl.seed, wl.num_blocks), device=dev)
+        for p in range(P):
+            k = W.normal_torch((pt, H, D), wl.seed, W.STREAM_K, p, dtype=torch.float16, device=dev)
+            v = W.normal_torch((pt, H, D), wl.seed, W.STREAM_V, p, dtype=torch.float16, device=dev)
+            eng.add_sequence(p * Sm, k, v)
+            for j in range(1, Sm):
+                eng.fork(p * Sm, p * Sm + j)
+        kn = W.normal_torch((S, H, D), wl.seed, W.STREAM_KNEW, 0, dtype=torch.float16, device=dev)
+        vn = W.normal_torch((S, H, D), wl.seed, W.STREAM_VNEW, 0, dtype=torch.float16, device=dev)
+        q = W.normal_torch((S, H, D), wl.seed, W.STREAM_Q, dtype=torch.float16, device=dev)
+        out = torch.empty_like(q)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+        torch.cuda.synchronize()
+        for _ in range(2):
+            pk.pa_stream_read(busy, sink)
+        ev[0].record()
+        eng.step(seqs, kn, vn, q, out, copy_events=(ev[1], ev[2]), decode_events=(ev[3], ev[4]))
+        ev[5].record()
+        torch.cuda.synchronize()
+        assert pk.pa_check_errors(eng.pool) == 0
+        pairs = eng.last_pairs
+        step_us.append(ev[0].elapsed_time(ev[5]) * 1e3)
+        copy_us.append(ev[1].elapsed_time(ev[2]) * 1e3)
+        dec_us.append(ev[3].elapsed_time(ev[4]) * 1e3)
+        del eng, kn, vn, q, out
+        torch.cuda.empty_cache()
+    block_bytes = 2 * H * 16 * D * 2                    # K and V of one block, fp16
+    med = lambda x: round(float(np.median(x)), 2)
+    return {"prompt_tokens": pt, "samples": S, "cow_pairs": int(pairs), "copy_bytes_read": int(pairs) * block_bytes,
+            "copy_kernel_us": med(copy_us), "decode_us": med(dec_us), "step_us": med(step_us),
+            "copy_gbs_read_plus_write": round(2 * int(pairs) * block_bytes / (np.median(copy_us) * 1e-6) / 1e9, 1),
+            "copy_share_of_step": round(float(np.median(copy_us) / np.median(step_us)), 4), "reps": reps}
 
 
 def setup_workload(name, args, dev, K, Wm):

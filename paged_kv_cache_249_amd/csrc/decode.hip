@@ -234,6 +234,86 @@ struct QSlice<_Float16, _Float16, 8> {
   }
 };
 
+// Codes as fp16 without a conversion instruction per value. A byte b placed
+// under the exponent byte 0x64 reads as the fp16 value 1024 + b (ulp 1); int8
+// codes, flipped to b = c + 128, become 1152 + c. An int4 nibble n placed in
+// the high nibble of a byte under 0x54 reads as 64 + n (ulp 1/16 times 16),
+// so a code c = n - 8 becomes 72 + c. One v_perm_b32 builds two such fp16
+// values from two code bytes; the dot with q then runs on v_dot2c_f32_f16
+// (exact fp16 products, fp32 sums) and the V sum on v_fma_mix_f32 (fp32
+// weight times fp16 value, fp32 sum). The constant offsets are taken off once
+// per row of logits (offset * sum of q) and once per hand-over of the
+// weighted V sum (offset * sum of the weights applied).
+constexpr uint32_t kPermLo = 0x04010400u;   // bytes b0, b1 of the second operand under the first's byte 0
+constexpr uint32_t kPermHi = 0x04030402u;   // bytes b2, b3
+constexpr float kInt8Offset = 1152.f;       // 1024 + 128
+constexpr float kInt4Offset = 72.f;         // 64 + 8
+
+__device__ __forceinline__ uint32_t i8_pair(uint32_t flipped, uint32_t sel) {
+  return __builtin_amdgcn_perm(0x64646464u, flipped, sel);
+}
+__device__ __forceinline__ uint32_t i4_pair(uint32_t high_nibbles, uint32_t sel) {
+  return __builtin_amdgcn_perm(0x54545454u, high_nibbles, sel);
+}
+
+// int8 pools with fp16 q: q as fp16 pairs in natural order (the order
+// i8_pair gives the codes of a word), and as floats for the fp16 hot rows of
+// mixed pages (dead, and dropped, in the other kernels).
+template <>
+struct QSlice<int8_t, _Float16, 16> {
+  uint32_t w[8];
+  float f[16];
+  __device__ void load(const _Float16* src) {
+    const uint4 a = reinterpret_cast<const uint4*>(src)[0];
+    const uint4 b = reinterpret_cast<const uint4*>(src)[1];
+    const uint32_t n[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      w[m] = n[m];
+      f[2 * m] = lo_f16(n[m]);
+      f[2 * m + 1] = hi_f16(n[m]);
+    }
+  }
+};
+
+// int4 pools with fp16 q. Word j of an 8-byte chunk holds dims 8j .. 8j+7,
+// the even ones in the low nibbles; i4_pair gives (8j, 8j+2), (8j+4, 8j+6)
+// from the even nibbles and (8j+1, 8j+3), (8j+5, 8j+7) from the odd ones, so
+// q is kept in pairs of that order.
+template <>
+struct QSlice<Int4, _Float16, 16> {
+  uint32_t w[8];
+  float f[16];
+  __device__ void load(const _Float16* src) {
+    const uint4 a = reinterpret_cast<const uint4*>(src)[0];
+    const uint4 b = reinterpret_cast<const uint4*>(src)[1];
+    const uint32_t n[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};   // n[m] = (q[2m], q[2m+1])
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      w[4 * j + 0] = __builtin_amdgcn_perm(n[4 * j + 1], n[4 * j], 0x05040100u);      // q[8j], q[8j+2]
+      w[4 * j + 1] = __builtin_amdgcn_perm(n[4 * j + 3], n[4 * j + 2], 0x05040100u);  // q[8j+4], q[8j+6]
+      w[4 * j + 2] = __builtin_amdgcn_perm(n[4 * j + 1], n[4 * j], 0x07060302u);      // q[8j+1], q[8j+3]
+      w[4 * j + 3] = __builtin_amdgcn_perm(n[4 * j + 3], n[4 * j + 2], 0x07060302u);  // q[8j+5], q[8j+7]
+    }
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      f[2 * m] = lo_f16(n[m]);
+      f[2 * m + 1] = hi_f16(n[m]);
+    }
+  }
+};
+
+// Offset carried by the logits of a path (0: none).
+template <typename KV, typename QT>
+constexpr float kKOffset = std::is_same<QT, _Float16>::value
+                               ? (std::is_same<KV, int8_t>::value ? kInt8Offset
+                                  : std::is_same<KV, Int4>::value ? kInt4Offset : 0.f)
+                               : (std::is_same<KV, Int4>::value ? 8.f : 0.f);
+// Offset carried by the values of a path's V sum (0: none).
+template <typename KV>
+constexpr float kVOffset = std::is_same<KV, int8_t>::value ? kInt8Offset
+                           : std::is_same<KV, Int4>::value ? kInt4Offset : 0.f;
+
 template <typename KV, typename QT, int EPC>
 __device__ __forceinline__ float dot16(const uint4& r, const QSlice<KV, QT, EPC>& q) {
   const uint32_t w[4] = {r.x, r.y, r.z, r.w};
@@ -251,6 +331,14 @@ __device__ __forceinline__ float dot16(const uint4& r, const QSlice<KV, QT, EPC>
         s = fmaf(lo_f16(w[j]), q.f[2 * j], s);
         s = fmaf(hi_f16(w[j]), q.f[2 * j + 1], s);
       }
+    }
+  } else if constexpr (std::is_same<QT, _Float16>::value) {
+    // int8 codes with fp16 q: sum of q (1152 + c).
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t x = w[j] ^ 0x80808080u;
+      s = __builtin_amdgcn_fdot2(as_h2(i8_pair(x, kPermLo)), as_h2(q.w[2 * j]), s, false);
+      s = __builtin_amdgcn_fdot2(as_h2(i8_pair(x, kPermHi)), as_h2(q.w[2 * j + 1]), s, false);
     }
   } else {
 #pragma unroll
@@ -277,22 +365,27 @@ __device__ __forceinline__ void axpy16(float p, const uint4& r, float (&acc)[EPC
       acc[2 * j + 1] = fmaf(p, hi_f16(w[j]), acc[2 * j + 1]);
     }
   } else {
+    // int8 codes: acc += p (1152 + c).
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      acc[4 * j + 0] = fmaf(p, i8_at<0>(w[j]), acc[4 * j + 0]);
-      acc[4 * j + 1] = fmaf(p, i8_at<1>(w[j]), acc[4 * j + 1]);
-      acc[4 * j + 2] = fmaf(p, i8_at<2>(w[j]), acc[4 * j + 2]);
-      acc[4 * j + 3] = fmaf(p, i8_at<3>(w[j]), acc[4 * j + 3]);
+      const uint32_t x = w[j] ^ 0x80808080u;
+      const h2_t lo = as_h2(i8_pair(x, kPermLo));
+      const h2_t hi = as_h2(i8_pair(x, kPermHi));
+      acc[4 * j + 0] = fmaf(p, float(lo.x), acc[4 * j + 0]);
+      acc[4 * j + 1] = fmaf(p, float(lo.y), acc[4 * j + 1]);
+      acc[4 * j + 2] = fmaf(p, float(hi.x), acc[4 * j + 2]);
+      acc[4 * j + 3] = fmaf(p, float(hi.y), acc[4 * j + 3]);
     }
   }
 }
 
-// int4 chunks: 8 bytes, 16 unsigned nibbles n = code + 8 (the callers account
-// for the offset). The low nibbles of word j are dims 8j, 8j+2, 8j+4, 8j+6,
-// the high ones 8j+1, ...; each byte of a masked word converts to float in
-// one instruction (v_cvt_f32_ubyte0..3). The masked words pass through an
-// empty asm statement so that the compiler, which knows they hold nibbles,
-// does not fold each conversion into a bit-field extract plus a conversion.
+// int4 chunks: 8 bytes, 16 unsigned nibbles n = code + 8. The low nibbles of
+// word j are dims 8j, 8j+2, 8j+4, 8j+6, the high ones 8j+1, .... With fp16 q
+// both products go through i4_pair (above). With fp32 q the logits take each
+// byte of a masked word to float in one instruction (v_cvt_f32_ubyte0..3);
+// the masked words pass through an empty asm statement so that the compiler,
+// which knows they hold nibbles, does not fold each conversion into a
+// bit-field extract plus a conversion.
 __device__ __forceinline__ void nibble_words(uint32_t w, uint32_t& lo, uint32_t& hi) {
   lo = w & 0x0F0F0F0Fu;
   hi = (w >> 4) & 0x0F0F0F0Fu;
@@ -303,32 +396,52 @@ __device__ __forceinline__ float dot16(const uint2& r, const QSlice<KV, QT, EPC>
   static_assert(std::is_same<KV, Int4>::value && EPC == 16, "8-byte chunks are int4");
   const uint32_t w[2] = {r.x, r.y};
   float s = 0.f;
+  if constexpr (std::is_same<QT, _Float16>::value) {
+    // Sum of q (72 + c): even dims' nibbles moved up into the high nibble.
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    uint32_t lo, hi;
-    nibble_words(w[j], lo, hi);
+    for (int j = 0; j < 2; ++j) {
+      const uint32_t ev = (w[j] << 4) & 0xF0F0F0F0u;
+      const uint32_t od = w[j] & 0xF0F0F0F0u;
+      s = __builtin_amdgcn_fdot2(as_h2(i4_pair(ev, kPermLo)), as_h2(q.w[4 * j + 0]), s, false);
+      s = __builtin_amdgcn_fdot2(as_h2(i4_pair(ev, kPermHi)), as_h2(q.w[4 * j + 1]), s, false);
+      s = __builtin_amdgcn_fdot2(as_h2(i4_pair(od, kPermLo)), as_h2(q.w[4 * j + 2]), s, false);
+      s = __builtin_amdgcn_fdot2(as_h2(i4_pair(od, kPermHi)), as_h2(q.w[4 * j + 3]), s, false);
+    }
+  } else {
+    // fp32 q: sum of q n with n = c + 8.
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      s = fmaf(float((lo >> (8 * b)) & 0xFFu), q.f[8 * j + 2 * b], s);
-      s = fmaf(float((hi >> (8 * b)) & 0xFFu), q.f[8 * j + 2 * b + 1], s);
+    for (int j = 0; j < 2; ++j) {
+      uint32_t lo, hi;
+      nibble_words(w[j], lo, hi);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        s = fmaf(float((lo >> (8 * b)) & 0xFFu), q.f[8 * j + 2 * b], s);
+        s = fmaf(float((hi >> (8 * b)) & 0xFFu), q.f[8 * j + 2 * b + 1], s);
+      }
     }
   }
   return s;
 }
 
+// acc += p (72 + c) over the 16 codes of an 8-byte int4 chunk.
 template <typename KV, int EPC>
 __device__ __forceinline__ void axpy16(float p, const uint2& r, float (&acc)[EPC]) {
   static_assert(std::is_same<KV, Int4>::value && EPC == 16, "8-byte chunks are int4");
   const uint32_t w[2] = {r.x, r.y};
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    uint32_t lo, hi;
-    nibble_words(w[j], lo, hi);
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      acc[8 * j + 2 * b] = fmaf(p, float((lo >> (8 * b)) & 0xFFu), acc[8 * j + 2 * b]);
-      acc[8 * j + 2 * b + 1] = fmaf(p, float((hi >> (8 * b)) & 0xFFu), acc[8 * j + 2 * b + 1]);
-    }
+    const uint32_t ev = (w[j] << 4) & 0xF0F0F0F0u;
+    const uint32_t od = w[j] & 0xF0F0F0F0u;
+    const h2_t e01 = as_h2(i4_pair(ev, kPermLo)), e23 = as_h2(i4_pair(ev, kPermHi));
+    const h2_t o01 = as_h2(i4_pair(od, kPermLo)), o23 = as_h2(i4_pair(od, kPermHi));
+    acc[8 * j + 0] = fmaf(p, float(e01.x), acc[8 * j + 0]);
+    acc[8 * j + 2] = fmaf(p, float(e01.y), acc[8 * j + 2]);
+    acc[8 * j + 4] = fmaf(p, float(e23.x), acc[8 * j + 4]);
+    acc[8 * j + 6] = fmaf(p, float(e23.y), acc[8 * j + 6]);
+    acc[8 * j + 1] = fmaf(p, float(o01.x), acc[8 * j + 1]);
+    acc[8 * j + 3] = fmaf(p, float(o01.y), acc[8 * j + 3]);
+    acc[8 * j + 5] = fmaf(p, float(o23.x), acc[8 * j + 5]);
+    acc[8 * j + 7] = fmaf(p, float(o23.y), acc[8 * j + 7]);
   }
 }
 
@@ -569,18 +682,21 @@ void decode_kernel(Params p, const int32_t* __restrict__ tables, const int32_t* 
   float acc[EPC];
 #pragma unroll
   for (int e = 0; e < EPC; ++e) acc[e] = 0.f;
-  // int4: the loop works on unsigned nibbles n = code + 8. A logit is then
-  // sum q n - 8 sum q (q_bias = 8 sum q over the row, set before the first
-  // unit), and every value of the lane's rows carries +8, so the lane also
-  // keeps vbias = sum of the weights it has applied (rescaled with acc) and
-  // takes 8 vbias off acc when it hands over.
+  // Quantised pools: the loop works on codes plus a constant offset (see
+  // kKOffset / kVOffset). A logit is then sum q (c + off_k) - off_k sum q
+  // (q_bias = off_k sum q over the row, set before the first unit), and
+  // every value of the lane's rows carries off_v, so the lane also keeps
+  // vbias = sum of the weights it has applied (rescaled with acc) and takes
+  // off_v vbias off acc when it hands over.
+  constexpr float kKOff = kKOffset<KV, QT>;
+  constexpr float kVOff = kVOffset<KV>;
   float q_bias = 0.f, vbias = 0.f;
   auto prepare_q = [&]() {
-    if constexpr (kInt4) {
+    if constexpr (kKOff != 0.f) {
       float qsum = 0.f;
 #pragma unroll
       for (int e = 0; e < EPC; ++e) qsum += qs.f[e];
-      q_bias = 8.f * group_sum<CPT>(qsum);
+      q_bias = kKOff * group_sum<CPT>(qsum);
     }
   };
   // A bad table entry is only recorded here and flagged after the loop: a
@@ -657,7 +773,7 @@ void decode_kernel(Params p, const int32_t* __restrict__ tables, const int32_t* 
   auto flush = [&](int pidx) {
     float fm = m, fl = l, fa[EPC];
 #pragma unroll
-    for (int e = 0; e < EPC; ++e) fa[e] = kInt4 ? acc[e] - 8.f * vbias : acc[e];
+    for (int e = 0; e < EPC; ++e) fa[e] = kVOff != 0.f ? acc[e] - kVOff * vbias : acc[e];
 #pragma unroll
     for (int mask = CPT; mask < kWave; mask <<= 1) {
       const float m2 = __shfl_xor(fm, mask);
@@ -722,7 +838,7 @@ void decode_kernel(Params p, const int32_t* __restrict__ tables, const int32_t* 
     float sc[NLD];
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
-      if constexpr (kInt4)
+      if constexpr (kKOff != 0.f)
         sc[i] = (group_sum<CPT>(dot16(kr[i], qs)) - q_bias) * (t.kscale * p.scale_log2);
       else
         sc[i] = group_sum<CPT>(dot16(kr[i], qs)) * (t.kscale * p.scale_log2);
@@ -742,7 +858,7 @@ void decode_kernel(Params p, const int32_t* __restrict__ tables, const int32_t* 
     const float mn = fmaxf(m, bmax);
     const float alpha = __builtin_amdgcn_exp2f(m - mn);
     l *= alpha;
-    if constexpr (kInt4) vbias *= alpha;
+    if constexpr (kVOff != 0.f) vbias *= alpha;
 #pragma unroll
     for (int e = 0; e < EPC; ++e) acc[e] *= alpha;
 #pragma unroll
@@ -750,7 +866,7 @@ void decode_kernel(Params p, const int32_t* __restrict__ tables, const int32_t* 
       const float pi = __builtin_amdgcn_exp2f(sc[i] - mn);
       l += pi;
       axpy16<KV, EPC>(pi * t.vscale, vr[i], acc);
-      if constexpr (kInt4) vbias += pi * t.vscale;
+      if constexpr (kVOff != 0.f) vbias += pi * t.vscale;
     }
     m = mn;
     if constexpr (!kWavePart && !kMixed) {
@@ -816,7 +932,7 @@ void decode_kernel(Params p, const int32_t* __restrict__ tables, const int32_t* 
       const float mn = fmaxf(m, bmax);
       const float alpha = __builtin_amdgcn_exp2f(m - mn);
       l *= alpha;
-      if constexpr (kInt4) vbias *= alpha;   // hot rows are fp16: they add no offset
+      if constexpr (kVOff != 0.f) vbias *= alpha;   // hot rows are fp16: they add no offset
 #pragma unroll
       for (int e = 0; e < EPC; ++e) acc[e] *= alpha;
 #pragma unroll
@@ -845,6 +961,20 @@ void decode_kernel(Params p, const int32_t* __restrict__ tables, const int32_t* 
   // 8 loads per unit (fp32 rows of 128) that would spill, and 8 loads per
   // lane already keep enough bytes in flight, so those run single-buffered.
   constexpr bool kDouble = PA_DECODE_PREFETCH != 0 && NLD <= 4;
+  // Work that goes out with the wave's first unit: the hot block of mixed
+  // pages is loaded just before it and folded in while it is in flight.
+  auto before_first = [&]() {
+    if constexpr (kMixed) {
+      if (hot_mine) hot_load();
+    }
+  };
+  auto after_first = [&]() {
+    prepare_q();
+    if constexpr (kMixed) {
+      if (hot_mine) hot_process();
+    }
+    convert_new_row();
+  };
   if (!kDouble) {
     prepare_q();
     convert_new_row();
@@ -860,15 +990,9 @@ void decode_kernel(Params p, const int32_t* __restrict__ tables, const int32_t* 
     Chunk ka[NLD], va[NLD], kb[NLD], vb[NLD];
     const int last = iters - 1;
     int e_next = last >= 1 ? e1 : e0;
-    if constexpr (kMixed) {
-      if (hot_mine) hot_load();
-    }
+    before_first();
     TileRef ta = fetch(0, e0, ka, va);
-    prepare_q();
-    if constexpr (kMixed) {
-      if (hot_mine) hot_process();
-    }
-    convert_new_row();
+    after_first();
     int k = 0;
     for (; k + 2 < iters; k += 2) {
       const int e1 = e_next;

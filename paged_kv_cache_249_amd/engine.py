@@ -351,11 +351,13 @@ class PagedDecodeEngine:
 
     # -- the step ---------------------------------------------------------------
     def step(self, seqs, k_new, v_new, q, out, *, decode: bool = True, stream=None,
-             decode_events=None) -> None:
+             decode_events=None, copy_events=None) -> None:
         """Append one token per sequence of ``seqs`` (order = rows of k_new/q) and decode.
 
-        ``decode_events``: optional (start, end) torch events recorded on the
-        step's stream right before and after the decode launch(es).
+        ``decode_events`` / ``copy_events``: optional (start, end) torch events
+        recorded on the step's stream right before and after the decode
+        launch(es) / the copy-on-write launch (both recorded, with nothing
+        between them, in a step without copies).
         """
         seqs = np.asarray(seqs, dtype=np.int64)
         n = seqs.size
@@ -382,8 +384,12 @@ class PagedDecodeEngine:
         # (or none: the kernels read the pinned buffer in place).
         dv = st["t"] if self.host_tables else self._stage.upload(st, n if decode else 0, cur)
         with torch.cuda.stream(cur):
+            if copy_events is not None:
+                copy_events[0].record(cur)
             if npairs:
                 N.pa_copy_blocks(self.pool, dv["pairs"][:npairs], stream=cur)
+            if copy_events is not None:
+                copy_events[1].record(cur)
             fused = decode and self.fuse_write
             if not fused:
                 N.pa_write_kv(self.pool, k_new, v_new, dv["slots"][:n], stream=cur)
