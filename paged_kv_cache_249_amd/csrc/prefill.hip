@@ -126,6 +126,26 @@ __device__ __forceinline__ float col_max(float x) {
 // Pool element types the kernel reads.
 enum : int { kKvF16 = 0, kKvI8 = 1, kKvI4 = 2 };
 
+// LDS layout of a step's K and V rows: rows of D halves, unpadded, with the
+// 16-byte chunks of row r stored at chunk index c ^ swz(r). The swizzle was
+// chosen by measuring the kernel's three access patterns on gfx950 (K operand
+// reads: 16 rows x one chunk per lane group; V reads: one chunk of each of 16
+// rows; staging stores: whole rows): with it, all three run at the LDS's
+// throughput, while rows padded by 16 bytes took 1.7x that for both reads
+// (4 bank-conflict cycles per LDS cycle) and unpadded rows 6.7x for the K
+// reads. D = 64: the K reads are bound the same way, the 8-byte V reads cost
+// the same under every layout tried.
+template <int D>
+__device__ __forceinline__ int lds_swizzle(int row) {
+  if constexpr (D == 128) return (row & 3) * 4 + ((row >> 2) & 3);
+  else return (row & 3) * 2 + ((row >> 2) & 1);
+}
+// Half offset of 16-byte chunk c of row r.
+template <int D>
+__device__ __forceinline__ int lds_at(int row, int c) {
+  return row * D + ((c ^ lds_swizzle<D>(row)) << 3);
+}
+
 template <int D, int BS, bool kTabLds, int kKV>
 __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(PrefillParams p) {
   constexpr bool kI8 = kKV == kKvI8;
@@ -134,7 +154,6 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(PrefillParams p)
   constexpr int kNT = D / 16;      // output tiles; lane column j holds dims kNT*j .. kNT*j + kNT - 1
   constexpr int kKS = D / 32;      // k steps of the QK product
   constexpr int kGD = D / 4;       // dims a lane group covers in the QK product
-  constexpr int kRS = D + 8;       // LDS row stride (halves): 16 bytes of padding per row
   // Staging: a thread moves kPerThr chunks of kChunkVals values of the step's
   // K and V rows (fp16: 16-byte chunks; int8, int4: one chunk of D/8 codes).
   constexpr int kChunkVals = kQuant ? D / 8 : 8;
@@ -152,8 +171,8 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(PrefillParams p)
   // Two steps' K and V rows (32 tokens each), shared by the workgroup's
   // waves: the products read one buffer while the next step is stored into
   // the other.
-  __shared__ __align__(16) _Float16 lk[2][kPfStep * kRS];
-  __shared__ __align__(16) _Float16 lv[2][kPfStep * kRS];
+  __shared__ __align__(16) _Float16 lk[2][kPfStep * D];
+  __shared__ __align__(16) _Float16 lv[2][kPfStep * D];
   // The workgroup's table row (when the launch's contexts fit): entries are
   // then LDS broadcasts, so the only vector loads in flight are K and V rows
   // and waiting for a table entry never drains them.
@@ -314,7 +333,8 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(PrefillParams p)
 #pragma unroll
     for (int j = 0; j < kPerThr; ++j) {
       const int c = tid + j * kPfWaves * 64;
-      const int at = (c / kRowChunks) * kRS + (c % kRowChunks) * kChunkVals;
+      const int srow = c / kRowChunks;
+      const int schunk = (c % kRowChunks) * (kChunkVals / 8);   // first 16-byte chunk it fills
       // Workgroup-uniform outer test: only the last step has such rows.
       const bool zero = t0 + kPfStep > wg_t_end && t0 + c / kRowChunks >= wg_t_end;
       if constexpr (kQuant) {
@@ -347,8 +367,8 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(PrefillParams p)
             kx = uint4{0u, 0u, 0u, 0u};
             vx = uint4{0u, 0u, 0u, 0u};
           }
-          *reinterpret_cast<uint4*>(&lk[buf][at + 8 * i]) = kx;
-          *reinterpret_cast<uint4*>(&lv[buf][at + 8 * i]) = vx;
+          *reinterpret_cast<uint4*>(&lk[buf][lds_at<D>(srow, schunk + i)]) = kx;
+          *reinterpret_cast<uint4*>(&lv[buf][lds_at<D>(srow, schunk + i)]) = vx;
         }
       } else {
         uint4 kx = st.k[j], vx = st.v[j];
@@ -356,8 +376,8 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(PrefillParams p)
           kx = uint4{0u, 0u, 0u, 0u};
           vx = uint4{0u, 0u, 0u, 0u};
         }
-        *reinterpret_cast<uint4*>(&lk[buf][at]) = kx;
-        *reinterpret_cast<uint4*>(&lv[buf][at]) = vx;
+        *reinterpret_cast<uint4*>(&lk[buf][lds_at<D>(srow, schunk)]) = kx;
+        *reinterpret_cast<uint4*>(&lv[buf][lds_at<D>(srow, schunk)]) = vx;
       }
     }
   };
@@ -397,7 +417,7 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(PrefillParams p)
         for (int qt = 0; qt < kPfTiles; ++qt) sc[qt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < kKS; ++kk) {
-          const f16x8 kv = *reinterpret_cast<const f16x8*>(ck + (16 * j + col) * kRS + grp * kGD + 8 * kk);
+          const f16x8 kv = *reinterpret_cast<const f16x8*>(ck + lds_at<D>(16 * j + col, grp * (kGD / 8) + kk));
 #pragma unroll
           for (int qt = 0; qt < kPfTiles; ++qt)
             sc[qt][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kv, qv[qt][kk], sc[qt][j], 0, 0, 0);
@@ -407,7 +427,8 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(PrefillParams p)
       Chunk vv[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        vv[e] = *reinterpret_cast<const Chunk*>(cv + (16 * (e >> 2) + grp * 4 + (e & 3)) * kRS + kNT * col);
+        vv[e] = *reinterpret_cast<const Chunk*>(cv + lds_at<D>(16 * (e >> 2) + grp * 4 + (e & 3), (kNT * col) >> 3) +
+                                                ((kNT * col) & 7));
 
       f16x8 pa[kPfTiles];
 #pragma unroll
