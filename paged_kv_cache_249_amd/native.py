@@ -7,6 +7,11 @@ current stream. All work happens in the library's kernels and host code.
 
 The library is loaded from this package directory. If it is missing, import
 fails with an error telling how to build it: there is no fallback path.
+
+Test hook: with ``PA_HOST_ONLY_LIB`` set to the path of a host-only build of
+the block managers (the sanitizer tests build one with g++), that library is
+loaded instead and only the host-side entry points it exports are bound; the
+device entry points are then absent, and calling one fails.
 """
 
 from __future__ import annotations
@@ -16,7 +21,8 @@ import os
 
 import numpy as np
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedkv.so")
+_HOST_ONLY_LIB = os.environ.get("PA_HOST_ONLY_LIB")
+_LIB_PATH = _HOST_ONLY_LIB or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedkv.so")
 
 PA_OK = 0
 PA_ERR_INVALID_ARG = -1
@@ -115,6 +121,8 @@ _SIGS = {
     "pa_bm_host_free_list": ([_vp, _vp, _i32, _pi32], _i32),
 }
 for _name, (_args, _ret) in _SIGS.items():
+    if _HOST_ONLY_LIB and not hasattr(lib, _name):
+        continue                     # a device entry point: not in the host-only build
     _fn = getattr(lib, _name)
     _fn.argtypes = _args
     _fn.restype = _ret
