@@ -498,7 +498,7 @@ def cpu_baseline(seconds: float) -> dict:
 def main():
     args = parse()
     if args.warmup is None:
-        args.warmup = 30 if args.workload == "prefill" else 10
+        args.warmup = PREFILL_WARMUP if args.workload == "prefill" else 10
     if args.cpu_baseline_only:
         if args.workload == "prefill":
             prefill_cpu_child(args.cpu_seconds)
@@ -874,9 +874,12 @@ def setup_workload(name, args, dev, K, Wm):
     return out
 
 
-def _time_calls(fn, reps=20):
+def _time_calls(fn, reps=20, warmup=1):
+    """Median duration (s) of ``reps`` calls of ``fn``, each bracketed by
+    events on the current stream, after ``warmup`` untimed calls."""
     import torch
-    fn()
+    for _ in range(warmup):
+        fn()
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
     for a, b in ev:
@@ -1054,6 +1057,7 @@ def causal_prefill_flops(ctx, nq, H, D):
 
 
 PREFILL_SHAPE = {"S": 16, "n": 2048, "H": 40, "D": 128, "seed": 7}
+PREFILL_WARMUP = 30                # untimed launches before a prefill case is timed
 PREFILL_SOURCE = os.path.join(ROOT, "paged_kv_cache_249_amd", "csrc", "prefill.hip")
 
 
@@ -1089,9 +1093,12 @@ def prefill_probe(pk, W, torch, np, dev, H=40, D=128):
     pool, tab, ctx, g = prefill_setup(pk, W, torch, np, dev, S, n, H, D, seed)
     res = {"seqs": S, "prompt_tokens": n, "heads": H, "head_dim": D,
            "peak_tflops_fp16": MFMA_PEAK_F16_TFLOPS}
+    # A long matrix-core launch runs slower on a GPU that has just been
+    # light (about 1.25 ms instead of 1.08 for the whole prompts, settling
+    # after some 15 launches), so each case warms up like the prefill line.
     for name, chunk in (("whole_prompt", n), ("last_512", 512)):
         q, out, qs = prefill_chunk(torch, np, dev, g, S, chunk, H, D)
-        t = _time_calls(lambda: pk.pa_prefill(pool, q, out, qs, tab, ctx, chunk, n))
+        t = _time_calls(lambda: pk.pa_prefill(pool, q, out, qs, tab, ctx, chunk, n), warmup=PREFILL_WARMUP)
         fl = causal_prefill_flops([n] * S, [chunk] * S, H, D)
         kv = S * n * H * D * 2 * 2
         res[name] = {"us": round(t * 1e6, 2), "tflops": round(fl / t / 1e12, 1),
@@ -1109,7 +1116,7 @@ def prefill_probe(pk, W, torch, np, dev, H=40, D=128):
         qp.k_scale.fill_(4.0 / qmax)
         qp.v_scale.fill_(4.0 / qmax)
         q, out, qs = prefill_chunk(torch, np, dev, g, S, n, H, D)
-        t = _time_calls(lambda: pk.pa_prefill(qp, q, out, qs, tab, ctx, n, n))
+        t = _time_calls(lambda: pk.pa_prefill(qp, q, out, qs, tab, ctx, n, n), warmup=PREFILL_WARMUP)
         res[f"whole_prompt_{name}_pool"] = {"us": round(t * 1e6, 2), "tflops": round(fl / t / 1e12, 1),
                                            "frac_of_mfma_peak": round(fl / t / 1e12 / MFMA_PEAK_F16_TFLOPS, 4)}
         del q, out, qp
