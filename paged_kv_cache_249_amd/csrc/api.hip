@@ -492,6 +492,9 @@ pa_status pa_prefill_ordered(pa_pool* pool, const void* q, pa_dtype q_dtype, voi
   if (!aligned16(q) || !aligned16(out)) return fail(PA_ERR_INVALID_ARG, "%s: q and out must be 16-byte aligned", fn);
   if (pa::prefill_groups(num_seqs, pool->num_heads, max_query_len) > int64_t(0x7fffffff))
     return fail(PA_ERR_INVALID_ARG, "%s: grid too large", fn);
+  // The kernel indexes pool rows (one token of one head) with 32 bits.
+  if (int64_t(pool->num_blocks) * pool->num_heads * pool->block_size > int64_t(0xffffffff))
+    return fail(PA_ERR_UNSUPPORTED, "%s: pool of more than 2^32 token-head rows", fn);
   pa::PrefillArgs a{};
   a.pool = pool;
   a.q = q;

@@ -168,11 +168,15 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(PrefillParams p)
       typename std::conditional<kI8 && D == 64, uint2, uint4>::type>::type;
   using Chunk = RowChunk<kNT>;
 
-  // Two steps' K and V rows (32 tokens each), shared by the workgroup's
-  // waves: the products read one buffer while the next step is stored into
-  // the other.
-  __shared__ __align__(16) _Float16 lk[2][kPfStep * D];
-  __shared__ __align__(16) _Float16 lv[2][kPfStep * D];
+  // Steps' K and V rows (32 tokens each), shared by the workgroup's waves.
+  // fp16 pools: three buffers of each, filled straight from memory (the
+  // products read one while the next two steps land in the others);
+  // quantised pools: two, filled through registers (the products read one
+  // while the next step is stored into the other). Separate arrays, so that
+  // the compiler can tell a load into one buffer from reads of another.
+  constexpr bool kDirect = !kQuant;
+  __shared__ __align__(16) _Float16 lk0[kPfStep * D], lk1[kPfStep * D], lk2[kDirect ? kPfStep * D : 8];
+  __shared__ __align__(16) _Float16 lv0[kPfStep * D], lv1[kPfStep * D], lv2[kDirect ? kPfStep * D : 8];
   // The workgroup's table row (when the launch's contexts fit): entries are
   // then LDS broadcasts, so the only vector loads in flight are K and V rows
   // and waiting for a table entry never drains them.
@@ -367,8 +371,8 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(PrefillParams p)
             kx = uint4{0u, 0u, 0u, 0u};
             vx = uint4{0u, 0u, 0u, 0u};
           }
-          *reinterpret_cast<uint4*>(&lk[buf][lds_at<D>(srow, schunk + i)]) = kx;
-          *reinterpret_cast<uint4*>(&lv[buf][lds_at<D>(srow, schunk + i)]) = vx;
+          *reinterpret_cast<uint4*>(&(buf ? lk1 : lk0)[lds_at<D>(srow, schunk + i)]) = kx;
+          *reinterpret_cast<uint4*>(&(buf ? lv1 : lv0)[lds_at<D>(srow, schunk + i)]) = vx;
         }
       } else {
         uint4 kx = st.k[j], vx = st.v[j];
@@ -376,8 +380,8 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(PrefillParams p)
           kx = uint4{0u, 0u, 0u, 0u};
           vx = uint4{0u, 0u, 0u, 0u};
         }
-        *reinterpret_cast<uint4*>(&lk[buf][lds_at<D>(srow, schunk)]) = kx;
-        *reinterpret_cast<uint4*>(&lv[buf][lds_at<D>(srow, schunk)]) = vx;
+        *reinterpret_cast<uint4*>(&(buf ? lk1 : lk0)[lds_at<D>(srow, schunk)]) = kx;
+        *reinterpret_cast<uint4*>(&(buf ? lv1 : lv0)[lds_at<D>(srow, schunk)]) = vx;
       }
     }
   };
@@ -488,40 +492,131 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(PrefillParams p)
     }
   };
 
-  // Two register stages: while a step is computed, the next one's rows wait
-  // in registers for the other LDS buffer and the one after is in flight
-  // from memory (a first touch from HBM can outlast one step's products).
-  // Table entries are read one step further ahead still.
-  Stage sA, sB;
-  {
-    int blk[2];
-    fetch_table(0, blk);
-    load_step(0, blk, sA);
-    fetch_table(kPfStep, blk);
-    load_step(kPfStep, blk, sB);
-    fetch_table(2 * kPfStep, tab);
-    store_step(0, 0, sA);
-  }
-  __syncthreads();
-  // nx: the next step's rows (stored after the products); fr: free, it
-  // receives the step after it.
-  auto step = [&](int t0, int buf, Stage& nx, Stage& fr) {
-    int nt[2];
-    fetch_table(t0 + 3 * kPfStep, nt);
-    load_step(t0 + 2 * kPfStep, tab, fr);
-    tab[0] = nt[0];
-    tab[1] = nt[1];
-    compute(t0, lk[buf], lv[buf]);
-    // The other buffer: every wave left it before the last barrier.
-    if (t0 + kPfStep < wg_t_end) store_step(buf ^ 1, t0 + kPfStep, nx);
-    __syncthreads();                 // next step's rows stored; this step's reads done
-  };
-  for (int t0 = 0; t0 < wg_t_end;) {
-    step(t0, 0, sB, sA);
-    t0 += kPfStep;
-    if (t0 >= wg_t_end) break;
-    step(t0, 1, sA, sB);
-    t0 += kPfStep;
+  if constexpr (kDirect) {
+    // fp16: each step's rows go from the pool straight into LDS
+    // (buffer_load_dwordx4 ... lds): a wave instruction fills 1 KB of LDS,
+    // lane L the 16 bytes at 16 L, i.e. kRpi whole rows; each lane loads the
+    // logical chunk that belongs at its LDS position under the swizzle. Rows
+    // at or past the workgroup's last token (and rows of a bad table entry)
+    // take an offset past the buffer resource, which covers one 16-row slice
+    // of a (block, head) tile, and land as zeros. Loads run two steps ahead:
+    // when step t is computed, steps t+1 and t+2 are on their way, and the
+    // wait before each barrier leaves exactly the newest step's loads in
+    // flight (loads complete in order). No register holds staged rows.
+    constexpr int kLaneChunks = D / 8;                  // 16-byte chunks per row
+    constexpr int kRpi = 64 / kLaneChunks;              // rows per wave instruction
+    constexpr int kIpw = kPfStep / kRpi / kPfWaves;     // instructions per wave, step and tensor
+    static_assert(kIpw * kRpi * kPfWaves == kPfStep && 16 % kRpi == 0, "step rows must split into waves");
+    constexpr int kSliceBytes = 16 * D * 2;             // one 16-row slice of a (block, head) tile
+    constexpr int kRsrcWord3 = 0x00020000;
+    // s_waitcnt: vmcnt <= 2 kIpw (the newest step's K and V loads), lgkmcnt
+    // 0 (this wave's LDS reads of the step done), expcnt unconstrained.
+    constexpr int kStepWait = (2 * kIpw) | (7 << 4);
+    const int drow = lane / kLaneChunks;                // row within a wave instruction
+    const int dchunk = lane % kLaneChunks;              // physical chunk this lane fills
+    // The buffer resource and the LDS address of an instruction are wave
+    // uniform (scalar registers); the wave index and the table entries (read
+    // from LDS, the same address in every lane) are declared so.
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    auto issue = [&](int t0, const int (&blk)[2], _Float16* dk, _Float16* dv) {
+#pragma unroll
+      for (int i = 0; i < kIpw; ++i) {
+        const int g = wv * kIpw + i;                    // rows g kRpi .. of the step
+        const int r = g * kRpi + drow;
+        const int half = (g * kRpi) >> 4;
+        int b = __builtin_amdgcn_readfirstlane(blk[half]);   // one entry for the whole instruction
+        bool ok = t0 + r < wg_t_end;
+        if (unsigned(b) >= unsigned(p.num_blocks)) {    // only possible when entries are read as we go
+          if (ok) flag_error(p.err, PA_DEV_BAD_TABLE_ENTRY);
+          b = 0;
+          ok = false;
+        }
+        // Row index of the slice: below 2^32 for any pool that fits in HBM
+        // (a row is at least 128 bytes). Read back as a scalar so that the
+        // resource is built in scalar registers.
+        const uint64_t slice = __builtin_amdgcn_readfirstlane(
+            (uint32_t(b) * uint32_t(p.num_heads) + uint32_t(h)) * uint32_t(BS) + uint32_t((t0 + 16 * half) % BS));
+        const int voff = ok ? (r & 15) * D * 2 + ((dchunk ^ lds_swizzle<D>(r)) << 4) : kSliceBytes;
+        const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<_Float16*>(static_cast<const _Float16*>(p.k)) + slice * D, 0, kSliceBytes, kRsrcWord3);
+        const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<_Float16*>(static_cast<const _Float16*>(p.v)) + slice * D, 0, kSliceBytes, kRsrcWord3);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(dk + g * kRpi * D), 16,
+                                                 voff, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(dv + g * kRpi * D), 16,
+                                                 voff, 0, 0, 0);
+      }
+    };
+    {
+      int blk[2];
+      fetch_table(0, blk);
+      issue(0, blk, lk0, lv0);
+      fetch_table(kPfStep, blk);
+      issue(kPfStep, blk, lk1, lv1);
+      fetch_table(2 * kPfStep, tab);
+    }
+    __builtin_amdgcn_s_waitcnt(kStepWait);
+    __builtin_amdgcn_s_barrier();
+    // Step at t0 from buffer (ck, cv); the step two ahead into (nk, nv), which
+    // every wave left before the last barrier.
+    auto dstep = [&](int t0, const _Float16* ck, const _Float16* cv, _Float16* nk, _Float16* nv) {
+      int nt[2];
+      fetch_table(t0 + 3 * kPfStep, nt);
+      issue(t0 + 2 * kPfStep, tab, nk, nv);
+      tab[0] = nt[0];
+      tab[1] = nt[1];
+      compute(t0, ck, cv);
+      __builtin_amdgcn_s_waitcnt(kStepWait);          // next step landed; this step's reads done
+      __builtin_amdgcn_s_barrier();
+    };
+    for (int t0 = 0; t0 < wg_t_end;) {
+      dstep(t0, lk0, lv0, lk2, lv2);
+      t0 += kPfStep;
+      if (t0 >= wg_t_end) break;
+      dstep(t0, lk1, lv1, lk0, lv0);
+      t0 += kPfStep;
+      if (t0 >= wg_t_end) break;
+      dstep(t0, lk2, lv2, lk1, lv1);
+      t0 += kPfStep;
+    }
+    // No load into LDS may still be in flight when the workgroup ends.
+    __builtin_amdgcn_s_waitcnt(0);
+  } else {
+    // Two register stages: while a step is computed, the next one's rows wait
+    // in registers for the other LDS buffer and the one after is in flight
+    // from memory (a first touch from HBM can outlast one step's products).
+    // Table entries are read one step further ahead still.
+    Stage sA, sB;
+    {
+      int blk[2];
+      fetch_table(0, blk);
+      load_step(0, blk, sA);
+      fetch_table(kPfStep, blk);
+      load_step(kPfStep, blk, sB);
+      fetch_table(2 * kPfStep, tab);
+      store_step(0, 0, sA);
+    }
+    __syncthreads();
+    // nx: the next step's rows (stored after the products); fr: free, it
+    // receives the step after it.
+    auto step = [&](int t0, int buf, Stage& nx, Stage& fr) {
+      int nt[2];
+      fetch_table(t0 + 3 * kPfStep, nt);
+      load_step(t0 + 2 * kPfStep, tab, fr);
+      tab[0] = nt[0];
+      tab[1] = nt[1];
+      compute(t0, buf ? lk1 : lk0, buf ? lv1 : lv0);
+      // The other buffer: every wave left it before the last barrier.
+      if (t0 + kPfStep < wg_t_end) store_step(buf ^ 1, t0 + kPfStep, nx);
+      __syncthreads();                 // next step's rows stored; this step's reads done
+    };
+    for (int t0 = 0; t0 < wg_t_end;) {
+      step(t0, 0, sB, sA);
+      t0 += kPfStep;
+      if (t0 >= wg_t_end) break;
+      step(t0, 1, sA, sB);
+      t0 += kPfStep;
+    }
   }
   if (!active) return;
 
