@@ -21,8 +21,10 @@
 //   O[q][d] += P[q][t] V[t][d]       one 16x16x32 product per 16 output columns
 // S^T's accumulator layout (lane = query column, 4 tokens per lane and lane
 // group) is exactly the A-operand layout P needs for the second product, so P
-// never leaves the registers. A lane's 16-byte V row chunk feeds eight output
-// tiles: output column j of tile c is dimension (head_dim/16)*j + c.
+// never leaves the registers. V reaches the second product through gfx950's
+// transposing LDS reads (ds_read_b64_tr_b16), which hand each lane one
+// dimension of four consecutive rows: output column j of tile c is dimension
+// 16c + j.
 #include <hip/hip_runtime.h>
 
 #include "device_common.h"
@@ -34,6 +36,9 @@ namespace {
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int kPfWaves = 4;          // waves per workgroup
 constexpr int kPfTiles = 2;          // 16-row query tiles per wave
@@ -66,21 +71,6 @@ struct PrefillParams {
   float scale_log2;              // sm_scale * log2(e)
   int32_t* err;
 };
-
-// Element c of a row chunk of kNT halves (kNT = 8: uint4, kNT = 4: uint2).
-template <int kNT>
-using RowChunk = typename std::conditional<kNT == 8, uint4, uint2>::type;
-
-template <int kNT>
-__device__ __forceinline__ _Float16 half_at(const RowChunk<kNT>& v, int c) {
-  uint32_t w;
-  if constexpr (kNT == 8) {
-    w = c < 2 ? v.x : c < 4 ? v.y : c < 6 ? v.z : v.w;
-  } else {
-    w = c < 2 ? v.x : v.y;
-  }
-  return __builtin_bit_cast(_Float16, uint16_t((c & 1) ? (w >> 16) : (w & 0xffffu)));
-}
 
 // Four int8 codes (one 32-bit word) times an fp16 scale, as four fp16
 // values (two words). Each code c becomes the half 1024 + (c + 128) by
@@ -166,7 +156,6 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(PrefillParams p)
   using Raw = typename std::conditional<
       kI4, typename std::conditional<D == 64, uint32_t, uint2>::type,
       typename std::conditional<kI8 && D == 64, uint2, uint4>::type>::type;
-  using Chunk = RowChunk<kNT>;
 
   // Steps' K and V rows (32 tokens each), shared by the workgroup's waves.
   // fp16 pools: three buffers of each, filled straight from memory (the
@@ -428,11 +417,23 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(PrefillParams p)
         }
       }
       // V rows t = 16*(e/4) + 4*grp + e%4, this lane's kNT dims.
-      Chunk vv[8];
+      // V as the B operand of the second product: column col of output tile c
+      // is dim 16c + col, k = this lane's 8 tokens t = 16*(e/4) + 4*grp + e%4
+      // (the order of P's A operand). Transposing LDS reads deliver it: in each
+      // 16-lane group, lane s fetches dims 16c + 4(s%4) .. +3 of row
+      // 16j + 4*grp + s/4 and receives dim 16c + s of the group's four rows.
+      f16x8 vb[kNT];
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        vv[e] = *reinterpret_cast<const Chunk*>(cv + lds_at<D>(16 * (e >> 2) + grp * 4 + (e & 3), (kNT * col) >> 3) +
-                                                ((kNT * col) & 7));
+      for (int c = 0; c < kNT; ++c) {
+        f16x4 t[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int dim = 16 * c + 4 * (col & 3);
+          t[j] = __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(
+                                               cv + lds_at<D>(16 * j + 4 * grp + (col >> 2), dim >> 3) + (dim & 7))));
+        }
+        vb[c] = __builtin_shufflevector(t[0], t[1], 0, 1, 2, 3, 4, 5, 6, 7);
+      }
 
       f16x8 pa[kPfTiles];
 #pragma unroll
@@ -478,16 +479,12 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(PrefillParams p)
           pa[qt][e] = _Float16(__builtin_amdgcn_exp2f(__builtin_fmaf(x[e], c2, -m[qt])));
         osum[qt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[qt], ones, osum[qt], 0, 0, 0);
       }
-      // P (A operand: row = this lane's query column, k = the lane's 8 tokens)
-      // times V (B operand: column j of tile c = dim kNT*j + c, the same 8 tokens).
+      // P (A operand: row = this lane's query column, k = the lane's 8 tokens) times V.
 #pragma unroll
       for (int c = 0; c < kNT; ++c) {
-        f16x8 vb;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) vb[e] = half_at<kNT>(vv[e], c);
 #pragma unroll
         for (int qt = 0; qt < kPfTiles; ++qt)
-          o[qt][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[qt], vb, o[qt][c], 0, 0, 0);
+          o[qt][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[qt], vb[c], o[qt][c], 0, 0, 0);
       }
     }
   };
@@ -628,17 +625,9 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(PrefillParams p)
       const float ir = 1.f / osum[qt][r];
       const int row = r0 + 16 * qt + grp * 4 + r;
       if (row < n) {
-        uint32_t w[kNT / 2];
+        _Float16* orow = p.out + (int64_t(qa + row) * p.num_heads + h) * D + col;
 #pragma unroll
-        for (int c = 0; c < kNT; c += 2) {
-          const uint32_t lo = __builtin_bit_cast(uint16_t, _Float16(o[qt][c][r] * ir));
-          const uint32_t hi = __builtin_bit_cast(uint16_t, _Float16(o[qt][c + 1][r] * ir));
-          w[c / 2] = lo | (hi << 16);
-        }
-        Chunk out;
-        if constexpr (kNT == 8) out = Chunk{w[0], w[1], w[2], w[3]};
-        else out = Chunk{w[0], w[1]};
-        *reinterpret_cast<Chunk*>(p.out + (int64_t(qa + row) * p.num_heads + h) * D + kNT * col) = out;
+        for (int c = 0; c < kNT; ++c) orow[16 * c] = _Float16(o[qt][c][r] * ir);
       }
     }
   }
