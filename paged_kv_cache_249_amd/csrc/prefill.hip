@@ -416,7 +416,6 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(PrefillParams p)
             sc[qt][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kv, qv[qt][kk], sc[qt][j], 0, 0, 0);
         }
       }
-      // V rows t = 16*(e/4) + 4*grp + e%4, this lane's kNT dims.
       // V as the B operand of the second product: column col of output tile c
       // is dim 16c + col, k = this lane's 8 tokens t = 16*(e/4) + 4*grp + e%4
       // (the order of P's A operand). Transposing LDS reads deliver it: in each
@@ -435,31 +434,46 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(PrefillParams p)
         vb[c] = __builtin_shufflevector(t[0], t[1], 0, 1, 2, 3, 4, 5, 6, 7);
       }
 
-      f16x8 pa[kPfTiles];
+      // Softmax of both query tiles. The tests below are taken once per step
+      // for both tiles, so the common path (no mask, no move of the
+      // reference max) is one straight run of code in which the weights of
+      // one tile are computed while the other's products are in flight.
+      float x[kPfTiles][8];
 #pragma unroll
-      for (int qt = 0; qt < kPfTiles; ++qt) {
-        float x[8];
+      for (int qt = 0; qt < kPfTiles; ++qt)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = sc[qt][e >> 2][e & 3];
-        // Only steps reaching past the tile's first position need the causal
-        // mask (it also hides the zero rows past the workgroup's last token).
-        if (t0 + kPfStep - 1 > base_pos + r0 + 16 * qt) {
+        for (int e = 0; e < 8; ++e) x[qt][e] = sc[qt][e >> 2][e & 3];
+      // Only steps reaching past the wave's first position need the causal
+      // mask (it also hides the zero rows past the workgroup's last token).
+      if (t0 + kPfStep - 1 > base_pos + r0) {
+#pragma unroll
+        for (int qt = 0; qt < kPfTiles; ++qt)
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const int t = t0 + 16 * (e >> 2) + grp * 4 + (e & 3);
-            if (t > my_pos[qt]) x[e] = -INFINITY;
+            if (t > my_pos[qt]) x[qt][e] = -INFINITY;
           }
-        }
-        float mx = x[0];
+      }
+      float mx[kPfTiles];
+      bool up = false;
 #pragma unroll
-        for (int e = 1; e < 8; ++e) mx = fmaxf(mx, x[e]);
-        // A logit of the column past m + kLazy shows in this lane's own
-        // maximum already (thr = (m + kLazy) / c2, c2 > 0): the column-wide
-        // maximum is needed only to move m. Token 0 is visible to every query
-        // in the first step, so every m is finite after it and the first step
-        // always rescales (from m = -inf, thr = -inf).
-        if (__any(mx > thr[qt])) {
-          const float m_new = fmaxf(m[qt], col_max(mx) * c2);
+      for (int qt = 0; qt < kPfTiles; ++qt) {
+        mx[qt] = x[qt][0];
+#pragma unroll
+        for (int e = 1; e < 8; ++e) mx[qt] = fmaxf(mx[qt], x[qt][e]);
+        up = up || mx[qt] > thr[qt];
+      }
+      // A logit of a column past m + kLazy shows in this lane's own maximum
+      // already (thr = (m + kLazy) / c2, c2 > 0): the column-wide maximum is
+      // needed only to move m. Moving m when no logit passed the threshold
+      // is harmless (any reference gives the same quotient o / osum, and
+      // weights stay at most 2^kLazy). Token 0 is visible to every query in
+      // the first step, so every m is finite after it and the first step
+      // always moves it (from m = -inf, thr = -inf).
+      if (__any(up)) {
+#pragma unroll
+        for (int qt = 0; qt < kPfTiles; ++qt) {
+          const float m_new = fmaxf(m[qt], col_max(mx[qt]) * c2);
           const float alpha = __builtin_amdgcn_exp2f(m[qt] - m_new);
           m[qt] = m_new;
           thr[qt] = (m_new + kLazy) / c2;
@@ -474,18 +488,34 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(PrefillParams p)
             for (int c = 0; c < kNT; ++c) o[qt][c][r] *= ar[r];
           }
         }
+      }
+      f16x8 pa[kPfTiles];
+#pragma unroll
+      for (int qt = 0; qt < kPfTiles; ++qt) {
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          pa[qt][e] = _Float16(__builtin_amdgcn_exp2f(__builtin_fmaf(x[e], c2, -m[qt])));
+          pa[qt][e] = _Float16(__builtin_amdgcn_exp2f(__builtin_fmaf(x[qt][e], c2, -m[qt])));
         osum[qt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[qt], ones, osum[qt], 0, 0, 0);
       }
       // P (A operand: row = this lane's query column, k = the lane's 8 tokens) times V.
 #pragma unroll
-      for (int c = 0; c < kNT; ++c) {
+      for (int qt = 0; qt < kPfTiles; ++qt) {
 #pragma unroll
-        for (int qt = 0; qt < kPfTiles; ++qt)
+        for (int c = 0; c < kNT; ++c)
           o[qt][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[qt], vb[c], o[qt][c], 0, 0, 0);
       }
+      // Issue order of this run of code: the first tile's weights (VALU),
+      // then its matrix products one at a time, each followed by two VALU
+      // instructions of the second tile's weights, then the second tile's
+      // products. The matrix cores work while the second tile's exponentials
+      // are computed. (Masks: 0x2 VALU, 0x8 MFMA.)
+      __builtin_amdgcn_sched_group_barrier(0x002, 14, 0);
+#pragma unroll
+      for (int i = 0; i < 9; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 9, 0);
     }
   };
 
