@@ -14,8 +14,9 @@
 // fp32 accumulation). A workgroup of 4 waves owns 128 query rows of one
 // (sequence, head); a wave holds two 16-row query tiles. The context is
 // walked 32 tokens per step; the workgroup stages each step's K and V rows in
-// LDS (double-buffered: the next step's global loads are in flight during
-// the products, one barrier per step). Per step and query tile:
+// LDS (fp16 pools straight from memory into three buffers, two steps ahead;
+// int8 and int4 pools through registers, where codes become fp16), one
+// barrier per step. Per step and query tile:
 //   S^T[t][q] = K[t] . Q[q]          two 16x16 tiles, k = head_dim in steps of 32
 //   online softmax per query column  (exp2 domain, fp32, lazy reference max)
 //   O[q][d] += P[q][t] V[t][d]       one 16x16x32 product per 16 output columns
