@@ -49,6 +49,7 @@ constexpr int kPfStep = 32;          // tokens per step: the k extent of one 16x
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazy = 8.f;        // log2 headroom before the reference max moves
 constexpr int kTabCap = 2048;       // table entries a workgroup can keep in LDS
+constexpr int kPfWindow = 4;        // groups whose row tiles an XCD interleaves
 
 struct PrefillParams {
   const _Float16* q;             // [num_rows][H][D]
@@ -181,17 +182,25 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(PrefillParams p)
   // Workgroup -> (sequence, head, row tile). Workgroups are dealt to the 8
   // XCDs round robin (block b runs on XCD b % 8, as its (b / 8)-th). Groups
   // (the row tiles of one (sequence, head)) are dealt round robin over the
-  // XCDs in dispatch order, each group's tiles consecutive on one XCD so they
-  // share its L2: XCD x takes groups x, x + 8, ... — every XCD gets its share
-  // of long and short sequences whatever the order. The heaviest row tile
-  // (the last rows attend to the most tokens) goes first.
+  // XCDs in dispatch order, all tiles of a group on one XCD so they share its
+  // L2: XCD x takes groups x, x + 8, ... — every XCD gets its share of long
+  // and short sequences whatever the order. Heavier row tiles (the last rows
+  // attend to the most tokens) go first.
   const int T = p.row_tiles;
   const int groups = int(gridDim.x) / T;
   int g, k;
   if ((groups & 7) == 0) {
+    // Within an XCD, windows of kPfWindow groups (about what its CUs hold
+    // at once, so their K/V share the L2 as before): a window's tiles go
+    // heaviest first across its groups, so the last tiles dealt are light
+    // ones and the XCD's CUs run out of work together.
     const int x = int(blockIdx.x) & 7, j = int(blockIdx.x) >> 3;
-    g = x + 8 * (j / T);
-    k = j % T;
+    const int per_xcd = groups >> 3;
+    const int win = j / (kPfWindow * T);
+    const int wg = min(kPfWindow, per_xcd - win * kPfWindow);   // groups in this window
+    const int r = j - win * kPfWindow * T;
+    g = x + 8 * (win * kPfWindow + r % wg);
+    k = r / wg;
   } else {
     g = int(blockIdx.x) / T;
     k = int(blockIdx.x) % T;
