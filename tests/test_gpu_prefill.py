@@ -115,6 +115,20 @@ def test_prefill_matches_the_oracle(D, bs):
     assert_close(got, b.oracle(), f"D={D} bs={bs}")
 
 
+def test_dispatch_windows_cover_every_tile():
+    # 6 sequences x 8 heads = 48 (sequence, head) groups: 6 per XCD, dealt
+    # as a window of 4 groups and a partial one of 2, each with up to 4 row
+    # tiles of 128 rows (whole prompts of 129..500 tokens, one chunk of 7).
+    pk = _pk()
+    ctx = [500, 129, 260, 384, 77, 450]
+    nq = [500, 129, 260, 7, 77, 450]
+    b = Chunks(ctx, nq, H=8, D=64, seed=83)
+    print("prefill windows 6x8", flush=True)
+    got = b.gpu()
+    assert pk.pa_check_errors(b.pool) == 0
+    assert_close(got, b.oracle(), "6 x 8 groups")
+
+
 def test_prefill_after_gpu_write_of_the_chunk():
     # The chunk's own K and V go through pa_write_kv first, as a prefill step does.
     b = Chunks([200, 77, 16], [120, 77, 5], H=4, D=128, seed=5, write_chunk_on_gpu=True)
