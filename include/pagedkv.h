@@ -309,7 +309,9 @@ pa_status pa_decode_ordered(pa_pool* pool, const void* q, pa_dtype q_dtype, void
  * leave that sequence's rows unwritten; a table entry outside the pool flags
  * PA_DEV_BAD_TABLE_ENTRY and block 0 is read in its place.
  * Errors: PA_ERR_INVALID_ARG (null pointers, misalignment, bad sizes),
- * PA_ERR_UNSUPPORTED (fp32 pool, non-fp16 q), PA_ERR_HIP. */
+ * PA_ERR_UNSUPPORTED (fp32 pool, non-fp16 q, a pool of more than 2^32
+ * token-head rows, num_blocks * num_heads * block_size: the kernel indexes
+ * rows with 32 bits), PA_ERR_HIP. */
 pa_status pa_prefill(pa_pool* pool, const void* q, pa_dtype q_dtype, void* out,
                      const int32_t* query_start, int32_t num_rows, const int32_t* block_tables,
                      int32_t max_blocks, const int32_t* context_lens, int32_t num_seqs,

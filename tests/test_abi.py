@@ -171,3 +171,21 @@ def test_device_calls_validate_before_launching():
         assert L.pa_stream_copy(p(0x1000), p(0x2000), 24, None) == pk.PA_ERR_INVALID_ARG
     finally:
         L.pa_free_pool(h)
+
+
+def test_prefill_refuses_pools_past_32_bit_rows():
+    # pa_prefill indexes pool rows (one token of one head) with 32 bits: a
+    # descriptor of 2^20 blocks x 64 heads x 64 tokens (2^32 rows, caller
+    # pointers never touched) is refused before any launch.
+    import paged_kv_cache_249_amd as pk
+    L = pk.lib
+    p = C.c_void_p
+    h = C.c_void_p()
+    assert L.pa_alloc_pool(1 << 20, 64, 64, 64, pk.PA_F16, p(0x10000000), p(0x20000000), None, None,
+                           C.byref(h)) == 0
+    try:
+        assert L.pa_prefill(h, p(0x4000), pk.PA_F16, p(0x5000), p(0x6000), 1, p(0x7000), 1, p(0x8000), 1, 1, 1,
+                            0.0, None) == pk.PA_ERR_UNSUPPORTED
+        assert b"2^32" in L.pa_last_error()
+    finally:
+        L.pa_free_pool(h)
