@@ -173,11 +173,14 @@ def test_table_rows_longer_than_the_kernel_keeps_in_lds():
     # more than a workgroup keeps in LDS (2048), so the kernel reads the
     # table from memory as it walks; 64-token blocks (516 entries) keep it in
     # LDS. Both against the oracle, with a ragged chunk and a short sequence.
-    for bs in (16, 64):
-        b = Chunks([33000, 100], [70, 100], H=2, D=64, bs=bs, seed=23)
+    # 66000 tokens in 32-token blocks (2063 entries) at head_dim 128: the
+    # table read from memory with two 16-row slices per block.
+    for ctx0, bs, D in ((33000, 16, 64), (33000, 64, 64), (66000, 32, 128)):
+        b = Chunks([ctx0, 100], [70, 100], H=2, D=D, bs=bs, seed=23)
+        print(f"prefill long table ctx={ctx0} bs={bs} D={D}", flush=True)
         got = b.gpu()
         assert _pk().pa_check_errors(b.pool) == 0
-        assert_close(got, b.oracle(), f"bs={bs}")
+        assert_close(got, b.oracle(), f"ctx={ctx0} bs={bs} D={D}")
 
 
 @pytest.mark.parametrize("ctx", [300, 33000])
