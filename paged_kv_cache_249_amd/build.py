@@ -44,7 +44,14 @@ CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", f"-I{INCLUDE}", f"-I{CSRC}"]
 # VGPRs, so the softmax rescale of the output tiles needs no AGPR moves; no
 # NaN reaches its arithmetic (rows past a context are zeroed before the
 # products, masked logits are -inf), so maxima skip NaN canonicalisation.
-EXTRA_FLAGS = {"prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true", "-fno-honor-nans", "-mno-amdgpu-ieee"]}
+# Both attention kernels use the machine scheduler's max-ILP strategy (it
+# orders instructions only; results are bit-identical): measured +0.4-3.5%
+# on prefill and +0.6-1.1% on the OPT-13B decode against the default.
+_MAX_ILP = ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]
+EXTRA_FLAGS = {
+    "prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true", "-fno-honor-nans", "-mno-amdgpu-ieee", *_MAX_ILP],
+    "decode.hip": _MAX_ILP,
+}
 
 
 def _run(cmd):
