@@ -46,11 +46,14 @@ CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", f"-I{INCLUDE}", f"-I{CSRC}"]
 # products, masked logits are -inf), so maxima skip NaN canonicalisation.
 # Both attention kernels use the machine scheduler's max-ILP strategy (it
 # orders instructions only; results are bit-identical): measured +0.4-3.5%
-# on prefill and +0.6-1.1% on the OPT-13B decode against the default.
+# on prefill and +0.6-1.9% on the OPT-13B decode against the default. The
+# decode kernel also lets the compiler raise a wave's priority while it
+# issues loads (s_setprio; +0.7% on the OPT-13B step over six paired runs,
+# nothing on prefill).
 _MAX_ILP = ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]
 EXTRA_FLAGS = {
     "prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true", "-fno-honor-nans", "-mno-amdgpu-ieee", *_MAX_ILP],
-    "decode.hip": _MAX_ILP,
+    "decode.hip": [*_MAX_ILP, "-mllvm", "-amdgpu-set-wave-priority"],
 }
 
 
