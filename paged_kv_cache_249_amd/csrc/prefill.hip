@@ -54,9 +54,9 @@ constexpr int kPfWindow = 4;        // groups whose row tiles an XCD interleaves
 struct PrefillParams {
   const _Float16* q;             // [num_rows][H][D]
   _Float16* out;                 // [num_rows][H][D]
-  const void* k;                 // pool [num_blocks][H][B][D]: fp16, or int8 codes
+  const void* k;                 // pool [num_blocks][H][B][D]: fp16, int8 codes, or int4 code pairs
   const void* v;
-  const _Float16* k_scale;       // int8 pools: fp16 [num_blocks][H]
+  const _Float16* k_scale;       // int8 and int4 pools: fp16 [num_blocks][H]
   const _Float16* v_scale;
   const int32_t* query_start;    // [S + 1]
   const int32_t* tables;         // [S][max_blocks]
@@ -143,22 +143,9 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(PrefillParams p)
   constexpr bool kI8 = kKV == kKvI8;
   constexpr bool kI4 = kKV == kKvI4;
   constexpr bool kQuant = kI8 || kI4;
-  constexpr int kNT = D / 16;      // output tiles; lane column j holds dims kNT*j .. kNT*j + kNT - 1
+  constexpr int kNT = D / 16;      // output tiles; column j of tile c is dim 16c + j
   constexpr int kKS = D / 32;      // k steps of the QK product
   constexpr int kGD = D / 4;       // dims a lane group covers in the QK product
-  // Staging: a thread moves kPerThr chunks of kChunkVals values of the step's
-  // K and V rows (fp16: 16-byte chunks; int8, int4: one chunk of D/8 codes).
-  constexpr int kChunkVals = kQuant ? D / 8 : 8;
-  constexpr int kRowChunks = D / kChunkVals;           // chunks per K or V row
-  constexpr int kPerThr = kPfStep * kRowChunks / (kPfWaves * 64);
-  static_assert(kPerThr * kPfWaves * 64 == kPfStep * kRowChunks, "step tile must split evenly");
-  static_assert(!kQuant || kPerThr == 1, "int8 and int4 staging move one chunk per thread");
-  // Raw staging registers per chunk: fp16 16 bytes; int8 16 (D 128) or 8
-  // bytes; int4 8 (D 128) or 4 bytes.
-  using Raw = typename std::conditional<
-      kI4, typename std::conditional<D == 64, uint32_t, uint2>::type,
-      typename std::conditional<kI8 && D == 64, uint2, uint4>::type>::type;
-
   // Steps' K and V rows (32 tokens each), shared by the workgroup's waves.
   // fp16 pools: three buffers of each, filled straight from memory (the
   // products read one while the next two steps land in the others);
@@ -259,11 +246,9 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(PrefillParams p)
   const int64_t head_off = int64_t(h) * BS * D;
   const int64_t block_elems = int64_t(p.num_heads) * BS * D;
 
-  // Staging: thread tid moves 16-byte chunks tid + 256 j of the step's K and
-  // V rows (row c / kRowChunks, chunk c % kRowChunks). A 16-row half of a
-  // step lies in one block (B is 16, 32 or 64 and steps start at multiples
-  // of 32), so its table entry is one value for the workgroup. No table
-  // entry at or past the workgroup's last token is read.
+  // A 16-row half of a step lies in one block (B is 16, 32 or 64 and steps
+  // start at multiples of 32), so its table entry is one value for the
+  // workgroup. No table entry at or past the workgroup's last token is read.
   int tab[2] = {0, 0};               // table entries of the two halves of the next step to load
   if constexpr (kTabLds) {
     // Entries are checked here, once: a bad one is flagged and read as block
@@ -288,103 +273,6 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(PrefillParams p)
       else dst[half] = t < wg_t_end ? trow[t / BS] : 0;
     }
   };
-  // Raw rows of one step as one thread holds them (and, for int8, the
-  // scales of the blocks its chunk came from).
-  struct Stage {
-    Raw k[kPerThr], v[kPerThr];
-    f16x2 ks, vs;
-  };
-  // Every call issues the same loads whatever the step (rows past the
-  // workgroup's last token, or a whole step past it, read the pool's first
-  // row instead), so the loads in flight are counted the same on every path
-  // and waiting for one stage never drains the next.
-  auto load_step = [&](int t0, const int (&blk)[2], Stage& st) {
-#pragma unroll
-    for (int j = 0; j < kPerThr; ++j) {
-      const int c = tid + j * kPfWaves * 64;
-      const int row = c / kRowChunks;
-      const int tt = t0 + row;
-      const int b = blk[row >> 4];
-      bool ok = tt < wg_t_end;
-      if constexpr (!kTabLds) {
-        if (ok && unsigned(b) >= unsigned(p.num_blocks)) {
-          flag_error(p.err, PA_DEV_BAD_TABLE_ENTRY);
-          ok = false;
-        }
-      }
-      const int64_t off =   // in elements (halves or codes)
-          ok ? int64_t(b) * block_elems + head_off + int64_t(tt % BS) * D + (c % kRowChunks) * kChunkVals
-             : int64_t(0);
-      if constexpr (kQuant) {
-        const int64_t byte = kI4 ? off / 2 : off;      // int4: two codes per byte
-        st.k[j] = *reinterpret_cast<const Raw*>(static_cast<const uint8_t*>(p.k) + byte);
-        st.v[j] = *reinterpret_cast<const Raw*>(static_cast<const uint8_t*>(p.v) + byte);
-        const int64_t si = ok ? int64_t(b) * p.num_heads + h : int64_t(0);
-        const _Float16 ks = p.k_scale[si], vs = p.v_scale[si];
-        st.ks = f16x2{ks, ks};
-        st.vs = f16x2{vs, vs};
-      } else {
-        st.k[j] = *reinterpret_cast<const Raw*>(static_cast<const _Float16*>(p.k) + off);
-        st.v[j] = *reinterpret_cast<const Raw*>(static_cast<const _Float16*>(p.v) + off);
-      }
-    }
-  };
-  // Rows at or past the workgroup's last token are stored as zeros: no
-  // unused slot of a last block (or other row read in its place) reaches the
-  // products. int8 codes are scaled into fp16 on the way.
-  auto store_step = [&](int buf, int t0, const Stage& st) {
-#pragma unroll
-    for (int j = 0; j < kPerThr; ++j) {
-      const int c = tid + j * kPfWaves * 64;
-      const int srow = c / kRowChunks;
-      const int schunk = (c % kRowChunks) * (kChunkVals / 8);   // first 16-byte chunk it fills
-      // Workgroup-uniform outer test: only the last step has such rows.
-      const bool zero = t0 + kPfStep > wg_t_end && t0 + c / kRowChunks >= wg_t_end;
-      if constexpr (kQuant) {
-        constexpr int kW = int(sizeof(Raw)) / 4;      // code words per chunk
-        constexpr int kOut = kI4 ? 4 * kW : 2 * kW;    // fp16 pair words they become
-        uint32_t kw[kOut], vw[kOut];
-        const uint32_t* kr = reinterpret_cast<const uint32_t*>(&st.k[j]);
-        const uint32_t* vr = reinterpret_cast<const uint32_t*>(&st.v[j]);
-#pragma unroll
-        for (int i = 0; i < kW; ++i) {
-          if constexpr (kI4) {
-            uint32_t a[4], b[4];
-            dequant8_i4(kr[i], st.ks, a);
-            dequant8_i4(vr[i], st.vs, b);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              kw[4 * i + e] = a[e];
-              vw[4 * i + e] = b[e];
-            }
-          } else {
-            dequant4(kr[i], st.ks, kw[2 * i], kw[2 * i + 1]);
-            dequant4(vr[i], st.vs, vw[2 * i], vw[2 * i + 1]);
-          }
-        }
-#pragma unroll
-        for (int i = 0; i < kOut / 4; ++i) {
-          uint4 kx = uint4{kw[4 * i], kw[4 * i + 1], kw[4 * i + 2], kw[4 * i + 3]};
-          uint4 vx = uint4{vw[4 * i], vw[4 * i + 1], vw[4 * i + 2], vw[4 * i + 3]};
-          if (zero) {
-            kx = uint4{0u, 0u, 0u, 0u};
-            vx = uint4{0u, 0u, 0u, 0u};
-          }
-          *reinterpret_cast<uint4*>(&(buf ? lk1 : lk0)[lds_at<D>(srow, schunk + i)]) = kx;
-          *reinterpret_cast<uint4*>(&(buf ? lv1 : lv0)[lds_at<D>(srow, schunk + i)]) = vx;
-        }
-      } else {
-        uint4 kx = st.k[j], vx = st.v[j];
-        if (zero) {
-          kx = uint4{0u, 0u, 0u, 0u};
-          vx = uint4{0u, 0u, 0u, 0u};
-        }
-        *reinterpret_cast<uint4*>(&(buf ? lk1 : lk0)[lds_at<D>(srow, schunk)]) = kx;
-        *reinterpret_cast<uint4*>(&(buf ? lv1 : lv0)[lds_at<D>(srow, schunk)]) = vx;
-      }
-    }
-  };
-
   f32x4 o[kPfTiles][kNT];
   // Weight sums of rows 4*grp + r (P times a ones operand: every column of
   // this tile holds its row's sum), rescaled together with o.
@@ -619,6 +507,87 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(PrefillParams p)
     // No load into LDS may still be in flight when the workgroup ends.
     __builtin_amdgcn_s_waitcnt(0);
   } else {
+    // int8 and int4 pools: thread tid stages one chunk of the step's K and V
+    // rows (row tid / 8, its D/8 codes from (tid % 8) D/8 on) through
+    // registers and scales it into fp16 on the way to LDS.
+    constexpr int kChunkVals = D / 8;
+    static_assert(kPfStep * 8 == kPfWaves * 64, "one chunk per thread covers a step");
+    // One chunk of codes: int8 16 bytes (D 128) or 8; int4 8 (D 128) or 4.
+    using Raw = typename std::conditional<
+        kI4, typename std::conditional<D == 64, uint32_t, uint2>::type,
+        typename std::conditional<D == 64, uint2, uint4>::type>::type;
+    const int srow = tid / 8;                           // step row this thread stages
+    const int schunk = (tid % 8) * (kChunkVals / 8);   // first 16-byte LDS chunk it fills
+    // A chunk as the thread holds it, with the scales of the block it came from.
+    struct Stage {
+      Raw k, v;
+      f16x2 ks, vs;
+    };
+    // Every call issues the same loads whatever the step (rows past the
+    // workgroup's last token, or a whole step past it, read the pool's first
+    // row instead), so the loads in flight are counted the same on every path
+    // and waiting for one stage never drains the next.
+    auto load_step = [&](int t0, const int (&blk)[2], Stage& st) {
+      const int tt = t0 + srow;
+      const int b = blk[srow >> 4];
+      bool ok = tt < wg_t_end;
+      if constexpr (!kTabLds) {
+        if (ok && unsigned(b) >= unsigned(p.num_blocks)) {
+          flag_error(p.err, PA_DEV_BAD_TABLE_ENTRY);
+          ok = false;
+        }
+      }
+      const int64_t off =   // in codes
+          ok ? int64_t(b) * block_elems + head_off + int64_t(tt % BS) * D + (tid % 8) * kChunkVals
+             : int64_t(0);
+      const int64_t byte = kI4 ? off / 2 : off;      // int4: two codes per byte
+      st.k = *reinterpret_cast<const Raw*>(static_cast<const uint8_t*>(p.k) + byte);
+      st.v = *reinterpret_cast<const Raw*>(static_cast<const uint8_t*>(p.v) + byte);
+      const int64_t si = ok ? int64_t(b) * p.num_heads + h : int64_t(0);
+      const _Float16 ks = p.k_scale[si], vs = p.v_scale[si];
+      st.ks = f16x2{ks, ks};
+      st.vs = f16x2{vs, vs};
+    };
+    // Rows at or past the workgroup's last token are stored as zeros: no
+    // unused slot of a last block (or other row read in its place) reaches
+    // the products.
+    auto store_step = [&](int buf, int t0, const Stage& st) {
+      // Workgroup-uniform outer test: only the last step has such rows.
+      const bool zero = t0 + kPfStep > wg_t_end && t0 + srow >= wg_t_end;
+      constexpr int kW = int(sizeof(Raw)) / 4;      // code words per chunk
+      constexpr int kOut = kI4 ? 4 * kW : 2 * kW;    // fp16 pair words they become
+      uint32_t kw[kOut], vw[kOut];
+      const uint32_t* kr = reinterpret_cast<const uint32_t*>(&st.k);
+      const uint32_t* vr = reinterpret_cast<const uint32_t*>(&st.v);
+#pragma unroll
+      for (int i = 0; i < kW; ++i) {
+        if constexpr (kI4) {
+          uint32_t a[4], b[4];
+          dequant8_i4(kr[i], st.ks, a);
+          dequant8_i4(vr[i], st.vs, b);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            kw[4 * i + e] = a[e];
+            vw[4 * i + e] = b[e];
+          }
+        } else {
+          dequant4(kr[i], st.ks, kw[2 * i], kw[2 * i + 1]);
+          dequant4(vr[i], st.vs, vw[2 * i], vw[2 * i + 1]);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < kOut / 4; ++i) {
+        uint4 kx = uint4{kw[4 * i], kw[4 * i + 1], kw[4 * i + 2], kw[4 * i + 3]};
+        uint4 vx = uint4{vw[4 * i], vw[4 * i + 1], vw[4 * i + 2], vw[4 * i + 3]};
+        if (zero) {
+          kx = uint4{0u, 0u, 0u, 0u};
+          vx = uint4{0u, 0u, 0u, 0u};
+        }
+        *reinterpret_cast<uint4*>(&(buf ? lk1 : lk0)[lds_at<D>(srow, schunk + i)]) = kx;
+        *reinterpret_cast<uint4*>(&(buf ? lv1 : lv0)[lds_at<D>(srow, schunk + i)]) = vx;
+      }
+    };
+
     // Two register stages: while a step is computed, the next one's rows wait
     // in registers for the other LDS buffer and the one after is in flight
     // from memory (a first touch from HBM can outlast one step's products).
