@@ -1,4 +1,5 @@
-// Several new tokens of each sequence attending at once over paged fp16 KV.
+// Several new tokens of each sequence attending at once over paged KV (fp16,
+// int8 or int4 pools).
 //
 // The attention formula of "One Deep Concept #01" (§2 Background) takes a
 // matrix of queries. When the last n tokens of a sequence are processed
@@ -120,13 +121,12 @@ enum : int { kKvF16 = 0, kKvI8 = 1, kKvI4 = 2 };
 
 // LDS layout of a step's K and V rows: rows of D halves, unpadded, with the
 // 16-byte chunks of row r stored at chunk index c ^ swz(r). The swizzle was
-// chosen by measuring the kernel's three access patterns on gfx950 (K operand
-// reads: 16 rows x one chunk per lane group; V reads: one chunk of each of 16
-// rows; staging stores: whole rows): with it, all three run at the LDS's
-// throughput, while rows padded by 16 bytes took 1.7x that for both reads
-// (4 bank-conflict cycles per LDS cycle) and unpadded rows 6.7x for the K
-// reads. D = 64: the K reads are bound the same way, the 8-byte V reads cost
-// the same under every layout tried.
+// chosen by measuring the kernel's access patterns on gfx950 (K operand
+// reads: 16 rows x one chunk per lane group; staging: whole rows): with it
+// the K reads run at the LDS's throughput, while rows padded by 16 bytes
+// took 1.7x that (4 bank-conflict cycles per LDS cycle) and unpadded rows
+// 6.7x. V's transposing reads (8 bytes of each of 4 rows per lane group)
+// cost about 2.4x a 16-byte read per byte under every swizzle measured.
 template <int D>
 __device__ __forceinline__ int lds_swizzle(int row) {
   if constexpr (D == 128) return (row & 3) * 4 + ((row >> 2) & 3);
@@ -273,6 +273,7 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(PrefillParams p)
       else dst[half] = t < wg_t_end ? trow[t / BS] : 0;
     }
   };
+
   f32x4 o[kPfTiles][kNT];
   // Weight sums of rows 4*grp + r (P times a ones operand: every column of
   // this tile holds its row's sum), rescaled together with o.
@@ -456,9 +457,10 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(PrefillParams p)
           b = 0;
           ok = false;
         }
-        // Row index of the slice: below 2^32 for any pool that fits in HBM
-        // (a row is at least 128 bytes). Read back as a scalar so that the
-        // resource is built in scalar registers.
+        // Token-head row index of the slice: 32 bits (the host refuses pools
+        // of more rows; a pool that fits in HBM has fewer, a row being at
+        // least 128 bytes). Read back as a scalar so that the resource is
+        // built in scalar registers.
         const uint64_t slice = __builtin_amdgcn_readfirstlane(
             (uint32_t(b) * uint32_t(p.num_heads) + uint32_t(h)) * uint32_t(BS) + uint32_t((t0 + 16 * half) % BS));
         const int voff = ok ? (r & 15) * D * 2 + ((dchunk ^ lds_swizzle<D>(r)) << 4) : kSliceBytes;
