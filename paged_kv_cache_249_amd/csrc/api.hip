@@ -1,6 +1,8 @@
 // C ABI of libpagedkv: argument validation, the error model, the pool
-// descriptor and the device error word. Kernels live in decode.hip and
-// cache_ops.hip; the host block manager in block_manager.cpp.
+// descriptor and the device error words. The attention kernels live in
+// decode.hip and prefill.hip, the cache kernels (write, copy, swap, demote)
+// in cache_ops.hip; the host block managers in block_manager.cpp and
+// mixed_manager.cpp.
 #include <hip/hip_runtime.h>
 
 #include <cmath>

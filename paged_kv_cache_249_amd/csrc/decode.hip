@@ -482,7 +482,8 @@ __device__ __forceinline__ QT to_out(float x) {
 }
 
 // NEW: element type of the fused-write source rows (void = no fused write).
-// kMixed: int8 cold pool through the table plus an fp16 hot block per sequence.
+// kMixed: an int8 or int4 cold pool (KV) through the table plus an fp16 hot
+// block per sequence.
 // kWavePart: each wave owns one whole partition (a workgroup covers kWaves
 // consecutive partitions of one (sequence, head)). Otherwise the kWaves waves
 // share each partition, taking every kWaves-th unit, and a workgroup streams
