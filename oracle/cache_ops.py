@@ -8,8 +8,8 @@ Pool layout used throughout: ``pool[block][head][offset][dim]``; a slot is
 
 * :func:`write_kv` — every row ``i`` with ``slot[i] >= 0`` goes to its slot,
   rounded to nearest even into the pool dtype. Negative slots are skipped.
-* :func:`copy_blocks` — copy-on-write copies whole blocks: the note's 案例 3
-  says the copy unit is one block, not the whole prompt.
+* :func:`copy_blocks` — copy-on-write copies whole blocks: on the same page,
+  实践案例 / 案例 3 makes the copy unit one block, not the whole prompt.
 * :func:`swap_blocks` — swapping moves whole blocks between the device pool
   and a host pool of the same per-block layout ("KV Cache与长上下文管理", the
   fourth point on what paging makes possible: page-by-page swap in and out).

@@ -1,10 +1,13 @@
 // Cache-side kernels for gfx950: writing new K/V rows into their slots,
-// copy-on-write block copies, and a plain streaming copy.
+// copy-on-write block copies, swapping blocks to pinned host memory and back,
+// demoting fp16 blocks to int8 or int4, the copy of a pinned staging buffer,
+// and plain streaming copy and read kernels (measurement baselines).
 //
 // write_kv (reshape-and-cache): row i of the new K/V goes to slot
 // slots[i] = block * B + offset for a block size B of 16, 32 or 64, the
-// lookup of "PagedAttention — 把 KV cache 当虚拟内存页来管理", 实践案例 / 案例 2. Writing new tokens into pages is also the
-// only data movement of the sliding window ("KV Cache与长上下文管理", the section
+// lookup of "PagedAttention — 把 KV cache 当虚拟内存页来管理", 实践案例 /
+// 案例 2. Writing new tokens into pages is also the only data movement of
+// the sliding window ("KV Cache与长上下文管理", the section
 // on the second problem paging solves: the new token is written into the page
 // the oldest data occupied).
 //
@@ -12,11 +15,12 @@
 // and V separately (FP16 -> INT8 compression is listed in "KV Cache与长上下文管理",
 // section 二.3, without a scheme; the group rule below is this library's and
 // is stated in pagedkv.h). int4 pools (INT4, the next entry of the same list)
-// use the same rule with codes in [-7, 7], two per byte. One wave handles one run of adjacent slot entries
-// that hit the same block (at most B rows), for one head and one tensor.
+// use the same rule with codes in [-7, 7], two per byte. One wave handles
+// one run of adjacent slot entries that hit the same block (at most B rows),
+// for one head and one tensor.
 //
-// copy_blocks: whole-block copies, the copy-on-write unit of the study note's
-// 实践案例 / 案例 3.
+// copy_blocks: whole-block copies, the copy-on-write unit of "PagedAttention
+// — 把 KV cache 当虚拟内存页来管理", 实践案例 / 案例 3.
 //
 // swap_blocks: whole blocks between the device pool and a pool in pinned host
 // memory, page by page ("KV Cache与长上下文管理", the fourth point on what paging
