@@ -54,6 +54,10 @@ def parse():
                     help="short run for rocprofv3: a 1 GiB calibration copy, then the steps")
     ap.add_argument("--summarize-profiles", metavar="DIR",
                     help="write profiles/*.txt from rocprofv3 output under DIR and exit")
+    ap.add_argument("--quantised-pools", action="store_true",
+                    help="only the OPT-13B contexts decoded from fp16, int8 and int4 pools (--steps timed "
+                         "calls each; with --profile-run, a calibration copy first): a run for rocprofv3, "
+                         "or with --summarize-profiles the summary of such runs")
     ap.add_argument("--cpu-baseline-only", action="store_true", help=argparse.SUPPRESS)
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help=argparse.SUPPRESS)
     ap.add_argument("--cpu-workers", type=int, default=1, help=argparse.SUPPRESS)
@@ -506,6 +510,8 @@ def main():
             cpu_baseline_child(args.cpu_seconds, args.cpu_workers)
         return 0
     if args.summarize_profiles:
+        if args.quantised_pools:
+            return summarize_quantised_profiles(args.summarize_profiles)
         if args.workload == "prefill":
             return summarize_prefill_profiles(args.summarize_profiles)
         return summarize_profiles(args.summarize_profiles, args.workload)
@@ -515,6 +521,8 @@ def main():
         return 2
     if args.workload == "prefill":
         return prefill_main(args)
+    if args.quantised_pools:
+        return quantised_main(args)
 
     import numpy as np
     import torch
@@ -1004,7 +1012,7 @@ def mixed_probe(pk, W, torch, np, wl, ctx, q, t_fp16, fp16_bytes, dev, cold_dtyp
             "speedup_vs_fp16": round(t_fp16 / t, 3), "cold_token_fraction": round(cold_tokens / int(cl.sum()), 4)}
 
 
-def quantised_probe(pk, W, torch, np, wl, ctx, q, dev):
+def quantised_probe(pk, W, torch, np, wl, ctx, q, dev, reps=20):
     """The same contexts stored as int8 and as int4 pools (quantised on write
     by pa_write_kv from the same fp32 rows an fp16 pool holds rounded): decode
     time, bytes read (codes and scales) and the largest output difference
@@ -1029,7 +1037,7 @@ def quantised_probe(pk, W, torch, np, wl, ctx, q, dev):
         tabd, ctxd = torch.from_numpy(tables).to(dev), torch.from_numpy(cl).to(dev)
         out = torch.empty_like(q)
         maxc = int(cl.max())
-        t = _time_calls(lambda: pk.pa_decode(eng.pool, q, out, tabd, ctxd, maxc, seq_order=order))
+        t = _time_calls(lambda: pk.pa_decode(eng.pool, q, out, tabd, ctxd, maxc, seq_order=order), reps=reps)
         torch.cuda.synchronize()
         outs[name] = out.float()
         tok = int(cl.astype(np.int64).sum())
@@ -1043,6 +1051,123 @@ def quantised_probe(pk, W, torch, np, wl, ctx, q, dev):
         res[name]["speedup_vs_f16"] = round(res["f16"]["decode_us"] / res[name]["decode_us"], 3)
         res[name]["max_abs_diff_vs_f16"] = round(float((outs[name] - outs["f16"]).abs().max()), 5)
     return res
+
+
+QUANT_STATS_FILE = os.path.join(ROOT, "profiles", "decode_quantised_pools_kernel_stats.txt")
+
+
+def quantised_profile_cmds() -> dict:
+    """The profiler commands behind QUANT_STATS_FILE (run from the repository root)."""
+    run = "-- python bench.py --quantised-pools --profile-run --steps 5"
+    return {
+        "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_quant_trace -o trace "
+                 "-- python bench.py --quantised-pools --steps 20 > gpurun_out/prof_quant_trace.log",
+        "fetch": f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/prof_quant_fetch -o fetch "
+                 f"{run} > gpurun_out/prof_quant_fetch.log",
+        "write": f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/prof_quant_write -o write "
+                 f"{run} > gpurun_out/prof_quant_write.log",
+    }
+
+
+def quantised_main(args):
+    """The OPT-13B-shaped contexts (their stated lengths) as fp16, int8 and
+    int4 pools, each decoded in --steps event-timed calls after one warm-up
+    call; prints the probe's JSON (not a bench line)."""
+    import numpy as np
+    import torch
+    import workloads as W
+    import paged_kv_cache_249_amd as pk
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = W.opt13b()
+    q = W.normal_torch((wl.num_seqs, wl.num_heads, wl.head_dim), wl.seed, W.STREAM_Q, dtype=torch.float16,
+                       device=dev)
+    if args.profile_run:
+        # Calibration for the HBM byte counters: a plain copy of known size.
+        a = torch.empty(CALIBRATION_BYTES, dtype=torch.uint8, device=dev)
+        b = torch.empty(CALIBRATION_BYTES, dtype=torch.uint8, device=dev)
+        pk.pa_stream_copy(b, a)
+        torch.cuda.synchronize()
+        del a, b
+        torch.cuda.empty_cache()
+    res = quantised_probe(pk, W, torch, np, wl, [int(c) for c in wl.context_lens], q, dev, reps=args.steps)
+    print(json.dumps({"quantised_pools": res, "calls_per_pool": args.steps + 1, "profile_run": args.profile_run,
+                      "calibration_bytes": CALIBRATION_BYTES if args.profile_run else 0,
+                      "decode_source_sha256": _sha256(DECODE_SOURCE)}), flush=True)
+    return 0
+
+
+def summarize_quantised_profiles(raw_dir: str) -> int:
+    """Write QUANT_STATS_FILE: kernel times of the three decode instantiations
+    (fp16, int8 and int4 pools) from the trace run, each one's bytes per
+    launch and rate, and their HBM bytes from the counter runs."""
+    import csv
+    import glob
+
+    cmds = quantised_profile_cmds()
+
+    def find(sub, pattern):
+        hits = glob.glob(os.path.join(raw_dir, sub, "**", pattern), recursive=True)
+        if not hits:
+            raise SystemExit(f"no {pattern} under {os.path.join(raw_dir, sub)}")
+        return hits[0]
+
+    def record(sub):
+        with open(os.path.join(raw_dir, sub + ".log")) as f:
+            return [json.loads(line) for line in f if line.startswith("{") and "quantised_pools" in line][-1]
+
+    rec = record("prof_quant_trace")
+    pools = rec["quantised_pools"]
+    # fp16 pool: decode_kernel<_Float16 ...>; int8: <signed char ...>; int4: <...Int4 ...>.
+    kind = lambda name: "i4" if "Int4" in name else ("i8" if "decode_kernelIa" in name else "f16")
+    stats = [r for r in csv.DictReader(open(find("prof_quant_trace", "*kernel_stats.csv")))
+             if "decode_kernel" in r["Name"]]
+    lines = ["# rocprofv3 kernel statistics: the OPT-13B-shaped contexts (64 seqs, 40 x 128) decoded from",
+             "# fp16, int8 and int4 pools, one single-pass decode launch per call, the stream idle between",
+             "# event-timed calls", "",
+             "command: " + cmds["trace"], "",
+             f"{'pool':<5} {'kernel':<58} {'calls':>6} {'avg_us':>9} {'min_us':>9} {'bytes':>12} "
+             f"{'avg_GB/s':>9} {'min_GB/s':>9} {'event_us':>9}"]
+    for r in stats:
+        k = kind(r["Name"])
+        nbytes = pools[k]["bytes"]
+        avg, mn = float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3
+        lines.append(f"{k:<5} {_short(r['Name']):<58} {int(r['Calls']):>6} {avg:>9.2f} {mn:>9.2f} {nbytes:>12} "
+                     f"{nbytes / avg / 1e3:>9.1f} {nbytes / mn / 1e3:>9.1f} {pools[k]['decode_us']:>9.2f}")
+    lines += ["", "bytes: K and V codes (or halves) of every context token plus, for int8 and int4, one fp16",
+              "scale per (block, head) for K and V; event_us: median event-timed call of the same run."]
+
+    def per_kernel(sub, counter):
+        agg = {}
+        for r in csv.DictReader(open(find(sub, "*counter_collection.csv"))):
+            if r["Counter_Name"] == counter:
+                name = "stream_copy_kernel" if "stream_copy_kernel" in r["Kernel_Name"] else (
+                    kind(r["Kernel_Name"]) if "decode_kernel" in r["Kernel_Name"] else None)
+                if name:
+                    agg.setdefault(name, []).append(float(r["Counter_Value"]))
+        return {k: sum(v) / len(v) for k, v in agg.items()}
+
+    if os.path.isdir(os.path.join(raw_dir, "prof_quant_fetch")) and os.path.isdir(
+            os.path.join(raw_dir, "prof_quant_write")):
+        fetch = per_kernel("prof_quant_fetch", "FETCH_SIZE")
+        write = per_kernel("prof_quant_write", "WRITE_SIZE")
+        cal_kib = CALIBRATION_BYTES / 1024
+        f_fac, w_fac = cal_kib / fetch["stream_copy_kernel"], cal_kib / write["stream_copy_kernel"]
+        lines += ["", "HBM traffic (commands:", "  " + cmds["fetch"], "  " + cmds["write"] + ")",
+                  f"calibration: stream_copy_kernel over {CALIBRATION_BYTES} B reads FETCH_SIZE "
+                  f"{fetch['stream_copy_kernel']:.1f} KiB (factor {f_fac:.4f}) and WRITE_SIZE "
+                  f"{write['stream_copy_kernel']:.1f} KiB (factor {w_fac:.4f})", ""]
+        for k in ("f16", "i8", "i4"):
+            t = (fetch[k] * f_fac + write[k] * w_fac) * 1024
+            lines.append(f"{k:<5} traffic_bytes_per_launch = {t:.0f}  over the bytes above = "
+                         f"{t / pools[k]['bytes']:.4f}")
+    lines.append("")
+    lines.append(f"decode_source_sha256 = {rec['decode_source_sha256']}")
+    with open(QUANT_STATS_FILE, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(QUANT_STATS_FILE)
+    return 0
 
 
 def causal_prefill_flops(ctx, nq, H, D):
